@@ -1,0 +1,234 @@
+"""CPU oracle for DeltaKV compression and decode attention (fp64, plain loops).
+
+TEST INFRASTRUCTURE ONLY: this package is the checker the GPU path is compared
+against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import it; the product package never does, and the two share no code.
+
+Method source: "DeltaKV: Residual-Based KV Cache Compression via Long-Range
+Similarity" (gist.science summary), section 3 "Metodologia".  The arithmetic
+lives in deltakv_oracle.c; this module only marshals numpy arrays to it and
+strings the per-step functions together into per-head helpers.
+
+Parity status per function (what pins it; the tests under tests/ hold them):
+  build_refs        pinned: bit equality with the strided rows.
+  select            pinned: brute force against numpy lexsort on tiny
+                    integer inputs, crafted ties / duplicates / short prefixes.
+  mlp / gelu        pinned: numpy matmul + scipy erf, standard-normal table
+                    values, GELU limits.
+  compress          pinned: closed form when all candidate refs are equal,
+                    orthogonal identity pair round trip.
+  reconstruct       pinned: orthogonal identity pair gives back the input.
+  attention         pinned: torch scaled_dot_product_attention in fp64 and the
+                    q = 0 closed form.
+  Latent and decode values under random GELU weights have no printed value to
+  compare with; they are pinned only through the pieces above.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+ACT_GELU = 0
+ACT_IDENTITY = 1
+
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oracle_num_refs.restype = ctypes.c_int64
+    lib.oracle_num_refs.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_build_refs.restype = None
+    lib.oracle_build_refs.argtypes = [_dp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp]
+    lib.oracle_sq_dist.restype = ctypes.c_double
+    lib.oracle_sq_dist.argtypes = [_dp, _dp, ctypes.c_int32]
+    lib.oracle_select.restype = ctypes.c_int
+    lib.oracle_select.argtypes = [_dp, _i64p, ctypes.c_int64, _dp, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p]
+    lib.oracle_gelu.restype = ctypes.c_double
+    lib.oracle_gelu.argtypes = [ctypes.c_double]
+    lib.oracle_mlp.restype = None
+    lib.oracle_mlp.argtypes = [_dp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_int32, _dp, _dp, _dp, _dp, ctypes.c_int32, _dp]
+    lib.oracle_compress.restype = None
+    lib.oracle_compress.argtypes = [_dp, ctypes.c_int64, ctypes.c_int32, _dp, _i32p,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _dp, _dp, _dp, _dp, ctypes.c_int32, _dp, _dp, _dp]
+    lib.oracle_reconstruct.restype = None
+    lib.oracle_reconstruct.argtypes = [_dp, _dp, _i32p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, _dp, _dp, _dp, _dp, ctypes.c_int32, _dp]
+    lib.oracle_attention.restype = None
+    lib.oracle_attention.argtypes = [_dp, ctypes.c_int32, _dp, _dp, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_double, _dp]
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a, typ=_dp):
+    if a is None:
+        return None
+    return a.ctypes.data_as(typ)
+
+
+@dataclass
+class MLP:
+    """One Linear -> act -> Linear block in fp64: w1 [hidden, in], b1 [hidden],
+    w2 [out, hidden], b2 [out]; act is ACT_GELU or ACT_IDENTITY."""
+    w1: np.ndarray
+    b1: np.ndarray
+    w2: np.ndarray
+    b2: np.ndarray
+    act: int = ACT_GELU
+
+    def __post_init__(self):
+        self.w1 = _f64(self.w1)
+        self.w2 = _f64(self.w2)
+        self.b1 = _f64(self.b1) if self.b1 is not None else np.zeros(self.w1.shape[0])
+        self.b2 = _f64(self.b2) if self.b2 is not None else np.zeros(self.w2.shape[0])
+
+    @property
+    def din(self):
+        return self.w1.shape[1]
+
+    @property
+    def hidden(self):
+        return self.w1.shape[0]
+
+    @property
+    def dout(self):
+        return self.w2.shape[0]
+
+
+def num_refs(T: int, s: int) -> int:
+    return int(_load().oracle_num_refs(int(T), int(s)))
+
+
+def nonref_positions(T: int, s: int) -> np.ndarray:
+    """Positions of the non-reference tokens among 0..T-1, increasing."""
+    p = np.arange(T, dtype=np.int64)
+    return p[p % s != 0]
+
+
+def build_refs(x, s: int) -> np.ndarray:
+    x = _f64(x)
+    T, d = x.shape
+    out = np.zeros((num_refs(T, s), d), dtype=np.float64)
+    _load().oracle_build_refs(_ptr(x), T, d, s, _ptr(out))
+    return out
+
+
+def sq_dist(a, b) -> float:
+    a = _f64(a)
+    b = _f64(b)
+    return float(_load().oracle_sq_dist(_ptr(a), _ptr(b), a.shape[0]))
+
+
+def select(xt, pos, refs, s: int, k: int) -> np.ndarray:
+    """Index rows (n, k) int32, -1 in unused slots."""
+    xt = _f64(xt)
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    refs = _f64(refs)
+    n, d = xt.shape
+    idx = np.full((n, k), -7, dtype=np.int32)
+    rc = _load().oracle_select(_ptr(xt), _ptr(pos, _i64p), n, _ptr(refs), refs.shape[0],
+                               d, s, k, _ptr(idx, _i32p))
+    if rc != 0:
+        raise ValueError(f"oracle_select failed with {rc}")
+    return idx
+
+
+def gelu(u: float) -> float:
+    return float(_load().oracle_gelu(float(u)))
+
+
+def mlp(inp, m: MLP) -> np.ndarray:
+    inp = _f64(inp)
+    n = inp.shape[0]
+    out = np.zeros((n, m.dout), dtype=np.float64)
+    _load().oracle_mlp(_ptr(inp), n, m.din, m.hidden, m.dout, _ptr(m.w1), _ptr(m.b1),
+                       _ptr(m.w2), _ptr(m.b2), m.act, _ptr(out))
+    return out
+
+
+def compress(xt, refs, idx, m: MLP):
+    """Returns (latent [n, d_c], kv_r [n, d], residual [n, d])."""
+    xt = _f64(xt)
+    refs = _f64(refs)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    n, d = xt.shape
+    k = idx.shape[1]
+    lat = np.zeros((n, m.dout), dtype=np.float64)
+    kvr = np.zeros((n, d), dtype=np.float64)
+    res = np.zeros((n, d), dtype=np.float64)
+    _load().oracle_compress(_ptr(xt), n, d, _ptr(refs), _ptr(idx, _i32p), k, m.hidden,
+                            m.dout, _ptr(m.w1), _ptr(m.b1), _ptr(m.w2), _ptr(m.b2), m.act,
+                            _ptr(lat), _ptr(kvr), _ptr(res))
+    return lat, kvr, res
+
+
+def reconstruct(refs, latents, idx, T: int, s: int, m: MLP) -> np.ndarray:
+    refs = _f64(refs)
+    latents = _f64(latents)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    d = refs.shape[1]
+    k = idx.shape[1]
+    xhat = np.zeros((T, d), dtype=np.float64)
+    _load().oracle_reconstruct(_ptr(refs), _ptr(latents), _ptr(idx, _i32p), T, s, d, k,
+                               m.din, m.hidden, _ptr(m.w1), _ptr(m.b1), _ptr(m.w2),
+                               _ptr(m.b2), m.act, _ptr(xhat))
+    return xhat
+
+
+def attention(q, keys, vals, scale: float) -> np.ndarray:
+    q = _f64(q)
+    keys = _f64(keys)
+    vals = _f64(vals)
+    n_q, d = q.shape
+    out = np.zeros((n_q, d), dtype=np.float64)
+    _load().oracle_attention(_ptr(q), n_q, _ptr(keys), _ptr(vals), keys.shape[0], d,
+                             float(scale), _ptr(out))
+    return out
+
+
+# ---- per-head helpers (composition of the steps above, no new arithmetic) ----
+
+def compress_head(x, s: int, k: int, m: MLP, positions=None):
+    """Offline compression of one head's rows x [T, d].
+
+    Returns refs [ceil(T/s), d], idx [n, k] and latents [n, d_c] for the
+    non-reference positions (all of them, or the given subset)."""
+    x = _f64(x)
+    T = x.shape[0]
+    refs = build_refs(x, s)
+    pos = nonref_positions(T, s) if positions is None else np.asarray(positions, np.int64)
+    idx = select(x[pos], pos, refs, s, k)
+    lat, _, _ = compress(x[pos], refs, idx, m)
+    return refs, idx, lat
+
+
+def decode_head(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat, v_idx,
+                v_dec: MLP, T: int, s: int, scale: float) -> np.ndarray:
+    """Attention of the query rows q_heads [G, d] (all mapped to this KV head)
+    over the T tokens rebuilt from the compressed K and V of one head."""
+    khat = reconstruct(k_refs, k_lat, k_idx, T, s, k_dec)
+    vhat = reconstruct(v_refs, v_lat, v_idx, T, s, v_dec)
+    return attention(q_heads, khat, vhat, scale)

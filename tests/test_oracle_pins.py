@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test ties one oracle function to something the pages or mathematics fix:
+brute force on tiny inputs, crafted ties, closed forms, textbook values and
+independent library routines (numpy, scipy, torch CPU).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import MLP, ACT_GELU, ACT_IDENTITY
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------- refs
+
+def test_build_refs_are_strided_rows_bitwise():
+    x = _rng(1).standard_normal((77, 9)).astype(np.float32).astype(np.float64)
+    for s in (1, 2, 5, 16, 77, 100):
+        r = oracle.build_refs(x, s)
+        assert r.shape == (-(-77 // s), 9)
+        assert np.array_equal(r.view(np.uint64), x[::s].view(np.uint64))
+
+
+def test_num_refs_counts_positions_multiple_of_stride():
+    for T in (0, 1, 15, 16, 17, 512, 1000):
+        for s in (1, 3, 16):
+            assert oracle.num_refs(T, s) == sum(1 for p in range(T) if p % s == 0)
+
+
+# ------------------------------------------------------------------- top-k select
+
+def _brute_force_select(x, s, k):
+    """Independent top-k: numpy distances + lexsort by (distance, ordinal)."""
+    T = x.shape[0]
+    refs = x[::s]
+    out = {}
+    for t in range(T):
+        if t % s == 0:
+            continue
+        cand = np.arange(len(refs))[np.arange(len(refs)) * s < t]
+        dist = ((x[t][None, :] - refs[cand]) ** 2).sum(axis=1)
+        order = cand[np.lexsort((cand, dist))]
+        row = np.full(k, -1, np.int32)
+        row[:min(k, len(order))] = order[:k]
+        out[t] = row
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_matches_brute_force_on_small_integers(seed):
+    # small integer coordinates: every distance is exact in any summation
+    # order, and exact ties are frequent, so the tie rule is exercised
+    rng = _rng(100 + seed)
+    T = int(rng.integers(2, 70))
+    d = int(rng.integers(1, 5))
+    s = int(rng.integers(2, 6))
+    k = int(rng.integers(1, 6))
+    x = rng.integers(-2, 3, size=(T, d)).astype(np.float64)
+    refs = oracle.build_refs(x, s)
+    pos = oracle.nonref_positions(T, s)
+    if len(pos) == 0:
+        return
+    idx = oracle.select(x[pos], pos, refs, s, k)
+    ref = _brute_force_select(x, s, k)
+    for row, t in zip(idx, pos):
+        assert np.array_equal(row, ref[int(t)]), (t, row, ref[int(t)])
+
+
+def test_select_on_float_rows_is_a_valid_ordering():
+    # fp32-valued rows at head_dim 64 (the tiny workload's shape): the chosen
+    # list must be sorted by distance and no excluded ref may be closer
+    rng = _rng(7)
+    x = rng.standard_normal((512, 64)).astype(np.float32).astype(np.float64) * 10
+    s, k = 16, 4
+    refs = oracle.build_refs(x, s)
+    pos = oracle.nonref_positions(512, s)
+    idx = oracle.select(x[pos], pos, refs, s, k)
+    for row, t in zip(idx, pos):
+        n_cand = -(-int(t) // s)
+        dist = ((x[t] - refs[:n_cand]) ** 2).sum(axis=1)
+        k_eff = min(k, n_cand)
+        assert np.all(row[k_eff:] == -1)
+        chosen = row[:k_eff]
+        assert np.all(np.diff(dist[chosen]) >= -1e-9 * dist.max())
+        rest = np.setdiff1d(np.arange(n_cand), chosen)
+        if len(rest):
+            assert dist[rest].min() >= dist[chosen].max() - 1e-9 * dist.max()
+
+
+def test_select_duplicate_refs_prefer_lower_position():
+    s, k, d = 4, 2, 3
+    x = np.zeros((21, d))
+    x[0] = x[8] = x[16] = [1, 2, 3]    # refs 0, 2, 4 identical
+    x[4] = x[12] = [9, 9, 9]           # refs 1, 3 far away
+    x[20] = [5, 5, 5]
+    x[17] = [1, 2, 3]                  # equal to refs 0, 2, 4
+    pos = np.array([17])
+    idx = oracle.select(x[pos], pos, oracle.build_refs(x, s), s, k)
+    assert idx.tolist() == [[0, 2]]
+
+
+def test_select_token_equal_to_ref_takes_it_first():
+    rng = _rng(3)
+    x = rng.standard_normal((40, 8))
+    s, k = 5, 3
+    x[33] = x[25]                      # position 25 is ref 5
+    pos = np.array([33])
+    refs = oracle.build_refs(x, s)
+    idx = oracle.select(x[pos], pos, refs, s, k)
+    assert idx[0, 0] == 5
+    assert oracle.sq_dist(x[33], refs[5]) == 0.0
+
+
+def test_select_short_prefix_uses_sentinels():
+    rng = _rng(4)
+    x = rng.standard_normal((40, 4))
+    s, k = 8, 4
+    refs = oracle.build_refs(x, s)
+    for t, k_eff in ((1, 1), (7, 1), (9, 2), (17, 3), (25, 4), (39, 4)):
+        idx = oracle.select(x[[t]], np.array([t]), refs, s, k)[0]
+        assert np.all(idx[:k_eff] >= 0) and np.all(idx[k_eff:] == -1), (t, idx)
+        assert len(set(idx[:k_eff].tolist())) == k_eff
+
+
+def test_select_all_refs_equal_gives_lowest_ordinals():
+    s, k = 3, 4
+    x = np.full((30, 5), 2.0)
+    x[1::3] = 1.0
+    x[2::3] = -1.0
+    refs = oracle.build_refs(x, s)
+    pos = oracle.nonref_positions(30, s)
+    idx = oracle.select(x[pos], pos, refs, s, k)
+    for row, t in zip(idx, pos):
+        k_eff = min(k, -(-int(t) // s))
+        assert row.tolist() == list(range(k_eff)) + [-1] * (k - k_eff)
+
+
+def test_select_is_causal():
+    # the token just before a reference position must not see that reference,
+    # the token just after it must
+    rng = _rng(5)
+    s, k = 4, 1
+    x = rng.standard_normal((30, 6)) * 10
+    x[11] = x[12] + 1e-3               # position 12 is ref 3
+    x[13] = x[12] + 1e-3
+    refs = oracle.build_refs(x, s)
+    before = oracle.select(x[[11]], np.array([11]), refs, s, k)[0, 0]
+    after = oracle.select(x[[13]], np.array([13]), refs, s, k)[0, 0]
+    assert before != 3
+    assert after == 3
+
+
+def test_select_rejects_reference_positions():
+    x = np.zeros((10, 2))
+    with pytest.raises(ValueError):
+        oracle.select(x[[4]], np.array([4]), oracle.build_refs(x, 2), 2, 1)
+
+
+def test_sq_dist_is_ordered_sum_of_squares():
+    a = np.array([1.0, -2.0, 3.5])
+    b = np.array([0.5, 2.0, -1.0])
+    assert oracle.sq_dist(a, b) == 0.25 + 16.0 + 20.25
+    assert oracle.sq_dist(a, a) == 0.0
+
+
+# ------------------------------------------------------------------------- GELU
+
+def test_gelu_textbook_values():
+    with open(os.path.join(GOLDEN, "std_normal_cdf.json")) as f:
+        table = json.load(f)["values"]
+    for e in table:
+        x, phi = e["x"], e["phi"]
+        assert abs(oracle.gelu(x) - x * phi) <= 1e-14 * max(1.0, abs(x))
+
+
+def test_gelu_limits():
+    assert oracle.gelu(0.0) == 0.0
+    assert abs(oracle.gelu(12.0) - 12.0) < 1e-15
+    assert abs(oracle.gelu(-12.0)) < 1e-30
+    for u in np.linspace(-6, 6, 49):
+        # GELU(u) - GELU(-u) = u (Phi(u) + Phi(-u) = 1)
+        assert abs(oracle.gelu(u) - oracle.gelu(-u) - u) < 1e-14
+
+
+# -------------------------------------------------------------------------- MLP
+
+def _np_mlp(inp, m):
+    h = inp @ m.w1.T + m.b1
+    if m.act == ACT_GELU:
+        h = 0.5 * h * (1 + scipy.special.erf(h / np.sqrt(2)))
+    return h @ m.w2.T + m.b2
+
+
+@pytest.mark.parametrize("act", [ACT_GELU, ACT_IDENTITY])
+def test_mlp_matches_numpy_and_scipy(act):
+    rng = _rng(11)
+    m = MLP(rng.standard_normal((48, 20)) * 0.3, rng.standard_normal(48),
+            rng.standard_normal((7, 48)) * 0.2, rng.standard_normal(7), act)
+    inp = rng.standard_normal((33, 20)) * 3
+    got = oracle.mlp(inp, m)
+    want = _np_mlp(inp, m)
+    assert got.shape == (33, 7)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+# ------------------------------------------------------------ compress / rebuild
+
+def test_compress_mean_and_residual_closed_form():
+    rng = _rng(12)
+    d, k = 6, 4
+    r = rng.standard_normal(d)
+    refs = np.stack([r, r, r, r, r])
+    xt = rng.standard_normal((3, d))
+    idx = np.array([[0, 1, 2, 3], [4, 2, -1, -1], [3, -1, -1, -1]], np.int32)
+    eye = MLP(np.eye(d), None, np.eye(d), None, ACT_IDENTITY)
+    lat, kvr, res = oracle.compress(xt, refs, idx, eye)
+    assert np.array_equal(kvr, np.tile(r, (3, 1)))
+    assert np.array_equal(res, xt - r)
+    assert np.array_equal(lat, xt - r)
+
+
+def test_compress_mean_over_existing_refs_only():
+    d = 3
+    refs = np.array([[1.0, 2.0, 3.0], [3.0, 2.0, 1.0], [2.0, 8.0, -4.0]])
+    idx = np.array([[2, 0, 1, -1]], np.int32)
+    xt = np.zeros((1, d))
+    eye = MLP(np.eye(d), None, np.eye(d), None, ACT_IDENTITY)
+    _, kvr, res = oracle.compress(xt, refs, idx, eye)
+    assert np.allclose(kvr[0], [2.0, 4.0, 0.0], rtol=0, atol=1e-15)
+    assert np.allclose(res[0], [-2.0, -4.0, 0.0], rtol=0, atol=1e-15)
+
+
+def test_compress_and_reconstruct_match_numpy_composition():
+    rng = _rng(13)
+    T, d, s, k, dc, h = 70, 12, 4, 3, 5, 16
+    x = rng.standard_normal((T, d)) * 4
+    comp = MLP(rng.standard_normal((h, d)) * 0.3, rng.standard_normal(h) * 0.1,
+               rng.standard_normal((dc, h)) * 0.3, rng.standard_normal(dc) * 0.1)
+    dec = MLP(rng.standard_normal((h, dc)) * 0.3, rng.standard_normal(h) * 0.1,
+              rng.standard_normal((d, h)) * 0.3, rng.standard_normal(d) * 0.1)
+    refs, idx, lat = oracle.compress_head(x, s, k, comp)
+    pos = oracle.nonref_positions(T, s)
+    kvr = np.stack([refs[row[row >= 0]].mean(axis=0) for row in idx])
+    want_lat = _np_mlp(x[pos] - kvr, comp)
+    assert np.max(np.abs(lat - want_lat)) <= 1e-12 * np.max(np.abs(want_lat))
+    xhat = oracle.reconstruct(refs, lat, idx, T, s, dec)
+    want = np.empty_like(x)
+    want[::s] = x[::s]
+    want[pos] = kvr + _np_mlp(lat, dec)
+    assert np.max(np.abs(xhat - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def _orthogonal_pair(d, seed):
+    q, _ = np.linalg.qr(_rng(seed).standard_normal((d, d)))
+    comp = MLP(q, None, np.eye(d), None, ACT_IDENTITY)
+    dec = MLP(q.T, None, np.eye(d), None, ACT_IDENTITY)
+    return comp, dec
+
+
+@pytest.mark.parametrize("d,s,k", [(64, 16, 4), (32, 8, 8), (16, 3, 2)])
+def test_orthogonal_pair_reconstructs_exactly(d, s, k):
+    # with an orthogonal linear Compressor / Decompressor pair and d_c = head_dim
+    # the rebuilt rows are the input rows (up to fp64 rounding)
+    from deltakv_synth import kv_rows
+    x = kv_rows(300, d, 4, 32, key=(9, d, s, k)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 21)
+    refs, idx, lat = oracle.compress_head(x, s, k, comp)
+    xhat = oracle.reconstruct(refs, lat, idx, 300, s, dec)
+    assert np.max(np.abs(xhat - x)) <= 1e-12 * np.max(np.abs(x))
+
+
+# ------------------------------------------------------------------- attention
+
+def test_attention_matches_torch_sdpa_fp64():
+    rng = _rng(14)
+    G, T, d = 4, 257, 32
+    q = rng.standard_normal((G, d))
+    kk = rng.standard_normal((T, d)) * 2
+    vv = rng.standard_normal((T, d))
+    scale = 1 / np.sqrt(d)
+    got = oracle.attention(q, kk, vv, scale)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kk)[None], torch.from_numpy(vv)[None],
+        scale=scale)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def test_attention_scale_is_applied():
+    rng = _rng(15)
+    q = rng.standard_normal((2, 8))
+    kk = rng.standard_normal((30, 8))
+    vv = rng.standard_normal((30, 8))
+    got = oracle.attention(q, kk, vv, 0.7)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kk)[None], torch.from_numpy(vv)[None],
+        scale=0.7)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def test_attention_zero_query_is_mean_of_values():
+    rng = _rng(16)
+    vv = rng.standard_normal((50, 8))
+    got = oracle.attention(np.zeros((1, 8)), rng.standard_normal((50, 8)), vv, 0.3)
+    assert np.max(np.abs(got[0] - vv.mean(axis=0))) <= 1e-14
+
+
+def test_decode_with_orthogonal_pair_is_dense_attention():
+    from deltakv_synth import kv_rows
+    T, d, s, k = 200, 32, 8, 4
+    kx = kv_rows(T, d, 4, 16, key=(10, 0)).double().numpy()
+    vx = kv_rows(T, d, 4, 16, key=(10, 1)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 5)
+    kr, ki, kl = oracle.compress_head(kx, s, k, comp)
+    vr, vi, vl = oracle.compress_head(vx, s, k, comp)
+    q = _rng(17).standard_normal((4, d))
+    scale = 1 / np.sqrt(d)
+    got = oracle.decode_head(q, kr, kl, ki, dec, vr, vl, vi, dec, T, s, scale)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kx)[None], torch.from_numpy(vx)[None],
+        scale=scale)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-10 * np.max(np.abs(want))
