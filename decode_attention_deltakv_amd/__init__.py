@@ -1,0 +1,274 @@
+"""Python binding of libdeltakv.so: DeltaKV compression and decode attention
+on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+libdeltakv.so, reached through its C ABI (include/deltakv.h); torch provides
+device memory and the current stream.  There is no fallback: if the library
+is missing, loading this package's functions raises.
+
+The functions keep the C names (without the `deltakv_` prefix, which is also
+available as an alias):
+
+    cache_bytes(shape)                         -> dict of byte sizes
+    compress_workspace_bytes(shape, t0, t1)    -> int
+    decode_workspace_bytes(shape, Hq, T)       -> int
+    build_refs(shape, x, t0, t1, cache)
+    compress(shape, x, t0, t1, compressor, cache, workspace, stats=None)
+    decode_attn(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out, workspace)
+
+`Cache` and `Mlp` below only hold torch tensors and build the C structs.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdeltakv.so")
+
+F32, BF16 = 0, 1
+ACT_GELU, ACT_IDENTITY = 0, 1
+
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE",
+                5: "HIP"}
+
+
+class DeltaKVError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"deltakv: {STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class CShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_c", ctypes.c_int32), ("capacity", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class CMlp(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("in_dim", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("out_dim", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [("refs", ctypes.c_void_p), ("ref_sqnorm", ctypes.c_void_p),
+                ("latents", ctypes.c_void_p), ("idx", ctypes.c_void_p)]
+
+
+_lib = None
+_SZ = ctypes.c_size_t
+_P = ctypes.c_void_p
+
+
+def lib():
+    """The loaded libdeltakv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decode_attention_deltakv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    sp = ctypes.POINTER(CShape)
+    L.deltakv_cache_bytes.argtypes = [sp, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
+                                      ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+    L.deltakv_compress_workspace_bytes.argtypes = [sp, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.POINTER(_SZ)]
+    L.deltakv_decode_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
+                                                 ctypes.POINTER(_SZ)]
+    L.deltakv_build_refs.argtypes = [sp, _P, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.POINTER(CCache), _P]
+    L.deltakv_compress.argtypes = [sp, _P, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(CMlp),
+                                   ctypes.POINTER(CCache), _P, _SZ, _P, _P]
+    L.deltakv_decode_attn.argtypes = [sp, ctypes.c_int32, ctypes.c_int64, _P,
+                                      ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                      ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                      ctypes.c_float, _P, _P, _SZ, _P]
+    for name in ("deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
+                 "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
+                 "deltakv_decode_attn"):
+        getattr(L, name).restype = ctypes.c_int
+    L.deltakv_status_string.argtypes = [ctypes.c_int]
+    L.deltakv_status_string.restype = ctypes.c_char_p
+    L.deltakv_last_error.argtypes = []
+    L.deltakv_last_error.restype = ctypes.c_char_p
+    L.deltakv_version.argtypes = []
+    L.deltakv_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise DeltaKVError(status, lib().deltakv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdeltakv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    # torch's current HIP stream; without a visible device only the argument
+    # checks of the library can run, and they never touch the stream
+    if not torch.cuda.is_available():
+        return None
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    num_kv_heads: int
+    head_dim: int
+    stride: int
+    k: int
+    d_c: int
+    capacity: int
+    dtype: int = BF16
+
+    def c(self) -> CShape:
+        return CShape(self.batch, self.num_kv_heads, self.head_dim, self.stride, self.k,
+                      self.d_c, self.capacity, self.dtype, 0)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == F32 else torch.bfloat16
+
+    @property
+    def n_refs(self):
+        return -(-self.capacity // self.stride)
+
+    @property
+    def n_toks(self):
+        return self.capacity - self.n_refs
+
+
+class Mlp:
+    """Linear -> act -> Linear weights as torch tensors (w1 [hidden, in],
+    b1 [hidden] fp32 or None, w2 [out, hidden], b2 [out] fp32 or None)."""
+
+    def __init__(self, w1, b1, w2, b2, act=ACT_GELU):
+        self.w1, self.b1, self.w2, self.b2, self.act = w1, b1, w2, b2, act
+
+    @classmethod
+    def from_dict(cls, d, act=ACT_GELU, device=None):
+        mv = (lambda t: t.to(device)) if device is not None else (lambda t: t)
+        return cls(mv(d["w1"]), mv(d["b1"]) if d.get("b1") is not None else None,
+                   mv(d["w2"]), mv(d["b2"]) if d.get("b2") is not None else None, act)
+
+    def c(self) -> CMlp:
+        return CMlp(_ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2),
+                    self.w1.shape[1], self.w1.shape[0], self.w2.shape[0], self.act)
+
+
+class Cache:
+    """The four arrays of one (layer, stream) compressed cache, allocated with
+    torch on `device` at the sizes deltakv_cache_bytes reports."""
+
+    def __init__(self, shape: Shape, device="cuda"):
+        sz = cache_bytes(shape)
+        B, H, R, N = shape.batch, shape.num_kv_heads, shape.n_refs, shape.n_toks
+        dt = shape.torch_dtype
+        self.refs = torch.empty(B, H, R, shape.head_dim, dtype=dt, device=device)
+        self.ref_sqnorm = torch.empty(B, H, R, dtype=torch.float32, device=device)
+        self.latents = torch.empty(B, H, max(N, 0), shape.d_c, dtype=dt, device=device)
+        self.idx = torch.empty(B, H, max(N, 0), shape.k, dtype=torch.uint16, device=device)
+        assert self.refs.numel() * self.refs.element_size() == sz["refs"]
+        assert self.latents.numel() * self.latents.element_size() == sz["latents"]
+        assert self.idx.numel() * 2 == sz["idx"]
+
+    def c(self) -> CCache:
+        return CCache(_ptr(self.refs), _ptr(self.ref_sqnorm),
+                      _ptr(self.latents) if self.latents.numel() else None,
+                      _ptr(self.idx) if self.idx.numel() else None)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.refs, self.ref_sqnorm, self.latents, self.idx))
+
+
+# --------------------------------------------------------------------- entry points
+
+def cache_bytes(shape: Shape) -> dict:
+    vals = [_SZ() for _ in range(4)]
+    cs = shape.c()
+    _check(lib().deltakv_cache_bytes(ctypes.byref(cs), *[ctypes.byref(v) for v in vals]))
+    return dict(zip(("refs", "ref_sqnorm", "latents", "idx"), (v.value for v in vals)))
+
+
+def compress_workspace_bytes(shape: Shape, t0: int, t1: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_compress_workspace_bytes(ctypes.byref(cs), t0, t1, ctypes.byref(v)))
+    return v.value
+
+
+def decode_workspace_bytes(shape: Shape, num_q_heads: int, n_tokens: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_decode_workspace_bytes(ctypes.byref(cs), num_q_heads, n_tokens,
+                                                ctypes.byref(v)))
+    return v.value
+
+
+def build_refs(shape: Shape, x: torch.Tensor, t0: int, t1: int, cache: Cache):
+    cs, cc = shape.c(), cache.c()
+    _check(lib().deltakv_build_refs(ctypes.byref(cs), _ptr(x), t0, t1, ctypes.byref(cc),
+                                    _stream()))
+
+
+def compress(shape: Shape, x: torch.Tensor, t0: int, t1: int, compressor: Mlp, cache: Cache,
+             workspace: Optional[torch.Tensor], stats: Optional[torch.Tensor] = None):
+    cs, cm, cc = shape.c(), compressor.c(), cache.c()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().deltakv_compress(ctypes.byref(cs), _ptr(x), t0, t1, ctypes.byref(cm),
+                                  ctypes.byref(cc), _ptr(workspace), wsb, _ptr(stats),
+                                  _stream()))
+
+
+def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, k_cache: Cache,
+                k_dec: Mlp, v_cache: Cache, v_dec: Mlp, scale: float, out: torch.Tensor,
+                workspace: Optional[torch.Tensor]):
+    cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().deltakv_decode_attn(ctypes.byref(cs), num_q_heads, n_tokens, _ptr(q),
+                                     ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
+                                     ctypes.byref(vm), float(scale), _ptr(out),
+                                     _ptr(workspace), wsb, _stream()))
+
+
+def status_string(status: int) -> str:
+    return lib().deltakv_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().deltakv_last_error().decode()
+
+
+def version() -> str:
+    return lib().deltakv_version().decode()
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned device buffer of at least nbytes (torch allocation)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+deltakv_cache_bytes = cache_bytes
+deltakv_compress_workspace_bytes = compress_workspace_bytes
+deltakv_decode_workspace_bytes = decode_workspace_bytes
+deltakv_build_refs = build_refs
+deltakv_compress = compress
+deltakv_decode_attn = decode_attn
+deltakv_status_string = status_string
+deltakv_last_error = last_error
+deltakv_version = version

@@ -1,0 +1,60 @@
+// dk_launch.h -- host-side launchers of libdeltakv's kernels.  Every launcher
+// enqueues on `stream` and returns hipSuccess or the launch error.  Arguments
+// have been validated by the C ABI layer (api.cpp) before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dk {
+
+// Sizes of one (layer, stream) cache, derived from deltakv_shape.
+struct Dims {
+    int B, H, d, s, k, dc;
+    int dtype;          // 0 fp32, 1 bf16
+    int64_t cap;        // capacity (positions)
+    int64_t R;          // reference rows per unit = ceil(cap / s)
+    int64_t N;          // compressed-token rows per unit = cap - R
+};
+
+struct MlpArgs {
+    const void *w1;
+    const float *b1;
+    const void *w2;
+    const float *b2;
+    int in_dim, hidden, out_dim, act;
+};
+
+struct CacheArgs {
+    void *refs;
+    float *sqn;
+    void *lat;
+    uint16_t *idx;
+};
+
+// reference-set build
+hipError_t launch_build_refs(const Dims &dm, const void *x, int64_t t0, int64_t t1,
+                             const CacheArgs &c, hipStream_t st);
+
+// compression: workspace layout and size
+size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);
+hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
+                           const MlpArgs &comp, const CacheArgs &c, void *ws, size_t ws_bytes,
+                           uint32_t *stats, hipStream_t st);
+
+// decode attention
+size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T);
+hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const CacheArgs &kc,
+                         const MlpArgs &kdec, const CacheArgs &vc, const MlpArgs &vdec,
+                         float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+
+}  // namespace dk
+
+namespace dk {
+// exact fp64 top-k scan (k_select.hip); list mode when `list` is non-null
+hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_t t1,
+                               int64_t q0, int64_t nq, const CacheArgs &c,
+                               const uint64_t *list, const uint32_t *list_count,
+                               int64_t list_cap, hipStream_t st);
+}  // namespace dk

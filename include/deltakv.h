@@ -1,0 +1,189 @@
+/*
+ * deltakv.h -- C ABI of libdeltakv.so: DeltaKV residual KV-cache compression
+ * and decode attention over the compressed cache, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method: "DeltaKV: Residual-Based KV Cache Compression via Long-Range
+ * Similarity" (gist.science summary of arXiv 2602.08005).  Section 3
+ * ("Metodologia") defines the operation; the page's section 4
+ * ("Implementazione") motivates a cache manager for irregular compressed
+ * layouts and kernels that reconstruct tokens on demand.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - A "unit" is one (sequence b, KV head h) of one layer and one stream (K or
+ *   V).  Units are independent; a call covers the B x H units of one
+ *   (layer, stream) cache.
+ * - Pointers are DEVICE pointers unless a comment says "host".  The caller owns
+ *   every buffer; the library keeps no allocation between calls and allocates
+ *   nothing itself (scratch space is the caller's workspace argument).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *   the call returns at once.  Argument errors are returned synchronously,
+ *   before anything is enqueued.  Faults inside a kernel surface at the
+ *   caller's next synchronisation of the stream.
+ * - Storage type (deltakv_dtype): x, reference rows, latents, MLP weights and
+ *   queries all use shape->dtype; biases, squared norms and the attention
+ *   output are fp32.  bf16 values are raw 16-bit bfloat16 patterns.
+ * - Positions: a sequence's tokens are positions 0 .. capacity-1.  Position p
+ *   is a REFERENCE token iff p % stride == 0 (reference ordinal j = p / stride;
+ *   token 0 is a reference).  All other positions are compressed tokens,
+ *   numbered by their "token ordinal" q in increasing position order:
+ *       q = (p / s) * (s - 1) + (p % s) - 1,
+ *       p = (q / (s - 1)) * s + (q % (s - 1)) + 1       (s = stride >= 2).
+ *   With stride 1 every token is a reference and nothing is compressed.
+ *   (section 3, "Struttura della Compressione": a small reference set at a
+ *   fixed stride, residuals for the rest.)
+ * - No C++ exception crosses this boundary.
+ */
+#ifndef DELTAKV_H
+#define DELTAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DELTAKV_OK = 0,
+    DELTAKV_ERR_INVALID_ARG = 1,  /* null pointer, bad range, inconsistent sizes */
+    DELTAKV_ERR_UNSUPPORTED = 2,  /* a size outside the compiled set (see deltakv_shape) */
+    DELTAKV_ERR_CAPACITY = 3,     /* t1 > capacity, or more references than 16-bit indices hold */
+    DELTAKV_ERR_WORKSPACE = 4,    /* workspace smaller than the matching *_workspace_bytes */
+    DELTAKV_ERR_HIP = 5           /* a HIP runtime call (e.g. a launch) failed */
+} deltakv_status;
+
+typedef enum { DELTAKV_F32 = 0, DELTAKV_BF16 = 1 } deltakv_dtype;
+
+typedef enum {
+    DELTAKV_ACT_GELU = 0,      /* GELU, erf form: u * Phi(u) */
+    DELTAKV_ACT_IDENTITY = 1   /* linear MLP (used by the exact-reconstruction check) */
+} deltakv_act;
+
+/* Sizes of one (layer, stream) cache: the quantities the method is stated in.
+ * Supported: head_dim in {64, 128}; stride >= 1; 1 <= k <= 8;
+ * d_c in {16, 32, 64, 128}; capacity >= 1 with ceil(capacity / stride) <= 65535
+ * (reference ordinals are stored as uint16). */
+typedef struct {
+    int32_t batch;         /* B: sequences */
+    int32_t num_kv_heads;  /* H: KV heads of the layer */
+    int32_t head_dim;      /* d */
+    int32_t stride;        /* s: every s-th position is a reference token */
+    int32_t k;             /* references averaged per compressed token */
+    int32_t d_c;           /* latent width */
+    int64_t capacity;      /* maximum context length in tokens (per sequence) */
+    int32_t dtype;         /* deltakv_dtype */
+    int32_t reserved;      /* must be 0 */
+} deltakv_shape;
+
+/* A light MLP: out = W2 act(W1 in + b1) + b2 (section 3, step 4: the
+ * Compressor maps d -> d_c; "Ricostruzione": the Decompressor maps d_c -> d).
+ * Weights row-major [out][in] in shape->dtype; biases fp32 or NULL (= zero).
+ * Supported hidden widths: 64, 128, 256.  Read-only. */
+typedef struct {
+    const void *w1;      /* [hidden][in_dim] */
+    const float *b1;     /* [hidden] or NULL */
+    const void *w2;      /* [out_dim][hidden] */
+    const float *b2;     /* [out_dim] or NULL */
+    int32_t in_dim;
+    int32_t hidden;
+    int32_t out_dim;
+    int32_t act;         /* deltakv_act */
+} deltakv_mlp;
+
+/* Compressed cache of one (layer, stream), structure of arrays.  With
+ * R = ceil(capacity / stride) and N = capacity - R:
+ *   refs        [B][H][R][d]     reference rows, verbatim copies of the input
+ *   ref_sqnorm  [B][H][R]        fp32 squared L2 norm of each reference row
+ *   latents     [B][H][N][d_c]   Compressor outputs, by token ordinal
+ *   idx         [B][H][N][k]     reference ordinals averaged into KV_R, nearest
+ *                                first; 0xFFFF marks an unused slot (a token at
+ *                                position p has min(k, ceil(p / s)) candidates)
+ * deltakv_cache_bytes gives the byte size of each array.  The caller allocates
+ * them; the library reads and writes them in place. */
+typedef struct {
+    void *refs;
+    float *ref_sqnorm;
+    void *latents;
+    uint16_t *idx;
+} deltakv_cache;
+
+/* Host-only.  Byte sizes of the four cache arrays for `shape` (any output
+ * pointer may be NULL).  Returns INVALID_ARG / UNSUPPORTED / CAPACITY for a
+ * shape the other entry points would reject. */
+deltakv_status deltakv_cache_bytes(const deltakv_shape *shape, size_t *refs_bytes,
+                                   size_t *ref_sqnorm_bytes, size_t *latents_bytes,
+                                   size_t *idx_bytes);
+
+/* Host-only.  Workspace that deltakv_compress needs for positions [t0, t1). */
+deltakv_status deltakv_compress_workspace_bytes(const deltakv_shape *shape, int64_t t0,
+                                                int64_t t1, size_t *bytes);
+
+/* Host-only.  Workspace that deltakv_decode_attn needs for num_q_heads query
+ * heads over n_tokens cached tokens. */
+deltakv_status deltakv_decode_workspace_bytes(const deltakv_shape *shape, int32_t num_q_heads,
+                                              int64_t n_tokens, size_t *bytes);
+
+/* Reference-set build (section 3, "Struttura della Compressione"): for every
+ * reference position p in [t0, t1), copy the input row into refs[p / s] and
+ * store its fp32 squared norm.
+ *   x: [B][H][t1 - t0][d], row i holding position t0 + i (read-only).
+ * Requires 0 <= t0 < t1 <= capacity.  Streaming callers call it chunk by chunk
+ * (t0 = previous t1); one call with t0 = 0, t1 = T builds an offline prefix. */
+deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
+                                  int64_t t1, const deltakv_cache *cache, void *stream);
+
+/* Compression of the non-reference positions in [t0, t1) (section 3,
+ * "Processo di Compressione", steps 1-4):
+ *   1. among the reference ordinals j with j * s < p, pick the k nearest to
+ *      x_p by L2 distance; distances are ranked exactly (fp64, coordinates
+ *      summed in order, no fused multiply-add) with equal distances ordered by
+ *      the lower ordinal; write them to idx, nearest first;
+ *   2. KV_R = mean of those k_eff = min(k, ceil(p / s)) reference rows;
+ *   3. residual = x_p - KV_R;
+ *   4. latents[q(p)] = compressor(residual).
+ * x: as for deltakv_build_refs.  Precondition: deltakv_build_refs has covered
+ * positions [0, t1) (earlier chunks included) and its work is ordered before
+ * this call on `stream`.  compressor: in_dim = d, out_dim = d_c.
+ * workspace: device scratch of deltakv_compress_workspace_bytes(shape, t0, t1).
+ * stats: NULL or a device uint32 to which the number of tokens whose
+ * selection needed the exhaustive fallback scan is added atomically. */
+deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64_t t0,
+                                int64_t t1, const deltakv_mlp *compressor,
+                                const deltakv_cache *cache, void *workspace,
+                                size_t workspace_bytes, uint32_t *stats, void *stream);
+
+/* Decode attention over the compressed cache ("Ricostruzione" in section 3,
+ * with textbook softmax attention): for every query head g of sequence b,
+ * with KV head h = g / (num_q_heads / H),
+ *   out[b][g] = sum_t softmax_t(scale * q[b][g] . K^_t) V^_t,   t = 0..n_tokens-1,
+ * where a reference position's K^/V^ is its stored row and a compressed
+ * token's is KV_R (mean of its idx rows) + decompressor(latent).
+ *   q:   [B][num_q_heads][d] in shape->dtype;  out: [B][num_q_heads][d] fp32.
+ *   k_dec / v_dec: in_dim = d_c, out_dim = d.
+ * num_q_heads must be a multiple of H with num_q_heads / H <= 8; 1 <= n_tokens
+ * <= capacity and every position < n_tokens must have been built and
+ * compressed.  workspace: deltakv_decode_workspace_bytes(shape, num_q_heads,
+ * n_tokens) bytes. */
+deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
+                                   int64_t n_tokens, const void *q,
+                                   const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                   const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                   float softmax_scale, float *out, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *deltakv_status_string(deltakv_status status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char *deltakv_last_error(void);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char *deltakv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTAKV_H */

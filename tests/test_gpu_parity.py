@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Indices must match bit for bit (rank order and unused
+slots included); latents and attention outputs must be within the stated
+tolerance (max over rows of max|g - o| / max|o|: 2e-2 for bf16, 1e-4 for
+fp32).  Decode is checked on the GPU's own stored cache, so each stage is
+compared on identical inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_deltakv_amd as dk
+import oracle
+from deltakv_synth import WORKLOADS, kv_rows, queries, xavier_mlp
+from parity import (TOL, check_compress_unit, gpu_compress, gpu_decode, gpu_mlp, make_kv,
+                    make_mlp, oracle_decode_head, oracle_mlp, rel_err_rows, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(name, B, H, G, T, d, s, k, dc, hid, dtype, seed, bias_std=0.0, chunks=None,
+              n_dirs=8, n_centroids=64, positions=None, decode_heads=None):
+    say(f"[case] {name}: B={B} H={H} G={G} T={T} d={d} s={s} k={k} dc={dc} hid={hid} "
+        f"dtype={dtype} seed={seed}")
+    tdt = torch.float32 if dtype == dk.F32 else torch.bfloat16
+    shape = dk.Shape(B, H, d, s, k, dc, T, dtype)
+    kx = make_kv(B, H, T, d, tdt, key=(seed, 0), n_dirs=n_dirs, n_centroids=n_centroids)
+    vx = make_kv(B, H, T, d, tdt, key=(seed, 1), n_dirs=n_dirs, n_centroids=n_centroids)
+    kcw, _ = make_mlp(d, hid, dc, tdt, key=(seed, 10), bias_std=bias_std)
+    vcw, _ = make_mlp(d, hid, dc, tdt, key=(seed, 11), bias_std=bias_std)
+    kdw, _ = make_mlp(dc, hid, d, tdt, key=(seed, 12), bias_std=bias_std)
+    vdw, _ = make_mlp(dc, hid, d, tdt, key=(seed, 13), bias_std=bias_std)
+    kc = gpu_compress(shape, kx, gpu_mlp(kcw, dk.ACT_GELU), chunks)
+    vc = gpu_compress(shape, vx, gpu_mlp(vcw, dk.ACT_GELU), chunks)
+    tol = TOL[dtype]
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            worst = max(worst, check_compress_unit(shape, kx[b, h], kc, b, h,
+                                                   oracle_mlp(kcw, dk.ACT_GELU), positions, tol))
+            worst = max(worst, check_compress_unit(shape, vx[b, h], vc, b, h,
+                                                   oracle_mlp(vcw, dk.ACT_GELU), positions, tol))
+    Hq = H * G
+    q = queries(B * Hq, d, key=(seed, 20), dtype=tdt).reshape(B, Hq, d)
+    scale = 1.0 / math.sqrt(d)
+    out = gpu_decode(shape, Hq, T, q, kc, gpu_mlp(kdw, dk.ACT_GELU), vc,
+                     gpu_mlp(vdw, dk.ACT_GELU), scale)
+    derr = 0.0
+    heads = [(b, h) for b in range(B) for h in range(H)] if decode_heads is None else decode_heads
+    for b, h in heads:
+        want = oracle_decode_head(shape, T, to_np(q[b, h * G:(h + 1) * G]), kc, vc, b, h,
+                                  oracle_mlp(kdw, dk.ACT_GELU), oracle_mlp(vdw, dk.ACT_GELU),
+                                  scale)
+        derr = max(derr, rel_err_rows(out[b, h * G:(h + 1) * G], want))
+    say(f"[case] {name}: latent rel err {worst:.3e}, decode rel err {derr:.3e}")
+    assert derr <= tol, f"decode rel err {derr} > {tol}"
+    return kc, vc, out
+
+
+def test_tiny_single_head_fp32():
+    w = WORKLOADS["tiny-1head-T512-fp32"]
+    _run_case("tiny-1head-T512-fp32", 1, 1, 1, w.T, w.head_dim, w.stride, w.k, w.d_c, w.hidden,
+              dk.F32, seed=1, n_dirs=w.n_dirs, n_centroids=w.n_centroids)
+
+
+def test_bf16_llama_heads_ragged():
+    # several token tiles, ragged tail, two sequences, GQA 4
+    _run_case("bf16-llama-heads-ragged", 2, 2, 4, 1000, 128, 16, 4, 32, 256, dk.BF16, seed=2,
+              bias_std=0.05)
+
+
+@pytest.mark.parametrize("cfg", [
+    # (d, s, k, dc, hid, G, T, dtype)
+    (128, 8, 8, 16, 256, 4, 777, dk.BF16),    # streaming workload's shapes
+    (64, 3, 2, 64, 64, 1, 500, dk.BF16),
+    (64, 5, 5, 128, 128, 8, 301, dk.BF16),
+    (128, 16, 4, 32, 256, 2, 600, dk.F32),
+    (64, 2, 1, 16, 128, 4, 257, dk.F32),
+])
+def test_shape_variants(cfg):
+    d, s, k, dc, hid, G, T, dtype = cfg
+    _run_case(f"variant-{cfg}", 1, 2, G, T, d, s, k, dc, hid, dtype, seed=3 + s + k)
+
+
+def test_streaming_chunks_match_offline_bitwise():
+    B, H, T, d, s, k, dc, hid = 1, 2, 700, 128, 8, 8, 16, 256
+    say(f"[case] streaming: T={T}")
+    shape = dk.Shape(B, H, d, s, k, dc, T, dk.BF16)
+    x = make_kv(B, H, T, d, torch.bfloat16, key=(40, 0))
+    cw, _ = make_mlp(d, hid, dc, torch.bfloat16, key=(40, 1))
+    comp = gpu_mlp(cw, dk.ACT_GELU)
+    off = gpu_compress(shape, x, comp)
+    bounds = [0, 100, 357, 358, 359, 360, 512, 513, 600] + list(range(601, 700, 9)) + [700]
+    ch = gpu_compress(shape, x, comp, chunks=sorted(set(bounds)))
+    for name in ("refs", "ref_sqnorm", "latents", "idx"):
+        a, b = getattr(off, name), getattr(ch, name)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
+def test_short_prefixes_and_single_token_context():
+    # tokens with fewer than k candidates (sentinel slots), and decode over
+    # T = 1 (only reference 0) and T = 2
+    B, H, G, d, s, k, dc, hid = 1, 1, 4, 64, 16, 4, 16, 128
+    _run_case("short-prefix", B, H, G, 40, d, s, k, dc, hid, dk.BF16, seed=50)
+    for T in (1, 2, 17):
+        _run_case(f"tiny-context-{T}", B, H, G, T, d, s, k, dc, hid, dk.F32, seed=51 + T)
+
+
+def test_stride_one_is_dense_attention():
+    B, H, G, T, d = 1, 2, 4, 300, 128
+    say("[case] stride-1")
+    shape = dk.Shape(B, H, d, 1, 4, 32, T, dk.BF16)
+    kx = make_kv(B, H, T, d, torch.bfloat16, key=(60, 0))
+    vx = make_kv(B, H, T, d, torch.bfloat16, key=(60, 1))
+    cw, _ = make_mlp(d, 256, 32, torch.bfloat16, key=(60, 2))
+    dw, _ = make_mlp(32, 256, d, torch.bfloat16, key=(60, 3))
+    kc = gpu_compress(shape, kx, gpu_mlp(cw, 0))
+    vc = gpu_compress(shape, vx, gpu_mlp(cw, 0))
+    q = queries(B * H * G, d, key=(60, 4), dtype=torch.bfloat16).reshape(B, H * G, d)
+    out = gpu_decode(shape, H * G, T, q, kc, gpu_mlp(dw, 0), vc, gpu_mlp(dw, 0), 1 / math.sqrt(d))
+    for h in range(H):
+        want = oracle.attention(to_np(q[0, h * G:(h + 1) * G]), to_np(kx[0, h]), to_np(vx[0, h]),
+                                1 / math.sqrt(d))
+        assert rel_err_rows(out[0, h * G:(h + 1) * G], want) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [dk.F32, dk.BF16])
+def test_orthogonal_identity_pair_gives_dense_attention(dtype):
+    # identity activation, d_c = hidden = head_dim, W1c = Q, W2c = I,
+    # W1d = Q^T, W2d = I: the rebuilt cache is the input, so decode equals
+    # dense attention on the original K / V
+    B, H, G, T, d, s, k = 1, 2, 4, 640, 64, 16, 4
+    say(f"[case] orthogonal pair dtype={dtype}")
+    tdt = torch.float32 if dtype == dk.F32 else torch.bfloat16
+    shape = dk.Shape(B, H, d, s, k, d, T, dtype)
+    kx = make_kv(B, H, T, d, tdt, key=(70, 0))
+    vx = make_kv(B, H, T, d, tdt, key=(70, 1))
+    Q, _ = np.linalg.qr(np.random.default_rng(70).standard_normal((d, d)))
+    Qt = torch.from_numpy(Q).to(tdt)
+    eye = torch.eye(d).to(tdt)
+    comp = dk.Mlp(Qt.contiguous().cuda(), None, eye.cuda(), None, dk.ACT_IDENTITY)
+    dec = dk.Mlp(Qt.T.contiguous().cuda(), None, eye.cuda(), None, dk.ACT_IDENTITY)
+    kc = gpu_compress(shape, kx, comp)
+    vc = gpu_compress(shape, vx, comp)
+    q = queries(B * H * G, d, key=(70, 2), dtype=tdt).reshape(B, H * G, d)
+    out = gpu_decode(shape, H * G, T, q, kc, dec, vc, dec, 1 / math.sqrt(d))
+    for h in range(H):
+        want = oracle.attention(to_np(q[0, h * G:(h + 1) * G]), to_np(kx[0, h]), to_np(vx[0, h]),
+                                1 / math.sqrt(d))
+        err = rel_err_rows(out[0, h * G:(h + 1) * G], want)
+        say(f"  head {h}: rel err vs dense attention {err:.3e}")
+        assert err <= TOL[dtype]
+
+
+def test_duplicate_reference_rows_break_ties_by_position():
+    B, H, T, d, s, k = 1, 1, 400, 128, 8, 4
+    say("[case] duplicate refs")
+    x = make_kv(B, H, T, d, torch.bfloat16, key=(80, 0))
+    # make references 3, 10, 20, 33 identical, and several tokens equal to them
+    for j in (10, 20, 33):
+        x[0, 0, j * s] = x[0, 0, 3 * s]
+    for p in (3 * s + 1, 21 * s + 5, 40 * s + 7, 49 * s + 3):
+        x[0, 0, p] = x[0, 0, 3 * s]
+    shape = dk.Shape(B, H, d, s, k, 32, T, dk.BF16)
+    cw, _ = make_mlp(d, 256, 32, torch.bfloat16, key=(80, 1))
+    c = gpu_compress(shape, x, gpu_mlp(cw, 0))
+    check_compress_unit(shape, x[0, 0], c, 0, 0, oracle_mlp(cw, 0), tol=2e-2)
+    q = lambda p: (p // s) * (s - 1) + (p % s) - 1
+    assert c.idx[0, 0, q(40 * s + 7)].tolist() == [3, 10, 20, 33]
+    assert c.idx[0, 0, q(21 * s + 5)].tolist()[:3] == [3, 10, 20]
+
+
+def test_repeat_runs_are_bitwise_identical():
+    B, H, G, T, d, s, k, dc, hid = 1, 2, 4, 900, 128, 16, 4, 32, 256
+    say("[case] determinism")
+    kc1, vc1, out1 = _run_case("determinism-a", B, H, G, T, d, s, k, dc, hid, dk.BF16, seed=90)
+    kc2, vc2, out2 = _run_case("determinism-b", B, H, G, T, d, s, k, dc, hid, dk.BF16, seed=90)
+    for a, b in ((kc1, kc2), (vc1, vc2)):
+        for name in ("refs", "latents", "idx"):
+            assert torch.equal(getattr(a, name).view(torch.uint8), getattr(b, name).view(torch.uint8))
+    assert np.array_equal(out1, out2)
+
+
+def test_llama_layer_32k_sampled():
+    # the one-layer Llama-3.1-8B-shaped workload at full size: every unit is
+    # compressed on the GPU; the oracle checks sampled tokens per unit (first
+    # and last 64 compressed tokens plus 128 random ones) and decode on two
+    # KV heads (8 query heads) over all 32768 tokens
+    w = WORKLOADS["llama8b-1layer-T32k-bf16"]
+    T, s = w.T, w.stride
+    nonref = oracle.nonref_positions(T, s)
+    rng = np.random.default_rng(7)
+    pos = np.unique(np.concatenate([nonref[:64], nonref[-64:],
+                                    rng.choice(nonref, 128, replace=False)]))
+    _run_case("llama8b-1layer-T32k-bf16 sampled", 1, w.kv_heads, w.q_heads // w.kv_heads, T,
+              w.head_dim, s, w.k, w.d_c, w.hidden, dk.BF16, seed=100, n_dirs=w.n_dirs,
+              n_centroids=w.n_centroids, positions=pos, decode_heads=[(0, 0), (0, 7)])
