@@ -1,0 +1,280 @@
+"""Benchmark: DeltaKV compression + decode attention on one MI355X.
+
+One step = the whole hot path over one synthetic batch of the workload:
+reference build + compression of the full prefix (every layer, KV head and
+stream), then `decode_steps` decode-attention steps over every layer, each with
+fresh N(0,1) queries.  Inputs (uncompressed K/V, weights, queries) are resident
+in HBM before the timed region.
+
+Prints one JSON line:
+  value              compressed KV tokens/s  (B * T / compression time)
+  decode_attn_tok_s  decode tokens/s         (B * decode_steps / decode time;
+                                              one token = attention over all layers)
+  decode_eff_hbm_gbs compressed bytes read per decode step / decode-step time
+  roofline           the dominant kernel against its roofline (HIP events)
+  cpu_baseline       the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b-32layer-T128k-bf16")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="override the workload's decode steps per bench step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    return ap.parse_args()
+
+
+class Setup:
+    """Inputs, weights, caches and workspaces of one workload, on the GPU."""
+
+    def __init__(self, wl, widx):
+        import decode_attention_deltakv_amd as dk
+        from deltakv_synth import kv_rows, queries, xavier_mlp, unit_key
+        self.dk = dk
+        self.wl = wl
+        dt = wl.torch_dtype
+        self.shape = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, wl.T,
+                              dk.F32 if wl.dtype == "fp32" else dk.BF16)
+        L, B, H, T, d = wl.layers, wl.batch, wl.kv_heads, wl.T, wl.head_dim
+        t0 = time.time()
+        self.x = []          # [layer][stream] -> [B, H, T, d]
+        for l in range(L):
+            row = []
+            for st in (0, 1):
+                x = torch.empty(B, H, T, d, dtype=dt, device="cuda")
+                for b in range(B):
+                    for h in range(H):
+                        x[b, h] = kv_rows(T, d, wl.n_dirs, wl.n_centroids,
+                                          key=unit_key(widx, b, l, h, st), dtype=dt,
+                                          device="cuda")
+                row.append(x)
+            self.x.append(row)
+        torch.cuda.synchronize()
+        log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
+        self.comp, self.dec = [], []
+        for l in range(L):
+            self.comp.append([dk.Mlp.from_dict(xavier_mlp(d, wl.hidden, wl.d_c,
+                                                          key=(1, widx, l, st), dtype=dt,
+                                                          device="cuda"))
+                              for st in (0, 1)])
+            self.dec.append([dk.Mlp.from_dict(xavier_mlp(wl.d_c, wl.hidden, d,
+                                                         key=(2, widx, l, st), dtype=dt,
+                                                         device="cuda"))
+                             for st in (0, 1)])
+        self.cache = [[dk.Cache(self.shape) for _ in (0, 1)] for _ in range(L)]
+        self.cws = dk.workspace(dk.compress_workspace_bytes(self.shape, 0, T))
+        self.Hq = wl.q_heads
+        self.dws = dk.workspace(dk.decode_workspace_bytes(self.shape, self.Hq, T))
+        self.out = torch.empty(B, self.Hq, d, dtype=torch.float32, device="cuda")
+        self.stats = torch.zeros(4, dtype=torch.int32, device="cuda")
+        self.scale = 1.0 / math.sqrt(d)
+        self.qbank = queries(64 * L * B * self.Hq, d, key=(3, widx), dtype=dt,
+                             device="cuda").reshape(64, L, B, self.Hq, d)
+
+    def compress_all(self):
+        dk, sh, T = self.dk, self.shape, self.wl.T
+        for l in range(self.wl.layers):
+            for st in (0, 1):
+                x = self.x[l][st]
+                dk.build_refs(sh, x, 0, T, self.cache[l][st])
+                dk.compress(sh, x, 0, T, self.comp[l][st], self.cache[l][st], self.cws,
+                            self.stats)
+
+    def decode_step(self, i):
+        dk, sh, T = self.dk, self.shape, self.wl.T
+        qs = self.qbank[i % 64]
+        for l in range(self.wl.layers):
+            c, d = self.cache[l], self.dec[l]
+            dk.decode_attn(sh, self.Hq, T, qs[l], c[0], d[0], c[1], d[1], self.scale, self.out,
+                           self.dws)
+
+
+def decode_bytes_per_layer(wl):
+    """Algorithmic HBM bytes one decode_attn call (one layer) must read:
+    per unit and stream the reference rows, latents and index lists, plus the
+    two Decompressors, the queries and the output."""
+    elt = 4 if wl.dtype == "fp32" else 2
+    R = -(-wl.T // wl.stride)
+    N = wl.T - R
+    unit = R * wl.head_dim * elt + N * wl.d_c * elt + N * wl.k * 2
+    dec = 2 * ((wl.d_c * wl.hidden + wl.hidden * wl.head_dim) * elt
+               + (wl.hidden + wl.head_dim) * 4)
+    qo = wl.batch * wl.q_heads * wl.head_dim * (elt + 4)
+    return wl.batch * wl.kv_heads * 2 * unit + dec + qo
+
+
+def compress_flops(wl):
+    """Algorithmic FLOPs of one full compression: 2 d per causal
+    (token, reference) pair, plus the Compressor's 2 (d h + h d_c) per token."""
+    s, T = wl.stride, wl.T
+    R = -(-T // s)
+    pairs = 0
+    # sum over non-reference positions p of ceil(p / s)
+    for j in range(R):
+        lo, hi = j * s + 1, min((j + 1) * s, T)    # positions with ceil(p/s) = j + 1
+        if hi >= lo:
+            pairs += (hi - lo + 1) * (j + 1)
+    N = T - R
+    units = wl.layers * wl.batch * wl.kv_heads * 2
+    return units * (2 * wl.head_dim * pairs + 2 * (wl.head_dim * wl.hidden
+                                                   + wl.hidden * wl.d_c) * N)
+
+
+def cpu_baseline(wl, widx, n_tok, threads):
+    """The oracle as it is, on a bounded sample of the same workload: select +
+    compress for n_tok uniformly sampled compressed positions of one unit
+    (layer 0, head 0, K stream), split over `threads` host threads."""
+    import oracle
+    from deltakv_synth import kv_rows, unit_key, xavier_mlp
+    T, s = wl.T, wl.stride
+    x = kv_rows(T, wl.head_dim, wl.n_dirs, wl.n_centroids, key=unit_key(widx, 0, 0, 0, 0),
+                dtype=wl.torch_dtype).float().double().numpy()
+    w = xavier_mlp(wl.head_dim, wl.hidden, wl.d_c, key=(1, widx, 0, 0), dtype=wl.torch_dtype)
+    f = lambda t: t.float().double().numpy()
+    m = oracle.MLP(f(w["w1"]), f(w["b1"]), f(w["w2"]), f(w["b2"]), oracle.ACT_GELU)
+    refs = oracle.build_refs(x, s)
+    pos = np.sort(np.random.default_rng(11).choice(oracle.nonref_positions(T, s), n_tok,
+                                                   replace=False))
+    parts = np.array_split(pos, threads)
+
+    def work(p):
+        idx = oracle.select(x[p], p, refs, s, wl.k)
+        oracle.compress(x[p], refs, idx, m)
+
+    t0 = time.perf_counter()
+    ths = [threading.Thread(target=work, args=(p,)) for p in parts]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    dt = time.perf_counter() - t0
+    rows_per_token = wl.layers * wl.kv_heads * 2 * (1 - 1 / s)   # compressed rows per position
+    return {"value": n_tok / dt / rows_per_token, "unit": "tok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"select+compress of {n_tok} uniformly sampled compressed positions of "
+                      f"one unit (layer 0, KV head 0, K) at T={T}; {dt:.2f}s; scaled by the "
+                      f"{rows_per_token:.0f} compressed rows per sequence position"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); nothing to do for "
+              "more GPUs in this build", flush=True)
+        sys.exit(2)
+    from deltakv_synth import WORKLOADS, workload_index
+    wl = WORKLOADS[a.workload]
+    widx = workload_index(a.workload)
+    dsteps = wl.decode_steps if a.decode_steps is None else a.decode_steps
+    torch.cuda.set_device(0)
+    S = Setup(wl, widx)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step(i, timed):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        S.compress_all()
+        e1.record(stream)
+        for k in range(dsteps):
+            S.decode_step(i * dsteps + k)
+        e2.record(stream)
+        return e0, e1, e2
+
+    for i in range(a.warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    t0 = time.perf_counter()
+    evs = [one_step(a.warmup + i, True) for i in range(a.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    comp_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    dec_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+    ms_per_step = wall * 1000 / a.steps
+    log(f"[bench] compress {comp_ms:.2f} ms, decode {dec_ms:.2f} ms for {dsteps} steps")
+
+    # per-launch timing of the decode entry point (the step's dominant cost),
+    # events on the launch stream around single calls
+    n_launch = min(32, wl.layers * 4)
+    starts, ends = [ev() for _ in range(n_launch)], [ev() for _ in range(n_launch)]
+    qs = S.qbank[0]
+    for i in range(n_launch):
+        l = i % wl.layers
+        c, d = S.cache[l], S.dec[l]
+        starts[i].record(stream)
+        S.dk.decode_attn(S.shape, S.Hq, wl.T, qs[l], c[0], d[0], c[1], d[1], S.scale, S.out,
+                         S.dws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]))
+    per_layer_bytes = decode_bytes_per_layer(wl)
+    achieved = per_layer_bytes / (launch_ms * 1e-3) / 1e9
+
+    B, T = wl.batch, wl.T
+    step_bytes = per_layer_bytes * wl.layers
+    res = {
+        "metric": "compressed KV tokens/s; decode-attn tok/s + effective HBM GB/s at 128k ctx",
+        "value": B * T / (comp_ms * 1e-3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded anisotropic + cluster K/V rows, Xavier random-init MLPs, "
+                "N(0,1) queries)",
+        "config": {"workload": wl.name, "layers": wl.layers, "batch": B, "kv_heads": wl.kv_heads,
+                   "q_heads": wl.q_heads, "head_dim": wl.head_dim, "T": T, "stride": wl.stride,
+                   "k": wl.k, "d_c": wl.d_c, "hidden": wl.hidden, "decode_steps": dsteps},
+        "compress_ms_per_step": comp_ms,
+        "compress_tflops": compress_flops(wl) / (comp_ms * 1e-3) / 1e12,
+        "decode_ms_per_step": dec_ms,
+        "decode_attn_tok_s": B * dsteps / (dec_ms * 1e-3),
+        "decode_eff_hbm_gbs": step_bytes * dsteps / (dec_ms * 1e-3) / 1e9,
+        "fallback_tokens": int(S.stats[0].item()),
+        "roofline": {"kernel": "deltakv_decode_attn (one layer)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": per_layer_bytes,
+                     "launch_ms": launch_ms},
+    }
+    if not a.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"[bench] cpu baseline on {threads} threads")
+        res["cpu_baseline"] = cpu_baseline(wl, widx, a.cpu_sample_tokens, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,86 @@
+// dk_mfma.h -- CDNA4 (gfx950) matrix-core helpers and packed-f16 activation.
+//
+// Operand layouts of the two 16x16x32 MFMA forms used here (checked on the
+// hardware): for lane l of a wave64,
+//   A (16 x 32, row-major M x K): lane holds A[l % 16][8 * (l / 16) + i], i = 0..7
+//   B (32 x 16, K x N):           lane holds B[8 * (l / 16) + i][l % 16]
+//   C (16 x 16):                  lane holds C[4 * (l / 16) + r][l % 16], r = 0..3
+// and for the 32x32x16 form:
+//   A (32 x 16): lane holds A[l % 32][8 * (l / 32) + i]
+//   B (16 x 32): lane holds B[8 * (l / 32) + i][l % 32]
+//   C (32 x 32): lane holds C[8 * (r / 4) + 4 * (l / 32) + (r % 4)][l % 32], r = 0..15
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 16-byte global load of 8 consecutive 16-bit values (pointer 16-byte aligned).
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Two fp32 values -> packed bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7fffu + ((ua >> 16) & 1u);
+    ub += 0x7fffu + ((ub >> 16) & 1u);
+    return (ua >> 16) | (ub & 0xffff0000u);
+}
+
+// Two fp32 values -> packed f16 (round toward zero; one instruction).
+__device__ __forceinline__ f16x2 pack_f16(float a, float b) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// GELU of two fp32 pre-activations, evaluated in packed f16:
+//   GELU(u) = u * Phi(u),   Phi(u) ~= clamp01(0.5 + v * Q(v * v)),  v = u / 2,
+// where Q is a degree-4 polynomial fitted (least squares with reweighting
+// toward the maximum error) to the standard normal CDF on |u| <= 3.5.  Its
+// leading coefficient is positive, so beyond the fitted range the clamp
+// saturates Phi to 0 or 1; the largest error of Phi over the real line is
+// below 9e-4 before f16 rounding, and of GELU after it below
+// 2.2e-3 * max(1, |u|).  Used only on the bf16 decode path, where the hidden
+// activations feed f16 matrix products.
+__device__ __forceinline__ f16x2 gelu2_f16(float a, float b) {
+    const f16x2 u = pack_f16(a, b);
+    const f16x2 half = {(_Float16)0.5f, (_Float16)0.5f};
+    const f16x2 v = u * half;
+    const f16x2 t = v * v;
+    const f16x2 c4 = {(_Float16)6.1716814e-3f, (_Float16)6.1716814e-3f};
+    const f16x2 c3 = {(_Float16)-5.8874029e-2f, (_Float16)-5.8874029e-2f};
+    const f16x2 c2 = {(_Float16)2.2937544e-1f, (_Float16)2.2937544e-1f};
+    const f16x2 c1 = {(_Float16)-4.9287843e-1f, (_Float16)-4.9287843e-1f};
+    const f16x2 c0 = {(_Float16)7.9291154e-1f, (_Float16)7.9291154e-1f};
+    f16x2 p = __builtin_elementwise_fma(c4, t, c3);
+    p = __builtin_elementwise_fma(p, t, c2);
+    p = __builtin_elementwise_fma(p, t, c1);
+    p = __builtin_elementwise_fma(p, t, c0);
+    f16x2 phi;
+    asm("v_pk_fma_f16 %0, %1, %2, %3 clamp" : "=v"(phi) : "v"(v), "v"(p), "v"(half));
+    return u * phi;
+}
+
+}  // namespace dk

@@ -23,8 +23,11 @@
 //   combine   log-sum-exp merge of the partitions, W2V applied once to acc_h
 #include <math.h>
 
+#include <algorithm>
+
 #include "dk_common.h"
 #include "dk_launch.h"
+#include "dk_mfma.h"
 
 namespace dk {
 namespace {
@@ -34,8 +37,9 @@ constexpr int kMaxD = 128;
 constexpr int kMaxH = 256;
 constexpr int kMaxDC = 128;
 constexpr int kMaxK = 8;
-constexpr int kTB = 16;        // tokens per tile
-constexpr int kTokPart = 1024; // compressed tokens per partition
+constexpr int kTB = 16;        // tokens per tile (general path)
+constexpr int kTileTok = 32;   // tokens per tile (matrix-core path); partitions hold whole tiles
+constexpr int kTargetBlocks = 1024;
 constexpr int kRefPart = 1024; // reference rows per partition
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
 
@@ -50,6 +54,7 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecPlan {
     int64_t Rt, Nt, Ptok, Pref, P;
+    int tiles_per_part;
     size_t off_u, off_cq, off_qr, off_part, total;
 };
 
@@ -58,7 +63,12 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     const int G = Hq / dm.H;
     p.Rt = refs_upto(T, dm.s);
     p.Nt = T - p.Rt;
-    p.Ptok = (p.Nt + kTokPart - 1) / kTokPart;
+    // about kTargetBlocks blocks per launch over all units, whole 32-token tiles
+    const int64_t U = (int64_t)dm.B * dm.H;
+    const int64_t tiles = (p.Nt + kTileTok - 1) / kTileTok;
+    const int64_t want = std::max<int64_t>(1, (kTargetBlocks + U - 1) / U);
+    p.tiles_per_part = (int)std::max<int64_t>(2, (tiles + want - 1) / want);
+    p.Ptok = (tiles + p.tiles_per_part - 1) / p.tiles_per_part;
     p.Pref = (p.Rt + kRefPart - 1) / kRefPart;
     p.P = p.Ptok + p.Pref;
     size_t off = 0;
@@ -125,7 +135,8 @@ __global__ __launch_bounds__(256) void refscore_kernel(const T *__restrict__ q, 
 template <typename T>
 __global__ __launch_bounds__(256) void main_kernel(
     int Hq, int G, int d, int dc, int k, int s, int64_t Rcap, int64_t Ncap, int64_t Rt,
-    int64_t Nt, int64_t Ptok, const T *__restrict__ kref, const T *__restrict__ klat,
+    int64_t Nt, int64_t Ptok, int64_t tok_per_part, const T *__restrict__ kref,
+    const T *__restrict__ klat,
     const uint16_t *__restrict__ kidx, const T *__restrict__ vref, const T *__restrict__ vlat,
     const uint16_t *__restrict__ vidx, const T *__restrict__ kw1, const float *__restrict__ kb1,
     int khid, int kact, const T *__restrict__ vw1, const float *__restrict__ vb1, int vhid,
@@ -161,8 +172,8 @@ __global__ __launch_bounds__(256) void main_kernel(
             us[i / khid][i % khid] = u[((int64_t)b * Hq + h * G + i / khid) * kMaxH + i % khid];
         if (tid < G) cqs[tid] = cq[(int64_t)b * Hq + h * G + tid];
         __syncthreads();
-        const int64_t qa = (int64_t)pidx * kTokPart;
-        const int64_t qb = min(Nt, qa + kTokPart);
+        const int64_t qa = (int64_t)pidx * tok_per_part;
+        const int64_t qb = min(Nt, qa + tok_per_part);
         for (int64_t q0 = qa; q0 < qb; q0 += kTB) {
             const int nt = (int)min((int64_t)kTB, qb - q0);
             // ---- K side: hidden tile and scores
@@ -353,6 +364,402 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core path (bf16 storage, hidden width 128 or 256).
+//
+// A block owns one KV head (unit) and a range of compressed tokens, walked in
+// tiles of 32.  The 4 waves split the hidden units (wave w: [w*HW, (w+1)*HW))
+// and the head_dim columns of the value sums (wave w: [w*D/4, (w+1)*D/4)).
+// Per tile:
+//   K side  hK^T = W1K z^T + b1K           bf16 MFMA, hidden x tokens
+//           GELU in packed f16
+//           partial scores U hK^T          f16 MFMA, U = W2K^T q (query heads x hidden)
+//   merge   scores of the 4 waves + mean_j q.R^K_j (from the qR table) + q.b2K,
+//           online softmax per query head
+//   V side  hV = z W1V^T + b1V             bf16 MFMA, tokens x hidden
+//           acc_h += P hV                  f16 MFMA
+//           acc_r += P~ R^V_gathered       bf16 MFMA over (token, slot) rows, the
+//                                          referenced V rows staged in LDS
+// Reference tokens are separate partitions (VALU), as in the general path.
+template <int D, int DC, int HID, int KP>
+__global__ __launch_bounds__(256, 2) void main_mfma_kernel(
+    int U, int Hq, int G, int k, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
+    int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
+    const uint16_t *__restrict__ kidx, const bf16_t *__restrict__ vref,
+    const bf16_t *__restrict__ vlat, const uint16_t *__restrict__ vidx,
+    const bf16_t *__restrict__ kw1, const float *__restrict__ kb1,
+    const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
+    const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
+    float *__restrict__ part) {
+    constexpr int TT = 32;              // tokens per tile
+    constexpr int HW = HID / 4;         // hidden units per wave
+    constexpr int MT = HW / 16;         // 16-row hidden tiles per wave
+    constexpr int KJ = HW / 32;         // 32-wide hidden k-steps per wave
+    constexpr int KS = (DC + 31) / 32;  // 32-wide latent k-steps
+    constexpr int DW = D / 4;           // value columns per wave
+    constexpr int NR = DW / 16;
+    constexpr int ROWS = TT * KP;       // gathered (token, slot) rows per tile
+    constexpr int VPAD = D + 8;
+    static_assert(HW % 32 == 0, "hidden width per wave must be a multiple of 32");
+
+    __shared__ float sp[4][kMaxG][TT];
+    __shared__ float p_s[kMaxG][TT];
+    __shared__ uint16_t ids_k[TT][KP];
+    __shared__ uint16_t ids_v[TT][KP];
+    __shared__ float kinv_v[TT];
+    __shared__ float m_run[kMaxG], l_run[kMaxG], alpha_s[kMaxG];
+    __shared__ __attribute__((aligned(16))) bf16_t vrow[ROWS][VPAD];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int unit = blockIdx.x % U;
+    const int pidx = blockIdx.x / U;
+    const int h = unit % (Hq / G);
+    const int bseq = unit / (Hq / G);
+    float *prec = part + (((int64_t)unit * P + pidx) * G) * kPStride;
+
+    if (pidx >= Ptok) {
+        // ---------------- reference tokens (VALU) ----------------
+        __shared__ float sc[kMaxG][64];
+        __shared__ float accr[kMaxG][kMaxD];
+        for (int i = tid; i < G * D; i += 256) accr[i / D][i % D] = 0.f;
+        if (tid < G) {
+            m_run[tid] = -INFINITY;
+            l_run[tid] = 0.f;
+        }
+        __syncthreads();
+        const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
+        const int64_t jb = min(Rt, ja + kRefPart);
+        for (int64_t j0 = ja; j0 < jb; j0 += 64) {
+            const int nj = (int)min((int64_t)64, jb - j0);
+            for (int i = tid; i < G * nj; i += 256) {
+                const int g = i / nj, t = i % nj;
+                sc[g][t] = scale * qr[((int64_t)unit * Rt + j0 + t) * G + g];
+            }
+            __syncthreads();
+            if (tid < G) {
+                const int g = tid;
+                float tmax = -INFINITY;
+                for (int t = 0; t < nj; ++t) tmax = fmaxf(tmax, sc[g][t]);
+                const float mnew = fmaxf(m_run[g], tmax);
+                const float alpha = __expf(m_run[g] - mnew);
+                float lsum = 0.f;
+                for (int t = 0; t < nj; ++t) {
+                    const float pv = __expf(sc[g][t] - mnew);
+                    sc[g][t] = pv;
+                    lsum += pv;
+                }
+                l_run[g] = l_run[g] * alpha + lsum;
+                m_run[g] = mnew;
+                alpha_s[g] = alpha;
+            }
+            __syncthreads();
+            for (int i = tid; i < G * D; i += 256) {
+                const int g = i / D, c = i % D;
+                float acc = accr[g][c] * alpha_s[g];
+                const bf16_t *vr = vref + ((int64_t)unit * Rcap + j0) * D + c;
+                for (int t = 0; t < nj; ++t) acc += sc[g][t] * bf2f(vr[(int64_t)t * D]);
+                accr[g][c] = acc;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < G * kPStride; i += 256) {
+            const int g = i / kPStride, e = i % kPStride;
+            float v = 0.f;
+            if (e == 0) v = m_run[g];
+            else if (e == 1) v = l_run[g];
+            else if (e >= 4 && e < 4 + D) v = accr[g][e - 4];
+            prec[(int64_t)g * kPStride + e] = v;
+        }
+        return;
+    }
+
+    // ---------------- compressed tokens (matrix cores) ----------------
+    const int hbase = w * HW;
+    const int cbase = w * DW;
+    const int64_t ubase_n = (int64_t)unit * Ncap;
+
+    // weights into registers
+    bf16x8 wK[MT][KS], wV[MT][KS];
+    f32x4 bK[MT];
+    float bV[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ch = 32 * ks + 8 * lq;
+            u32x4 zero = {0u, 0u, 0u, 0u};
+            wK[m][ks] = as_bf16x8(ch < DC ? ld16(kw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
+                                          : zero);
+            wV[m][ks] = as_bf16x8(ch < DC ? ld16(vw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
+                                          : zero);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bK[m][r] = kb1 ? kb1[hbase + 16 * m + 4 * lq + r] : 0.f;
+        bV[m] = vb1 ? vb1[hbase + 16 * m + l16] : 0.f;
+    }
+    // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
+    f16x8 uA[KJ];
+    {
+        const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + l16) * kMaxH;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int hid = hbase + 32 * j + (e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4));
+                uA[j][e] = (_Float16)(l16 < G ? ug[hid] : 0.f);
+            }
+        }
+    }
+    f32x4 acc_h[MT], acc_r[NR];
+#pragma unroll
+    for (int n = 0; n < MT; ++n) acc_h[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NR; ++n) acc_r[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid < G) {
+        m_run[tid] = -INFINITY;
+        l_run[tid] = 0.f;
+    }
+    float cq_g = 0.f;
+    {
+        const int g = tid >> 5;
+        if (g < G) cq_g = cq[(int64_t)bseq * Hq + h * G + g];
+    }
+
+    const int64_t qa = (int64_t)pidx * tiles_per_part * TT;
+    const int64_t qe = min(Nt, qa + (int64_t)tiles_per_part * TT);
+    for (int64_t q0 = qa; q0 < qe; q0 += TT) {
+        // ---- latents (operand layout straight from HBM) and index rows
+        bf16x8 zK[2][KS], zV[2][KS];
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const int64_t tk = q0 + 16 * n2 + l16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ch = 32 * ks + 8 * lq;
+                const bool ok = tk < qe && ch < DC;
+                u32x4 zero = {0u, 0u, 0u, 0u};
+                zK[n2][ks] = as_bf16x8(ok ? ld16(klat + (ubase_n + tk) * DC + ch) : zero);
+                zV[n2][ks] = as_bf16x8(ok ? ld16(vlat + (ubase_n + tk) * DC + ch) : zero);
+            }
+        }
+        if (tid < TT * KP) {
+            const int t = tid / KP, i = tid % KP;
+            const bool ok = q0 + t < qe && i < k;
+            ids_k[t][i] = ok ? kidx[(ubase_n + q0 + t) * k + i] : kIdxUnused;
+            ids_v[t][i] = ok ? vidx[(ubase_n + q0 + t) * k + i] : kIdxUnused;
+        }
+        // ---- K side: hidden tile (hidden x tokens), GELU, partial scores
+        f32x4 S[2];
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            f32x4 cK[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                cK[m] = bK[m];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) cK[m] = mfma16_bf16(wK[m][ks], zK[n2][ks], cK[m]);
+            }
+            S[n2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const f16x2 h0 = gelu2_f16(cK[2 * j][0], cK[2 * j][1]);
+                const f16x2 h1 = gelu2_f16(cK[2 * j][2], cK[2 * j][3]);
+                const f16x2 h2 = gelu2_f16(cK[2 * j + 1][0], cK[2 * j + 1][1]);
+                const f16x2 h3 = gelu2_f16(cK[2 * j + 1][2], cK[2 * j + 1][3]);
+                u32x4 hv = {as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)};
+                S[n2] = mfma16_f16(uA[j], as_f16x8(hv), S[n2]);
+            }
+        }
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int g = 4 * lq + r;
+                if (g < G) sp[w][g][16 * n2 + l16] = S[n2][r];
+            }
+        __syncthreads();
+
+        // ---- gather the referenced V rows for this tile (row = token * KP + slot)
+        for (int it = tid; it < ROWS * (D / 8); it += 256) {
+            const int row = it / (D / 8), c8 = it % (D / 8);
+            const int t = row / KP, i = row % KP;
+            const uint16_t j = ids_v[t][i];
+            const int64_t jr = (j == kIdxUnused) ? 0 : (int64_t)j;
+            *reinterpret_cast<u32x4 *>(&vrow[row][8 * c8]) =
+                ld16(vref + ((int64_t)unit * Rcap + jr) * D + 8 * c8);
+        }
+        // ---- merge scores, online softmax (thread = (query head g, token t))
+        {
+            const int g = tid >> 5, t = tid & 31;
+            if (g < G) {
+                float s = -INFINITY;
+                if (q0 + t < qe) {
+                    float rs = 0.f;
+                    int ke = 0;
+#pragma unroll
+                    for (int i = 0; i < KP; ++i) {
+                        const uint16_t j = ids_k[t][i];
+                        if (i < k && j != kIdxUnused) {
+                            rs += qr[((int64_t)unit * Rt + j) * G + g];
+                            ++ke;
+                        }
+                    }
+                    s = scale * (sp[0][g][t] + sp[1][g][t] + sp[2][g][t] + sp[3][g][t] +
+                                 rs / (float)ke + cq_g);
+                }
+                float tmax = s;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
+                const float mold = m_run[g];
+                const float mnew = fmaxf(mold, tmax);
+                const float pv = (q0 + t < qe) ? __expf(s - mnew) : 0.f;
+                float psum = pv;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 32);
+                p_s[g][t] = pv;
+                if (t == 0) {
+                    const float alpha = __expf(mold - mnew);
+                    alpha_s[g] = alpha;
+                    l_run[g] = l_run[g] * alpha + psum;
+                    m_run[g] = mnew;
+                }
+                if (g == 0) {
+                    int ke = 0;
+#pragma unroll
+                    for (int i = 0; i < KP; ++i) ke += (i < k && ids_v[t][i] != kIdxUnused);
+                    kinv_v[t] = ke > 0 ? 1.f / (float)ke : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- V side
+        {
+            float al[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) al[r] = (4 * lq + r < G) ? alpha_s[4 * lq + r] : 0.f;
+#pragma unroll
+            for (int n = 0; n < MT; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc_h[n][r] *= al[r];
+#pragma unroll
+            for (int n = 0; n < NR; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc_r[n][r] *= al[r];
+        }
+        // P (query heads x tokens, tokens permuted to the hV operand layout), f16
+        f16x8 pa;
+        {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4);
+                pa[e] = (_Float16)(l16 < G ? p_s[l16][t] : 0.f);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < MT; ++n) {
+            f32x4 c0 = {bV[n], bV[n], bV[n], bV[n]};
+            f32x4 c1 = c0;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                c0 = mfma16_bf16(zV[0][ks], wV[n][ks], c0);
+                c1 = mfma16_bf16(zV[1][ks], wV[n][ks], c1);
+            }
+            const f16x2 h0 = gelu2_f16(c0[0], c0[1]);
+            const f16x2 h1 = gelu2_f16(c0[2], c0[3]);
+            const f16x2 h2 = gelu2_f16(c1[0], c1[1]);
+            const f16x2 h3 = gelu2_f16(c1[2], c1[3]);
+            u32x4 hv = {as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)};
+            acc_h[n] = mfma16_f16(pa, as_f16x8(hv), acc_h[n]);
+        }
+        // value reference rows: acc_r += P~ R, P~[g][row] = p[g][t] / k_eff(t)
+#pragma unroll
+        for (int ks = 0; ks < ROWS / 32; ++ks) {
+            const int rb = 32 * ks + 8 * lq;
+            float wv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int row = rb + e, t = row / KP, i = row % KP;
+                const bool ok = l16 < G && i < k && ids_v[t][i] != kIdxUnused;
+                wv[e] = ok ? p_s[l16][t] * kinv_v[t] : 0.f;
+            }
+            u32x4 pw = {pack_bf16(wv[0], wv[1]), pack_bf16(wv[2], wv[3]),
+                        pack_bf16(wv[4], wv[5]), pack_bf16(wv[6], wv[7])};
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const int c = cbase + 16 * n + l16;
+                u32x4 bv;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][c] |
+                             ((uint32_t)vrow[rb + 2 * e2 + 1][c] << 16);
+                acc_r[n] = mfma16_bf16(as_bf16x8(pw), as_bf16x8(bv), acc_r[n]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- partial record: m, l, l over compressed tokens, acc_r[d], acc_h[hidden]
+    if (tid < G) {
+        prec[(int64_t)tid * kPStride + 0] = m_run[tid];
+        prec[(int64_t)tid * kPStride + 1] = l_run[tid];
+        prec[(int64_t)tid * kPStride + 2] = l_run[tid];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int g = 4 * lq + r;
+        if (g >= G) continue;
+        float *pg = prec + (int64_t)g * kPStride;
+#pragma unroll
+        for (int n = 0; n < MT; ++n) pg[4 + kMaxD + hbase + 16 * n + l16] = acc_h[n][r];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) pg[4 + cbase + 16 * n + l16] = acc_r[n][r];
+    }
+}
+
+template <int D, int DC, int HID, int KP>
+void launch_mfma_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
+                   const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
+                   const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+    const int U = dm.B * dm.H;
+    const int G = Hq / dm.H;
+    hipLaunchKernelGGL((main_mfma_kernel<D, DC, HID, KP>), dim3((unsigned)(pl.P * U)), dim3(256),
+                       0, st, U, Hq, G, dm.k, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part,
+                       (int)pl.Ptok, (int)pl.P, (const bf16_t *)kc.lat, kc.idx,
+                       (const bf16_t *)vc.refs, (const bf16_t *)vc.lat, vc.idx,
+                       (const bf16_t *)kd.w1, kd.b1, (const bf16_t *)vd.w1, vd.b1, scale, u, cq,
+                       qr, part);
+}
+
+template <int D, int DC>
+bool launch_mfma_dc(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
+                    const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
+                    const float *u, const float *cq, const float *qr, float *part,
+                    hipStream_t st) {
+    const bool kp4 = dm.k <= 4;
+    if (kd.hidden == 256) {
+        if (kp4) launch_mfma_t<D, DC, 256, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        else launch_mfma_t<D, DC, 256, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        return true;
+    }
+    if (kd.hidden == 128) {
+        if (kp4) launch_mfma_t<D, DC, 128, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        else launch_mfma_t<D, DC, 128, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        return true;
+    }
+    return false;
+}
+
+// The matrix-core path covers bf16 storage with GELU decompressors of hidden
+// width 128 or 256 (same width for K and V) and d_c <= 64; everything else
+// takes the general path.
+bool mfma_eligible(const Dims &dm, const MlpArgs &kd, const MlpArgs &vd) {
+    return dm.dtype == 1 && kd.hidden == vd.hidden && (kd.hidden == 128 || kd.hidden == 256) &&
+           kd.act == 0 && vd.act == 0 && dm.dc <= 64;
+}
+
 template <typename T>
 hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            const CacheArgs &kc, const MlpArgs &kd, const CacheArgs &vc,
@@ -370,11 +777,27 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     hipLaunchKernelGGL(refscore_kernel<T>, dim3((unsigned)((pl.Rt + 63) / 64), dm.H, dm.B),
                        dim3(256), 0, st, (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R,
                        pl.Rt, qr);
-    hipLaunchKernelGGL(main_kernel<T>, dim3((unsigned)pl.P, dm.H, dm.B), dim3(256), 0, st, Hq, G,
-                       dm.d, dm.dc, dm.k, dm.s, dm.R, dm.N, pl.Rt, pl.Nt, pl.Ptok,
-                       (const T *)kc.refs, (const T *)kc.lat, kc.idx, (const T *)vc.refs,
-                       (const T *)vc.lat, vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act,
-                       (const T *)vd.w1, vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part);
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+        if (mfma_eligible(dm, kd, vd)) {
+            if (dm.d == 128) {
+                if (dm.dc == 16) done = launch_mfma_dc<128, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                else if (dm.dc == 32) done = launch_mfma_dc<128, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                else done = launch_mfma_dc<128, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+            } else {
+                if (dm.dc == 16) done = launch_mfma_dc<64, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                else if (dm.dc == 32) done = launch_mfma_dc<64, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                else done = launch_mfma_dc<64, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+            }
+        }
+    }
+    if (!done)
+        hipLaunchKernelGGL(main_kernel<T>, dim3((unsigned)pl.P, dm.H, dm.B), dim3(256), 0, st, Hq,
+                           G, dm.d, dm.dc, dm.k, dm.s, dm.R, dm.N, pl.Rt, pl.Nt, pl.Ptok,
+                           (int64_t)pl.tiles_per_part * kTileTok, (const T *)kc.refs,
+                           (const T *)kc.lat, kc.idx, (const T *)vc.refs, (const T *)vc.lat,
+                           vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act, (const T *)vd.w1,
+                           vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part);
     hipLaunchKernelGGL(combine_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, Hq, G, dm.d, dm.H,
                        pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out);
     return hipGetLastError();

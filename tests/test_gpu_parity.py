@@ -75,6 +75,8 @@ def test_bf16_llama_heads_ragged():
     (128, 8, 8, 16, 256, 4, 777, dk.BF16),    # streaming workload's shapes
     (64, 3, 2, 64, 64, 1, 500, dk.BF16),
     (64, 5, 5, 128, 128, 8, 301, dk.BF16),
+    (64, 4, 3, 64, 128, 2, 999, dk.BF16),     # matrix-core decode at head_dim 64
+    (128, 16, 4, 32, 128, 4, 1500, dk.BF16),
     (128, 16, 4, 32, 256, 2, 600, dk.F32),
     (64, 2, 1, 16, 128, 4, 257, dk.F32),
 ])
