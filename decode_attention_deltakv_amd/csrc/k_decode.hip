@@ -39,8 +39,9 @@ constexpr int kMaxDC = 128;
 constexpr int kMaxK = 8;
 constexpr int kTB = 16;        // tokens per tile (general path)
 constexpr int kTileTok = 32;   // tokens per tile (matrix-core path); partitions hold whole tiles
-constexpr int kTargetBlocks = 1024;
-constexpr int kRefPart = 1024; // reference rows per partition
+constexpr int kTargetBlocks = 512;
+constexpr int kRefPart = 512;  // reference rows per partition
+constexpr int kMaxParts = 4096; // partitions per unit (combine keeps their weights in LDS)
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
 
 struct DecWs {
@@ -68,8 +69,12 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     const int64_t tiles = (p.Nt + kTileTok - 1) / kTileTok;
     const int64_t want = std::max<int64_t>(1, (kTargetBlocks + U - 1) / U);
     p.tiles_per_part = (int)std::max<int64_t>(2, (tiles + want - 1) / want);
-    p.Ptok = (tiles + p.tiles_per_part - 1) / p.tiles_per_part;
     p.Pref = (p.Rt + kRefPart - 1) / kRefPart;
+    // keep the partition count within what the merge holds in LDS
+    const int64_t max_tok_parts = kMaxParts - p.Pref;
+    if ((tiles + p.tiles_per_part - 1) / p.tiles_per_part > max_tok_parts)
+        p.tiles_per_part = (int)((tiles + max_tok_parts - 1) / max_tok_parts);
+    p.Ptok = (tiles + p.tiles_per_part - 1) / p.tiles_per_part;
     p.P = p.Ptok + p.Pref;
     size_t off = 0;
     p.off_u = off;
@@ -319,6 +324,17 @@ __global__ __launch_bounds__(256) void main_kernel(
 
 // Log-sum-exp merge of the partitions of one query head; W2V applied to the
 // merged hidden sum.  grid (Hq, B).
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int H, int64_t P,
                                                       const float *__restrict__ part,
@@ -326,44 +342,41 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
                                                       const float *__restrict__ vb2,
                                                       float *__restrict__ out) {
     __shared__ float acch[kMaxH];
-    __shared__ float red[3];
+    __shared__ float wgt[kMaxParts];
+    __shared__ float red[4];
     const int gq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int h = gq / G, g = gq % G;
     const int64_t unit = (int64_t)b * H + h;
     const float *base = part + (unit * P * G + g) * kPStride;
     const int64_t pstep = (int64_t)G * kPStride;
-    if (tid == 0) {
-        float M = -INFINITY;
-        for (int64_t p = 0; p < P; ++p) M = fmaxf(M, base[p * pstep]);
-        float L = 0.f, Lt = 0.f;
-        for (int64_t p = 0; p < P; ++p) {
-            const float w = expf(base[p * pstep] - M);
-            L += w * base[p * pstep + 1];
-            Lt += w * base[p * pstep + 2];
-        }
-        red[0] = M;
-        red[1] = L;
-        red[2] = Lt;
+    float mx = -INFINITY;
+    for (int64_t p = tid; p < P; p += 256) mx = fmaxf(mx, base[p * pstep]);
+    const float M = block_reduce(mx, red, true);
+    float lsum = 0.f, ltsum = 0.f;
+    for (int64_t p = tid; p < P; p += 256) {
+        const float wp = __expf(base[p * pstep] - M);
+        wgt[p] = wp;
+        lsum += wp * base[p * pstep + 1];
+        ltsum += wp * base[p * pstep + 2];
+    }
+    const float L = block_reduce(lsum, red, false);
+    const float Lt = block_reduce(ltsum, red, false);  // (its barriers also publish wgt)
+    for (int o = tid; o < vhid; o += 256) {
+        float a = 0.f;
+        for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + kMaxD + o];
+        acch[o] = a;
     }
     __syncthreads();
-    const float M = red[0], L = red[1], Lt = red[2];
-    if (tid < vhid) {
+    for (int c = tid; c < d; c += 256) {
         float a = 0.f;
-        for (int64_t p = 0; p < P; ++p)
-            a += expf(base[p * pstep] - M) * base[p * pstep + 4 + kMaxD + tid];
-        acch[tid] = a;
-    }
-    __syncthreads();
-    if (tid < d) {
-        float a = 0.f;
-        for (int64_t p = 0; p < P; ++p) a += expf(base[p * pstep] - M) * base[p * pstep + 4 + tid];
-        float w = 0.f;
-        for (int o = 0; o < vhid; ++o) w += to_f32(vw2[(int64_t)tid * vhid + o]) * acch[o];
-        const float bias = vb2 ? vb2[tid] : 0.f;
-        out[((int64_t)b * Hq + gq) * d + tid] = (a + w + Lt * bias) / L;
+        for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + c];
+        float wsum = 0.f;
+        const T *wr = vw2 + (int64_t)c * vhid;
+        for (int o = 0; o < vhid; ++o) wsum += to_f32(wr[o]) * acch[o];
+        const float bias = vb2 ? vb2[c] : 0.f;
+        out[((int64_t)b * Hq + gq) * d + c] = (a + wsum + Lt * bias) / L;
     }
 }
-
 
 // ---------------------------------------------------------------------------
 // Matrix-core path (bf16 storage, hidden width 128 or 256).
@@ -376,14 +389,22 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
 //           GELU in packed f16
 //           partial scores U hK^T          f16 MFMA, U = W2K^T q (query heads x hidden)
 //   merge   scores of the 4 waves + mean_j q.R^K_j (from the qR table) + q.b2K,
-//           online softmax per query head
+//           online softmax per query head (one thread per (head, token))
 //   V side  hV = z W1V^T + b1V             bf16 MFMA, tokens x hidden
 //           acc_h += P hV                  f16 MFMA
-//           acc_r += P~ R^V_gathered       bf16 MFMA over (token, slot) rows, the
-//                                          referenced V rows staged in LDS
-// Reference tokens are separate partitions (VALU), as in the general path.
+//           acc_r += P~ R^V_gathered       bf16 MFMA over (token, slot) rows; the
+//                                          referenced V rows are staged in LDS
+// The next tile's latents and index rows are loaded while the current tile
+// computes, and the V-row gather is issued at the start of the tile so its
+// latency hides behind the K side.  Reference tokens are separate partitions
+// (VALU), as in the general path.
+//
+// LDS layouts: V rows are stored row-major with their 16-byte chunks XOR-
+// swizzled by 2 * ((row / 8) % 4), so that the column reads of the B operand
+// (8 rows, 16 columns per lane group) spread over all banks; the per-head
+// weight rows carry 16 bytes of padding for the same reason.
 template <int D, int DC, int HID, int KP>
-__global__ __launch_bounds__(256, 2) void main_mfma_kernel(
+__global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
     int U, int Hq, int G, int k, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
     const uint16_t *__restrict__ kidx, const bf16_t *__restrict__ vref,
@@ -400,85 +421,34 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     constexpr int DW = D / 4;           // value columns per wave
     constexpr int NR = DW / 16;
     constexpr int ROWS = TT * KP;       // gathered (token, slot) rows per tile
-    constexpr int VPAD = D + 8;
+    constexpr int CH = D / 8;           // 16-byte chunks per V row
+    constexpr int GIT = ROWS * CH / 256;  // gather chunks per thread
+    constexpr int WPAD = ROWS + 8;
     static_assert(HW % 32 == 0, "hidden width per wave must be a multiple of 32");
+    static_assert((ROWS * CH) % 256 == 0, "gather must split evenly");
 
     __shared__ float sp[4][kMaxG][TT];
-    __shared__ float p_s[kMaxG][TT];
-    __shared__ uint16_t ids_k[TT][KP];
-    __shared__ uint16_t ids_v[TT][KP];
-    __shared__ float kinv_v[TT];
-    __shared__ float m_run[kMaxG], l_run[kMaxG], alpha_s[kMaxG];
-    __shared__ __attribute__((aligned(16))) bf16_t vrow[ROWS][VPAD];
+    __shared__ float alpha_s[kMaxG];
+    __shared__ __attribute__((aligned(16))) _Float16 pperm[16][TT + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t wrow[16][WPAD];
+    __shared__ __attribute__((aligned(16))) bf16_t vrow[ROWS][D];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const int unit = blockIdx.x % U;
     const int pidx = blockIdx.x / U;
-    const int h = unit % (Hq / G);
-    const int bseq = unit / (Hq / G);
+    const int H = Hq / G;
+    const int h = unit % H;
+    const int bseq = unit / H;
     float *prec = part + (((int64_t)unit * P + pidx) * G) * kPStride;
-
-    if (pidx >= Ptok) {
-        // ---------------- reference tokens (VALU) ----------------
-        __shared__ float sc[kMaxG][64];
-        __shared__ float accr[kMaxG][kMaxD];
-        for (int i = tid; i < G * D; i += 256) accr[i / D][i % D] = 0.f;
-        if (tid < G) {
-            m_run[tid] = -INFINITY;
-            l_run[tid] = 0.f;
-        }
-        __syncthreads();
-        const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
-        const int64_t jb = min(Rt, ja + kRefPart);
-        for (int64_t j0 = ja; j0 < jb; j0 += 64) {
-            const int nj = (int)min((int64_t)64, jb - j0);
-            for (int i = tid; i < G * nj; i += 256) {
-                const int g = i / nj, t = i % nj;
-                sc[g][t] = scale * qr[((int64_t)unit * Rt + j0 + t) * G + g];
-            }
-            __syncthreads();
-            if (tid < G) {
-                const int g = tid;
-                float tmax = -INFINITY;
-                for (int t = 0; t < nj; ++t) tmax = fmaxf(tmax, sc[g][t]);
-                const float mnew = fmaxf(m_run[g], tmax);
-                const float alpha = __expf(m_run[g] - mnew);
-                float lsum = 0.f;
-                for (int t = 0; t < nj; ++t) {
-                    const float pv = __expf(sc[g][t] - mnew);
-                    sc[g][t] = pv;
-                    lsum += pv;
-                }
-                l_run[g] = l_run[g] * alpha + lsum;
-                m_run[g] = mnew;
-                alpha_s[g] = alpha;
-            }
-            __syncthreads();
-            for (int i = tid; i < G * D; i += 256) {
-                const int g = i / D, c = i % D;
-                float acc = accr[g][c] * alpha_s[g];
-                const bf16_t *vr = vref + ((int64_t)unit * Rcap + j0) * D + c;
-                for (int t = 0; t < nj; ++t) acc += sc[g][t] * bf2f(vr[(int64_t)t * D]);
-                accr[g][c] = acc;
-            }
-            __syncthreads();
-        }
-        for (int i = tid; i < G * kPStride; i += 256) {
-            const int g = i / kPStride, e = i % kPStride;
-            float v = 0.f;
-            if (e == 0) v = m_run[g];
-            else if (e == 1) v = l_run[g];
-            else if (e >= 4 && e < 4 + D) v = accr[g][e - 4];
-            prec[(int64_t)g * kPStride + e] = v;
-        }
-        return;
-    }
 
     // ---------------- compressed tokens (matrix cores) ----------------
     const int hbase = w * HW;
     const int cbase = w * DW;
     const int64_t ubase_n = (int64_t)unit * Ncap;
+    const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
+    const float *qr_u = qr + (int64_t)unit * Rt * G;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     // weights into registers
     bf16x8 wK[MT][KS], wV[MT][KS];
@@ -489,11 +459,10 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int ch = 32 * ks + 8 * lq;
-            u32x4 zero = {0u, 0u, 0u, 0u};
             wK[m][ks] = as_bf16x8(ch < DC ? ld16(kw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
-                                          : zero);
+                                          : zero4);
             wV[m][ks] = as_bf16x8(ch < DC ? ld16(vw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
-                                          : zero);
+                                          : zero4);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) bK[m][r] = kb1 ? kb1[hbase + 16 * m + 4 * lq + r] : 0.f;
@@ -502,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
     f16x8 uA[KJ];
     {
-        const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + l16) * kMaxH;
+        const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + (l16 < G ? l16 : 0)) * kMaxH;
 #pragma unroll
         for (int j = 0; j < KJ; ++j) {
 #pragma unroll
@@ -517,39 +486,170 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     for (int n = 0; n < MT; ++n) acc_h[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < NR; ++n) acc_r[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tid < G) {
-        m_run[tid] = -INFINITY;
-        l_run[tid] = 0.f;
-    }
-    float cq_g = 0.f;
-    {
-        const int g = tid >> 5;
-        if (g < G) cq_g = cq[(int64_t)bseq * Hq + h * G + g];
+    // rows of the weight tables that belong to no query head stay zero
+    for (int i = tid; i < 16 * (TT + 8); i += 256) pperm[i / (TT + 8)][i % (TT + 8)] = (_Float16)0.f;
+    for (int i = tid; i < 16 * WPAD; i += 256) wrow[i / WPAD][i % WPAD] = 0;
+
+    // softmax role: (query head sg, token st)
+    const int sg = tid >> 5, st = tid & 31;
+    const bool sg_ok = sg < G;
+    const float cq_g = sg_ok ? cq[(int64_t)bseq * Hq + h * G + sg] : 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    // inverse of the token permutation of the P operand
+    const int st_slot = st < 16 ? 8 * (st >> 2) + (st & 3) : 8 * ((st - 16) >> 2) + 4 + (st & 3);
+
+    if (pidx >= Ptok) {
+        // ---------------- reference tokens ----------------
+        // A reference token is attended with its stored rows: score
+        // scale * qR[j], value R^V_j.  Tiles of 32 consecutive references:
+        // the rows go straight to LDS and enter the same value MFMA with one
+        // slot per token and weight p.
+        const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
+        const int64_t je = min(Rt, ja + kRefPart);
+        for (int64_t j0 = ja; j0 < je; j0 += TT) {
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < (TT * CH) / 256; ++m) {
+                const int it = tid + 256 * m;
+                const int row = it / CH, c8 = it % CH;
+                const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+                const int64_t j = min(j0 + row, Rt - 1);
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(vref_u + j * D + 8 * sc8),
+                    (__attribute__((address_space(3))) void *)&vrow[(256 * m + 64 * w) / CH][0],
+                    16, 0, 0);
+            }
+            if (sg_ok) {
+                const bool ok = j0 + st < je;
+                const float s = ok ? scale * qr_u[(j0 + st) * G + sg] : -INFINITY;
+                float tmax = s;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
+                const float mnew = fmaxf(m_run, tmax);
+                const float alpha = __expf(m_run - mnew);
+                const float pv = ok ? __expf(s - mnew) : 0.f;
+                float psum = pv;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 32);
+                l_run = l_run * alpha + psum;
+                m_run = mnew;
+                if (st == 0) alpha_s[sg] = alpha;
+                wrow[sg][st] = f2bf(pv);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            float al[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) al[r] = (4 * lq + r < G) ? alpha_s[4 * lq + r] : 0.f;
+#pragma unroll
+            for (int n = 0; n < NR; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc_r[n][r] *= al[r];
+            const int rb = 8 * lq;
+            const bf16x8 pw = as_bf16x8(*reinterpret_cast<const u32x4 *>(&wrow[l16][rb]));
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const int c = cbase + 16 * n + l16;
+                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                u32x4 bv;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][pcol] |
+                             ((uint32_t)vrow[rb + 2 * e2 + 1][pcol] << 16);
+                acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
+            }
+        }
+        if (sg_ok && st == 0) {
+            prec[(int64_t)sg * kPStride + 0] = m_run;
+            prec[(int64_t)sg * kPStride + 1] = l_run;
+            prec[(int64_t)sg * kPStride + 2] = 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            if (g >= G) continue;
+            float *pg = prec + (int64_t)g * kPStride;
+#pragma unroll
+            for (int n = 0; n < MT; ++n) pg[4 + kMaxD + hbase + 16 * n + l16] = 0.f;
+#pragma unroll
+            for (int n = 0; n < NR; ++n) pg[4 + cbase + 16 * n + l16] = acc_r[n][r];
+        }
+        return;
     }
 
     const int64_t qa = (int64_t)pidx * tiles_per_part * TT;
     const int64_t qe = min(Nt, qa + (int64_t)tiles_per_part * TT);
-    for (int64_t q0 = qa; q0 < qe; q0 += TT) {
-        // ---- latents (operand layout straight from HBM) and index rows
-        bf16x8 zK[2][KS], zV[2][KS];
+
+    // ---- prefetched inputs of the next tile
+    bf16x8 zKn[2][KS], zVn[2][KS];
+    uint16_t idkn[KP], idvn[KP], gidn[GIT];
+    auto load_tile = [&](int64_t t0) {
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2) {
-            const int64_t tk = q0 + 16 * n2 + l16;
+            const int64_t tk = t0 + 16 * n2 + l16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = 32 * ks + 8 * lq;
                 const bool ok = tk < qe && ch < DC;
-                u32x4 zero = {0u, 0u, 0u, 0u};
-                zK[n2][ks] = as_bf16x8(ok ? ld16(klat + (ubase_n + tk) * DC + ch) : zero);
-                zV[n2][ks] = as_bf16x8(ok ? ld16(vlat + (ubase_n + tk) * DC + ch) : zero);
+                zKn[n2][ks] = as_bf16x8(ok ? ld16(klat + (ubase_n + tk) * DC + ch) : zero4);
+                zVn[n2][ks] = as_bf16x8(ok ? ld16(vlat + (ubase_n + tk) * DC + ch) : zero4);
             }
         }
-        if (tid < TT * KP) {
-            const int t = tid / KP, i = tid % KP;
-            const bool ok = q0 + t < qe && i < k;
-            ids_k[t][i] = ok ? kidx[(ubase_n + q0 + t) * k + i] : kIdxUnused;
-            ids_v[t][i] = ok ? vidx[(ubase_n + q0 + t) * k + i] : kIdxUnused;
+        const bool tok_ok = t0 + st < qe;
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            const bool ok = tok_ok && i < k;
+            idkn[i] = ok ? kidx[(ubase_n + t0 + st) * k + i] : kIdxUnused;
+            idvn[i] = ok ? vidx[(ubase_n + t0 + st) * k + i] : kIdxUnused;
         }
+#pragma unroll
+        for (int m = 0; m < GIT; ++m) {
+            const int row = (tid + 256 * m) / CH;
+            const int t = row / KP, i = row % KP;
+            const bool ok = t0 + t < qe && i < k;
+            gidn[m] = ok ? vidx[(ubase_n + t0 + t) * k + i] : kIdxUnused;
+        }
+    };
+    if (qa < qe) load_tile(qa);
+
+    for (int64_t q0 = qa; q0 < qe; q0 += TT) {
+        bf16x8 zK[2][KS], zV[2][KS];
+        uint16_t idk[KP], idv[KP], gid[GIT];
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                zK[n2][ks] = zKn[n2][ks];
+                zV[n2][ks] = zVn[n2][ks];
+            }
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            idk[i] = idkn[i];
+            idv[i] = idvn[i];
+        }
+#pragma unroll
+        for (int m = 0; m < GIT; ++m) gid[m] = gidn[m];
+
+        __syncthreads();  // the previous tile's V side is done with the shared tables
+        // ---- referenced V rows straight into LDS (global -> LDS, 16 bytes per
+        // lane, lanes of a wave fill consecutive 16-byte slots); the XOR swizzle
+        // is applied on the source side.  Their latency hides behind the K side.
+#pragma unroll
+        for (int m = 0; m < GIT; ++m) {
+            const int it = tid + 256 * m;
+            const int row = it / CH, c8 = it % CH;
+            const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+            const int64_t j = gid[m] == kIdxUnused ? 0 : (int64_t)gid[m];
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(vref_u + j * D + 8 * sc8),
+                (__attribute__((address_space(3))) void *)&vrow[(256 * m + 64 * w) / CH][0], 16,
+                0, 0);
+        }
+        float qrv[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+            qrv[i] = (sg_ok && idk[i] != kIdxUnused) ? qr_u[(int64_t)idk[i] * G + sg] : 0.f;
+
         // ---- K side: hidden tile (hidden x tokens), GELU, partial scores
         f32x4 S[2];
 #pragma unroll
@@ -579,61 +679,47 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 const int g = 4 * lq + r;
                 if (g < G) sp[w][g][16 * n2 + l16] = S[n2][r];
             }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS fills landed
         __syncthreads();
 
-        // ---- gather the referenced V rows for this tile (row = token * KP + slot)
-        for (int it = tid; it < ROWS * (D / 8); it += 256) {
-            const int row = it / (D / 8), c8 = it % (D / 8);
-            const int t = row / KP, i = row % KP;
-            const uint16_t j = ids_v[t][i];
-            const int64_t jr = (j == kIdxUnused) ? 0 : (int64_t)j;
-            *reinterpret_cast<u32x4 *>(&vrow[row][8 * c8]) =
-                ld16(vref + ((int64_t)unit * Rcap + jr) * D + 8 * c8);
-        }
-        // ---- merge scores, online softmax (thread = (query head g, token t))
-        {
-            const int g = tid >> 5, t = tid & 31;
-            if (g < G) {
-                float s = -INFINITY;
-                if (q0 + t < qe) {
-                    float rs = 0.f;
-                    int ke = 0;
+        // ---- merge scores, online softmax (thread = (query head sg, token st))
+        if (sg_ok) {
+            const bool tok_ok = q0 + st < qe;
+            float s = -INFINITY;
+            if (tok_ok) {
+                float rs = 0.f;
+                int ke = 0;
 #pragma unroll
-                    for (int i = 0; i < KP; ++i) {
-                        const uint16_t j = ids_k[t][i];
-                        if (i < k && j != kIdxUnused) {
-                            rs += qr[((int64_t)unit * Rt + j) * G + g];
-                            ++ke;
-                        }
-                    }
-                    s = scale * (sp[0][g][t] + sp[1][g][t] + sp[2][g][t] + sp[3][g][t] +
-                                 rs / (float)ke + cq_g);
+                for (int i = 0; i < KP; ++i) {
+                    rs += qrv[i];
+                    ke += idk[i] != kIdxUnused;
                 }
-                float tmax = s;
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
-                const float mold = m_run[g];
-                const float mnew = fmaxf(mold, tmax);
-                const float pv = (q0 + t < qe) ? __expf(s - mnew) : 0.f;
-                float psum = pv;
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 32);
-                p_s[g][t] = pv;
-                if (t == 0) {
-                    const float alpha = __expf(mold - mnew);
-                    alpha_s[g] = alpha;
-                    l_run[g] = l_run[g] * alpha + psum;
-                    m_run[g] = mnew;
-                }
-                if (g == 0) {
-                    int ke = 0;
-#pragma unroll
-                    for (int i = 0; i < KP; ++i) ke += (i < k && ids_v[t][i] != kIdxUnused);
-                    kinv_v[t] = ke > 0 ? 1.f / (float)ke : 0.f;
-                }
+                s = scale * (sp[0][sg][st] + sp[1][sg][st] + sp[2][sg][st] + sp[3][sg][st] +
+                             rs / (float)ke + cq_g);
             }
+            float tmax = s;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
+            const float mnew = fmaxf(m_run, tmax);
+            const float alpha = __expf(m_run - mnew);
+            const float pv = tok_ok ? __expf(s - mnew) : 0.f;
+            float psum = pv;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 32);
+            l_run = l_run * alpha + psum;
+            m_run = mnew;
+            if (st == 0) alpha_s[sg] = alpha;
+            pperm[sg][st_slot] = (_Float16)pv;
+            int ke = 0;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) ke += idv[i] != kIdxUnused;
+            const float wv = ke > 0 ? pv / (float)ke : 0.f;
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+                wrow[sg][st * KP + i] = idv[i] != kIdxUnused ? f2bf(wv) : (bf16_t)0;
         }
         __syncthreads();
+        if (q0 + TT < qe) load_tile(q0 + TT);
 
         // ---- V side
         {
@@ -649,15 +735,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc_r[n][r] *= al[r];
         }
-        // P (query heads x tokens, tokens permuted to the hV operand layout), f16
-        f16x8 pa;
-        {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4);
-                pa[e] = (_Float16)(l16 < G ? p_s[l16][t] : 0.f);
-            }
-        }
+        const f16x8 pa = as_f16x8(*reinterpret_cast<const u32x4 *>(&pperm[l16][8 * lq]));
 #pragma unroll
         for (int n = 0; n < MT; ++n) {
             f32x4 c0 = {bV[n], bV[n], bV[n], bV[n]};
@@ -678,34 +756,26 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < ROWS / 32; ++ks) {
             const int rb = 32 * ks + 8 * lq;
-            float wv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = rb + e, t = row / KP, i = row % KP;
-                const bool ok = l16 < G && i < k && ids_v[t][i] != kIdxUnused;
-                wv[e] = ok ? p_s[l16][t] * kinv_v[t] : 0.f;
-            }
-            u32x4 pw = {pack_bf16(wv[0], wv[1]), pack_bf16(wv[2], wv[3]),
-                        pack_bf16(wv[4], wv[5]), pack_bf16(wv[6], wv[7])};
+            const bf16x8 pw = as_bf16x8(*reinterpret_cast<const u32x4 *>(&wrow[l16][rb]));
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + l16;
+                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
                 u32x4 bv;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2)
-                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][c] |
-                             ((uint32_t)vrow[rb + 2 * e2 + 1][c] << 16);
-                acc_r[n] = mfma16_bf16(as_bf16x8(pw), as_bf16x8(bv), acc_r[n]);
+                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][pcol] |
+                             ((uint32_t)vrow[rb + 2 * e2 + 1][pcol] << 16);
+                acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
             }
         }
-        __syncthreads();
     }
 
     // ---- partial record: m, l, l over compressed tokens, acc_r[d], acc_h[hidden]
-    if (tid < G) {
-        prec[(int64_t)tid * kPStride + 0] = m_run[tid];
-        prec[(int64_t)tid * kPStride + 1] = l_run[tid];
-        prec[(int64_t)tid * kPStride + 2] = l_run[tid];
+    if (sg_ok && st == 0) {
+        prec[(int64_t)sg * kPStride + 0] = m_run;
+        prec[(int64_t)sg * kPStride + 1] = l_run;
+        prec[(int64_t)sg * kPStride + 2] = l_run;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
