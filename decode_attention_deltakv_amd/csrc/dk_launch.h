@@ -58,3 +58,10 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
                                const uint64_t *list, const uint32_t *list_count,
                                int64_t list_cap, hipStream_t st);
 }  // namespace dk
+
+namespace dk {
+// matrix-core top-k with certificate and exact fallback (k_select.hip, bf16)
+hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                              int64_t nq, const CacheArgs &c, uint64_t *flist, uint32_t *fcount,
+                              uint32_t *stats, hipStream_t st);
+}  // namespace dk

@@ -70,23 +70,30 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
 
 }  // namespace
 
+// Workspace of one compress call (bf16 path): a 256-byte header holding the
+// fallback counter, then one 8-byte fallback-list entry per compressed token
+// of the range and unit.
 size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
-    (void)dm;
-    (void)t0;
-    (void)t1;
-    return 0;
+    if (dm.dtype != 1) return 0;
+    const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
+    return 256 + (size_t)nq * dm.B * dm.H * sizeof(uint64_t);
 }
 
 hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                            const MlpArgs &comp, const CacheArgs &c, void *ws, size_t ws_bytes,
                            uint32_t *stats, hipStream_t st) {
-    (void)ws;
     (void)ws_bytes;
-    (void)stats;
     const int64_t q0 = toks_upto(t0, dm.s);
     const int64_t nq = toks_upto(t1, dm.s) - q0;
     if (nq <= 0) return hipSuccess;
-    hipError_t e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, st);
+    hipError_t e;
+    if (dm.dtype == 1) {
+        uint32_t *fcount = (uint32_t *)ws;
+        uint64_t *flist = (uint64_t *)((char *)ws + 256);
+        e = launch_select_mfma(dm, x, t0, t1, q0, nq, c, flist, fcount, stats, st);
+    } else {
+        e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, st);
+    }
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)((nq + kTB - 1) / kTB), (unsigned)(dm.B * dm.H));
     if (dm.dtype == 0)

@@ -13,8 +13,11 @@
 // approximate (MFMA) ranking could not be certified.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "dk_common.h"
 #include "dk_launch.h"
+#include "dk_mfma.h"
 
 namespace dk {
 namespace {
@@ -76,17 +79,17 @@ __global__ __launch_bounds__(256) void select_exact_kernel(
     const int wv = threadIdx.x >> 6;
     double *xs = xs_all[wv];
 
+    const int64_t nwork = list ? (int64_t)*list_count : nq;
+    const int64_t wstep = list ? (int64_t)gridDim.x * 4 : (int64_t)1 << 62;
+    for (int64_t wi = (int64_t)blockIdx.x * 4 + wv; wi < nwork; wi += wstep) {
     int64_t unit, qrel;
     if (list) {
-        const int64_t w = (int64_t)blockIdx.x * 4 + wv;
-        if (w >= (int64_t)*list_count) return;
-        const uint64_t e = list[w];
+        const uint64_t e = list[wi];
         unit = (int64_t)(e >> 32);
         qrel = (int64_t)(e & 0xffffffffu);
     } else {
         unit = blockIdx.y;
-        qrel = (int64_t)blockIdx.x * 4 + wv;
-        if (qrel >= nq) return;
+        qrel = wi;
     }
     const int64_t q = q0 + qrel;
     const int64_t p = tok_pos(q, s);
@@ -145,6 +148,10 @@ __global__ __launch_bounds__(256) void select_exact_kernel(
         }
         if (lane == 0) out[r] = (mj == INT_MAX) ? kIdxUnused : (uint16_t)mj;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
 
 template <typename T, int D>
@@ -153,13 +160,343 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                           const uint32_t *list_count, int64_t list_cap, hipStream_t st) {
     dim3 grid;
     if (list)
-        grid = dim3((unsigned)((list_cap + 3) / 4), 1);
+        grid = dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((list_cap + 3) / 4, 2048)), 1);
     else
         grid = dim3((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
     hipLaunchKernelGGL((select_exact_kernel<T, D>), grid, dim3(256), 0, st, (const T *)x, t0,
                        t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0, nq, dm.k, c.idx, list,
                        list_count);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core top-k (bf16 storage).
+//
+// Scores e~ = x . r - |r|^2 / 2 (larger is nearer; D = |x|^2 - 2 e) come from
+// 32x32x16 bf16 MFMA with the accumulator seeded with -|r|^2 / 2: references
+// are the M dimension, tokens the N dimension, so each lane holds 16 scores of
+// one token per 32-reference block.  A block takes 256 consecutive compressed
+// tokens (4 waves x 2 N-tiles of 32) and streams the references they can see
+// (j * s < p) through LDS in stages of 64, double-buffered, loaded straight
+// from global memory with 16-byte chunks XOR-swizzled by (row % 8).
+//
+// Per lane, a descending list of the LK best scores is kept as packed floats:
+// the low `ibits` mantissa bits of each score are replaced by its reference
+// ordinal (ordered so that, among equal truncated scores, the lower ordinal
+// ranks higher), which lets one insertion be LK v_med3 operations.  The two
+// lanes that share a token merge their lists, then the LK candidates are
+// rescored exactly (fp64, coordinate order, no fused multiply-add) and sorted
+// by (distance, ordinal).  The result is written only when a certificate
+// holds: every reference outside the list has an approximate score at most
+// the list's last entry (plus its truncation), hence a true distance of at
+// least |x|^2 - 2 (tau + delta), where delta bounds the fp32 accumulation
+// error of the MFMA score (and of the fp32 norm); this lower bound must exceed
+// the k-th exact distance.  Tokens that fail go to a list for the exact scan.
+
+__device__ __forceinline__ float pack_score(float sc, int j, uint32_t imask) {
+    const uint32_t u = __float_as_uint(sc);
+    const uint32_t code = (u >> 31) ? (uint32_t)j : (imask - (uint32_t)j);
+    return __uint_as_float((u & ~imask) | code);
+}
+__device__ __forceinline__ int unpack_ordinal(float v, uint32_t imask) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t code = u & imask;
+    return (u >> 31) ? (int)code : (int)(imask - code);
+}
+
+template <int LK>
+__device__ __forceinline__ void list_insert(float (&a)[LK], float v) {
+#pragma unroll
+    for (int i = LK - 1; i > 0; --i) a[i] = __builtin_amdgcn_fmed3f(a[i - 1], a[i], v);
+    a[0] = fmaxf(a[0], v);
+}
+
+template <int D, int LK>
+__device__ void rescore_and_emit(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
+                                 const float (&lst)[LK], uint32_t imask, int ibits, int k,
+                                 float rmax2, bool write, uint16_t *__restrict__ out,
+                                 uint64_t fentry, uint64_t *__restrict__ flist,
+                                 uint32_t *__restrict__ fcount) {
+#pragma clang fp contract(off)
+    constexpr int HALF = LK / 2;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    int cj[HALF];
+    bool cv[HALF];
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+        // bitwise lane select (a conditional on the index would make the list
+        // memory-indexed)
+        const uint32_t hm = 0u - (uint32_t)h;
+        const float v = __uint_as_float((__float_as_uint(lst[e]) & ~hm) |
+                                        (__float_as_uint(lst[HALF + e]) & hm));
+        cv[e] = v != -INFINITY;
+        cj[e] = cv[e] ? unpack_ordinal(v, imask) : 0;
+    }
+    double dacc[HALF];
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) dacc[e] = 0.0;
+    double xsq = 0.0;
+    for (int c = 0; c < D / 8; ++c) {
+        const u32x4 xv = ld16(xrow + 8 * c);
+        double xd[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xd[2 * i] = (double)__uint_as_float(xv[i] << 16);
+            xd[2 * i + 1] = (double)__uint_as_float(xv[i] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double sq = xd[i] * xd[i];
+            xsq = xsq + sq;
+        }
+#pragma unroll
+        for (int e = 0; e < HALF; ++e) {
+            const u32x4 rv = ld16(urefs + (int64_t)cj[e] * D + 8 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double r0 = (double)__uint_as_float(rv[i] << 16);
+                const double r1 = (double)__uint_as_float(rv[i] & 0xffff0000u);
+                const double d0 = xd[2 * i] - r0;
+                const double s0 = d0 * d0;
+                dacc[e] = dacc[e] + s0;
+                const double d1 = xd[2 * i + 1] - r1;
+                const double s1 = d1 * d1;
+                dacc[e] = dacc[e] + s1;
+            }
+        }
+    }
+    // both lanes of the pair assemble the full candidate set
+    double dd[LK];
+    int jj[LK];
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) {
+        const double mine = cv[e] ? dacc[e] : __builtin_inf();
+        const double other = __shfl_xor(mine, 32, 64);
+        const int ojj = __shfl_xor(cj[e], 32, 64);
+        const int mj = cv[e] ? cj[e] : INT_MAX;
+        const int oj = other == __builtin_inf() ? INT_MAX : ojj;
+        dd[e] = h ? other : mine;
+        jj[e] = h ? oj : mj;
+        dd[HALF + e] = h ? mine : other;
+        jj[HALF + e] = h ? mj : oj;
+    }
+    if (!write || h != 0) return;
+    // sort by (distance, ordinal): odd-even transposition network
+#pragma unroll
+    for (int pass = 0; pass < LK; ++pass) {
+#pragma unroll
+        for (int i = pass & 1; i + 1 < LK; i += 2) {
+            const bool sw = dd[i + 1] < dd[i] || (dd[i + 1] == dd[i] && jj[i + 1] < jj[i]);
+            const double td = dd[i];
+            const int tj = jj[i];
+            dd[i] = sw ? dd[i + 1] : dd[i];
+            jj[i] = sw ? jj[i + 1] : jj[i];
+            dd[i + 1] = sw ? td : dd[i + 1];
+            jj[i + 1] = sw ? tj : jj[i + 1];
+        }
+    }
+    const bool full = lst[LK - 1] != -INFINITY;
+    int nvalid = 0;
+#pragma unroll
+    for (int e = 0; e < LK; ++e) nvalid += jj[e] != INT_MAX;
+    const int kk = min(k, nvalid);
+    bool ok = true;
+    if (full) {
+        // certificate: excluded references have D >= xsq - 2 (tau + delta)
+        const double tp = (double)lst[LK - 1];
+        const double tau = tp + fabs(tp) * ldexp(1.0, ibits - 21);
+        const double rm = sqrt((double)rmax2 * (1.0 + 1e-6));
+        const double xn = sqrt(xsq);
+        const double nu = (double)(D + 1) * ldexp(1.0, -23);
+        const double gam = nu / (1.0 - nu);
+        const double delta = 2.0 * gam * (xn * rm + rm * rm) + 1e-30;
+        const double lb = xsq - 2.0 * (tau + delta);
+        const double slack = 1e-9 * (xsq + fabs(tau) + delta);
+        double dk_ = dd[0];
+#pragma unroll
+        for (int e = 1; e < LK; ++e) dk_ = (e == kk - 1) ? dd[e] : dk_;
+        ok = (lb - slack) > dk_;
+    }
+    if (ok) {
+#pragma unroll
+        for (int r = 0; r < LK; ++r)
+            if (r < k) out[r] = r < kk ? (uint16_t)jj[r] : kIdxUnused;
+    } else {
+        const uint32_t slot = atomicAdd(fcount, 1u);
+        flist[slot] = fentry;
+    }
+}
+
+template <int D, int LK>
+__global__ __launch_bounds__(256, 2) void dist_topk_kernel(
+    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
+    const bf16_t *__restrict__ refs, const float *__restrict__ sqn, int64_t Rcap, int64_t Ncap,
+    int64_t q0, int64_t nq, int U, int ntiles, uint32_t imask, int ibits,
+    uint16_t *__restrict__ idx, uint64_t *__restrict__ flist, uint32_t *__restrict__ fcount) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int CH = D / 8;
+    constexpr int RB = 64;
+    constexpr int DMA_IT = RB * CH / 256;
+    __shared__ __attribute__((aligned(16))) bf16_t rt[2][RB][D];
+    __shared__ __attribute__((aligned(16))) float nsq[2][RB];
+    __shared__ float red[4];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int unit = blockIdx.x % U;
+    const int tile = ntiles - 1 - (int)(blockIdx.x / U);  // heaviest tiles first
+    const int64_t qb = q0 + (int64_t)tile * 256;
+    const int64_t qend = q0 + nq;
+    const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
+    const float *usqn = sqn + (int64_t)unit * Rcap;
+
+    const int64_t qlast = min(qb + 255, qend - 1);
+    const int64_t ncand_max = (tok_pos(qlast, s) + s - 1) / s;
+
+    int64_t qn[2], pos[2];
+    int64_t ncand[2], ncand_lo[2];
+    bool valid[2];
+    bf16x8 xb[2][KSTEPS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int64_t qq = qb + 64 * w + 32 * nt + l32;
+        valid[nt] = qq < qend;
+        qn[nt] = min(qq, qend - 1);
+        pos[nt] = tok_pos(qn[nt], s);
+        ncand[nt] = (pos[nt] + s - 1) / s;
+        const int64_t qf = min(qb + 64 * w + 32 * nt, qend - 1);
+        ncand_lo[nt] = (tok_pos(qf, s) + s - 1) / s;
+        const bf16_t *xr = x + ((int64_t)unit * nrows + (pos[nt] - t0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) xb[nt][ks] = as_bf16x8(ld16(xr + 16 * ks + 8 * hl));
+    }
+    float lst[2][LK];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < LK; ++e) lst[nt][e] = -INFINITY;
+
+    float rmax2 = 0.f;
+    auto stage_load = [&](int64_t jbase, int b) {
+#pragma unroll
+        for (int m = 0; m < DMA_IT; ++m) {
+            const int it = tid + 256 * m;
+            const int row = it / CH, c8 = it % CH;
+            const int sc8 = c8 ^ (row & 7);
+            const int64_t j = min(jbase + row, ncand_max - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(urefs + j * D + 8 * sc8),
+                (__attribute__((address_space(3))) void *)&rt[b][(256 * m + 64 * w) / CH][0], 16,
+                0, 0);
+        }
+    };
+    float sq_next = 0.f;
+    const int nstage = (int)((ncand_max + RB - 1) / RB);
+    stage_load(0, 0);
+    if (tid < RB) {
+        const float v = tid < ncand_max ? usqn[tid] : 0.f;
+        rmax2 = fmaxf(rmax2, v);
+        nsq[0][tid] = -0.5f * v;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int st = 0; st < nstage; ++st) {
+        const int b = st & 1;
+        const int64_t jst = (int64_t)st * RB;
+        const bool more = st + 1 < nstage;
+        if (more) {
+            stage_load(jst + RB, b ^ 1);
+            if (tid < RB) sq_next = (jst + RB + tid < ncand_max) ? usqn[jst + RB + tid] : 0.f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int64_t j0 = jst + 32 * mb;
+            if (j0 >= ncand_max) break;
+            f32x16 init;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&nsq[b][32 * mb + 8 * g4 + 4 * hl]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) init[4 * g4 + i] = v[i];
+            }
+            f32x16 acc0 = init, acc1 = init;
+            const int r = 32 * mb + l32;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const int pc = (2 * ks + hl) ^ (r & 7);
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&rt[b][r][8 * pc]));
+                acc0 = mfma32_bf16(a, xb[0][ks], acc0);
+                acc1 = mfma32_bf16(a, xb[1][ks], acc1);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16 sc = nt == 0 ? acc0 : acc1;
+                if (j0 + 32 > ncand_lo[nt]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int64_t j = j0 + 8 * (i / 4) + 4 * hl + (i % 4);
+                        sc[i] = j < ncand[nt] ? sc[i] : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const bool pass = sc[i] > lst[nt][LK - 1];
+                    if (__builtin_amdgcn_ballot_w64(pass)) {
+                        const int j = (int)j0 + 8 * (i / 4) + 4 * hl + (i % 4);
+                        list_insert<LK>(lst[nt], pass ? pack_score(sc[i], j, imask) : -INFINITY);
+                    }
+                }
+            }
+        }
+        if (more && tid < RB) {
+            rmax2 = fmaxf(rmax2, sq_next);
+            nsq[b ^ 1][tid] = -0.5f * sq_next;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    // largest reference norm the block saw (bounds the score error)
+    rmax2 = wave_max(rmax2);
+    if (lane == 0) red[w] = rmax2;
+    __syncthreads();
+    rmax2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        // merge the two half-lists of each token (lanes l and l ^ 32)
+        float other[LK];
+#pragma unroll
+        for (int e = 0; e < LK; ++e) other[e] = __shfl_xor(lst[nt][e], 32, 64);
+#pragma unroll
+        for (int e = 0; e < LK; ++e) list_insert<LK>(lst[nt], other[e]);
+        const bf16_t *xr = x + ((int64_t)unit * nrows + (pos[nt] - t0)) * D;
+        rescore_and_emit<D, LK>(xr, urefs, lst[nt], imask, ibits, k, rmax2, valid[nt],
+                                idx + ((int64_t)unit * Ncap + qn[nt]) * k,
+                                ((uint64_t)unit << 32) | (uint64_t)(qn[nt] - q0), flist, fcount);
+    }
+}
+
+__global__ void zero_u32_kernel(uint32_t *p) {
+    if (threadIdx.x == 0) *p = 0u;
+}
+
+__global__ void add_stats_kernel(const uint32_t *count, uint32_t *stats) {
+    if (threadIdx.x == 0) atomicAdd(stats, *count);
+}
+
+template <int D, int LK>
+void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0, int64_t nq,
+                   const CacheArgs &c, uint64_t *flist, uint32_t *fcount, hipStream_t st) {
+    const int U = dm.B * dm.H;
+    const int ntiles = (int)((nq + 255) / 256);
+    int ibits = 1;
+    while (((int64_t)1 << ibits) < dm.R) ++ibits;
+    const uint32_t imask = (1u << ibits) - 1u;
+    hipLaunchKernelGGL((dist_topk_kernel<D, LK>), dim3((unsigned)(ntiles * U)), dim3(256), 0, st,
+                       (const bf16_t *)x, t0, t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs, c.sqn,
+                       dm.R, dm.N, q0, nq, U, ntiles, imask, ibits, c.idx, flist, fcount);
 }
 
 }  // namespace
@@ -177,6 +514,33 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
                                                    list_cap, st)
                       : launch_exact_t<bf16_t, 128>(dm, x, t0, t1, q0, nq, c, list,
                                                     list_count, list_cap, st);
+}
+
+}  // namespace dk
+
+namespace dk {
+
+// Matrix-core candidate search with certificate; tokens it cannot certify are
+// appended to `flist` and rescanned exactly.  fcount must point to a device
+// counter; it is cleared here.
+hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                              int64_t nq, const CacheArgs &c, uint64_t *flist, uint32_t *fcount,
+                              uint32_t *stats, hipStream_t st) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, fcount);
+    if (dm.d == 128) {
+        if (dm.k <= 4) launch_topk_t<128, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        else launch_topk_t<128, 12>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+    } else {
+        if (dm.k <= 4) launch_topk_t<64, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        else launch_topk_t<64, 12>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_select_exact(dm, x, t0, t1, q0, nq, c, flist, fcount,
+                            (int64_t)nq * dm.B * dm.H, st);
+    if (e != hipSuccess) return e;
+    if (stats) hipLaunchKernelGGL(add_stats_kernel, dim3(1), dim3(64), 0, st, fcount, stats);
+    return hipGetLastError();
 }
 
 }  // namespace dk

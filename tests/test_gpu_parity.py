@@ -198,3 +198,30 @@ def test_llama_layer_32k_sampled():
     _run_case("llama8b-1layer-T32k-bf16 sampled", 1, w.kv_heads, w.q_heads // w.kv_heads, T,
               w.head_dim, s, w.k, w.d_c, w.hidden, dk.BF16, seed=100, n_dirs=w.n_dirs,
               n_centroids=w.n_centroids, positions=pos, decode_heads=[(0, 0), (0, 7)])
+
+
+def test_exact_ties_beyond_candidate_list_take_exact_fallback():
+    # 12 identical reference rows (more than the approximate candidate list
+    # keeps) and tokens equal to them: the certificate cannot separate the
+    # tied references, so those tokens are rescanned exactly; the result must
+    # still be the lowest ordinals, and the fallback counter must see them
+    B, H, T, d, s, k = 1, 1, 600, 128, 8, 4
+    say("[case] fallback via exact ties")
+    x = make_kv(B, H, T, d, torch.bfloat16, key=(110, 0))
+    dup = [2, 5, 9, 11, 14, 20, 23, 30, 31, 40, 47, 55]
+    for j in dup:
+        x[0, 0, j * s] = x[0, 0, 2 * s]
+    tie_pos = [56 * s + 3, 60 * s + 1, 70 * s + 6, 74 * s + 2]
+    for p in tie_pos:
+        x[0, 0, p] = x[0, 0, 2 * s]
+    shape = dk.Shape(B, H, d, s, k, 32, T, dk.BF16)
+    cw, _ = make_mlp(d, 256, 32, torch.bfloat16, key=(110, 1))
+    stats = torch.zeros(4, dtype=torch.int32, device="cuda")
+    c = gpu_compress(shape, x, gpu_mlp(cw, 0), stats=stats)
+    check_compress_unit(shape, x[0, 0], c, 0, 0, oracle_mlp(cw, 0), tol=2e-2)
+    q = lambda p: (p // s) * (s - 1) + (p % s) - 1
+    for p in tie_pos:
+        assert c.idx[0, 0, q(p)].tolist() == dup[:4]
+    n_fb = int(stats[0].item())
+    say(f"  fallback tokens: {n_fb}")
+    assert n_fb >= len(tie_pos)
