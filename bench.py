@@ -210,11 +210,15 @@ def main():
 
     for i in range(a.warmup):
         one_step(i, False)
-    torch.cuda.synchronize()
-    log("[bench] warmup done")
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{a.warmup} done")
     t0 = time.perf_counter()
-    evs = [one_step(a.warmup + i, True) for i in range(a.steps)]
-    torch.cuda.synchronize()
+    evs = []
+    for i in range(a.steps):
+        evs.append(one_step(a.warmup + i, True))
+        torch.cuda.synchronize()
+        log(f"[bench] step {i + 1}/{a.steps}: compress {evs[-1][0].elapsed_time(evs[-1][1]):.2f} ms, "
+            f"decode {evs[-1][1].elapsed_time(evs[-1][2]):.2f} ms")
     wall = time.perf_counter() - t0
     comp_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs]))
     dec_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs]))

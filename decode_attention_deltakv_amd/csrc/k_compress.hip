@@ -9,6 +9,9 @@
 // W2 h + b2 is rounded to the storage type.  Weights are read through L1/L2.
 #include "dk_common.h"
 #include "dk_launch.h"
+#include "dk_mfma.h"
+
+#include <algorithm>
 
 namespace dk {
 namespace {
@@ -68,6 +71,181 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
     }
 }
 
+// Matrix-core path (bf16 storage, hidden width 128 or 256, d_c <= 64).
+// A block walks tiles of 32 tokens of one unit.  Per tile the residual tile
+// (x - mean of the chosen reference rows, fp32, rounded to bf16) is formed in
+// LDS; the 4 waves split the hidden units: h^T = act(W1 r^T + b1) on bf16
+// MFMA (hidden x tokens), then each wave's share of the second product
+// W2 h^T is summed across waves in LDS, b2 added, and the latent rounded to
+// bf16.  The hidden tile never leaves registers (its MFMA output layout is
+// the B operand of the second product, with the hidden index permuted
+// consistently in W2's operand).
+template <int D, int HID, int DC, bool GELU>
+__global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
+    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
+    const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
+    int64_t Ncap, int64_t q0, int64_t nq, int U, int tiles_per_block,
+    const bf16_t *__restrict__ w1, const float *__restrict__ b1, const bf16_t *__restrict__ w2,
+    const float *__restrict__ b2, bf16_t *__restrict__ lat) {
+    constexpr int TT = 32;
+    constexpr int HW = HID / 4;
+    constexpr int MT = HW / 16;
+    constexpr int KSD = D / 32;
+    constexpr int KJ = HW / 32;
+    constexpr int MD = DC / 16;
+    constexpr int CH = D / 8;
+    static_assert(HW % 32 == 0 && DC % 16 == 0, "unsupported shape");
+    __shared__ __attribute__((aligned(16))) bf16_t dl[TT][D + 8];
+    __shared__ float zp[4][DC][TT + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int unit = blockIdx.x % U;
+    const int blk = blockIdx.x / U;
+    const int hb = w * HW;
+    const int64_t qend = q0 + nq;
+    const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
+
+    bf16x8 a1[MT][KSD];
+    f32x4 bias1[MT];
+    bf16x8 a2[MD][KJ];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+            a1[m][ks] = as_bf16x8(ld16(w1 + (int64_t)(hb + 16 * m + l16) * D + 32 * ks + 8 * lq));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bias1[m][r] = b1 ? b1[hb + 16 * m + 4 * lq + r] : 0.f;
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const bf16_t *wr = w2 + (int64_t)(16 * md + l16) * HID + hb + 32 * j + 4 * lq;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(wr);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(wr + 16);
+            u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+            a2[md][j] = as_bf16x8(v);
+        }
+
+    for (int it = 0; it < tiles_per_block; ++it) {
+        const int64_t qt = q0 + ((int64_t)blk * tiles_per_block + it) * TT;
+        if (qt >= qend) break;
+        // ---- residual tile
+#pragma unroll
+        for (int m = 0; m < (TT * CH) / 256; ++m) {
+            const int item = tid + 256 * m;
+            const int t = item / CH, c8 = item % CH;
+            const int64_t q = min(qt + t, qend - 1);
+            const int64_t p = tok_pos(q, s);
+            const u32x4 xv = ld16(x + ((int64_t)unit * nrows + (p - t0)) * D + 8 * c8);
+            const uint16_t *ir = idx + ((int64_t)unit * Ncap + q) * k;
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+            int keff = 0;
+            for (int r = 0; r < k; ++r) {
+                const uint16_t j = ir[r];
+                if (j == kIdxUnused) continue;
+                const u32x4 rv = ld16(urefs + (int64_t)j * D + 8 * c8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += __uint_as_float(rv[e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(rv[e] & 0xffff0000u);
+                }
+                ++keff;
+            }
+            const float inv = 1.f / (float)keff;
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d0 = __uint_as_float(xv[e] << 16) - acc[2 * e] * inv;
+                const float d1 = __uint_as_float(xv[e] & 0xffff0000u) - acc[2 * e + 1] * inv;
+                o[e] = pack_bf16(d0, d1);
+            }
+            *reinterpret_cast<u32x4 *>(&dl[t][8 * c8]) = o;
+        }
+        __syncthreads();
+        // ---- hidden tile and the wave's share of the latent
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            bf16x8 bd[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                bd[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&dl[16 * nt + l16][32 * ks + 8 * lq]));
+            f32x4 c[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                c[m] = bias1[m];
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) c[m] = mfma16_bf16(a1[m][ks], bd[ks], c[m]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c[m][r] = GELU ? gelu_poly_f32(c[m][r]) : c[m][r];
+            }
+            f32x4 zc[MD];
+#pragma unroll
+            for (int md = 0; md < MD; ++md) zc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                u32x4 hv = {pack_bf16(c[2 * j][0], c[2 * j][1]), pack_bf16(c[2 * j][2], c[2 * j][3]),
+                            pack_bf16(c[2 * j + 1][0], c[2 * j + 1][1]),
+                            pack_bf16(c[2 * j + 1][2], c[2 * j + 1][3])};
+#pragma unroll
+                for (int md = 0; md < MD; ++md)
+                    zc[md] = mfma16_bf16(a2[md][j], as_bf16x8(hv), zc[md]);
+            }
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zp[w][16 * md + 4 * lq + r][16 * nt + l16] = zc[md][r];
+        }
+        __syncthreads();
+        // ---- sum the waves' shares, add b2, round, store
+        for (int i = tid; i < TT * DC; i += 256) {
+            const int t = i / DC, o = i % DC;
+            if (qt + t >= qend) continue;
+            const float z = zp[0][o][t] + zp[1][o][t] + zp[2][o][t] + zp[3][o][t] + (b2 ? b2[o] : 0.f);
+            lat[((int64_t)unit * Ncap + qt + t) * DC + o] = f2bf(z);
+        }
+    }
+}
+
+template <int D, int HID, int DC>
+void launch_cmfma_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0, int64_t nq,
+                    const MlpArgs &m, const CacheArgs &c, hipStream_t st) {
+    const int U = dm.B * dm.H;
+    const int64_t tiles = (nq + 31) / 32;
+    const int tpb = (int)std::max<int64_t>(1, std::min<int64_t>(16, (tiles * U + 1023) / 1024));
+    const int64_t nblk = (tiles + tpb - 1) / tpb;
+    auto kern = m.act == 0 ? compress_mfma_kernel<D, HID, DC, true>
+                           : compress_mfma_kernel<D, HID, DC, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nblk * U)), dim3(256), 0, st, (const bf16_t *)x, t0,
+                       t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs, dm.R, c.idx, dm.N, q0, nq, U,
+                       tpb, (const bf16_t *)m.w1, m.b1, (const bf16_t *)m.w2, m.b2,
+                       (bf16_t *)c.lat);
+}
+
+template <int D, int HID>
+bool launch_cmfma_dc(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                     int64_t nq, const MlpArgs &m, const CacheArgs &c, hipStream_t st) {
+    switch (dm.dc) {
+        case 16: launch_cmfma_t<D, HID, 16>(dm, x, t0, t1, q0, nq, m, c, st); return true;
+        case 32: launch_cmfma_t<D, HID, 32>(dm, x, t0, t1, q0, nq, m, c, st); return true;
+        case 64: launch_cmfma_t<D, HID, 64>(dm, x, t0, t1, q0, nq, m, c, st); return true;
+    }
+    return false;
+}
+
+bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                          int64_t nq, const MlpArgs &m, const CacheArgs &c, hipStream_t st) {
+    if (dm.dtype != 1 || (m.hidden != 128 && m.hidden != 256)) return false;
+    if (dm.d == 128)
+        return m.hidden == 256 ? launch_cmfma_dc<128, 256>(dm, x, t0, t1, q0, nq, m, c, st)
+                               : launch_cmfma_dc<128, 128>(dm, x, t0, t1, q0, nq, m, c, st);
+    return m.hidden == 256 ? launch_cmfma_dc<64, 256>(dm, x, t0, t1, q0, nq, m, c, st)
+                           : launch_cmfma_dc<64, 128>(dm, x, t0, t1, q0, nq, m, c, st);
+}
+
 }  // namespace
 
 // Workspace of one compress call (bf16 path): a 256-byte header holding the
@@ -95,6 +273,7 @@ hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1
         e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, st);
     }
     if (e != hipSuccess) return e;
+    if (launch_compress_mfma(dm, x, t0, t1, q0, nq, comp, c, st)) return hipGetLastError();
     dim3 grid((unsigned)((nq + kTB - 1) / kTB), (unsigned)(dm.B * dm.H));
     if (dm.dtype == 0)
         hipLaunchKernelGGL(compress_mlp_kernel<float>, grid, dim3(256), 0, st, (const float *)x,
