@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy before timing (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -147,40 +149,102 @@ def compress_flops(wl):
                                                    + wl.hidden * wl.d_c) * N)
 
 
-def cpu_baseline(wl, widx, n_tok, threads):
-    """The oracle as it is, on a bounded sample of the same workload: select +
-    compress for n_tok uniformly sampled compressed positions of one unit
-    (layer 0, head 0, K stream), split over `threads` host threads."""
+def cpu_baseline(wl, widx, threads, budget_s=12.0):
+    """The oracle as it is, timed on this host on bounded samples of the same
+    workload (one unit: layer 0, KV head 0):
+      compress: select + compress of uniformly sampled compressed positions,
+                pulled in chunks by `threads` host threads until `budget_s`;
+      decode:   one decode step of the 4 query heads of that KV head over all
+                T tokens (K and V rebuilt in two threads, then attention).
+    Rates are scaled to the metric's units (a sequence position = every
+    layer, KV head and stream; a decode token = every layer and KV head)."""
     import oracle
-    from deltakv_synth import kv_rows, unit_key, xavier_mlp
+    from deltakv_synth import kv_rows, queries, unit_key, xavier_mlp
     T, s = wl.T, wl.stride
-    x = kv_rows(T, wl.head_dim, wl.n_dirs, wl.n_centroids, key=unit_key(widx, 0, 0, 0, 0),
-                dtype=wl.torch_dtype).float().double().numpy()
-    w = xavier_mlp(wl.head_dim, wl.hidden, wl.d_c, key=(1, widx, 0, 0), dtype=wl.torch_dtype)
     f = lambda t: t.float().double().numpy()
-    m = oracle.MLP(f(w["w1"]), f(w["b1"]), f(w["w2"]), f(w["b2"]), oracle.ACT_GELU)
-    refs = oracle.build_refs(x, s)
-    pos = np.sort(np.random.default_rng(11).choice(oracle.nonref_positions(T, s), n_tok,
-                                                   replace=False))
-    parts = np.array_split(pos, threads)
+    xk = f(kv_rows(T, wl.head_dim, wl.n_dirs, wl.n_centroids, key=unit_key(widx, 0, 0, 0, 0),
+                   dtype=wl.torch_dtype))
+    xv = f(kv_rows(T, wl.head_dim, wl.n_dirs, wl.n_centroids, key=unit_key(widx, 0, 0, 0, 1),
+                   dtype=wl.torch_dtype))
+    mlp = lambda key, a, b, c: (lambda w: oracle.MLP(f(w["w1"]), f(w["b1"]), f(w["w2"]),
+                                                     f(w["b2"]), oracle.ACT_GELU))(
+        xavier_mlp(a, b, c, key=key, dtype=wl.torch_dtype))
+    ck, cv = mlp((1, widx, 0, 0), wl.head_dim, wl.hidden, wl.d_c), \
+        mlp((1, widx, 0, 1), wl.head_dim, wl.hidden, wl.d_c)
+    dk_, dv_ = mlp((2, widx, 0, 0), wl.d_c, wl.hidden, wl.head_dim), \
+        mlp((2, widx, 0, 1), wl.d_c, wl.hidden, wl.head_dim)
+    refs = oracle.build_refs(xk, s)
+    pos = np.random.default_rng(11).permutation(oracle.nonref_positions(T, s))
+    lock = threading.Lock()
+    state = {"next": 0, "done": 0}
+    chunk = 32
+    deadline = time.perf_counter() + budget_s
 
-    def work(p):
-        idx = oracle.select(x[p], p, refs, s, wl.k)
-        oracle.compress(x[p], refs, idx, m)
+    def work():
+        while time.perf_counter() < deadline:
+            with lock:
+                i = state["next"]
+                state["next"] += chunk
+            p = np.sort(pos[i:i + chunk])
+            if len(p) == 0:
+                return
+            idx = oracle.select(xk[p], p, refs, s, wl.k)
+            oracle.compress(xk[p], refs, idx, ck)
+            with lock:
+                state["done"] += len(p)
 
     t0 = time.perf_counter()
-    ths = [threading.Thread(target=work, args=(p,)) for p in parts]
+    ths = [threading.Thread(target=work) for _ in range(threads)]
     for t in ths:
         t.start()
     for t in ths:
         t.join()
     dt = time.perf_counter() - t0
-    rows_per_token = wl.layers * wl.kv_heads * 2 * (1 - 1 / s)   # compressed rows per position
+    n_tok = state["done"]
+    rows_per_token = wl.layers * wl.batch * wl.kv_heads * 2 * (1 - 1 / s)
+
+    # decode sample: the first Ts positions of the head, compressed by the
+    # oracle, then one decode step; its time is scaled by T / Ts
+    Ts = min(T, 8192)
+    G = wl.q_heads // wl.kv_heads
+    out = {}
+
+    def comp(name, x, m):
+        out[name] = oracle.compress_head(x[:Ts], s, wl.k, m)
+
+    th = [threading.Thread(target=comp, args=("k", xk, ck)),
+          threading.Thread(target=comp, args=("v", xv, cv))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    q = f(queries(G, wl.head_dim, key=(4, widx), dtype=wl.torch_dtype))
+    rec = {}
+
+    def rebuild(name, m):
+        r_, i_, l_ = out[name]
+        rec[name] = oracle.reconstruct(r_, l_, i_, Ts, s, m)
+
+    t1 = time.perf_counter()
+    th = [threading.Thread(target=rebuild, args=("k", dk_)),
+          threading.Thread(target=rebuild, args=("v", dv_))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    oracle.attention(q, rec["k"], rec["v"], 1.0 / math.sqrt(wl.head_dim))
+    t_head = (time.perf_counter() - t1) * (T / Ts)
+    heads_per_step = wl.layers * wl.kv_heads * wl.batch
     return {"value": n_tok / dt / rows_per_token, "unit": "tok/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"select+compress of {n_tok} uniformly sampled compressed positions of "
-                      f"one unit (layer 0, KV head 0, K) at T={T}; {dt:.2f}s; scaled by the "
-                      f"{rows_per_token:.0f} compressed rows per sequence position"}
+            "decode_attn_tok_s": wl.batch / (t_head * heads_per_step),
+            "sample": f"compress: oracle select+compress of {n_tok} uniformly sampled compressed "
+                      f"positions of one unit (layer 0, KV head 0, K) at T={T}, {dt:.1f}s on "
+                      f"{threads} threads, scaled by the {rows_per_token:.0f} compressed rows per "
+                      f"sequence position; decode: one step of one KV head ({G} query heads) over "
+                      f"its first {Ts} positions (K and V rebuilt on 2 threads), {t_head * Ts / T:.2f}s, "
+                      f"scaled by T/{Ts} and by the {heads_per_step} KV heads x layers of a step, "
+                      f"2 threads"}
 
 
 def main():
@@ -196,6 +260,13 @@ def main():
     torch.cuda.set_device(0)
     S = Setup(wl, widx)
     stream = torch.cuda.current_stream()
+    if a.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of 1 GiB done")
+        del src, dst
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def one_step(i, timed):
@@ -276,7 +347,7 @@ def main():
     if not a.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"[bench] cpu baseline on {threads} threads")
-        res["cpu_baseline"] = cpu_baseline(wl, widx, a.cpu_sample_tokens, threads)
+        res["cpu_baseline"] = cpu_baseline(wl, widx, threads)
     print(json.dumps(res), flush=True)
 
 

@@ -34,6 +34,21 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, let M[i] be the four 16-bit values at lane i's 8-byte address; lane j
+// receives {M[4e + j/4][j%4] : e = 0..3} (checked on the hardware).  Two such
+// reads build an MFMA operand column slice: with lane i pointing at row
+// (base + i/4), columns (4 (i%4) .. +3) of a row-major tile, lane j gets rows
+// base .. base+3 of column j.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -56,30 +71,29 @@ __device__ __forceinline__ f16x2 pack_f16(float a, float b) {
 }
 
 // GELU of two fp32 pre-activations, evaluated in packed f16:
-//   GELU(u) = u * Phi(u),   Phi(u) ~= clamp01(0.5 + v * Q(v * v)),  v = u / 2,
+//   GELU(u) = u * Phi(u),   Phi(u) ~= clamp01(0.5 + u * Q(u * u)),
 // where Q is a degree-4 polynomial fitted (least squares with reweighting
 // toward the maximum error) to the standard normal CDF on |u| <= 3.5.  Its
 // leading coefficient is positive, so beyond the fitted range the clamp
-// saturates Phi to 0 or 1; the largest error of Phi over the real line is
+// saturates Phi to 0 or 1.  The largest error of Phi over the real line is
 // below 9e-4 before f16 rounding, and of GELU after it below
-// 2.2e-3 * max(1, |u|).  Used only on the bf16 decode path, where the hidden
-// activations feed f16 matrix products.
+// 2.8e-3 * max(1, |u|).  8 packed instructions per pair.  Used only on the
+// bf16 decode path, where the hidden activations feed f16 matrix products.
 __device__ __forceinline__ f16x2 gelu2_f16(float a, float b) {
     const f16x2 u = pack_f16(a, b);
     const f16x2 half = {(_Float16)0.5f, (_Float16)0.5f};
-    const f16x2 v = u * half;
-    const f16x2 t = v * v;
-    const f16x2 c4 = {(_Float16)6.1716814e-3f, (_Float16)6.1716814e-3f};
-    const f16x2 c3 = {(_Float16)-5.8874029e-2f, (_Float16)-5.8874029e-2f};
-    const f16x2 c2 = {(_Float16)2.2937544e-1f, (_Float16)2.2937544e-1f};
-    const f16x2 c1 = {(_Float16)-4.9287843e-1f, (_Float16)-4.9287843e-1f};
-    const f16x2 c0 = {(_Float16)7.9291154e-1f, (_Float16)7.9291154e-1f};
+    const f16x2 t = u * u;
+    const f16x2 c4 = {(_Float16)1.20540652e-05f, (_Float16)1.20540652e-05f};
+    const f16x2 c3 = {(_Float16)-4.59953350e-04f, (_Float16)-4.59953350e-04f};
+    const f16x2 c2 = {(_Float16)7.16798242e-03f, (_Float16)7.16798242e-03f};
+    const f16x2 c1 = {(_Float16)-6.16098042e-02f, (_Float16)-6.16098042e-02f};
+    const f16x2 c0 = {(_Float16)3.96455769e-01f, (_Float16)3.96455769e-01f};
     f16x2 p = __builtin_elementwise_fma(c4, t, c3);
     p = __builtin_elementwise_fma(p, t, c2);
     p = __builtin_elementwise_fma(p, t, c1);
     p = __builtin_elementwise_fma(p, t, c0);
     f16x2 phi;
-    asm("v_pk_fma_f16 %0, %1, %2, %3 clamp" : "=v"(phi) : "v"(v), "v"(p), "v"(half));
+    asm("v_pk_fma_f16 %0, %1, %2, %3 clamp" : "=v"(phi) : "v"(u), "v"(p), "v"(half));
     return u * phi;
 }
 

@@ -89,7 +89,8 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     return p;
 }
 
-// u_g = W2K^T q_g (hidden entries), c_g = q_g . b2K.  grid (Hq, B).
+// u_g = W2K^T q_g (hidden entries), c_g = q_g . b2K.  grid (Hq, B); thread i
+// owns hidden unit i and reads column i of W2K (coalesced across threads).
 template <typename T>
 __global__ __launch_bounds__(256) void qprep_kernel(const T *__restrict__ q, int Hq, int d,
                                                     const T *__restrict__ w2, int hid,
@@ -97,21 +98,26 @@ __global__ __launch_bounds__(256) void qprep_kernel(const T *__restrict__ q, int
                                                     float *__restrict__ u,
                                                     float *__restrict__ cq) {
     __shared__ float qs[kMaxD];
+    __shared__ float red[4];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const T *qrow = q + ((int64_t)b * Hq + g) * d;
     if (tid < d) qs[tid] = to_f32(qrow[tid]);
     __syncthreads();
     if (tid < hid) {
-        float acc = 0.f;
-        for (int c = 0; c < d; ++c) acc += to_f32(w2[(int64_t)c * hid + tid]) * qs[c];
-        u[((int64_t)b * Hq + g) * kMaxH + tid] = acc;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < d; c += 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] += to_f32(w2[(int64_t)(c + e) * hid + tid]) * qs[c + e];
+        }
+        u[((int64_t)b * Hq + g) * kMaxH + tid] =
+            ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     }
-    if (tid == 0) {
-        float acc = 0.f;
-        if (b2)
-            for (int c = 0; c < d; ++c) acc += qs[c] * b2[c];
-        cq[(int64_t)b * Hq + g] = acc;
-    }
+    float v = (b2 && tid < d) ? qs[tid] * b2[tid] : 0.f;
+    v = wave_sum(v);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    if (tid == 0) cq[(int64_t)b * Hq + g] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // qR[j][g] = q_g . R^K_j over the Rt reference rows.  grid (ceil(Rt/64), H, B).
@@ -363,15 +369,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
     const float Lt = block_reduce(ltsum, red, false);  // (its barriers also publish wgt)
     for (int o = tid; o < vhid; o += 256) {
         float a = 0.f;
+#pragma unroll 8
         for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + kMaxD + o];
         acch[o] = a;
     }
     __syncthreads();
     for (int c = tid; c < d; c += 256) {
         float a = 0.f;
+#pragma unroll 8
         for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + c];
         float wsum = 0.f;
         const T *wr = vw2 + (int64_t)c * vhid;
+#pragma unroll 8
         for (int o = 0; o < vhid; ++o) wsum += to_f32(wr[o]) * acch[o];
         const float bias = vb2 ? vb2[c] : 0.f;
         out[((int64_t)b * Hq + gq) * d + c] = (a + wsum + Lt * bias) / L;
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
 // (8 rows, 16 columns per lane group) spread over all banks; the per-head
 // weight rows carry 16 bytes of padding for the same reason.
 template <int D, int DC, int HID, int KP>
-__global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     int U, int Hq, int G, int k, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
     const uint16_t *__restrict__ kidx, const bf16_t *__restrict__ vref,
@@ -424,14 +433,20 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
     constexpr int CH = D / 8;           // 16-byte chunks per V row
     constexpr int GIT = ROWS * CH / 256;  // gather chunks per thread
     constexpr int WPAD = ROWS + 8;
+    constexpr int NB = 1;  // V-row buffers (one: the next gather is issued after the V side)
     static_assert(HW % 32 == 0, "hidden width per wave must be a multiple of 32");
     static_assert((ROWS * CH) % 256 == 0, "gather must split evenly");
 
     __shared__ float sp[4][kMaxG][TT];
     __shared__ float alpha_s[kMaxG];
-    __shared__ __attribute__((aligned(16))) _Float16 pperm[16][TT + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t wrow[16][WPAD];
-    __shared__ __attribute__((aligned(16))) bf16_t vrow[ROWS][D];
+    __shared__ __attribute__((aligned(16))) _Float16 pperm[kMaxG][TT + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t wrow[kMaxG][WPAD];
+    __shared__ __attribute__((aligned(16))) bf16_t vrow[NB][ROWS][D];
+    __shared__ __attribute__((aligned(16))) float bias_k[HID];
+    __shared__ float bias_v[HID];
+    // first Decompressor layers (K, V) as operand tiles when they fit in 32 KiB
+    constexpr bool WL = 2 * HID * (KS * 32) * 2 <= 32768;
+    __shared__ __attribute__((aligned(16))) bf16_t w1s[WL ? 2 : 1][WL ? HID : 1][KS * 32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
@@ -442,61 +457,52 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
     const int bseq = unit / H;
     float *prec = part + (((int64_t)unit * P + pidx) * G) * kPStride;
 
-    // ---------------- compressed tokens (matrix cores) ----------------
     const int hbase = w * HW;
     const int cbase = w * DW;
     const int64_t ubase_n = (int64_t)unit * Ncap;
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
     const float *qr_u = qr + (int64_t)unit * Rt * G;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
+    const int64_t qe_ = min(Nt, qa_ + (int64_t)tiles_per_part * TT);
+    // per-unit bases; all in-loop offsets are 32-bit
+    const bf16_t *klat_u = klat + (int64_t)unit * Ncap * DC;
+    const bf16_t *vlat_u = vlat + (int64_t)unit * Ncap * DC;
+    const uint16_t *kidx_u = kidx + (int64_t)unit * Ncap * k;
+    const uint16_t *vidx_u = vidx + (int64_t)unit * Ncap * k;
+    const int qa32 = (int)qa_, qe32 = (int)qe_;
+    const bool gl = l16 < G;  // lane carries a query-head row of the P operands
 
-    // weights into registers
-    bf16x8 wK[MT][KS], wV[MT][KS];
-    f32x4 bK[MT];
-    float bV[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int ch = 32 * ks + 8 * lq;
-            wK[m][ks] = as_bf16x8(ch < DC ? ld16(kw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
-                                          : zero4);
-            wV[m][ks] = as_bf16x8(ch < DC ? ld16(vw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
-                                          : zero4);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bK[m][r] = kb1 ? kb1[hbase + 16 * m + 4 * lq + r] : 0.f;
-        bV[m] = vb1 ? vb1[hbase + 16 * m + l16] : 0.f;
-    }
-    // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
-    f16x8 uA[KJ];
-    {
-        const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + (l16 < G ? l16 : 0)) * kMaxH;
-#pragma unroll
-        for (int j = 0; j < KJ; ++j) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int hid = hbase + 32 * j + (e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4));
-                uA[j][e] = (_Float16)(l16 < G ? ug[hid] : 0.f);
-            }
-        }
-    }
     f32x4 acc_h[MT], acc_r[NR];
 #pragma unroll
     for (int n = 0; n < MT; ++n) acc_h[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < NR; ++n) acc_r[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // rows of the weight tables that belong to no query head stay zero
-    for (int i = tid; i < 16 * (TT + 8); i += 256) pperm[i / (TT + 8)][i % (TT + 8)] = (_Float16)0.f;
-    for (int i = tid; i < 16 * WPAD; i += 256) wrow[i / WPAD][i % WPAD] = 0;
 
     // softmax role: (query head sg, token st)
     const int sg = tid >> 5, st = tid & 31;
     const bool sg_ok = sg < G;
-    const float cq_g = sg_ok ? cq[(int64_t)bseq * Hq + h * G + sg] : 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-    // inverse of the token permutation of the P operand
-    const int st_slot = st < 16 ? 8 * (st >> 2) + (st & 3) : 8 * ((st - 16) >> 2) + 4 + (st & 3);
+
+    // V rows of one tile straight into LDS (global -> LDS, 16 bytes per lane,
+    // the lanes of a wave fill consecutive 16-byte slots); the XOR swizzle is
+    // applied on the source side.  gr holds the raw index entries of this
+    // thread's chunks; slots that are past the range or unused load row 0
+    // (their weight is 0).
+    auto issue_gather = [&](int t0, const uint32_t (&gr)[GIT], int b) {
+#pragma unroll
+        for (int m = 0; m < GIT; ++m) {
+            const int it = tid + 256 * m;
+            const int row = it / CH, c8 = it % CH;
+            const int t = row / KP, i = row % KP;
+            const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+            const bool ok = t0 + t < qe32 && i < k && gr[m] != kIdxUnused;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(vref_u + (uint32_t)((ok ? gr[m] : 0u) * D + 8 * sc8)),
+                (__attribute__((address_space(3))) void *)&vrow[b][(256 * m + 64 * w) / CH][0],
+                16, 0, 0);
+        }
+    };
 
     if (pidx >= Ptok) {
         // ---------------- reference tokens ----------------
@@ -516,7 +522,7 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
                 const int64_t j = min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
-                    (__attribute__((address_space(3))) void *)&vrow[(256 * m + 64 * w) / CH][0],
+                    (__attribute__((address_space(3))) void *)&vrow[0][(256 * m + 64 * w) / CH][0],
                     16, 0, 0);
             }
             if (sg_ok) {
@@ -546,16 +552,14 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc_r[n][r] *= al[r];
             const int rb = 8 * lq;
-            const bf16x8 pw = as_bf16x8(*reinterpret_cast<const u32x4 *>(&wrow[l16][rb]));
+            const bf16x8 pw = as_bf16x8(gl ? *reinterpret_cast<const u32x4 *>(&wrow[l16][rb]) : zero4);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-                const int c = cbase + 16 * n + l16;
+                const int c = cbase + 16 * n + 4 * (l16 & 3);
                 const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
-                u32x4 bv;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][pcol] |
-                             ((uint32_t)vrow[rb + 2 * e2 + 1][pcol] << 16);
+                const u32x2 lo = lds_read_tr16(&vrow[0][rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&vrow[0][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
                 acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
             }
         }
@@ -577,97 +581,140 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
         return;
     }
 
-    const int64_t qa = (int64_t)pidx * tiles_per_part * TT;
-    const int64_t qe = min(Nt, qa + (int64_t)tiles_per_part * TT);
-
-    // ---- prefetched inputs of the next tile
-    bf16x8 zKn[2][KS], zVn[2][KS];
-    uint16_t idkn[KP], idvn[KP], gidn[GIT];
-    auto load_tile = [&](int64_t t0) {
+    // ---------------- compressed tokens (matrix cores) ----------------
+    // weights into registers
+    bf16x8 wK[WL ? 1 : MT][KS], wV[WL ? 1 : MT][KS];
+    if constexpr (WL) {
+        // rows of W1K / W1V, zero-padded to whole 32-wide k-steps
+        for (int i = tid; i < 2 * HID * KS * 4; i += 256) {
+            const int mat = i / (HID * KS * 4), rem = i % (HID * KS * 4);
+            const int row = rem / (KS * 4), c8 = rem % (KS * 4);
+            const bf16_t *src = mat == 0 ? kw1 : vw1;
+            *reinterpret_cast<u32x4 *>(&w1s[mat][row][8 * c8]) =
+                8 * c8 < DC ? ld16(src + (int64_t)row * DC + 8 * c8) : zero4;
+        }
+    } else {
 #pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2) {
-            const int64_t tk = t0 + 16 * n2 + l16;
+        for (int m = 0; m < MT; ++m) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = 32 * ks + 8 * lq;
-                const bool ok = tk < qe && ch < DC;
-                zKn[n2][ks] = as_bf16x8(ok ? ld16(klat + (ubase_n + tk) * DC + ch) : zero4);
-                zVn[n2][ks] = as_bf16x8(ok ? ld16(vlat + (ubase_n + tk) * DC + ch) : zero4);
+                wK[m][ks] = as_bf16x8(ch < DC ? ld16(kw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
+                                              : zero4);
+                wV[m][ks] = as_bf16x8(ch < DC ? ld16(vw1 + (int64_t)(hbase + 16 * m + l16) * DC + ch)
+                                              : zero4);
             }
         }
-        const bool tok_ok = t0 + st < qe;
+    }
+    auto w1op = [&](int mat, int m, int ks) -> bf16x8 {
+        if constexpr (WL)
+            return as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                &w1s[mat][hbase + 16 * m + l16][32 * ks + 8 * lq]));
+        else
+            return mat == 0 ? wK[m][ks] : wV[m][ks];
+    };
+    for (int i = tid; i < HID; i += 256) {
+        bias_k[i] = kb1 ? kb1[i] : 0.f;
+        bias_v[i] = vb1 ? vb1[i] : 0.f;
+    }
+    __syncthreads();
+    // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
+    f16x8 uA[KJ];
+    {
+        const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + (gl ? l16 : 0)) * kMaxH;
+        float uv[KJ][8];
+#pragma unroll
+        for (int j = 0; j < KJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                uv[j][e] = ug[hbase + 32 * j + (e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4))];
+        const float gm = gl ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) uA[j][e] = (_Float16)(uv[j][e] * gm);
+    }
+    const float cq_g = sg_ok ? cq[(int64_t)bseq * Hq + h * G + sg] : 0.f;
+    // inverse of the token permutation of the P operand
+    const int st_slot = st < 16 ? 8 * (st >> 2) + (st & 3) : 8 * ((st - 16) >> 2) + 4 + (st & 3);
+
+    const int64_t qa = qa_, qe = qe_;
+
+    // ---- loaders.  Loads go to clamped, always-valid addresses and keep
+    // their raw values; validity is applied where the values are used (a
+    // tile later), so no load forces an early wait.
+    struct TileIn {
+        uint32_t ik[KP], iv[KP];   // the softmax thread's token's K / V index rows
+        bf16x8 zk[2][KS], zv[2][KS];
+    };
+    auto load_tile = [&](int t0, TileIn &T) {
+        const uint32_t tk = (uint32_t)min(t0 + st, qe32 - 1);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            const bool ok = tok_ok && i < k;
-            idkn[i] = ok ? kidx[(ubase_n + t0 + st) * k + i] : kIdxUnused;
-            idvn[i] = ok ? vidx[(ubase_n + t0 + st) * k + i] : kIdxUnused;
+            const uint32_t ic = (uint32_t)(i < k ? i : k - 1);
+            T.ik[i] = kidx_u[tk * k + ic];
+            T.iv[i] = vidx_u[tk * k + ic];
         }
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+            const uint32_t tz = (uint32_t)min(t0 + 16 * n2 + l16, qe32 - 1);  // tail: a valid row
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ch = 32 * ks + 8 * lq;
+                T.zk[n2][ks] = as_bf16x8(ch < DC ? ld16(klat_u + (tz * DC + ch)) : zero4);
+                T.zv[n2][ks] = as_bf16x8(ch < DC ? ld16(vlat_u + (tz * DC + ch)) : zero4);
+            }
+        }
+    };
+    auto load_rows = [&](int t0, uint32_t (&gr)[GIT]) {
 #pragma unroll
         for (int m = 0; m < GIT; ++m) {
             const int row = (tid + 256 * m) / CH;
             const int t = row / KP, i = row % KP;
-            const bool ok = t0 + t < qe && i < k;
-            gidn[m] = ok ? vidx[(ubase_n + t0 + t) * k + i] : kIdxUnused;
+            const uint32_t tk = (uint32_t)min(t0 + t, qe32 - 1);
+            gr[m] = vidx_u[tk * k + (uint32_t)(i < k ? i : k - 1)];
         }
     };
-    if (qa < qe) load_tile(qa);
 
-    for (int64_t q0 = qa; q0 < qe; q0 += TT) {
-        bf16x8 zK[2][KS], zV[2][KS];
-        uint16_t idk[KP], idv[KP], gid[GIT];
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                zK[n2][ks] = zKn[n2][ks];
-                zV[n2][ks] = zVn[n2][ks];
-            }
+    // ---- one tile: T holds its inputs; the next tile's inputs go to Tn, the
+    // V-row ordinals of the tile after that to grn; gr are the next tile's
+    auto tile = [&](int q0, int buf, TileIn &T, TileIn &Tn, const uint32_t (&gr)[GIT],
+                    uint32_t (&grn)[GIT]) {
+        const bool tok_ok = q0 + st < qe32;
+        // qR of this tile's references (latency hides behind the K side)
+        float qv[KP];
+        int kek = 0;
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            idk[i] = idkn[i];
-            idv[i] = idvn[i];
+            const bool ok = sg_ok && i < k && T.ik[i] != kIdxUnused;
+            qv[i] = qr_u[(uint32_t)((ok ? T.ik[i] : 0u) * G + (sg_ok ? sg : 0))];
+            qv[i] = ok ? qv[i] : 0.f;
+            kek += ok;
         }
+        // ---- K side: hidden tile (hidden x tokens), GELU, partial scores.
+        // All hidden-tile products are issued before any GELU reads them.
+        f32x4 cK[2][MT];
 #pragma unroll
-        for (int m = 0; m < GIT; ++m) gid[m] = gidn[m];
-
-        __syncthreads();  // the previous tile's V side is done with the shared tables
-        // ---- referenced V rows straight into LDS (global -> LDS, 16 bytes per
-        // lane, lanes of a wave fill consecutive 16-byte slots); the XOR swizzle
-        // is applied on the source side.  Their latency hides behind the K side.
+        for (int m = 0; m < MT; ++m) {
+            const f32x4 bk = *reinterpret_cast<const f32x4 *>(&bias_k[hbase + 16 * m + 4 * lq]);
 #pragma unroll
-        for (int m = 0; m < GIT; ++m) {
-            const int it = tid + 256 * m;
-            const int row = it / CH, c8 = it % CH;
-            const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
-            const int64_t j = gid[m] == kIdxUnused ? 0 : (int64_t)gid[m];
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(vref_u + j * D + 8 * sc8),
-                (__attribute__((address_space(3))) void *)&vrow[(256 * m + 64 * w) / CH][0], 16,
-                0, 0);
+            for (int n2 = 0; n2 < 2; ++n2) {
+                cK[n2][m] = bk;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    cK[n2][m] = mfma16_bf16(w1op(0, m, ks), T.zk[n2][ks], cK[n2][m]);
+            }
         }
-        float qrv[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-            qrv[i] = (sg_ok && idk[i] != kIdxUnused) ? qr_u[(int64_t)idk[i] * G + sg] : 0.f;
-
-        // ---- K side: hidden tile (hidden x tokens), GELU, partial scores
         f32x4 S[2];
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2) {
-            f32x4 cK[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                cK[m] = bK[m];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) cK[m] = mfma16_bf16(wK[m][ks], zK[n2][ks], cK[m]);
-            }
             S[n2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
-                const f16x2 h0 = gelu2_f16(cK[2 * j][0], cK[2 * j][1]);
-                const f16x2 h1 = gelu2_f16(cK[2 * j][2], cK[2 * j][3]);
-                const f16x2 h2 = gelu2_f16(cK[2 * j + 1][0], cK[2 * j + 1][1]);
-                const f16x2 h3 = gelu2_f16(cK[2 * j + 1][2], cK[2 * j + 1][3]);
+                const f16x2 h0 = gelu2_f16(cK[n2][2 * j][0], cK[n2][2 * j][1]);
+                const f16x2 h1 = gelu2_f16(cK[n2][2 * j][2], cK[n2][2 * j][3]);
+                const f16x2 h2 = gelu2_f16(cK[n2][2 * j + 1][0], cK[n2][2 * j + 1][1]);
+                const f16x2 h3 = gelu2_f16(cK[n2][2 * j + 1][2], cK[n2][2 * j + 1][3]);
                 u32x4 hv = {as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)};
                 S[n2] = mfma16_f16(uA[j], as_f16x8(hv), S[n2]);
             }
@@ -679,23 +726,18 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
                 const int g = 4 * lq + r;
                 if (g < G) sp[w][g][16 * n2 + l16] = S[n2][r];
             }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS fills landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's V rows landed
         __syncthreads();
 
         // ---- merge scores, online softmax (thread = (query head sg, token st))
         if (sg_ok) {
-            const bool tok_ok = q0 + st < qe;
             float s = -INFINITY;
             if (tok_ok) {
                 float rs = 0.f;
-                int ke = 0;
 #pragma unroll
-                for (int i = 0; i < KP; ++i) {
-                    rs += qrv[i];
-                    ke += idk[i] != kIdxUnused;
-                }
+                for (int i = 0; i < KP; ++i) rs += qv[i];
                 s = scale * (sp[0][sg][st] + sp[1][sg][st] + sp[2][sg][st] + sp[3][sg][st] +
-                             rs / (float)ke + cq_g);
+                             rs / (float)kek + cq_g);
             }
             float tmax = s;
 #pragma unroll
@@ -710,16 +752,23 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
             m_run = mnew;
             if (st == 0) alpha_s[sg] = alpha;
             pperm[sg][st_slot] = (_Float16)pv;
-            int ke = 0;
+            int kev = 0;
 #pragma unroll
-            for (int i = 0; i < KP; ++i) ke += idv[i] != kIdxUnused;
-            const float wv = ke > 0 ? pv / (float)ke : 0.f;
+            for (int i = 0; i < KP; ++i) kev += (i < k && T.iv[i] != kIdxUnused);
+            const float wv = kev > 0 ? pv / (float)kev : 0.f;
 #pragma unroll
             for (int i = 0; i < KP; ++i)
-                wrow[sg][st * KP + i] = idv[i] != kIdxUnused ? f2bf(wv) : (bf16_t)0;
+                wrow[sg][st * KP + i] = (i < k && T.iv[i] != kIdxUnused) ? f2bf(wv) : (bf16_t)0;
         }
         __syncthreads();
-        if (q0 + TT < qe) load_tile(q0 + TT);
+
+        // ---- the next tile's loads (their latency hides behind the V side)
+        const bool more = q0 + TT < qe32;
+        if (more) {
+            if (NB == 2) issue_gather(q0 + TT, gr, buf ^ 1);
+            load_tile(q0 + TT, Tn);
+            load_rows(q0 + 2 * TT, grn);
+        }
 
         // ---- V side
         {
@@ -735,20 +784,26 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc_r[n][r] *= al[r];
         }
-        const f16x8 pa = as_f16x8(*reinterpret_cast<const u32x4 *>(&pperm[l16][8 * lq]));
+        const f16x8 pa = as_f16x8(gl ? *reinterpret_cast<const u32x4 *>(&pperm[l16][8 * lq]) : zero4);
+        f32x4 cV[MT][2];
 #pragma unroll
         for (int n = 0; n < MT; ++n) {
-            f32x4 c0 = {bV[n], bV[n], bV[n], bV[n]};
-            f32x4 c1 = c0;
+            const float bv_ = bias_v[hbase + 16 * n + l16];
+            cV[n][0] = f32x4{bv_, bv_, bv_, bv_};
+            cV[n][1] = cV[n][0];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                c0 = mfma16_bf16(zV[0][ks], wV[n][ks], c0);
-                c1 = mfma16_bf16(zV[1][ks], wV[n][ks], c1);
+                const bf16x8 wv_ = w1op(1, n, ks);
+                cV[n][0] = mfma16_bf16(T.zv[0][ks], wv_, cV[n][0]);
+                cV[n][1] = mfma16_bf16(T.zv[1][ks], wv_, cV[n][1]);
             }
-            const f16x2 h0 = gelu2_f16(c0[0], c0[1]);
-            const f16x2 h1 = gelu2_f16(c0[2], c0[3]);
-            const f16x2 h2 = gelu2_f16(c1[0], c1[1]);
-            const f16x2 h3 = gelu2_f16(c1[2], c1[3]);
+        }
+#pragma unroll
+        for (int n = 0; n < MT; ++n) {
+            const f16x2 h0 = gelu2_f16(cV[n][0][0], cV[n][0][1]);
+            const f16x2 h1 = gelu2_f16(cV[n][0][2], cV[n][0][3]);
+            const f16x2 h2 = gelu2_f16(cV[n][1][0], cV[n][1][1]);
+            const f16x2 h3 = gelu2_f16(cV[n][1][2], cV[n][1][3]);
             u32x4 hv = {as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)};
             acc_h[n] = mfma16_f16(pa, as_f16x8(hv), acc_h[n]);
         }
@@ -756,19 +811,38 @@ __global__ __launch_bounds__(256, KP == 4 ? 2 : 1) void main_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < ROWS / 32; ++ks) {
             const int rb = 32 * ks + 8 * lq;
-            const bf16x8 pw = as_bf16x8(*reinterpret_cast<const u32x4 *>(&wrow[l16][rb]));
+            const bf16x8 pw = as_bf16x8(gl ? *reinterpret_cast<const u32x4 *>(&wrow[l16][rb]) : zero4);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-                const int c = cbase + 16 * n + l16;
+                // B operand: rows rb .. rb+7 of column cbase + 16 n + l16, two
+                // transposing reads (rows rb + l16/4 and rb + 4 + l16/4)
+                const int c = cbase + 16 * n + 4 * (l16 & 3);
                 const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
-                u32x4 bv;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    bv[e2] = (uint32_t)vrow[rb + 2 * e2][pcol] |
-                             ((uint32_t)vrow[rb + 2 * e2 + 1][pcol] << 16);
+                const u32x2 lo = lds_read_tr16(&vrow[buf][rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&vrow[buf][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
                 acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
             }
         }
+        if (NB == 1 && more) {
+            __syncthreads();  // single V-row buffer: every wave is done reading it
+            issue_gather(q0 + TT, gr, 0);
+        }
+    };
+
+    // ---- pipeline: prologue, then tiles in pairs with ping-pong register sets
+    TileIn TA, TB;
+    uint32_t g0[GIT], g1[GIT];
+    {
+        uint32_t gfirst[GIT];
+        load_rows(qa32, gfirst);
+        load_tile(qa32, TA);
+        load_rows(qa32 + TT, g1);
+        issue_gather(qa32, gfirst, 0);
+    }
+    for (int q0 = qa32; q0 < qe32; q0 += 2 * TT) {
+        tile(q0, 0, TA, TB, g1, g0);
+        if (q0 + TT < qe32) tile(q0 + TT, NB == 2 ? 1 : 0, TB, TA, g0, g1);
     }
 
     // ---- partial record: m, l, l over compressed tokens, acc_r[d], acc_h[hidden]

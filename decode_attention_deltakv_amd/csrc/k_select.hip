@@ -154,15 +154,108 @@ __global__ __launch_bounds__(256) void select_exact_kernel(
     }
 }
 
+// Exact top-k of listed tokens, one block per token (grid-stride over the
+// list): the 256 threads split the candidate references, each keeps a sorted
+// top-k of its share, and the block merges the 256 lists by k rounds of a
+// lexicographic (distance, ordinal) minimum.  Same arithmetic as the
+// wave-per-token scan; used for the few tokens the matrix-core search could
+// not certify.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_exact_block_kernel(
+    const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
+    int64_t Rcap, int64_t Ncap, int64_t q0, int k, uint16_t *__restrict__ idx,
+    const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count) {
+    __shared__ double xs[D];
+    __shared__ double wd[4];
+    __shared__ int wj[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t n = (int64_t)*list_count;
+    for (int64_t wi = blockIdx.x; wi < n; wi += gridDim.x) {
+        const uint64_t e = list[wi];
+        const int64_t unit = (int64_t)(e >> 32);
+        const int64_t q = q0 + (int64_t)(e & 0xffffffffu);
+        const int64_t p = tok_pos(q, s);
+        const T *xrow = x + (unit * nrows + (p - t0)) * D;
+        __syncthreads();
+        for (int i = tid; i < D; i += 256) xs[i] = to_f64(xrow[i]);
+        __syncthreads();
+        const int64_t ncand = (p + s - 1) / s;
+        const T *ubase = refs + unit * Rcap * D;
+        double bd[kMaxK];
+        int bj[kMaxK];
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) {
+            bd[i] = __builtin_inf();
+            bj[i] = INT_MAX;
+        }
+        for (int64_t j = tid; j < ncand; j += 256) {
+            double cd = exact_sq_dist<T, D>(xs, ubase + j * D);
+            int cj = (int)j;
+            if (!(cd < bd[kMaxK - 1] || (cd == bd[kMaxK - 1] && cj < bj[kMaxK - 1]))) continue;
+#pragma unroll
+            for (int i = 0; i < kMaxK; ++i) {
+                const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
+                const double td = bd[i];
+                const int tj = bj[i];
+                bd[i] = lt ? cd : td;
+                bj[i] = lt ? cj : tj;
+                cd = lt ? td : cd;
+                cj = lt ? tj : cj;
+            }
+        }
+        uint16_t *out = idx + (unit * Ncap + q) * k;
+        for (int r = 0; r < k; ++r) {
+            double md = bd[0];
+            int mj = bj[0];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double od = __shfl_xor(md, o, 64);
+                const int oj = __shfl_xor(mj, o, 64);
+                if (od < md || (od == md && oj < mj)) {
+                    md = od;
+                    mj = oj;
+                }
+            }
+            if (lane == 0) {
+                wd[wv] = md;
+                wj[wv] = mj;
+            }
+            __syncthreads();
+            md = wd[0];
+            mj = wj[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                if (wd[i] < md || (wd[i] == md && wj[i] < mj)) {
+                    md = wd[i];
+                    mj = wj[i];
+                }
+            __syncthreads();
+            if (mj != INT_MAX && bj[0] == mj) {
+#pragma unroll
+                for (int i = 0; i + 1 < kMaxK; ++i) {
+                    bd[i] = bd[i + 1];
+                    bj[i] = bj[i + 1];
+                }
+                bd[kMaxK - 1] = __builtin_inf();
+                bj[kMaxK - 1] = INT_MAX;
+            }
+            if (tid == 0) out[r] = (mj == INT_MAX) ? kIdxUnused : (uint16_t)mj;
+        }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                           int64_t nq, const CacheArgs &c, const uint64_t *list,
                           const uint32_t *list_count, int64_t list_cap, hipStream_t st) {
-    dim3 grid;
-    if (list)
-        grid = dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((list_cap + 3) / 4, 2048)), 1);
-    else
-        grid = dim3((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
+    if (list) {
+        const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap, 1024));
+        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(256), 0, st,
+                           (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
+                           dm.k, c.idx, list, list_count);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
     hipLaunchKernelGGL((select_exact_kernel<T, D>), grid, dim3(256), 0, st, (const T *)x, t0,
                        t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0, nq, dm.k, c.idx, list,
                        list_count);
