@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dk_common.h"
 #include "dk_launch.h"
@@ -433,20 +434,24 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     constexpr int CH = D / 8;           // 16-byte chunks per V row
     constexpr int GIT = ROWS * CH / 256;  // gather chunks per thread
     constexpr int WPAD = ROWS + 8;
-    constexpr int NB = 1;  // V-row buffers (one: the next gather is issued after the V side)
+    constexpr int NB = (ROWS * D * 2 <= 32768) ? 2 : 1;  // V-row buffers
     static_assert(HW % 32 == 0, "hidden width per wave must be a multiple of 32");
     static_assert((ROWS * CH) % 256 == 0, "gather must split evenly");
 
-    __shared__ float sp[4][kMaxG][TT];
+    __shared__ float sp[4][kMaxG][TT + 4];
     __shared__ float alpha_s[kMaxG];
     __shared__ __attribute__((aligned(16))) _Float16 pperm[kMaxG][TT + 8];
     __shared__ __attribute__((aligned(16))) bf16_t wrow[kMaxG][WPAD];
-    __shared__ __attribute__((aligned(16))) bf16_t vrow[NB][ROWS][D];
+    // V rows of the current and the next tile (two objects, so the compiler
+    // can tell an LDS fill of one from reads of the other)
+    __shared__ __attribute__((aligned(16))) bf16_t vrowA[ROWS][D];
+    __shared__ __attribute__((aligned(16))) bf16_t vrowB[NB == 2 ? ROWS : 1][D];
     __shared__ __attribute__((aligned(16))) float bias_k[HID];
     __shared__ float bias_v[HID];
-    // first Decompressor layers (K, V) as operand tiles when they fit in 32 KiB
-    constexpr bool WL = 2 * HID * (KS * 32) * 2 <= 32768;
-    __shared__ __attribute__((aligned(16))) bf16_t w1s[WL ? 2 : 1][WL ? HID : 1][KS * 32];
+    // first Decompressor layers (K, V) as LDS operand tiles only when the V-row
+    // tile is single-buffered; rows padded by 16 bytes against bank conflicts
+    constexpr bool WL = NB == 1 && 2 * HID * (KS * 32 + 8) * 2 <= 40960;
+    __shared__ __attribute__((aligned(16))) bf16_t w1s[WL ? 2 : 1][WL ? HID : 1][KS * 32 + 8];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     // applied on the source side.  gr holds the raw index entries of this
     // thread's chunks; slots that are past the range or unused load row 0
     // (their weight is 0).
-    auto issue_gather = [&](int t0, const uint32_t (&gr)[GIT], int b) {
+    auto issue_gather = [&](int t0, const uint32_t (&gr)[GIT], bf16_t (*dst)[D]) {
 #pragma unroll
         for (int m = 0; m < GIT; ++m) {
             const int it = tid + 256 * m;
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             const bool ok = t0 + t < qe32 && i < k && gr[m] != kIdxUnused;
             __builtin_amdgcn_global_load_lds(
                 (const void *)(vref_u + (uint32_t)((ok ? gr[m] : 0u) * D + 8 * sc8)),
-                (__attribute__((address_space(3))) void *)&vrow[b][(256 * m + 64 * w) / CH][0],
+                (__attribute__((address_space(3))) void *)&dst[(256 * m + 64 * w) / CH][0],
                 16, 0, 0);
         }
     };
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 const int64_t j = min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
-                    (__attribute__((address_space(3))) void *)&vrow[0][(256 * m + 64 * w) / CH][0],
+                    (__attribute__((address_space(3))) void *)&vrowA[(256 * m + 64 * w) / CH][0],
                     16, 0, 0);
             }
             if (sg_ok) {
@@ -557,8 +562,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
                 const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
-                const u32x2 lo = lds_read_tr16(&vrow[0][rb + (l16 >> 2)][pcol]);
-                const u32x2 hi = lds_read_tr16(&vrow[0][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x2 lo = lds_read_tr16(&vrowA[rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&vrowA[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
                 acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
             }
@@ -678,8 +683,11 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 
     // ---- one tile: T holds its inputs; the next tile's inputs go to Tn, the
     // V-row ordinals of the tile after that to grn; gr are the next tile's
-    auto tile = [&](int q0, int buf, TileIn &T, TileIn &Tn, const uint32_t (&gr)[GIT],
+    auto tile = [&](auto bufc, int q0, TileIn &T, TileIn &Tn, const uint32_t (&gr)[GIT],
                     uint32_t (&grn)[GIT]) {
+        constexpr int BUF = decltype(bufc)::value;
+        bf16_t (*cur)[D] = (NB == 2 && BUF == 1) ? vrowB : vrowA;
+        bf16_t (*nxt)[D] = (NB == 2 && BUF == 0) ? vrowB : vrowA;
         const bool tok_ok = q0 + st < qe32;
         // qR of this tile's references (latency hides behind the K side)
         float qv[KP];
@@ -728,6 +736,10 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's V rows landed
         __syncthreads();
+        // every wave is past the previous tile's V side: the other V-row
+        // buffer is free for the next tile
+        const bool more = q0 + TT < qe32;
+        if (NB == 2 && more) issue_gather(q0 + TT, gr, nxt);
 
         // ---- merge scores, online softmax (thread = (query head sg, token st))
         if (sg_ok) {
@@ -763,9 +775,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         __syncthreads();
 
         // ---- the next tile's loads (their latency hides behind the V side)
-        const bool more = q0 + TT < qe32;
         if (more) {
-            if (NB == 2) issue_gather(q0 + TT, gr, buf ^ 1);
             load_tile(q0 + TT, Tn);
             load_rows(q0 + 2 * TT, grn);
         }
@@ -818,15 +828,15 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 // transposing reads (rows rb + l16/4 and rb + 4 + l16/4)
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
                 const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
-                const u32x2 lo = lds_read_tr16(&vrow[buf][rb + (l16 >> 2)][pcol]);
-                const u32x2 hi = lds_read_tr16(&vrow[buf][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
                 acc_r[n] = mfma16_bf16(pw, as_bf16x8(bv), acc_r[n]);
             }
         }
         if (NB == 1 && more) {
             __syncthreads();  // single V-row buffer: every wave is done reading it
-            issue_gather(q0 + TT, gr, 0);
+            issue_gather(q0 + TT, gr, vrowA);
         }
     };
 
@@ -838,11 +848,11 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         load_rows(qa32, gfirst);
         load_tile(qa32, TA);
         load_rows(qa32 + TT, g1);
-        issue_gather(qa32, gfirst, 0);
+        issue_gather(qa32, gfirst, vrowA);
     }
     for (int q0 = qa32; q0 < qe32; q0 += 2 * TT) {
-        tile(q0, 0, TA, TB, g1, g0);
-        if (q0 + TT < qe32) tile(q0 + TT, NB == 2 ? 1 : 0, TB, TA, g0, g1);
+        tile(std::integral_constant<int, 0>(), q0, TA, TB, g1, g0);
+        if (q0 + TT < qe32) tile(std::integral_constant<int, 1>(), q0 + TT, TB, TA, g0, g1);
     }
 
     // ---- partial record: m, l, l over compressed tokens, acc_r[d], acc_h[hidden]
