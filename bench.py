@@ -17,6 +17,7 @@ Prints one JSON line:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +33,36 @@ import torch
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+# HBM traffic of one decode_attn call on the 128k, 32-layer workload, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, summed over
+# the call's kernels).  FETCH_SIZE reads 0.5 KiB per KiB for a plain 1 GiB
+# device copy, so it is scaled by 2; WRITE_SIZE reads 1:1.  The figures hold
+# only for the decode source they were taken on (its SHA-256 prefix); after any
+# change to it the traffic is reported as null until it is measured again.
+DECODE_TRAFFIC = {
+    "workload": "llama8b-32layer-T128k-bf16",
+    "source_sha256": "840709aea770",
+    "fetch_kib": {"main_mfma": 85013.3, "refscore": 8242.5, "combine": 2366.5, "qprep": 279.0},
+    "write_kib": {"main_mfma": 3880.0, "refscore": 1024.0, "combine": 16.0, "qprep": 33.0},
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+}
+
+
+def decode_source_sha():
+    path = os.path.join(ROOT, "decode_attention_deltakv_amd", "csrc", "k_decode.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:12]
+
+
+def decode_traffic_bytes(wl):
+    t = DECODE_TRAFFIC
+    if wl.name != t["workload"] or decode_source_sha() != t["source_sha256"]:
+        return None
+    kib = (sum(t["fetch_kib"].values()) * t["fetch_scale"]
+           + sum(t["write_kib"].values()) * t["write_scale"])
+    return kib * 1024.0
 
 
 def log(*a):
@@ -110,8 +141,10 @@ class Setup:
                             self.stats)
 
     def decode_step(self, i):
+        self.decode_step_q(self.qbank[i % 64])
+
+    def decode_step_q(self, qs):
         dk, sh, T = self.dk, self.shape, self.wl.T
-        qs = self.qbank[i % 64]
         for l in range(self.wl.layers):
             c, d = self.cache[l], self.dec[l]
             dk.decode_attn(sh, self.Hq, T, qs[l], c[0], d[0], c[1], d[1], self.scale, self.out,
@@ -138,9 +171,10 @@ def compress_flops(wl):
     s, T = wl.stride, wl.T
     R = -(-T // s)
     pairs = 0
-    # sum over non-reference positions p of ceil(p / s)
+    # sum over non-reference positions p of ceil(p / s): the positions strictly
+    # between references j and j + 1 see j + 1 references
     for j in range(R):
-        lo, hi = j * s + 1, min((j + 1) * s, T)    # positions with ceil(p/s) = j + 1
+        lo, hi = j * s + 1, min((j + 1) * s - 1, T - 1)
         if hi >= lo:
             pairs += (hi - lo + 1) * (j + 1)
     N = T - R
@@ -235,6 +269,15 @@ def cpu_baseline(wl, widx, threads, budget_s=12.0):
     oracle.attention(q, rec["k"], rec["v"], 1.0 / math.sqrt(wl.head_dim))
     t_head = (time.perf_counter() - t1) * (T / Ts)
     heads_per_step = wl.layers * wl.kv_heads * wl.batch
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": n_tok / dt / rows_per_token, "unit": "tok/s", "cores": threads,
             "kind": "oracle",
             "decode_attn_tok_s": wl.batch / (t_head * heads_per_step),
@@ -244,7 +287,7 @@ def cpu_baseline(wl, widx, threads, budget_s=12.0):
                       f"sequence position; decode: one step of one KV head ({G} query heads) over "
                       f"its first {Ts} positions (K and V rebuilt on 2 threads), {t_head * Ts / T:.2f}s, "
                       f"scaled by T/{Ts} and by the {heads_per_step} KV heads x layers of a step, "
-                      f"2 threads"}
+                      f"2 threads; host CPU {cpu}"}
 
 
 def main():
@@ -283,6 +326,7 @@ def main():
         one_step(i, False)
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{a.warmup} done")
+    S.stats.zero_()
     t0 = time.perf_counter()
     evs = []
     for i in range(a.steps):
@@ -313,6 +357,46 @@ def main():
     per_layer_bytes = decode_bytes_per_layer(wl)
     achieved = per_layer_bytes / (launch_ms * 1e-3) / 1e9
 
+    # one decode step (every layer) captured in a HIP graph and replayed, with
+    # fresh queries copied into the captured query buffer before each replay
+    graph_ms = None
+    try:
+        qstat = S.qbank[0].clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            S.decode_step_q(qstat)   # untimed run on the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                S.decode_step_q(qstat)
+        torch.cuda.synchronize()
+        n_rep = max(4, min(32, dsteps))
+        gs, ge = [ev() for _ in range(n_rep)], [ev() for _ in range(n_rep)]
+        for i in range(n_rep):
+            qstat.copy_(S.qbank[(i + 1) % 64])
+            gs[i].record(stream)
+            g.replay()
+            ge[i].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(gs, ge)]))
+        del g
+    except Exception as e:  # graph capture is a reported extra, not the metric
+        log(f"[bench] graph capture skipped: {e}")
+
+    # measured HBM copy rate (1 GiB device-to-device) as a second denominator
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     B, T = wl.batch, wl.T
     step_bytes = per_layer_bytes * wl.layers
     res = {
@@ -335,14 +419,17 @@ def main():
         "compress_ms_per_step": comp_ms,
         "compress_tflops": compress_flops(wl) / (comp_ms * 1e-3) / 1e12,
         "decode_ms_per_step": dec_ms,
+        "decode_graph_ms_per_step": graph_ms,
         "decode_attn_tok_s": B * dsteps / (dec_ms * 1e-3),
         "decode_eff_hbm_gbs": step_bytes * dsteps / (dec_ms * 1e-3) / 1e9,
-        "fallback_tokens": int(S.stats[0].item()),
+        "fallback_tokens_per_compress": int(S.stats[0].item()) // a.steps,
+        "measured_copy_gbs": copy_gbs,
         "roofline": {"kernel": "deltakv_decode_attn (one layer)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(wl),
                      "algorithmic_bytes_per_launch": per_layer_bytes,
-                     "launch_ms": launch_ms},
+                     "launch_ms": launch_ms,
+                     "frac_of_measured_copy": achieved / copy_gbs},
     }
     if not a.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))

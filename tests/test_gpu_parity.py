@@ -225,3 +225,46 @@ def test_exact_ties_beyond_candidate_list_take_exact_fallback():
     n_fb = int(stats[0].item())
     say(f"  fallback tokens: {n_fb}")
     assert n_fb >= len(tie_pos)
+
+
+def test_decode_graph_replays_match_eager():
+    # decode captured in a HIP graph (as a serving loop would), replayed several
+    # times with eager library work and synchronisations between the replays;
+    # every replay must equal the eager result bit for bit
+    B, H, G, T, d, s, k, dc, hid = 1, 2, 4, 1500, 128, 16, 4, 32, 256
+    say("[case] decode graph replay")
+    tdt = torch.bfloat16
+    shape = dk.Shape(B, H, d, s, k, dc, T, dk.BF16)
+    kx = make_kv(B, H, T, d, tdt, key=(120, 0))
+    vx = make_kv(B, H, T, d, tdt, key=(120, 1))
+    kc = gpu_compress(shape, kx, gpu_mlp(make_mlp(d, hid, dc, tdt, key=(120, 2))[0], 0))
+    vc = gpu_compress(shape, vx, gpu_mlp(make_mlp(d, hid, dc, tdt, key=(120, 3))[0], 0))
+    kd = gpu_mlp(make_mlp(dc, hid, d, tdt, key=(120, 4))[0], 0)
+    vd = gpu_mlp(make_mlp(dc, hid, d, tdt, key=(120, 5))[0], 0)
+    Hq = H * G
+    scale = 1.0 / math.sqrt(d)
+    qa = queries(B * Hq, d, key=(120, 6), dtype=tdt).reshape(B, Hq, d).cuda()
+    qb = queries(B * Hq, d, key=(120, 7), dtype=tdt).reshape(B, Hq, d).cuda()
+    ws = dk.workspace(dk.decode_workspace_bytes(shape, Hq, T))
+    ws2 = dk.workspace(dk.decode_workspace_bytes(shape, Hq, T))
+    out_e = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    dk.decode_attn(shape, Hq, T, qa, kc, kd, vc, vd, scale, out_e, ws)
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(out_e)
+    out_o = torch.empty_like(out_e)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dk.decode_attn(shape, Hq, T, qa, kc, kd, vc, vd, scale, out_g, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep} differs from eager"
+        # eager work on another query between replays
+        dk.decode_attn(shape, Hq, T, qb, kc, kd, vc, vd, scale, out_o, ws2)
+        torch.cuda.synchronize()
+    say("  4 replays equal to eager")
