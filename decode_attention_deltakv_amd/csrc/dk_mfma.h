@@ -5,6 +5,8 @@
 //   A (16 x 32, row-major M x K): lane holds A[l % 16][8 * (l / 16) + i], i = 0..7
 //   B (32 x 16, K x N):           lane holds B[8 * (l / 16) + i][l % 16]
 //   C (16 x 16):                  lane holds C[4 * (l / 16) + r][l % 16], r = 0..3
+// The 16x16x16 f16 form has the same pattern with four K values per lane:
+//   A: lane holds A[l % 16][4 * (l / 16) + i], B: B[4 * (l / 16) + i][l % 16], i = 0..3.
 // and for the 32x32x16 form:
 //   A (32 x 16): lane holds A[l % 32][8 * (l / 32) + i]
 //   B (16 x 32): lane holds B[8 * (l / 32) + i][l % 32]
@@ -19,6 +21,7 @@ namespace dk {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -28,6 +31,9 @@ __device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16k16_f16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -45,12 +45,9 @@ constexpr int kRefPart = 512;  // reference rows per partition
 constexpr int kMaxParts = 4096; // partitions per unit (combine keeps their weights in LDS)
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
 
-struct DecWs {
-    float *u;      // [B][Hq][kMaxH]
-    float *cq;     // [B][Hq]
-    float *qr;     // [B][H][Rt][G]
-    float *part;   // [B][H][P][G][kPStride]
-};
+// The q.R^K table keeps its query heads padded to a multiple of 4 (zeros), so
+// a lane can read the 4 heads of its row group with one 16-byte load.
+__host__ __device__ inline int qr_heads(int G) { return (G + 3) & ~3; }
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -83,7 +80,7 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     p.off_cq = off;
     off += align_up((size_t)dm.B * Hq * 4);
     p.off_qr = off;
-    off += align_up((size_t)dm.B * dm.H * p.Rt * G * 4);
+    off += align_up((size_t)dm.B * dm.H * p.Rt * qr_heads(G) * 4);
     p.off_part = off;
     off += align_up((size_t)dm.B * dm.H * p.P * G * kPStride * 4);
     p.total = off;
@@ -121,7 +118,8 @@ __global__ __launch_bounds__(256) void qprep_kernel(const T *__restrict__ q, int
     if (tid == 0) cq[(int64_t)b * Hq + g] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// qR[j][g] = q_g . R^K_j over the Rt reference rows.  grid (ceil(Rt/64), H, B).
+// qR[j][g] = q_g . R^K_j over the Rt reference rows (heads padded to
+// qr_heads(G) with zeros).  grid (ceil(Rt/64), H, B).
 template <typename T>
 __global__ __launch_bounds__(256) void refscore_kernel(const T *__restrict__ q, int Hq, int G,
                                                        int d, const T *__restrict__ krefs,
@@ -133,14 +131,17 @@ __global__ __launch_bounds__(256) void refscore_kernel(const T *__restrict__ q, 
         qs[i / d][i % d] = to_f32(q[((int64_t)b * Hq + h * G + i / d) * d + i % d]);
     __syncthreads();
     const int64_t unit = (int64_t)b * H + h;
-    for (int i = tid; i < 64 * G; i += 256) {
-        const int64_t j = (int64_t)blockIdx.x * 64 + i / G;
-        const int g = i % G;
+    const int GQ = qr_heads(G);
+    for (int i = tid; i < 64 * GQ; i += 256) {
+        const int64_t j = (int64_t)blockIdx.x * 64 + i / GQ;
+        const int g = i % GQ;
         if (j >= Rt) continue;
-        const T *r = krefs + (unit * Rcap + j) * d;
         float acc = 0.f;
-        for (int c = 0; c < d; ++c) acc += qs[g][c] * to_f32(r[c]);
-        qr[(unit * Rt + j) * G + g] = acc;
+        if (g < G) {
+            const T *r = krefs + (unit * Rcap + j) * d;
+            for (int c = 0; c < d; ++c) acc += qs[g][c] * to_f32(r[c]);
+        }
+        qr[(unit * Rt + j) * GQ + g] = acc;
     }
 }
 
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void main_kernel(
                 for (int r = 0; r < k; ++r) {
                     const uint16_t j = ids[t][r];
                     if (j == kIdxUnused) continue;
-                    rs += qr[(unit * Rt + j) * G + g];
+                    rs += qr[(unit * Rt + j) * qr_heads(G) + g];
                     ++keff;
                 }
                 float hsum = 0.f;
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void main_kernel(
             const int nj = (int)min((int64_t)64, jb - j0);
             for (int i = tid; i < G * nj; i += 256) {
                 const int g = i / nj, t = i % nj;
-                sc[g][t] = scale * qr[(unit * Rt + j0 + t) * G + g];
+                sc[g][t] = scale * qr[(unit * Rt + j0 + t) * qr_heads(G) + g];
             }
             __syncthreads();
             if (tid < G) {
@@ -466,7 +467,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const int cbase = w * DW;
     const int64_t ubase_n = (int64_t)unit * Ncap;
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
-    const float *qr_u = qr + (int64_t)unit * Rt * G;
+    const int GQ = qr_heads(G);
+    const float *qr_u = qr + (int64_t)unit * Rt * GQ;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
     const int64_t qe_ = min(Nt, qa_ + (int64_t)tiles_per_part * TT);
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             }
             if (sg_ok) {
                 const bool ok = j0 + st < je;
-                const float s = ok ? scale * qr_u[(j0 + st) * G + sg] : -INFINITY;
+                const float s = ok ? scale * qr_u[(j0 + st) * GQ + sg] : -INFINITY;
                 float tmax = s;
 #pragma unroll
                 for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const bool ok = sg_ok && i < k && T.ik[i] != kIdxUnused;
-            qv[i] = qr_u[(uint32_t)((ok ? T.ik[i] : 0u) * G + (sg_ok ? sg : 0))];
+            qv[i] = qr_u[(uint32_t)((ok ? T.ik[i] : 0u) * GQ + (sg_ok ? sg : 0))];
             qv[i] = ok ? qv[i] : 0.f;
             kek += ok;
         }
@@ -873,6 +875,554 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wave-specialised matrix-core path (bf16 storage, k = 4, d_c <= 32, hidden
+// width 128 or 256).
+//
+// Waves 0 and 1 ("score waves") each own 16 of a tile's 32 tokens and the
+// whole hidden width of the K Decompressor:
+//   hK^T = W1K z^T + b1K   bf16 MFMA (hidden x 16 tokens), bias from LDS as C
+//   GELU                   packed f16
+//   scores U hK^T          f16 MFMA, U = W2K^T q (query heads x hidden)
+//   + mean_j q.R^K_j + q.b2K, then the online softmax of those 16 tokens.
+// Softmax weights are taken relative to a reference maximum per query head:
+// the larger of the two waves' maxima published with the previous tile.  A
+// wave raises its own only when one of its scores exceeds that by more than
+// kSlack (a wave-wide vote; then a row reduction), so in the common tile both
+// waves use the same reference, no cross-lane reduction runs, and p stays
+// below e^kSlack.  Per tile each score wave publishes, in LDS, p (f16, per
+// token), p / k_eff (bf16, per (token, slot) row of the value gather) and the
+// maxima it used, and keeps its own running sum.
+//
+// Waves 2 and 3 ("value waves") each own half of the V hidden units and half
+// of the value columns for all 32 tokens:
+//   hV = z W1V^T + b1V     bf16 MFMA (tokens x hidden), bias as C
+//   GELU                   packed f16
+//   acc_h += P hV          f16 MFMA (16x16x16), one per score wave's tokens
+//   acc_r += P~ R^V        bf16 MFMA over the gathered (token, slot) rows
+// Their accumulators are relative to the larger published maximum and are
+// rescaled only when it moves; in a tile where the two waves' maxima differ,
+// the weights of the lower one are scaled down first.  The referenced
+// V rows go global -> LDS by DMA (16-byte chunks, XOR swizzle on the source
+// side), double-buffered.
+//
+// Schedule: the score waves run one tile ahead.  Between two barriers the
+// score waves produce tile i+1 while the value waves consume tile i and gather
+// the V rows of tile i+1 into the other buffer: one barrier per tile.
+// Reference tokens are separate partitions handled by all four waves.
+constexpr float kSlack = 8.f;
+
+template <int D, int DC, int HID>
+__global__ __launch_bounds__(256, 2) void main_ws_kernel(
+    int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
+    int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
+    const uint16_t *__restrict__ kidx, const bf16_t *__restrict__ vref,
+    const bf16_t *__restrict__ vlat, const uint16_t *__restrict__ vidx,
+    const bf16_t *__restrict__ kw1, const float *__restrict__ kb1,
+    const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
+    const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
+    float *__restrict__ part) {
+    constexpr int KX = 4;              // references per token
+    constexpr int TT = 32;             // tokens per tile
+    constexpr int TH = 16;             // tokens per score wave
+    constexpr int MB = HID / 16;       // 16-row hidden blocks (score waves)
+    constexpr int KJ = HID / 32;       // 32-wide hidden steps of the score product
+    constexpr int HV = HID / 2;        // hidden units per value wave
+    constexpr int NBV = HV / 16;
+    constexpr int DV = D / 2;          // value columns per value wave
+    constexpr int NC = DV / 16;
+    constexpr int ROWS = TT * KX;      // gathered V rows per tile
+    constexpr int CH = D / 8;          // 16-byte chunks per row
+    constexpr int RPD = 64 / CH;       // rows per gather instruction
+    constexpr int NDMA = (ROWS / 2) / RPD;  // gather instructions per value wave per tile
+    constexpr int WR = ROWS + 8;       // padded weight row (bf16)
+    constexpr int PR = TH + 4;         // padded p row (f16)
+    static_assert(DC <= 32, "one 32-wide latent step");
+    static_assert(HID == 128 || HID == 256, "hidden width");
+    static_assert(D == 64 || D == 128, "head_dim");
+
+    __shared__ __attribute__((aligned(16))) bf16_t vbuf[2][ROWS][D];
+    __shared__ __attribute__((aligned(16))) bf16_t wr[2][16][WR];
+    __shared__ __attribute__((aligned(16))) _Float16 pw[2][2][16][PR];
+    __shared__ __attribute__((aligned(16))) float msl[2][2][16];
+    __shared__ __attribute__((aligned(16))) float biask[HID];
+    __shared__ float lfin[2][16], mfin[2][16];
+    __shared__ float alpha_s[kMaxG];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int unit = blockIdx.x % U;
+    const int pidx = blockIdx.x / U;
+    const int H = Hq / G;
+    const int h = unit % H;
+    const int bseq = unit / H;
+    const int GQ = qr_heads(G);
+    float *prec = part + (((int64_t)unit * P + pidx) * G) * kPStride;
+    const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
+    const float *qr_u = qr + (int64_t)unit * Rt * GQ;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    if (pidx >= Ptok) {
+        // ---------------- reference tokens ----------------
+        // score scale * qR[j], value = the stored row.  Tiles of 32 references,
+        // rows straight to LDS; the four waves split the value columns.
+        constexpr int NR = D / 64;
+        const int sg = tid >> 5, st = tid & 31;
+        const bool sg_ok = sg < G;
+        const bool gl = l16 < G;
+        const int cbase = w * (D / 4);
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x4 acc[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
+        const int64_t je = min(Rt, ja + kRefPart);
+        for (int64_t j0 = ja; j0 < je; j0 += TT) {
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < (TT * CH) / 256; ++m) {
+                const int it = tid + 256 * m;
+                const int row = it / CH, c8 = it % CH;
+                const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+                const int64_t j = min(j0 + row, Rt - 1);
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(vref_u + j * D + 8 * sc8),
+                    (__attribute__((address_space(3))) void *)&vbuf[0][(256 * m + 64 * w) / CH][0],
+                    16, 0, 0);
+            }
+            if (sg_ok) {
+                const bool ok = j0 + st < je;
+                const float s = ok ? scale * qr_u[(j0 + st) * GQ + sg] : -INFINITY;
+                float tmax = s;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
+                const float mnew = fmaxf(m_run, tmax);
+                const float alpha = __expf(m_run - mnew);
+                const float pv = ok ? __expf(s - mnew) : 0.f;
+                float psum = pv;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 32);
+                l_run = l_run * alpha + psum;
+                m_run = mnew;
+                if (st == 0) alpha_s[sg] = alpha;
+                wr[0][sg][st] = f2bf(pv);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            float al[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) al[r] = (4 * lq + r < G) ? alpha_s[4 * lq + r] : 0.f;
+#pragma unroll
+            for (int n = 0; n < NR; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[n][r] *= al[r];
+            const int rb = 8 * lq;
+            const bf16x8 pwv =
+                as_bf16x8(gl ? *reinterpret_cast<const u32x4 *>(&wr[0][l16][rb]) : zero4);
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                const int c = cbase + 16 * n + 4 * (l16 & 3);
+                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                const u32x2 lo = lds_read_tr16(&vbuf[0][rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&vbuf[0][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
+                acc[n] = mfma16_bf16(pwv, as_bf16x8(bv), acc[n]);
+            }
+        }
+        if (sg_ok && st == 0) {
+            prec[(int64_t)sg * kPStride + 0] = m_run;
+            prec[(int64_t)sg * kPStride + 1] = l_run;
+            prec[(int64_t)sg * kPStride + 2] = 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            if (g >= G) continue;
+            float *pg = prec + (int64_t)g * kPStride;
+#pragma unroll
+            for (int n = 0; n < HID / 64; ++n) pg[4 + kMaxD + w * (HID / 4) + 16 * n + l16] = 0.f;
+#pragma unroll
+            for (int n = 0; n < NR; ++n) pg[4 + cbase + 16 * n + l16] = acc[n][r];
+        }
+        return;
+    }
+
+    // ---------------- compressed tokens ----------------
+    const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
+    const int qa = (int)qa_;
+    const int qe = (int)min(Nt, qa_ + (int64_t)tiles_per_part * TT);
+    const int ntile = (qe - qa + TT - 1) / TT;
+    const int Ntm1 = (int)Nt - 1;
+    const bf16_t *klat_u = klat + (int64_t)unit * Ncap * DC;
+    const bf16_t *vlat_u = vlat + (int64_t)unit * Ncap * DC;
+    const uint16_t *kidx_u = kidx + (int64_t)unit * Ncap * KX;
+    const uint16_t *vidx_u = vidx + (int64_t)unit * Ncap * KX;
+
+    // rows of absent query heads stay zero; maxima start at -inf
+    for (int i = tid; i < (int)(sizeof(wr) / 16); i += 256)
+        reinterpret_cast<u32x4 *>(&wr[0][0][0])[i] = zero4;
+    for (int i = tid; i < (int)(sizeof(pw) / 16); i += 256)
+        reinterpret_cast<u32x4 *>(&pw[0][0][0][0])[i] = zero4;
+    for (int i = tid; i < 2 * 2 * 16; i += 256) (&msl[0][0][0])[i] = -INFINITY;
+    for (int i = tid; i < HID; i += 256) biask[i] = kb1 ? kb1[i] : 0.f;
+    __syncthreads();
+
+    if (w < 2) {
+        // ================= score waves =================
+        const int src = w;
+        bf16x8 wK[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            wK[mb] = as_bf16x8(8 * lq < DC ? ld16(kw1 + (16 * mb + l16) * DC + 8 * lq) : zero4);
+        // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
+        f16x8 uA[KJ];
+        {
+            const bool gl = l16 < G;
+            const float *ug = ubuf + ((int64_t)bseq * Hq + h * G + (gl ? l16 : 0)) * kMaxH;
+            const float gm = gl ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    uA[j][e] = (_Float16)(gm * ug[32 * j + (e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4))]);
+        }
+        const bool hq_ok = 4 * lq < G;  // this lane's row group carries real heads
+        float cqv[4], m_w[4], l_run[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            cqv[r] = g < G ? cq[(int64_t)bseq * Hq + h * G + g] : 0.f;
+            m_w[r] = -INFINITY;
+            l_run[r] = 0.f;
+        }
+
+        struct KIn {
+            bf16x8 z;
+            u32x2 ik, iv;
+        };
+        // inputs of token (t0 + 16 src + l16), clamped to a stored token
+        auto kload = [&](int t0, KIn &in) {
+            const uint32_t tok = (uint32_t)min(t0 + TH * src + l16, Ntm1);
+            in.z = as_bf16x8(8 * lq < DC ? ld16(klat_u + (tok * DC + 8 * lq)) : zero4);
+            in.ik = *reinterpret_cast<const u32x2 *>(kidx_u + tok * KX);
+            in.iv = *reinterpret_cast<const u32x2 *>(vidx_u + tok * KX);
+        };
+
+        // one tile: scores, softmax, publish into slot (it & 1); the inputs of
+        // tile (nt0) are loaded into `nxt` once this tile's table reads are out
+        auto ktile = [&](int it, int t0, const KIn &in, int nt0, KIn &nxt) {
+            const int sl = it & 1;
+            const uint32_t jk[4] = {in.ik[0] & 0xffffu, in.ik[0] >> 16, in.ik[1] & 0xffffu,
+                                    in.ik[1] >> 16};
+            f32x4 qv[4];
+            float kek = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = jk[i] != kIdxUnused;
+                kek += ok ? 1.f : 0.f;
+                qv[i] = *reinterpret_cast<const f32x4 *>(
+                    qr_u + ((ok ? jk[i] : 0u) * (uint32_t)GQ + (hq_ok ? 4u * lq : 0u)));
+                if (!ok) qv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if (nt0 < qe) kload(nt0, nxt);
+            // hidden tile and partial scores, 32 hidden units per step
+            f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 4 * lq]);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 16 + 4 * lq]);
+                const f32x4 c0 = mfma16_bf16(wK[2 * j], in.z, b0);
+                const f32x4 c1 = mfma16_bf16(wK[2 * j + 1], in.z, b1);
+                const u32x4 hv = {as_u32(gelu2_f16(c0[0], c0[1])), as_u32(gelu2_f16(c0[2], c0[3])),
+                                  as_u32(gelu2_f16(c1[0], c1[1])), as_u32(gelu2_f16(c1[2], c1[3]))};
+                S = mfma16_f16(uA[j], as_f16x8(hv), S);
+            }
+            // scores of token l16 for heads 4 lq + r
+            const bool tok_ok = t0 + TH * src + l16 < qe;
+            const float inv_k = __builtin_amdgcn_rcpf(kek);
+            // reference maxima: the larger of the two waves' previous ones
+            const f32x4 pm0 = *reinterpret_cast<const f32x4 *>(&msl[sl ^ 1][0][4 * lq]);
+            const f32x4 pm1 = *reinterpret_cast<const f32x4 *>(&msl[sl ^ 1][1][4 * lq]);
+            float s[4], mref[4];
+            bool up = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float rs = (qv[0][r] + qv[1][r]) + (qv[2][r] + qv[3][r]);
+                s[r] = (tok_ok && 4 * lq + r < G) ? scale * (S[r] + rs * inv_k + cqv[r]) : -INFINITY;
+                mref[r] = fmaxf(pm0[r], pm1[r]);
+                up = up || s[r] > mref[r] + kSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                // a score far above the reference: raise it to the row group's
+                // maximum (all 16 lanes of a row group agree)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float tm = s[r];
+#pragma unroll
+                    for (int o = 8; o > 0; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 16));
+                    mref[r] = tm > mref[r] + kSlack ? tm : mref[r];
+                }
+            }
+            bool moved = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) moved = moved || mref[r] != m_w[r];
+            if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    l_run[r] *= mref[r] == -INFINITY ? 1.f : __expf(m_w[r] - mref[r]);
+                    m_w[r] = mref[r];
+                }
+            }
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = s[r] == -INFINITY ? 0.f : __expf(s[r] - m_w[r]);
+                l_run[r] += p[r];
+            }
+            // publish
+            const uint32_t jv[4] = {in.iv[0] & 0xffffu, in.iv[0] >> 16, in.iv[1] & 0xffffu,
+                                    in.iv[1] >> 16};
+            float kev = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kev += jv[i] != kIdxUnused ? 1.f : 0.f;
+            const float inv_v = __builtin_amdgcn_rcpf(kev);
+            if (hq_ok) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int g = 4 * lq + r;
+                    if (g < G) {
+                        pw[sl][src][g][l16] = (_Float16)p[r];
+                        const uint32_t wb = f2bf(p[r] * inv_v);
+                        const uint32_t w0 = jv[0] != kIdxUnused ? wb : 0u;
+                        const uint32_t w1 = jv[1] != kIdxUnused ? wb : 0u;
+                        const uint32_t w2 = jv[2] != kIdxUnused ? wb : 0u;
+                        const uint32_t w3 = jv[3] != kIdxUnused ? wb : 0u;
+                        *reinterpret_cast<u32x2 *>(&wr[sl][g][(TH * src + l16) * KX]) =
+                            u32x2{w0 | (w1 << 16), w2 | (w3 << 16)};
+                        if (l16 == 0) msl[sl][src][g] = m_w[r];
+                    }
+                }
+            }
+        };
+
+        KIn X0, X1;
+        kload(qa, X0);
+        ktile(0, qa, X0, qa + TT, X1);
+        __syncthreads();
+        for (int it = 0; it < ntile; it += 2) {
+            if (it + 1 < ntile) ktile(it + 1, qa + (it + 1) * TT, X1, qa + (it + 2) * TT, X0);
+            __syncthreads();
+            if (it + 1 >= ntile) break;
+            if (it + 2 < ntile) ktile(it + 2, qa + (it + 2) * TT, X0, qa + (it + 3) * TT, X1);
+            __syncthreads();
+        }
+        // per-head sums of this wave's tokens
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float lsum = l_run[r];
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 16);
+            if (l16 == 0) {
+                lfin[src][4 * lq + r] = lsum;
+                mfin[src][4 * lq + r] = m_w[r];
+            }
+        }
+        __syncthreads();
+    } else {
+        // ================= value waves =================
+        const int vj = w - 2;
+        const int hb = vj * HV, cb = vj * DV;
+        bf16x8 wV[NBV];
+        f32x4 bV[NBV];
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) {
+            const int hh = hb + 16 * nb + l16;
+            wV[nb] = as_bf16x8(8 * lq < DC ? ld16(vw1 + hh * DC + 8 * lq) : zero4);
+            const float bb = vb1 ? vb1[hh] : 0.f;
+            bV[nb] = f32x4{bb, bb, bb, bb};
+        }
+        f32x4 acc_h[NBV], acc_r[NC];
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) acc_h[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) acc_r[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float macc[4];  // maxima the accumulators are relative to (heads 4 lq + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) macc[r] = -INFINITY;
+
+        // gather addressing: a gather instruction covers RPD rows of 16-byte
+        // chunks; this lane's chunk and its swizzled source offsets
+        const uint32_t lrow = (uint32_t)(lane / CH);
+        const uint32_t c8 = (uint32_t)(lane % CH);
+        uint32_t coff[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) coff[x] = 16u * (c8 ^ (2u * x));
+        const uint32_t rlast = (uint32_t)Rt - 1u;
+        uint32_t gi[NDMA];
+        // index entries of rows [64 vj, 64 vj + 64) of the tile at t0: rows
+        // are (token, slot) pairs in order, i.e. consecutive index entries
+        auto gload = [&](int t0) {
+            const uint32_t base = (uint32_t)(t0 + TH * vj) * KX + lrow;
+            if (t0 + TT <= (int)Nt) {
+#pragma unroll
+                for (int m = 0; m < NDMA; ++m) gi[m] = vidx_u[base + RPD * m];
+            } else {
+                const uint32_t lim = (uint32_t)Nt * KX - 1u;
+#pragma unroll
+                for (int m = 0; m < NDMA; ++m) gi[m] = vidx_u[min(base + RPD * m, lim)];
+            }
+        };
+        // unused slots (0xFFFF) and rows past the stored range read the last
+        // stored reference row: finite data under a zero weight
+        auto gissue = [&](bf16_t (*dst)[D]) {
+#pragma unroll
+            for (int m = 0; m < NDMA; ++m) {
+                const uint32_t j = min(gi[m], rlast);
+                const int x = ((RPD * m) >> 3) & 3;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)((const char *)vref_u + (j * (uint32_t)(D * 2) + coff[x])),
+                    (__attribute__((address_space(3))) void *)&dst[64 * vj + RPD * m][0], 16, 0, 0);
+            }
+        };
+        auto zload = [&](int t0, bf16x8 (&z)[2]) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const uint32_t tok = (uint32_t)min(t0 + 16 * mb + l16, Ntm1);
+                z[mb] = as_bf16x8(8 * lq < DC ? ld16(vlat_u + (tok * DC + 8 * lq)) : zero4);
+            }
+        };
+
+        auto vtile = [&](int it, const bf16x8 (&zv)[2], bf16_t (*cur)[D]) {
+            const int sl = it & 1;
+            // maxima the score waves used for this tile
+            const f32x4 mn0 = *reinterpret_cast<const f32x4 *>(&msl[sl][0][4 * lq]);
+            const f32x4 mn1 = *reinterpret_cast<const f32x4 *>(&msl[sl][1][4 * lq]);
+            bool moved = false, split = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                moved = moved || mn0[r] != macc[r] || mn1[r] != macc[r];
+                split = split || mn0[r] != mn1[r];
+            }
+            if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float mn = fmaxf(mn0[r], mn1[r]);
+                    const float al = mn == -INFINITY ? 1.f : __expf(macc[r] - mn);
+                    macc[r] = mn;
+#pragma unroll
+                    for (int nb = 0; nb < NBV; ++nb) acc_h[nb][r] *= al;
+#pragma unroll
+                    for (int nc = 0; nc < NC; ++nc) acc_r[nc][r] *= al;
+                }
+            }
+            // P operands (rows = query heads l16), per score wave
+            f16x4 pa[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                pa[s2] = *reinterpret_cast<const f16x4 *>(&pw[sl][s2][l16][4 * lq]);
+            const bool scl = __builtin_amdgcn_ballot_w64(split) != 0;
+            float es[2] = {1.f, 1.f};
+            if (scl) {
+                // the two waves used different maxima: bring the lower one's
+                // weights to the larger maximum
+                const float a0 = msl[sl][0][l16], a1 = msl[sl][1][l16];
+                const float mx = fmaxf(a0, a1);
+                es[0] = a0 == -INFINITY ? 0.f : __expf(a0 - mx);
+                es[1] = a1 == -INFINITY ? 0.f : __expf(a1 - mx);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) pa[s2] = pa[s2] * (_Float16)es[s2];
+            }
+            // hidden tiles (tokens x hidden), GELU, acc_h
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const f32x4 c0 = mfma16_bf16(zv[0], wV[nb], bV[nb]);
+                const f32x4 c1 = mfma16_bf16(zv[1], wV[nb], bV[nb]);
+                const u32x2 h0 = {as_u32(gelu2_f16(c0[0], c0[1])), as_u32(gelu2_f16(c0[2], c0[3]))};
+                const u32x2 h1 = {as_u32(gelu2_f16(c1[0], c1[1])), as_u32(gelu2_f16(c1[2], c1[3]))};
+                acc_h[nb] = mfma16k16_f16(pa[0], __builtin_bit_cast(f16x4, h0), acc_h[nb]);
+                acc_h[nb] = mfma16k16_f16(pa[1], __builtin_bit_cast(f16x4, h1), acc_h[nb]);
+            }
+            // reference rows: rows 64 s2 .. 64 s2 + 63 belong to score wave s2
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = 64 * s2 + 32 * ks + 8 * lq;
+                    u32x4 pv = *reinterpret_cast<const u32x4 *>(&wr[sl][l16][rb]);
+                    if (scl) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pv[e] = pack_bf16(__uint_as_float(pv[e] << 16) * es[s2],
+                                              __uint_as_float(pv[e] & 0xffff0000u) * es[s2]);
+                    }
+                    const bf16x8 pwv = as_bf16x8(pv);
+#pragma unroll
+                    for (int nc = 0; nc < NC; ++nc) {
+                        const int c = cb + 16 * nc + 4 * (l16 & 3);
+                        const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                        const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
+                        const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
+                        const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
+                        acc_r[nc] = mfma16_bf16(pwv, as_bf16x8(bv), acc_r[nc]);
+                    }
+                }
+            }
+        };
+
+        bf16x8 zA[2], zB[2];
+        gload(qa);
+        gissue(vbuf[0]);
+        zload(qa, zA);
+        if (ntile > 1) gload(qa + TT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int it = 0; it < ntile; it += 2) {
+            if (it + 1 < ntile) {
+                gissue(vbuf[1]);
+                zload(qa + (it + 1) * TT, zB);
+                if (it + 2 < ntile) gload(qa + (it + 2) * TT);
+            }
+            vtile(it, zA, vbuf[0]);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (it + 1 >= ntile) break;
+            if (it + 2 < ntile) {
+                gissue(vbuf[0]);
+                zload(qa + (it + 2) * TT, zA);
+                if (it + 3 < ntile) gload(qa + (it + 3) * TT);
+            }
+            vtile(it + 1, zB, vbuf[1]);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        __syncthreads();  // the score waves' sums and maxima are in LDS
+        // partial record: accumulators relative to macc; the two waves' sums
+        // brought to the same maximum
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * lq + r;
+            if (g < G) {
+                const float m0 = mfin[0][g], m1 = mfin[1][g];
+                const float M = macc[r];
+                const float e0 = m0 == -INFINITY ? 0.f : __expf(m0 - M);
+                const float e1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
+                float *pg = prec + (int64_t)g * kPStride;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) pg[4 + kMaxD + hb + 16 * nb + l16] = acc_h[nb][r];
+#pragma unroll
+                for (int nc = 0; nc < NC; ++nc) pg[4 + cb + 16 * nc + l16] = acc_r[nc][r];
+                if (vj == 0 && l16 == 0) {
+                    const float L = lfin[0][g] * e0 + lfin[1][g] * e1;
+                    pg[0] = M;
+                    pg[1] = L;
+                    pg[2] = L;
+                }
+            }
+        }
+    }
+}
+
 template <int D, int DC, int HID, int KP>
 void launch_mfma_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                    const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
@@ -885,6 +1435,36 @@ void launch_mfma_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &k
                        (const bf16_t *)vc.refs, (const bf16_t *)vc.lat, vc.idx,
                        (const bf16_t *)kd.w1, kd.b1, (const bf16_t *)vd.w1, vd.b1, scale, u, cq,
                        qr, part);
+}
+
+template <int D, int DC, int HID>
+void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
+                 const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
+                 const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+    const int U = dm.B * dm.H;
+    const int G = Hq / dm.H;
+    hipLaunchKernelGGL((main_ws_kernel<D, DC, HID>), dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
+                       U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
+                       (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
+                       (const bf16_t *)vc.lat, vc.idx, (const bf16_t *)kd.w1, kd.b1,
+                       (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part);
+}
+
+// The wave-specialised kernel covers k = 4 and d_c <= 32.
+template <int D>
+bool launch_ws_d(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
+                 const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
+                 const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+    if (dm.k != 4 || dm.dc > 32) return false;
+    const bool h256 = kd.hidden == 256;
+    if (dm.dc <= 16) {
+        if (h256) launch_ws_t<D, 16, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        else launch_ws_t<D, 16, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+    } else {
+        if (h256) launch_ws_t<D, 32, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        else launch_ws_t<D, 32, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+    }
+    return true;
 }
 
 template <int D, int DC>
@@ -934,6 +1514,11 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     bool done = false;
     if constexpr (sizeof(T) == 2) {
         if (mfma_eligible(dm, kd, vd)) {
+            done = dm.d == 128
+                       ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st)
+                       : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        }
+        if (!done && mfma_eligible(dm, kd, vd)) {
             if (dm.d == 128) {
                 if (dm.dc == 16) done = launch_mfma_dc<128, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
                 else if (dm.dc == 32) done = launch_mfma_dc<128, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);

@@ -79,6 +79,11 @@ def test_bf16_llama_heads_ragged():
     (128, 16, 4, 32, 128, 4, 1500, dk.BF16),
     (128, 16, 4, 32, 256, 2, 600, dk.F32),
     (64, 2, 1, 16, 128, 4, 257, dk.F32),
+    # k = 4 and d_c <= 32: the wave-specialised decode kernel
+    (64, 16, 4, 16, 256, 8, 1100, dk.BF16),
+    (128, 8, 4, 32, 256, 1, 900, dk.BF16),
+    (128, 16, 4, 16, 128, 3, 2000, dk.BF16),
+    (64, 4, 4, 32, 128, 2, 45, dk.BF16),       # a single partial tile
 ])
 def test_shape_variants(cfg):
     d, s, k, dc, hid, G, T, dtype = cfg
