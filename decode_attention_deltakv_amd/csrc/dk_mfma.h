@@ -58,6 +58,22 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Wait until every vector memory operation of the wave has completed (loads
+// into registers and global -> LDS copies).  Written as the builtin, not as
+// inline assembly, so the compiler's own wait-count tracking knows that
+// nothing is outstanding afterwards and adds no waits of its own.
+// gfx9 encoding: vmcnt = 0, expcnt and lgkmcnt left at their maximum.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// base + a 32-bit byte offset.  Written with the offset already in bytes and
+// unsigned 32-bit, so the compiler can use the scalar-base + 32-bit vector
+// offset addressing form (and fold constant offsets into the instruction)
+// instead of 64-bit per-lane address arithmetic.
+template <typename T>
+__device__ __forceinline__ const T *at_byte(const T *base, uint32_t off) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
+}
+
 // 16-byte global load of 8 consecutive 16-bit values (pointer 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
@@ -101,6 +117,35 @@ __device__ __forceinline__ f16x2 gelu2_f16(float a, float b) {
     f16x2 phi;
     asm("v_pk_fma_f16 %0, %1, %2, %3 clamp" : "=v"(phi) : "v"(u), "v"(p), "v"(half));
     return u * phi;
+}
+
+// Two GELU pairs at once (the same polynomial as gelu2_f16), written so that
+// the two packed chains interleave: each step issues both pairs' instruction
+// before either result is needed.
+__device__ __forceinline__ void gelu4_f16(float a, float b, float c, float d, f16x2 &r0,
+                                          f16x2 &r1) {
+    const f16x2 u0 = pack_f16(a, b), u1 = pack_f16(c, d);
+    const f16x2 half = {(_Float16)0.5f, (_Float16)0.5f};
+    const f16x2 c4 = {(_Float16)1.20540652e-05f, (_Float16)1.20540652e-05f};
+    const f16x2 c3 = {(_Float16)-4.59953350e-04f, (_Float16)-4.59953350e-04f};
+    const f16x2 c2 = {(_Float16)7.16798242e-03f, (_Float16)7.16798242e-03f};
+    const f16x2 c1 = {(_Float16)-6.16098042e-02f, (_Float16)-6.16098042e-02f};
+    const f16x2 c0 = {(_Float16)3.96455769e-01f, (_Float16)3.96455769e-01f};
+    const f16x2 t0 = u0 * u0, t1 = u1 * u1;
+    f16x2 p0 = __builtin_elementwise_fma(c4, t0, c3);
+    f16x2 p1 = __builtin_elementwise_fma(c4, t1, c3);
+    p0 = __builtin_elementwise_fma(p0, t0, c2);
+    p1 = __builtin_elementwise_fma(p1, t1, c2);
+    p0 = __builtin_elementwise_fma(p0, t0, c1);
+    p1 = __builtin_elementwise_fma(p1, t1, c1);
+    p0 = __builtin_elementwise_fma(p0, t0, c0);
+    p1 = __builtin_elementwise_fma(p1, t1, c0);
+    f16x2 phi0, phi1;
+    asm("v_pk_fma_f16 %0, %2, %3, %6 clamp\n\tv_pk_fma_f16 %1, %4, %5, %6 clamp"
+        : "=&v"(phi0), "=v"(phi1)
+        : "v"(u0), "v"(p0), "v"(u1), "v"(p1), "v"(half));
+    r0 = u0 * phi0;
+    r1 = u1 * phi1;
 }
 
 // GELU in fp32, u * Phi(u) with Phi(u) ~= clamp01(0.5 + u * P(u * u)), P of

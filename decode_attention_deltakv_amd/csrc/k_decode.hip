@@ -46,8 +46,11 @@ constexpr int kMaxParts = 4096; // partitions per unit (combine keeps their weig
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
 
 // The q.R^K table keeps its query heads padded to a multiple of 4 (zeros), so
-// a lane can read the 4 heads of its row group with one 16-byte load.
+// a lane can read the 4 heads of its row group with one 16-byte load, and one
+// extra all-zero row after the Rt reference rows, which unused index slots
+// read instead of a masked load.
 __host__ __device__ inline int qr_heads(int G) { return (G + 3) & ~3; }
+__host__ __device__ inline int64_t qr_rows(int64_t Rt) { return Rt + 1; }
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -80,7 +83,7 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     p.off_cq = off;
     off += align_up((size_t)dm.B * Hq * 4);
     p.off_qr = off;
-    off += align_up((size_t)dm.B * dm.H * p.Rt * qr_heads(G) * 4);
+    off += align_up((size_t)dm.B * dm.H * qr_rows(p.Rt) * qr_heads(G) * 4);
     p.off_part = off;
     off += align_up((size_t)dm.B * dm.H * p.P * G * kPStride * 4);
     p.total = off;
@@ -135,13 +138,13 @@ __global__ __launch_bounds__(256) void refscore_kernel(const T *__restrict__ q, 
     for (int i = tid; i < 64 * GQ; i += 256) {
         const int64_t j = (int64_t)blockIdx.x * 64 + i / GQ;
         const int g = i % GQ;
-        if (j >= Rt) continue;
+        if (j > Rt) continue;
         float acc = 0.f;
-        if (g < G) {
+        if (g < G && j < Rt) {
             const T *r = krefs + (unit * Rcap + j) * d;
             for (int c = 0; c < d; ++c) acc += qs[g][c] * to_f32(r[c]);
         }
-        qr[(unit * Rt + j) * GQ + g] = acc;
+        qr[(unit * qr_rows(Rt) + j) * GQ + g] = acc;
     }
 }
 
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256) void main_kernel(
                 for (int r = 0; r < k; ++r) {
                     const uint16_t j = ids[t][r];
                     if (j == kIdxUnused) continue;
-                    rs += qr[(unit * Rt + j) * qr_heads(G) + g];
+                    rs += qr[(unit * qr_rows(Rt) + j) * qr_heads(G) + g];
                     ++keff;
                 }
                 float hsum = 0.f;
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256) void main_kernel(
             const int nj = (int)min((int64_t)64, jb - j0);
             for (int i = tid; i < G * nj; i += 256) {
                 const int g = i / nj, t = i % nj;
-                sc[g][t] = scale * qr[(unit * Rt + j0 + t) * qr_heads(G) + g];
+                sc[g][t] = scale * qr[(unit * qr_rows(Rt) + j0 + t) * qr_heads(G) + g];
             }
             __syncthreads();
             if (tid < G) {
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const int64_t ubase_n = (int64_t)unit * Ncap;
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
     const int GQ = qr_heads(G);
-    const float *qr_u = qr + (int64_t)unit * Rt * GQ;
+    const float *qr_u = qr + (int64_t)unit * qr_rows(Rt) * GQ;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
     const int64_t qe_ = min(Nt, qa_ + (int64_t)tiles_per_part * TT);
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 if (st == 0) alpha_s[sg] = alpha;
                 wrow[sg][st] = f2bf(pv);
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_vm_all();
             __syncthreads();
             float al[4];
 #pragma unroll
@@ -736,7 +739,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 const int g = 4 * lq + r;
                 if (g < G) sp[w][g][16 * n2 + l16] = S[n2][r];
             }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's V rows landed
+        wait_vm_all();  // this tile's V rows landed
         __syncthreads();
         // every wave is past the previous tile's V side: the other V-row
         // buffer is free for the next tile
@@ -941,7 +944,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     static_assert(HID == 128 || HID == 256, "hidden width");
     static_assert(D == 64 || D == 128, "head_dim");
 
-    __shared__ __attribute__((aligned(16))) bf16_t vbuf[2][ROWS][D];
+    // V rows of two tiles: two objects, so the compiler can tell the DMA fill
+    // of one from reads of the other (one array would make it wait for the
+    // fill before every read)
+    __shared__ __attribute__((aligned(16))) bf16_t vbufA[ROWS][D];
+    __shared__ __attribute__((aligned(16))) bf16_t vbufB[ROWS][D];
     __shared__ __attribute__((aligned(16))) bf16_t wr[2][16][WR];
     __shared__ __attribute__((aligned(16))) _Float16 pw[2][2][16][PR];
     __shared__ __attribute__((aligned(16))) float msl[2][2][16];
@@ -960,7 +967,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int GQ = qr_heads(G);
     float *prec = part + (((int64_t)unit * P + pidx) * G) * kPStride;
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
-    const float *qr_u = qr + (int64_t)unit * Rt * GQ;
+    const float *qr_u = qr + (int64_t)unit * qr_rows(Rt) * GQ;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     if (pidx >= Ptok) {
@@ -988,7 +995,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const int64_t j = min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
-                    (__attribute__((address_space(3))) void *)&vbuf[0][(256 * m + 64 * w) / CH][0],
+                    (__attribute__((address_space(3))) void *)&vbufA[(256 * m + 64 * w) / CH][0],
                     16, 0, 0);
             }
             if (sg_ok) {
@@ -1008,7 +1015,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 if (st == 0) alpha_s[sg] = alpha;
                 wr[0][sg][st] = f2bf(pv);
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_vm_all();
             __syncthreads();
             float al[4];
 #pragma unroll
@@ -1024,8 +1031,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
                 const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
-                const u32x2 lo = lds_read_tr16(&vbuf[0][rb + (l16 >> 2)][pcol]);
-                const u32x2 hi = lds_read_tr16(&vbuf[0][rb + 4 + (l16 >> 2)][pcol]);
+                const u32x2 lo = lds_read_tr16(&vbufA[rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&vbufA[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
                 acc[n] = mfma16_bf16(pwv, as_bf16x8(bv), acc[n]);
             }
@@ -1104,9 +1111,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // inputs of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = (uint32_t)min(t0 + TH * src + l16, Ntm1);
-            in.z = as_bf16x8(8 * lq < DC ? ld16(klat_u + (tok * DC + 8 * lq)) : zero4);
-            in.ik = *reinterpret_cast<const u32x2 *>(kidx_u + tok * KX);
-            in.iv = *reinterpret_cast<const u32x2 *>(vidx_u + tok * KX);
+            in.z = as_bf16x8(8 * lq < DC ? ld16(at_byte(klat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
+            in.ik = *reinterpret_cast<const u32x2 *>(at_byte(kidx_u, tok * (KX * 2)));
+            in.iv = *reinterpret_cast<const u32x2 *>(at_byte(vidx_u, tok * (KX * 2)));
         };
 
         // one tile: scores, softmax, publish into slot (it & 1); the inputs of
@@ -1119,13 +1126,19 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             float kek = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                // unused slots read the all-zero row Rt
                 const bool ok = jk[i] != kIdxUnused;
                 kek += ok ? 1.f : 0.f;
-                qv[i] = *reinterpret_cast<const f32x4 *>(
-                    qr_u + ((ok ? jk[i] : 0u) * (uint32_t)GQ + (hq_ok ? 4u * lq : 0u)));
-                if (!ok) qv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qv[i] = *reinterpret_cast<const f32x4 *>(at_byte(
+                    qr_u, ((ok ? jk[i] : (uint32_t)Rt) * (uint32_t)GQ + (hq_ok ? 4u * lq : 0u)) * 4u));
             }
-            if (nt0 < qe) kload(nt0, nxt);
+            // the next tile's loads go out after these table reads, so waiting
+            // for the table does not wait for them; they are issued on every
+            // tile (past the range they read a clamped, stored token) so the
+            // wait count does not depend on a branch
+            __builtin_amdgcn_sched_barrier(0);
+            kload(nt0, nxt);
+            __builtin_amdgcn_sched_barrier(0);
             // hidden tile and partial scores, 32 hidden units per step
             f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1134,8 +1147,10 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 16 + 4 * lq]);
                 const f32x4 c0 = mfma16_bf16(wK[2 * j], in.z, b0);
                 const f32x4 c1 = mfma16_bf16(wK[2 * j + 1], in.z, b1);
-                const u32x4 hv = {as_u32(gelu2_f16(c0[0], c0[1])), as_u32(gelu2_f16(c0[2], c0[3])),
-                                  as_u32(gelu2_f16(c1[0], c1[1])), as_u32(gelu2_f16(c1[2], c1[3]))};
+                f16x2 g0, g1, g2, g3;
+                gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
+                gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
+                const u32x4 hv = {as_u32(g0), as_u32(g1), as_u32(g2), as_u32(g3)};
                 S = mfma16_f16(uA[j], as_f16x8(hv), S);
             }
             // scores of token l16 for heads 4 lq + r
@@ -1149,7 +1164,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float rs = (qv[0][r] + qv[1][r]) + (qv[2][r] + qv[3][r]);
-                s[r] = (tok_ok && 4 * lq + r < G) ? scale * (S[r] + rs * inv_k + cqv[r]) : -INFINITY;
+                const float sv = scale * (S[r] + rs * inv_k + cqv[r]);
+                s[r] = (tok_ok && 4 * lq + r < G) ? sv : -INFINITY;
                 mref[r] = fmaxf(pm0[r], pm1[r]);
                 up = up || s[r] > mref[r] + kSlack;
             }
@@ -1261,17 +1277,18 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         const uint32_t rlast = (uint32_t)Rt - 1u;
         uint32_t gi[NDMA];
         // index entries of rows [64 vj, 64 vj + 64) of the tile at t0: rows
-        // are (token, slot) pairs in order, i.e. consecutive index entries
+        // are (token, slot) pairs in order, i.e. consecutive index entries.
+        // Buffer loads over the stored tokens' entries: past them they
+        // return 0 (reference 0, a stored row) instead of reading on.
+        const __amdgpu_buffer_rsrc_t idx_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)vidx_u, (short)0, (int)(Nt * KX * 2), 0x00020000);
+        // (the tile offset goes in the per-lane offset, which the range check
+        // covers, not in the scalar offset)
         auto gload = [&](int t0) {
-            const uint32_t base = (uint32_t)(t0 + TH * vj) * KX + lrow;
-            if (t0 + TT <= (int)Nt) {
+            const int vbase = (t0 + TH * vj) * (KX * 2) + (int)(lrow * 2u);
 #pragma unroll
-                for (int m = 0; m < NDMA; ++m) gi[m] = vidx_u[base + RPD * m];
-            } else {
-                const uint32_t lim = (uint32_t)Nt * KX - 1u;
-#pragma unroll
-                for (int m = 0; m < NDMA; ++m) gi[m] = vidx_u[min(base + RPD * m, lim)];
-            }
+            for (int m = 0; m < NDMA; ++m)
+                gi[m] = __builtin_amdgcn_raw_buffer_load_b16(idx_rsrc, vbase + 2 * RPD * m, 0, 0);
         };
         // unused slots (0xFFFF) and rows past the stored range read the last
         // stored reference row: finite data under a zero weight
@@ -1289,7 +1306,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const uint32_t tok = (uint32_t)min(t0 + 16 * mb + l16, Ntm1);
-                z[mb] = as_bf16x8(8 * lq < DC ? ld16(vlat_u + (tok * DC + 8 * lq)) : zero4);
+                z[mb] = as_bf16x8(8 * lq < DC ? ld16(at_byte(vlat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
             }
         };
 
@@ -1338,8 +1355,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             for (int nb = 0; nb < NBV; ++nb) {
                 const f32x4 c0 = mfma16_bf16(zv[0], wV[nb], bV[nb]);
                 const f32x4 c1 = mfma16_bf16(zv[1], wV[nb], bV[nb]);
-                const u32x2 h0 = {as_u32(gelu2_f16(c0[0], c0[1])), as_u32(gelu2_f16(c0[2], c0[3]))};
-                const u32x2 h1 = {as_u32(gelu2_f16(c1[0], c1[1])), as_u32(gelu2_f16(c1[2], c1[3]))};
+                f16x2 g0, g1, g2, g3;
+                gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
+                gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
+                const u32x2 h0 = {as_u32(g0), as_u32(g1)};
+                const u32x2 h1 = {as_u32(g2), as_u32(g3)};
                 acc_h[nb] = mfma16k16_f16(pa[0], __builtin_bit_cast(f16x4, h0), acc_h[nb]);
                 acc_h[nb] = mfma16k16_f16(pa[1], __builtin_bit_cast(f16x4, h1), acc_h[nb]);
             }
@@ -1372,28 +1392,28 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 
         bf16x8 zA[2], zB[2];
         gload(qa);
-        gissue(vbuf[0]);
+        gissue(vbufA);
         zload(qa, zA);
         if (ntile > 1) gload(qa + TT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vm_all();
         __syncthreads();
         for (int it = 0; it < ntile; it += 2) {
             if (it + 1 < ntile) {
-                gissue(vbuf[1]);
+                gissue(vbufB);
                 zload(qa + (it + 1) * TT, zB);
                 if (it + 2 < ntile) gload(qa + (it + 2) * TT);
             }
-            vtile(it, zA, vbuf[0]);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            vtile(it, zA, vbufA);
+            wait_vm_all();
             __syncthreads();
             if (it + 1 >= ntile) break;
             if (it + 2 < ntile) {
-                gissue(vbuf[0]);
+                gissue(vbufA);
                 zload(qa + (it + 2) * TT, zA);
                 if (it + 3 < ntile) gload(qa + (it + 3) * TT);
             }
-            vtile(it + 1, zB, vbuf[1]);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            vtile(it + 1, zB, vbufB);
+            wait_vm_all();
             __syncthreads();
         }
         __syncthreads();  // the score waves' sums and maxima are in LDS
@@ -1508,7 +1528,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     float *part = (float *)(w + pl.off_part);
     hipLaunchKernelGGL(qprep_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, (const T *)q, Hq, dm.d,
                        (const T *)kd.w2, kd.hidden, kd.b2, u, cq);
-    hipLaunchKernelGGL(refscore_kernel<T>, dim3((unsigned)((pl.Rt + 63) / 64), dm.H, dm.B),
+    hipLaunchKernelGGL(refscore_kernel<T>, dim3((unsigned)((qr_rows(pl.Rt) + 63) / 64), dm.H, dm.B),
                        dim3(256), 0, st, (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R,
                        pl.Rt, qr);
     bool done = false;

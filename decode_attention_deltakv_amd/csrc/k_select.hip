@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         rmax2 = fmaxf(rmax2, v);
         nsq[0][tid] = -0.5f * v;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
     __syncthreads();
 
     for (int st = 0; st < nstage; ++st) {
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
             rmax2 = fmaxf(rmax2, sq_next);
             nsq[b ^ 1][tid] = -0.5f * sq_next;
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vm_all();
         __syncthreads();
     }
     // largest reference norm the block saw (bounds the score error)
