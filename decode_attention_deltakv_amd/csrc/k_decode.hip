@@ -915,7 +915,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 // Reference tokens are separate partitions handled by all four waves.
 constexpr float kSlack = 8.f;
 
-template <int D, int DC, int HID>
+// EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8)
+template <int D, int DC, int HID, int EG>
 __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -1094,14 +1095,15 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 for (int e = 0; e < 8; ++e)
                     uA[j][e] = (_Float16)(gm * ug[32 * j + (e < 4 ? 4 * lq + e : 16 + 4 * lq + (e - 4))]);
         }
-        const bool hq_ok = 4 * lq < G;  // this lane's row group carries real heads
-        float cqv[4], m_w[4], l_run[4];
+        // softmax role: lane (lq, l16) owns token l16 and heads lq + 4 e
+        int gh[EG];
+        float cqv[EG], m_w[EG], l_run[EG];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = 4 * lq + r;
-            cqv[r] = g < G ? cq[(int64_t)bseq * Hq + h * G + g] : 0.f;
-            m_w[r] = -INFINITY;
-            l_run[r] = 0.f;
+        for (int e = 0; e < EG; ++e) {
+            gh[e] = lq + 4 * e;
+            cqv[e] = gh[e] < G ? cq[(int64_t)bseq * Hq + h * G + gh[e]] : 0.f;
+            m_w[e] = -INFINITY;
+            l_run[e] = 0.f;
         }
 
         struct KIn {
@@ -1122,15 +1124,18 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             const int sl = it & 1;
             const uint32_t jk[4] = {in.ik[0] & 0xffffu, in.ik[0] >> 16, in.ik[1] & 0xffffu,
                                     in.ik[1] >> 16};
-            f32x4 qv[4];
+            // q.R^K of the token's references for the lane's heads (unused
+            // slots read the all-zero row Rt)
+            float qv[EG][4];
             float kek = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // unused slots read the all-zero row Rt
                 const bool ok = jk[i] != kIdxUnused;
                 kek += ok ? 1.f : 0.f;
-                qv[i] = *reinterpret_cast<const f32x4 *>(at_byte(
-                    qr_u, ((ok ? jk[i] : (uint32_t)Rt) * (uint32_t)GQ + (hq_ok ? 4u * lq : 0u)) * 4u));
+                const uint32_t row = (ok ? jk[i] : (uint32_t)Rt) * (uint32_t)GQ;
+#pragma unroll
+                for (int e = 0; e < EG; ++e)
+                    qv[e][i] = *at_byte(qr_u, (row + (uint32_t)min(gh[e], GQ - 1)) * 4u);
             }
             // the next tile's loads go out after these table reads, so waiting
             // for the table does not wait for them; they are issued on every
@@ -1153,71 +1158,70 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const u32x4 hv = {as_u32(g0), as_u32(g1), as_u32(g2), as_u32(g3)};
                 S = mfma16_f16(uA[j], as_f16x8(hv), S);
             }
-            // scores of token l16 for heads 4 lq + r
+            // S[4 q + r][t] sits in lane 16 q + t, register r.  Move it so that
+            // lane (lq, l16) holds head lq + 4 e of token l16: all 64 lanes
+            // then carry one (token, head) pair each for G <= 4.
+            float sv[EG];
+#pragma unroll
+            for (int e = 0; e < EG; ++e) {
+                const int srcl = 16 * e + l16;
+                const float x0 = __shfl(S[0], srcl), x1 = __shfl(S[1], srcl);
+                const float x2 = __shfl(S[2], srcl), x3 = __shfl(S[3], srcl);
+                sv[e] = lq == 0 ? x0 : lq == 1 ? x1 : lq == 2 ? x2 : x3;
+            }
             const bool tok_ok = t0 + TH * src + l16 < qe;
             const float inv_k = __builtin_amdgcn_rcpf(kek);
-            // reference maxima: the larger of the two waves' previous ones
-            const f32x4 pm0 = *reinterpret_cast<const f32x4 *>(&msl[sl ^ 1][0][4 * lq]);
-            const f32x4 pm1 = *reinterpret_cast<const f32x4 *>(&msl[sl ^ 1][1][4 * lq]);
-            float s[4], mref[4];
+            float s[EG], mref[EG];
             bool up = false;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float rs = (qv[0][r] + qv[1][r]) + (qv[2][r] + qv[3][r]);
-                const float sv = scale * (S[r] + rs * inv_k + cqv[r]);
-                s[r] = (tok_ok && 4 * lq + r < G) ? sv : -INFINITY;
-                mref[r] = fmaxf(pm0[r], pm1[r]);
-                up = up || s[r] > mref[r] + kSlack;
+            for (int e = 0; e < EG; ++e) {
+                const float rs = (qv[e][0] + qv[e][1]) + (qv[e][2] + qv[e][3]);
+                const float v = scale * (sv[e] + rs * inv_k + cqv[e]);
+                s[e] = (tok_ok && gh[e] < G) ? v : -INFINITY;
+                // reference maximum: the larger of the two waves' previous ones
+                mref[e] = fmaxf(msl[sl ^ 1][0][gh[e]], msl[sl ^ 1][1][gh[e]]);
+                up = up || s[e] > mref[e] + kSlack;
             }
             if (__builtin_amdgcn_ballot_w64(up)) {
-                // a score far above the reference: raise it to the row group's
-                // maximum (all 16 lanes of a row group agree)
+                // a score far above the reference: raise it to the maximum over
+                // the 16 tokens (the 16 lanes of a row group share the head)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float tm = s[r];
+                for (int e = 0; e < EG; ++e) {
+                    float tm = s[e];
 #pragma unroll
                     for (int o = 8; o > 0; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 16));
-                    mref[r] = tm > mref[r] + kSlack ? tm : mref[r];
+                    mref[e] = tm > mref[e] + kSlack ? tm : mref[e];
                 }
             }
             bool moved = false;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) moved = moved || mref[r] != m_w[r];
+            for (int e = 0; e < EG; ++e) moved = moved || mref[e] != m_w[e];
             if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    l_run[r] *= mref[r] == -INFINITY ? 1.f : __expf(m_w[r] - mref[r]);
-                    m_w[r] = mref[r];
+                for (int e = 0; e < EG; ++e) {
+                    l_run[e] *= mref[e] == -INFINITY ? 1.f : __expf(m_w[e] - mref[e]);
+                    m_w[e] = mref[e];
                 }
             }
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = s[r] == -INFINITY ? 0.f : __expf(s[r] - m_w[r]);
-                l_run[r] += p[r];
-            }
-            // publish
-            const uint32_t jv[4] = {in.iv[0] & 0xffffu, in.iv[0] >> 16, in.iv[1] & 0xffffu,
-                                    in.iv[1] >> 16};
-            float kev = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kev += jv[i] != kIdxUnused ? 1.f : 0.f;
+            // publish p (f16, by token), p / k_eff on the token's used V slots
+            // (bf16, by (token, slot) row) and the maxima
+            const uint32_t vmask_lo = ((in.iv[0] & 0xffffu) != kIdxUnused ? 0x0000ffffu : 0u) |
+                                      ((in.iv[0] >> 16) != kIdxUnused ? 0xffff0000u : 0u);
+            const uint32_t vmask_hi = ((in.iv[1] & 0xffffu) != kIdxUnused ? 0x0000ffffu : 0u) |
+                                      ((in.iv[1] >> 16) != kIdxUnused ? 0xffff0000u : 0u);
+            const float kev = (float)(__builtin_popcount(vmask_lo) + __builtin_popcount(vmask_hi)) *
+                              (1.f / 16.f);
             const float inv_v = __builtin_amdgcn_rcpf(kev);
-            if (hq_ok) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int g = 4 * lq + r;
-                    if (g < G) {
-                        pw[sl][src][g][l16] = (_Float16)p[r];
-                        const uint32_t wb = f2bf(p[r] * inv_v);
-                        const uint32_t w0 = jv[0] != kIdxUnused ? wb : 0u;
-                        const uint32_t w1 = jv[1] != kIdxUnused ? wb : 0u;
-                        const uint32_t w2 = jv[2] != kIdxUnused ? wb : 0u;
-                        const uint32_t w3 = jv[3] != kIdxUnused ? wb : 0u;
-                        *reinterpret_cast<u32x2 *>(&wr[sl][g][(TH * src + l16) * KX]) =
-                            u32x2{w0 | (w1 << 16), w2 | (w3 << 16)};
-                        if (l16 == 0) msl[sl][src][g] = m_w[r];
-                    }
+            for (int e = 0; e < EG; ++e) {
+                const float p = s[e] == -INFINITY ? 0.f : __expf(s[e] - m_w[e]);
+                l_run[e] += p;
+                if (gh[e] < G) {
+                    pw[sl][src][gh[e]][l16] = (_Float16)p;
+                    const uint32_t wb = pack_bf16(p * inv_v, p * inv_v);
+                    *reinterpret_cast<u32x2 *>(&wr[sl][gh[e]][(TH * src + l16) * KX]) =
+                        u32x2{wb & vmask_lo, wb & vmask_hi};
+                    if (l16 == 0) msl[sl][src][gh[e]] = m_w[e];
                 }
             }
         };
@@ -1235,13 +1239,13 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         }
         // per-head sums of this wave's tokens
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float lsum = l_run[r];
+        for (int e = 0; e < EG; ++e) {
+            float lsum = l_run[e];
 #pragma unroll
             for (int o = 8; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 16);
             if (l16 == 0) {
-                lfin[src][4 * lq + r] = lsum;
-                mfin[src][4 * lq + r] = m_w[r];
+                lfin[src][gh[e]] = lsum;
+                mfin[src][gh[e]] = m_w[e];
             }
         }
         __syncthreads();
@@ -1463,7 +1467,8 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
-    hipLaunchKernelGGL((main_ws_kernel<D, DC, HID>), dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
+    auto kern = G <= 4 ? main_ws_kernel<D, DC, HID, 1> : main_ws_kernel<D, DC, HID, 2>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
                        (const bf16_t *)vc.lat, vc.idx, (const bf16_t *)kd.w1, kd.b1,
