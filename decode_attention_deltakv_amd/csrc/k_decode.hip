@@ -15,8 +15,8 @@
 // sum per query head) over token partitions, merged by log-sum-exp.
 //
 // Kernels, in stream order:
-//   qprep     u_g = W2K^T q_g and c_g = q_g . b2K for every query head
-//   refscore  qR[j][g] = q_g . R^K_j for every reference row
+//   prep      qR[j][g] = q_g . R^K_j for every reference row, and
+//             u_g = W2K^T q_g, c_g = q_g . b2K for every query head
 //   main      one block per (partition, KV head, sequence): token partitions
 //             rebuild hidden tiles and fold them into (m, l, acc_r, acc_h);
 //             reference partitions fold the reference tokens themselves
@@ -88,64 +88,6 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     off += align_up((size_t)dm.B * dm.H * p.P * G * kPStride * 4);
     p.total = off;
     return p;
-}
-
-// u_g = W2K^T q_g (hidden entries), c_g = q_g . b2K.  grid (Hq, B); thread i
-// owns hidden unit i and reads column i of W2K (coalesced across threads).
-template <typename T>
-__global__ __launch_bounds__(256) void qprep_kernel(const T *__restrict__ q, int Hq, int d,
-                                                    const T *__restrict__ w2, int hid,
-                                                    const float *__restrict__ b2,
-                                                    float *__restrict__ u,
-                                                    float *__restrict__ cq) {
-    __shared__ float qs[kMaxD];
-    __shared__ float red[4];
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const T *qrow = q + ((int64_t)b * Hq + g) * d;
-    if (tid < d) qs[tid] = to_f32(qrow[tid]);
-    __syncthreads();
-    if (tid < hid) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < d; c += 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[e] += to_f32(w2[(int64_t)(c + e) * hid + tid]) * qs[c + e];
-        }
-        u[((int64_t)b * Hq + g) * kMaxH + tid] =
-            ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    }
-    float v = (b2 && tid < d) ? qs[tid] * b2[tid] : 0.f;
-    v = wave_sum(v);
-    if ((tid & 63) == 0) red[tid >> 6] = v;
-    __syncthreads();
-    if (tid == 0) cq[(int64_t)b * Hq + g] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// qR[j][g] = q_g . R^K_j over the Rt reference rows (heads padded to
-// qr_heads(G) with zeros).  grid (ceil(Rt/64), H, B).
-template <typename T>
-__global__ __launch_bounds__(256) void refscore_kernel(const T *__restrict__ q, int Hq, int G,
-                                                       int d, const T *__restrict__ krefs,
-                                                       int64_t Rcap, int64_t Rt,
-                                                       float *__restrict__ qr) {
-    __shared__ float qs[kMaxG][kMaxD];
-    const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, H = gridDim.y;
-    for (int i = tid; i < G * d; i += 256)
-        qs[i / d][i % d] = to_f32(q[((int64_t)b * Hq + h * G + i / d) * d + i % d]);
-    __syncthreads();
-    const int64_t unit = (int64_t)b * H + h;
-    const int GQ = qr_heads(G);
-    for (int i = tid; i < 64 * GQ; i += 256) {
-        const int64_t j = (int64_t)blockIdx.x * 64 + i / GQ;
-        const int g = i % GQ;
-        if (j > Rt) continue;
-        float acc = 0.f;
-        if (g < G && j < Rt) {
-            const T *r = krefs + (unit * Rcap + j) * d;
-            for (int c = 0; c < d; ++c) acc += qs[g][c] * to_f32(r[c]);
-        }
-        qr[(unit * qr_rows(Rt) + j) * GQ + g] = acc;
-    }
 }
 
 template <typename T>
@@ -333,8 +275,7 @@ __global__ __launch_bounds__(256) void main_kernel(
     }
 }
 
-// Log-sum-exp merge of the partitions of one query head; W2V applied to the
-// merged hidden sum.  grid (Hq, B).
+// Block-wide max or sum (256 threads).
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = is_max ? wave_max(v) : wave_sum(v);
@@ -346,14 +287,158 @@ __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) 
     return r;
 }
 
+// Eight consecutive elements as fp32 (16-byte loads; 16-byte aligned).
+__device__ __forceinline__ void load8(const bf16_t *p, float (&v)[8]) {
+    const u32x4 w = ld16(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = a[i];
+        v[4 + i] = b[i];
+    }
+}
+
+// Query-side tables of one decode step, one launch.  grid (nrb + G, H, B):
+//   blockIdx.x <  nrb  rows [256 x, 256 x + 256) of qR[j][g] = q_g . R^K_j
+//                      (bf16: matrix cores; row Rt is the zero row)
+//   blockIdx.x >= nrb  u_g = W2K^T q_g and c_g = q_g . b2K for query head
+//                      g = x - nrb of the KV head
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int H, int64_t P,
-                                                      const float *__restrict__ part,
-                                                      const T *__restrict__ vw2, int vhid,
-                                                      const float *__restrict__ vb2,
-                                                      float *__restrict__ out) {
-    __shared__ float acch[kMaxH];
+__global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int Hq, int G, int d,
+                                                   const T *__restrict__ krefs, int64_t Rcap,
+                                                   int64_t Rt, int nrb, const T *__restrict__ w2,
+                                                   int hid, const float *__restrict__ b2,
+                                                   float *__restrict__ u, float *__restrict__ cq,
+                                                   float *__restrict__ qr) {
+    __shared__ float qs[kMaxG][kMaxD];
+    __shared__ float red[1][32][kMaxH];
+    const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, H = gridDim.y;
+    for (int i = tid; i < G * d; i += 256)
+        qs[i / d][i % d] = to_f32(q[((int64_t)b * Hq + h * G + i / d) * d + i % d]);
+    __syncthreads();
+    const int64_t unit = (int64_t)b * H + h;
+    const int GQ = qr_heads(G);
+    if ((int)blockIdx.x < nrb) {
+        if constexpr (sizeof(T) == 2) {
+            // bf16: matrix cores, qR^T tile = R (16 rows x d) . Q^T (d x 16
+            // heads); reference rows come straight from global memory
+            const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+            const u32x4 zero4 = {0u, 0u, 0u, 0u};
+            const T *qg = q + ((int64_t)b * Hq + h * G + (l16 < G ? l16 : 0)) * d;
+            bf16x8 qb[kMaxD / 32];
+#pragma unroll
+            for (int ks = 0; ks < kMaxD / 32; ++ks)
+                qb[ks] = as_bf16x8(l16 < G && 32 * ks < d ? ld16(qg + 32 * ks + 8 * lq) : zero4);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int64_t j0 = (int64_t)blockIdx.x * 256 + 64 * it + 16 * w;
+                if (j0 > Rt) break;
+                const int64_t jr = min(j0 + l16, Rt - 1 < 0 ? 0 : Rt - 1);
+                const T *r = krefs + (unit * Rcap + jr) * d;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < kMaxD / 32; ++ks)
+                    if (32 * ks < d) acc = mfma16_bf16(as_bf16x8(ld16(r + 32 * ks + 8 * lq)), qb[ks], acc);
+                // acc[r] = qR[j0 + 4 lq + r][head l16]
+                if (l16 < GQ) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t j = j0 + 4 * lq + e;
+                        if (j <= Rt)
+                            qr[(unit * qr_rows(Rt) + j) * GQ + l16] = (j < Rt && l16 < G) ? acc[e] : 0.f;
+                    }
+                }
+            }
+            return;
+        } else {
+            const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+            if (j > Rt) return;
+            float acc[kMaxG];
+#pragma unroll
+            for (int g = 0; g < kMaxG; ++g) acc[g] = 0.f;
+            if (j < Rt) {
+                const T *r = krefs + (unit * Rcap + j) * d;
+                for (int c0 = 0; c0 < d; c0 += 8) {
+                    float v[8];
+                    load8(r + c0, v);
+#pragma unroll
+                    for (int g = 0; g < kMaxG; ++g) {
+                        if (g >= G) break;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[g] += qs[g][c0 + e] * v[e];
+                    }
+                }
+            }
+            float *dst = qr + (unit * qr_rows(Rt) + j) * GQ;
+#pragma unroll
+            for (int g4 = 0; g4 < kMaxG; g4 += 4) {
+                if (g4 >= GQ) break;
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = g4 + e < G ? acc[g4 + e] : 0.f;
+                *reinterpret_cast<f32x4 *>(dst + g4) = o;
+            }
+            return;
+        }
+    }
+    // u_g = W2K^T q_g for query head g = blockIdx.x - nrb: thread (hb, cg)
+    // sums 8 consecutive hidden units (one 16-byte load per row) over a slice
+    // of head_dim; the slices are then added in LDS
+    const int g = (int)blockIdx.x - nrb;
+    const int NHB = hid / 8, NCG = 256 / NHB, cper = d / NCG;
+    const int hb = tid % NHB, cg = tid / NHB;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+    for (int c = cg * cper; c < (cg + 1) * cper; ++c) {
+        float v[8];
+        load8(w2 + (int64_t)c * hid + 8 * hb, v);
+        const float qv = qs[g][c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e] * qv;
+    }
+    float *redf = &red[0][0][0];  // [NCG][hid]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) redf[cg * hid + 8 * hb + e] = acc[e];
+    __syncthreads();
+    for (int i = tid; i < hid; i += 256) {
+        float sum = 0.f;
+        for (int k2 = 0; k2 < NCG; ++k2) sum += redf[k2 * hid + i];
+        u[((int64_t)b * Hq + h * G + g) * kMaxH + i] = sum;
+    }
+    if (tid < 64) {
+        float v = 0.f;
+        if (b2)
+            for (int c = tid; c < d; c += 64) v += qs[g][c] * b2[c];
+        v = wave_sum(v);
+        if (tid == 0) cq[(int64_t)b * Hq + h * G + g] = v;
+    }
+}
+
+// Log-sum-exp merge of the partitions of one query head, then W2V applied to
+// the merged hidden sum.  grid (Hq, B).  The merge of the record vectors runs
+// with one float4 column per thread and the partitions split across thread
+// groups, so all partition loads of a thread are independent.
+template <typename T>
+__global__ __launch_bounds__(256) void combine2_kernel(int Hq, int G, int d, int H, int64_t P,
+                                                       const float *__restrict__ part,
+                                                       const T *__restrict__ vw2, int vhid,
+                                                       const float *__restrict__ vb2,
+                                                       float *__restrict__ out) {
     __shared__ float wgt[kMaxParts];
+    __shared__ f32x4 gred[8][(kMaxD + kMaxH) / 4];
+    __shared__ float accr[kMaxD];
+    __shared__ float acch[kMaxH];
+    __shared__ float ored[4][kMaxD];
     __shared__ float red[4];
     const int gq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int h = gq / G, g = gq % G;
@@ -372,23 +457,49 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int G, int d, int 
     }
     const float L = block_reduce(lsum, red, false);
     const float Lt = block_reduce(ltsum, red, false);  // (its barriers also publish wgt)
-    for (int o = tid; o < vhid; o += 256) {
-        float a = 0.f;
+    // columns: acc_r as d/4 float4s, then acc_h as vhid/4 float4s
+    const int ncr = d / 4, nc = ncr + vhid / 4;
+    const int ngrp = min(8, 256 / nc);
+    const int col = tid % nc, grp = tid / nc;
+    if (grp < ngrp) {
+        const int off = col < ncr ? 4 + 4 * col : 4 + kMaxD + 4 * (col - ncr);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-        for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + kMaxD + o];
-        acch[o] = a;
+        for (int64_t p = grp; p < P; p += ngrp) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(base + p * pstep + off);
+            a += wgt[p] * v;
+        }
+        gred[grp][col] = a;
     }
     __syncthreads();
-    for (int c = tid; c < d; c += 256) {
-        float a = 0.f;
-#pragma unroll 8
-        for (int64_t p = 0; p < P; ++p) a += wgt[p] * base[p * pstep + 4 + c];
-        float wsum = 0.f;
-        const T *wr = vw2 + (int64_t)c * vhid;
-#pragma unroll 8
-        for (int o = 0; o < vhid; ++o) wsum += to_f32(wr[o]) * acch[o];
-        const float bias = vb2 ? vb2[c] : 0.f;
-        out[((int64_t)b * Hq + gq) * d + c] = (a + wsum + Lt * bias) / L;
+    if (tid < nc) {
+        f32x4 a = gred[0][tid];
+        for (int k2 = 1; k2 < ngrp; ++k2) a += gred[k2][tid];
+        float *dst = tid < ncr ? &accr[4 * tid] : &acch[4 * (tid - ncr)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = a[e];
+    }
+    __syncthreads();
+    // out[c] = (acc_r[c] + W2V[c] . acc_h + Lt b2V[c]) / L; the hidden sum of
+    // a row is split over 256 / d threads
+    const int nsp = 256 / d;
+    const int c = tid % d, sp = tid / d;
+    const int oper = vhid / nsp;
+    float wsum = 0.f;
+    const T *wr = vw2 + (int64_t)c * vhid + sp * oper;
+    for (int o = 0; o < oper; o += 8) {
+        float v[8];
+        load8(wr + o, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wsum += v[e] * acch[sp * oper + o + e];
+    }
+    ored[sp][c] = wsum;
+    __syncthreads();
+    if (tid < d) {
+        float ws = 0.f;
+        for (int k2 = 0; k2 < nsp; ++k2) ws += ored[k2][tid];
+        const float bias = vb2 ? vb2[tid] : 0.f;
+        out[((int64_t)b * Hq + gq) * d + tid] = (accr[tid] + ws + Lt * bias) / L;
     }
 }
 
@@ -468,7 +579,6 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 
     const int hbase = w * HW;
     const int cbase = w * DW;
-    const int64_t ubase_n = (int64_t)unit * Ncap;
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
     const int GQ = qr_heads(G);
     const float *qr_u = qr + (int64_t)unit * qr_rows(Rt) * GQ;
@@ -648,7 +758,6 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     // inverse of the token permutation of the P operand
     const int st_slot = st < 16 ? 8 * (st >> 2) + (st & 3) : 8 * ((st - 16) >> 2) + 4 + (st & 3);
 
-    const int64_t qa = qa_, qe = qe_;
 
     // ---- loaders.  Loads go to clamped, always-valid addresses and keep
     // their raw values; validity is applied where the values are used (a
@@ -1531,11 +1640,10 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     float *cq = (float *)(w + pl.off_cq);
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
-    hipLaunchKernelGGL(qprep_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, (const T *)q, Hq, dm.d,
-                       (const T *)kd.w2, kd.hidden, kd.b2, u, cq);
-    hipLaunchKernelGGL(refscore_kernel<T>, dim3((unsigned)((qr_rows(pl.Rt) + 63) / 64), dm.H, dm.B),
-                       dim3(256), 0, st, (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R,
-                       pl.Rt, qr);
+    const int nrb = (int)((qr_rows(pl.Rt) + 255) / 256);
+    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)(nrb + G), dm.H, dm.B), dim3(256), 0, st,
+                       (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R, pl.Rt, nrb,
+                       (const T *)kd.w2, kd.hidden, kd.b2, u, cq, qr);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
         if (mfma_eligible(dm, kd, vd)) {
@@ -1562,7 +1670,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            (const T *)kc.lat, kc.idx, (const T *)vc.refs, (const T *)vc.lat,
                            vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act, (const T *)vd.w1,
                            vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part);
-    hipLaunchKernelGGL(combine_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, Hq, G, dm.d, dm.H,
+    hipLaunchKernelGGL(combine2_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, Hq, G, dm.d, dm.H,
                        pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out);
     return hipGetLastError();
 }
