@@ -301,7 +301,11 @@ template <int LK>
 __device__ __forceinline__ void list_insert(float (&a)[LK], float v) {
 #pragma unroll
     for (int i = LK - 1; i > 0; --i) a[i] = __builtin_amdgcn_fmed3f(a[i - 1], a[i], v);
-    a[0] = fmaxf(a[0], v);
+    // max(a[0], v) as one instruction: the list holds no NaN, so the
+    // NaN-quieting operations the compiler adds around fmaxf are not needed
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(a[0]), "v"(v));
+    a[0] = m;
 }
 
 template <int D, int LK>
@@ -445,10 +449,11 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     const float *usqn = sqn + (int64_t)unit * Rcap;
 
     const int64_t qlast = min(qb + 255, qend - 1);
-    const int64_t ncand_max = (tok_pos(qlast, s) + s - 1) / s;
+    // reference counts stay below 2^16: 32-bit arithmetic in the loop
+    const int ncand_max = (int)((tok_pos(qlast, s) + s - 1) / s);
 
     int64_t qn[2], pos[2];
-    int64_t ncand[2], ncand_lo[2];
+    int ncand[2], ncand_lo[2];
     bool valid[2];
     bf16x8 xb[2][KSTEPS];
 #pragma unroll
@@ -457,9 +462,9 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         valid[nt] = qq < qend;
         qn[nt] = min(qq, qend - 1);
         pos[nt] = tok_pos(qn[nt], s);
-        ncand[nt] = (pos[nt] + s - 1) / s;
+        ncand[nt] = (int)((pos[nt] + s - 1) / s);
         const int64_t qf = min(qb + 64 * w + 32 * nt, qend - 1);
-        ncand_lo[nt] = (tok_pos(qf, s) + s - 1) / s;
+        ncand_lo[nt] = (int)((tok_pos(qf, s) + s - 1) / s);
         const bf16_t *xr = x + ((int64_t)unit * nrows + (pos[nt] - t0)) * D;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) xb[nt][ks] = as_bf16x8(ld16(xr + 16 * ks + 8 * hl));
@@ -471,15 +476,15 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         for (int e = 0; e < LK; ++e) lst[nt][e] = -INFINITY;
 
     float rmax2 = 0.f;
-    auto stage_load = [&](int64_t jbase, int b) {
+    auto stage_load = [&](int jbase, int b) {
 #pragma unroll
         for (int m = 0; m < DMA_IT; ++m) {
             const int it = tid + 256 * m;
             const int row = it / CH, c8 = it % CH;
             const int sc8 = c8 ^ (row & 7);
-            const int64_t j = min(jbase + row, ncand_max - 1);
+            const uint32_t j = (uint32_t)min(jbase + row, ncand_max - 1);
             __builtin_amdgcn_global_load_lds(
-                (const void *)(urefs + j * D + 8 * sc8),
+                (const void *)at_byte(urefs, (j * D + 8u * sc8) * 2u),
                 (__attribute__((address_space(3))) void *)&rt[b][(256 * m + 64 * w) / CH][0], 16,
                 0, 0);
         }
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
 
     for (int st = 0; st < nstage; ++st) {
         const int b = st & 1;
-        const int64_t jst = (int64_t)st * RB;
+        const int jst = st * RB;
         const bool more = st + 1 < nstage;
         if (more) {
             stage_load(jst + RB, b ^ 1);
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int64_t j0 = jst + 32 * mb;
+            const int j0 = jst + 32 * mb;
             if (j0 >= ncand_max) break;
             f32x16 init;
 #pragma unroll
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
                 if (j0 + 32 > ncand_lo[nt]) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int64_t j = j0 + 8 * (i / 4) + 4 * hl + (i % 4);
+                        const int j = j0 + 8 * (i / 4) + 4 * hl + (i % 4);
                         sc[i] = j < ncand[nt] ? sc[i] : -INFINITY;
                     }
                 }
