@@ -42,9 +42,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # change to it the traffic is reported as null until it is measured again.
 DECODE_TRAFFIC = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "840709aea770",
-    "fetch_kib": {"main_mfma": 85013.3, "refscore": 8242.5, "combine": 2366.5, "qprep": 279.0},
-    "write_kib": {"main_mfma": 3880.0, "refscore": 1024.0, "combine": 16.0, "qprep": 33.0},
+    "source_sha256": "592829c37ca7",
+    "fetch_kib": {"main_ws": 85708.6, "prep": 8539.3, "combine2": 2389.0},
+    "write_kib": {"main_ws": 3880.1, "prep": 1061.2, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
