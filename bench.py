@@ -93,22 +93,30 @@ class Setup:
         self.dk = dk
         self.wl = wl
         dt = wl.torch_dtype
-        self.shape = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, wl.T,
-                              dk.F32 if wl.dtype == "fp32" else dk.BF16)
         L, B, H, T, d = wl.layers, wl.batch, wl.kv_heads, wl.T, wl.head_dim
+        # streaming: the cache also holds the tokens appended during decode
+        self.A = wl.appends
+        cap = T + self.A
+        self.shape = dk.Shape(B, H, d, wl.stride, wl.k, wl.d_c, cap,
+                              dk.F32 if wl.dtype == "fp32" else dk.BF16)
         t0 = time.time()
-        self.x = []          # [layer][stream] -> [B, H, T, d]
+        self.x = []          # [layer][stream] -> [B, H, T, d]     (the prompt)
+        self.xa = []         # [layer][stream] -> [A, B, H, 1, d]  (appended tokens)
         for l in range(L):
-            row = []
+            row, rowa = [], []
             for st in (0, 1):
-                x = torch.empty(B, H, T, d, dtype=dt, device="cuda")
+                x = torch.empty(B, H, cap, d, dtype=dt, device="cuda")
                 for b in range(B):
                     for h in range(H):
-                        x[b, h] = kv_rows(T, d, wl.n_dirs, wl.n_centroids,
+                        x[b, h] = kv_rows(cap, d, wl.n_dirs, wl.n_centroids,
                                           key=unit_key(widx, b, l, h, st), dtype=dt,
                                           device="cuda")
-                row.append(x)
+                row.append(x[:, :, :T].contiguous() if self.A else x)
+                if self.A:
+                    rowa.append(x[:, :, T:].permute(2, 0, 1, 3).unsqueeze(3).contiguous())
+                del x
             self.x.append(row)
+            self.xa.append(rowa)
         torch.cuda.synchronize()
         log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
         self.comp, self.dec = [], []
@@ -122,9 +130,11 @@ class Setup:
                                                          device="cuda"))
                              for st in (0, 1)])
         self.cache = [[dk.Cache(self.shape) for _ in (0, 1)] for _ in range(L)]
-        self.cws = dk.workspace(dk.compress_workspace_bytes(self.shape, 0, T))
+        self.chunk = wl.chunk or T
+        self.cws = dk.workspace(max(dk.compress_workspace_bytes(self.shape, 0, min(T, self.chunk)),
+                                    dk.compress_workspace_bytes(self.shape, T - 1, T)))
         self.Hq = wl.q_heads
-        self.dws = dk.workspace(dk.decode_workspace_bytes(self.shape, self.Hq, T))
+        self.dws = dk.workspace(dk.decode_workspace_bytes(self.shape, self.Hq, cap))
         self.out = torch.empty(B, self.Hq, d, dtype=torch.float32, device="cuda")
         self.stats = torch.zeros(4, dtype=torch.int32, device="cuda")
         self.scale = 1.0 / math.sqrt(d)
@@ -132,16 +142,38 @@ class Setup:
                              device="cuda").reshape(64, L, B, self.Hq, d)
 
     def compress_all(self):
+        """The whole prompt: one call per (layer, stream), or chunk by chunk
+        for the streaming workload (references accumulate across chunks)."""
         dk, sh, T = self.dk, self.shape, self.wl.T
+        for c0 in range(0, T, self.chunk):
+            c1 = min(T, c0 + self.chunk)
+            for l in range(self.wl.layers):
+                for st in (0, 1):
+                    x = self.x[l][st] if (c0, c1) == (0, T) else \
+                        self.x[l][st][:, :, c0:c1].contiguous()
+                    dk.build_refs(sh, x, c0, c1, self.cache[l][st])
+                    dk.compress(sh, x, c0, c1, self.comp[l][st], self.cache[l][st], self.cws,
+                                self.stats)
+
+    def decode_step(self, i, k=0):
+        """Decode step k of a bench step, queries i.  Streaming: first append
+        token T + k (reference copy or compression against the references so
+        far), then attend over T + k + 1 tokens."""
+        qs = self.qbank[i % 64]
+        if not self.A:
+            self.decode_step_q(qs)
+            return
+        dk, sh, T = self.dk, self.shape, self.wl.T
+        p = T + k
         for l in range(self.wl.layers):
             for st in (0, 1):
-                x = self.x[l][st]
-                dk.build_refs(sh, x, 0, T, self.cache[l][st])
-                dk.compress(sh, x, 0, T, self.comp[l][st], self.cache[l][st], self.cws,
+                xa = self.xa[l][st][k]
+                dk.build_refs(sh, xa, p, p + 1, self.cache[l][st])
+                dk.compress(sh, xa, p, p + 1, self.comp[l][st], self.cache[l][st], self.cws,
                             self.stats)
-
-    def decode_step(self, i):
-        self.decode_step_q(self.qbank[i % 64])
+            c, d = self.cache[l], self.dec[l]
+            dk.decode_attn(sh, self.Hq, p + 1, qs[l], c[0], d[0], c[1], d[1], self.scale,
+                           self.out, self.dws)
 
     def decode_step_q(self, qs):
         dk, sh, T = self.dk, self.shape, self.wl.T
@@ -300,6 +332,8 @@ def main():
     wl = WORKLOADS[a.workload]
     widx = workload_index(a.workload)
     dsteps = wl.decode_steps if a.decode_steps is None else a.decode_steps
+    if wl.appends:
+        dsteps = min(dsteps, wl.appends)   # each streaming decode step appends a token
     torch.cuda.set_device(0)
     S = Setup(wl, widx)
     stream = torch.cuda.current_stream()
@@ -318,7 +352,7 @@ def main():
         S.compress_all()
         e1.record(stream)
         for k in range(dsteps):
-            S.decode_step(i * dsteps + k)
+            S.decode_step(i * dsteps + k, k)
         e2.record(stream)
         return e0, e1, e2
 
@@ -415,7 +449,8 @@ def main():
                 "N(0,1) queries)",
         "config": {"workload": wl.name, "layers": wl.layers, "batch": B, "kv_heads": wl.kv_heads,
                    "q_heads": wl.q_heads, "head_dim": wl.head_dim, "T": T, "stride": wl.stride,
-                   "k": wl.k, "d_c": wl.d_c, "hidden": wl.hidden, "decode_steps": dsteps},
+                   "k": wl.k, "d_c": wl.d_c, "hidden": wl.hidden, "decode_steps": dsteps,
+                   "prompt_chunk": wl.chunk, "appends_per_step": min(dsteps, wl.appends)},
         "compress_ms_per_step": comp_ms,
         "compress_tflops": compress_flops(wl) / (comp_ms * 1e-3) / 1e12,
         "decode_ms_per_step": dec_ms,

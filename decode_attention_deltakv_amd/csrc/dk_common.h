@@ -15,6 +15,11 @@ namespace dk {
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 constexpr uint16_t kIdxUnused = 0xFFFFu;
+// Compressed-token ranges up to this length (per unit) are selected by the
+// exact block-per-token scan instead of the matrix-core search.
+constexpr int64_t kSmallRange = 32;
+// Most blocks the reference range of one such token is split over.
+constexpr int64_t kSplitMax = 64;
 
 // ---- layout: positions, reference ordinals, token ordinals ---------------------
 

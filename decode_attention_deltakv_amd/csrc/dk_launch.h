@@ -57,6 +57,11 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
                                int64_t q0, int64_t nq, const CacheArgs &c,
                                const uint64_t *list, const uint32_t *list_count,
                                int64_t list_cap, hipStream_t st);
+// exact selection of a few tokens (bf16) with the references split over
+// blocks; workspace of select_split_ws_bytes
+size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);
+hipError_t launch_select_split(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                               int64_t nq, const CacheArgs &c, void *ws, hipStream_t st);
 }  // namespace dk
 
 namespace dk {

@@ -254,7 +254,8 @@ bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     if (dm.dtype != 1) return 0;
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
-    return 256 + (size_t)nq * dm.B * dm.H * sizeof(uint64_t);
+    return std::max<size_t>(256 + (size_t)nq * dm.B * dm.H * sizeof(uint64_t),
+                            select_split_ws_bytes(dm, t0, t1));
 }
 
 hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
@@ -265,11 +266,15 @@ hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1
     const int64_t nq = toks_upto(t1, dm.s) - q0;
     if (nq <= 0) return hipSuccess;
     hipError_t e;
-    if (dm.dtype == 1) {
+    if (dm.dtype == 1 && nq > kSmallRange) {
         uint32_t *fcount = (uint32_t *)ws;
         uint64_t *flist = (uint64_t *)((char *)ws + 256);
         e = launch_select_mfma(dm, x, t0, t1, q0, nq, c, flist, fcount, stats, st);
+    } else if (dm.dtype == 1) {
+        // a few tokens (a streaming append): exact, references split over blocks
+        e = launch_select_split(dm, x, t0, t1, q0, nq, c, ws, st);
     } else {
+        // fp32 storage, or a few tokens: exact scan
         e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, st);
     }
     if (e != hipSuccess) return e;

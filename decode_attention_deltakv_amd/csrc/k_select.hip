@@ -164,14 +164,17 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void select_exact_block_kernel(
     const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
     int64_t Rcap, int64_t Ncap, int64_t q0, int k, uint16_t *__restrict__ idx,
-    const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count) {
+    const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count, int64_t nunits,
+    int64_t nq) {
     __shared__ double xs[D];
     __shared__ double wd[4];
     __shared__ int wj[4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t n = (int64_t)*list_count;
+    // work items: the listed (unit, token) entries, or without a list every
+    // token of [q0, q0 + nq) of every unit
+    const int64_t n = list ? (int64_t)*list_count : nunits * nq;
     for (int64_t wi = blockIdx.x; wi < n; wi += gridDim.x) {
-        const uint64_t e = list[wi];
+        const uint64_t e = list ? list[wi] : (((uint64_t)(wi / nq) << 32) | (uint64_t)(wi % nq));
         const int64_t unit = (int64_t)(e >> 32);
         const int64_t q = q0 + (int64_t)(e & 0xffffffffu);
         const int64_t p = tok_pos(q, s);
@@ -244,6 +247,155 @@ __global__ __launch_bounds__(256) void select_exact_block_kernel(
     }
 }
 
+// Exact top-k of a few tokens with their candidate references split over many
+// blocks (a streaming append has one token per unit but up to 65535
+// references): block (split, item) scans references [split * chunk, ...) of
+// token item with the same fp64 arithmetic as the scans above and writes its
+// kMaxK best (distance, ordinal) pairs; select_merge_kernel takes the k best
+// over all splits.  grid (nsplit, units * nq).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_split_kernel(
+    const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
+    int64_t Rcap, int64_t q0, int64_t nq, int chunk, double *__restrict__ pd,
+    int *__restrict__ pj) {
+    __shared__ double xs[D];
+    __shared__ double wd[4];
+    __shared__ int wj[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t item = blockIdx.y;
+    const int64_t unit = item / nq, q = q0 + item % nq;
+    const int64_t p = tok_pos(q, s);
+    const int64_t ncand = (p + s - 1) / s;
+    const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
+    double *od = pd + (item * gridDim.x + blockIdx.x) * kMaxK;
+    int *oj = pj + (item * gridDim.x + blockIdx.x) * kMaxK;
+    const T *xrow = x + (unit * nrows + (p - t0)) * D;
+    for (int i = tid; i < D; i += 256) xs[i] = to_f64(xrow[i]);
+    __syncthreads();
+    const T *ubase = refs + unit * Rcap * D;
+    double bd[kMaxK];
+    int bj[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) {
+        bd[i] = __builtin_inf();
+        bj[i] = INT_MAX;
+    }
+    for (int64_t j = ja + tid; j < jb; j += 256) {
+        double cd = exact_sq_dist<T, D>(xs, ubase + j * D);
+        int cj = (int)j;
+        if (!(cd < bd[kMaxK - 1] || (cd == bd[kMaxK - 1] && cj < bj[kMaxK - 1]))) continue;
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) {
+            const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
+            const double td = bd[i];
+            const int tj = bj[i];
+            bd[i] = lt ? cd : td;
+            bj[i] = lt ? cj : tj;
+            cd = lt ? td : cd;
+            cj = lt ? tj : cj;
+        }
+    }
+    for (int r = 0; r < kMaxK; ++r) {
+        double md = bd[0];
+        int mj = bj[0];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double odd = __shfl_xor(md, o, 64);
+            const int ojj = __shfl_xor(mj, o, 64);
+            if (odd < md || (odd == md && ojj < mj)) {
+                md = odd;
+                mj = ojj;
+            }
+        }
+        if (lane == 0) {
+            wd[wv] = md;
+            wj[wv] = mj;
+        }
+        __syncthreads();
+        md = wd[0];
+        mj = wj[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+            if (wd[i] < md || (wd[i] == md && wj[i] < mj)) {
+                md = wd[i];
+                mj = wj[i];
+            }
+        __syncthreads();
+        if (mj != INT_MAX && bj[0] == mj) {
+#pragma unroll
+            for (int i = 0; i + 1 < kMaxK; ++i) {
+                bd[i] = bd[i + 1];
+                bj[i] = bj[i + 1];
+            }
+            bd[kMaxK - 1] = __builtin_inf();
+            bj[kMaxK - 1] = INT_MAX;
+        }
+        if (tid == 0) {
+            od[r] = md;
+            oj[r] = mj;
+        }
+    }
+}
+
+// The k best (distance, ordinal) of the nsplit partial lists of one token;
+// one wave per token.
+__global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int64_t q0,
+                                                          int64_t nq, int64_t Ncap,
+                                                          const double *__restrict__ pd,
+                                                          const int *__restrict__ pj,
+                                                          uint16_t *__restrict__ idx) {
+    const int lane = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    const int64_t unit = item / nq, q = q0 + item % nq;
+    const double *cd_ = pd + item * nsplit * kMaxK;
+    const int *cj_ = pj + item * nsplit * kMaxK;
+    double bd[kMaxK];
+    int bj[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) {
+        bd[i] = __builtin_inf();
+        bj[i] = INT_MAX;
+    }
+    for (int c = lane; c < nsplit * kMaxK; c += 64) {
+        double cd = cd_[c];
+        int cj = cj_[c];
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) {
+            const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
+            const double td = bd[i];
+            const int tj = bj[i];
+            bd[i] = lt ? cd : td;
+            bj[i] = lt ? cj : tj;
+            cd = lt ? td : cd;
+            cj = lt ? tj : cj;
+        }
+    }
+    uint16_t *out = idx + (unit * Ncap + q) * k;
+    for (int r = 0; r < k; ++r) {
+        double md = bd[0];
+        int mj = bj[0];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double odd = __shfl_xor(md, o, 64);
+            const int ojj = __shfl_xor(mj, o, 64);
+            if (odd < md || (odd == md && ojj < mj)) {
+                md = odd;
+                mj = ojj;
+            }
+        }
+        if (mj != INT_MAX && bj[0] == mj) {
+#pragma unroll
+            for (int i = 0; i + 1 < kMaxK; ++i) {
+                bd[i] = bd[i + 1];
+                bj[i] = bj[i + 1];
+            }
+            bd[kMaxK - 1] = __builtin_inf();
+            bj[kMaxK - 1] = INT_MAX;
+        }
+        if (lane == 0) out[r] = (mj == INT_MAX) ? kIdxUnused : (uint16_t)mj;
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                           int64_t nq, const CacheArgs &c, const uint64_t *list,
@@ -252,7 +404,17 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
         const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap, 1024));
         hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(256), 0, st,
                            (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
-                           dm.k, c.idx, list, list_count);
+                           dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq);
+        return hipGetLastError();
+    }
+    if (nq <= kSmallRange) {
+        // a few tokens (a streaming append): one block per token, the
+        // references split over its threads
+        const int64_t n = (int64_t)dm.B * dm.H * nq;
+        const unsigned g = (unsigned)std::min<int64_t>(n, 1024);
+        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(256), 0, st,
+                           (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
+                           dm.k, c.idx, nullptr, nullptr, (int64_t)dm.B * dm.H, nq);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
@@ -599,6 +761,44 @@ void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_
 
 }  // namespace
 
+// Reference chunk per block and block count of the split exact scan.
+static void split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
+    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    const int64_t c = std::max<int64_t>(256, (rmax + kSplitMax - 1) / kSplitMax);
+    *chunk = (int)c;
+    *nsplit = (int)((rmax + c - 1) / c);
+}
+
+size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
+    const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
+    if (nq <= 0 || nq > kSmallRange) return 0;
+    int chunk, nsplit;
+    split_plan(dm, t1, &chunk, &nsplit);
+    const size_t n = (size_t)dm.B * dm.H * nq * nsplit * kMaxK;
+    return n * sizeof(double) + n * sizeof(int) + 256;
+}
+
+hipError_t launch_select_split(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
+                               int64_t nq, const CacheArgs &c, void *ws, hipStream_t st) {
+    int chunk, nsplit;
+    split_plan(dm, t1, &chunk, &nsplit);
+    const int64_t items = (int64_t)dm.B * dm.H * nq;
+    double *pd = (double *)ws;
+    int *pj = (int *)((char *)ws + (size_t)items * nsplit * kMaxK * sizeof(double));
+    dim3 grid((unsigned)nsplit, (unsigned)items);
+    if (dm.d == 128)
+        hipLaunchKernelGGL((select_split_kernel<bf16_t, 128>), grid, dim3(256), 0, st,
+                           (const bf16_t *)x, t0, t1 - t0, dm.s, (const bf16_t *)c.refs, dm.R,
+                           q0, nq, chunk, pd, pj);
+    else
+        hipLaunchKernelGGL((select_split_kernel<bf16_t, 64>), grid, dim3(256), 0, st,
+                           (const bf16_t *)x, t0, t1 - t0, dm.s, (const bf16_t *)c.refs, dm.R,
+                           q0, nq, chunk, pd, pj);
+    hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)items), dim3(64), 0, st, nsplit, dm.k,
+                       q0, nq, dm.N, pd, pj, c.idx);
+    return hipGetLastError();
+}
+
 hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                                int64_t q0, int64_t nq, const CacheArgs &c,
                                const uint64_t *list, const uint32_t *list_count,
@@ -627,10 +827,10 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, fcount);
     if (dm.d == 128) {
         if (dm.k <= 4) launch_topk_t<128, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
-        else launch_topk_t<128, 12>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        else launch_topk_t<128, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
     } else {
         if (dm.k <= 4) launch_topk_t<64, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
-        else launch_topk_t<64, 12>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        else launch_topk_t<64, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -273,3 +273,24 @@ def test_decode_graph_replays_match_eager():
         dk.decode_attn(shape, Hq, T, qb, kc, kd, vc, vd, scale, out_o, ws2)
         torch.cuda.synchronize()
     say("  4 replays equal to eager")
+
+
+def test_single_token_appends_over_many_references_match_offline():
+    # one-token appends at the end of a context with many references (the
+    # exact per-token scan with the references split over several blocks)
+    # must store the same indices and latents as one offline call
+    B, H, T, d, s, k, dc, hid = 1, 2, 1600, 128, 2, 8, 16, 256
+    say(f"[case] appends: T={T} s={s} k={k}")
+    shape = dk.Shape(B, H, d, s, k, dc, T, dk.BF16)
+    x = make_kv(B, H, T, d, torch.bfloat16, key=(130, 0))
+    cw, _ = make_mlp(d, hid, dc, torch.bfloat16, key=(130, 1))
+    comp = gpu_mlp(cw, dk.ACT_GELU)
+    off = gpu_compress(shape, x, comp)
+    bounds = [0, T - 41] + list(range(T - 40, T + 1))
+    ap = gpu_compress(shape, x, comp, chunks=bounds)
+    for name in ("refs", "ref_sqnorm", "latents", "idx"):
+        a, b = getattr(off, name), getattr(ap, name)
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    tail = [p for p in range(T - 40, T) if p % s != 0]
+    check_compress_unit(shape, x[0, 1], ap, 0, 1, oracle_mlp(cw, dk.ACT_GELU),
+                        positions=np.array(tail), tol=2e-2)
