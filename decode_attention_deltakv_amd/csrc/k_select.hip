@@ -438,8 +438,10 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 // Per lane, a descending list of the LK best scores is kept as packed floats:
 // the low `ibits` mantissa bits of each score are replaced by its reference
 // ordinal (ordered so that, among equal truncated scores, the lower ordinal
-// ranks higher), which lets one insertion be LK v_med3 operations.  The two
-// lanes that share a token merge their lists, then the LK candidates are
+// ranks higher), which lets one insertion be LK v_med3 operations.  After each
+// 32 x 32 product the two lane halves exchange scores (one v_permlane32_swap
+// per register) so that every lane holds all 32 scores of one token and keeps
+// one list; at the end the LK candidates are
 // rescored exactly (fp64, coordinate order, no fused multiply-add) and sorted
 // by (distance, ordinal).  The result is written only when a certificate
 // holds: every reference outside the list has an approximate score at most
@@ -470,31 +472,26 @@ __device__ __forceinline__ void list_insert(float (&a)[LK], float v) {
     a[0] = m;
 }
 
+// Exact rescore of one token's LK candidates in one lane: fp64 distances in
+// coordinate order without fused multiply-add, sort by (distance, ordinal),
+// certificate; the result or a fallback entry is written.
 template <int D, int LK>
-__device__ void rescore_and_emit(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
-                                 const float (&lst)[LK], uint32_t imask, int ibits, int k,
-                                 float rmax2, bool write, uint16_t *__restrict__ out,
-                                 uint64_t fentry, uint64_t *__restrict__ flist,
-                                 uint32_t *__restrict__ fcount) {
+__device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
+                             const float (&lst)[LK], uint32_t imask, int ibits, int k,
+                             float rmax2, bool write, uint16_t *__restrict__ out,
+                             uint64_t fentry, uint64_t *__restrict__ flist,
+                             uint32_t *__restrict__ fcount) {
 #pragma clang fp contract(off)
-    constexpr int HALF = LK / 2;
-    const int lane = threadIdx.x & 63;
-    const int h = lane >> 5;
-    int cj[HALF];
-    bool cv[HALF];
+    int jj[LK];
+    bool cv[LK];
 #pragma unroll
-    for (int e = 0; e < HALF; ++e) {
-        // bitwise lane select (a conditional on the index would make the list
-        // memory-indexed)
-        const uint32_t hm = 0u - (uint32_t)h;
-        const float v = __uint_as_float((__float_as_uint(lst[e]) & ~hm) |
-                                        (__float_as_uint(lst[HALF + e]) & hm));
-        cv[e] = v != -INFINITY;
-        cj[e] = cv[e] ? unpack_ordinal(v, imask) : 0;
+    for (int e = 0; e < LK; ++e) {
+        cv[e] = lst[e] != -INFINITY;
+        jj[e] = cv[e] ? unpack_ordinal(lst[e], imask) : 0;
     }
-    double dacc[HALF];
+    double dd[LK];
 #pragma unroll
-    for (int e = 0; e < HALF; ++e) dacc[e] = 0.0;
+    for (int e = 0; e < LK; ++e) dd[e] = 0.0;
     double xsq = 0.0;
     for (int c = 0; c < D / 8; ++c) {
         const u32x4 xv = ld16(xrow + 8 * c);
@@ -510,37 +507,27 @@ __device__ void rescore_and_emit(const bf16_t *__restrict__ xrow, const bf16_t *
             xsq = xsq + sq;
         }
 #pragma unroll
-        for (int e = 0; e < HALF; ++e) {
-            const u32x4 rv = ld16(urefs + (int64_t)cj[e] * D + 8 * c);
+        for (int e = 0; e < LK; ++e) {
+            const u32x4 rv = ld16(at_byte(urefs, ((uint32_t)jj[e] * D + 8u * c) * 2u));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const double r0 = (double)__uint_as_float(rv[i] << 16);
                 const double r1 = (double)__uint_as_float(rv[i] & 0xffff0000u);
                 const double d0 = xd[2 * i] - r0;
                 const double s0 = d0 * d0;
-                dacc[e] = dacc[e] + s0;
+                dd[e] = dd[e] + s0;
                 const double d1 = xd[2 * i + 1] - r1;
                 const double s1 = d1 * d1;
-                dacc[e] = dacc[e] + s1;
+                dd[e] = dd[e] + s1;
             }
         }
     }
-    // both lanes of the pair assemble the full candidate set
-    double dd[LK];
-    int jj[LK];
 #pragma unroll
-    for (int e = 0; e < HALF; ++e) {
-        const double mine = cv[e] ? dacc[e] : __builtin_inf();
-        const double other = __shfl_xor(mine, 32, 64);
-        const int ojj = __shfl_xor(cj[e], 32, 64);
-        const int mj = cv[e] ? cj[e] : INT_MAX;
-        const int oj = other == __builtin_inf() ? INT_MAX : ojj;
-        dd[e] = h ? other : mine;
-        jj[e] = h ? oj : mj;
-        dd[HALF + e] = h ? mine : other;
-        jj[HALF + e] = h ? mj : oj;
+    for (int e = 0; e < LK; ++e) {
+        dd[e] = cv[e] ? dd[e] : __builtin_inf();
+        jj[e] = cv[e] ? jj[e] : INT_MAX;
     }
-    if (!write || h != 0) return;
+    if (!write) return;
     // sort by (distance, ordinal): odd-even transposition network
 #pragma unroll
     for (int pass = 0; pass < LK; ++pass) {
@@ -614,28 +601,27 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     // reference counts stay below 2^16: 32-bit arithmetic in the loop
     const int ncand_max = (int)((tok_pos(qlast, s) + s - 1) / s);
 
-    int64_t qn[2], pos[2];
-    int ncand[2], ncand_lo[2];
-    bool valid[2];
+    // MFMA column operands: the wave's two N-tiles of 32 tokens
     bf16x8 xb[2][KSTEPS];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const int64_t qq = qb + 64 * w + 32 * nt + l32;
-        valid[nt] = qq < qend;
-        qn[nt] = min(qq, qend - 1);
-        pos[nt] = tok_pos(qn[nt], s);
-        ncand[nt] = (int)((pos[nt] + s - 1) / s);
-        const int64_t qf = min(qb + 64 * w + 32 * nt, qend - 1);
-        ncand_lo[nt] = (int)((tok_pos(qf, s) + s - 1) / s);
-        const bf16_t *xr = x + ((int64_t)unit * nrows + (pos[nt] - t0)) * D;
+        const int64_t qq = min(qb + 64 * w + 32 * nt + l32, qend - 1);
+        const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(qq, s) - t0)) * D;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) xb[nt][ks] = as_bf16x8(ld16(xr + 16 * ks + 8 * hl));
     }
-    float lst[2][LK];
+    // after the half swap below, lane L holds all 32 scores of token
+    // qb + 64 w + L: one candidate list per lane
+    const int64_t qq = qb + 64 * w + lane;
+    const bool valid = qq < qend;
+    const int64_t qn = min(qq, qend - 1);
+    const int64_t pos = tok_pos(qn, s);
+    const int ncand = (int)((pos + s - 1) / s);
+    const int ncand_lo =
+        (int)((tok_pos(min(qb + 64 * w, qend - 1), s) + s - 1) / s);  // the wave's first token
+    float lst[LK];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int e = 0; e < LK; ++e) lst[nt][e] = -INFINITY;
+    for (int e = 0; e < LK; ++e) lst[e] = -INFINITY;
 
     float rmax2 = 0.f;
     auto stage_load = [&](int jbase, int b) {
@@ -690,22 +676,34 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
                 acc0 = mfma32_bf16(a, xb[0][ks], acc0);
                 acc1 = mfma32_bf16(a, xb[1][ks], acc1);
             }
+            // swap the upper half of acc0 with the lower half of acc1: lane L
+            // then holds rows 8 (i / 4) + (i % 4) (acc0) and + 4 (acc1) of
+            // token qb + 64 w + L
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x16 sc = nt == 0 ? acc0 : acc1;
-                if (j0 + 32 > ncand_lo[nt]) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = j0 + 8 * (i / 4) + 4 * hl + (i % 4);
-                        sc[i] = j < ncand[nt] ? sc[i] : -INFINITY;
-                    }
-                }
+            for (int i = 0; i < 16; ++i) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[i]),
+                                                                 __float_as_uint(acc1[i]), false,
+                                                                 false);
+                acc0[i] = __uint_as_float(sw[0]);
+                acc1[i] = __uint_as_float(sw[1]);
+            }
+            if (j0 + 32 > ncand_lo) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const bool pass = sc[i] > lst[nt][LK - 1];
+                    const int j = j0 + 8 * (i / 4) + (i % 4);
+                    acc0[i] = j < ncand ? acc0[i] : -INFINITY;
+                    acc1[i] = j + 4 < ncand ? acc1[i] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const float sc = h2 ? acc1[i] : acc0[i];
+                    const bool pass = sc > lst[LK - 1];
                     if (__builtin_amdgcn_ballot_w64(pass)) {
-                        const int j = (int)j0 + 8 * (i / 4) + 4 * hl + (i % 4);
-                        list_insert<LK>(lst[nt], pass ? pack_score(sc[i], j, imask) : -INFINITY);
+                        const int j = j0 + 8 * (i / 4) + 4 * h2 + (i % 4);
+                        list_insert<LK>(lst, pass ? pack_score(sc, j, imask) : -INFINITY);
                     }
                 }
             }
@@ -723,19 +721,10 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     __syncthreads();
     rmax2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        // merge the two half-lists of each token (lanes l and l ^ 32)
-        float other[LK];
-#pragma unroll
-        for (int e = 0; e < LK; ++e) other[e] = __shfl_xor(lst[nt][e], 32, 64);
-#pragma unroll
-        for (int e = 0; e < LK; ++e) list_insert<LK>(lst[nt], other[e]);
-        const bf16_t *xr = x + ((int64_t)unit * nrows + (pos[nt] - t0)) * D;
-        rescore_and_emit<D, LK>(xr, urefs, lst[nt], imask, ibits, k, rmax2, valid[nt],
-                                idx + ((int64_t)unit * Ncap + qn[nt]) * k,
-                                ((uint64_t)unit << 32) | (uint64_t)(qn[nt] - q0), flist, fcount);
-    }
+    const bf16_t *xr = x + ((int64_t)unit * nrows + (pos - t0)) * D;
+    rescore_lane<D, LK>(xr, urefs, lst, imask, ibits, k, rmax2, valid,
+                        idx + ((int64_t)unit * Ncap + qn) * k,
+                        ((uint64_t)unit << 32) | (uint64_t)(qn - q0), flist, fcount);
 }
 
 __global__ void zero_u32_kernel(uint32_t *p) {
