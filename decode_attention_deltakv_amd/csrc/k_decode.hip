@@ -525,9 +525,9 @@ __global__ __launch_bounds__(256) void combine2_kernel(int Hq, int G, int d, int
 // (VALU), as in the general path.
 //
 // LDS layouts: V rows are stored row-major with their 16-byte chunks XOR-
-// swizzled by 2 * ((row / 8) % 4), so that the column reads of the B operand
-// (8 rows, 16 columns per lane group) spread over all banks; the per-head
-// weight rows carry 16 bytes of padding for the same reason.
+// swizzled by 2 * (row % 4), so that the transposing reads of the B operand
+// (4 consecutive rows x 32 bytes per 16-lane group) fall in disjoint banks;
+// the per-head weight rows carry 16 bytes of padding for the same reason.
 template <int D, int DC, int HID, int KP>
 __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     int U, int Hq, int G, int k, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             const int it = tid + 256 * m;
             const int row = it / CH, c8 = it % CH;
             const int t = row / KP, i = row % KP;
-            const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+            const int sc8 = c8 ^ (2 * (row & 3));
             const bool ok = t0 + t < qe32 && i < k && gr[m] != kIdxUnused;
             __builtin_amdgcn_global_load_lds(
                 (const void *)(vref_u + (uint32_t)((ok ? gr[m] : 0u) * D + 8 * sc8)),
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             for (int m = 0; m < (TT * CH) / 256; ++m) {
                 const int it = tid + 256 * m;
                 const int row = it / CH, c8 = it % CH;
-                const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+                const int sc8 = c8 ^ (2 * (row & 3));
                 const int64_t j = min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
-                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
                 const u32x2 lo = lds_read_tr16(&vrowA[rb + (l16 >> 2)][pcol]);
                 const u32x2 hi = lds_read_tr16(&vrowA[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 // B operand: rows rb .. rb+7 of column cbase + 16 n + l16, two
                 // transposing reads (rows rb + l16/4 and rb + 4 + l16/4)
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
-                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
                 const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
                 const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
@@ -1101,7 +1101,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             for (int m = 0; m < (TT * CH) / 256; ++m) {
                 const int it = tid + 256 * m;
                 const int row = it / CH, c8 = it % CH;
-                const int sc8 = c8 ^ (2 * ((row >> 3) & 3));
+                const int sc8 = c8 ^ (2 * (row & 3));
                 const int64_t j = min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
@@ -1140,7 +1140,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
-                const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
                 const u32x2 lo = lds_read_tr16(&vbufA[rb + (l16 >> 2)][pcol]);
                 const u32x2 hi = lds_read_tr16(&vbufA[rb + 4 + (l16 >> 2)][pcol]);
                 const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
@@ -1384,9 +1384,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // chunks; this lane's chunk and its swizzled source offsets
         const uint32_t lrow = (uint32_t)(lane / CH);
         const uint32_t c8 = (uint32_t)(lane % CH);
-        uint32_t coff[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) coff[x] = 16u * (c8 ^ (2u * x));
+        // source chunk of this lane's LDS slot (rows of a gather instruction
+        // start at a multiple of 4, so the row's swizzle is lrow % 4)
+        const uint32_t coff = 16u * (c8 ^ (2u * (lrow & 3u)));
         const uint32_t rlast = (uint32_t)Rt - 1u;
         uint32_t gi[NDMA];
         // index entries of rows [64 vj, 64 vj + 64) of the tile at t0: rows
@@ -1409,9 +1409,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int m = 0; m < NDMA; ++m) {
                 const uint32_t j = min(gi[m], rlast);
-                const int x = ((RPD * m) >> 3) & 3;
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)((const char *)vref_u + (j * (uint32_t)(D * 2) + coff[x])),
+                    (const void *)((const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
                     (__attribute__((address_space(3))) void *)&dst[64 * vj + RPD * m][0], 16, 0, 0);
             }
         };
@@ -1493,7 +1492,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
                     for (int nc = 0; nc < NC; ++nc) {
                         const int c = cb + 16 * nc + 4 * (l16 & 3);
-                        const int pcol = (((c >> 3) ^ (2 * lq)) << 3) | (c & 7);
+                        const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
                         const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
                         const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
                         const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
