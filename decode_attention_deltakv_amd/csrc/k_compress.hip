@@ -80,7 +80,14 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
 // bf16.  The hidden tile never leaves registers (its MFMA output layout is
 // the B operand of the second product, with the hidden index permuted
 // consistently in W2's operand).
-template <int D, int HID, int DC, bool GELU>
+//
+// The global loads run ahead of the products in a three-stage pipeline: the
+// index lists two tiles ahead, the token rows and the chosen reference rows
+// (whose addresses those lists give) one tile ahead, so neither the
+// index-then-gather dependence nor HBM latency sits between two tiles.
+// Each thread owns NI 16-byte chunks (token t, columns 8 c8 .. 8 c8 + 7) of
+// every tile.  KX: largest k (4 or 8).
+template <int D, int HID, int DC, int KX, bool GELU>
 __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
@@ -94,6 +101,7 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     constexpr int KJ = HW / 32;
     constexpr int MD = DC / 16;
     constexpr int CH = D / 8;
+    constexpr int NI = (TT * CH) / 256;
     static_assert(HW % 32 == 0 && DC % 16 == 0, "unsupported shape");
     __shared__ __attribute__((aligned(16))) bf16_t dl[TT][D + 8];
     __shared__ float zp[4][DC][TT + 1];
@@ -105,6 +113,9 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     const int hb = w * HW;
     const int64_t qend = q0 + nq;
     const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
+    const bf16_t *ux = x + (int64_t)unit * nrows * D;
+    const uint16_t *uidx = idx + (int64_t)unit * Ncap * k;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     bf16x8 a1[MT][KSD];
     f32x4 bias1[MT];
@@ -128,43 +139,77 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
             a2[md][j] = as_bf16x8(v);
         }
 
-    for (int it = 0; it < tiles_per_block; ++it) {
-        const int64_t qt = q0 + ((int64_t)blk * tiles_per_block + it) * TT;
-        if (qt >= qend) break;
-        // ---- residual tile
+    const int ntile = (int)min((int64_t)tiles_per_block,
+                               (qend - q0 + TT - 1) / TT - (int64_t)blk * tiles_per_block);
+    auto tile_q = [&](int it) { return q0 + ((int64_t)blk * tiles_per_block + it) * TT; };
+    // token ordinal of chunk m in the tile at qt (clamped to the range)
+    auto chunk_q = [&](int64_t qt, int m) { return min(qt + (tid + 256 * m) / CH, qend - 1); };
+
+    uint32_t jn[NI][KX];  // index lists, two tiles ahead
+    u32x4 xv[NI];         // token chunks, one tile ahead
+    u32x4 rv[NI][KX];     // chosen reference chunks, one tile ahead
+    float inv[NI];        // 1 / k_eff of those tokens
+
+    auto stage_idx = [&](int64_t qt) {
 #pragma unroll
-        for (int m = 0; m < (TT * CH) / 256; ++m) {
+        for (int m = 0; m < NI; ++m) {
+            const uint16_t *ir = uidx + chunk_q(qt, m) * k;
+#pragma unroll
+            for (int r = 0; r < KX; ++r) jn[m][r] = r < k ? (uint32_t)ir[r] : (uint32_t)kIdxUnused;
+        }
+    };
+    auto stage_rows = [&](int64_t qt) {
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+            const int c8 = (tid + 256 * m) % CH;
+            xv[m] = ld16(ux + (tok_pos(chunk_q(qt, m), s) - t0) * D + 8 * c8);
+            int keff = 0;
+#pragma unroll
+            for (int r = 0; r < KX; ++r) {
+                const bool used = jn[m][r] != kIdxUnused;
+                keff += used ? 1 : 0;
+                rv[m][r] = used ? ld16(urefs + (int64_t)jn[m][r] * D + 8 * c8) : zero4;
+            }
+            inv[m] = 1.f / (float)keff;
+        }
+    };
+    auto residual = [&]() {
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
             const int item = tid + 256 * m;
             const int t = item / CH, c8 = item % CH;
-            const int64_t q = min(qt + t, qend - 1);
-            const int64_t p = tok_pos(q, s);
-            const u32x4 xv = ld16(x + ((int64_t)unit * nrows + (p - t0)) * D + 8 * c8);
-            const uint16_t *ir = idx + ((int64_t)unit * Ncap + q) * k;
             float acc[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-            int keff = 0;
-            for (int r = 0; r < k; ++r) {
-                const uint16_t j = ir[r];
-                if (j == kIdxUnused) continue;
-                const u32x4 rv = ld16(urefs + (int64_t)j * D + 8 * c8);
+#pragma unroll
+            for (int r = 0; r < KX; ++r)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += __uint_as_float(rv[e] << 16);
-                    acc[2 * e + 1] += __uint_as_float(rv[e] & 0xffff0000u);
+                    acc[2 * e] += __uint_as_float(rv[m][r][e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(rv[m][r][e] & 0xffff0000u);
                 }
-                ++keff;
-            }
-            const float inv = 1.f / (float)keff;
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float d0 = __uint_as_float(xv[e] << 16) - acc[2 * e] * inv;
-                const float d1 = __uint_as_float(xv[e] & 0xffff0000u) - acc[2 * e + 1] * inv;
+                const float d0 = __uint_as_float(xv[m][e] << 16) - acc[2 * e] * inv[m];
+                const float d1 = __uint_as_float(xv[m][e] & 0xffff0000u) - acc[2 * e + 1] * inv[m];
                 o[e] = pack_bf16(d0, d1);
             }
             *reinterpret_cast<u32x4 *>(&dl[t][8 * c8]) = o;
         }
+    };
+
+    if (ntile > 0) {
+        stage_idx(tile_q(0));
+        stage_rows(tile_q(0));
+        if (ntile > 1) stage_idx(tile_q(1));
+    }
+    for (int it = 0; it < ntile; ++it) {
+        const int64_t qt = tile_q(it);
+        // ---- residual tile from the staged rows, then the next loads
+        residual();
+        if (it + 1 < ntile) stage_rows(tile_q(it + 1));
+        if (it + 2 < ntile) stage_idx(tile_q(it + 2));
         __syncthreads();
         // ---- hidden tile and the wave's share of the latent
 #pragma unroll
@@ -217,8 +262,10 @@ void launch_cmfma_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64
     const int64_t tiles = (nq + 31) / 32;
     const int tpb = (int)std::max<int64_t>(1, std::min<int64_t>(16, (tiles * U + 1023) / 1024));
     const int64_t nblk = (tiles + tpb - 1) / tpb;
-    auto kern = m.act == 0 ? compress_mfma_kernel<D, HID, DC, true>
-                           : compress_mfma_kernel<D, HID, DC, false>;
+    auto kern = dm.k <= 4 ? (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 4, true>
+                                        : compress_mfma_kernel<D, HID, DC, 4, false>)
+                          : (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 8, true>
+                                        : compress_mfma_kernel<D, HID, DC, 8, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)(nblk * U)), dim3(256), 0, st, (const bf16_t *)x, t0,
                        t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs, dm.R, c.idx, dm.N, q0, nq, U,
                        tpb, (const bf16_t *)m.w1, m.b1, (const bf16_t *)m.w2, m.b2,

@@ -23,6 +23,8 @@ namespace dk {
 namespace {
 
 constexpr int kMaxK = 8;
+// threads of the block-per-token exact scan
+constexpr int kExactThreads = 1024;
 
 // Squared distance between the fp64 row xs (LDS) and reference row r, summed
 // in order with separately rounded products and sums.
@@ -63,6 +65,38 @@ __device__ __forceinline__ double exact_sq_dist(const double *xs, const T *__res
         }
     }
     return acc;
+}
+
+// The same distance for four reference rows at once (four independent sums,
+// each in coordinate order): one pass over xs, four add chains in flight.
+template <int D>
+__device__ __forceinline__ void exact_sq_dist4(const double *xs, const bf16_t *r0,
+                                               const bf16_t *r1, const bf16_t *r2,
+                                               const bf16_t *r3, double (&acc)[4]) {
+#pragma clang fp contract(off)
+    const uint4 *rv[4] = {reinterpret_cast<const uint4 *>(r0), reinterpret_cast<const uint4 *>(r1),
+                          reinterpret_cast<const uint4 *>(r2), reinterpret_cast<const uint4 *>(r3)};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = 0.0;
+#pragma unroll 2
+    for (int c = 0; c < D / 8; ++c) {
+        uint4 u[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) u[v] = rv[v][c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double xe = xs[c * 8 + e];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t wv = (e >> 1) == 0 ? u[v].x : (e >> 1) == 1 ? u[v].y
+                                  : (e >> 1) == 2 ? u[v].z : u[v].w;
+                const double rr = (double)__uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+                const double df = xe - rr;
+                const double sq = df * df;
+                acc[v] = acc[v] + sq;
+            }
+        }
+    }
 }
 
 // Exact top-k of one token per wave.  Work item w of the launch is token
@@ -155,20 +189,22 @@ __global__ __launch_bounds__(256) void select_exact_kernel(
 }
 
 // Exact top-k of listed tokens, one block per token (grid-stride over the
-// list): the 256 threads split the candidate references, each keeps a sorted
-// top-k of its share, and the block merges the 256 lists by k rounds of a
-// lexicographic (distance, ordinal) minimum.  Same arithmetic as the
-// wave-per-token scan; used for the few tokens the matrix-core search could
-// not certify.
+// list): the kExactThreads threads split the candidate references (bf16: four
+// per thread and pass, so four independent fp64 sums are in flight), each
+// keeps a sorted top-k of its share, and the block merges the lists by k
+// rounds of a lexicographic (distance, ordinal) minimum.  Same arithmetic as
+// the wave-per-token scan; used for the few tokens the matrix-core search
+// could not certify.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void select_exact_block_kernel(
+__global__ __launch_bounds__(kExactThreads) void select_exact_block_kernel(
     const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
     int64_t Rcap, int64_t Ncap, int64_t q0, int k, uint16_t *__restrict__ idx,
     const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count, int64_t nunits,
     int64_t nq) {
+    constexpr int NT = kExactThreads, NW = NT / 64;
     __shared__ double xs[D];
-    __shared__ double wd[4];
-    __shared__ int wj[4];
+    __shared__ double wd[NW];
+    __shared__ int wj[NW];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // work items: the listed (unit, token) entries, or without a list every
     // token of [q0, q0 + nq) of every unit
@@ -180,9 +216,9 @@ __global__ __launch_bounds__(256) void select_exact_block_kernel(
         const int64_t p = tok_pos(q, s);
         const T *xrow = x + (unit * nrows + (p - t0)) * D;
         __syncthreads();
-        for (int i = tid; i < D; i += 256) xs[i] = to_f64(xrow[i]);
+        for (int i = tid; i < D; i += NT) xs[i] = to_f64(xrow[i]);
         __syncthreads();
-        const int64_t ncand = (p + s - 1) / s;
+        const int ncand = (int)((p + s - 1) / s);
         const T *ubase = refs + unit * Rcap * D;
         double bd[kMaxK];
         int bj[kMaxK];
@@ -191,10 +227,8 @@ __global__ __launch_bounds__(256) void select_exact_block_kernel(
             bd[i] = __builtin_inf();
             bj[i] = INT_MAX;
         }
-        for (int64_t j = tid; j < ncand; j += 256) {
-            double cd = exact_sq_dist<T, D>(xs, ubase + j * D);
-            int cj = (int)j;
-            if (!(cd < bd[kMaxK - 1] || (cd == bd[kMaxK - 1] && cj < bj[kMaxK - 1]))) continue;
+        auto offer = [&](double cd, int cj) {
+            if (!(cd < bd[kMaxK - 1] || (cd == bd[kMaxK - 1] && cj < bj[kMaxK - 1]))) return;
 #pragma unroll
             for (int i = 0; i < kMaxK; ++i) {
                 const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
@@ -205,6 +239,22 @@ __global__ __launch_bounds__(256) void select_exact_block_kernel(
                 cd = lt ? td : cd;
                 cj = lt ? tj : cj;
             }
+        };
+        if constexpr (sizeof(T) == 2) {
+            // four references per thread and pass: j, j + NT, j + 2 NT, j + 3 NT
+            for (int j = tid; j < ncand; j += 4 * NT) {
+                int jv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) jv[v] = min(j + v * NT, ncand - 1);
+                double cd[4];
+                exact_sq_dist4<D>(xs, ubase + (int64_t)jv[0] * D, ubase + (int64_t)jv[1] * D,
+                                  ubase + (int64_t)jv[2] * D, ubase + (int64_t)jv[3] * D, cd);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (j + v * NT < ncand) offer(cd[v], j + v * NT);
+            }
+        } else {
+            for (int j = tid; j < ncand; j += NT) offer(exact_sq_dist<T, D>(xs, ubase + (int64_t)j * D), j);
         }
         uint16_t *out = idx + (unit * Ncap + q) * k;
         for (int r = 0; r < k; ++r) {
@@ -227,7 +277,7 @@ __global__ __launch_bounds__(256) void select_exact_block_kernel(
             md = wd[0];
             mj = wj[0];
 #pragma unroll
-            for (int i = 1; i < 4; ++i)
+            for (int i = 1; i < NW; ++i)
                 if (wd[i] < md || (wd[i] == md && wj[i] < mj)) {
                     md = wd[i];
                     mj = wj[i];
@@ -402,7 +452,7 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                           const uint32_t *list_count, int64_t list_cap, hipStream_t st) {
     if (list) {
         const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap, 1024));
-        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(256), 0, st,
+        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0, st,
                            (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
                            dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq);
         return hipGetLastError();
@@ -412,7 +462,7 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
         // references split over its threads
         const int64_t n = (int64_t)dm.B * dm.H * nq;
         const unsigned g = (unsigned)std::min<int64_t>(n, 1024);
-        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(256), 0, st,
+        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0, st,
                            (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
                            dm.k, c.idx, nullptr, nullptr, (int64_t)dm.B * dm.H, nq);
         return hipGetLastError();
@@ -436,9 +486,11 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 // from global memory with 16-byte chunks XOR-swizzled by (row % 8).
 //
 // Per lane, a descending list of the LK best scores is kept as packed floats:
-// the low `ibits` mantissa bits of each score are replaced by its reference
-// ordinal (ordered so that, among equal truncated scores, the lower ordinal
-// ranks higher), which lets one insertion be LK v_med3 operations.  After each
+// the low `ibits` mantissa bits of each score are replaced by imask - ordinal
+// (among equal truncated positive scores the lower ordinal ranks higher; the
+// order among ties does not matter for the result, which the exact rescore
+// and the certificate decide), which lets one insertion be LK v_med3
+// operations and one packing be a single bitwise instruction.  After each
 // 32 x 32 product the two lane halves exchange scores (one v_permlane32_swap
 // per register) so that every lane holds all 32 scores of one token and keeps
 // one list; at the end the LK candidates are
@@ -450,15 +502,12 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 // error of the MFMA score (and of the fp32 norm); this lower bound must exceed
 // the k-th exact distance.  Tokens that fail go to a list for the exact scan.
 
-__device__ __forceinline__ float pack_score(float sc, int j, uint32_t imask) {
-    const uint32_t u = __float_as_uint(sc);
-    const uint32_t code = (u >> 31) ? (uint32_t)j : (imask - (uint32_t)j);
-    return __uint_as_float((u & ~imask) | code);
+// the low bits of a packed score hold imask - j (one instruction to pack)
+__device__ __forceinline__ float pack_score(float sc, uint32_t code, uint32_t nmask) {
+    return __uint_as_float((__float_as_uint(sc) & nmask) | code);
 }
 __device__ __forceinline__ int unpack_ordinal(float v, uint32_t imask) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t code = u & imask;
-    return (u >> 31) ? (int)code : (int)(imask - code);
+    return (int)(imask - (__float_as_uint(v) & imask));
 }
 
 template <int LK>
@@ -622,6 +671,10 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     float lst[LK];
 #pragma unroll
     for (int e = 0; e < LK; ++e) lst[e] = -INFINITY;
+    // in a vector register, so a packing is one v_and_or_b32 with the
+    // (scalar) code as its other operand
+    uint32_t nmask = ~imask;
+    asm volatile("" : "+v"(nmask));
 
     float rmax2 = 0.f;
     auto stage_load = [&](int jbase, int b) {
@@ -660,6 +713,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         for (int mb = 0; mb < 2; ++mb) {
             const int j0 = jst + 32 * mb;
             if (j0 >= ncand_max) break;
+            const uint32_t cbase = imask - (uint32_t)j0;
             f32x16 init;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
@@ -695,16 +749,18 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
                     acc1[i] = j + 4 < ncand ? acc1[i] : -INFINITY;
                 }
             }
+            // slots in pairs: one wave-wide test per pair, then each slot's
+            // insertion under the mask of the lanes it passes in (a second
+            // slot that no longer beats the list after the first went in
+            // leaves the list unchanged)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const float sc = h2 ? acc1[i] : acc0[i];
-                    const bool pass = sc > lst[LK - 1];
-                    if (__builtin_amdgcn_ballot_w64(pass)) {
-                        const int j = j0 + 8 * (i / 4) + 4 * h2 + (i % 4);
-                        list_insert<LK>(lst, pass ? pack_score(sc, j, imask) : -INFINITY);
-                    }
+                const float thr = lst[LK - 1];
+                const bool p0 = acc0[i] > thr, p1 = acc1[i] > thr;
+                if (__builtin_amdgcn_ballot_w64(p0 || p1)) {
+                    const uint32_t code = cbase - (uint32_t)(8 * (i / 4) + (i % 4));
+                    if (p0) list_insert<LK>(lst, pack_score(acc0[i], code, nmask));
+                    if (p1) list_insert<LK>(lst, pack_score(acc1[i], code - 4u, nmask));
                 }
             }
         }

@@ -73,6 +73,7 @@ def test_bf16_llama_heads_ragged():
 @pytest.mark.parametrize("cfg", [
     # (d, s, k, dc, hid, G, T, dtype)
     (128, 8, 8, 16, 256, 4, 777, dk.BF16),    # streaming workload's shapes
+    (128, 8, 6, 32, 256, 4, 1200, dk.BF16),   # k > 4 with d_c = 32 in the Compressor
     (64, 3, 2, 64, 64, 1, 500, dk.BF16),
     (64, 5, 5, 128, 128, 8, 301, dk.BF16),
     (64, 4, 3, 64, 128, 2, 999, dk.BF16),     # matrix-core decode at head_dim 64
