@@ -79,12 +79,13 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-// Two fp32 values -> packed bf16 (round to nearest even).
+// Two fp32 values -> packed bf16, round to nearest even (gfx950's
+// v_cvt_pk_bf16_f32: one instruction).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-    ua += 0x7fffu + ((ua >> 16) & 1u);
-    ub += 0x7fffu + ((ub >> 16) & 1u);
-    return (ua >> 16) | (ub & 0xffff0000u);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Two fp32 values -> packed f16 (round toward zero; one instruction).

@@ -11,7 +11,10 @@
 #include "dk_launch.h"
 #include "dk_mfma.h"
 
+#include <limits.h>
+
 #include <algorithm>
+#include <type_traits>
 
 namespace dk {
 namespace {
@@ -119,7 +122,10 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
 
     bf16x8 a1[MT][KSD];
     f32x4 bias1[MT];
-    bf16x8 a2[MD][KJ];
+    // W2 operand: bf16 for the identity activation, f16 after the GELU (whose
+    // packed-f16 output then feeds an f16 product without a conversion)
+    using A2 = typename std::conditional<GELU, f16x8, bf16x8>::type;
+    A2 a2[MD][KJ];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -136,39 +142,80 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
             const uint2 lo = *reinterpret_cast<const uint2 *>(wr);
             const uint2 hi = *reinterpret_cast<const uint2 *>(wr + 16);
             u32x4 v = {lo.x, lo.y, hi.x, hi.y};
-            a2[md][j] = as_bf16x8(v);
+            if constexpr (GELU) {
+                f16x8 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[2 * e] = (_Float16)__uint_as_float(v[e] << 16);
+                    h[2 * e + 1] = (_Float16)__uint_as_float(v[e] & 0xffff0000u);
+                }
+                a2[md][j] = h;
+            } else {
+                a2[md][j] = as_bf16x8(v);
+            }
         }
 
     const int ntile = (int)min((int64_t)tiles_per_block,
                                (qend - q0 + TT - 1) / TT - (int64_t)blk * tiles_per_block);
-    auto tile_q = [&](int it) { return q0 + ((int64_t)blk * tiles_per_block + it) * TT; };
+    // token ordinals and positions fit in 32 bits (the cache holds fewer
+    // than 2^31 rows per unit)
+    const uint32_t qlast = (uint32_t)(qend - 1);
+    const uint32_t sm1 = (uint32_t)(s - 1);
+    auto tile_q = [&](int it) {
+        return (uint32_t)(q0 + ((int64_t)blk * tiles_per_block + it) * TT);
+    };
     // token ordinal of chunk m in the tile at qt (clamped to the range)
-    auto chunk_q = [&](int64_t qt, int m) { return min(qt + (tid + 256 * m) / CH, qend - 1); };
+    auto chunk_q = [&](uint32_t qt, int m) { return min(qt + (uint32_t)((tid + 256 * m) / CH), qlast); };
+    // index lists and reference rows through buffer resources: every load
+    // is issued (no branch, so the wait counts stay exact) and a read past a
+    // resource's end returns zeros
+    const __amdgpu_buffer_rsrc_t idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)uidx, (short)0, (int)(Ncap * k * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ref_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)urefs, (short)0, (int)(Rcap * D * 2), 0x00020000);
+
+    // latents of the range [q0, qend) of this unit; stores past qend drop
+    const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(lat + (int64_t)unit * Ncap * DC), (short)0, (int)(qend * DC * 2), 0x00020000);
+    // b2 of the two latent columns this thread stores (fixed across tiles)
+    float bias2[2];
+    {
+        const int o = 2 * (tid % (DC / 2));
+        bias2[0] = b2 ? b2[o] : 0.f;
+        bias2[1] = b2 ? b2[o + 1] : 0.f;
+    }
 
     uint32_t jn[NI][KX];  // index lists, two tiles ahead
     u32x4 xv[NI];         // token chunks, one tile ahead
-    u32x4 rv[NI][KX];     // chosen reference chunks, one tile ahead
+    u32x4 rv[NI][KX];     // chosen reference chunks (zeros for unused slots)
     float inv[NI];        // 1 / k_eff of those tokens
 
-    auto stage_idx = [&](int64_t qt) {
+    auto stage_idx = [&](uint32_t qt) {
 #pragma unroll
         for (int m = 0; m < NI; ++m) {
-            const uint16_t *ir = uidx + chunk_q(qt, m) * k;
+            const uint32_t base = chunk_q(qt, m) * (uint32_t)k * 2u;
+            // slots r >= k read the next entries (or zeros); they are
+            // masked where used, so nothing waits for these loads here
 #pragma unroll
-            for (int r = 0; r < KX; ++r) jn[m][r] = r < k ? (uint32_t)ir[r] : (uint32_t)kIdxUnused;
+            for (int r = 0; r < KX; ++r)
+                jn[m][r] = __builtin_amdgcn_raw_buffer_load_b16(idx_rsrc, base + 2u * r, 0, 0);
         }
     };
-    auto stage_rows = [&](int64_t qt) {
+    auto stage_rows = [&](uint32_t qt) {
 #pragma unroll
         for (int m = 0; m < NI; ++m) {
-            const int c8 = (tid + 256 * m) % CH;
-            xv[m] = ld16(ux + (tok_pos(chunk_q(qt, m), s) - t0) * D + 8 * c8);
+            const uint32_t c8 = (uint32_t)((tid + 256 * m) % CH);
+            const uint32_t q = chunk_q(qt, m);
+            const uint32_t pos = (q / sm1) * (uint32_t)s + q % sm1 + 1u;
+            xv[m] = ld16(ux + ((int64_t)pos - t0) * D + 8 * c8);
             int keff = 0;
 #pragma unroll
             for (int r = 0; r < KX; ++r) {
-                const bool used = jn[m][r] != kIdxUnused;
+                const bool used = r < k && jn[m][r] != kIdxUnused;
                 keff += used ? 1 : 0;
-                rv[m][r] = used ? ld16(urefs + (int64_t)jn[m][r] * D + 8 * c8) : zero4;
+                const uint32_t off = used ? (jn[m][r] * D + 8u * c8) * 2u : 0x80000000u;
+                rv[m][r] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(ref_rsrc, off, 0, 0));
             }
             inv[m] = 1.f / (float)keff;
         }
@@ -180,9 +227,12 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
             const int t = item / CH, c8 = item % CH;
             float acc[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = __uint_as_float(rv[m][0][e] << 16);
+                acc[2 * e + 1] = __uint_as_float(rv[m][0][e] & 0xffff0000u);
+            }
 #pragma unroll
-            for (int r = 0; r < KX; ++r)
+            for (int r = 1; r < KX; ++r)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     acc[2 * e] += __uint_as_float(rv[m][r][e] << 16);
@@ -202,14 +252,20 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     if (ntile > 0) {
         stage_idx(tile_q(0));
         stage_rows(tile_q(0));
-        if (ntile > 1) stage_idx(tile_q(1));
+        stage_idx(tile_q(min(1, ntile - 1)));
     }
     for (int it = 0; it < ntile; ++it) {
-        const int64_t qt = tile_q(it);
+        const int64_t qt = (int64_t)tile_q(it);
         // ---- residual tile from the staged rows, then the next loads
         residual();
-        if (it + 1 < ntile) stage_rows(tile_q(it + 1));
-        if (it + 2 < ntile) stage_idx(tile_q(it + 2));
+        // issued on every tile (the last tiles load the final one again), so
+        // the loop body has no branch around its loads
+        // (in this order: the next residual then waits only for the rows)
+        __builtin_amdgcn_sched_barrier(0);
+        stage_rows(tile_q(min(it + 1, ntile - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+        stage_idx(tile_q(min(it + 2, ntile - 1)));
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         // ---- hidden tile and the wave's share of the latent
 #pragma unroll
@@ -224,20 +280,30 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 c[m] = bias1[m];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks) c[m] = mfma16_bf16(a1[m][ks], bd[ks], c[m]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c[m][r] = GELU ? gelu_poly_f32(c[m][r]) : c[m][r];
             }
             f32x4 zc[MD];
 #pragma unroll
             for (int md = 0; md < MD; ++md) zc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
-                u32x4 hv = {pack_bf16(c[2 * j][0], c[2 * j][1]), pack_bf16(c[2 * j][2], c[2 * j][3]),
-                            pack_bf16(c[2 * j + 1][0], c[2 * j + 1][1]),
-                            pack_bf16(c[2 * j + 1][2], c[2 * j + 1][3])};
+                u32x4 hv;
+                if constexpr (GELU) {
+                    // packed-f16 GELU, two pairs per call
+                    f16x2 g0, g1, g2, g3;
+                    gelu4_f16(c[2 * j][0], c[2 * j][1], c[2 * j][2], c[2 * j][3], g0, g1);
+                    gelu4_f16(c[2 * j + 1][0], c[2 * j + 1][1], c[2 * j + 1][2], c[2 * j + 1][3], g2, g3);
+                    hv = u32x4{as_u32(g0), as_u32(g1), as_u32(g2), as_u32(g3)};
 #pragma unroll
-                for (int md = 0; md < MD; ++md)
-                    zc[md] = mfma16_bf16(a2[md][j], as_bf16x8(hv), zc[md]);
+                    for (int md = 0; md < MD; ++md)
+                        zc[md] = mfma16_f16(a2[md][j], as_f16x8(hv), zc[md]);
+                } else {
+                    hv = u32x4{pack_bf16(c[2 * j][0], c[2 * j][1]), pack_bf16(c[2 * j][2], c[2 * j][3]),
+                               pack_bf16(c[2 * j + 1][0], c[2 * j + 1][1]),
+                               pack_bf16(c[2 * j + 1][2], c[2 * j + 1][3])};
+#pragma unroll
+                    for (int md = 0; md < MD; ++md)
+                        zc[md] = mfma16_bf16(a2[md][j], as_bf16x8(hv), zc[md]);
+                }
             }
 #pragma unroll
             for (int md = 0; md < MD; ++md)
@@ -245,12 +311,18 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 for (int r = 0; r < 4; ++r) zp[w][16 * md + 4 * lq + r][16 * nt + l16] = zc[md][r];
         }
         __syncthreads();
-        // ---- sum the waves' shares, add b2, round, store
-        for (int i = tid; i < TT * DC; i += 256) {
-            const int t = i / DC, o = i % DC;
-            if (qt + t >= qend) continue;
-            const float z = zp[0][o][t] + zp[1][o][t] + zp[2][o][t] + zp[3][o][t] + (b2 ? b2[o] : 0.f);
-            lat[((int64_t)unit * Ncap + qt + t) * DC + o] = f2bf(z);
+        // ---- sum the waves' shares, add b2, round, store (pairs of latent
+        // values; rows past the range fall outside the store resource)
+        static_assert((TT * DC / 2) % 256 == 0, "whole store passes");
+#pragma unroll
+        for (int n = 0; n < TT * DC / 512; ++n) {
+            const int i = tid + 256 * n;
+            const int t = i / (DC / 2), o = 2 * (i % (DC / 2));
+            const float z0 = zp[0][o][t] + zp[1][o][t] + zp[2][o][t] + zp[3][o][t] + bias2[0];
+            const float z1 = zp[0][o + 1][t] + zp[1][o + 1][t] + zp[2][o + 1][t] + zp[3][o + 1][t] +
+                             bias2[1];
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(z0, z1), lat_rsrc,
+                                                  (((uint32_t)qt + t) * DC + o) * 2u, 0, 0);
         }
     }
 }
@@ -286,6 +358,11 @@ bool launch_cmfma_dc(const Dims &dm, const void *x, int64_t t0, int64_t t1, int6
 bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                           int64_t nq, const MlpArgs &m, const CacheArgs &c, hipStream_t st) {
     if (dm.dtype != 1 || (m.hidden != 128 && m.hidden != 256)) return false;
+    // the index lists and reference rows of a unit are read through buffer
+    // resources with 31-bit byte ranges
+    if (dm.N * dm.k * 2 > INT32_MAX || dm.R * dm.d * 2 > INT32_MAX ||
+        dm.N * dm.dc * 2 > INT32_MAX)
+        return false;
     if (dm.d == 128)
         return m.hidden == 256 ? launch_cmfma_dc<128, 256>(dm, x, t0, t1, q0, nq, m, c, st)
                                : launch_cmfma_dc<128, 128>(dm, x, t0, t1, q0, nq, m, c, st);
