@@ -483,7 +483,9 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 // one token per 32-reference block.  A block takes 256 consecutive compressed
 // tokens (4 waves x 2 N-tiles of 32) and streams the references they can see
 // (j * s < p) through LDS in stages of 64, double-buffered, loaded straight
-// from global memory with 16-byte chunks XOR-swizzled by (row % 8).
+// from global memory with 16-byte chunks XOR-swizzled per row (row % 16 for
+// head_dim 128, (row / 2) % 8 for 64: the 16 rows one pass of a 16-byte LDS
+// read touches then fall in disjoint banks).
 //
 // Per lane, a descending list of the LK best scores is kept as packed floats:
 // the low `ibits` mantissa bits of each score are replaced by imask - ordinal
@@ -633,6 +635,9 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     constexpr int CH = D / 8;
     constexpr int RB = 64;
     constexpr int DMA_IT = RB * CH / 256;
+    // LDS chunk swizzle of reference row r (bank = 4 chunk + 32 (r % 2) for
+    // 128-byte rows, 4 chunk for 256-byte rows)
+    auto swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
     __shared__ __attribute__((aligned(16))) bf16_t rt[2][RB][D];
     __shared__ __attribute__((aligned(16))) float nsq[2][RB];
     __shared__ float red[4];
@@ -682,7 +687,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
         for (int m = 0; m < DMA_IT; ++m) {
             const int it = tid + 256 * m;
             const int row = it / CH, c8 = it % CH;
-            const int sc8 = c8 ^ (row & 7);
+            const int sc8 = c8 ^ swz(row);
             const uint32_t j = (uint32_t)min(jbase + row, ncand_max - 1);
             __builtin_amdgcn_global_load_lds(
                 (const void *)at_byte(urefs, (j * D + 8u * sc8) * 2u),
@@ -725,7 +730,7 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
             const int r = 32 * mb + l32;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int pc = (2 * ks + hl) ^ (r & 7);
+                const int pc = (2 * ks + hl) ^ swz(r);
                 const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&rt[b][r][8 * pc]));
                 acc0 = mfma32_bf16(a, xb[0][ks], acc0);
                 acc1 = mfma32_bf16(a, xb[1][ks], acc1);

@@ -206,6 +206,14 @@ def test_llama_layer_32k_sampled():
               n_centroids=w.n_centroids, positions=pos, decode_heads=[(0, 0), (0, 7)])
 
 
+def test_long_reference_ranges_checked_everywhere():
+    # every token of a 12288-token context with stride 8 (up to 1536
+    # candidate references per token, 48 reference blocks of the top-k
+    # search), compared index for index with the oracle
+    _run_case("long-reference-ranges", 1, 1, 4, 12288, 128, 8, 4, 32, 256, dk.BF16, seed=60,
+              n_dirs=8, n_centroids=256)
+
+
 def test_exact_ties_beyond_candidate_list_take_exact_fallback():
     # 12 identical reference rows (more than the approximate candidate list
     # keeps) and tokens equal to them: the certificate cannot separate the
