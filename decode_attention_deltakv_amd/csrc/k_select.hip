@@ -584,7 +584,7 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
     for (int pass = 0; pass < LK; ++pass) {
 #pragma unroll
         for (int i = pass & 1; i + 1 < LK; i += 2) {
-            const bool sw = dd[i + 1] < dd[i] || (dd[i + 1] == dd[i] && jj[i + 1] < jj[i]);
+            const bool sw = (dd[i + 1] < dd[i]) | ((dd[i + 1] == dd[i]) & (jj[i + 1] < jj[i]));
             const double td = dd[i];
             const int tj = jj[i];
             dd[i] = sw ? dd[i + 1] : dd[i];
@@ -626,7 +626,7 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
 }
 
 template <int D, int LK>
-__global__ __launch_bounds__(256, 2) void dist_topk_kernel(
+__global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, const float *__restrict__ sqn, int64_t Rcap, int64_t Ncap,
     int64_t q0, int64_t nq, int U, int ntiles, uint32_t imask, int ibits,
@@ -783,9 +783,204 @@ __global__ __launch_bounds__(256, 2) void dist_topk_kernel(
     rmax2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
     const bf16_t *xr = x + ((int64_t)unit * nrows + (pos - t0)) * D;
-    rescore_lane<D, LK>(xr, urefs, lst, imask, ibits, k, rmax2, valid,
-                        idx + ((int64_t)unit * Ncap + qn) * k,
-                        ((uint64_t)unit << 32) | (uint64_t)(qn - q0), flist, fcount);
+    uint16_t *out = idx + ((int64_t)unit * Ncap + qn) * k;
+    // First pass of the rescore, in fp32: d'_e = |r_e|^2 - 2 x.r_e (the
+    // distance minus |x|^2, which every candidate of the token shares) from
+    // bf16 dot products (the products are exact; eight partial sums per dot
+    // product) with a rigorous bound on the error of each d'_e.  When the
+    // bounds order the candidates the result needs (the first min(k, n)
+    // positions and the one after them) and the certificate holds with the
+    // k-th candidate's upper bound, the result is written from this pass and
+    // true is returned; false sends the lane to the exact fp64 rescore.  Each
+    // dot-product step's rounding is bounded by 2^-23 relative
+    // (round-to-nearest or toward zero).
+    //
+    // The token's row is the lane's MFMA operand, made whole by the half
+    // swap; the candidate rows are gathered through this wave's quarter of
+    // the (now idle) reference-tile buffer: a round brings one 128-byte half
+    // row of candidate e for LPR lanes' tokens, 8 lanes per half row
+    // (coalesced), slots XOR-swizzled so that each lane then reads its own
+    // half row without bank conflicts.
+    auto rescore_fast = [&](const bf16_t *xrow_unused, uint16_t *o) -> bool {
+        (void)xrow_unused;
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        constexpr int NA = 8;             // partial sums per dot product
+        constexpr int LPR = D / 2;        // lanes per round
+        constexpr int NDM = LPR / 8;      // gather instructions per round
+        constexpr int HR = D / 64;        // half rows per row
+        constexpr int NG = 64 / LPR;      // lane groups
+        u32x4 xs0[KSTEPS], xs1[KSTEPS];   // chunk c: xs0[c / 2] (even), xs1[c / 2] (odd)
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4 a = __builtin_bit_cast(u32x4, xb[0][ks]);
+            const u32x4 b = __builtin_bit_cast(u32x4, xb[1][ks]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t aq = a[q], bq = b[q];
+                const auto sw = __builtin_amdgcn_permlane32_swap(aq, bq, false, false);
+                xs0[ks][q] = sw[0];
+                xs1[ks][q] = sw[1];
+            }
+        }
+        auto xw = [&](int c, int i) -> uint32_t {
+            const uint32_t v = (c & 1) ? xs1[c >> 1][i] : xs0[c >> 1][i];
+            return v;
+        };
+        auto dot = [](uint32_t a, uint32_t b, float acc) {
+            return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                                   __builtin_bit_cast(bf16x2_t, b), acc, false);
+        };
+        auto tree = [](const float (&v)[NA]) {
+            return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        };
+        int jj[LK];
+        bool cv[LK];
+#pragma unroll
+        for (int e = 0; e < LK; ++e) {
+            cv[e] = lst[e] != -INFINITY;
+            jj[e] = cv[e] ? unpack_ordinal(lst[e], imask) : 0;
+        }
+        float xa[NA];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) xa[a] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2 * KSTEPS; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[4 * (c & 1) + i] = dot(xw(c, i), xw(c, i), xa[4 * (c & 1) + i]);
+        const float xsq = tree(xa);
+        // error of a partial-sum dot product of D terms over NA sums: at most
+        // D / NA + 3 roundings on any path, each within 2^-23 of the running
+        // sum, hence <= g * sum |terms|
+        constexpr float u = 1.1920929e-07f;  // 2^-23
+        constexpr float g = (float)(D / NA + 4) * u * 1.01f;
+        const float xsq_hi = xsq * (1.f + 4.f * g);
+        char *wst = reinterpret_cast<char *>(&rt[0][0][0]) + w * (64 * D);
+        float dp[LK], er[LK];
+#pragma unroll
+        for (int e = 0; e < LK; ++e) {
+            dp[e] = INFINITY;
+            er[e] = 0.f;
+        }
+        // one candidate at a time (a run-time loop: the registers of one
+        // candidate's rounds only)
+#pragma unroll 1
+        for (int e = 0; e < LK; ++e) {
+            int je = jj[0];
+            bool ce = cv[0];
+#pragma unroll
+            for (int q = 1; q < LK; ++q) {
+                je = q == e ? jj[q] : je;
+                ce = q == e ? cv[q] : ce;
+            }
+            float ra[NA];
+#pragma unroll
+            for (int a = 0; a < NA; ++a) ra[a] = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < HR; ++hh) {
+#pragma unroll
+                for (int gq = 0; gq < NG; ++gq) {
+                    // the previous round's reads are done before its slots
+                    // are filled again
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+                    for (int m = 0; m < NDM; ++m) {
+                        const int tl = 8 * m + (lane >> 3);
+                        const int src = __shfl(je, gq * LPR + tl);
+                        const int cc = (lane & 7) ^ ((tl >> 1) & 7);
+                        __builtin_amdgcn_global_load_lds(
+                            (const void *)at_byte(urefs, ((uint32_t)src * D + 64u * hh + 8u * cc) * 2u),
+                            (__attribute__((address_space(3))) void *)(wst + 1024 * m), 16, 0, 0);
+                    }
+                    wait_vm_all();
+                    if (NG == 1 || lane / LPR == gq) {
+                        const int tl = lane - gq * LPR;
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) {
+                            const int pp = cc ^ ((tl >> 1) & 7);
+                            const u32x4 rv = *reinterpret_cast<const u32x4 *>(wst + 128 * tl + 16 * pp);
+                            const int c = 8 * hh + cc;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const uint32_t rw = rv[i];
+                                ra[4 * (c & 1) + i] = dot(xw(c, i), rw, ra[4 * (c & 1) + i]);
+                            }
+                        }
+                    }
+                }
+            }
+            const float rsq = usqn[je];  // fp32 norm: within 8 u rsq
+            const float xr_ = tree(ra);
+            // |2 x.r - 2 xr| <= 2 g |x||r| <= g (|x|^2 + |r|^2); evaluating
+            // rsq - 2 xr adds <= u (rsq + 2 |xr|); a denormal product flushed
+            // to zero is within 2^-126 max(|x|, |r|) each
+            const float dpe = ce ? rsq - 2.f * xr_ : INFINITY;
+            const float ere = ce ? 8.f * u * rsq + g * (xsq_hi + rsq) + u * (rsq + 2.f * fabsf(xr_)) +
+                                       1e-30f * (1.f + xsq_hi + rsq)
+                                 : 0.f;
+#pragma unroll
+            for (int q = 0; q < LK; ++q) {
+                dp[q] = q == e ? dpe : dp[q];
+                er[q] = q == e ? ere : er[q];
+            }
+        }
+        if (!valid) return true;
+        // sort by d' (ordinals break exact ties; a tie cannot be certified)
+#pragma unroll
+        for (int pass = 0; pass < LK; ++pass) {
+#pragma unroll
+            for (int i = pass & 1; i + 1 < LK; i += 2) {
+                const bool sw = (dp[i + 1] < dp[i]) | ((dp[i + 1] == dp[i]) & (jj[i + 1] < jj[i]));
+                const float td = dp[i], te = er[i];
+                const int tj = jj[i];
+                dp[i] = sw ? dp[i + 1] : dp[i];
+                er[i] = sw ? er[i + 1] : er[i];
+                jj[i] = sw ? jj[i + 1] : jj[i];
+                dp[i + 1] = sw ? td : dp[i + 1];
+                er[i + 1] = sw ? te : er[i + 1];
+                jj[i + 1] = sw ? tj : jj[i + 1];
+            }
+        }
+        int nvalid = 0;
+#pragma unroll
+        for (int e = 0; e < LK; ++e) nvalid += cv[e] ? 1 : 0;
+        const int kk = min(k, nvalid);
+        // a certified gap must also clear the fp64 rounding of the exact values
+        const float slack = 1e-9f * (xsq_hi + rmax2);
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i + 1 < LK; ++i)
+            if (i < kk && i + 1 < nvalid) ok = ok && (dp[i + 1] - er[i + 1]) - (dp[i] + er[i]) > slack;
+        if (lst[LK - 1] != -INFINITY) {
+            // certificate in d' terms: an excluded reference has
+            // d' >= -2 (tau + delta); the k-th candidate has d' <= dp + er
+            const double tp = (double)lst[LK - 1];
+            const double tau = tp + fabs(tp) * ldexp(1.0, ibits - 21);
+            const double rm = sqrt((double)rmax2 * (1.0 + 1e-6));
+            const double xn = sqrt((double)xsq_hi);
+            const double nu = (double)(D + 1) * ldexp(1.0, -23);
+            const double gam = nu / (1.0 - nu);
+            const double delta = 2.0 * gam * (xn * rm + rm * rm) + 1e-30;
+            double dk_ = (double)dp[0] + (double)er[0];
+#pragma unroll
+            for (int e = 1; e < LK; ++e) dk_ = (e == kk - 1) ? (double)dp[e] + (double)er[e] : dk_;
+            const double lb = -2.0 * (tau + delta);
+            ok = ok && (lb - 1e-9 * ((double)xsq_hi + fabs(tau) + delta)) > dk_;
+        }
+        if (!ok) return false;
+#pragma unroll
+        for (int r = 0; r < LK; ++r)
+            if (r < k) o[r] = r < kk ? (uint16_t)jj[r] : kIdxUnused;
+        return true;
+    };
+
+    // fp32 pass with error bounds (lists of up to 8: its partial sums for
+    // longer ones would not fit the registers); the lanes it cannot settle
+    // take the exact fp64 rescore
+    bool settled = false;
+    if constexpr (LK <= 8) settled = rescore_fast(xr, out);
+    if (!settled)
+        rescore_lane<D, LK>(xr, urefs, lst, imask, ibits, k, rmax2, valid, out,
+                            ((uint64_t)unit << 32) | (uint64_t)(qn - q0), flist, fcount);
 }
 
 __global__ void zero_u32_kernel(uint32_t *p) {
