@@ -1253,14 +1253,21 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             __builtin_amdgcn_sched_barrier(0);
             kload(nt0, nxt);
             __builtin_amdgcn_sched_barrier(0);
-            // hidden tile and partial scores, 32 hidden units per step
+            // hidden tile and partial scores, 32 hidden units per step; the
+            // products of step j + 1 are issued before the GELU of step j
             f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
+            auto hstep = [&](int j, f32x4 &c0, f32x4 &c1) {
                 const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 4 * lq]);
                 const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 16 + 4 * lq]);
-                const f32x4 c0 = mfma16_bf16(wK[2 * j], in.z, b0);
-                const f32x4 c1 = mfma16_bf16(wK[2 * j + 1], in.z, b1);
+                c0 = mfma16_bf16(wK[2 * j], in.z, b0);
+                c1 = mfma16_bf16(wK[2 * j + 1], in.z, b1);
+            };
+            f32x4 cn0, cn1;
+            hstep(0, cn0, cn1);
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const f32x4 c0 = cn0, c1 = cn1;
+                if (j + 1 < KJ) hstep(j + 1, cn0, cn1);
                 f16x2 g0, g1, g2, g3;
                 gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
                 gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
@@ -1422,6 +1429,59 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
         };
 
+        // One tile's value work, without branches (kScl: the two score waves'
+        // maxima differ and their weights are scaled by es0, es1).  The
+        // products of hidden block nb + 1 are issued before the GELU of block
+        // nb, and the reference-row products are spread over the blocks, so
+        // matrix and vector work overlap.
+        auto vbody = [&](auto kScl, const bf16x8 (&zv)[2], bf16_t (*cur)[D], const f16x4 (&pa)[2],
+                         float es0, float es1, int sl) {
+            constexpr bool SCL = decltype(kScl)::value;
+            u32x4 pv = {0u, 0u, 0u, 0u};
+            // reference-row step q: rows 64 s2 + 32 ks + 8 lq of score wave
+            // s2's tokens, value columns block nc
+            constexpr int NQ = 4 * NC;  // reference steps: score wave s2, half ks, block nc
+            auto rstep = [&](int q) {
+                const int s2 = q / (2 * NC), ks = (q / NC) & 1, nc = q % NC;
+                const int rb = 64 * s2 + 32 * ks + 8 * lq;
+                if (nc == 0) {
+                    pv = *reinterpret_cast<const u32x4 *>(&wr[sl][l16][rb]);
+                    if constexpr (SCL) {
+                        const float es = s2 ? es1 : es0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pv[e] = pack_bf16(__uint_as_float(pv[e] << 16) * es,
+                                              __uint_as_float(pv[e] & 0xffff0000u) * es);
+                    }
+                }
+                const int c = cb + 16 * nc + 4 * (l16 & 3);
+                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
+                const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
+                const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
+                acc_r[nc] = mfma16_bf16(as_bf16x8(pv), as_bf16x8(bv), acc_r[nc]);
+            };
+            f32x4 hn0 = mfma16_bf16(zv[0], wV[0], bV[0]);
+            f32x4 hn1 = mfma16_bf16(zv[1], wV[0], bV[0]);
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const f32x4 c0 = hn0, c1 = hn1;
+                if (nb + 1 < NBV) {
+                    hn0 = mfma16_bf16(zv[0], wV[nb + 1], bV[nb + 1]);
+                    hn1 = mfma16_bf16(zv[1], wV[nb + 1], bV[nb + 1]);
+                }
+                f16x2 g0, g1, g2, g3;
+                gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
+                gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
+                const u32x2 h0 = {as_u32(g0), as_u32(g1)};
+                const u32x2 h1 = {as_u32(g2), as_u32(g3)};
+                acc_h[nb] = mfma16k16_f16(pa[0], __builtin_bit_cast(f16x4, h0), acc_h[nb]);
+                acc_h[nb] = mfma16k16_f16(pa[1], __builtin_bit_cast(f16x4, h1), acc_h[nb]);
+#pragma unroll
+                for (int q = NQ * nb / NBV; q < NQ * (nb + 1) / NBV; ++q) rstep(q);
+            }
+        };
+
         auto vtile = [&](int it, const bf16x8 (&zv)[2], bf16_t (*cur)[D]) {
             const int sl = it & 1;
             // maxima the score waves used for this tile
@@ -1450,55 +1510,18 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 pa[s2] = *reinterpret_cast<const f16x4 *>(&pw[sl][s2][l16][4 * lq]);
-            const bool scl = __builtin_amdgcn_ballot_w64(split) != 0;
-            float es[2] = {1.f, 1.f};
-            if (scl) {
+            if (__builtin_amdgcn_ballot_w64(split) == 0) {
+                vbody(std::integral_constant<bool, false>{}, zv, cur, pa, 1.f, 1.f, sl);
+            } else {
                 // the two waves used different maxima: bring the lower one's
                 // weights to the larger maximum
                 const float a0 = msl[sl][0][l16], a1 = msl[sl][1][l16];
                 const float mx = fmaxf(a0, a1);
-                es[0] = a0 == -INFINITY ? 0.f : __expf(a0 - mx);
-                es[1] = a1 == -INFINITY ? 0.f : __expf(a1 - mx);
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) pa[s2] = pa[s2] * (_Float16)es[s2];
-            }
-            // hidden tiles (tokens x hidden), GELU, acc_h
-#pragma unroll
-            for (int nb = 0; nb < NBV; ++nb) {
-                const f32x4 c0 = mfma16_bf16(zv[0], wV[nb], bV[nb]);
-                const f32x4 c1 = mfma16_bf16(zv[1], wV[nb], bV[nb]);
-                f16x2 g0, g1, g2, g3;
-                gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
-                gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
-                const u32x2 h0 = {as_u32(g0), as_u32(g1)};
-                const u32x2 h1 = {as_u32(g2), as_u32(g3)};
-                acc_h[nb] = mfma16k16_f16(pa[0], __builtin_bit_cast(f16x4, h0), acc_h[nb]);
-                acc_h[nb] = mfma16k16_f16(pa[1], __builtin_bit_cast(f16x4, h1), acc_h[nb]);
-            }
-            // reference rows: rows 64 s2 .. 64 s2 + 63 belong to score wave s2
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int rb = 64 * s2 + 32 * ks + 8 * lq;
-                    u32x4 pv = *reinterpret_cast<const u32x4 *>(&wr[sl][l16][rb]);
-                    if (scl) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            pv[e] = pack_bf16(__uint_as_float(pv[e] << 16) * es[s2],
-                                              __uint_as_float(pv[e] & 0xffff0000u) * es[s2]);
-                    }
-                    const bf16x8 pwv = as_bf16x8(pv);
-#pragma unroll
-                    for (int nc = 0; nc < NC; ++nc) {
-                        const int c = cb + 16 * nc + 4 * (l16 & 3);
-                        const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
-                        const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
-                        const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
-                        const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
-                        acc_r[nc] = mfma16_bf16(pwv, as_bf16x8(bv), acc_r[nc]);
-                    }
-                }
+                const float e0 = a0 == -INFINITY ? 0.f : __expf(a0 - mx);
+                const float e1 = a1 == -INFINITY ? 0.f : __expf(a1 - mx);
+                pa[0] = pa[0] * (_Float16)e0;
+                pa[1] = pa[1] * (_Float16)e1;
+                vbody(std::integral_constant<bool, true>{}, zv, cur, pa, e0, e1, sl);
             }
         };
 
