@@ -44,6 +44,7 @@ constexpr int kTargetBlocks = 512;
 constexpr int kRefPart = 512;  // reference rows per partition
 constexpr int kMaxParts = 4096; // partitions per unit (combine keeps their weights in LDS)
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
+constexpr int kCombThreads = 256;               // threads of the combine kernel
 
 // The q.R^K table keeps its query heads padded to a multiple of 4 (zeros), so
 // a lane can read the 4 heads of its row group with one 16-byte load, and one
@@ -276,6 +277,7 @@ __global__ __launch_bounds__(256) void main_kernel(
 }
 
 // Block-wide max or sum (256 threads).
+template <int NW = 4>
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = is_max ? wave_max(v) : wave_sum(v);
@@ -283,7 +285,7 @@ __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) 
     if (lane == 0) red[w] = v;
     __syncthreads();
     float r = red[0];
-    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    for (int i = 1; i < NW; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
     return r;
 }
 
@@ -337,16 +339,26 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
 #pragma unroll
             for (int ks = 0; ks < kMaxD / 32; ++ks)
                 qb[ks] = as_bf16x8(l16 < G && 32 * ks < d ? ld16(qg + 32 * ks + 8 * lq) : zero4);
+            // all of the block's row loads first (every load issued: rows
+            // past the range read the last row, columns past d the last
+            // chunk, both under zero weight or never stored)
+            constexpr int NKS = kMaxD / 32;
+            u32x4 rv[4][NKS];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int64_t j0 = (int64_t)blockIdx.x * 256 + 64 * it + 16 * w;
+                const int64_t jr = min(j0 + l16, Rt - 1 < 0 ? 0 : Rt - 1);
+                const T *r = krefs + (unit * Rcap + jr) * d;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) rv[it][ks] = ld16(r + min(32 * ks, d - 32) + 8 * lq);
+            }
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int64_t j0 = (int64_t)blockIdx.x * 256 + 64 * it + 16 * w;
                 if (j0 > Rt) break;
-                const int64_t jr = min(j0 + l16, Rt - 1 < 0 ? 0 : Rt - 1);
-                const T *r = krefs + (unit * Rcap + jr) * d;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < kMaxD / 32; ++ks)
-                    if (32 * ks < d) acc = mfma16_bf16(as_bf16x8(ld16(r + 32 * ks + 8 * lq)), qb[ks], acc);
+                for (int ks = 0; ks < NKS; ++ks) acc = mfma16_bf16(as_bf16x8(rv[it][ks]), qb[ks], acc);
                 // acc[r] = qR[j0 + 4 lq + r][head l16]
                 if (l16 < GQ) {
 #pragma unroll
@@ -429,37 +441,38 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
 // with one float4 column per thread and the partitions split across thread
 // groups, so all partition loads of a thread are independent.
 template <typename T>
-__global__ __launch_bounds__(256) void combine2_kernel(int Hq, int G, int d, int H, int64_t P,
+__global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, int d, int H, int64_t P,
                                                        const float *__restrict__ part,
                                                        const T *__restrict__ vw2, int vhid,
                                                        const float *__restrict__ vb2,
                                                        float *__restrict__ out) {
+    constexpr int NT = kCombThreads, NW = NT / 64, NGR = 8;
     __shared__ float wgt[kMaxParts];
-    __shared__ f32x4 gred[8][(kMaxD + kMaxH) / 4];
+    __shared__ f32x4 gred[NGR][(kMaxD + kMaxH) / 4];
     __shared__ float accr[kMaxD];
     __shared__ float acch[kMaxH];
-    __shared__ float ored[4][kMaxD];
-    __shared__ float red[4];
+    __shared__ float ored[NT / 64][kMaxD];
+    __shared__ float red[NW];
     const int gq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int h = gq / G, g = gq % G;
     const int64_t unit = (int64_t)b * H + h;
     const float *base = part + (unit * P * G + g) * kPStride;
     const int64_t pstep = (int64_t)G * kPStride;
     float mx = -INFINITY;
-    for (int64_t p = tid; p < P; p += 256) mx = fmaxf(mx, base[p * pstep]);
-    const float M = block_reduce(mx, red, true);
+    for (int64_t p = tid; p < P; p += NT) mx = fmaxf(mx, base[p * pstep]);
+    const float M = block_reduce<NW>(mx, red, true);
     float lsum = 0.f, ltsum = 0.f;
-    for (int64_t p = tid; p < P; p += 256) {
+    for (int64_t p = tid; p < P; p += NT) {
         const float wp = __expf(base[p * pstep] - M);
         wgt[p] = wp;
         lsum += wp * base[p * pstep + 1];
         ltsum += wp * base[p * pstep + 2];
     }
-    const float L = block_reduce(lsum, red, false);
-    const float Lt = block_reduce(ltsum, red, false);  // (its barriers also publish wgt)
+    const float L = block_reduce<NW>(lsum, red, false);
+    const float Lt = block_reduce<NW>(ltsum, red, false);  // (its barriers also publish wgt)
     // columns: acc_r as d/4 float4s, then acc_h as vhid/4 float4s
     const int ncr = d / 4, nc = ncr + vhid / 4;
-    const int ngrp = min(8, 256 / nc);
+    const int ngrp = min(NGR, NT / nc);
     const int col = tid % nc, grp = tid / nc;
     if (grp < ngrp) {
         const int off = col < ncr ? 4 + 4 * col : 4 + kMaxD + 4 * (col - ncr);
@@ -481,19 +494,21 @@ __global__ __launch_bounds__(256) void combine2_kernel(int Hq, int G, int d, int
     }
     __syncthreads();
     // out[c] = (acc_r[c] + W2V[c] . acc_h + Lt b2V[c]) / L; the hidden sum of
-    // a row is split over 256 / d threads
-    const int nsp = 256 / d;
+    // a row is split over nsp threads, at least 8 hidden units each
+    const int nsp = min(NT / d, vhid / 8);
     const int c = tid % d, sp = tid / d;
     const int oper = vhid / nsp;
-    float wsum = 0.f;
-    const T *wr = vw2 + (int64_t)c * vhid + sp * oper;
-    for (int o = 0; o < oper; o += 8) {
-        float v[8];
-        load8(wr + o, v);
+    if (sp < nsp) {
+        float wsum = 0.f;
+        const T *wr = vw2 + (int64_t)c * vhid + sp * oper;
+        for (int o = 0; o < oper; o += 8) {
+            float v[8];
+            load8(wr + o, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wsum += v[e] * acch[sp * oper + o + e];
+            for (int e = 0; e < 8; ++e) wsum += v[e] * acch[sp * oper + o + e];
+        }
+        ored[sp][c] = wsum;
     }
-    ored[sp][c] = wsum;
     __syncthreads();
     if (tid < d) {
         float ws = 0.f;
@@ -1692,7 +1707,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            (const T *)kc.lat, kc.idx, (const T *)vc.refs, (const T *)vc.lat,
                            vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act, (const T *)vd.w1,
                            vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part);
-    hipLaunchKernelGGL(combine2_kernel<T>, dim3(Hq, dm.B), dim3(256), 0, st, Hq, G, dm.d, dm.H,
+    hipLaunchKernelGGL(combine2_kernel<T>, dim3(Hq, dm.B), dim3(kCombThreads), 0, st, Hq, G, dm.d, dm.H,
                        pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out);
     return hipGetLastError();
 }
