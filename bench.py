@@ -42,18 +42,22 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # change to it the traffic is reported as null until it is measured again.
 DECODE_TRAFFIC = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "592829c37ca7",
-    "fetch_kib": {"main_ws": 85708.6, "prep": 8539.3, "combine2": 2389.0},
-    "write_kib": {"main_ws": 3880.1, "prep": 1061.2, "combine2": 16.0},
+    "source_sha256": "db050ce7c7f4",
+    "fetch_kib": {"main_ws": 85700.2, "prep": 8539.3, "combine2": 2388.5},
+    "write_kib": {"main_ws": 3880.3, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
 
 
 def decode_source_sha():
-    path = os.path.join(ROOT, "decode_attention_deltakv_amd", "csrc", "k_decode.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:12]
+    """SHA-256 prefix of the decode kernels' sources (the kernel file and the
+    device headers it includes)."""
+    h = hashlib.sha256()
+    for name in ("k_decode.hip", "dk_mfma.h", "dk_common.h"):
+        with open(os.path.join(ROOT, "decode_attention_deltakv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:12]
 
 
 def decode_traffic_bytes(wl):

@@ -149,21 +149,4 @@ __device__ __forceinline__ void gelu4_f16(float a, float b, float c, float d, f1
     r1 = u1 * phi1;
 }
 
-// GELU in fp32, u * Phi(u) with Phi(u) ~= clamp01(0.5 + u * P(u * u)), P of
-// degree 6 fitted to the standard normal CDF on |u| <= 4 (positive leading
-// coefficient, so the clamp saturates outside).  Largest error of Phi over the
-// real line 1.3e-4; used by the bf16 compression path.
-__device__ __forceinline__ float gelu_poly_f32(float u) {
-    const float t = u * u;
-    float p = 2.96670575e-08f;
-    p = __builtin_fmaf(p, t, -1.96252867e-06f);
-    p = __builtin_fmaf(p, t, 5.54439211e-05f);
-    p = __builtin_fmaf(p, t, -8.89424659e-04f);
-    p = __builtin_fmaf(p, t, 9.15395090e-03f);
-    p = __builtin_fmaf(p, t, -6.54541771e-02f);
-    p = __builtin_fmaf(p, t, 3.98554853e-01f);
-    const float phi = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, p, 0.5f), 0.0f, 1.0f);
-    return u * phi;
-}
-
 }  // namespace dk
