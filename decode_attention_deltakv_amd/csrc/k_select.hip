@@ -638,7 +638,11 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     // LDS chunk swizzle of reference row r (bank = 4 chunk + 32 (r % 2) for
     // 128-byte rows, 4 chunk for 256-byte rows)
     auto swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-    __shared__ __attribute__((aligned(16))) bf16_t rt[2][RB][D];
+    // reference tiles of two stages: two objects, so the compiler can tell
+    // the DMA fill of one from the reads of the other (one array would make
+    // every read wait for the fill just issued)
+    __shared__ __attribute__((aligned(16))) bf16_t rtA[RB][D];
+    __shared__ __attribute__((aligned(16))) bf16_t rtB[RB][D];
     __shared__ __attribute__((aligned(16))) float nsq[2][RB];
     __shared__ float red[4];
 
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     asm volatile("" : "+v"(nmask));
 
     float rmax2 = 0.f;
-    auto stage_load = [&](int jbase, int b) {
+    auto stage_load = [&](int jbase, bf16_t (*dst)[D]) {
 #pragma unroll
         for (int m = 0; m < DMA_IT; ++m) {
             const int it = tid + 256 * m;
@@ -691,13 +695,13 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
             const uint32_t j = (uint32_t)min(jbase + row, ncand_max - 1);
             __builtin_amdgcn_global_load_lds(
                 (const void *)at_byte(urefs, (j * D + 8u * sc8) * 2u),
-                (__attribute__((address_space(3))) void *)&rt[b][(256 * m + 64 * w) / CH][0], 16,
+                (__attribute__((address_space(3))) void *)&dst[(256 * m + 64 * w) / CH][0], 16,
                 0, 0);
         }
     };
     float sq_next = 0.f;
     const int nstage = (int)((ncand_max + RB - 1) / RB);
-    stage_load(0, 0);
+    stage_load(0, rtA);
     if (tid < RB) {
         const float v = tid < ncand_max ? usqn[tid] : 0.f;
         rmax2 = fmaxf(rmax2, v);
@@ -706,13 +710,15 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     wait_vm_all();
     __syncthreads();
 
-    for (int st = 0; st < nstage; ++st) {
+    // one stage: 64 references from cur (nsq[b]) while the next stage is
+    // gathered into nxt
+    auto stage = [&](int st, bf16_t (*cur)[D], bf16_t (*nxt)[D]) {
         const int b = st & 1;
         const int jst = st * RB;
         const bool more = st + 1 < nstage;
         if (more) {
-            stage_load(jst + RB, b ^ 1);
             if (tid < RB) sq_next = (jst + RB + tid < ncand_max) ? usqn[jst + RB + tid] : 0.f;
+            stage_load(jst + RB, nxt);
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -731,7 +737,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const int pc = (2 * ks + hl) ^ swz(r);
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&rt[b][r][8 * pc]));
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&cur[r][8 * pc]));
                 acc0 = mfma32_bf16(a, xb[0][ks], acc0);
                 acc1 = mfma32_bf16(a, xb[1][ks], acc1);
             }
@@ -775,6 +781,10 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
         }
         wait_vm_all();
         __syncthreads();
+    };
+    for (int st = 0; st < nstage; st += 2) {
+        stage(st, rtA, rtB);
+        if (st + 1 < nstage) stage(st + 1, rtB, rtA);
     }
     // largest reference norm the block saw (bounds the score error)
     rmax2 = wave_max(rmax2);
@@ -854,7 +864,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
         constexpr float u = 1.1920929e-07f;  // 2^-23
         constexpr float g = (float)(D / NA + 4) * u * 1.01f;
         const float xsq_hi = xsq * (1.f + 4.f * g);
-        char *wst = reinterpret_cast<char *>(&rt[0][0][0]) + w * (64 * D);
+        char *wst = reinterpret_cast<char *>(w < 2 ? &rtA[0][0] : &rtB[0][0]) + (w & 1) * (64 * D);
         float dp[LK], er[LK];
 #pragma unroll
         for (int e = 0; e < LK; ++e) {
