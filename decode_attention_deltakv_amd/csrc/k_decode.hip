@@ -1039,8 +1039,9 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
 // Reference tokens are separate partitions handled by all four waves.
 constexpr float kSlack = 8.f;
 
-// EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8)
-template <int D, int DC, int HID, int EG>
+// EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8).
+// KX: references per token (k = 4 or k = 8).
+template <int D, int DC, int HID, int EG, int KX>
 __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -1050,7 +1051,6 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
     float *__restrict__ part) {
-    constexpr int KX = 4;              // references per token
     constexpr int TT = 32;             // tokens per tile
     constexpr int TH = 16;             // tokens per score wave
     constexpr int MB = HID / 16;       // 16-row hidden blocks (score waves)
@@ -1060,6 +1060,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     constexpr int DV = D / 2;          // value columns per value wave
     constexpr int NC = DV / 16;
     constexpr int ROWS = TT * KX;      // gathered V rows per tile
+    constexpr int BROWS = 128;         // rows per LDS buffer (a tile at k = 4, half at 8)
+    constexpr int WH = KX == 4 ? 16 : 4 * EG;  // query-head rows kept of the row weights
     constexpr int CH = D / 8;          // 16-byte chunks per row
     constexpr int RPD = 64 / CH;       // rows per gather instruction
     constexpr int NDMA = (ROWS / 2) / RPD;  // gather instructions per value wave per tile
@@ -1068,13 +1070,15 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     static_assert(DC <= 32, "one 32-wide latent step");
     static_assert(HID == 128 || HID == 256, "hidden width");
     static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(KX == 4 || KX == 8, "references per token");
+    using IdxV = typename std::conditional<KX == 4, u32x2, u32x4>::type;
 
     // V rows of two tiles: two objects, so the compiler can tell the DMA fill
     // of one from reads of the other (one array would make it wait for the
     // fill before every read)
-    __shared__ __attribute__((aligned(16))) bf16_t vbufA[ROWS][D];
-    __shared__ __attribute__((aligned(16))) bf16_t vbufB[ROWS][D];
-    __shared__ __attribute__((aligned(16))) bf16_t wr[2][16][WR];
+    __shared__ __attribute__((aligned(16))) bf16_t vbufA[BROWS][D];
+    __shared__ __attribute__((aligned(16))) bf16_t vbufB[BROWS][D];
+    __shared__ __attribute__((aligned(16))) bf16_t wr[2][WH][WR];
     __shared__ __attribute__((aligned(16))) _Float16 pw[2][2][16][PR];
     __shared__ __attribute__((aligned(16))) float msl[2][2][16];
     __shared__ __attribute__((aligned(16))) float biask[HID];
@@ -1151,7 +1155,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 for (int r = 0; r < 4; ++r) acc[n][r] *= al[r];
             const int rb = 8 * lq;
             const bf16x8 pwv =
-                as_bf16x8(gl ? *reinterpret_cast<const u32x4 *>(&wr[0][l16][rb]) : zero4);
+                as_bf16x8(gl ? *reinterpret_cast<const u32x4 *>(&wr[0][min(l16, WH - 1)][rb]) : zero4);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const int c = cbase + 16 * n + 4 * (l16 & 3);
@@ -1232,28 +1236,32 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 
         struct KIn {
             bf16x8 z;
-            u32x2 ik, iv;
+            IdxV ik, iv;
         };
         // inputs of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = (uint32_t)min(t0 + TH * src + l16, Ntm1);
             in.z = as_bf16x8(8 * lq < DC ? ld16(at_byte(klat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
-            in.ik = *reinterpret_cast<const u32x2 *>(at_byte(kidx_u, tok * (KX * 2)));
-            in.iv = *reinterpret_cast<const u32x2 *>(at_byte(vidx_u, tok * (KX * 2)));
+            in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
+            in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
         };
 
         // one tile: scores, softmax, publish into slot (it & 1); the inputs of
         // tile (nt0) are loaded into `nxt` once this tile's table reads are out
         auto ktile = [&](int it, int t0, const KIn &in, int nt0, KIn &nxt) {
             const int sl = it & 1;
-            const uint32_t jk[4] = {in.ik[0] & 0xffffu, in.ik[0] >> 16, in.ik[1] & 0xffffu,
-                                    in.ik[1] >> 16};
+            uint32_t jk[KX];
+#pragma unroll
+            for (int i = 0; i < KX; ++i) {
+                const uint32_t wv = in.ik[i >> 1];
+                jk[i] = (i & 1) ? (wv >> 16) : (wv & 0xffffu);
+            }
             // q.R^K of the token's references for the lane's heads (unused
             // slots read the all-zero row Rt)
-            float qv[EG][4];
+            float qv[EG][KX];
             float kek = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < KX; ++i) {
                 const bool ok = jk[i] != kIdxUnused;
                 kek += ok ? 1.f : 0.f;
                 const uint32_t row = (ok ? jk[i] : (uint32_t)Rt) * (uint32_t)GQ;
@@ -1306,7 +1314,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             bool up = false;
 #pragma unroll
             for (int e = 0; e < EG; ++e) {
-                const float rs = (qv[e][0] + qv[e][1]) + (qv[e][2] + qv[e][3]);
+                float rs = (qv[e][0] + qv[e][1]) + (qv[e][2] + qv[e][3]);
+                if constexpr (KX == 8) rs += (qv[e][4] + qv[e][5]) + (qv[e][6] + qv[e][7]);
                 const float v = scale * (sv[e] + rs * inv_k + cqv[e]);
                 s[e] = (tok_ok && gh[e] < G) ? v : -INFINITY;
                 // reference maximum: the larger of the two waves' previous ones
@@ -1336,12 +1345,17 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
             // publish p (f16, by token), p / k_eff on the token's used V slots
             // (bf16, by (token, slot) row) and the maxima
-            const uint32_t vmask_lo = ((in.iv[0] & 0xffffu) != kIdxUnused ? 0x0000ffffu : 0u) |
-                                      ((in.iv[0] >> 16) != kIdxUnused ? 0xffff0000u : 0u);
-            const uint32_t vmask_hi = ((in.iv[1] & 0xffffu) != kIdxUnused ? 0x0000ffffu : 0u) |
-                                      ((in.iv[1] >> 16) != kIdxUnused ? 0xffff0000u : 0u);
-            const float kev = (float)(__builtin_popcount(vmask_lo) + __builtin_popcount(vmask_hi)) *
-                              (1.f / 16.f);
+            // per 32-bit word of the V index entries: which halves are used
+            IdxV vmask;
+            int nbits = 0;
+#pragma unroll
+            for (int q = 0; q < KX / 2; ++q) {
+                const uint32_t wv = in.iv[q];
+                vmask[q] = ((wv & 0xffffu) != kIdxUnused ? 0x0000ffffu : 0u) |
+                           ((wv >> 16) != kIdxUnused ? 0xffff0000u : 0u);
+                nbits += __builtin_popcount(vmask[q]);
+            }
+            const float kev = (float)nbits * (1.f / 16.f);
             const float inv_v = __builtin_amdgcn_rcpf(kev);
 #pragma unroll
             for (int e = 0; e < EG; ++e) {
@@ -1350,8 +1364,10 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 if (gh[e] < G) {
                     pw[sl][src][gh[e]][l16] = (_Float16)p;
                     const uint32_t wb = pack_bf16(p * inv_v, p * inv_v);
-                    *reinterpret_cast<u32x2 *>(&wr[sl][gh[e]][(TH * src + l16) * KX]) =
-                        u32x2{wb & vmask_lo, wb & vmask_hi};
+                    IdxV wv;
+#pragma unroll
+                    for (int q = 0; q < KX / 2; ++q) wv[q] = wb & vmask[q];
+                    *reinterpret_cast<IdxV *>(&wr[sl][gh[e]][(TH * src + l16) * KX]) = wv;
                     if (l16 == 0) msl[sl][src][gh[e]] = m_w[e];
                 }
             }
@@ -1361,12 +1377,18 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         kload(qa, X0);
         ktile(0, qa, X0, qa + TT, X1);
         __syncthreads();
+        // the value waves' barriers of a tile: one at k = 4, two at k = 8
+        // (mid-tile, once the tile's rows are gathered, and end of tile)
+        auto tile_sync = [&]() {
+            __syncthreads();
+            if constexpr (KX == 8) __syncthreads();
+        };
         for (int it = 0; it < ntile; it += 2) {
             if (it + 1 < ntile) ktile(it + 1, qa + (it + 1) * TT, X1, qa + (it + 2) * TT, X0);
-            __syncthreads();
+            tile_sync();
             if (it + 1 >= ntile) break;
             if (it + 2 < ntile) ktile(it + 2, qa + (it + 2) * TT, X0, qa + (it + 3) * TT, X1);
-            __syncthreads();
+            tile_sync();
         }
         // per-head sums of this wave's tokens
 #pragma unroll
@@ -1411,7 +1433,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         const uint32_t coff = 16u * (c8 ^ (2u * (lrow & 3u)));
         const uint32_t rlast = (uint32_t)Rt - 1u;
         uint32_t gi[NDMA];
-        // index entries of rows [64 vj, 64 vj + 64) of the tile at t0: rows
+        // index entries of this wave's rows of the tile at t0 (k = 4: rows
+        // [64 vj, 64 vj + 64) of the tile's buffer; k = 8: the 128 rows of
+        // tokens 16 vj .. 16 vj + 15, the whole of this wave's buffer): rows
         // are (token, slot) pairs in order, i.e. consecutive index entries.
         // Buffer loads over the stored tokens' entries: past them they
         // return 0 (reference 0, a stored row) instead of reading on.
@@ -1433,7 +1457,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const uint32_t j = min(gi[m], rlast);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)((const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
-                    (__attribute__((address_space(3))) void *)&dst[64 * vj + RPD * m][0], 16, 0, 0);
+                    (__attribute__((address_space(3))) void *)&dst[(KX == 4 ? 64 * vj : 0) + RPD * m][0], 16, 0, 0);
             }
         };
         auto zload = [&](int t0, bf16x8 (&z)[2]) {
@@ -1455,7 +1479,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             u32x4 pv = {0u, 0u, 0u, 0u};
             // reference-row step q: rows 64 s2 + 32 ks + 8 lq of score wave
             // s2's tokens, value columns block nc
-            constexpr int NQ = 4 * NC;  // reference steps: score wave s2, half ks, block nc
+            // reference steps spread over the hidden blocks (k = 4: score wave
+            // s2, half ks, block nc; k = 8 takes them after a barrier instead)
+            constexpr int NQ = KX == 4 ? 4 * NC : 0;
             auto rstep = [&](int q) {
                 const int s2 = q / (2 * NC), ks = (q / NC) & 1, nc = q % NC;
                 const int rb = 64 * s2 + 32 * ks + 8 * lq;
@@ -1497,6 +1523,37 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
         };
 
+        // k = 8: the reference-row products of one tile, rows 32 q8 .. 32 q8 +
+        // 31 (tokens of score wave q8 / 4) from the buffer that holds them
+        auto racc8 = [&](auto kScl, float es0, float es1, int sl) {
+            constexpr bool SCL = decltype(kScl)::value;
+#pragma unroll
+            for (int q8 = 0; q8 < ROWS / 32; ++q8) {
+                const int rb = 32 * q8 + 8 * lq;
+                const int s2 = q8 / (ROWS / 64);
+                bf16_t (*buf)[D] = s2 == 0 ? vbufA : vbufB;
+                const int rl = rb - BROWS * s2;
+                u32x4 pv = *reinterpret_cast<const u32x4 *>(&wr[sl][min(l16, WH - 1)][rb]);
+                if (l16 >= WH) pv = zero4;
+                if constexpr (SCL) {
+                    const float es = s2 ? es1 : es0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pv[e] = pack_bf16(__uint_as_float(pv[e] << 16) * es,
+                                          __uint_as_float(pv[e] & 0xffff0000u) * es);
+                }
+#pragma unroll
+                for (int nc = 0; nc < NC; ++nc) {
+                    const int c = cb + 16 * nc + 4 * (l16 & 3);
+                    const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
+                    const u32x2 lo = lds_read_tr16(&buf[rl + (l16 >> 2)][pcol]);
+                    const u32x2 hi = lds_read_tr16(&buf[rl + 4 + (l16 >> 2)][pcol]);
+                    const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
+                    acc_r[nc] = mfma16_bf16(as_bf16x8(pv), as_bf16x8(bv), acc_r[nc]);
+                }
+            }
+        };
+
         auto vtile = [&](int it, const bf16x8 (&zv)[2], bf16_t (*cur)[D]) {
             const int sl = it & 1;
             // maxima the score waves used for this tile
@@ -1525,22 +1582,57 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 pa[s2] = *reinterpret_cast<const f16x4 *>(&pw[sl][s2][l16][4 * lq]);
-            if (__builtin_amdgcn_ballot_w64(split) == 0) {
+            const bool scl = __builtin_amdgcn_ballot_w64(split) != 0;
+            float e0 = 1.f, e1 = 1.f;
+            if (!scl) {
                 vbody(std::integral_constant<bool, false>{}, zv, cur, pa, 1.f, 1.f, sl);
             } else {
                 // the two waves used different maxima: bring the lower one's
                 // weights to the larger maximum
                 const float a0 = msl[sl][0][l16], a1 = msl[sl][1][l16];
                 const float mx = fmaxf(a0, a1);
-                const float e0 = a0 == -INFINITY ? 0.f : __expf(a0 - mx);
-                const float e1 = a1 == -INFINITY ? 0.f : __expf(a1 - mx);
+                e0 = a0 == -INFINITY ? 0.f : __expf(a0 - mx);
+                e1 = a1 == -INFINITY ? 0.f : __expf(a1 - mx);
                 pa[0] = pa[0] * (_Float16)e0;
                 pa[1] = pa[1] * (_Float16)e1;
                 vbody(std::integral_constant<bool, true>{}, zv, cur, pa, e0, e1, sl);
             }
+            if constexpr (KX == 8) {
+                // both value waves' gathers of this tile have landed and are
+                // visible: the reference-row products over all 256 rows
+                wait_vm_all();
+                __syncthreads();
+                if (!scl)
+                    racc8(std::integral_constant<bool, false>{}, 1.f, 1.f, sl);
+                else
+                    racc8(std::integral_constant<bool, true>{}, e0, e1, sl);
+            }
         };
 
         bf16x8 zA[2], zB[2];
+        if constexpr (KX == 8) {
+            // each tile's rows are gathered into both buffers (this wave's
+            // tokens into its own) after the previous tile is done with them,
+            // under the tile's hidden work
+            bf16_t (*own)[D] = vj == 0 ? vbufA : vbufB;
+            gload(qa);
+            zload(qa, zA);
+            wait_vm_all();
+            __syncthreads();
+            for (int it = 0; it < ntile; it += 2) {
+                gissue(own);
+                zload(qa + (it + 1) * TT, zB);
+                gload(qa + (it + 1) * TT);
+                vtile(it, zA, own);
+                __syncthreads();
+                if (it + 1 >= ntile) break;
+                gissue(own);
+                zload(qa + (it + 2) * TT, zA);
+                gload(qa + (it + 2) * TT);
+                vtile(it + 1, zB, own);
+                __syncthreads();
+            }
+        } else {
         gload(qa);
         gissue(vbufA);
         zload(qa, zA);
@@ -1565,6 +1657,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             vtile(it + 1, zB, vbufB);
             wait_vm_all();
             __syncthreads();
+        }
         }
         __syncthreads();  // the score waves' sums and maxima are in LDS
         // partial record: accumulators relative to macc; the two waves' sums
@@ -1613,7 +1706,8 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
-    auto kern = G <= 4 ? main_ws_kernel<D, DC, HID, 1> : main_ws_kernel<D, DC, HID, 2>;
+    auto kern = dm.k == 4 ? (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 4> : main_ws_kernel<D, DC, HID, 2, 4>)
+                          : (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 8> : main_ws_kernel<D, DC, HID, 2, 8>);
     hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
@@ -1621,12 +1715,12 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                        (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part);
 }
 
-// The wave-specialised kernel covers k = 4 and d_c <= 32.
+// The wave-specialised kernel covers k = 4 or 8 and d_c <= 32.
 template <int D>
 bool launch_ws_d(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
                  const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
-    if (dm.k != 4 || dm.dc > 32) return false;
+    if ((dm.k != 4 && dm.k != 8) || dm.dc > 32) return false;
     const bool h256 = kd.hidden == 256;
     if (dm.dc <= 16) {
         if (h256) launch_ws_t<D, 16, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);

@@ -74,6 +74,7 @@ def test_bf16_llama_heads_ragged():
     # (d, s, k, dc, hid, G, T, dtype)
     (128, 8, 8, 16, 256, 4, 777, dk.BF16),    # streaming workload's shapes
     (128, 8, 6, 32, 256, 4, 1200, dk.BF16),   # k > 4 with d_c = 32 in the Compressor
+    (64, 8, 8, 32, 128, 8, 1300, dk.BF16),    # k = 8 wave-specialised decode, 8 heads per KV head
     (64, 3, 2, 64, 64, 1, 500, dk.BF16),
     (64, 5, 5, 128, 128, 8, 301, dk.BF16),
     (64, 4, 3, 64, 128, 2, 999, dk.BF16),     # matrix-core decode at head_dim 64
