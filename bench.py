@@ -135,8 +135,11 @@ class Setup:
                              for st in (0, 1)])
         self.cache = [[dk.Cache(self.shape) for _ in (0, 1)] for _ in range(L)]
         self.chunk = wl.chunk or T
-        self.cws = dk.workspace(max(dk.compress_workspace_bytes(self.shape, 0, min(T, self.chunk)),
-                                    dk.compress_workspace_bytes(self.shape, T - 1, T)))
+        # one workspace for every compress call: the prompt's chunks and the
+        # appends up to the capacity (its size grows with the references seen)
+        ranges = [(c0, min(T, c0 + self.chunk)) for c0 in range(0, T, self.chunk)]
+        ranges.append((cap - 1, cap))
+        self.cws = dk.workspace(max(dk.compress_workspace_bytes(self.shape, a, b) for a, b in ranges))
         self.Hq = wl.q_heads
         self.dws = dk.workspace(dk.decode_workspace_bytes(self.shape, self.Hq, cap))
         self.out = torch.empty(B, self.Hq, d, dtype=torch.float32, device="cuda")

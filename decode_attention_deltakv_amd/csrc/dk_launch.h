@@ -60,6 +60,10 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
 // exact selection of a few tokens (bf16) with the references split over
 // blocks; workspace of select_split_ws_bytes
 size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);
+// Reference-range splits of the matrix-core top-k search of nq tokens ending
+// before t1, and the workspace their lists take beyond the fallback list
+void topk_split_plan(const Dims &dm, int64_t t1, int64_t nq, int *nsplit, int *chunk);
+size_t topk_split_ws_bytes(const Dims &dm, int64_t t1, int64_t nq);
 hipError_t launch_select_split(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                                int64_t nq, const CacheArgs &c, void *ws, hipStream_t st);
 }  // namespace dk

@@ -374,11 +374,13 @@ bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 
 // Workspace of one compress call (bf16 path): a 256-byte header holding the
 // fallback counter, then one 8-byte fallback-list entry per compressed token
-// of the range and unit.
+// of the range and unit, then (when the top-k search splits its reference
+// ranges) each split's candidate lists and largest reference norms.
 size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     if (dm.dtype != 1) return 0;
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
-    return std::max<size_t>(256 + (size_t)nq * dm.B * dm.H * sizeof(uint64_t),
+    const size_t flist = ((size_t)nq * dm.B * dm.H * sizeof(uint64_t) + 255) & ~(size_t)255;
+    return std::max<size_t>(256 + flist + topk_split_ws_bytes(dm, t1, nq),
                             select_split_ws_bytes(dm, t0, t1));
 }
 

@@ -20,6 +20,37 @@
 #include "dk_mfma.h"
 
 namespace dk {
+
+static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Reference-range splits of the matrix-core top-k search: when the token tiles
+// of a call give fewer than two blocks per CU (a prompt compressed in chunks),
+// each tile's references are split over up to three blocks per CU's worth of
+// blocks, at least 512 references (8 stages) per split.
+void topk_split_plan(const Dims &dm, int64_t t1, int64_t nq, int *nsplit, int *chunk) {
+    const int64_t U = (int64_t)dm.B * dm.H;
+    const int64_t blocks = std::max<int64_t>(1, (nq + 255) / 256 * U);
+    const int64_t R = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    int64_t n = 1;
+    if (blocks < 512) n = std::max<int64_t>(1, std::min((768 + blocks - 1) / blocks, (R + 511) / 512));
+    int64_t c = (R + n - 1) / n;
+    c = (c + 63) / 64 * 64;
+    *nsplit = (int)((R + c - 1) / c);
+    *chunk = (int)c;
+}
+
+// Workspace beyond the fallback list that the split search needs.
+size_t topk_split_ws_bytes(const Dims &dm, int64_t t1, int64_t nq) {
+    int nsplit, chunk;
+    topk_split_plan(dm, t1, nq, &nsplit, &chunk);
+    if (nsplit <= 1) return 0;
+    const int LK = dm.k <= 4 ? 8 : 16;
+    const int64_t U = (int64_t)dm.B * dm.H;
+    const int64_t ntiles = (nq + 255) / 256;
+    return align256((size_t)nsplit * U * nq * LK * sizeof(float)) +
+           align256((size_t)nsplit * U * ntiles * sizeof(float));
+}
+
 namespace {
 
 constexpr int kMaxK = 8;
@@ -630,7 +661,8 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, const float *__restrict__ sqn, int64_t Rcap, int64_t Ncap,
     int64_t q0, int64_t nq, int U, int ntiles, uint32_t imask, int ibits,
-    uint16_t *__restrict__ idx, uint64_t *__restrict__ flist, uint32_t *__restrict__ fcount) {
+    uint16_t *__restrict__ idx, uint64_t *__restrict__ flist, uint32_t *__restrict__ fcount,
+    int nsplit, int chunk, float *__restrict__ lists, float *__restrict__ rmaxs) {
     constexpr int KSTEPS = D / 16;
     constexpr int CH = D / 8;
     constexpr int RB = 64;
@@ -649,7 +681,10 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
     const int unit = blockIdx.x % U;
-    const int tile = ntiles - 1 - (int)(blockIdx.x / U);  // heaviest tiles first
+    // heaviest tiles first; split sp of the tile's reference range
+    const int rest = (int)(blockIdx.x / U);
+    const int sp = rest % nsplit;
+    const int tile = ntiles - 1 - rest / nsplit;
     const int64_t qb = q0 + (int64_t)tile * 256;
     const int64_t qend = q0 + nq;
     const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
@@ -658,6 +693,9 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     const int64_t qlast = min(qb + 255, qend - 1);
     // reference counts stay below 2^16: 32-bit arithmetic in the loop
     const int ncand_max = (int)((tok_pos(qlast, s) + s - 1) / s);
+    // this block's references [jbeg, jend) (the whole range unless split)
+    const int jbeg = sp * chunk;
+    const int jend = min(ncand_max, jbeg + chunk);
 
     // MFMA column operands: the wave's two N-tiles of 32 tokens
     bf16x8 xb[2][KSTEPS];
@@ -692,7 +730,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
             const int it = tid + 256 * m;
             const int row = it / CH, c8 = it % CH;
             const int sc8 = c8 ^ swz(row);
-            const uint32_t j = (uint32_t)min(jbase + row, ncand_max - 1);
+            const uint32_t j = (uint32_t)min(jbase + row, jend - 1);
             __builtin_amdgcn_global_load_lds(
                 (const void *)at_byte(urefs, (j * D + 8u * sc8) * 2u),
                 (__attribute__((address_space(3))) void *)&dst[(256 * m + 64 * w) / CH][0], 16,
@@ -700,30 +738,32 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
         }
     };
     float sq_next = 0.f;
-    const int nstage = (int)((ncand_max + RB - 1) / RB);
-    stage_load(0, rtA);
-    if (tid < RB) {
-        const float v = tid < ncand_max ? usqn[tid] : 0.f;
-        rmax2 = fmaxf(rmax2, v);
-        nsq[0][tid] = -0.5f * v;
+    const int nstage = jend > jbeg ? (jend - jbeg + RB - 1) / RB : 0;
+    if (nstage > 0) {
+        stage_load(jbeg, rtA);
+        if (tid < RB) {
+            const float v = jbeg + tid < jend ? usqn[jbeg + tid] : 0.f;
+            rmax2 = fmaxf(rmax2, v);
+            nsq[0][tid] = -0.5f * v;
+        }
+        wait_vm_all();
+        __syncthreads();
     }
-    wait_vm_all();
-    __syncthreads();
 
     // one stage: 64 references from cur (nsq[b]) while the next stage is
     // gathered into nxt
     auto stage = [&](int st, bf16_t (*cur)[D], bf16_t (*nxt)[D]) {
         const int b = st & 1;
-        const int jst = st * RB;
+        const int jst = jbeg + st * RB;
         const bool more = st + 1 < nstage;
         if (more) {
-            if (tid < RB) sq_next = (jst + RB + tid < ncand_max) ? usqn[jst + RB + tid] : 0.f;
+            if (tid < RB) sq_next = (jst + RB + tid < jend) ? usqn[jst + RB + tid] : 0.f;
             stage_load(jst + RB, nxt);
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int j0 = jst + 32 * mb;
-            if (j0 >= ncand_max) break;
+            if (j0 >= jend) break;
             const uint32_t cbase = imask - (uint32_t)j0;
             f32x16 init;
 #pragma unroll
@@ -791,6 +831,18 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     if (lane == 0) red[w] = rmax2;
     __syncthreads();
     rmax2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    if (nsplit > 1) {
+        // a split of the reference range: its lists and largest norm go to
+        // the workspace; the merge kernel rescores
+        if (valid) {
+            float *dst = lists + (((int64_t)sp * U + unit) * nq + (qq - q0)) * LK;
+#pragma unroll
+            for (int e = 0; e < LK; ++e) dst[e] = lst[e];
+        }
+        if (tid == 0) rmaxs[((int64_t)sp * U + unit) * ntiles + tile] = rmax2;
+        return;
+    }
 
     const bf16_t *xr = x + ((int64_t)unit * nrows + (pos - t0)) * D;
     uint16_t *out = idx + ((int64_t)unit * Ncap + qn) * k;
@@ -993,6 +1045,39 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
                             ((uint64_t)unit << 32) | (uint64_t)(qn - q0), flist, fcount);
 }
 
+// Merge of the split top-k searches: per token, the LK best of the splits'
+// lists (each split excluded only references below its own last entry, which
+// is at most the merged last entry, so the certificate holds with it), then
+// the exact fp64 rescore and certificate of one lane per token.
+template <int D, int LK>
+__global__ __launch_bounds__(256) void topk_merge_kernel(
+    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
+    const bf16_t *__restrict__ refs, int64_t Rcap, int64_t Ncap, int64_t q0, int64_t nq, int U,
+    int nsplit, uint32_t imask, int ibits, const float *__restrict__ lists,
+    const float *__restrict__ rmaxs, int ntiles, uint16_t *__restrict__ idx,
+    uint64_t *__restrict__ flist, uint32_t *__restrict__ fcount) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)U * nq) return;
+    const int unit = (int)(gid / nq);
+    const int64_t qi = gid % nq;
+    float lst[LK];
+#pragma unroll
+    for (int e = 0; e < LK; ++e) lst[e] = -INFINITY;
+    float rmax2 = 0.f;
+    const int tile = (int)(qi / 256);
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const float *src = lists + (((int64_t)sp * U + unit) * nq + qi) * LK;
+#pragma unroll
+        for (int e = 0; e < LK; ++e) list_insert<LK>(lst, src[e]);
+        rmax2 = fmaxf(rmax2, rmaxs[((int64_t)sp * U + unit) * ntiles + tile]);
+    }
+    const int64_t q = q0 + qi;
+    const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(q, s) - t0)) * D;
+    rescore_lane<D, LK>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, rmax2, true,
+                        idx + ((int64_t)unit * Ncap + q) * k, ((uint64_t)unit << 32) | (uint64_t)qi,
+                        flist, fcount);
+}
+
 __global__ void zero_u32_kernel(uint32_t *p) {
     if (threadIdx.x == 0) *p = 0u;
 }
@@ -1003,15 +1088,29 @@ __global__ void add_stats_kernel(const uint32_t *count, uint32_t *stats) {
 
 template <int D, int LK>
 void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0, int64_t nq,
-                   const CacheArgs &c, uint64_t *flist, uint32_t *fcount, hipStream_t st) {
+                   const CacheArgs &c, uint64_t *flist, uint32_t *fcount, void *tail,
+                   hipStream_t st) {
     const int U = dm.B * dm.H;
     const int ntiles = (int)((nq + 255) / 256);
     int ibits = 1;
     while (((int64_t)1 << ibits) < dm.R) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u;
-    hipLaunchKernelGGL((dist_topk_kernel<D, LK>), dim3((unsigned)(ntiles * U)), dim3(256), 0, st,
-                       (const bf16_t *)x, t0, t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs, c.sqn,
-                       dm.R, dm.N, q0, nq, U, ntiles, imask, ibits, c.idx, flist, fcount);
+    int nsplit, chunk;
+    topk_split_plan(dm, t1, nq, &nsplit, &chunk);
+    float *lists = nullptr, *rmaxs = nullptr;
+    if (nsplit > 1) {
+        lists = (float *)tail;
+        rmaxs = (float *)((char *)tail + align256((size_t)nsplit * U * nq * LK * sizeof(float)));
+    }
+    hipLaunchKernelGGL((dist_topk_kernel<D, LK>), dim3((unsigned)(ntiles * U * nsplit)), dim3(256),
+                       0, st, (const bf16_t *)x, t0, t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs,
+                       c.sqn, dm.R, dm.N, q0, nq, U, ntiles, imask, ibits, c.idx, flist, fcount,
+                       nsplit, chunk, lists, rmaxs);
+    if (nsplit > 1)
+        hipLaunchKernelGGL((topk_merge_kernel<D, LK>), dim3((unsigned)((U * nq + 255) / 256)),
+                           dim3(256), 0, st, (const bf16_t *)x, t0, t1 - t0, dm.s, dm.k,
+                           (const bf16_t *)c.refs, dm.R, dm.N, q0, nq, U, nsplit, imask, ibits,
+                           lists, rmaxs, ntiles, c.idx, flist, fcount);
 }
 
 }  // namespace
@@ -1080,12 +1179,14 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
                               int64_t nq, const CacheArgs &c, uint64_t *flist, uint32_t *fcount,
                               uint32_t *stats, hipStream_t st) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, fcount);
+    // split lists after the fallback list (one entry per unit and token)
+    void *tail = (char *)flist + align256((size_t)nq * dm.B * dm.H * sizeof(uint64_t));
     if (dm.d == 128) {
-        if (dm.k <= 4) launch_topk_t<128, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
-        else launch_topk_t<128, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        if (dm.k <= 4) launch_topk_t<128, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        else launch_topk_t<128, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
     } else {
-        if (dm.k <= 4) launch_topk_t<64, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
-        else launch_topk_t<64, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, st);
+        if (dm.k <= 4) launch_topk_t<64, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        else launch_topk_t<64, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

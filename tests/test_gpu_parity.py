@@ -215,6 +215,14 @@ def test_long_reference_ranges_checked_everywhere():
               n_dirs=8, n_centroids=256)
 
 
+def test_long_reference_ranges_in_chunks_k8():
+    # the prompt compressed in 2048-token chunks with k = 8: later chunks see
+    # up to 1536 references in few token tiles, so the top-k search splits
+    # each tile's reference range over several blocks and merges their lists
+    _run_case("long-reference-ranges-chunks-k8", 1, 1, 4, 12288, 128, 8, 8, 16, 256, dk.BF16,
+              seed=61, n_dirs=8, n_centroids=256, chunks=list(range(0, 12288 + 1, 2048)))
+
+
 def test_exact_ties_beyond_candidate_list_take_exact_fallback():
     # 12 identical reference rows (more than the approximate candidate list
     # keeps) and tokens equal to them: the certificate cannot separate the
