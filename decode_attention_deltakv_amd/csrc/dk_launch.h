@@ -53,10 +53,14 @@ hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const
 
 namespace dk {
 // exact fp64 top-k scan (k_select.hip); list mode when `list` is non-null
+// (bf16: the first listed tokens split over blocks, with partial lists in
+// `scratch`, up to exact_list_ws_bytes)
 hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                                int64_t q0, int64_t nq, const CacheArgs &c,
                                const uint64_t *list, const uint32_t *list_count,
-                               int64_t list_cap, hipStream_t st);
+                               int64_t list_cap, void *scratch, size_t scratch_bytes,
+                               hipStream_t st);
+size_t exact_list_ws_bytes(const Dims &dm, int64_t t1);
 // exact selection of a few tokens (bf16) with the references split over
 // blocks; workspace of select_split_ws_bytes
 size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);

@@ -43,6 +43,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, let M[i] be the four 16-bit values at lane i's 8-byte address; lane j

@@ -380,8 +380,11 @@ size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     if (dm.dtype != 1) return 0;
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
     const size_t flist = ((size_t)nq * dm.B * dm.H * sizeof(uint64_t) + 255) & ~(size_t)255;
-    return std::max<size_t>(256 + flist + topk_split_ws_bytes(dm, t1, nq),
-                            select_split_ws_bytes(dm, t0, t1));
+    // fallback list, then the search's split lists, whose space the split
+    // exact scan of the fallback list reuses
+    return std::max<size_t>(
+        256 + flist + std::max(topk_split_ws_bytes(dm, t1, nq), exact_list_ws_bytes(dm, t1)),
+        select_split_ws_bytes(dm, t0, t1));
 }
 
 hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
@@ -401,7 +404,7 @@ hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1
         e = launch_select_split(dm, x, t0, t1, q0, nq, c, ws, st);
     } else {
         // fp32 storage, or a few tokens: exact scan
-        e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, st);
+        e = launch_select_exact(dm, x, t0, t1, q0, nq, c, nullptr, nullptr, 0, nullptr, 0, st);
     }
     if (e != hipSuccess) return e;
     if (launch_compress_mfma(dm, x, t0, t1, q0, nq, comp, c, st)) return hipGetLastError();

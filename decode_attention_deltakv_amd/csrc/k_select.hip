@@ -40,20 +40,48 @@ void topk_split_plan(const Dims &dm, int64_t t1, int64_t nq, int *nsplit, int *c
 }
 
 // Workspace beyond the fallback list that the split search needs.
+// Candidate list length of the matrix-core search for k <= 4 and k <= 8:
+// the k best plus a margin, so that the list's last entry usually clears the
+// k-th exact distance by more than the certificate's error terms (a shorter
+// list means fewer insertions; a failed certificate costs an exact scan).
+constexpr int kListLen4 = 7;
+constexpr int kListLen8 = 12;
+
 size_t topk_split_ws_bytes(const Dims &dm, int64_t t1, int64_t nq) {
     int nsplit, chunk;
     topk_split_plan(dm, t1, nq, &nsplit, &chunk);
     if (nsplit <= 1) return 0;
-    const int LK = dm.k <= 4 ? 8 : 16;
+    const int LK = dm.k <= 4 ? kListLen4 : kListLen8;
     const int64_t U = (int64_t)dm.B * dm.H;
     const int64_t ntiles = (nq + 255) / 256;
     return align256((size_t)nsplit * U * nq * LK * sizeof(float)) +
            align256((size_t)nsplit * U * ntiles * sizeof(float));
 }
 
+// Reference chunk per block and block count of the split exact scans (a few
+// tokens of a streaming append, or the listed tokens the matrix-core search
+// could not certify): at least 256 references per block, at most kSplitMax
+// blocks per token.
+static void split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
+    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    const int64_t c = std::max<int64_t>(256, (rmax + kSplitMax - 1) / kSplitMax);
+    *chunk = (int)c;
+    *nsplit = (int)((rmax + c - 1) / c);
+}
+
+// Listed tokens whose exact scan is split over blocks; further entries of a
+// fallback list take one block each.
+constexpr int64_t kListSplitCap = 1024;
+constexpr int kMaxK = 8;
+
+size_t exact_list_ws_bytes(const Dims &dm, int64_t t1) {
+    int chunk, nsplit;
+    split_plan(dm, t1, &chunk, &nsplit);
+    return (size_t)kListSplitCap * nsplit * kMaxK * (sizeof(double) + sizeof(int));
+}
+
 namespace {
 
-constexpr int kMaxK = 8;
 // threads of the block-per-token exact scan
 constexpr int kExactThreads = 1024;
 
@@ -231,16 +259,16 @@ __global__ __launch_bounds__(kExactThreads) void select_exact_block_kernel(
     const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
     int64_t Rcap, int64_t Ncap, int64_t q0, int k, uint16_t *__restrict__ idx,
     const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count, int64_t nunits,
-    int64_t nq) {
+    int64_t nq, int64_t first) {
     constexpr int NT = kExactThreads, NW = NT / 64;
     __shared__ double xs[D];
     __shared__ double wd[NW];
     __shared__ int wj[NW];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // work items: the listed (unit, token) entries, or without a list every
-    // token of [q0, q0 + nq) of every unit
+    // work items: the listed (unit, token) entries from `first` on, or
+    // without a list every token of [q0, q0 + nq) of every unit
     const int64_t n = list ? (int64_t)*list_count : nunits * nq;
-    for (int64_t wi = blockIdx.x; wi < n; wi += gridDim.x) {
+    for (int64_t wi = first + blockIdx.x; wi < n; wi += gridDim.x) {
         const uint64_t e = list ? list[wi] : (((uint64_t)(wi / nq) << 32) | (uint64_t)(wi % nq));
         const int64_t unit = (int64_t)(e >> 32);
         const int64_t q = q0 + (int64_t)(e & 0xffffffffu);
@@ -328,32 +356,20 @@ __global__ __launch_bounds__(kExactThreads) void select_exact_block_kernel(
     }
 }
 
-// Exact top-k of a few tokens with their candidate references split over many
-// blocks (a streaming append has one token per unit but up to 65535
-// references): block (split, item) scans references [split * chunk, ...) of
-// token item with the same fp64 arithmetic as the scans above and writes its
-// kMaxK best (distance, ordinal) pairs; select_merge_kernel takes the k best
-// over all splits.  grid (nsplit, units * nq).
+// Exact kMaxK best (distance, ordinal) pairs of one token row over the
+// references [ja, jb) of one unit, by a block of 256 threads: each thread
+// keeps a sorted list of its share (the same fp64 arithmetic as the scans
+// above), then kMaxK rounds of a block-wide lexicographic minimum write the
+// merged list to od / oj (unused slots: +inf, INT_MAX).  Every thread of the
+// block must call it; xs, wd and wj are the block's LDS scratch.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void select_split_kernel(
-    const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
-    int64_t Rcap, int64_t q0, int64_t nq, int chunk, double *__restrict__ pd,
-    int *__restrict__ pj) {
-    __shared__ double xs[D];
-    __shared__ double wd[4];
-    __shared__ int wj[4];
+__device__ void block_range_topk(const T *__restrict__ xrow, const T *__restrict__ ubase,
+                                 int64_t ja, int64_t jb, double *xs, double *wd, int *wj,
+                                 double *__restrict__ od, int *__restrict__ oj) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t item = blockIdx.y;
-    const int64_t unit = item / nq, q = q0 + item % nq;
-    const int64_t p = tok_pos(q, s);
-    const int64_t ncand = (p + s - 1) / s;
-    const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
-    double *od = pd + (item * gridDim.x + blockIdx.x) * kMaxK;
-    int *oj = pj + (item * gridDim.x + blockIdx.x) * kMaxK;
-    const T *xrow = x + (unit * nrows + (p - t0)) * D;
+    __syncthreads();
     for (int i = tid; i < D; i += 256) xs[i] = to_f64(xrow[i]);
     __syncthreads();
-    const T *ubase = refs + unit * Rcap * D;
     double bd[kMaxK];
     int bj[kMaxK];
 #pragma unroll
@@ -418,18 +434,11 @@ __global__ __launch_bounds__(256) void select_split_kernel(
     }
 }
 
-// The k best (distance, ordinal) of the nsplit partial lists of one token;
-// one wave per token.
-__global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int64_t q0,
-                                                          int64_t nq, int64_t Ncap,
-                                                          const double *__restrict__ pd,
-                                                          const int *__restrict__ pj,
-                                                          uint16_t *__restrict__ idx) {
-    const int lane = threadIdx.x;
-    const int64_t item = blockIdx.x;
-    const int64_t unit = item / nq, q = q0 + item % nq;
-    const double *cd_ = pd + item * nsplit * kMaxK;
-    const int *cj_ = pj + item * nsplit * kMaxK;
+// The k best (distance, ordinal) of nsplit partial lists of one token, by one
+// wave; written to out (kIdxUnused past the candidates).
+__device__ void wave_merge_lists(int nsplit, int k, const double *__restrict__ cd_,
+                                 const int *__restrict__ cj_, uint16_t *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
     double bd[kMaxK];
     int bj[kMaxK];
 #pragma unroll
@@ -451,7 +460,6 @@ __global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int
             cj = lt ? tj : cj;
         }
     }
-    uint16_t *out = idx + (unit * Ncap + q) * k;
     for (int r = 0; r < k; ++r) {
         double md = bd[0];
         int mj = bj[0];
@@ -477,15 +485,121 @@ __global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int
     }
 }
 
+// Exact top-k of a few tokens with their candidate references split over many
+// blocks (a streaming append has one token per unit but up to 65535
+// references): block (split, item) scans references [split * chunk, ...) of
+// token item and writes its kMaxK best pairs; select_merge_kernel takes the
+// k best over all splits.  grid (nsplit, units * nq).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_split_kernel(
+    const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
+    int64_t Rcap, int64_t q0, int64_t nq, int chunk, double *__restrict__ pd,
+    int *__restrict__ pj) {
+    __shared__ double xs[D];
+    __shared__ double wd[4];
+    __shared__ int wj[4];
+    const int64_t item = blockIdx.y;
+    const int64_t unit = item / nq, q = q0 + item % nq;
+    const int64_t p = tok_pos(q, s);
+    const int64_t ncand = (p + s - 1) / s;
+    const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
+    const size_t o = (size_t)(item * gridDim.x + blockIdx.x) * kMaxK;
+    block_range_topk<T, D>(x + (unit * nrows + (p - t0)) * D, refs + unit * Rcap * D, ja, jb, xs,
+                           wd, wj, pd + o, pj + o);
+}
+
+// The k best (distance, ordinal) of the nsplit partial lists of one token;
+// one wave per token.
+__global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int64_t q0,
+                                                          int64_t nq, int64_t Ncap,
+                                                          const double *__restrict__ pd,
+                                                          const int *__restrict__ pj,
+                                                          uint16_t *__restrict__ idx) {
+    const int64_t item = blockIdx.x;
+    const int64_t unit = item / nq, q = q0 + item % nq;
+    wave_merge_lists(nsplit, k, pd + item * nsplit * kMaxK, pj + item * nsplit * kMaxK,
+                     idx + (unit * Ncap + q) * k);
+}
+
+// The same split scan for the first min(*list_count, cap) entries of a
+// fallback list (entries unit << 32 | (q - q0); the count is known on the
+// device only): work item (entry e, split sp), grid-stride.
+template <int D>
+__global__ __launch_bounds__(256) void select_list_split_kernel(
+    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s,
+    const bf16_t *__restrict__ refs, int64_t Rcap, int64_t q0, const uint64_t *__restrict__ list,
+    const uint32_t *__restrict__ list_count, int64_t cap, int nsplit, int chunk,
+    double *__restrict__ pd, int *__restrict__ pj) {
+    __shared__ double xs[D];
+    __shared__ double wd[4];
+    __shared__ int wj[4];
+    const int64_t n = min((int64_t)*list_count, cap) * nsplit;
+    for (int64_t wi = blockIdx.x; wi < n; wi += gridDim.x) {
+        const int64_t e = wi / nsplit;
+        const int sp = (int)(wi % nsplit);
+        const uint64_t ent = list[e];
+        const int64_t unit = (int64_t)(ent >> 32);
+        const int64_t q = q0 + (int64_t)(ent & 0xffffffffu);
+        const int64_t p = tok_pos(q, s);
+        const int64_t ncand = (p + s - 1) / s;
+        const int64_t ja = (int64_t)sp * chunk, jb = min(ncand, ja + (int64_t)chunk);
+        block_range_topk<bf16_t, D>(x + (unit * nrows + (p - t0)) * D, refs + unit * Rcap * D, ja,
+                                    jb, xs, wd, wj, pd + wi * kMaxK, pj + wi * kMaxK);
+    }
+}
+
+// Merge of select_list_split_kernel's lists: one wave per entry, grid-stride.
+__global__ __launch_bounds__(256) void select_list_merge_kernel(
+    int nsplit, int k, int64_t q0, int64_t Ncap, const uint64_t *__restrict__ list,
+    const uint32_t *__restrict__ list_count, int64_t cap, const double *__restrict__ pd,
+    const int *__restrict__ pj, uint16_t *__restrict__ idx) {
+    const int64_t n = min((int64_t)*list_count, cap);
+    const int64_t wstep = (int64_t)gridDim.x * 4;
+    for (int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); e < n; e += wstep) {
+        const uint64_t ent = list[e];
+        const int64_t unit = (int64_t)(ent >> 32);
+        const int64_t q = q0 + (int64_t)(ent & 0xffffffffu);
+        wave_merge_lists(nsplit, k, pd + e * nsplit * kMaxK, pj + e * nsplit * kMaxK,
+                         idx + (unit * Ncap + q) * k);
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                           int64_t nq, const CacheArgs &c, const uint64_t *list,
-                          const uint32_t *list_count, int64_t list_cap, hipStream_t st) {
+                          const uint32_t *list_count, int64_t list_cap, void *scratch,
+                          size_t scratch_bytes, hipStream_t st) {
     if (list) {
-        const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap, 1024));
-        hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0, st,
-                           (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
-                           dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq);
+        // the first entries with their references split over blocks (as many
+        // as the scratch holds partial lists for), the rest one block each
+        int64_t first = 0;
+        if constexpr (sizeof(T) == 2) {
+            int chunk, nsplit;
+            split_plan(dm, t1, &chunk, &nsplit);
+            const size_t per = (size_t)nsplit * kMaxK * (sizeof(double) + sizeof(int));
+            const int64_t cap = std::min<int64_t>({list_cap, kListSplitCap,
+                                                   scratch ? (int64_t)(scratch_bytes / per) : 0});
+            if (cap > 0) {
+                double *pd = (double *)scratch;
+                int *pj = (int *)((char *)scratch + (size_t)cap * nsplit * kMaxK * sizeof(double));
+                const unsigned g = (unsigned)std::min<int64_t>(cap * nsplit, 2048);
+                hipLaunchKernelGGL((select_list_split_kernel<D>), dim3(g), dim3(256), 0, st,
+                                   (const bf16_t *)x, t0, t1 - t0, dm.s, (const bf16_t *)c.refs,
+                                   dm.R, q0, list, list_count, cap, nsplit, chunk, pd, pj);
+                hipLaunchKernelGGL(select_list_merge_kernel,
+                                   dim3((unsigned)std::min<int64_t>((cap + 3) / 4, 256)), dim3(256),
+                                   0, st, nsplit, dm.k, q0, dm.N, list, list_count, cap, pd, pj,
+                                   c.idx);
+                first = cap;
+            }
+        }
+        if (first < list_cap) {
+            const unsigned g =
+                (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap - first, 256));
+            hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0,
+                               st, (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N,
+                               q0, dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq, first);
+        }
         return hipGetLastError();
     }
     if (nq <= kSmallRange) {
@@ -495,7 +609,7 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
         const unsigned g = (unsigned)std::min<int64_t>(n, 1024);
         hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0, st,
                            (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N, q0,
-                           dm.k, c.idx, nullptr, nullptr, (int64_t)dm.B * dm.H, nq);
+                           dm.k, c.idx, nullptr, nullptr, (int64_t)dm.B * dm.H, nq, (int64_t)0);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
@@ -508,32 +622,38 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 // ---------------------------------------------------------------------------
 // Matrix-core top-k (bf16 storage).
 //
-// Scores e~ = x . r - |r|^2 / 2 (larger is nearer; D = |x|^2 - 2 e) come from
-// 32x32x16 bf16 MFMA with the accumulator seeded with -|r|^2 / 2: references
-// are the M dimension, tokens the N dimension, so each lane holds 16 scores of
-// one token per 32-reference block.  A block takes 256 consecutive compressed
+// The matrix cores give approximate squared distances directly: with the
+// token operand scaled by -2 (exact in bf16), the accumulator seeded with
+// the reference's fp32 norm |r|^2 and one 32x32x8 step that adds the token's
+// fp32 norm |x|^2 (split into three bf16 pieces whose sum is that fp32 value
+// exactly, times a column of ones), a chain of 32x32x16 bf16 MFMAs yields
+// S = |r|^2 - 2 x.r + |x|^2 ~ |x - r|^2.  References are the M
+// dimension, tokens the N dimension, so each lane holds 16 values of one
+// token per 32-reference block.  A block takes 256 consecutive compressed
 // tokens (4 waves x 2 N-tiles of 32) and streams the references they can see
-// (j * s < p) through LDS in stages of 64, double-buffered, loaded straight
-// from global memory with 16-byte chunks XOR-swizzled per row (row % 16 for
-// head_dim 128, (row / 2) % 8 for 64: the 16 rows one pass of a 16-byte LDS
-// read touches then fall in disjoint banks).
+// (j * s < p) and their norms through LDS in stages of 64, double-buffered,
+// loaded straight from global memory with 16-byte chunks XOR-swizzled per row
+// (row % 16 for head_dim 128, (row / 2) % 8 for 64: the 16 rows one pass of a
+// 16-byte LDS read touches then fall in disjoint banks).
 //
-// Per lane, a descending list of the LK best scores is kept as packed floats:
-// the low `ibits` mantissa bits of each score are replaced by imask - ordinal
-// (among equal truncated positive scores the lower ordinal ranks higher; the
-// order among ties does not matter for the result, which the exact rescore
-// and the certificate decide), which lets one insertion be LK v_med3
-// operations and one packing be a single bitwise instruction.  After each
-// 32 x 32 product the two lane halves exchange scores (one v_permlane32_swap
-// per register) so that every lane holds all 32 scores of one token and keeps
-// one list; at the end the LK candidates are
-// rescored exactly (fp64, coordinate order, no fused multiply-add) and sorted
-// by (distance, ordinal).  The result is written only when a certificate
-// holds: every reference outside the list has an approximate score at most
-// the list's last entry (plus its truncation), hence a true distance of at
-// least |x|^2 - 2 (tau + delta), where delta bounds the fp32 accumulation
-// error of the MFMA score (and of the fp32 norm); this lower bound must exceed
-// the k-th exact distance.  Tokens that fail go to a list for the exact scan.
+// Per lane, a descending list of the LK largest -S is kept as packed floats:
+// the low `ibits` mantissa bits of each value are replaced by imask - ordinal
+// (the order among values equal after truncation does not matter for the
+// result, which the exact rescore and the certificate decide), which lets one
+// insertion be LK v_med3 operations with the negation folded into their
+// source modifiers and one packing be a single bitwise instruction.  After
+// each 32 x 32 product the two lane halves exchange values (one
+// v_permlane32_swap per register) so that every lane holds all 32 values of
+// one token and keeps one list; at the end the LK candidates are rescored
+// exactly (fp64, coordinate order, no fused multiply-add) and sorted by
+// (distance, ordinal).  The result is written only when a certificate holds:
+// every reference outside the list has an approximate S of at least minus
+// the list's last entry (less its truncation), hence a true distance of at
+// least -tau - delta, where delta bounds the fp32 accumulation error of the
+// MFMA chain and of the two fp32 norms; this lower bound must exceed the k-th
+// exact distance.  As S is of the size of the distances themselves (not of
+// |x|^2), the truncation costs a relative 2^(ibits - 22) of the distance.
+// Tokens that fail go to a list for the exact scan.
 
 // the low bits of a packed score hold imask - j (one instruction to pack)
 __device__ __forceinline__ float pack_score(float sc, uint32_t code, uint32_t nmask) {
@@ -554,12 +674,47 @@ __device__ __forceinline__ void list_insert(float (&a)[LK], float v) {
     a[0] = m;
 }
 
+// Insertion of -v (the negations are source modifiers of the same
+// instructions).
+template <int LK>
+__device__ __forceinline__ void list_insert_neg(float (&a)[LK], float v) {
+#pragma unroll
+    for (int i = LK - 1; i > 0; --i) a[i] = __builtin_amdgcn_fmed3f(a[i - 1], a[i], -v);
+    float m;
+    asm("v_max_f32_e64 %0, %1, -%2" : "=v"(m) : "v"(a[0]), "v"(v));
+    a[0] = m;
+}
+
+// Lower bound on the true squared distance of every reference the search
+// excluded, from the list's last entry tp (a packed -S): S >= -tau with tau
+// = tp + |tp| 2^(ibits - 22) (the packing moves a value by less than
+// |value| 2^(ibits - 23)), and |S - |x - r|^2| <= delta: the chain sums
+// D + 16 products and the two norms, each partial sum rounded within 2^-23
+// of itself (round to nearest or toward zero), so its error is at most
+// gam (2 |x||r| + |x|^2 + |r|^2) = gam (|x| + |r|)^2; the fp32 norms
+// themselves are within gam of |x|^2 and |r|^2.  xn and rm bound |x| and
+// every excluded |r|.
+template <int D>
+__device__ __forceinline__ double excluded_lower_bound(float tpf, int ibits, double xn,
+                                                       double rm) {
+    // every term and partial sum of the chain must stay finite in fp32
+    if ((xn + rm) * (xn + rm) > 1e38) return -INFINITY;
+    const double tp = (double)tpf;
+    const double tau = tp + fabs(tp) * ldexp(1.0, ibits - 22);
+    const double nu = (double)(D + 16) * ldexp(1.0, -23);
+    const double gam = nu / (1.0 - nu);
+    const double delta = 2.0 * gam * (xn + rm) * (xn + rm) + 1e-30 * (1.0 + rm * rm);
+    // the bound itself is evaluated in fp64: keep a relative margin for it
+    return -tau - delta - 1e-9 * (fabs(tau) + delta + xn * xn);
+}
+
 // Exact rescore of one token's LK candidates in one lane: fp64 distances in
 // coordinate order without fused multiply-add, sort by (distance, ordinal),
-// certificate; the result or a fallback entry is written.
+// certificate; the result or a fallback entry is written.  ncand is the
+// token's reference count: a list that is not full must hold all of them.
 template <int D, int LK>
 __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
-                             const float (&lst)[LK], uint32_t imask, int ibits, int k,
+                             const float (&lst)[LK], uint32_t imask, int ibits, int k, int ncand,
                              float rmax2, bool write, uint16_t *__restrict__ out,
                              uint64_t fentry, uint64_t *__restrict__ flist,
                              uint32_t *__restrict__ fcount) {
@@ -629,22 +784,18 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
 #pragma unroll
     for (int e = 0; e < LK; ++e) nvalid += jj[e] != INT_MAX;
     const int kk = min(k, nvalid);
-    bool ok = true;
+    // the fp32 norms behind the approximate values must be finite (else a
+    // reference may have dropped out of the list unseen)
+    bool ok = xsq <= 3.0e38 && rmax2 <= 3.0e38f;
     if (full) {
-        // certificate: excluded references have D >= xsq - 2 (tau + delta)
-        const double tp = (double)lst[LK - 1];
-        const double tau = tp + fabs(tp) * ldexp(1.0, ibits - 21);
         const double rm = sqrt((double)rmax2 * (1.0 + 1e-6));
-        const double xn = sqrt(xsq);
-        const double nu = (double)(D + 1) * ldexp(1.0, -23);
-        const double gam = nu / (1.0 - nu);
-        const double delta = 2.0 * gam * (xn * rm + rm * rm) + 1e-30;
-        const double lb = xsq - 2.0 * (tau + delta);
-        const double slack = 1e-9 * (xsq + fabs(tau) + delta);
+        const double xn = sqrt(xsq) * (1.0 + 1e-12);
         double dk_ = dd[0];
 #pragma unroll
         for (int e = 1; e < LK; ++e) dk_ = (e == kk - 1) ? dd[e] : dk_;
-        ok = (lb - slack) > dk_;
+        ok = ok && excluded_lower_bound<D>(lst[LK - 1], ibits, xn, rm) > dk_;
+    } else {
+        ok = ok && nvalid == ncand;
     }
     if (ok) {
 #pragma unroll
@@ -675,7 +826,8 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     // every read wait for the fill just issued)
     __shared__ __attribute__((aligned(16))) bf16_t rtA[RB][D];
     __shared__ __attribute__((aligned(16))) bf16_t rtB[RB][D];
-    __shared__ __attribute__((aligned(16))) float nsq[2][RB];
+    __shared__ __attribute__((aligned(16))) float nsA[RB];
+    __shared__ __attribute__((aligned(16))) float nsB[RB];
     __shared__ float red[4];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -697,16 +849,57 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     const int jbeg = sp * chunk;
     const int jend = min(ncand_max, jbeg + chunk);
 
-    // MFMA column operands: the wave's two N-tiles of 32 tokens
+    // MFMA column operands: the wave's two N-tiles of 32 tokens, times -2
+    // (exact: a power of two; an overflow to infinity makes the fp32 norm
+    // infinite too, which the certificate rejects), and the fp32 norm of
+    // each token from the same products (lane and lane ^ 32 hold the two
+    // halves of a row)
     bf16x8 xb[2][KSTEPS];
+    float xnorm[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int64_t qq = min(qb + 64 * w + 32 * nt + l32, qend - 1);
         const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(qq, s) - t0)) * D;
+        float part[8];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) xb[nt][ks] = as_bf16x8(ld16(xr + 16 * ks + 8 * hl));
+        for (int i = 0; i < 8; ++i) part[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4 v = ld16(xr + 16 * ks + 8 * hl);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+                part[2 * i] += lo * lo;
+                part[2 * i + 1] += hi * hi;
+                o[i] = (__float_as_uint(-2.f * lo) >> 16) | (__float_as_uint(-2.f * hi) & 0xffff0000u);
+            }
+            xb[nt][ks] = as_bf16x8(o);
+        }
+        const float half_sq = ((part[0] + part[1]) + (part[2] + part[3])) +
+                              ((part[4] + part[5]) + (part[6] + part[7]));
+        xnorm[nt] = half_sq + __shfl_xor(half_sq, 32, 64);
     }
-    // after the half swap below, lane L holds all 32 scores of token
+    // extra K step (32x32x8: k 0-3 in the lower lane half): the token norm as
+    // hi + mid + lo (bf16 pieces cut from the fp32 value, so their sum is
+    // that value exactly) against ones
+    s16x4 xext[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t hb = __float_as_uint(xnorm[nt]) & 0xffff0000u;
+        const float r1 = xnorm[nt] - __uint_as_float(hb);
+        const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+        const uint32_t lb = __float_as_uint(r1 - __uint_as_float(mb));
+        u32x2 e;
+        e[0] = hl ? 0u : ((hb >> 16) | mb);
+        e[1] = hl ? 0u : (lb >> 16);
+        xext[nt] = __builtin_bit_cast(s16x4, e);
+    }
+    u32x2 ones_w;
+    ones_w[0] = 0x3f803f80u;
+    ones_w[1] = 0x00003f80u;
+    const s16x4 ones = __builtin_bit_cast(s16x4, ones_w);
+    // after the half swap below, lane L holds all 32 values of token
     // qb + 64 w + L: one candidate list per lane
     const int64_t qq = qb + 64 * w + lane;
     const bool valid = qq < qend;
@@ -723,43 +916,47 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     uint32_t nmask = ~imask;
     asm volatile("" : "+v"(nmask));
 
+    // largest fp32 reference norm among the rows the block reads (bounds the
+    // error of S for every reference it excludes)
     float rmax2 = 0.f;
-    auto stage_load = [&](int jbase, bf16_t (*dst)[D]) {
+    // one stage's reference rows and their norms, all by DMA (no register
+    // results, so nothing waits for them before the stage's barrier)
+    // a DMA pass of the block moves 256 16-byte chunks = 256 / CH rows;
+    // the thread's row within a pass and its (swizzled) chunk are the same
+    // in every pass (the swizzle depends on row % 16 or (row / 2) % 8 only)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int dma_row = tid / CH;
+    const uint32_t dma_col = 16u * (uint32_t)((tid % CH) ^ swz(dma_row));
+    auto stage_load = [&](int jbase, bf16_t (*dst)[D], float *ndst) {
 #pragma unroll
         for (int m = 0; m < DMA_IT; ++m) {
-            const int it = tid + 256 * m;
-            const int row = it / CH, c8 = it % CH;
-            const int sc8 = c8 ^ swz(row);
-            const uint32_t j = (uint32_t)min(jbase + row, jend - 1);
+            const uint32_t j = (uint32_t)min(jbase + (256 / CH) * m + dma_row, jend - 1);
             __builtin_amdgcn_global_load_lds(
-                (const void *)at_byte(urefs, (j * D + 8u * sc8) * 2u),
-                (__attribute__((address_space(3))) void *)&dst[(256 * m + 64 * w) / CH][0], 16,
+                (const void *)at_byte(urefs, j * (2u * D) + dma_col),
+                (__attribute__((address_space(3))) void *)&dst[(256 * m + 64 * wu) / CH][0], 16,
                 0, 0);
         }
+        if (wu == 0) {
+            const uint32_t j = (uint32_t)min(jbase + lane, jend - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(usqn + j),
+                                             (__attribute__((address_space(3))) void *)ndst, 4,
+                                             0, 0);
+        }
     };
-    float sq_next = 0.f;
     const int nstage = jend > jbeg ? (jend - jbeg + RB - 1) / RB : 0;
     if (nstage > 0) {
-        stage_load(jbeg, rtA);
-        if (tid < RB) {
-            const float v = jbeg + tid < jend ? usqn[jbeg + tid] : 0.f;
-            rmax2 = fmaxf(rmax2, v);
-            nsq[0][tid] = -0.5f * v;
-        }
+        stage_load(jbeg, rtA, nsA);
         wait_vm_all();
         __syncthreads();
     }
 
-    // one stage: 64 references from cur (nsq[b]) while the next stage is
-    // gathered into nxt
-    auto stage = [&](int st, bf16_t (*cur)[D], bf16_t (*nxt)[D]) {
-        const int b = st & 1;
+    // one stage: 64 references from cur (norms ncur) while the next stage is
+    // gathered into nxt (nnxt)
+    auto stage = [&](int st, bf16_t (*cur)[D], const float *ncur, bf16_t (*nxt)[D], float *nnxt) {
         const int jst = jbeg + st * RB;
         const bool more = st + 1 < nstage;
-        if (more) {
-            if (tid < RB) sq_next = (jst + RB + tid < jend) ? usqn[jst + RB + tid] : 0.f;
-            stage_load(jst + RB, nxt);
-        }
+        if (more) stage_load(jst + RB, nxt, nnxt);
+        rmax2 = fmaxf(rmax2, ncur[lane]);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int j0 = jst + 32 * mb;
@@ -768,11 +965,12 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
             f32x16 init;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(&nsq[b][32 * mb + 8 * g4 + 4 * hl]);
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&ncur[32 * mb + 8 * g4 + 4 * hl]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) init[4 * g4 + i] = v[i];
             }
-            f32x16 acc0 = init, acc1 = init;
+            f32x16 acc0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones, xext[0], init, 0, 0, 0);
+            f32x16 acc1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones, xext[1], init, 0, 0, 0);
             const int r = 32 * mb + l32;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -796,8 +994,8 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int j = j0 + 8 * (i / 4) + (i % 4);
-                    acc0[i] = j < ncand ? acc0[i] : -INFINITY;
-                    acc1[i] = j + 4 < ncand ? acc1[i] : -INFINITY;
+                    acc0[i] = j < ncand ? acc0[i] : INFINITY;
+                    acc1[i] = j + 4 < ncand ? acc1[i] : INFINITY;
                 }
             }
             // slots in pairs: one wave-wide test per pair, then each slot's
@@ -807,26 +1005,21 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float thr = lst[LK - 1];
-                const bool p0 = acc0[i] > thr, p1 = acc1[i] > thr;
+                const bool p0 = -acc0[i] > thr, p1 = -acc1[i] > thr;
                 if (__builtin_amdgcn_ballot_w64(p0 || p1)) {
                     const uint32_t code = cbase - (uint32_t)(8 * (i / 4) + (i % 4));
-                    if (p0) list_insert<LK>(lst, pack_score(acc0[i], code, nmask));
-                    if (p1) list_insert<LK>(lst, pack_score(acc1[i], code - 4u, nmask));
+                    if (p0) list_insert_neg<LK>(lst, pack_score(acc0[i], code, nmask));
+                    if (p1) list_insert_neg<LK>(lst, pack_score(acc1[i], code - 4u, nmask));
                 }
             }
-        }
-        if (more && tid < RB) {
-            rmax2 = fmaxf(rmax2, sq_next);
-            nsq[b ^ 1][tid] = -0.5f * sq_next;
         }
         wait_vm_all();
         __syncthreads();
     };
     for (int st = 0; st < nstage; st += 2) {
-        stage(st, rtA, rtB);
-        if (st + 1 < nstage) stage(st + 1, rtB, rtA);
+        stage(st, rtA, nsA, rtB, nsB);
+        if (st + 1 < nstage) stage(st + 1, rtB, nsB, rtA, nsA);
     }
-    // largest reference norm the block saw (bounds the score error)
     rmax2 = wave_max(rmax2);
     if (lane == 0) red[w] = rmax2;
     __syncthreads();
@@ -848,8 +1041,9 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     uint16_t *out = idx + ((int64_t)unit * Ncap + qn) * k;
     // First pass of the rescore, in fp32: d'_e = |r_e|^2 - 2 x.r_e (the
     // distance minus |x|^2, which every candidate of the token shares) from
-    // bf16 dot products (the products are exact; eight partial sums per dot
-    // product) with a rigorous bound on the error of each d'_e.  When the
+    // bf16 dot products with the -2 x operand (the products are exact; eight
+    // partial sums per dot product) with a rigorous bound on the error of
+    // each d'_e.  When the
     // bounds order the candidates the result needs (the first min(k, n)
     // positions and the one after them) and the certificate holds with the
     // k-th candidate's upper bound, the result is written from this pass and
@@ -909,7 +1103,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
         for (int c = 0; c < 2 * KSTEPS; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) xa[4 * (c & 1) + i] = dot(xw(c, i), xw(c, i), xa[4 * (c & 1) + i]);
-        const float xsq = tree(xa);
+        const float xsq = 0.25f * tree(xa);  // the operand is -2 x
         // error of a partial-sum dot product of D terms over NA sums: at most
         // D / NA + 3 roundings on any path, each within 2^-23 of the running
         // sum, hence <= g * sum |terms|
@@ -971,12 +1165,12 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
                 }
             }
             const float rsq = usqn[je];  // fp32 norm: within 8 u rsq
-            const float xr_ = tree(ra);
-            // |2 x.r - 2 xr| <= 2 g |x||r| <= g (|x|^2 + |r|^2); evaluating
-            // rsq - 2 xr adds <= u (rsq + 2 |xr|); a denormal product flushed
-            // to zero is within 2^-126 max(|x|, |r|) each
-            const float dpe = ce ? rsq - 2.f * xr_ : INFINITY;
-            const float ere = ce ? 8.f * u * rsq + g * (xsq_hi + rsq) + u * (rsq + 2.f * fabsf(xr_)) +
+            const float xr2 = tree(ra);    // ~ -2 x.r
+            // |xr2 + 2 x.r| <= 2 g |x||r| <= g (|x|^2 + |r|^2); evaluating
+            // rsq + xr2 adds <= u (rsq + |xr2|); a denormal product flushed
+            // to zero is within 2^-125 max(|x|, |r|) each
+            const float dpe = ce ? rsq + xr2 : INFINITY;
+            const float ere = ce ? 8.f * u * rsq + g * (xsq_hi + rsq) + u * (rsq + fabsf(xr2)) +
                                        1e-30f * (1.f + xsq_hi + rsq)
                                  : 0.f;
 #pragma unroll
@@ -1008,25 +1202,21 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
         const int kk = min(k, nvalid);
         // a certified gap must also clear the fp64 rounding of the exact values
         const float slack = 1e-9f * (xsq_hi + rmax2);
-        bool ok = true;
+        bool ok = xsq_hi <= 3.0e38f && rmax2 <= 3.0e38f;
 #pragma unroll
         for (int i = 0; i + 1 < LK; ++i)
             if (i < kk && i + 1 < nvalid) ok = ok && (dp[i + 1] - er[i + 1]) - (dp[i] + er[i]) > slack;
         if (lst[LK - 1] != -INFINITY) {
-            // certificate in d' terms: an excluded reference has
-            // d' >= -2 (tau + delta); the k-th candidate has d' <= dp + er
-            const double tp = (double)lst[LK - 1];
-            const double tau = tp + fabs(tp) * ldexp(1.0, ibits - 21);
+            // certificate: an excluded reference is at distance >= lb; the
+            // k-th candidate at most dp + er + |x|^2
             const double rm = sqrt((double)rmax2 * (1.0 + 1e-6));
             const double xn = sqrt((double)xsq_hi);
-            const double nu = (double)(D + 1) * ldexp(1.0, -23);
-            const double gam = nu / (1.0 - nu);
-            const double delta = 2.0 * gam * (xn * rm + rm * rm) + 1e-30;
             double dk_ = (double)dp[0] + (double)er[0];
 #pragma unroll
             for (int e = 1; e < LK; ++e) dk_ = (e == kk - 1) ? (double)dp[e] + (double)er[e] : dk_;
-            const double lb = -2.0 * (tau + delta);
-            ok = ok && (lb - 1e-9 * ((double)xsq_hi + fabs(tau) + delta)) > dk_;
+            ok = ok && excluded_lower_bound<D>(lst[LK - 1], ibits, xn, rm) > dk_ + (double)xsq_hi;
+        } else {
+            ok = ok && nvalid == ncand;
         }
         if (!ok) return false;
 #pragma unroll
@@ -1041,7 +1231,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
     bool settled = false;
     if constexpr (LK <= 8) settled = rescore_fast(xr, out);
     if (!settled)
-        rescore_lane<D, LK>(xr, urefs, lst, imask, ibits, k, rmax2, valid, out,
+        rescore_lane<D, LK>(xr, urefs, lst, imask, ibits, k, ncand, rmax2, valid, out,
                             ((uint64_t)unit << 32) | (uint64_t)(qn - q0), flist, fcount);
 }
 
@@ -1073,7 +1263,8 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
     }
     const int64_t q = q0 + qi;
     const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(q, s) - t0)) * D;
-    rescore_lane<D, LK>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, rmax2, true,
+    const int ncand = (int)((tok_pos(q, s) + s - 1) / s);
+    rescore_lane<D, LK>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, ncand, rmax2, true,
                         idx + ((int64_t)unit * Ncap + q) * k, ((uint64_t)unit << 32) | (uint64_t)qi,
                         flist, fcount);
 }
@@ -1115,14 +1306,6 @@ void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_
 
 }  // namespace
 
-// Reference chunk per block and block count of the split exact scan.
-static void split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
-    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
-    const int64_t c = std::max<int64_t>(256, (rmax + kSplitMax - 1) / kSplitMax);
-    *chunk = (int)c;
-    *nsplit = (int)((rmax + c - 1) / c);
-}
-
 size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
     if (nq <= 0 || nq > kSmallRange) return 0;
@@ -1156,16 +1339,17 @@ hipError_t launch_select_split(const Dims &dm, const void *x, int64_t t0, int64_
 hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                                int64_t q0, int64_t nq, const CacheArgs &c,
                                const uint64_t *list, const uint32_t *list_count,
-                               int64_t list_cap, hipStream_t st) {
+                               int64_t list_cap, void *scratch, size_t scratch_bytes,
+                               hipStream_t st) {
     if (dm.dtype == 0)
-        return dm.d == 64 ? launch_exact_t<float, 64>(dm, x, t0, t1, q0, nq, c, list,
-                                                      list_count, list_cap, st)
-                          : launch_exact_t<float, 128>(dm, x, t0, t1, q0, nq, c, list,
-                                                       list_count, list_cap, st);
+        return dm.d == 64 ? launch_exact_t<float, 64>(dm, x, t0, t1, q0, nq, c, list, list_count,
+                                                      list_cap, scratch, scratch_bytes, st)
+                          : launch_exact_t<float, 128>(dm, x, t0, t1, q0, nq, c, list, list_count,
+                                                       list_cap, scratch, scratch_bytes, st);
     return dm.d == 64 ? launch_exact_t<bf16_t, 64>(dm, x, t0, t1, q0, nq, c, list, list_count,
-                                                   list_cap, st)
-                      : launch_exact_t<bf16_t, 128>(dm, x, t0, t1, q0, nq, c, list,
-                                                    list_count, list_cap, st);
+                                                   list_cap, scratch, scratch_bytes, st)
+                      : launch_exact_t<bf16_t, 128>(dm, x, t0, t1, q0, nq, c, list, list_count,
+                                                    list_cap, scratch, scratch_bytes, st);
 }
 
 }  // namespace dk
@@ -1182,16 +1366,18 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
     // split lists after the fallback list (one entry per unit and token)
     void *tail = (char *)flist + align256((size_t)nq * dm.B * dm.H * sizeof(uint64_t));
     if (dm.d == 128) {
-        if (dm.k <= 4) launch_topk_t<128, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
-        else launch_topk_t<128, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        if (dm.k <= 4) launch_topk_t<128, kListLen4>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        else launch_topk_t<128, kListLen8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
     } else {
-        if (dm.k <= 4) launch_topk_t<64, 8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
-        else launch_topk_t<64, 16>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        if (dm.k <= 4) launch_topk_t<64, kListLen4>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
+        else launch_topk_t<64, kListLen8>(dm, x, t0, t1, q0, nq, c, flist, fcount, tail, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_select_exact(dm, x, t0, t1, q0, nq, c, flist, fcount,
-                            (int64_t)nq * dm.B * dm.H, st);
+    // the split lists of the search are consumed: their space holds the
+    // partial lists of the split exact scan
+    e = launch_select_exact(dm, x, t0, t1, q0, nq, c, flist, fcount, (int64_t)nq * dm.B * dm.H,
+                            tail, exact_list_ws_bytes(dm, t1), st);
     if (e != hipSuccess) return e;
     if (stats) hipLaunchKernelGGL(add_stats_kernel, dim3(1), dim3(64), 0, st, fcount, stats);
     return hipGetLastError();

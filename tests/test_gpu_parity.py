@@ -250,6 +250,36 @@ def test_exact_ties_beyond_candidate_list_take_exact_fallback():
     assert n_fb >= len(tie_pos)
 
 
+def test_near_tied_references_take_split_and_block_fallbacks():
+    # every reference row is one base row with one coordinate moved by a
+    # single bf16 step: all distances of a token differ by far less than the
+    # certificate's error terms, so (nearly) every token goes to the exact
+    # fallback scan; 3840 listed tokens exceed the entries whose scan is split
+    # over blocks, so the per-token block scan takes the rest.  Every token
+    # is compared with the oracle.
+    B, H, T, d, s, k = 1, 1, 4096, 128, 16, 4
+    say("[case] near-tied references: split and block fallback scans")
+    x = make_kv(B, H, T, d, torch.bfloat16, key=(120, 0))
+    base = x[0, 0, 0].clone()
+    g = torch.Generator().manual_seed(120)
+    for j in range(T // s):
+        row = base.clone()
+        c = int(torch.randint(0, d, (1,), generator=g))
+        f = row[c].float()
+        step = torch.tensor(float(f) * (1 + 2.0 ** -7) if int(torch.randint(0, 2, (1,), generator=g))
+                            else float(f) * (1 - 2.0 ** -7)).to(torch.bfloat16)
+        row[c] = step
+        x[0, 0, j * s] = row
+    shape = dk.Shape(B, H, d, s, k, 32, T, dk.BF16)
+    cw, _ = make_mlp(d, 256, 32, torch.bfloat16, key=(120, 1))
+    stats = torch.zeros(4, dtype=torch.int32, device="cuda")
+    c = gpu_compress(shape, x, gpu_mlp(cw, 0), stats=stats)
+    n_fb = int(stats[0].item())
+    say(f"  fallback tokens: {n_fb}")
+    check_compress_unit(shape, x[0, 0], c, 0, 0, oracle_mlp(cw, 0), tol=2e-2)
+    assert n_fb > 1024
+
+
 def test_decode_graph_replays_match_eager():
     # decode captured in a HIP graph (as a serving loop would), replayed several
     # times with eager library work and synchronisations between the replays;
