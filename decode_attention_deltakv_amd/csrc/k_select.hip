@@ -69,14 +69,24 @@ static void split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
     *nsplit = (int)((rmax + c - 1) / c);
 }
 
-// Listed tokens whose exact scan is split over blocks; further entries of a
+// Listed tokens whose exact scan is split over waves; further entries of a
 // fallback list take one block each.
 constexpr int64_t kListSplitCap = 1024;
 constexpr int kMaxK = 8;
 
+// Reference chunk per wave and wave count per token of the split scan of a
+// fallback list: 64 references (one per lane) per wave, more once a token
+// would need over 256 waves.
+static void list_split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
+    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    const int64_t c = std::max<int64_t>(64, (rmax + 255) / 256 + 63) / 64 * 64;
+    *chunk = (int)c;
+    *nsplit = (int)((rmax + c - 1) / c);
+}
+
 size_t exact_list_ws_bytes(const Dims &dm, int64_t t1) {
     int chunk, nsplit;
-    split_plan(dm, t1, &chunk, &nsplit);
+    list_split_plan(dm, t1, &chunk, &nsplit);
     return (size_t)kListSplitCap * nsplit * kMaxK * (sizeof(double) + sizeof(int));
 }
 
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(kExactThreads) void select_exact_block_kernel(
 // merged list to od / oj (unused slots: +inf, INT_MAX).  Every thread of the
 // block must call it; xs, wd and wj are the block's LDS scratch.
 template <typename T, int D>
-__device__ void block_range_topk(const T *__restrict__ xrow, const T *__restrict__ ubase,
+__device__ __forceinline__ void block_range_topk(const T *__restrict__ xrow, const T *__restrict__ ubase,
                                  int64_t ja, int64_t jb, double *xs, double *wd, int *wj,
                                  double *__restrict__ od, int *__restrict__ oj) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -434,9 +444,11 @@ __device__ void block_range_topk(const T *__restrict__ xrow, const T *__restrict
     }
 }
 
-// The k best (distance, ordinal) of nsplit partial lists of one token, by one
-// wave; written to out (kIdxUnused past the candidates).
-__device__ void wave_merge_lists(int nsplit, int k, const double *__restrict__ cd_,
+// The k best (distance, ordinal) of nsplit partial lists of one token (each
+// kMaxK long, sorted; only their first k entries can make the result), by
+// one wave; written to out (kIdxUnused past the candidates).  Candidates are
+// read eight per lane at a time, all loads before the insertions.
+__device__ __forceinline__ void wave_merge_lists(int nsplit, int k, const double *__restrict__ cd_,
                                  const int *__restrict__ cj_, uint16_t *__restrict__ out) {
     const int lane = threadIdx.x & 63;
     double bd[kMaxK];
@@ -446,18 +458,31 @@ __device__ void wave_merge_lists(int nsplit, int k, const double *__restrict__ c
         bd[i] = __builtin_inf();
         bj[i] = INT_MAX;
     }
-    for (int c = lane; c < nsplit * kMaxK; c += 64) {
-        double cd = cd_[c];
-        int cj = cj_[c];
+    const int n = nsplit * k;
+    for (int base = 0; base < n; base += 8 * 64) {
+        double vd[8];
+        int vj[8];
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i) {
-            const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
-            const double td = bd[i];
-            const int tj = bj[i];
-            bd[i] = lt ? cd : td;
-            bj[i] = lt ? cj : tj;
-            cd = lt ? td : cd;
-            cj = lt ? tj : cj;
+        for (int u = 0; u < 8; ++u) {
+            const int c = base + 64 * u + lane;
+            const int at = (c / k) * kMaxK + c % k;
+            vd[u] = c < n ? cd_[at] : __builtin_inf();
+            vj[u] = c < n ? cj_[at] : INT_MAX;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            double cd = vd[u];
+            int cj = vj[u];
+#pragma unroll
+            for (int i = 0; i < kMaxK; ++i) {
+                const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
+                const double td = bd[i];
+                const int tj = bj[i];
+                bd[i] = lt ? cd : td;
+                bj[i] = lt ? cj : tj;
+                cd = lt ? td : cd;
+                cj = lt ? tj : cj;
+            }
         }
     }
     for (int r = 0; r < k; ++r) {
@@ -521,20 +546,59 @@ __global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int
                      idx + (unit * Ncap + q) * k);
 }
 
+// Squared distance of one bf16 reference row (already loaded, u) from the
+// fp64 row xs: the same arithmetic and order as exact_sq_dist.
+template <int D>
+__device__ __forceinline__ double exact_sq_dist_regs(const double *xs, const uint4 (&u)[D / 8]) {
+#pragma clang fp contract(off)
+    // an opaque offset keeps the row's LDS reads inside a caller's loop
+    // (hoisted, they would hold the whole fp64 row in registers)
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    xs += off;
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const uint32_t w[4] = {u[c].x, u[c].y, u[c].z, u[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double lo = (double)__uint_as_float(w[e] << 16);
+            const double hi = (double)__uint_as_float(w[e] & 0xffff0000u);
+            const double d0 = xs[c * 8 + 2 * e] - lo;
+            const double s0 = d0 * d0;
+            acc = acc + s0;
+            const double d1 = xs[c * 8 + 2 * e + 1] - hi;
+            const double s1 = d1 * d1;
+            acc = acc + s1;
+        }
+    }
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void load_row(const bf16_t *__restrict__ r, uint4 (&u)[D / 8]) {
+    const uint4 *rv = reinterpret_cast<const uint4 *>(r);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) u[c] = rv[c];
+}
+
 // The same split scan for the first min(*list_count, cap) entries of a
 // fallback list (entries unit << 32 | (q - q0); the count is known on the
-// device only): work item (entry e, split sp), grid-stride.
+// device only), one wave per work item (entry e, split sp), grid-stride: lane
+// l scores references ja + l, ja + l + 64, ... below jb, keeps a sorted list,
+// and kMaxK rounds of a wave-wide lexicographic minimum write the item's list.
 template <int D>
 __global__ __launch_bounds__(256) void select_list_split_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s,
     const bf16_t *__restrict__ refs, int64_t Rcap, int64_t q0, const uint64_t *__restrict__ list,
     const uint32_t *__restrict__ list_count, int64_t cap, int nsplit, int chunk,
     double *__restrict__ pd, int *__restrict__ pj) {
-    __shared__ double xs[D];
-    __shared__ double wd[4];
-    __shared__ int wj[4];
+    __shared__ double xs_all[4][D];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    double *xs = xs_all[wv];
     const int64_t n = min((int64_t)*list_count, cap) * nsplit;
-    for (int64_t wi = blockIdx.x; wi < n; wi += gridDim.x) {
+    const int64_t wstep = (int64_t)gridDim.x * 4;
+    for (int64_t wi = (int64_t)blockIdx.x * 4 + wv; wi < n; wi += wstep) {
         const int64_t e = wi / nsplit;
         const int sp = (int)(wi % nsplit);
         const uint64_t ent = list[e];
@@ -543,8 +607,70 @@ __global__ __launch_bounds__(256) void select_list_split_kernel(
         const int64_t p = tok_pos(q, s);
         const int64_t ncand = (p + s - 1) / s;
         const int64_t ja = (int64_t)sp * chunk, jb = min(ncand, ja + (int64_t)chunk);
-        block_range_topk<bf16_t, D>(x + (unit * nrows + (p - t0)) * D, refs + unit * Rcap * D, ja,
-                                    jb, xs, wd, wj, pd + wi * kMaxK, pj + wi * kMaxK);
+        const bf16_t *xrow = x + (unit * nrows + (p - t0)) * D;
+        const bf16_t *ubase = refs + unit * Rcap * D;
+        // the lane's first reference row is requested before the token row
+        // is staged, so the two memory round trips overlap
+        uint4 u[D / 8];
+        load_row<D>(ubase + (ja < jb ? min(ja + lane, jb - 1) : 0) * D, u);
+        for (int i = lane; i < D; i += 64) xs[i] = (double)bf2f(xrow[i]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        double bd[kMaxK];
+        int bj[kMaxK];
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) {
+            bd[i] = __builtin_inf();
+            bj[i] = INT_MAX;
+        }
+        for (int64_t j = ja + lane; j < jb; j += 64) {
+            if (j != ja + lane) load_row<D>(ubase + j * D, u);
+            double cd = exact_sq_dist_regs<D>(xs, u);
+            int cj = (int)j;
+#pragma unroll
+            for (int i = 0; i < kMaxK; ++i) {
+                const bool lt = cd < bd[i] || (cd == bd[i] && cj < bj[i]);
+                const double td = bd[i];
+                const int tj = bj[i];
+                bd[i] = lt ? cd : td;
+                bj[i] = lt ? cj : tj;
+                cd = lt ? td : cd;
+                cj = lt ? tj : cj;
+            }
+        }
+        double *od = pd + wi * kMaxK;
+        int *oj = pj + wi * kMaxK;
+        for (int r = 0; r < kMaxK; ++r) {
+            double md = bd[0];
+            int mj = bj[0];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double odd = __shfl_xor(md, o, 64);
+                const int ojj = __shfl_xor(mj, o, 64);
+                if (odd < md || (odd == md && ojj < mj)) {
+                    md = odd;
+                    mj = ojj;
+                }
+            }
+            if (mj != INT_MAX && bj[0] == mj) {
+#pragma unroll
+                for (int i = 0; i + 1 < kMaxK; ++i) {
+                    bd[i] = bd[i + 1];
+                    bj[i] = bj[i + 1];
+                }
+                bd[kMaxK - 1] = __builtin_inf();
+                bj[kMaxK - 1] = INT_MAX;
+            }
+            if (lane == 0) {
+                od[r] = md;
+                oj[r] = mj;
+            }
+        }
+        // the next item rewrites xs
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -575,14 +701,14 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
         int64_t first = 0;
         if constexpr (sizeof(T) == 2) {
             int chunk, nsplit;
-            split_plan(dm, t1, &chunk, &nsplit);
+            list_split_plan(dm, t1, &chunk, &nsplit);
             const size_t per = (size_t)nsplit * kMaxK * (sizeof(double) + sizeof(int));
             const int64_t cap = std::min<int64_t>({list_cap, kListSplitCap,
                                                    scratch ? (int64_t)(scratch_bytes / per) : 0});
             if (cap > 0) {
                 double *pd = (double *)scratch;
                 int *pj = (int *)((char *)scratch + (size_t)cap * nsplit * kMaxK * sizeof(double));
-                const unsigned g = (unsigned)std::min<int64_t>(cap * nsplit, 2048);
+                const unsigned g = (unsigned)std::min<int64_t>((cap * nsplit + 3) / 4, 2048);
                 hipLaunchKernelGGL((select_list_split_kernel<D>), dim3(g), dim3(256), 0, st,
                                    (const bf16_t *)x, t0, t1 - t0, dm.s, (const bf16_t *)c.refs,
                                    dm.R, q0, list, list_count, cap, nsplit, chunk, pd, pj);
