@@ -834,6 +834,32 @@ __device__ __forceinline__ double excluded_lower_bound(float tpf, int ibits, dou
     return -tau - delta - 1e-9 * (fabs(tau) + delta + xn * xn);
 }
 
+// The k result ordinals of a token (kIdxUnused past the kk found), as one
+// 8- or 16-byte store for k = 4 or 8 (the index row is then aligned to its
+// size), else one store per slot.
+template <int LK>
+__device__ __forceinline__ void store_idx(uint16_t *__restrict__ out, const int (&jj)[LK], int k,
+                                          int kk) {
+    auto at = [&](int r) -> uint32_t {
+        return r < kk ? ((uint32_t)jj[r] & 0xffffu) : (uint32_t)kIdxUnused;
+    };
+    if (k == 4 && LK >= 4) {
+        u32x2 v;
+        v[0] = at(0) | (at(1) << 16);
+        v[1] = at(2) | (at(3) << 16);
+        *reinterpret_cast<u32x2 *>(out) = v;
+    } else if (k == 8 && LK >= 8) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = at(2 * i) | (at(2 * i + 1) << 16);
+        *reinterpret_cast<u32x4 *>(out) = v;
+    } else {
+#pragma unroll
+        for (int r = 0; r < LK; ++r)
+            if (r < k) out[r] = (uint16_t)at(r);
+    }
+}
+
 // Exact rescore of one token's LK candidates in one lane: fp64 distances in
 // coordinate order without fused multiply-add, sort by (distance, ordinal),
 // certificate; the result or a fallback entry is written.  ncand is the
@@ -924,9 +950,7 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
         ok = ok && nvalid == ncand;
     }
     if (ok) {
-#pragma unroll
-        for (int r = 0; r < LK; ++r)
-            if (r < k) out[r] = r < kk ? (uint16_t)jj[r] : kIdxUnused;
+        store_idx<LK>(out, jj, k, kk);
     } else {
         const uint32_t slot = atomicAdd(fcount, 1u);
         flist[slot] = fentry;
@@ -1345,9 +1369,7 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
             ok = ok && nvalid == ncand;
         }
         if (!ok) return false;
-#pragma unroll
-        for (int r = 0; r < LK; ++r)
-            if (r < k) o[r] = r < kk ? (uint16_t)jj[r] : kIdxUnused;
+        store_idx<LK>(o, jj, k, kk);
         return true;
     };
 
