@@ -864,7 +864,9 @@ __device__ __forceinline__ void store_idx(uint16_t *__restrict__ out, const int 
 // coordinate order without fused multiply-add, sort by (distance, ordinal),
 // certificate; the result or a fallback entry is written.  ncand is the
 // token's reference count: a list that is not full must hold all of them.
-template <int D, int LK>
+// CU chunks of 16 bytes are requested per candidate at once (memory round
+// trips: D / 8 / CU; registers: 4 LK CU).
+template <int D, int LK, int CU = 1>
 __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
                              const float (&lst)[LK], uint32_t imask, int ibits, int k, int ncand,
                              float rmax2, bool write, uint16_t *__restrict__ out,
@@ -882,6 +884,7 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
 #pragma unroll
     for (int e = 0; e < LK; ++e) dd[e] = 0.0;
     double xsq = 0.0;
+#pragma unroll CU
     for (int c = 0; c < D / 8; ++c) {
         const u32x4 xv = ld16(xrow + 8 * c);
         double xd[8];
@@ -1412,7 +1415,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
     const int64_t q = q0 + qi;
     const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(q, s) - t0)) * D;
     const int ncand = (int)((tok_pos(q, s) + s - 1) / s);
-    rescore_lane<D, LK>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, ncand, rmax2, true,
+    rescore_lane<D, LK, 4>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, ncand, rmax2, true,
                         idx + ((int64_t)unit * Ncap + q) * k, ((uint64_t)unit << 32) | (uint64_t)qi,
                         flist, fcount);
 }
