@@ -92,6 +92,21 @@ def test_shape_variants(cfg):
     _run_case(f"variant-{cfg}", 1, 2, G, T, d, s, k, dc, hid, dtype, seed=3 + s + k)
 
 
+@pytest.mark.parametrize("cfg", [
+    # (B, H, G, T, d, s, k, dc, hid, dtype)
+    (3, 2, 4, 1100, 128, 16, 4, 32, 256, dk.BF16),   # wave-specialised decode
+    (2, 3, 2, 700, 64, 8, 8, 16, 128, dk.BF16),      # four-wave decode, k = 8
+    (2, 2, 4, 300, 64, 16, 4, 16, 128, dk.F32),      # general (fp32) paths
+    (8, 8, 4, 1536, 128, 16, 4, 32, 256, dk.BF16),   # batch 8, all KV heads
+])
+def test_batched_sequences(cfg):
+    # several sequences in one call: every (sequence, KV head) unit of the
+    # compression and every query head of the decode against the oracle
+    B, H, G, T, d, s, k, dc, hid, dtype = cfg
+    _run_case(f"batch-{cfg}", B, H, G, T, d, s, k, dc, hid, dtype, seed=130 + B + d,
+              bias_std=0.05)
+
+
 def test_streaming_chunks_match_offline_bitwise():
     B, H, T, d, s, k, dc, hid = 1, 2, 700, 128, 8, 8, 16, 256
     say(f"[case] streaming: T={T}")
