@@ -217,32 +217,38 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 rv[m][r] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(ref_rsrc, off, 0, 0));
             }
-            inv[m] = 1.f / (float)keff;
+            // 1 / k_eff (exact for 1, 2, 4, 8; within an ulp otherwise,
+            // far below the bf16 rounding of the residual)
+            inv[m] = __builtin_amdgcn_rcpf((float)keff);
         }
+    };
+    // the sum of the chosen rows per coordinate with bf16 dot products: one
+    // byte permute pairs coordinate c of two rows, one v_dot2 adds both
+    // (products by one are exact; fp32 sums), then x - sum / k_eff
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+    auto dot_ones = [&](uint32_t pair, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), one2, acc, false);
     };
     auto residual = [&]() {
 #pragma unroll
         for (int m = 0; m < NI; ++m) {
             const int item = tid + 256 * m;
             const int t = item / CH, c8 = item % CH;
-            float acc[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = __uint_as_float(rv[m][0][e] << 16);
-                acc[2 * e + 1] = __uint_as_float(rv[m][0][e] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int r = 1; r < KX; ++r)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += __uint_as_float(rv[m][r][e] << 16);
-                    acc[2 * e + 1] += __uint_as_float(rv[m][r][e] & 0xffff0000u);
-                }
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float d0 = __uint_as_float(xv[m][e] << 16) - acc[2 * e] * inv[m];
-                const float d1 = __uint_as_float(xv[m][e] & 0xffff0000u) - acc[2 * e + 1] * inv[m];
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int r = 0; r + 1 < KX; r += 2) {
+                    // [row r, row r + 1] of the low, then the high coordinate
+                    const uint32_t lo = __builtin_amdgcn_perm(rv[m][r + 1][e], rv[m][r][e], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(rv[m][r + 1][e], rv[m][r][e], 0x07060302u);
+                    s0 = dot_ones(lo, s0);
+                    s1 = dot_ones(hi, s1);
+                }
+                const float d0 = __builtin_fmaf(-s0, inv[m], __uint_as_float(xv[m][e] << 16));
+                const float d1 = __builtin_fmaf(-s1, inv[m], __uint_as_float(xv[m][e] & 0xffff0000u));
                 o[e] = pack_bf16(d0, d1);
             }
             *reinterpret_cast<u32x4 *>(&dl[t][8 * c8]) = o;
