@@ -75,11 +75,12 @@ constexpr int64_t kListSplitCap = 1024;
 constexpr int kMaxK = 8;
 
 // Reference chunk per wave and wave count per token of the split scan of a
-// fallback list: 64 references (one per lane) per wave, more once a token
-// would need over 256 waves.
+// fallback list: 64 references (one per lane) per wave, more (a multiple of
+// 64) once a token would need over 128 waves, which bounds the candidates
+// its merge reads.
 static void list_split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
     const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
-    const int64_t c = std::max<int64_t>(64, (rmax + 255) / 256 + 63) / 64 * 64;
+    const int64_t c = ((rmax + 127) / 128 + 63) / 64 * 64;
     *chunk = (int)c;
     *nsplit = (int)((rmax + c - 1) / c);
 }
@@ -1406,11 +1407,26 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
     for (int e = 0; e < LK; ++e) lst[e] = -INFINITY;
     float rmax2 = 0.f;
     const int tile = (int)(qi / 256);
-    for (int sp = 0; sp < nsplit; ++sp) {
-        const float *src = lists + (((int64_t)sp * U + unit) * nq + qi) * LK;
+    // four splits' lists requested at a time, then merged
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
+        float v[4][LK];
+        float rm[4];
 #pragma unroll
-        for (int e = 0; e < LK; ++e) list_insert<LK>(lst, src[e]);
-        rmax2 = fmaxf(rmax2, rmaxs[((int64_t)sp * U + unit) * ntiles + tile]);
+        for (int u = 0; u < 4; ++u) {
+            const int sp = min(sp0 + u, nsplit - 1);  // a repeated list merges to no change
+            const float *src = lists + (((int64_t)sp * U + unit) * nq + qi) * LK;
+#pragma unroll
+            for (int e = 0; e < LK; ++e) v[u][e] = src[e];
+            rm[u] = rmaxs[((int64_t)sp * U + unit) * ntiles + tile];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (sp0 + u < nsplit) {
+#pragma unroll
+                for (int e = 0; e < LK; ++e) list_insert<LK>(lst, v[u][e]);
+                rmax2 = fmaxf(rmax2, rm[u]);
+            }
+        }
     }
     const int64_t q = q0 + qi;
     const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(q, s) - t0)) * D;
