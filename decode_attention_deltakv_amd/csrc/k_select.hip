@@ -867,6 +867,13 @@ __device__ __forceinline__ void store_idx(uint16_t *__restrict__ out, const int 
 // token's reference count: a list that is not full must hold all of them.
 // CU chunks of 16 bytes are requested per candidate at once (memory round
 // trips: D / 8 / CU; registers: 4 LK CU).
+template <int D, int LK>
+__device__ __forceinline__ void rescore_finish(double (&dd)[LK], int (&jj)[LK], const float (&lst)[LK],
+                                               double xsq, int ibits, int k, int ncand, float rmax2,
+                                               uint16_t *__restrict__ out, uint64_t fentry,
+                                               uint64_t *__restrict__ flist,
+                                               uint32_t *__restrict__ fcount);
+
 template <int D, int LK, int CU = 1>
 __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__restrict__ urefs,
                              const float (&lst)[LK], uint32_t imask, int ibits, int k, int ncand,
@@ -921,6 +928,18 @@ __device__ void rescore_lane(const bf16_t *__restrict__ xrow, const bf16_t *__re
         jj[e] = cv[e] ? jj[e] : INT_MAX;
     }
     if (!write) return;
+    rescore_finish<D, LK>(dd, jj, lst, xsq, ibits, k, ncand, rmax2, out, fentry, flist, fcount);
+}
+
+// Sort of a token's exact candidate distances by (distance, ordinal)
+// (unused candidates: +inf, INT_MAX), certificate, and the result or a
+// fallback entry.
+template <int D, int LK>
+__device__ __forceinline__ void rescore_finish(double (&dd)[LK], int (&jj)[LK], const float (&lst)[LK],
+                                               double xsq, int ibits, int k, int ncand, float rmax2,
+                                               uint16_t *__restrict__ out, uint64_t fentry,
+                                               uint64_t *__restrict__ flist,
+                                               uint32_t *__restrict__ fcount) {
     // sort by (distance, ordinal): odd-even transposition network
 #pragma unroll
     for (int pass = 0; pass < LK; ++pass) {
@@ -1390,7 +1409,10 @@ __global__ __launch_bounds__(256, 3) void dist_topk_kernel(
 // Merge of the split top-k searches: per token, the LK best of the splits'
 // lists (each split excluded only references below its own last entry, which
 // is at most the merged last entry, so the certificate holds with it), then
-// the exact fp64 rescore and certificate of one lane per token.
+// the exact fp64 rescore and certificate.  Four lanes per token: each merges
+// the lists, computes the exact distances of every fourth candidate (the
+// whole row requested at once) and the token norm, the distances are shared
+// within the four lanes, and the first lane sorts, certifies and writes.
 template <int D, int LK>
 __global__ __launch_bounds__(256) void topk_merge_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
@@ -1398,7 +1420,11 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
     int nsplit, uint32_t imask, int ibits, const float *__restrict__ lists,
     const float *__restrict__ rmaxs, int ntiles, uint16_t *__restrict__ idx,
     uint64_t *__restrict__ flist, uint32_t *__restrict__ fcount) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+#pragma clang fp contract(off)
+    constexpr int NE = (LK + 3) / 4;  // candidates per lane
+    const int lane = threadIdx.x & 63, sub = lane & 3;
+    const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x / 4;
+    // the four lanes of a token share gid, so they leave together
     if (gid >= (int64_t)U * nq) return;
     const int unit = (int)(gid / nq);
     const int64_t qi = gid % nq;
@@ -1430,10 +1456,78 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
     }
     const int64_t q = q0 + qi;
     const bf16_t *xr = x + ((int64_t)unit * nrows + (tok_pos(q, s) - t0)) * D;
+    const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
     const int ncand = (int)((tok_pos(q, s) + s - 1) / s);
-    rescore_lane<D, LK, 4>(xr, refs + (int64_t)unit * Rcap * D, lst, imask, ibits, k, ncand, rmax2, true,
-                        idx + ((int64_t)unit * Ncap + q) * k, ((uint64_t)unit << 32) | (uint64_t)qi,
-                        flist, fcount);
+    int jj[LK];
+    bool cv[LK];
+#pragma unroll
+    for (int e = 0; e < LK; ++e) {
+        cv[e] = lst[e] != -INFINITY;
+        jj[e] = cv[e] ? unpack_ordinal(lst[e], imask) : 0;
+    }
+    // the token row in fp64-ready form and its norm (coordinate order)
+    u32x4 xv[D / 8];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) xv[c] = ld16(xr + 8 * c);
+    double xsq = 0.0;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double a0 = (double)__uint_as_float(xv[c][i] << 16);
+            const double a1 = (double)__uint_as_float(xv[c][i] & 0xffff0000u);
+            const double s0 = a0 * a0;
+            xsq = xsq + s0;
+            const double s1 = a1 * a1;
+            xsq = xsq + s1;
+        }
+    // this lane's candidates sub, sub + 4, ...: each row requested whole
+    double mine[NE];
+#pragma unroll
+    for (int u = 0; u < NE; ++u) mine[u] = 0.0;
+#pragma unroll 1
+    for (int u = 0; u < NE; ++u) {
+        const int e = sub + 4 * u;
+        int je = jj[0];
+#pragma unroll
+        for (int q2 = 1; q2 < LK; ++q2) je = q2 == e ? jj[q2] : je;
+        u32x4 rv[D / 8];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) rv[c] = ld16(at_byte(urefs, ((uint32_t)je * D + 8u * c) * 2u));
+        // (the token row's fp64 conversions stay in the loop: hoisted, they
+        // would take 2 D registers)
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) asm volatile("" : "+v"(xv[c]));
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double d0 = (double)__uint_as_float(xv[c][i] << 16) -
+                                  (double)__uint_as_float(rv[c][i] << 16);
+                const double s0 = d0 * d0;
+                acc = acc + s0;
+                const double d1 = (double)__uint_as_float(xv[c][i] & 0xffff0000u) -
+                                  (double)__uint_as_float(rv[c][i] & 0xffff0000u);
+                const double s1 = d1 * d1;
+                acc = acc + s1;
+            }
+#pragma unroll
+        for (int u2 = 0; u2 < NE; ++u2) mine[u2] = u2 == u ? acc : mine[u2];
+    }
+    // gather the distances of all candidates (candidate e from lane e % 4)
+    double dd[LK];
+    const int gbase = lane & ~3;
+#pragma unroll
+    for (int e = 0; e < LK; ++e) {
+        const double d = __shfl(mine[e / 4], gbase + (e % 4), 64);
+        dd[e] = cv[e] ? d : __builtin_inf();
+        jj[e] = cv[e] ? jj[e] : INT_MAX;
+    }
+    if (sub == 0)
+        rescore_finish<D, LK>(dd, jj, lst, xsq, ibits, k, ncand, rmax2,
+                              idx + ((int64_t)unit * Ncap + q) * k,
+                              ((uint64_t)unit << 32) | (uint64_t)qi, flist, fcount);
 }
 
 __global__ void zero_u32_kernel(uint32_t *p) {
@@ -1465,7 +1559,7 @@ void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_
                        c.sqn, dm.R, dm.N, q0, nq, U, ntiles, imask, ibits, c.idx, flist, fcount,
                        nsplit, chunk, lists, rmaxs);
     if (nsplit > 1)
-        hipLaunchKernelGGL((topk_merge_kernel<D, LK>), dim3((unsigned)((U * nq + 255) / 256)),
+        hipLaunchKernelGGL((topk_merge_kernel<D, LK>), dim3((unsigned)((U * nq + 63) / 64)),
                            dim3(256), 0, st, (const bf16_t *)x, t0, t1 - t0, dm.s, dm.k,
                            (const bf16_t *)c.refs, dm.R, dm.N, q0, nq, U, nsplit, imask, ibits,
                            lists, rmaxs, ntiles, c.idx, flist, fcount);
