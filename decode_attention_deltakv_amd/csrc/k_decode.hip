@@ -323,11 +323,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
     __shared__ float qs[kMaxG][kMaxD];
     __shared__ float red[1][32][kMaxH];
     const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, H = gridDim.y;
-    for (int i = tid; i < G * d; i += 256)
-        qs[i / d][i % d] = to_f32(q[((int64_t)b * Hq + h * G + i / d) * d + i % d]);
-    __syncthreads();
+    // the query rows in LDS (fp32), for every block but the matrix-core
+    // qR blocks, which load their operands straight into registers together
+    // with the reference rows (one memory round trip)
+    auto stage_q = [&]() {
+        for (int i = tid; i < G * d; i += 256)
+            qs[i / d][i % d] = to_f32(q[((int64_t)b * Hq + h * G + i / d) * d + i % d]);
+        __syncthreads();
+    };
     const int64_t unit = (int64_t)b * H + h;
     const int GQ = qr_heads(G);
+    if (sizeof(T) != 2 || (int)blockIdx.x >= nrb) stage_q();
     if ((int)blockIdx.x < nrb) {
         if constexpr (sizeof(T) == 2) {
             // bf16: matrix cores, qR^T tile = R (16 rows x d) . Q^T (d x 16
