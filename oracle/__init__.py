@@ -20,6 +20,11 @@ Parity status per function (what pins it; the tests under tests/ hold them):
   reconstruct       pinned: orthogonal identity pair gives back the input.
   attention         pinned: torch scaled_dot_product_attention in fp64 and the
                     q = 0 closed form.
+  reconstruct_at    pinned: orthogonal identity pair gives back the input rows
+                    at the listed positions; rows equal the full rebuild's.
+  decode_head_sparse pinned: the full position list gives the dense decode;
+                    with the identity pair it is dense attention over x at the
+                    listed positions; order, padding and duplicate invariants.
   Latent and decode values under random GELU weights have no printed value to
   compare with; they are pinned only through the pieces above.
 """
@@ -72,6 +77,11 @@ def _load():
     lib.oracle_reconstruct.argtypes = [_dp, _dp, _i32p, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _dp, _dp, _dp, _dp, ctypes.c_int32, _dp]
+    lib.oracle_reconstruct_at.restype = None
+    lib.oracle_reconstruct_at.argtypes = [_dp, _dp, _i32p, _i64p, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp, _dp,
+                                          ctypes.c_int32, _dp]
     lib.oracle_attention.restype = None
     lib.oracle_attention.argtypes = [_dp, ctypes.c_int32, _dp, _dp, ctypes.c_int64,
                                      ctypes.c_int32, ctypes.c_double, _dp]
@@ -198,6 +208,22 @@ def reconstruct(refs, latents, idx, T: int, s: int, m: MLP) -> np.ndarray:
     return xhat
 
 
+def reconstruct_at(refs, latents, idx, positions, s: int, m: MLP) -> np.ndarray:
+    """Rows of the given positions (each in [0, T)), rebuilt on demand."""
+    refs = _f64(refs)
+    latents = _f64(latents)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64))
+    d = refs.shape[1]
+    k = idx.shape[1]
+    xhat = np.zeros((len(pos), d), dtype=np.float64)
+    _load().oracle_reconstruct_at(_ptr(refs), _ptr(latents), _ptr(idx, _i32p),
+                                  _ptr(pos, _i64p), len(pos), s, d, k, m.din, m.hidden,
+                                  _ptr(m.w1), _ptr(m.b1), _ptr(m.w2), _ptr(m.b2), m.act,
+                                  _ptr(xhat))
+    return xhat
+
+
 def attention(q, keys, vals, scale: float) -> np.ndarray:
     q = _f64(q)
     keys = _f64(keys)
@@ -231,4 +257,20 @@ def decode_head(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat, v_idx,
     over the T tokens rebuilt from the compressed K and V of one head."""
     khat = reconstruct(k_refs, k_lat, k_idx, T, s, k_dec)
     vhat = reconstruct(v_refs, v_lat, v_idx, T, s, v_dec)
+    return attention(q_heads, khat, vhat, scale)
+
+
+def decode_head_sparse(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat, v_idx,
+                       v_dec: MLP, T: int, s: int, scale: float, positions) -> np.ndarray:
+    """Attention of q_heads [G, d] over only the listed positions of one head
+    (on-demand reconstruction for a sparse selection).  Entries outside
+    [0, T) are skipped; a position listed twice takes part twice; with no
+    position left the output is zero."""
+    pos = np.asarray(positions, dtype=np.int64).reshape(-1)
+    pos = pos[(pos >= 0) & (pos < T)]
+    q_heads = _f64(q_heads)
+    if len(pos) == 0:
+        return np.zeros_like(q_heads)
+    khat = reconstruct_at(k_refs, k_lat, k_idx, pos, s, k_dec)
+    vhat = reconstruct_at(v_refs, v_lat, v_idx, pos, s, v_dec)
     return attention(q_heads, khat, vhat, scale)

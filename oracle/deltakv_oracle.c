@@ -218,6 +218,37 @@ void oracle_reconstruct(const double *refs, const double *latents,
     free(dec);
 }
 
+/* On-demand reconstruction (section 4, "Implementazione: Sparse-vLLM": the
+ * kernels rebuild a token only when the sparse attention asks for it): the
+ * rows of the n_pos given positions, in the given order, each rebuilt exactly
+ * as oracle_reconstruct rebuilds it.  Every position must lie in [0, T) of a
+ * cache laid out as for oracle_reconstruct; a non-reference position p reads
+ * latent / index row q = p - (number of reference positions below p) =
+ * p - ((p - 1) / s + 1) (reading R1: the references below p are 0, s, 2s, ...
+ * up to p - 1).  xhat receives n_pos x d. */
+void oracle_reconstruct_at(const double *refs, const double *latents,
+                           const int32_t *idx, const int64_t *pos, int64_t n_pos,
+                           int32_t s, int32_t d, int32_t k, int32_t d_c, int32_t hidden,
+                           const double *w1, const double *b1, const double *w2,
+                           const double *b2, int32_t act, double *xhat) {
+    double *kvr = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dec = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int64_t i = 0; i < n_pos; ++i) {
+        const int64_t p = pos[i];
+        double *row = xhat + i * d;
+        if (p % s == 0) {
+            memcpy(row, refs + (p / s) * d, sizeof(double) * (size_t)d);
+            continue;
+        }
+        const int64_t q = p - ((p - 1) / s + 1);
+        oracle_ref_mean(refs, idx + q * k, k, d, kvr);
+        oracle_mlp(latents + q * d_c, 1, d_c, hidden, d, w1, b1, w2, b2, act, dec);
+        for (int32_t c = 0; c < d; ++c) row[c] = kvr[c] + dec[c];
+    }
+    free(kvr);
+    free(dec);
+}
+
 /* Textbook softmax attention of n_q query rows against T key/value rows:
  * out_g = sum_t softmax_t(scale * q_g . k_t) v_t, with the row maximum
  * subtracted before exponentiation. */

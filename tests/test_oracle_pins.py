@@ -330,3 +330,131 @@ def test_decode_with_orthogonal_pair_is_dense_attention():
         torch.from_numpy(q)[None], torch.from_numpy(kx)[None], torch.from_numpy(vx)[None],
         scale=scale)[0].numpy()
     assert np.max(np.abs(got - want)) <= 1e-10 * np.max(np.abs(want))
+
+
+# ------------------------------------------------- on-demand (sparse) rebuild
+
+def _gelu_pair(rng, d, dc, h):
+    comp = MLP(rng.standard_normal((h, d)) * 0.3, rng.standard_normal(h) * 0.1,
+               rng.standard_normal((dc, h)) * 0.3, rng.standard_normal(dc) * 0.1)
+    dec = MLP(rng.standard_normal((h, dc)) * 0.3, rng.standard_normal(h) * 0.1,
+              rng.standard_normal((d, h)) * 0.3, rng.standard_normal(d) * 0.1)
+    return comp, dec
+
+
+@pytest.mark.parametrize("d,s,k", [(32, 16, 4), (16, 5, 3), (16, 1, 2)])
+def test_reconstruct_at_identity_pair_gives_input_rows(d, s, k):
+    # any order, references and compressed tokens mixed, repeats allowed
+    from deltakv_synth import kv_rows
+    T = 260
+    x = kv_rows(T, d, 4, 16, key=(31, d, s, k)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 23)
+    refs, idx, lat = oracle.compress_head(x, s, k, comp)
+    pos = np.concatenate([_rng(32).integers(0, T, 90), [0, T - 1, s, s + 1, 1, 1]])
+    got = oracle.reconstruct_at(refs, lat, idx, pos, s, dec)
+    assert np.max(np.abs(got - x[pos])) <= 1e-12 * np.max(np.abs(x))
+
+
+def test_reconstruct_at_matches_numpy_composition_by_searched_ordinal():
+    # the latent / index row of a compressed position is found here by searching
+    # the sorted list of non-reference positions, not by the oracle's closed form
+    rng = _rng(33)
+    T, d, s, k, dc, h = 150, 12, 6, 3, 5, 16
+    x = rng.standard_normal((T, d)) * 3
+    comp, dec = _gelu_pair(rng, d, dc, h)
+    refs, idx, lat = oracle.compress_head(x, s, k, comp)
+    nonref = oracle.nonref_positions(T, s)
+    pos = rng.integers(0, T, 70)
+    got = oracle.reconstruct_at(refs, lat, idx, pos, s, dec)
+    for i, p in enumerate(pos):
+        if p % s == 0:
+            want = refs[p // s]
+        else:
+            q = int(np.searchsorted(nonref, p))
+            assert nonref[q] == p
+            row = idx[q][idx[q] >= 0]
+            want = refs[row].mean(axis=0) + _np_mlp(lat[q:q + 1], dec)[0]
+        assert np.max(np.abs(got[i] - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+    full = oracle.reconstruct(refs, lat, idx, T, s, dec)
+    assert np.max(np.abs(got - full[pos])) <= 1e-13 * np.max(np.abs(full))
+
+
+def _sparse_setup(seed, T=180, d=16, s=8, k=4, dc=6, h=16, G=3):
+    rng = _rng(seed)
+    kx = rng.standard_normal((T, d)) * 2
+    vx = rng.standard_normal((T, d))
+    comp, kdec = _gelu_pair(rng, d, dc, h)
+    _, vdec = _gelu_pair(rng, d, dc, h)
+    kr, ki, kl = oracle.compress_head(kx, s, k, comp)
+    vr, vi, vl = oracle.compress_head(vx, s, k, comp)
+    q = rng.standard_normal((G, d))
+    args = (kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, 1 / np.sqrt(d))
+    return rng, q, args
+
+
+def test_sparse_decode_over_every_position_is_the_dense_decode():
+    rng, q, args = _sparse_setup(34)
+    T = args[8]
+    dense = oracle.decode_head(q, *args)
+    got = oracle.decode_head_sparse(q, *args, rng.permutation(T))
+    assert np.max(np.abs(got - dense)) <= 1e-12 * np.max(np.abs(dense))
+
+
+def test_sparse_decode_with_identity_pair_is_attention_over_selected_rows():
+    from deltakv_synth import kv_rows
+    T, d, s, k = 240, 32, 8, 4
+    kx = kv_rows(T, d, 4, 16, key=(35, 0)).double().numpy()
+    vx = kv_rows(T, d, 4, 16, key=(35, 1)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 36)
+    kr, ki, kl = oracle.compress_head(kx, s, k, comp)
+    vr, vi, vl = oracle.compress_head(vx, s, k, comp)
+    q = _rng(37).standard_normal((4, d))
+    pos = np.sort(_rng(38).choice(T, 50, replace=False))
+    scale = 1 / np.sqrt(d)
+    got = oracle.decode_head_sparse(q, kr, kl, ki, dec, vr, vl, vi, dec, T, s, scale, pos)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kx[pos])[None],
+        torch.from_numpy(vx[pos])[None], scale=scale)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-10 * np.max(np.abs(want))
+
+
+def test_sparse_decode_order_and_padding_do_not_matter():
+    rng, q, args = _sparse_setup(39)
+    T = args[8]
+    pos = rng.choice(T, 40, replace=False)
+    base = oracle.decode_head_sparse(q, *args, pos)
+    shuffled = oracle.decode_head_sparse(q, *args, rng.permutation(pos))
+    padded = oracle.decode_head_sparse(q, *args, np.concatenate([[-1, T, T + 7], pos, [-5]]))
+    assert np.max(np.abs(shuffled - base)) <= 1e-13 * np.max(np.abs(base))
+    assert np.array_equal(padded, base)
+
+
+def test_sparse_decode_repeated_position_weighs_twice():
+    # listing a position twice is attention with that row's logit raised by ln 2
+    rng, q, args = _sparse_setup(40)
+    kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, scale = args
+    pos = rng.choice(T, 30, replace=False)
+    got = oracle.decode_head_sparse(q, *args, np.concatenate([pos, pos[:1]]))
+    kh = oracle.reconstruct_at(kr, kl, ki, pos, s, kdec)
+    vh = oracle.reconstruct_at(vr, vl, vi, pos, s, vdec)
+    bias = torch.zeros(1, len(pos), dtype=torch.float64)
+    bias[0, 0] = np.log(2.0)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kh)[None], torch.from_numpy(vh)[None],
+        attn_mask=bias[None], scale=scale)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_sparse_decode_single_position_returns_its_value_row():
+    rng, q, args = _sparse_setup(41)
+    kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, scale = args
+    for p in (0, 1, s, T - 1):
+        got = oracle.decode_head_sparse(q, *args, [p])
+        vrow = oracle.reconstruct_at(vr, vl, vi, [p], s, vdec)[0]
+        assert np.max(np.abs(got - vrow[None])) <= 1e-14 * max(1.0, np.max(np.abs(vrow)))
+
+
+def test_sparse_decode_with_nothing_selected_is_zero():
+    rng, q, args = _sparse_setup(42)
+    T = args[8]
+    assert np.array_equal(oracle.decode_head_sparse(q, *args, [-1, T]), np.zeros_like(q))
