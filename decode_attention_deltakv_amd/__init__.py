@@ -15,6 +15,9 @@ available as an alias):
     build_refs(shape, x, t0, t1, cache)
     compress(shape, x, t0, t1, compressor, cache, workspace, stats=None)
     decode_attn(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out, workspace)
+    decode_sparse_workspace_bytes(shape, Hq, T, n_sel) -> int
+    decode_attn_sparse(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, positions, scale,
+                       out, workspace)
 
 `Cache` and `Mlp` below only hold torch tensors and build the C structs.
 """
@@ -89,9 +92,16 @@ def lib():
                                       ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                       ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                       ctypes.c_float, _P, _P, _SZ, _P]
+    L.deltakv_decode_sparse_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
+                                                        ctypes.c_int32, ctypes.POINTER(_SZ)]
+    L.deltakv_decode_attn_sparse.argtypes = [sp, ctypes.c_int32, ctypes.c_int64, _P,
+                                             ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                             ctypes.POINTER(CCache), ctypes.POINTER(CMlp), _P,
+                                             ctypes.c_int32, ctypes.c_float, _P, _P, _SZ, _P]
     for name in ("deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
-                 "deltakv_decode_attn"):
+                 "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
+                 "deltakv_decode_attn_sparse"):
         getattr(L, name).restype = ctypes.c_int
     L.deltakv_status_string.argtypes = [ctypes.c_int]
     L.deltakv_status_string.restype = ctypes.c_char_p
@@ -246,6 +256,32 @@ def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, 
                                      _ptr(workspace), wsb, _stream()))
 
 
+def decode_sparse_workspace_bytes(shape: Shape, num_q_heads: int, n_tokens: int,
+                                  n_sel: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_decode_sparse_workspace_bytes(ctypes.byref(cs), num_q_heads, n_tokens,
+                                                       n_sel, ctypes.byref(v)))
+    return v.value
+
+
+def decode_attn_sparse(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor,
+                       k_cache: Cache, k_dec: Mlp, v_cache: Cache, v_dec: Mlp,
+                       positions: torch.Tensor, scale: float, out: torch.Tensor,
+                       workspace: Optional[torch.Tensor]):
+    """positions: int32 [B, H, n_sel] on the device (n_sel = its last size)."""
+    cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if positions is not None and positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    n_sel = int(positions.shape[-1]) if positions is not None else 0
+    _check(lib().deltakv_decode_attn_sparse(ctypes.byref(cs), num_q_heads, n_tokens, _ptr(q),
+                                            ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
+                                            ctypes.byref(vm), _ptr(positions), n_sel,
+                                            float(scale), _ptr(out), _ptr(workspace), wsb,
+                                            _stream()))
+
+
 def status_string(status: int) -> str:
     return lib().deltakv_status_string(status).decode()
 
@@ -269,6 +305,8 @@ deltakv_decode_workspace_bytes = decode_workspace_bytes
 deltakv_build_refs = build_refs
 deltakv_compress = compress
 deltakv_decode_attn = decode_attn
+deltakv_decode_sparse_workspace_bytes = decode_sparse_workspace_bytes
+deltakv_decode_attn_sparse = decode_attn_sparse
 deltakv_status_string = status_string
 deltakv_last_error = last_error
 deltakv_version = version

@@ -126,6 +126,18 @@ deltakv_status check_range(const dk::Dims &dm, int64_t t0, int64_t t1) {
     return DELTAKV_OK;
 }
 
+deltakv_status check_heads_tokens(const dk::Dims &dm, int32_t num_q_heads, int64_t n_tokens) {
+    if (num_q_heads < 1 || num_q_heads % dm.H != 0 || num_q_heads / dm.H > 8)
+        return fail(DELTAKV_ERR_UNSUPPORTED,
+                    "num_q_heads %d must be a multiple of num_kv_heads %d, at most 8x",
+                    num_q_heads, dm.H);
+    if (n_tokens < 1 || n_tokens > dm.cap)
+        return fail(n_tokens > dm.cap ? DELTAKV_ERR_CAPACITY : DELTAKV_ERR_INVALID_ARG,
+                    "n_tokens %lld not in [1, capacity %lld]", (long long)n_tokens,
+                    (long long)dm.cap);
+    return DELTAKV_OK;
+}
+
 deltakv_status from_hip(hipError_t e, const char *what) {
     if (e == hipSuccess) return ok();
     return fail(DELTAKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -176,6 +188,21 @@ deltakv_status deltakv_decode_workspace_bytes(const deltakv_shape *shape, int32_
                     (long long)n_tokens);
     if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
     *bytes = dk::decode_ws_bytes(dm, num_q_heads, n_tokens);
+    return ok();
+}
+
+deltakv_status deltakv_decode_sparse_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     int32_t n_sel, size_t *bytes) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (n_sel < 1 || n_sel > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_sel %d not in [1, %d]", n_sel,
+                    DELTAKV_MAX_SPARSE_SELECT);
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::decode_sparse_ws_bytes(dm, num_q_heads, n_tokens, n_sel);
     return ok();
 }
 
@@ -257,6 +284,46 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
                                       softmax_scale, out, workspace, workspace_bytes,
                                       (hipStream_t)stream),
                     "deltakv_decode_attn");
+}
+
+deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          const int32_t *positions, int32_t n_sel,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (n_sel < 1 || n_sel > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_sel %d not in [1, %d]", n_sel,
+                    DELTAKV_MAX_SPARSE_SELECT);
+    if (!positions) return fail(DELTAKV_ERR_INVALID_ARG, "positions is NULL");
+    if (!aligned16(positions))
+        return fail(DELTAKV_ERR_INVALID_ARG, "positions must be 16-byte aligned");
+    if (!q || !out) return fail(DELTAKV_ERR_INVALID_ARG, "q / out is NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(DELTAKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
+    if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    const size_t need = dk::decode_sparse_ws_bytes(dm, num_q_heads, n_tokens, n_sel);
+    if (workspace_bytes < need || !workspace)
+        return fail(DELTAKV_ERR_WORKSPACE, "sparse decode needs %zu workspace bytes, got %zu",
+                    need, workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return from_hip(dk::launch_decode_sparse(dm, num_q_heads, n_tokens, q, kc, km, vc, vm,
+                                             positions, n_sel, softmax_scale, out, workspace,
+                                             workspace_bytes, (hipStream_t)stream),
+                    "deltakv_decode_attn_sparse");
 }
 
 const char *deltakv_status_string(deltakv_status status) {

@@ -48,6 +48,12 @@ size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T);
 hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const CacheArgs &kc,
                          const MlpArgs &kdec, const CacheArgs &vc, const MlpArgs &vdec,
                          float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+// sparse decode attention over listed positions pos[B][H][nsel]
+size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel);
+hipError_t launch_decode_sparse(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const int32_t *pos, int nsel, float scale,
+                                float *out, void *ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace dk
 

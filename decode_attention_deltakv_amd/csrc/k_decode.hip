@@ -58,20 +58,26 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct DecPlan {
     int64_t Rt, Nt, Ptok, Pref, P;
     int tiles_per_part;
-    size_t off_u, off_cq, off_qr, off_part, total;
+    size_t off_u, off_cq, off_qr, off_part, off_ord, off_cnt, total;
 };
 
-DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
+// Partitions and workspace of one decode call over T cached tokens; with
+// nsel >= 0, of a sparse call whose units list nsel positions each (the
+// partitions then cover the most compressed tokens and references such a
+// list can hold, and the workspace adds the split lists and their counts).
+DecPlan plan_decode(const Dims &dm, int Hq, int64_t T, int64_t nsel = -1) {
     DecPlan p;
     const int G = Hq / dm.H;
     p.Rt = refs_upto(T, dm.s);
     p.Nt = T - p.Rt;
+    const int64_t nc = nsel >= 0 ? std::min(nsel, p.Nt) : p.Nt;
+    const int64_t nr = nsel >= 0 ? std::min(nsel, p.Rt) : p.Rt;
     // about kTargetBlocks blocks per launch over all units, whole 32-token tiles
     const int64_t U = (int64_t)dm.B * dm.H;
-    const int64_t tiles = (p.Nt + kTileTok - 1) / kTileTok;
+    const int64_t tiles = (nc + kTileTok - 1) / kTileTok;
     const int64_t want = std::max<int64_t>(1, (kTargetBlocks + U - 1) / U);
     p.tiles_per_part = (int)std::max<int64_t>(2, (tiles + want - 1) / want);
-    p.Pref = (p.Rt + kRefPart - 1) / kRefPart;
+    p.Pref = (nr + kRefPart - 1) / kRefPart;
     // keep the partition count within what the merge holds in LDS
     const int64_t max_tok_parts = kMaxParts - p.Pref;
     if ((tiles + p.tiles_per_part - 1) / p.tiles_per_part > max_tok_parts)
@@ -87,6 +93,10 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T) {
     off += align_up((size_t)dm.B * dm.H * qr_rows(p.Rt) * qr_heads(G) * 4);
     p.off_part = off;
     off += align_up((size_t)dm.B * dm.H * p.P * G * kPStride * 4);
+    p.off_ord = off;
+    if (nsel >= 0) off += align_up((size_t)2 * U * nsel * 4);
+    p.off_cnt = off;
+    if (nsel >= 0) off += align_up((size_t)2 * U * 4);
     p.total = off;
     return p;
 }
@@ -100,7 +110,8 @@ __global__ __launch_bounds__(256) void main_kernel(
     const uint16_t *__restrict__ vidx, const T *__restrict__ kw1, const float *__restrict__ kb1,
     int khid, int kact, const T *__restrict__ vw1, const float *__restrict__ vb1, int vhid,
     int vact, float scale, const float *__restrict__ u, const float *__restrict__ cq,
-    const float *__restrict__ qr, float *__restrict__ part) {
+    const float *__restrict__ qr, float *__restrict__ part, const int32_t *__restrict__ sord,
+    const int32_t *__restrict__ scnt, int nsel) {
     (void)kref;
     (void)s;
     __shared__ float us[kMaxG][kMaxH];
@@ -118,6 +129,14 @@ __global__ __launch_bounds__(256) void main_kernel(
     const int tid = threadIdx.x;
     const int64_t unit = (int64_t)b * H + h;
     const int P = gridDim.x;
+    // sparse mode (sord non-null): list positions of the unit's selected
+    // compressed-token ordinals (sord[0][unit]) and reference ordinals
+    // (sord[1][unit]) replace consecutive ordinals
+    const bool sp = sord != nullptr;
+    const int32_t *cord_u = sp ? sord + unit * nsel : nullptr;
+    const int32_t *rord_u = sp ? sord + ((int64_t)gridDim.y * gridDim.z + unit) * nsel : nullptr;
+    const int64_t Nt_u = sp ? (int64_t)scnt[2 * unit] : Nt;
+    const int64_t Rt_u = sp ? (int64_t)scnt[2 * unit + 1] : Rt;
 
     for (int i = tid; i < G * kMaxH; i += 256) acc_h[i / kMaxH][i % kMaxH] = 0.f;
     for (int i = tid; i < G * kMaxD; i += 256) acc_r[i / kMaxD][i % kMaxD] = 0.f;
@@ -132,14 +151,18 @@ __global__ __launch_bounds__(256) void main_kernel(
         if (tid < G) cqs[tid] = cq[(int64_t)b * Hq + h * G + tid];
         __syncthreads();
         const int64_t qa = (int64_t)pidx * tok_per_part;
-        const int64_t qb = min(Nt, qa + tok_per_part);
+        const int64_t qb = min(Nt_u, qa + tok_per_part);
         for (int64_t q0 = qa; q0 < qb; q0 += kTB) {
             const int nt = (int)min((int64_t)kTB, qb - q0);
             // ---- K side: hidden tile and scores
-            for (int i = tid; i < nt * dc; i += 256)
-                z[i / dc][i % dc] = to_f32(klat[(unit * Ncap + q0 + i / dc) * dc + i % dc]);
-            for (int i = tid; i < nt * k; i += 256)
-                ids[i / k][i % k] = kidx[(unit * Ncap + q0 + i / k) * k + i % k];
+            for (int i = tid; i < nt * dc; i += 256) {
+                const int64_t o = sp ? cord_u[q0 + i / dc] : q0 + i / dc;
+                z[i / dc][i % dc] = to_f32(klat[(unit * Ncap + o) * dc + i % dc]);
+            }
+            for (int i = tid; i < nt * k; i += 256) {
+                const int64_t o = sp ? cord_u[q0 + i / k] : q0 + i / k;
+                ids[i / k][i % k] = kidx[(unit * Ncap + o) * k + i % k];
+            }
             __syncthreads();
             for (int i = tid; i < nt * khid; i += 256) {
                 const int t = i / khid, o = i % khid;
@@ -181,10 +204,14 @@ __global__ __launch_bounds__(256) void main_kernel(
                 alphas[g] = alpha;
             }
             // ---- V side: latents, hidden tile
-            for (int i = tid; i < nt * dc; i += 256)
-                z[i / dc][i % dc] = to_f32(vlat[(unit * Ncap + q0 + i / dc) * dc + i % dc]);
-            for (int i = tid; i < nt * k; i += 256)
-                ids[i / k][i % k] = vidx[(unit * Ncap + q0 + i / k) * k + i % k];
+            for (int i = tid; i < nt * dc; i += 256) {
+                const int64_t o = sp ? cord_u[q0 + i / dc] : q0 + i / dc;
+                z[i / dc][i % dc] = to_f32(vlat[(unit * Ncap + o) * dc + i % dc]);
+            }
+            for (int i = tid; i < nt * k; i += 256) {
+                const int64_t o = sp ? cord_u[q0 + i / k] : q0 + i / k;
+                ids[i / k][i % k] = vidx[(unit * Ncap + o) * k + i % k];
+            }
             __syncthreads();
             for (int i = tid; i < G * kMaxH; i += 256) acc_h[i / kMaxH][i % kMaxH] *= alphas[i / kMaxH];
             for (int i = tid; i < G * kMaxD; i += 256) acc_r[i / kMaxD][i % kMaxD] *= alphas[i / kMaxD];
@@ -226,12 +253,13 @@ __global__ __launch_bounds__(256) void main_kernel(
         // reference tokens: score = scale * qR, value = stored V row
         __syncthreads();
         const int64_t ja = (pidx - Ptok) * (int64_t)kRefPart;
-        const int64_t jb = min(Rt, ja + kRefPart);
+        const int64_t jb = min(Rt_u, ja + kRefPart);
         for (int64_t j0 = ja; j0 < jb; j0 += 64) {
             const int nj = (int)min((int64_t)64, jb - j0);
             for (int i = tid; i < G * nj; i += 256) {
                 const int g = i / nj, t = i % nj;
-                sc[g][t] = scale * qr[(unit * qr_rows(Rt) + j0 + t) * qr_heads(G) + g];
+                const int64_t j = sp ? rord_u[j0 + t] : j0 + t;
+                sc[g][t] = scale * qr[(unit * qr_rows(Rt) + j) * qr_heads(G) + g];
             }
             __syncthreads();
             if (tid < G) {
@@ -254,8 +282,10 @@ __global__ __launch_bounds__(256) void main_kernel(
             for (int i = tid; i < G * d; i += 256) {
                 const int g = i / d, c = i % d;
                 float acc = acc_r[g][c] * alphas[g];
-                for (int t = 0; t < nj; ++t)
-                    acc += sc[g][t] * to_f32(vref[(unit * Rcap + j0 + t) * d + c]);
+                for (int t = 0; t < nj; ++t) {
+                    const int64_t j = sp ? rord_u[j0 + t] : j0 + t;
+                    acc += sc[g][t] * to_f32(vref[(unit * Rcap + j) * d + c]);
+                }
                 acc_r[g][c] = acc;
             }
             __syncthreads();
@@ -442,6 +472,66 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
     }
 }
 
+// Split of the sparse position lists (on-demand reconstruction of selected
+// tokens).  grid U (one block per unit), 256 threads.  The valid entries
+// (0 <= p < T) of the unit's list pos[unit][0..nsel) are written, in list
+// order, as compressed-token ordinals q = p - ((p - 1) / s + 1) to
+// ord[0][unit][..] and as reference ordinals p / s to ord[1][unit][..]; the
+// two counts go to cnt[unit][0..1].  Entries outside [0, T) are skipped.
+__global__ __launch_bounds__(256) void sparse_split_kernel(const int32_t *__restrict__ pos,
+                                                           int nsel, int64_t T, int s, int U,
+                                                           int32_t *__restrict__ ord,
+                                                           int32_t *__restrict__ cnt) {
+    constexpr int PER = 4;  // entries per thread and chunk
+    __shared__ uint32_t wtot[4];
+    const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t *pu = pos + (int64_t)unit * nsel;
+    int32_t *cu = ord + (int64_t)unit * nsel;
+    int32_t *ru = ord + ((int64_t)U + unit) * nsel;
+    int nc = 0, nr = 0;  // entries written so far (block-uniform)
+    for (int base = 0; base < nsel; base += 256 * PER) {
+        int32_t v[PER];
+        uint32_t mine = 0;  // compressed count | reference count << 16
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int i = base + tid * PER + e;
+            v[e] = i < nsel ? pu[i] : -1;
+            const bool ok = v[e] >= 0 && (int64_t)v[e] < T;
+            mine += ok ? (v[e] % s == 0 ? 0x10000u : 1u) : 0u;
+        }
+        // exclusive scan of the packed counts over the block
+        uint32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        uint32_t before = inc - mine, total = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            before += i < w ? wtot[i] : 0u;
+            total += wtot[i];
+        }
+        int oc = nc + (int)(before & 0xffffu), orr = nr + (int)(before >> 16);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int32_t p = v[e];
+            if (p < 0 || (int64_t)p >= T) continue;
+            if (p % s == 0) ru[orr++] = p / s;
+            else cu[oc++] = p - ((p - 1) / s + 1);
+        }
+        nc += (int)(total & 0xffffu);
+        nr += (int)(total >> 16);
+        __syncthreads();  // wtot is rewritten by the next chunk
+    }
+    if (tid == 0) {
+        cnt[2 * unit] = nc;
+        cnt[2 * unit + 1] = nr;
+    }
+}
+
 // Log-sum-exp merge of the partitions of one query head, then W2V applied to
 // the merged hidden sum.  grid (Hq, B).  The merge of the record vectors runs
 // with one float4 column per thread and the partitions split across thread
@@ -466,7 +556,10 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
     const int64_t pstep = (int64_t)G * kPStride;
     float mx = -INFINITY;
     for (int64_t p = tid; p < P; p += NT) mx = fmaxf(mx, base[p * pstep]);
-    const float M = block_reduce<NW>(mx, red, true);
+    // M = -inf only when no partition holds a token (a sparse selection with
+    // no valid position): every weight is then 0 and the output row 0
+    const float M0 = block_reduce<NW>(mx, red, true);
+    const float M = M0 == -INFINITY ? 0.f : M0;
     float lsum = 0.f, ltsum = 0.f;
     for (int64_t p = tid; p < P; p += NT) {
         const float wp = __expf(base[p * pstep] - M);
@@ -520,7 +613,7 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
         float ws = 0.f;
         for (int k2 = 0; k2 < nsp; ++k2) ws += ored[k2][tid];
         const float bias = vb2 ? vb2[tid] : 0.f;
-        out[((int64_t)b * Hq + gq) * d + tid] = (accr[tid] + ws + Lt * bias) / L;
+        out[((int64_t)b * Hq + gq) * d + tid] = L > 0.f ? (accr[tid] + ws + Lt * bias) / L : 0.f;
     }
 }
 
@@ -549,7 +642,7 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
 // swizzled by 2 * (row % 4), so that the transposing reads of the B operand
 // (4 consecutive rows x 32 bytes per 16-lane group) fall in disjoint banks;
 // the per-head weight rows carry 16 bytes of padding for the same reason.
-template <int D, int DC, int HID, int KP>
+template <int D, int DC, int HID, int KP, bool SP>
 __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     int U, int Hq, int G, int k, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -558,7 +651,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const bf16_t *__restrict__ kw1, const float *__restrict__ kb1,
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
-    float *__restrict__ part) {
+    float *__restrict__ part, const int32_t *__restrict__ sord, const int32_t *__restrict__ scnt,
+    int nsel) {
     constexpr int TT = 32;              // tokens per tile
     constexpr int HW = HID / 4;         // hidden units per wave
     constexpr int MT = HW / 16;         // 16-row hidden tiles per wave
@@ -604,8 +698,18 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const int GQ = qr_heads(G);
     const float *qr_u = qr + (int64_t)unit * qr_rows(Rt) * GQ;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // Sparse mode (SP): the block walks the unit's lists of selected
+    // compressed-token ordinals (sord[0][unit]) and reference ordinals
+    // (sord[1][unit]) instead of consecutive ordinals; the list lengths are
+    // the unit's counts.  Ranges below are list positions, ord_c / the
+    // reference lookups map them to ordinals.
+    const int32_t *cord_u = SP ? sord + (int64_t)unit * nsel : nullptr;
+    const int32_t *rord_u = SP ? sord + ((int64_t)U + unit) * nsel : nullptr;
+    const int64_t Nt_u = SP ? (int64_t)scnt[2 * unit] : Nt;
+    const int64_t Rt_u = SP ? (int64_t)scnt[2 * unit + 1] : Rt;
+    auto ord_c = [&](int i) -> uint32_t { return SP ? (uint32_t)cord_u[i] : (uint32_t)i; };
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
-    const int64_t qe_ = min(Nt, qa_ + (int64_t)tiles_per_part * TT);
+    const int64_t qe_ = min(Nt_u, qa_ + (int64_t)tiles_per_part * TT);
     // per-unit bases; all in-loop offsets are 32-bit
     const bf16_t *klat_u = klat + (int64_t)unit * Ncap * DC;
     const bf16_t *vlat_u = vlat + (int64_t)unit * Ncap * DC;
@@ -652,7 +756,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         // the rows go straight to LDS and enter the same value MFMA with one
         // slot per token and weight p.
         const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
-        const int64_t je = min(Rt, ja + kRefPart);
+        const int64_t je = min(Rt_u, ja + kRefPart);
         for (int64_t j0 = ja; j0 < je; j0 += TT) {
             __syncthreads();
 #pragma unroll
@@ -660,7 +764,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 const int it = tid + 256 * m;
                 const int row = it / CH, c8 = it % CH;
                 const int sc8 = c8 ^ (2 * (row & 3));
-                const int64_t j = min(j0 + row, Rt - 1);
+                const int64_t j = SP ? (int64_t)rord_u[min(j0 + row, je - 1)]
+                                     : min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
                     (__attribute__((address_space(3))) void *)&vrowA[(256 * m + 64 * w) / CH][0],
@@ -668,7 +773,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
             }
             if (sg_ok) {
                 const bool ok = j0 + st < je;
-                const float s = ok ? scale * qr_u[(j0 + st) * GQ + sg] : -INFINITY;
+                const int64_t jr = SP ? (int64_t)rord_u[min(j0 + st, je - 1)] : j0 + st;
+                const float s = ok ? scale * qr_u[jr * GQ + sg] : -INFINITY;
                 float tmax = s;
 #pragma unroll
                 for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
@@ -723,6 +829,12 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     }
 
     // ---------------- compressed tokens (matrix cores) ----------------
+    if (SP && qa32 >= qe32) {
+        // a partition past the end of this unit's list: a neutral record
+        for (int i = tid; i < G * kPStride; i += 256)
+            prec[i] = (i % kPStride == 0) ? -INFINITY : 0.f;
+        return;
+    }
     // weights into registers
     bf16x8 wK[WL ? 1 : MT][KS], wV[WL ? 1 : MT][KS];
     if constexpr (WL) {
@@ -788,7 +900,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         bf16x8 zk[2][KS], zv[2][KS];
     };
     auto load_tile = [&](int t0, TileIn &T) {
-        const uint32_t tk = (uint32_t)min(t0 + st, qe32 - 1);
+        const uint32_t tk = ord_c(min(t0 + st, qe32 - 1));
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const uint32_t ic = (uint32_t)(i < k ? i : k - 1);
@@ -797,7 +909,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         }
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2) {
-            const uint32_t tz = (uint32_t)min(t0 + 16 * n2 + l16, qe32 - 1);  // tail: a valid row
+            const uint32_t tz = ord_c(min(t0 + 16 * n2 + l16, qe32 - 1));  // tail: a valid row
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = 32 * ks + 8 * lq;
@@ -811,7 +923,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         for (int m = 0; m < GIT; ++m) {
             const int row = (tid + 256 * m) / CH;
             const int t = row / KP, i = row % KP;
-            const uint32_t tk = (uint32_t)min(t0 + t, qe32 - 1);
+            const uint32_t tk = ord_c(min(t0 + t, qe32 - 1));
             gr[m] = vidx_u[tk * k + (uint32_t)(i < k ? i : k - 1)];
         }
     };
@@ -1692,18 +1804,27 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     }
 }
 
+// Sparse lists of a call (SparseArgs::ord == nullptr: a dense call).
+struct SparseArgs {
+    const int32_t *ord;
+    const int32_t *cnt;
+    int nsel;
+};
+
 template <int D, int DC, int HID, int KP>
 void launch_mfma_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                    const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
-                   const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+                   const float *u, const float *cq, const float *qr, float *part,
+                   const SparseArgs &sa, hipStream_t st) {
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
-    hipLaunchKernelGGL((main_mfma_kernel<D, DC, HID, KP>), dim3((unsigned)(pl.P * U)), dim3(256),
+    auto kern = sa.ord ? main_mfma_kernel<D, DC, HID, KP, true> : main_mfma_kernel<D, DC, HID, KP, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256),
                        0, st, U, Hq, G, dm.k, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part,
                        (int)pl.Ptok, (int)pl.P, (const bf16_t *)kc.lat, kc.idx,
                        (const bf16_t *)vc.refs, (const bf16_t *)vc.lat, vc.idx,
                        (const bf16_t *)kd.w1, kd.b1, (const bf16_t *)vd.w1, vd.b1, scale, u, cq,
-                       qr, part);
+                       qr, part, sa.ord, sa.cnt, sa.nsel);
 }
 
 template <int D, int DC, int HID>
@@ -1742,16 +1863,16 @@ template <int D, int DC>
 bool launch_mfma_dc(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                     const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
                     const float *u, const float *cq, const float *qr, float *part,
-                    hipStream_t st) {
+                    const SparseArgs &sa, hipStream_t st) {
     const bool kp4 = dm.k <= 4;
     if (kd.hidden == 256) {
-        if (kp4) launch_mfma_t<D, DC, 256, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-        else launch_mfma_t<D, DC, 256, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        if (kp4) launch_mfma_t<D, DC, 256, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+        else launch_mfma_t<D, DC, 256, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
         return true;
     }
     if (kd.hidden == 128) {
-        if (kp4) launch_mfma_t<D, DC, 128, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-        else launch_mfma_t<D, DC, 128, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        if (kp4) launch_mfma_t<D, DC, 128, 4>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+        else launch_mfma_t<D, DC, 128, 8>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
         return true;
     }
     return false;
@@ -1765,38 +1886,49 @@ bool mfma_eligible(const Dims &dm, const MlpArgs &kd, const MlpArgs &vd) {
            kd.act == 0 && vd.act == 0 && dm.dc <= 64;
 }
 
+// One decode call; with pos non-null, the sparse call over the listed
+// positions pos[B][H][nsel] (the lists are split first, then the same
+// kernels walk them).
 template <typename T>
 hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            const CacheArgs &kc, const MlpArgs &kd, const CacheArgs &vc,
                            const MlpArgs &vd, float scale, float *out, void *ws,
-                           hipStream_t st) {
-    const DecPlan pl = plan_decode(dm, Hq, T_);
+                           const int32_t *pos, int nsel, hipStream_t st) {
+    const DecPlan pl = plan_decode(dm, Hq, T_, pos ? (int64_t)nsel : -1);
     const int G = Hq / dm.H;
     char *w = (char *)ws;
     float *u = (float *)(w + pl.off_u);
     float *cq = (float *)(w + pl.off_cq);
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
+    SparseArgs sa{nullptr, nullptr, 0};
+    if (pos) {
+        int32_t *ord = (int32_t *)(w + pl.off_ord);
+        int32_t *cnt = (int32_t *)(w + pl.off_cnt);
+        hipLaunchKernelGGL(sparse_split_kernel, dim3((unsigned)(dm.B * dm.H)), dim3(256), 0, st,
+                           pos, nsel, T_, dm.s, dm.B * dm.H, ord, cnt);
+        sa = SparseArgs{ord, cnt, nsel};
+    }
     const int nrb = (int)((qr_rows(pl.Rt) + 255) / 256);
     hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)(nrb + G), dm.H, dm.B), dim3(256), 0, st,
                        (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R, pl.Rt, nrb,
                        (const T *)kd.w2, kd.hidden, kd.b2, u, cq, qr);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-        if (mfma_eligible(dm, kd, vd)) {
+        if (!pos && mfma_eligible(dm, kd, vd)) {
             done = dm.d == 128
                        ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st)
                        : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
         }
         if (!done && mfma_eligible(dm, kd, vd)) {
             if (dm.d == 128) {
-                if (dm.dc == 16) done = launch_mfma_dc<128, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-                else if (dm.dc == 32) done = launch_mfma_dc<128, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-                else done = launch_mfma_dc<128, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                if (dm.dc == 16) done = launch_mfma_dc<128, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+                else if (dm.dc == 32) done = launch_mfma_dc<128, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+                else done = launch_mfma_dc<128, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
             } else {
-                if (dm.dc == 16) done = launch_mfma_dc<64, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-                else if (dm.dc == 32) done = launch_mfma_dc<64, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-                else done = launch_mfma_dc<64, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                if (dm.dc == 16) done = launch_mfma_dc<64, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+                else if (dm.dc == 32) done = launch_mfma_dc<64, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+                else done = launch_mfma_dc<64, 64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
             }
         }
     }
@@ -1806,7 +1938,8 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            (int64_t)pl.tiles_per_part * kTileTok, (const T *)kc.refs,
                            (const T *)kc.lat, kc.idx, (const T *)vc.refs, (const T *)vc.lat,
                            vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act, (const T *)vd.w1,
-                           vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part);
+                           vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part, sa.ord, sa.cnt,
+                           sa.nsel);
     hipLaunchKernelGGL(combine2_kernel<T>, dim3(Hq, dm.B), dim3(kCombThreads), 0, st, Hq, G, dm.d, dm.H,
                        pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out);
     return hipGetLastError();
@@ -1816,13 +1949,31 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
 
 size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T) { return plan_decode(dm, Hq, T).total; }
 
+size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel) {
+    return plan_decode(dm, Hq, T, nsel).total;
+}
+
 hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const CacheArgs &kc,
                          const MlpArgs &kdec, const CacheArgs &vc, const MlpArgs &vdec,
                          float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st) {
     (void)ws_bytes;
     if (dm.dtype == 0)
-        return launch_decode_t<float>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, st);
-    return launch_decode_t<bf16_t>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, st);
+        return launch_decode_t<float>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, nullptr,
+                                      0, st);
+    return launch_decode_t<bf16_t>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, nullptr, 0,
+                                   st);
+}
+
+hipError_t launch_decode_sparse(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const int32_t *pos, int nsel, float scale,
+                                float *out, void *ws, size_t ws_bytes, hipStream_t st) {
+    (void)ws_bytes;
+    if (dm.dtype == 0)
+        return launch_decode_t<float>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, pos,
+                                      nsel, st);
+    return launch_decode_t<bf16_t>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, pos, nsel,
+                                   st);
 }
 
 }  // namespace dk

@@ -173,6 +173,41 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
                                    float softmax_scale, float *out, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* Largest position list per (sequence, KV head) that the sparse decode takes. */
+#define DELTAKV_MAX_SPARSE_SELECT 1048576
+
+/* Host-only.  Workspace that deltakv_decode_attn_sparse needs for num_q_heads
+ * query heads over n_tokens cached tokens and lists of n_sel positions. */
+deltakv_status deltakv_decode_sparse_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     int32_t n_sel, size_t *bytes);
+
+/* Decode attention with on-demand reconstruction of selected tokens only
+ * (section 4, "Implementazione: Sparse-vLLM": the kernels rebuild a
+ * compressed token only when a sparse attention selects it, e.g. a
+ * query-aware selector of the OmniKV kind).  The selector is the caller's:
+ *   positions: device int32 [B][H][n_sel], read-only, the caller's buffer.
+ *              Row (b, h) lists the positions that the query heads of KV head
+ *              h of sequence b attend to, in any order.  Entries outside
+ *              [0, n_tokens) are skipped (padding for shorter lists); an entry
+ *              listed twice takes part twice.
+ * For each query head g of KV head h,
+ *   out[b][g] = sum_{t in list} softmax_t(scale * q[b][g] . K^_t) V^_t
+ * with K^/V^ rebuilt exactly as deltakv_decode_attn rebuilds them; a list
+ * with no valid entry gives a zero output row.  Listing every position
+ * 0..n_tokens-1 gives deltakv_decode_attn's result.  Other arguments, their
+ * layouts and requirements are as for deltakv_decode_attn; 1 <= n_sel <=
+ * DELTAKV_MAX_SPARSE_SELECT; workspace: deltakv_decode_sparse_workspace_bytes
+ * (the split position lists are kept there, so it must not be shared with a
+ * call still in flight). */
+deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          const int32_t *positions, int32_t n_sel,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *deltakv_status_string(deltakv_status status);
 

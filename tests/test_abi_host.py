@@ -163,3 +163,58 @@ def test_decode_head_grouping_checked():
     assert e.value.status == 2
     with pytest.raises(dk.DeltaKVError):
         dk.decode_workspace_bytes(sh, 32, 0)
+
+
+class _FakePos(_FakePtr):
+    """An int32 [B, H, n_sel] position-list stand-in."""
+
+    def __init__(self, n_sel, addr=0x40000):
+        super().__init__(addr, 4 * n_sel)
+        import torch
+        self.dtype = torch.int32
+        self.shape = (1, 8, n_sel)
+
+
+def test_sparse_workspace_grows_with_the_list_and_adds_to_the_dense_tables():
+    sh = _shape(capacity=131072)
+    small = dk.decode_sparse_workspace_bytes(sh, 32, 131072, 1024)
+    big = dk.decode_sparse_workspace_bytes(sh, 32, 131072, 8192)
+    assert 0 < small < big
+    # the split lists alone: two int32 lists of n_sel per unit
+    assert big - small >= 2 * 8 * (8192 - 1024) * 4
+    for bad in (0, -3, (1 << 20) + 1):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.decode_sparse_workspace_bytes(sh, 32, 131072, bad)
+        assert e.value.status == 1
+
+
+def test_sparse_decode_argument_errors_return_before_any_launch():
+    sh = _shape(capacity=4096)
+    dec = _mlp(32, 256, 128)
+    need = dk.decode_sparse_workspace_bytes(sh, 32, 4096, 64)
+    ok_ws = _FakePtr(0x30000, need)
+
+    def call(pos, ws=ok_ws, n_tokens=4096, hq=32):
+        dk.decode_attn_sparse(sh, hq, n_tokens, _FakePtr(), _cache(), dec, _cache(), dec, pos,
+                              0.088, _FakePtr(), ws)
+
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(None)                                   # no list
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64, addr=0x40004))             # misaligned list
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64), ws=_FakePtr(0x30000, need - 1))
+    assert e.value.status == 4
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64), n_tokens=4097)
+    assert e.value.status == 3
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64), hq=36)
+    assert e.value.status == 2
+    with pytest.raises(ValueError):
+        p = _FakePos(64)
+        import torch
+        p.dtype = torch.int64
+        call(p)
