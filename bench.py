@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sparse-select", type=int, default=4096,
+                    help="positions per (sequence, KV head) of the timed sparse decode calls "
+                         "(0: skip them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy before timing (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -202,6 +205,37 @@ def decode_bytes_per_layer(wl):
                + (wl.hidden + wl.head_dim) * 4)
     qo = wl.batch * wl.q_heads * wl.head_dim * (elt + 4)
     return wl.batch * wl.kv_heads * 2 * unit + dec + qo
+
+
+def sparse_bytes_per_layer(S, l, pos):
+    """Algorithmic HBM bytes of one sparse decode call (layer l) over the
+    position lists pos [B, H, n_sel]: per unit and stream, the latent and index
+    rows of the listed compressed tokens and one row of every reference that a
+    listed token names or that is listed itself (each read once), plus the
+    position lists, the two Decompressors, the queries and the output."""
+    wl = S.wl
+    elt = 4 if wl.dtype == "fp32" else 2
+    s = wl.stride
+    B, H, n = pos.shape
+    p = pos.long()
+    isref = p % s == 0
+    total = 0
+    for st in (0, 1):
+        idx = S.cache[l][st].idx.view(torch.int16)
+        for b in range(B):
+            for h in range(H):
+                r = isref[b, h]
+                pc = p[b, h][~r]
+                qc = pc - ((pc - 1) // s + 1)
+                rows = idx[b, h][qc].to(torch.int32) & 0xFFFF
+                rows = rows[rows != 0xFFFF]
+                touched = torch.unique(torch.cat([rows.flatten(), (p[b, h][r] // s).int()]))
+                total += int(pc.numel()) * (wl.d_c * elt + wl.k * 2)
+                total += int(touched.numel()) * wl.head_dim * elt
+    dec = 2 * ((wl.d_c * wl.hidden + wl.hidden * wl.head_dim) * elt
+               + (wl.hidden + wl.head_dim) * 4)
+    qo = wl.batch * wl.q_heads * wl.head_dim * (elt + 4)
+    return total + B * H * n * 4 + dec + qo
 
 
 def compress_flops(wl):
@@ -398,6 +432,35 @@ def main():
     per_layer_bytes = decode_bytes_per_layer(wl)
     achieved = per_layer_bytes / (launch_ms * 1e-3) / 1e9
 
+    # sparse decode (on-demand reconstruction of a selected subset only):
+    # n_sel sorted random positions per (sequence, KV head), single calls
+    sparse = None
+    if not wl.appends and a.sparse_select > 0:
+        from deltakv_synth import selections
+        n_sel = min(a.sparse_select, wl.T)
+        pos = selections(wl.batch * wl.kv_heads, wl.T, n_sel, key=(4, widx),
+                         device="cuda").reshape(wl.batch, wl.kv_heads, n_sel)
+        sws = S.dk.workspace(S.dk.decode_sparse_workspace_bytes(S.shape, S.Hq, wl.T, n_sel))
+        sstarts, sends = [ev() for _ in range(n_launch)], [ev() for _ in range(n_launch)]
+        for rep_ in range(2):   # the first pass warms up
+            for i in range(n_launch):
+                l = i % wl.layers
+                c, d = S.cache[l], S.dec[l]
+                sstarts[i].record(stream)
+                S.dk.decode_attn_sparse(S.shape, S.Hq, wl.T, qs[l], c[0], d[0], c[1], d[1],
+                                        pos, S.scale, S.out, sws)
+                sends[i].record(stream)
+            torch.cuda.synchronize()
+        sp_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
+        sp_bytes = float(np.mean([sparse_bytes_per_layer(S, i % wl.layers, pos)
+                                  for i in range(min(n_launch, wl.layers))]))
+        sparse = {"positions_per_kv_head": n_sel, "selected_fraction": n_sel / wl.T,
+                  "launch_ms": sp_ms, "speedup_vs_dense_launch": launch_ms / sp_ms,
+                  "algorithmic_bytes_per_launch": sp_bytes,
+                  "eff_hbm_gbs": sp_bytes / (sp_ms * 1e-3) / 1e9}
+        log(f"[bench] sparse decode ({n_sel} positions per KV head): {sp_ms:.4f} ms per layer")
+        del sws
+
     # one decode step (every layer) captured in a HIP graph and replayed, with
     # fresh queries copied into the captured query buffer before each replay
     graph_ms = None
@@ -466,6 +529,7 @@ def main():
         "decode_eff_hbm_gbs": step_bytes * dsteps / (dec_ms * 1e-3) / 1e9,
         "fallback_tokens_per_compress": int(S.stats[0].item()) // a.steps,
         "measured_copy_gbs": copy_gbs,
+        "sparse_decode": sparse,
         "roofline": {"kernel": "deltakv_decode_attn (one layer)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(wl),

@@ -45,6 +45,7 @@ constexpr int kRefPart = 512;  // reference rows per partition
 constexpr int kMaxParts = 4096; // partitions per unit (combine keeps their weights in LDS)
 constexpr int kPStride = 4 + kMaxD + kMaxH;  // floats per (partition, query head)
 constexpr int kCombThreads = 256;               // threads of the combine kernel
+constexpr int kSpTiles = 16;   // most 32-token tiles per partition of a sparse call
 
 // The q.R^K table keeps its query heads padded to a multiple of 4 (zeros), so
 // a lane can read the 4 heads of its row group with one 16-byte load, and one
@@ -78,10 +79,19 @@ DecPlan plan_decode(const Dims &dm, int Hq, int64_t T, int64_t nsel = -1) {
     const int64_t want = std::max<int64_t>(1, (kTargetBlocks + U - 1) / U);
     p.tiles_per_part = (int)std::max<int64_t>(2, (tiles + want - 1) / want);
     p.Pref = (nr + kRefPart - 1) / kRefPart;
+    if (nsel >= 0) {
+        // a sparse call is short: its token and reference blocks together
+        // should fit the kTargetBlocks that run at once (two per CU), or the
+        // blocks past them run as a second round
+        const int64_t ptok_max = std::max<int64_t>(1, kTargetBlocks / U - p.Pref);
+        p.tiles_per_part = (int)std::max<int64_t>(1, (tiles + ptok_max - 1) / ptok_max);
+    }
     // keep the partition count within what the merge holds in LDS
     const int64_t max_tok_parts = kMaxParts - p.Pref;
     if ((tiles + p.tiles_per_part - 1) / p.tiles_per_part > max_tok_parts)
         p.tiles_per_part = (int)((tiles + max_tok_parts - 1) / max_tok_parts);
+    // a sparse partition stages its list entries in LDS: at most kSpTiles tiles
+    if (nsel >= 0) p.tiles_per_part = std::min(p.tiles_per_part, kSpTiles);
     p.Ptok = (tiles + p.tiles_per_part - 1) / p.tiles_per_part;
     p.P = p.Ptok + p.Pref;
     size_t off = 0;
@@ -338,18 +348,87 @@ __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
     }
 }
 
+// Split of one unit's sparse position list (on-demand reconstruction of
+// selected tokens), run by one 256-thread block.  The valid entries
+// (0 <= p < T) of pos[unit][0..nsel) are written, in list order, as
+// compressed-token ordinals q = p - ((p - 1) / s + 1) to ord[0][unit][..] and
+// as reference ordinals p / s to ord[1][unit][..]; the two counts go to
+// cnt[unit][0..1].  Entries outside [0, T) are skipped.  Chunks of 4096
+// entries: all of a chunk's loads are issued before any is used.
+__device__ __forceinline__ void sparse_split_block(const int32_t *__restrict__ pos, int nsel,
+                                                   int64_t T, int s, int U, int unit,
+                                                   int32_t *__restrict__ ord,
+                                                   int32_t *__restrict__ cnt) {
+    constexpr int PER = 16;  // entries per thread and chunk
+    __shared__ uint32_t wtot[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t *pu = pos + (int64_t)unit * nsel;
+    int32_t *cu = ord + (int64_t)unit * nsel;
+    int32_t *ru = ord + ((int64_t)U + unit) * nsel;
+    int nc = 0, nr = 0;  // entries written so far (block-uniform)
+    for (int base = 0; base < nsel; base += 256 * PER) {
+        int32_t v[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int i = base + tid * PER + e;
+            v[e] = i < nsel ? pu[i] : -1;
+        }
+        uint32_t mine = 0;  // compressed count | reference count << 16
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const bool ok = v[e] >= 0 && (int64_t)v[e] < T;
+            mine += ok ? (v[e] % s == 0 ? 0x10000u : 1u) : 0u;
+        }
+        // exclusive scan of the packed counts over the block
+        uint32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        uint32_t before = inc - mine, total = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            before += i < w ? wtot[i] : 0u;
+            total += wtot[i];
+        }
+        int oc = nc + (int)(before & 0xffffu), orr = nr + (int)(before >> 16);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int32_t p = v[e];
+            if (p < 0 || (int64_t)p >= T) continue;
+            if (p % s == 0) ru[orr++] = p / s;
+            else cu[oc++] = p - ((p - 1) / s + 1);
+        }
+        nc += (int)(total & 0xffffu);
+        nr += (int)(total >> 16);
+        __syncthreads();  // wtot is rewritten by the next chunk
+    }
+    if (tid == 0) {
+        cnt[2 * unit] = nc;
+        cnt[2 * unit + 1] = nr;
+    }
+}
+
 // Query-side tables of one decode step, one launch.  grid (nrb + G, H, B):
 //   blockIdx.x <  nrb  rows [256 x, 256 x + 256) of qR[j][g] = q_g . R^K_j
 //                      (bf16: matrix cores; row Rt is the zero row)
-//   blockIdx.x >= nrb  u_g = W2K^T q_g and c_g = q_g . b2K for query head
+//   nrb <= x < nrb + G u_g = W2K^T q_g and c_g = q_g . b2K for query head
 //                      g = x - nrb of the KV head
+//   x == nrb + G       (sparse calls only, pos non-null, one more block) the
+//                      split of the unit's position list (sparse_split_block)
 template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int Hq, int G, int d,
                                                    const T *__restrict__ krefs, int64_t Rcap,
                                                    int64_t Rt, int nrb, const T *__restrict__ w2,
                                                    int hid, const float *__restrict__ b2,
                                                    float *__restrict__ u, float *__restrict__ cq,
-                                                   float *__restrict__ qr) {
+                                                   float *__restrict__ qr,
+                                                   const int32_t *__restrict__ pos, int nsel,
+                                                   int64_t ntok, int s, int32_t *__restrict__ ord,
+                                                   int32_t *__restrict__ cnt) {
     __shared__ float qs[kMaxG][kMaxD];
     __shared__ float red[1][32][kMaxH];
     const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, H = gridDim.y;
@@ -363,6 +442,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
     };
     const int64_t unit = (int64_t)b * H + h;
     const int GQ = qr_heads(G);
+    if (pos && (int)blockIdx.x == nrb + G) {
+        sparse_split_block(pos, nsel, ntok, s, H * (int)gridDim.z, (int)unit, ord, cnt);
+        return;
+    }
     if (sizeof(T) != 2 || (int)blockIdx.x >= nrb) stage_q();
     if ((int)blockIdx.x < nrb) {
         if constexpr (sizeof(T) == 2) {
@@ -469,66 +552,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
             for (int c = tid; c < d; c += 64) v += qs[g][c] * b2[c];
         v = wave_sum(v);
         if (tid == 0) cq[(int64_t)b * Hq + h * G + g] = v;
-    }
-}
-
-// Split of the sparse position lists (on-demand reconstruction of selected
-// tokens).  grid U (one block per unit), 256 threads.  The valid entries
-// (0 <= p < T) of the unit's list pos[unit][0..nsel) are written, in list
-// order, as compressed-token ordinals q = p - ((p - 1) / s + 1) to
-// ord[0][unit][..] and as reference ordinals p / s to ord[1][unit][..]; the
-// two counts go to cnt[unit][0..1].  Entries outside [0, T) are skipped.
-__global__ __launch_bounds__(256) void sparse_split_kernel(const int32_t *__restrict__ pos,
-                                                           int nsel, int64_t T, int s, int U,
-                                                           int32_t *__restrict__ ord,
-                                                           int32_t *__restrict__ cnt) {
-    constexpr int PER = 4;  // entries per thread and chunk
-    __shared__ uint32_t wtot[4];
-    const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int32_t *pu = pos + (int64_t)unit * nsel;
-    int32_t *cu = ord + (int64_t)unit * nsel;
-    int32_t *ru = ord + ((int64_t)U + unit) * nsel;
-    int nc = 0, nr = 0;  // entries written so far (block-uniform)
-    for (int base = 0; base < nsel; base += 256 * PER) {
-        int32_t v[PER];
-        uint32_t mine = 0;  // compressed count | reference count << 16
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int i = base + tid * PER + e;
-            v[e] = i < nsel ? pu[i] : -1;
-            const bool ok = v[e] >= 0 && (int64_t)v[e] < T;
-            mine += ok ? (v[e] % s == 0 ? 0x10000u : 1u) : 0u;
-        }
-        // exclusive scan of the packed counts over the block
-        uint32_t inc = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        if (lane == 63) wtot[w] = inc;
-        __syncthreads();
-        uint32_t before = inc - mine, total = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            before += i < w ? wtot[i] : 0u;
-            total += wtot[i];
-        }
-        int oc = nc + (int)(before & 0xffffu), orr = nr + (int)(before >> 16);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int32_t p = v[e];
-            if (p < 0 || (int64_t)p >= T) continue;
-            if (p % s == 0) ru[orr++] = p / s;
-            else cu[oc++] = p - ((p - 1) / s + 1);
-        }
-        nc += (int)(total & 0xffffu);
-        nr += (int)(total >> 16);
-        __syncthreads();  // wtot is rewritten by the next chunk
-    }
-    if (tid == 0) {
-        cnt[2 * unit] = nc;
-        cnt[2 * unit + 1] = nr;
     }
 }
 
@@ -707,7 +730,8 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const int32_t *rord_u = SP ? sord + ((int64_t)U + unit) * nsel : nullptr;
     const int64_t Nt_u = SP ? (int64_t)scnt[2 * unit] : Nt;
     const int64_t Rt_u = SP ? (int64_t)scnt[2 * unit + 1] : Rt;
-    auto ord_c = [&](int i) -> uint32_t { return SP ? (uint32_t)cord_u[i] : (uint32_t)i; };
+    // a sparse partition's compressed-token ordinals, staged in LDS once
+    __shared__ int32_t ordl[SP ? kSpTiles * TT : 1];
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
     const int64_t qe_ = min(Nt_u, qa_ + (int64_t)tiles_per_part * TT);
     // per-unit bases; all in-loop offsets are 32-bit
@@ -870,7 +894,10 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
         bias_k[i] = kb1 ? kb1[i] : 0.f;
         bias_v[i] = vb1 ? vb1[i] : 0.f;
     }
+    if constexpr (SP)
+        for (int i = tid; i < qe32 - qa32; i += 256) ordl[i] = cord_u[qa32 + i];
     __syncthreads();
+    auto ord_c = [&](int i) -> uint32_t { return SP ? (uint32_t)ordl[i - qa32] : (uint32_t)i; };
     // U = W2K^T q in f16, hidden permuted to match the hK^T operand layout
     f16x8 uA[KJ];
     {
@@ -1902,17 +1929,19 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
     SparseArgs sa{nullptr, nullptr, 0};
+    int32_t *ord = nullptr, *cnt = nullptr;
     if (pos) {
-        int32_t *ord = (int32_t *)(w + pl.off_ord);
-        int32_t *cnt = (int32_t *)(w + pl.off_cnt);
-        hipLaunchKernelGGL(sparse_split_kernel, dim3((unsigned)(dm.B * dm.H)), dim3(256), 0, st,
-                           pos, nsel, T_, dm.s, dm.B * dm.H, ord, cnt);
+        ord = (int32_t *)(w + pl.off_ord);
+        cnt = (int32_t *)(w + pl.off_cnt);
         sa = SparseArgs{ord, cnt, nsel};
     }
+    // the query-side tables, and for a sparse call the list split (one more
+    // block per unit)
     const int nrb = (int)((qr_rows(pl.Rt) + 255) / 256);
-    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)(nrb + G), dm.H, dm.B), dim3(256), 0, st,
-                       (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R, pl.Rt, nrb,
-                       (const T *)kd.w2, kd.hidden, kd.b2, u, cq, qr);
+    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)(nrb + G + (pos ? 1 : 0)), dm.H, dm.B),
+                       dim3(256), 0, st, (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R,
+                       pl.Rt, nrb, (const T *)kd.w2, kd.hidden, kd.b2, u, cq, qr, pos, nsel, T_,
+                       dm.s, ord, cnt);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
         if (!pos && mfma_eligible(dm, kd, vd)) {

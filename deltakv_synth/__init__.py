@@ -24,7 +24,7 @@ import numpy as np
 import torch
 
 # purposes, used as the last element of a seed key
-P_DIRS, P_CENTROIDS, P_COEFFS, P_ASSIGN, P_NOISE, P_WEIGHTS, P_QUERIES, P_BIAS = range(8)
+P_DIRS, P_CENTROIDS, P_COEFFS, P_ASSIGN, P_NOISE, P_WEIGHTS, P_QUERIES, P_BIAS, P_SELECT = range(9)
 
 
 def seed_of(*key: int) -> int:
@@ -96,6 +96,20 @@ def queries(n: int, d: int, key: Tuple[int, ...], dtype=torch.float32,
     """n query rows ~ N(0, I), shape [n, d]."""
     g = _gen(device, *key, P_QUERIES)
     return torch.randn(n, d, generator=g, device=device).to(dtype)
+
+
+def selections(n_lists: int, T: int, n_sel: int, key: Tuple[int, ...],
+               device="cpu") -> torch.Tensor:
+    """n_lists position lists, each n_sel distinct positions drawn uniformly
+    from [0, T) and sorted ascending: int32 [n_lists, n_sel].  A stand-in for
+    a sparse-attention selector's output (which positions a query-aware
+    selector keeps depends on a trained model; only the list sizes matter to
+    the cost of rebuilding them)."""
+    g = _gen(device, *key, P_SELECT)
+    out = torch.empty(n_lists, n_sel, dtype=torch.int32, device=device)
+    for i in range(n_lists):
+        out[i] = torch.randperm(T, generator=g, device=device)[:n_sel].sort().values
+    return out
 
 
 @dataclass(frozen=True)
