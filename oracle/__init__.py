@@ -25,6 +25,10 @@ Parity status per function (what pins it; the tests under tests/ hold them):
   decode_head_sparse pinned: the full position list gives the dense decode;
                     with the identity pair it is dense attention over x at the
                     listed positions; order, padding and duplicate invariants.
+  group_attention_mass pinned: torch softmax weights summed over the group,
+                    total mass = number of query rows.
+  top_positions     pinned: a pure-Python sort on (-score, position) tuples,
+                    crafted ties, n_keep >= T.
   Latent and decode values under random GELU weights have no printed value to
   compare with; they are pinned only through the pieces above.
 """
@@ -82,6 +86,9 @@ def _load():
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp, _dp,
                                           ctypes.c_int32, _dp]
+    lib.oracle_group_attention_mass.restype = None
+    lib.oracle_group_attention_mass.argtypes = [_dp, ctypes.c_int32, _dp, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.c_double, _dp]
     lib.oracle_attention.restype = None
     lib.oracle_attention.argtypes = [_dp, ctypes.c_int32, _dp, _dp, ctypes.c_int64,
                                      ctypes.c_int32, ctypes.c_double, _dp]
@@ -235,6 +242,29 @@ def attention(q, keys, vals, scale: float) -> np.ndarray:
     return out
 
 
+def group_attention_mass(q, keys, scale: float) -> np.ndarray:
+    """sum over the query rows of each one's softmax attention weights [T]."""
+    q = _f64(q)
+    keys = _f64(keys)
+    n_q, d = q.shape
+    mass = np.zeros(keys.shape[0], dtype=np.float64)
+    _load().oracle_group_attention_mass(_ptr(q), n_q, _ptr(keys), keys.shape[0], d,
+                                        float(scale), _ptr(mass))
+    return mass
+
+
+def top_positions(scores, n_keep: int) -> np.ndarray:
+    """The selection rule: the n_keep positions of largest score, equal scores
+    ordered by the lower position, returned in increasing position order;
+    with n_keep >= len(scores), every position and then -1 (int32)."""
+    scores = np.asarray(scores)
+    T = len(scores)
+    if n_keep >= T:
+        return np.concatenate([np.arange(T), np.full(n_keep - T, -1)]).astype(np.int32)
+    order = np.lexsort((np.arange(T), -scores))   # primary: score descending
+    return np.sort(order[:n_keep]).astype(np.int32)
+
+
 # ---- per-head helpers (composition of the steps above, no new arithmetic) ----
 
 def compress_head(x, s: int, k: int, m: MLP, positions=None):
@@ -274,3 +304,13 @@ def decode_head_sparse(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat,
     khat = reconstruct_at(k_refs, k_lat, k_idx, pos, s, k_dec)
     vhat = reconstruct_at(v_refs, v_lat, v_idx, pos, s, v_dec)
     return attention(q_heads, khat, vhat, scale)
+
+
+def select_head(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, T: int, s: int, scale: float,
+                n_keep: int):
+    """Query-aware selection for one KV head: the attention mass of every
+    position (rebuilt keys, summed over the query rows q_heads [G, d]) and the
+    positions the selection rule keeps.  Returns (positions, mass)."""
+    khat = reconstruct(k_refs, k_lat, k_idx, T, s, k_dec)
+    mass = group_attention_mass(q_heads, khat, scale)
+    return top_positions(mass, n_keep), mass

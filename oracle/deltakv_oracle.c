@@ -278,3 +278,31 @@ void oracle_attention(const double *q, int32_t n_q, const double *keys,
     }
     free(a);
 }
+
+/* Attention mass per key row, summed over a group of query rows (the score a
+ * query-aware token selector ranks by; section 4 of the DeltaKV page pairs
+ * on-demand reconstruction with such a selector):
+ *   mass_t = sum_g softmax_t(scale * q_g . k_t),   t = 0..T-1,
+ * each softmax with its row maximum subtracted.  mass receives T values. */
+void oracle_group_attention_mass(const double *q, int32_t n_q, const double *keys,
+                                 int64_t T, int32_t d, double scale, double *mass) {
+    double *a = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int64_t t = 0; t < T; ++t) mass[t] = 0.0;
+    for (int32_t g = 0; g < n_q; ++g) {
+        const double *qg = q + (int64_t)g * d;
+        double m = -INFINITY;
+        for (int64_t t = 0; t < T; ++t) {
+            double dot = 0.0;
+            for (int32_t i = 0; i < d; ++i) dot += qg[i] * keys[t * d + i];
+            a[t] = scale * dot;
+            if (a[t] > m) m = a[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            a[t] = exp(a[t] - m);
+            l += a[t];
+        }
+        for (int64_t t = 0; t < T; ++t) mass[t] += a[t] / l;
+    }
+    free(a);
+}

@@ -458,3 +458,65 @@ def test_sparse_decode_with_nothing_selected_is_zero():
     rng, q, args = _sparse_setup(42)
     T = args[8]
     assert np.array_equal(oracle.decode_head_sparse(q, *args, [-1, T]), np.zeros_like(q))
+
+
+# ------------------------------------------------ query-aware token selection
+
+def test_group_attention_mass_matches_torch_softmax_and_sums_to_group_size():
+    rng = _rng(50)
+    G, T, d = 4, 300, 16
+    q = rng.standard_normal((G, d))
+    kk = rng.standard_normal((T, d)) * 2
+    got = oracle.group_attention_mass(q, kk, 0.25)
+    want = torch.softmax(torch.from_numpy(q) @ torch.from_numpy(kk).T * 0.25, dim=1).sum(0)
+    assert np.max(np.abs(got - want.numpy())) <= 1e-13
+    assert abs(got.sum() - G) <= 1e-12
+
+
+def _rule_by_tuples(scores, n_keep):
+    # the rule written out with Python's tuple order
+    ranked = sorted(range(len(scores)), key=lambda t: (-float(scores[t]), t))
+    if n_keep >= len(scores):
+        return list(range(len(scores))) + [-1] * (n_keep - len(scores))
+    return sorted(ranked[:n_keep])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_top_positions_matches_tuple_sort_with_ties(seed):
+    rng = _rng(60 + seed)
+    T = int(rng.integers(1, 80))
+    # few distinct values: many exact ties, including at the cut
+    scores = rng.integers(0, 5, T).astype(np.float32) / 4
+    for n_keep in (1, max(1, T // 3), T - 1 if T > 1 else 1, T, T + 5):
+        assert list(oracle.top_positions(scores, n_keep)) == _rule_by_tuples(scores, n_keep)
+
+
+def test_select_head_with_identity_pair_ranks_the_input_rows():
+    # with the orthogonal identity pair the rebuilt keys are the input rows,
+    # so the selection is the rule applied to softmax weights over x
+    from deltakv_synth import kv_rows
+    T, d, s, k = 200, 32, 8, 4
+    kx = kv_rows(T, d, 4, 16, key=(51, 0)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 52)
+    kr, ki, kl = oracle.compress_head(kx, s, k, comp)
+    q = _rng(53).standard_normal((4, d))
+    scale = 1 / np.sqrt(d)
+    pos, mass = oracle.select_head(q, kr, kl, ki, dec, T, s, scale, 37)
+    want_mass = torch.softmax(torch.from_numpy(q) @ torch.from_numpy(kx).T * scale, 1).sum(0)
+    assert np.max(np.abs(mass - want_mass.numpy())) <= 1e-10
+    assert list(pos) == _rule_by_tuples(want_mass.numpy(), 37)
+
+
+def test_select_head_equal_keys_prefer_the_lower_position():
+    # two tokens with the same rebuilt key get the same mass; the cut between
+    # them keeps the lower position
+    rng = _rng(54)
+    T, d = 40, 8
+    kk = rng.standard_normal((T, d))
+    q = rng.standard_normal((2, d))
+    mass0 = oracle.group_attention_mass(q, kk, 1.0)
+    top = int(np.argmax(mass0))
+    kk[T - 1] = kk[top]          # a later copy of the best key
+    mass = oracle.group_attention_mass(q, kk, 1.0)
+    assert mass[T - 1] == mass[top]
+    assert list(oracle.top_positions(mass, 1)) == [min(top, T - 1)]
