@@ -452,13 +452,30 @@ def main():
                 sends[i].record(stream)
             torch.cuda.synchronize()
         sp_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
+        # the selector: a dense call that also ranks the positions and writes
+        # the n_sel kept per KV head (the lists above could come from it)
+        selws = S.dk.workspace(S.dk.decode_select_workspace_bytes(S.shape, S.Hq, wl.T))
+        kept = torch.empty_like(pos)
+        for rep_ in range(2):
+            for i in range(n_launch):
+                l = i % wl.layers
+                c, d = S.cache[l], S.dec[l]
+                sstarts[i].record(stream)
+                S.dk.decode_attn_select(S.shape, S.Hq, wl.T, qs[l], c[0], d[0], c[1], d[1],
+                                        S.scale, S.out, kept, None, selws)
+                sends[i].record(stream)
+            torch.cuda.synchronize()
+        sel_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
+        del selws
         sp_bytes = float(np.mean([sparse_bytes_per_layer(S, i % wl.layers, pos)
                                   for i in range(min(n_launch, wl.layers))]))
         sparse = {"positions_per_kv_head": n_sel, "selected_fraction": n_sel / wl.T,
                   "launch_ms": sp_ms, "speedup_vs_dense_launch": launch_ms / sp_ms,
                   "algorithmic_bytes_per_launch": sp_bytes,
-                  "eff_hbm_gbs": sp_bytes / (sp_ms * 1e-3) / 1e9}
-        log(f"[bench] sparse decode ({n_sel} positions per KV head): {sp_ms:.4f} ms per layer")
+                  "eff_hbm_gbs": sp_bytes / (sp_ms * 1e-3) / 1e9,
+                  "select_launch_ms": sel_ms}
+        log(f"[bench] sparse decode ({n_sel} positions per KV head): {sp_ms:.4f} ms per layer; "
+            f"dense decode with selection {sel_ms:.4f} ms")
         del sws
 
     # one decode step (every layer) captured in a HIP graph and replayed, with

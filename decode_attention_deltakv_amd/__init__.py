@@ -18,6 +18,9 @@ available as an alias):
     decode_sparse_workspace_bytes(shape, Hq, T, n_sel) -> int
     decode_attn_sparse(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, positions, scale,
                        out, workspace)
+    decode_select_workspace_bytes(shape, Hq, T) -> int
+    decode_attn_select(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out,
+                       positions, scores, workspace)
 
 `Cache` and `Mlp` below only hold torch tensors and build the C structs.
 """
@@ -98,10 +101,18 @@ def lib():
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp), _P,
                                              ctypes.c_int32, ctypes.c_float, _P, _P, _SZ, _P]
+    L.deltakv_decode_select_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
+                                                        ctypes.POINTER(_SZ)]
+    L.deltakv_decode_attn_select.argtypes = [sp, ctypes.c_int32, ctypes.c_int64, _P,
+                                             ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                             ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                             ctypes.c_float, _P, ctypes.c_int32, _P, _P, _P, _SZ,
+                                             _P]
     for name in ("deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
                  "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
-                 "deltakv_decode_attn_sparse"):
+                 "deltakv_decode_attn_sparse", "deltakv_decode_select_workspace_bytes",
+                 "deltakv_decode_attn_select"):
         getattr(L, name).restype = ctypes.c_int
     L.deltakv_status_string.argtypes = [ctypes.c_int]
     L.deltakv_status_string.restype = ctypes.c_char_p
@@ -282,6 +293,32 @@ def decode_attn_sparse(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.T
                                             _stream()))
 
 
+def decode_select_workspace_bytes(shape: Shape, num_q_heads: int, n_tokens: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_decode_select_workspace_bytes(ctypes.byref(cs), num_q_heads, n_tokens,
+                                                       ctypes.byref(v)))
+    return v.value
+
+
+def decode_attn_select(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor,
+                       k_cache: Cache, k_dec: Mlp, v_cache: Cache, v_dec: Mlp, scale: float,
+                       out: torch.Tensor, positions: torch.Tensor,
+                       scores: Optional[torch.Tensor], workspace: Optional[torch.Tensor]):
+    """positions: int32 [B, H, n_keep] on the device, written (n_keep = its
+    last size); scores: None or fp32 [B, H, n_tokens], written."""
+    cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if positions is not None and positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    n_keep = int(positions.shape[-1]) if positions is not None else 0
+    _check(lib().deltakv_decode_attn_select(ctypes.byref(cs), num_q_heads, n_tokens, _ptr(q),
+                                            ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
+                                            ctypes.byref(vm), float(scale), _ptr(out), n_keep,
+                                            _ptr(positions), _ptr(scores), _ptr(workspace), wsb,
+                                            _stream()))
+
+
 def status_string(status: int) -> str:
     return lib().deltakv_status_string(status).decode()
 
@@ -307,6 +344,8 @@ deltakv_compress = compress
 deltakv_decode_attn = decode_attn
 deltakv_decode_sparse_workspace_bytes = decode_sparse_workspace_bytes
 deltakv_decode_attn_sparse = decode_attn_sparse
+deltakv_decode_select_workspace_bytes = decode_select_workspace_bytes
+deltakv_decode_attn_select = decode_attn_select
 deltakv_status_string = status_string
 deltakv_last_error = last_error
 deltakv_version = version

@@ -206,6 +206,18 @@ deltakv_status deltakv_decode_sparse_workspace_bytes(const deltakv_shape *shape,
     return ok();
 }
 
+deltakv_status deltakv_decode_select_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     size_t *bytes) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::decode_select_ws_bytes(dm, num_q_heads, n_tokens);
+    return ok();
+}
+
 deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
                                   int64_t t1, const deltakv_cache *cache, void *stream) {
     dk::Dims dm;
@@ -324,6 +336,46 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
                                              positions, n_sel, softmax_scale, out, workspace,
                                              workspace_bytes, (hipStream_t)stream),
                     "deltakv_decode_attn_sparse");
+}
+
+deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          float softmax_scale, float *out, int32_t n_keep,
+                                          int32_t *positions, float *scores, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (n_keep < 1 || n_keep > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_keep %d not in [1, %d]", n_keep,
+                    DELTAKV_MAX_SPARSE_SELECT);
+    if (!positions) return fail(DELTAKV_ERR_INVALID_ARG, "positions is NULL");
+    if (!aligned16(positions) || (scores && !aligned16(scores)))
+        return fail(DELTAKV_ERR_INVALID_ARG, "positions / scores must be 16-byte aligned");
+    if (!q || !out) return fail(DELTAKV_ERR_INVALID_ARG, "q / out is NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(DELTAKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
+    if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    const size_t need = dk::decode_select_ws_bytes(dm, num_q_heads, n_tokens);
+    if (workspace_bytes < need || !workspace)
+        return fail(DELTAKV_ERR_WORKSPACE, "decode with selection needs %zu workspace bytes, "
+                    "got %zu", need, workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return from_hip(dk::launch_decode_select(dm, num_q_heads, n_tokens, q, kc, km, vc, vm,
+                                             softmax_scale, out, n_keep, positions, scores,
+                                             workspace, workspace_bytes, (hipStream_t)stream),
+                    "deltakv_decode_attn_select");
 }
 
 const char *deltakv_status_string(deltakv_status status) {

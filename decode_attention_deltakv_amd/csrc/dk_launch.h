@@ -48,6 +48,14 @@ size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T);
 hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const CacheArgs &kc,
                          const MlpArgs &kdec, const CacheArgs &vc, const MlpArgs &vdec,
                          float scale, float *out, void *ws, size_t ws_bytes, hipStream_t st);
+// dense decode attention that also selects, per (sequence, KV head), the
+// n_keep positions of largest attention probability summed over the group
+size_t decode_select_ws_bytes(const Dims &dm, int Hq, int64_t T);
+hipError_t launch_decode_select(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, float scale, float *out, int n_keep,
+                                int32_t *positions, float *scores, void *ws, size_t ws_bytes,
+                                hipStream_t st);
 // sparse decode attention over listed positions pos[B][H][nsel]
 size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel);
 hipError_t launch_decode_sparse(const Dims &dm, int Hq, int64_t T, const void *q,

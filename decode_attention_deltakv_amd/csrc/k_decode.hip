@@ -53,6 +53,8 @@ constexpr int kSpTiles = 16;   // most 32-token tiles per partition of a sparse 
 // read instead of a masked load.
 __host__ __device__ inline int qr_heads(int G) { return (G + 3) & ~3; }
 __host__ __device__ inline int64_t qr_rows(int64_t Rt) { return Rt + 1; }
+// selection keys of a unit: T entries, rows padded to a multiple of 4
+__host__ __device__ inline int64_t keys_stride(int64_t T) { return (T + 3) & ~(int64_t)3; }
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(256) void main_kernel(
     int khid, int kact, const T *__restrict__ vw1, const float *__restrict__ vb1, int vhid,
     int vact, float scale, const float *__restrict__ u, const float *__restrict__ cq,
     const float *__restrict__ qr, float *__restrict__ part, const int32_t *__restrict__ sord,
-    const int32_t *__restrict__ scnt, int nsel) {
+    const int32_t *__restrict__ scnt, int nsel, float *__restrict__ logc,
+    float *__restrict__ logr) {
     (void)kref;
     (void)s;
     __shared__ float us[kMaxG][kMaxH];
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(256) void main_kernel(
                 float hsum = 0.f;
                 for (int o = 0; o < khid; ++o) hsum += us[g][o] * hs[t][o];
                 sc[g][t] = scale * (rs / (float)keff + hsum + cqs[g]);
+                if (!sp && logc) logc[(unit * G + g) * Nt + q0 + t] = sc[g][t];
             }
             __syncthreads();
             // ---- online softmax update
@@ -270,6 +274,7 @@ __global__ __launch_bounds__(256) void main_kernel(
                 const int g = i / nj, t = i % nj;
                 const int64_t j = sp ? rord_u[j0 + t] : j0 + t;
                 sc[g][t] = scale * qr[(unit * qr_rows(Rt) + j) * qr_heads(G) + g];
+                if (!sp && logr) logr[(unit * G + g) * Rt + j] = sc[g][t];
             }
             __syncthreads();
             if (tid < G) {
@@ -555,6 +560,211 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
     }
 }
 
+// Query-aware token selection from the logits a dense decode wrote (the
+// selector a sparse attention uses at a filter layer: tokens are ranked by
+// the attention they received).  Two launches.
+//
+// select_keys_kernel, grid (ceil(T / 2048), U), 256 threads: for every
+// position p < T of unit u,
+//   key_p = sum over the unit's G query heads g of exp(logit_{g,p} - lse_g)
+// (the attention probability of p summed over the group) into keys[u][p]
+// and, if non-null, scores[u][p]; the counts of the keys' first (most
+// significant) byte are added to hist0[u][256], which the merge kernel
+// cleared.
+constexpr int kKeyPer = 8;  // positions per thread of the key kernel
+__global__ __launch_bounds__(256) void select_keys_kernel(
+    const float *__restrict__ logc, const float *__restrict__ logr,
+    const float *__restrict__ lse, int Hq, int G, int H, int64_t T, int64_t Nt, int64_t Rt,
+    int s, uint32_t *__restrict__ keys, float *__restrict__ scores,
+    uint32_t *__restrict__ hist0) {
+    __shared__ uint32_t lh[256];
+    const int unit = blockIdx.y, b = unit / H, h = unit % H;
+    lh[threadIdx.x] = 0u;
+    float lg[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) lg[g] = g < G ? lse[(int64_t)b * Hq + h * G + g] : 0.f;
+    const float *lc = logc + (int64_t)unit * G * Nt;
+    const float *lr = logr + (int64_t)unit * G * Rt;
+    const int64_t p0 = (int64_t)blockIdx.x * (256 * kKeyPer) + threadIdx.x;
+    float v[kKeyPer][kMaxG];
+#pragma unroll
+    for (int e = 0; e < kKeyPer; ++e) {
+        const int64_t p = min(p0 + 256 * e, T - 1);
+        const bool ref = p % s == 0;
+        const float *src = ref ? lr + p / s : lc + (p - ((p - 1) / s + 1));
+        const int64_t gs = ref ? Rt : Nt;
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) v[e][g] = g < G ? src[g * gs] : 0.f;
+    }
+    __syncthreads();  // lh cleared
+#pragma unroll
+    for (int e = 0; e < kKeyPer; ++e) {
+        const int64_t p = p0 + 256 * e;
+        if (p >= T) break;
+        float sg = 0.f;
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g)
+            if (g < G) sg += __expf(v[e][g] - lg[g]);
+        keys[unit * keys_stride(T) + p] = __float_as_uint(sg);
+        if (scores) scores[(int64_t)unit * T + p] = sg;
+        atomicAdd(&lh[__float_as_uint(sg) >> 24], 1u);
+    }
+    __syncthreads();
+    // the block's counts of the keys' first byte into the unit's histogram
+    if (lh[threadIdx.x]) atomicAdd(&hist0[unit * 256 + threadIdx.x], lh[threadIdx.x]);
+}
+
+// select_topn_kernel, grid U, kSelThreads threads: positions[u][0..n_keep)
+// = the n_keep positions of largest key, equal keys ordered by the lower
+// position, written in increasing position order (n_keep >= T: every
+// position, then -1).  The n_keep-th largest key is found by a 4 x 8-bit
+// radix select on the keys' bit patterns (non-negative floats order as their
+// bits): the first byte's histogram comes from the key kernel, the other
+// three count only the keys that share the bytes fixed so far.  One ordered
+// pass then takes every key above the threshold and the first equal ones.
+// Keys are read with 16-byte loads, all of a batch's loads first; a unit's
+// keys start at a multiple of 4 entries (keys_stride).
+constexpr int kSelThreads = 1024;
+__global__ __launch_bounds__(kSelThreads) void select_topn_kernel(
+    const uint32_t *__restrict__ keys, const uint32_t *__restrict__ hist0, int64_t T,
+    int n_keep, int32_t *__restrict__ positions) {
+    constexpr int NT = kSelThreads, NW = NT / 64;
+    constexpr int HB = 8;   // 16-byte loads per thread per histogram batch (coalesced)
+    constexpr int OB = 4;   // 16-byte loads per thread per ordered batch (contiguous)
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wtot[NW];
+    __shared__ uint32_t sel[2];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int unit = blockIdx.x;
+    const int64_t T4 = keys_stride(T) / 4;
+    const u32x4 *ku4 = reinterpret_cast<const u32x4 *>(keys + (int64_t)unit * keys_stride(T));
+    int32_t *pu = positions + (int64_t)unit * n_keep;
+    if (n_keep >= T) {
+        for (int64_t i = tid; i < n_keep; i += NT) pu[i] = i < T ? (int32_t)i : -1;
+        return;
+    }
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // radix select of the n_keep-th largest key: prefix / mask of the bits
+    // fixed so far, rem = its rank (from the top, 1-based) among the keys
+    // that share them
+    uint32_t prefix = 0u, mask = 0u, rem = (uint32_t)n_keep;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (shift == 24) {
+            // the first byte's counts come from the key kernel
+            for (int i = tid; i < 256; i += NT) hist[i] = hist0[(int64_t)unit * 256 + i];
+        } else {
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+            for (int64_t b4 = 0; b4 < T4; b4 += (int64_t)NT * HB) {
+                u32x4 kv[HB];
+#pragma unroll
+                for (int e = 0; e < HB; ++e) {
+                    const int64_t i4 = b4 + (int64_t)e * NT + tid;
+                    kv[e] = i4 < T4 ? ku4[i4] : zero4;
+                }
+#pragma unroll
+                for (int e = 0; e < HB; ++e)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int64_t p = (b4 + (int64_t)e * NT + tid) * 4 + j;
+                        if (p < T && (kv[e][j] & mask) == prefix)
+                            atomicAdd(&hist[(kv[e][j] >> shift) & 255u], 1u);
+                    }
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // lane l holds bins 255 - 4 l .. 252 - 4 l (from the top)
+            uint32_t c[4], tot = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] = hist[255 - 4 * lane - i];
+                tot += c[i];
+            }
+            uint32_t inc = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            const uint32_t excl = inc - tot;
+            if (excl < rem && rem <= inc) {
+                uint32_t r = rem - excl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (r <= c[i]) {
+                        sel[0] = (uint32_t)(255 - 4 * lane - i);
+                        sel[1] = r;
+                        break;
+                    }
+                    r -= c[i];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        mask |= 255u << shift;
+        rem = sel[1];
+        __syncthreads();  // sel and hist are rewritten by the next pass
+    }
+    // ordered pass (each thread 16 consecutive positions): keys above the
+    // threshold, and the first rem equal ones; the out index of a taken
+    // position = keys above it taken before it + min(equal keys before it, rem)
+    const uint32_t thr = prefix;
+    uint32_t gt_run = 0u, eq_run = 0u;
+    for (int64_t b4 = 0; b4 < T4; b4 += (int64_t)NT * OB) {
+        u32x4 kv[OB];
+#pragma unroll
+        for (int e = 0; e < OB; ++e) {
+            const int64_t i4 = b4 + (int64_t)tid * OB + e;
+            kv[e] = i4 < T4 ? ku4[i4] : zero4;
+        }
+        const int64_t p0 = (b4 + (int64_t)tid * OB) * 4;
+        uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+        for (int e = 0; e < OB; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool inr = p0 + 4 * e + j < T;
+                cg += (inr && kv[e][j] > thr) ? 1u : 0u;
+                ce += (inr && kv[e][j] == thr) ? 1u : 0u;
+            }
+        const uint32_t mine = cg | (ce << 16);
+        uint32_t inc = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        uint32_t before = inc - mine, total = 0u;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            before += i < w ? wtot[i] : 0u;
+            total += wtot[i];
+        }
+        uint32_t g0 = gt_run + (before & 0xffffu), e0 = eq_run + (before >> 16);
+#pragma unroll
+        for (int e = 0; e < OB; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t p = p0 + 4 * e + j;
+                const uint32_t k = kv[e][j];
+                if (p < T && k > thr) {
+                    pu[g0 + min(e0, rem)] = (int32_t)p;
+                    ++g0;
+                } else if (p < T && k == thr) {
+                    if (e0 < rem) pu[g0 + e0] = (int32_t)p;
+                    ++e0;
+                }
+            }
+        gt_run += total & 0xffffu;
+        eq_run += total >> 16;
+        __syncthreads();  // wtot is rewritten by the next chunk
+    }
+}
+
 // Log-sum-exp merge of the partitions of one query head, then W2V applied to
 // the merged hidden sum.  grid (Hq, B).  The merge of the record vectors runs
 // with one float4 column per thread and the partitions split across thread
@@ -564,7 +774,9 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
                                                        const float *__restrict__ part,
                                                        const T *__restrict__ vw2, int vhid,
                                                        const float *__restrict__ vb2,
-                                                       float *__restrict__ out) {
+                                                       float *__restrict__ out,
+                                                       float *__restrict__ lse,
+                                                       uint32_t *__restrict__ hist0) {
     constexpr int NT = kCombThreads, NW = NT / 64, NGR = 8;
     __shared__ float wgt[kMaxParts];
     __shared__ f32x4 gred[NGR][(kMaxD + kMaxH) / 4];
@@ -576,6 +788,10 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
     const int h = gq / G, g = gq % G;
     const int64_t unit = (int64_t)b * H + h;
     const float *base = part + (unit * P * G + g) * kPStride;
+    // token selection: the first query head of the group clears the unit's
+    // key histogram that the key kernel fills next
+    if (hist0 && g == 0)
+        for (int i = tid; i < 256; i += NT) hist0[unit * 256 + i] = 0u;
     const int64_t pstep = (int64_t)G * kPStride;
     float mx = -INFINITY;
     for (int64_t p = tid; p < P; p += NT) mx = fmaxf(mx, base[p * pstep]);
@@ -592,6 +808,7 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
     }
     const float L = block_reduce<NW>(lsum, red, false);
     const float Lt = block_reduce<NW>(ltsum, red, false);  // (its barriers also publish wgt)
+    if (lse && tid == 0) lse[(int64_t)b * Hq + gq] = L > 0.f ? M + __logf(L) : -INFINITY;
     // columns: acc_r as d/4 float4s, then acc_h as vhid/4 float4s
     const int ncr = d / 4, nc = ncr + vhid / 4;
     const int ngrp = min(NGR, NT / nc);
@@ -675,7 +892,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
     float *__restrict__ part, const int32_t *__restrict__ sord, const int32_t *__restrict__ scnt,
-    int nsel) {
+    int nsel, float *__restrict__ logc, float *__restrict__ logr) {
     constexpr int TT = 32;              // tokens per tile
     constexpr int HW = HID / 4;         // hidden units per wave
     constexpr int MT = HW / 16;         // 16-row hidden tiles per wave
@@ -799,6 +1016,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 const bool ok = j0 + st < je;
                 const int64_t jr = SP ? (int64_t)rord_u[min(j0 + st, je - 1)] : j0 + st;
                 const float s = ok ? scale * qr_u[jr * GQ + sg] : -INFINITY;
+                if (!SP && logr && ok) logr[((int64_t)unit * G + sg) * Rt + j0 + st] = s;
                 float tmax = s;
 #pragma unroll
                 for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
@@ -1024,6 +1242,7 @@ __global__ __launch_bounds__(256, 2) void main_mfma_kernel(
                 for (int i = 0; i < KP; ++i) rs += qv[i];
                 s = scale * (sp[0][sg][st] + sp[1][sg][st] + sp[2][sg][st] + sp[3][sg][st] +
                              rs / (float)kek + cq_g);
+                if (!SP && logc) logc[((int64_t)unit * G + sg) * Nt + q0 + st] = s;
             }
             float tmax = s;
 #pragma unroll
@@ -1195,7 +1414,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const bf16_t *__restrict__ kw1, const float *__restrict__ kb1,
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
-    float *__restrict__ part) {
+    float *__restrict__ part, float *__restrict__ logc, float *__restrict__ logr) {
     constexpr int TT = 32;             // tokens per tile
     constexpr int TH = 16;             // tokens per score wave
     constexpr int MB = HID / 16;       // 16-row hidden blocks (score waves)
@@ -1275,6 +1494,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             if (sg_ok) {
                 const bool ok = j0 + st < je;
                 const float s = ok ? scale * qr_u[(j0 + st) * GQ + sg] : -INFINITY;
+                if (logr && ok) logr[((int64_t)unit * G + sg) * Rt + j0 + st] = s;
                 float tmax = s;
 #pragma unroll
                 for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
@@ -1463,6 +1683,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 if constexpr (KX == 8) rs += (qv[e][4] + qv[e][5]) + (qv[e][6] + qv[e][7]);
                 const float v = scale * (sv[e] + rs * inv_k + cqv[e]);
                 s[e] = (tok_ok && gh[e] < G) ? v : -INFINITY;
+                if (logc && tok_ok && gh[e] < G)
+                    logc[((int64_t)unit * G + gh[e]) * Nt + (t0 + TH * src + l16)] = v;
                 // reference maximum: the larger of the two waves' previous ones
                 mref[e] = fmaxf(msl[sl ^ 1][0][gh[e]], msl[sl ^ 1][1][gh[e]]);
                 up = up || s[e] > mref[e] + kSlack;
@@ -1831,11 +2053,15 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     }
 }
 
-// Sparse lists of a call (SparseArgs::ord == nullptr: a dense call).
+// Per-call extras: the sparse lists (ord == nullptr: a dense call) and the
+// optional logit outputs of a dense call (logc [U][G][Nt] by token ordinal,
+// logr [U][G][Rt] by reference ordinal; nullptr: not written).
 struct SparseArgs {
     const int32_t *ord;
     const int32_t *cnt;
     int nsel;
+    float *logc;
+    float *logr;
 };
 
 template <int D, int DC, int HID, int KP>
@@ -1851,13 +2077,14 @@ void launch_mfma_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &k
                        (int)pl.Ptok, (int)pl.P, (const bf16_t *)kc.lat, kc.idx,
                        (const bf16_t *)vc.refs, (const bf16_t *)vc.lat, vc.idx,
                        (const bf16_t *)kd.w1, kd.b1, (const bf16_t *)vd.w1, vd.b1, scale, u, cq,
-                       qr, part, sa.ord, sa.cnt, sa.nsel);
+                       qr, part, sa.ord, sa.cnt, sa.nsel, sa.logc, sa.logr);
 }
 
 template <int D, int DC, int HID>
 void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
-                 const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+                 const float *u, const float *cq, const float *qr, float *part,
+                 const SparseArgs &sa, hipStream_t st) {
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
     auto kern = dm.k == 4 ? (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 4> : main_ws_kernel<D, DC, HID, 2, 4>)
@@ -1866,22 +2093,23 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
                        (const bf16_t *)vc.lat, vc.idx, (const bf16_t *)kd.w1, kd.b1,
-                       (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part);
+                       (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part, sa.logc, sa.logr);
 }
 
 // The wave-specialised kernel covers k = 4 or 8 and d_c <= 32.
 template <int D>
 bool launch_ws_d(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const MlpArgs &kd, const CacheArgs &vc, const MlpArgs &vd, float scale,
-                 const float *u, const float *cq, const float *qr, float *part, hipStream_t st) {
+                 const float *u, const float *cq, const float *qr, float *part,
+                 const SparseArgs &sa, hipStream_t st) {
     if ((dm.k != 4 && dm.k != 8) || dm.dc > 32) return false;
     const bool h256 = kd.hidden == 256;
     if (dm.dc <= 16) {
-        if (h256) launch_ws_t<D, 16, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-        else launch_ws_t<D, 16, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        if (h256) launch_ws_t<D, 16, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+        else launch_ws_t<D, 16, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
     } else {
-        if (h256) launch_ws_t<D, 32, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
-        else launch_ws_t<D, 32, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+        if (h256) launch_ws_t<D, 32, 256>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
+        else launch_ws_t<D, 32, 128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
     }
     return true;
 }
@@ -1920,7 +2148,9 @@ template <typename T>
 hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            const CacheArgs &kc, const MlpArgs &kd, const CacheArgs &vc,
                            const MlpArgs &vd, float scale, float *out, void *ws,
-                           const int32_t *pos, int nsel, hipStream_t st) {
+                           const int32_t *pos, int nsel, hipStream_t st,
+                           float *logc = nullptr, float *logr = nullptr, float *lse = nullptr,
+                           uint32_t *hist0 = nullptr) {
     const DecPlan pl = plan_decode(dm, Hq, T_, pos ? (int64_t)nsel : -1);
     const int G = Hq / dm.H;
     char *w = (char *)ws;
@@ -1928,12 +2158,12 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     float *cq = (float *)(w + pl.off_cq);
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
-    SparseArgs sa{nullptr, nullptr, 0};
+    SparseArgs sa{nullptr, nullptr, 0, logc, logr};
     int32_t *ord = nullptr, *cnt = nullptr;
     if (pos) {
         ord = (int32_t *)(w + pl.off_ord);
         cnt = (int32_t *)(w + pl.off_cnt);
-        sa = SparseArgs{ord, cnt, nsel};
+        sa = SparseArgs{ord, cnt, nsel, nullptr, nullptr};
     }
     // the query-side tables, and for a sparse call the list split (one more
     // block per unit)
@@ -1946,8 +2176,8 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     if constexpr (sizeof(T) == 2) {
         if (!pos && mfma_eligible(dm, kd, vd)) {
             done = dm.d == 128
-                       ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st)
-                       : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, st);
+                       ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st)
+                       : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
         }
         if (!done && mfma_eligible(dm, kd, vd)) {
             if (dm.d == 128) {
@@ -1968,9 +2198,9 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            (const T *)kc.lat, kc.idx, (const T *)vc.refs, (const T *)vc.lat,
                            vc.idx, (const T *)kd.w1, kd.b1, kd.hidden, kd.act, (const T *)vd.w1,
                            vd.b1, vd.hidden, vd.act, scale, u, cq, qr, part, sa.ord, sa.cnt,
-                           sa.nsel);
+                           sa.nsel, sa.logc, sa.logr);
     hipLaunchKernelGGL(combine2_kernel<T>, dim3(Hq, dm.B), dim3(kCombThreads), 0, st, Hq, G, dm.d, dm.H,
-                       pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out);
+                       pl.P, part, (const T *)vd.w2, vd.hidden, vd.b2, out, lse, hist0);
     return hipGetLastError();
 }
 
@@ -1980,6 +2210,64 @@ size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T) { return plan_decode(d
 
 size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel) {
     return plan_decode(dm, Hq, T, nsel).total;
+}
+
+// Workspace of a decode call with token selection: the dense call's, then the
+// logits (by token and by reference ordinal), the per-head log-sum-exp and the
+// selection keys.
+struct SelPlan {
+    DecPlan dec;
+    size_t off_logc, off_logr, off_lse, off_keys, off_hist, total;
+};
+SelPlan plan_select(const Dims &dm, int Hq, int64_t T) {
+    SelPlan p;
+    p.dec = plan_decode(dm, Hq, T);
+    const size_t U = (size_t)dm.B * dm.H, G = (size_t)(Hq / dm.H);
+    size_t off = p.dec.total;
+    p.off_logc = off;
+    off += align_up(U * G * (size_t)p.dec.Nt * 4);
+    p.off_logr = off;
+    off += align_up(U * G * (size_t)p.dec.Rt * 4);
+    p.off_lse = off;
+    off += align_up((size_t)dm.B * Hq * 4);
+    p.off_keys = off;
+    off += align_up(U * (size_t)keys_stride(T) * 4);
+    p.off_hist = off;
+    off += align_up(U * 256 * 4);
+    p.total = off;
+    return p;
+}
+
+size_t decode_select_ws_bytes(const Dims &dm, int Hq, int64_t T) { return plan_select(dm, Hq, T).total; }
+
+hipError_t launch_decode_select(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, float scale, float *out, int n_keep,
+                                int32_t *positions, float *scores, void *ws, size_t ws_bytes,
+                                hipStream_t st) {
+    (void)ws_bytes;
+    const SelPlan sp = plan_select(dm, Hq, T);
+    char *w = (char *)ws;
+    float *logc = (float *)(w + sp.off_logc);
+    float *logr = (float *)(w + sp.off_logr);
+    float *lse = (float *)(w + sp.off_lse);
+    uint32_t *keys = (uint32_t *)(w + sp.off_keys);
+    uint32_t *hist0 = (uint32_t *)(w + sp.off_hist);
+    const hipError_t e =
+        dm.dtype == 0
+            ? launch_decode_t<float>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, nullptr, 0,
+                                     st, logc, logr, lse, hist0)
+            : launch_decode_t<bf16_t>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, out, ws, nullptr,
+                                      0, st, logc, logr, lse, hist0);
+    if (e != hipSuccess) return e;
+    const unsigned U = (unsigned)(dm.B * dm.H);
+    hipLaunchKernelGGL(select_keys_kernel,
+                       dim3((unsigned)((T + 256 * kKeyPer - 1) / (256 * kKeyPer)), U), dim3(256), 0,
+                       st, logc, logr, lse, Hq, Hq / dm.H, dm.H, T, sp.dec.Nt, sp.dec.Rt, dm.s,
+                       keys, scores, hist0);
+    hipLaunchKernelGGL(select_topn_kernel, dim3(U), dim3(kSelThreads), 0, st, keys, hist0, T,
+                       n_keep, positions);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dims &dm, int Hq, int64_t T, const void *q, const CacheArgs &kc,

@@ -208,6 +208,38 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
                                           float softmax_scale, float *out, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* Host-only.  Workspace that deltakv_decode_attn_select needs for num_q_heads
+ * query heads over n_tokens cached tokens. */
+deltakv_status deltakv_decode_select_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     size_t *bytes);
+
+/* Dense decode attention that also picks the tokens for sparse attention at
+ * later steps or layers: the query-aware selector that section 4 pairs with
+ * on-demand reconstruction (OmniKV in its example: a filter layer's full
+ * attention chooses the tokens the other layers attend to).  out is written
+ * exactly as deltakv_decode_attn writes it.  For each (b, h), with G =
+ * num_q_heads / H query heads g of KV head h:
+ *   score_p = sum_g softmax_p(scale * q[b][g] . K^_p),   p = 0..n_tokens-1
+ * (the attention probability of position p, summed over the group), and
+ *   positions [B][H][n_keep] (device int32, written): the n_keep positions of
+ *       largest score, equal scores ordered by the lower position, listed in
+ *       increasing position order; if n_keep >= n_tokens every position
+ *       0..n_tokens-1, then -1.  A valid list for deltakv_decode_attn_sparse
+ *       with n_sel = n_keep.
+ *   scores [B][H][n_tokens] (device fp32, written; may be NULL): score_p.
+ * The scores come from the logits the attention itself uses (the bf16 path's
+ * approximations included); the ranking of those fp32 scores is exact.
+ * 1 <= n_keep <= DELTAKV_MAX_SPARSE_SELECT; other arguments as for
+ * deltakv_decode_attn; workspace: deltakv_decode_select_workspace_bytes. */
+deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          float softmax_scale, float *out, int32_t n_keep,
+                                          int32_t *positions, float *scores, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *deltakv_status_string(deltakv_status status);
 
