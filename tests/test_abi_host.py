@@ -218,3 +218,28 @@ def test_sparse_decode_argument_errors_return_before_any_launch():
         import torch
         p.dtype = torch.int64
         call(p)
+
+
+def test_select_argument_errors_return_before_any_launch():
+    sh = _shape(capacity=4096)
+    dec = _mlp(32, 256, 128)
+    need = dk.decode_select_workspace_bytes(sh, 32, 4096)
+    assert need > dk.decode_workspace_bytes(sh, 32, 4096)
+    ok_ws = _FakePtr(0x30000, need)
+
+    def call(pos, ws=ok_ws, scores=None):
+        dk.decode_attn_select(sh, 32, 4096, _FakePtr(), _cache(), dec, _cache(), dec, 0.088,
+                              _FakePtr(), pos, scores, ws)
+
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(None)                                       # no output list
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64), scores=_FakePtr(0x50004))     # misaligned scores
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos(64), ws=_FakePtr(0x30000, need - 1))
+    assert e.value.status == 4
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakePos((1 << 20) + 1))                    # n_keep too large
+    assert e.value.status == 1
