@@ -1405,7 +1405,7 @@ constexpr float kSlack = 8.f;
 
 // EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8).
 // KX: references per token (k = 4 or k = 8).
-template <int D, int DC, int HID, int EG, int KX>
+template <int D, int DC, int HID, int EG, int KX, bool SP>
 __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -1414,7 +1414,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const bf16_t *__restrict__ kw1, const float *__restrict__ kb1,
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
-    float *__restrict__ part, float *__restrict__ logc, float *__restrict__ logr) {
+    float *__restrict__ part, float *__restrict__ logc, float *__restrict__ logr,
+    const int32_t *__restrict__ sord, const int32_t *__restrict__ scnt, int nsel) {
     constexpr int TT = 32;             // tokens per tile
     constexpr int TH = 16;             // tokens per score wave
     constexpr int MB = HID / 16;       // 16-row hidden blocks (score waves)
@@ -1462,6 +1463,14 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const bf16_t *vref_u = vref + (int64_t)unit * Rcap * D;
     const float *qr_u = qr + (int64_t)unit * qr_rows(Rt) * GQ;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // sparse mode (SP): list positions of the unit's selected compressed-token
+    // ordinals (sord[0][unit]) and reference ordinals (sord[1][unit]) replace
+    // consecutive ordinals; the lists' lengths are the unit's counts
+    const int32_t *cord_u = SP ? sord + (int64_t)unit * nsel : nullptr;
+    const int32_t *rord_u = SP ? sord + ((int64_t)U + unit) * nsel : nullptr;
+    const int64_t Nt_u = SP ? (int64_t)scnt[2 * unit] : Nt;
+    const int64_t Rt_u = SP ? (int64_t)scnt[2 * unit + 1] : Rt;
+    __shared__ int32_t ordl[SP ? kSpTiles * 32 : 1];
 
     if (pidx >= Ptok) {
         // ---------------- reference tokens ----------------
@@ -1477,7 +1486,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
         for (int n = 0; n < NR; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
-        const int64_t je = min(Rt, ja + kRefPart);
+        const int64_t je = min(Rt_u, ja + kRefPart);
         for (int64_t j0 = ja; j0 < je; j0 += TT) {
             __syncthreads();
 #pragma unroll
@@ -1485,7 +1494,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const int it = tid + 256 * m;
                 const int row = it / CH, c8 = it % CH;
                 const int sc8 = c8 ^ (2 * (row & 3));
-                const int64_t j = min(j0 + row, Rt - 1);
+                const int64_t j = SP ? (int64_t)rord_u[min(j0 + row, je - 1)]
+                                     : min(j0 + row, Rt - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
                     (__attribute__((address_space(3))) void *)&vbufA[(256 * m + 64 * w) / CH][0],
@@ -1493,8 +1503,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
             if (sg_ok) {
                 const bool ok = j0 + st < je;
-                const float s = ok ? scale * qr_u[(j0 + st) * GQ + sg] : -INFINITY;
-                if (logr && ok) logr[((int64_t)unit * G + sg) * Rt + j0 + st] = s;
+                const int64_t jr = SP ? (int64_t)rord_u[min(j0 + st, je - 1)] : j0 + st;
+                const float s = ok ? scale * qr_u[jr * GQ + sg] : -INFINITY;
+                if (!SP && logr && ok) logr[((int64_t)unit * G + sg) * Rt + j0 + st] = s;
                 float tmax = s;
 #pragma unroll
                 for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 32));
@@ -1552,7 +1563,13 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     // ---------------- compressed tokens ----------------
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
     const int qa = (int)qa_;
-    const int qe = (int)min(Nt, qa_ + (int64_t)tiles_per_part * TT);
+    const int qe = (int)min(Nt_u, qa_ + (int64_t)tiles_per_part * TT);
+    if (SP && qa >= qe) {
+        // a partition past the end of this unit's list: a neutral record
+        for (int i = tid; i < G * kPStride; i += 256)
+            prec[i] = (i % kPStride == 0) ? -INFINITY : 0.f;
+        return;
+    }
     const int ntile = (qe - qa + TT - 1) / TT;
     const int Ntm1 = (int)Nt - 1;
     const bf16_t *klat_u = klat + (int64_t)unit * Ncap * DC;
@@ -1567,7 +1584,14 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         reinterpret_cast<u32x4 *>(&pw[0][0][0][0])[i] = zero4;
     for (int i = tid; i < 2 * 2 * 16; i += 256) (&msl[0][0][0])[i] = -INFINITY;
     for (int i = tid; i < HID; i += 256) biask[i] = kb1 ? kb1[i] : 0.f;
+    if constexpr (SP)
+        for (int i = tid; i < qe - qa; i += 256) ordl[i] = cord_u[qa + i];
     __syncthreads();
+    // the stored token (ordinal) behind list position i of this partition,
+    // clamped into it; dense: the ordinal itself, clamped to the stored ones
+    auto tok_of = [&](int i) -> uint32_t {
+        return SP ? (uint32_t)ordl[min(i, qe - 1) - qa] : (uint32_t)min(i, Ntm1);
+    };
 
     if (w < 2) {
         // ================= score waves =================
@@ -1605,7 +1629,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         };
         // inputs of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
-            const uint32_t tok = (uint32_t)min(t0 + TH * src + l16, Ntm1);
+            const uint32_t tok = tok_of(t0 + TH * src + l16);
             in.z = as_bf16x8(8 * lq < DC ? ld16(at_byte(klat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
             in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
             in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
@@ -1683,7 +1707,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 if constexpr (KX == 8) rs += (qv[e][4] + qv[e][5]) + (qv[e][6] + qv[e][7]);
                 const float v = scale * (sv[e] + rs * inv_k + cqv[e]);
                 s[e] = (tok_ok && gh[e] < G) ? v : -INFINITY;
-                if (logc && tok_ok && gh[e] < G)
+                if (!SP && logc && tok_ok && gh[e] < G)
                     logc[((int64_t)unit * G + gh[e]) * Nt + (t0 + TH * src + l16)] = v;
                 // reference maximum: the larger of the two waves' previous ones
                 mref[e] = fmaxf(msl[sl ^ 1][0][gh[e]], msl[sl ^ 1][1][gh[e]]);
@@ -1811,10 +1835,22 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // (the tile offset goes in the per-lane offset, which the range check
         // covers, not in the scalar offset)
         auto gload = [&](int t0) {
-            const int vbase = (t0 + TH * vj) * (KX * 2) + (int)(lrow * 2u);
+            if constexpr (SP) {
+                // row r = lrow + RPD m is (token r / KX, slot r % KX) of this
+                // wave's 16 tokens, looked up through the list
 #pragma unroll
-            for (int m = 0; m < NDMA; ++m)
-                gi[m] = __builtin_amdgcn_raw_buffer_load_b16(idx_rsrc, vbase + 2 * RPD * m, 0, 0);
+                for (int m = 0; m < NDMA; ++m) {
+                    const uint32_t r = lrow + (uint32_t)(RPD * m);
+                    const uint32_t tok = tok_of(t0 + TH * vj + (int)(r / KX));
+                    gi[m] = __builtin_amdgcn_raw_buffer_load_b16(
+                        idx_rsrc, (int)(tok * (KX * 2) + (r % KX) * 2u), 0, 0);
+                }
+            } else {
+                const int vbase = (t0 + TH * vj) * (KX * 2) + (int)(lrow * 2u);
+#pragma unroll
+                for (int m = 0; m < NDMA; ++m)
+                    gi[m] = __builtin_amdgcn_raw_buffer_load_b16(idx_rsrc, vbase + 2 * RPD * m, 0, 0);
+            }
         };
         // unused slots (0xFFFF) and rows past the stored range read the last
         // stored reference row: finite data under a zero weight
@@ -1830,7 +1866,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         auto zload = [&](int t0, bf16x8 (&z)[2]) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const uint32_t tok = (uint32_t)min(t0 + 16 * mb + l16, Ntm1);
+                const uint32_t tok = tok_of(t0 + 16 * mb + l16);
                 z[mb] = as_bf16x8(8 * lq < DC ? ld16(at_byte(vlat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
             }
         };
@@ -2087,13 +2123,18 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
                  const SparseArgs &sa, hipStream_t st) {
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
-    auto kern = dm.k == 4 ? (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 4> : main_ws_kernel<D, DC, HID, 2, 4>)
-                          : (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 8> : main_ws_kernel<D, DC, HID, 2, 8>);
+    const bool sp = sa.ord != nullptr;
+    auto kern = dm.k == 4
+                    ? (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 4, true> : main_ws_kernel<D, DC, HID, 1, 4, false>)
+                              : (sp ? main_ws_kernel<D, DC, HID, 2, 4, true> : main_ws_kernel<D, DC, HID, 2, 4, false>))
+                    : (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 8, true> : main_ws_kernel<D, DC, HID, 1, 8, false>)
+                              : (sp ? main_ws_kernel<D, DC, HID, 2, 8, true> : main_ws_kernel<D, DC, HID, 2, 8, false>));
     hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
                        (const bf16_t *)vc.lat, vc.idx, (const bf16_t *)kd.w1, kd.b1,
-                       (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part, sa.logc, sa.logr);
+                       (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part, sa.logc, sa.logr,
+                       sa.ord, sa.cnt, sa.nsel);
 }
 
 // The wave-specialised kernel covers k = 4 or 8 and d_c <= 32.
@@ -2174,7 +2215,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                        dm.s, ord, cnt);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-        if (!pos && mfma_eligible(dm, kd, vd)) {
+        if (mfma_eligible(dm, kd, vd)) {
             done = dm.d == 128
                        ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st)
                        : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
