@@ -42,9 +42,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # change to it the traffic is reported as null until it is measured again.
 DECODE_TRAFFIC = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "b59d0cfd8f49",
-    "fetch_kib": {"main_ws": 85678.0, "prep": 8539.8, "combine2": 2389.5},
-    "write_kib": {"main_ws": 3880.3, "prep": 1061.1, "combine2": 16.0},
+    "source_sha256": "0e0b01c24f8f",
+    "fetch_kib": {"main_ws": 85686.7, "prep": 8549.2, "combine2": 2393.0},
+    "write_kib": {"main_ws": 3880.2, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
