@@ -29,6 +29,10 @@ Parity status per function (what pins it; the tests under tests/ hold them):
                     total mass = number of query rows.
   top_positions     pinned: a pure-Python sort on (-score, position) tuples,
                     crafted ties, n_keep >= T.
+  quantize_latents  pinned: every value within half a step of its code's value,
+                    row extremes on codes 0 and 15, rows built from chosen codes
+                    recovered exactly, constant rows exact; an independent
+                    bf16 rounding through torch.
   Latent and decode values under random GELU weights have no printed value to
   compare with; they are pinned only through the pieces above.
 """
@@ -263,6 +267,38 @@ def top_positions(scores, n_keep: int) -> np.ndarray:
         return np.concatenate([np.arange(T), np.full(n_keep - T, -1)]).astype(np.int32)
     order = np.lexsort((np.arange(T), -scores))   # primary: score descending
     return np.sort(order[:n_keep]).astype(np.int32)
+
+
+def _bf16_round(x32):
+    """fp32 -> the nearest bf16 value (ties to even), returned as fp32."""
+    b = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def quantize_latents(z):
+    """4-bit latent storage, one group per latent row (the 4-bit quantisation
+    the DeltaKV page quotes its memory figure with; the format is this
+    project's reading): rows z [n, d_c] of bf16 values (as any float array)
+    -> codes [n, d_c] uint8 in 0..15, shift [n] and scale [n] (bf16 values as
+    fp32).  In fp32 arithmetic: shift = min of the row, scale = bf16((max -
+    min) / 15), code = clamp(rint((z - shift) / scale), 0, 15); a constant row
+    has scale 0 and codes 0."""
+    z = np.asarray(z, dtype=np.float32)
+    shift = z.min(axis=1)
+    rng = z.max(axis=1) - shift
+    scale = _bf16_round(rng / np.float32(15.0))
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint((z - shift[:, None]) / safe[:, None])
+    codes = np.clip(q, 0, 15).astype(np.uint8)
+    codes[scale == 0] = 0
+    return codes, shift.astype(np.float32), scale.astype(np.float32)
+
+
+def dequantize_latents(codes, shift, scale):
+    """Latent rows from 4-bit storage: shift + code * scale (fp64, exact)."""
+    return (np.asarray(shift, np.float64)[:, None]
+            + np.asarray(codes, np.float64) * np.asarray(scale, np.float64)[:, None])
 
 
 # ---- per-head helpers (composition of the steps above, no new arithmetic) ----

@@ -520,3 +520,53 @@ def test_select_head_equal_keys_prefer_the_lower_position():
     mass = oracle.group_attention_mass(q, kk, 1.0)
     assert mass[T - 1] == mass[top]
     assert list(oracle.top_positions(mass, 1)) == [min(top, T - 1)]
+
+
+# ---------------------------------------------------------- 4-bit latents
+
+def _bf16_rows(rng, n, dc, scale=1.0):
+    return torch.from_numpy(rng.standard_normal((n, dc)) * scale).to(torch.bfloat16).float().numpy()
+
+
+def test_bf16_rounding_helper_matches_torch():
+    x = _rng(70).standard_normal(5000).astype(np.float32) * 100
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle._bf16_round(x), want)
+
+
+@pytest.mark.parametrize("dc", [16, 32])
+def test_quantized_latents_within_half_a_step(dc):
+    z = _bf16_rows(_rng(71), 500, dc, 3.0)
+    codes, shift, scale = oracle.quantize_latents(z)
+    assert codes.dtype == np.uint8 and codes.max() <= 15
+    zh = oracle.dequantize_latents(codes, shift, scale)
+    # scale is rounded to bf16 (relative error <= 2^-9); the clamp at 15 can
+    # add that rounding times 15 at the top of the range
+    bound = scale[:, None] * (0.5 + 15 * 2.0 ** -8) + 1e-30
+    assert np.all(np.abs(zh - z) <= bound)
+    assert np.all(codes[np.arange(500), z.argmin(1)] == 0)
+    assert np.all(codes[np.arange(500), z.argmax(1)] >= 14)
+    assert np.array_equal(shift, z.min(1))
+
+
+def test_quantized_latents_recover_rows_built_from_codes():
+    # rows that are exactly shift + code * scale with min code 0 and max 15
+    rng = _rng(72)
+    n, dc = 200, 32
+    codes = rng.integers(0, 16, (n, dc)).astype(np.uint8)
+    codes[:, 0], codes[:, 1] = 0, 15
+    shift = torch.from_numpy(rng.standard_normal(n)).to(torch.bfloat16).float().numpy()
+    scale = np.float32(2.0) ** rng.integers(-6, 2, n).astype(np.float32)  # exact in bf16
+    z = (shift[:, None] + codes.astype(np.float32) * scale[:, None]).astype(np.float32)
+    z = oracle._bf16_round(z)
+    keep = np.all(oracle.dequantize_latents(codes, shift, scale) == z, axis=1)  # rows exact in bf16
+    c2, s2, k2 = oracle.quantize_latents(z[keep])
+    assert keep.sum() > 50
+    assert np.array_equal(c2, codes[keep]) and np.array_equal(k2, scale[keep])
+
+
+def test_quantized_constant_rows_are_exact():
+    z = np.full((4, 16), -1.5, np.float32)
+    codes, shift, scale = oracle.quantize_latents(z)
+    assert np.all(codes == 0) and np.all(scale == 0)
+    assert np.array_equal(oracle.dequantize_latents(codes, shift, scale), z.astype(np.float64))
