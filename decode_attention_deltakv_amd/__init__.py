@@ -36,6 +36,7 @@ LIB_PATH = os.path.join(PKG, "libdeltakv.so")
 
 F32, BF16 = 0, 1
 ACT_GELU, ACT_IDENTITY = 0, 1
+LATENT_DTYPE, LATENT_Q4 = 0, 1
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE",
                 5: "HIP"}
@@ -52,7 +53,7 @@ class CShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("stride", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_c", ctypes.c_int32), ("capacity", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("latent_format", ctypes.c_int32)]
 
 
 class CMlp(ctypes.Structure):
@@ -155,10 +156,11 @@ class Shape:
     d_c: int
     capacity: int
     dtype: int = BF16
+    latent_format: int = 0   # LATENT_DTYPE or LATENT_Q4
 
     def c(self) -> CShape:
         return CShape(self.batch, self.num_kv_heads, self.head_dim, self.stride, self.k,
-                      self.d_c, self.capacity, self.dtype, 0)
+                      self.d_c, self.capacity, self.dtype, self.latent_format)
 
     @property
     def torch_dtype(self):
@@ -201,8 +203,18 @@ class Cache:
         dt = shape.torch_dtype
         self.refs = torch.empty(B, H, R, shape.head_dim, dtype=dt, device=device)
         self.ref_sqnorm = torch.empty(B, H, R, dtype=torch.float32, device=device)
-        self.latents = torch.empty(B, H, max(N, 0), shape.d_c, dtype=dt, device=device)
-        self.idx = torch.empty(B, H, max(N, 0), shape.k, dtype=torch.uint16, device=device)
+        N = max(N, 0)
+        if shape.latent_format == LATENT_Q4:
+            # per unit: N rows of d_c / 2 code bytes, then N (shift, scale) bf16 pairs
+            self.latents = torch.empty(B, H, N * (shape.d_c // 2 + 4), dtype=torch.uint8,
+                                       device=device)
+            self.latent_codes = self.latents[:, :, :N * shape.d_c // 2].unflatten(
+                2, (N, shape.d_c // 2))
+            self.latent_params = self.latents[:, :, N * shape.d_c // 2:].view(
+                torch.bfloat16).unflatten(2, (N, 2))
+        else:
+            self.latents = torch.empty(B, H, N, shape.d_c, dtype=dt, device=device)
+        self.idx = torch.empty(B, H, N, shape.k, dtype=torch.uint16, device=device)
         assert self.refs.numel() * self.refs.element_size() == sz["refs"]
         assert self.latents.numel() * self.latents.element_size() == sz["latents"]
         assert self.idx.numel() * 2 == sz["idx"]

@@ -48,7 +48,11 @@ deltakv_status check_shape(const deltakv_shape *sh, dk::Dims *dm) {
                                       (long long)sh->capacity);
     if (sh->dtype != DELTAKV_F32 && sh->dtype != DELTAKV_BF16)
         return fail(DELTAKV_ERR_UNSUPPORTED, "dtype %d unknown", sh->dtype);
-    if (sh->reserved != 0) return fail(DELTAKV_ERR_INVALID_ARG, "reserved field must be 0");
+    if (sh->latent_format != DELTAKV_LATENT_DTYPE && sh->latent_format != DELTAKV_LATENT_Q4)
+        return fail(DELTAKV_ERR_INVALID_ARG, "latent_format %d unknown", sh->latent_format);
+    if (sh->latent_format == DELTAKV_LATENT_Q4 &&
+        (sh->dtype != DELTAKV_BF16 || (sh->d_c != 16 && sh->d_c != 32)))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents need bf16 and d_c 16 or 32");
     const int64_t R = dk::refs_upto(sh->capacity, sh->stride);
     if (R > 65535)
         return fail(DELTAKV_ERR_CAPACITY,
@@ -65,6 +69,7 @@ deltakv_status check_shape(const deltakv_shape *sh, dk::Dims *dm) {
         dm->k = sh->k;
         dm->dc = sh->d_c;
         dm->dtype = sh->dtype;
+        dm->lat_fmt = sh->latent_format;
         dm->cap = sh->capacity;
         dm->R = R;
         dm->N = sh->capacity - R;
@@ -158,7 +163,7 @@ deltakv_status deltakv_cache_bytes(const deltakv_shape *shape, size_t *refs_byte
     const size_t units = (size_t)dm.B * dm.H;
     if (refs_bytes) *refs_bytes = units * dm.R * dm.d * elt_bytes(dm);
     if (ref_sqnorm_bytes) *ref_sqnorm_bytes = units * dm.R * sizeof(float);
-    if (latents_bytes) *latents_bytes = units * dm.N * dm.dc * elt_bytes(dm);
+    if (latents_bytes) *latents_bytes = units * (size_t)dk::lat_unit_bytes(dm);
     if (idx_bytes) *idx_bytes = units * dm.N * dm.k * sizeof(uint16_t);
     return ok();
 }
@@ -245,6 +250,9 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
     if (!x) return fail(DELTAKV_ERR_INVALID_ARG, "x is NULL");
     if (!aligned16(x)) return fail(DELTAKV_ERR_INVALID_ARG, "x must be 16-byte aligned");
     if ((st = check_mlp(compressor, "compressor", dm.d, dm.dc, &ma)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::compress_q4_supported(dm, ma))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: compressor must have hidden width "
+                    "128 or 256");
     if ((st = check_cache(cache, dm, "cache", true, &ca)) != DELTAKV_OK) return st;
     const size_t need = dk::compress_ws_bytes(dm, t0, t1);
     if (workspace_bytes < need || (need > 0 && !workspace))
@@ -284,6 +292,9 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
         return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
     if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
+                    "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_ws_bytes(dm, num_q_heads, n_tokens);
@@ -324,6 +335,9 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
         return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
     if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
+                    "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_sparse_ws_bytes(dm, num_q_heads, n_tokens, n_sel);
@@ -364,6 +378,9 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
         return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
     if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
+                    "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_select_ws_bytes(dm, num_q_heads, n_tokens);

@@ -13,6 +13,7 @@ namespace dk {
 struct Dims {
     int B, H, d, s, k, dc;
     int dtype;          // 0 fp32, 1 bf16
+    int lat_fmt;        // 0: latents in dtype, 1: 4-bit codes + per-row bf16 shift / scale
     int64_t cap;        // capacity (positions)
     int64_t R;          // reference rows per unit = ceil(cap / s)
     int64_t N;          // compressed-token rows per unit = cap - R
@@ -56,6 +57,13 @@ hipError_t launch_decode_select(const Dims &dm, int Hq, int64_t T, const void *q
                                 const MlpArgs &vdec, float scale, float *out, int n_keep,
                                 int32_t *positions, float *scores, void *ws, size_t ws_bytes,
                                 hipStream_t st);
+// whether a call on a 4-bit latent cache has a kernel (compress / decode)
+bool compress_q4_supported(const Dims &dm, const MlpArgs &comp);
+bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec);
+// bytes of one unit's latent array
+inline int64_t lat_unit_bytes(const Dims &dm) {
+    return dm.lat_fmt ? dm.N * (dm.dc / 2 + 4) : dm.N * dm.dc * (dm.dtype == 0 ? 4 : 2);
+}
 // sparse decode attention over listed positions pos[B][H][nsel]
 size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel);
 hipError_t launch_decode_sparse(const Dims &dm, int Hq, int64_t T, const void *q,

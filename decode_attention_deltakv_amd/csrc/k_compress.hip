@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
 // (whose addresses those lists give) one tile ahead, so neither the
 // index-then-gather dependence nor HBM latency sits between two tiles.
 // Each thread owns NI 16-byte chunks (token t, columns 8 c8 .. 8 c8 + 7) of
-// every tile.  KX: largest k (4 or 8).
-template <int D, int HID, int DC, int KX, bool GELU>
+// every tile.  KX: largest k (4 or 8).  Q4: latents stored as 4-bit codes
+// with a per-row bf16 shift and scale (d_c / 4 lanes per row quantise it).
+template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
 __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
@@ -174,9 +175,23 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     const __amdgpu_buffer_rsrc_t ref_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)urefs, (short)0, (int)(Rcap * D * 2), 0x00020000);
 
-    // latents of the range [q0, qend) of this unit; stores past qend drop
-    const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(lat + (int64_t)unit * Ncap * DC), (short)0, (int)(qend * DC * 2), 0x00020000);
+    // latents of the range [q0, qend) of this unit; stores past qend drop.
+    // Q4: the unit's code rows, then its (shift, scale) words
+    uint8_t *lat_q4 = reinterpret_cast<uint8_t *>(lat) + (int64_t)unit * Ncap * (DC / 2 + 4);
+    const __amdgpu_buffer_rsrc_t lat_rsrc =
+        Q4 ? __builtin_amdgcn_make_buffer_rsrc((void *)lat_q4, (short)0, (int)(qend * (DC / 2)),
+                                               0x00020000)
+           : __builtin_amdgcn_make_buffer_rsrc((void *)(lat + (int64_t)unit * Ncap * DC),
+                                               (short)0, (int)(qend * DC * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t par_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(lat_q4 + Ncap * (DC / 2)), (short)0, (int)(qend * 4), 0x00020000);
+    // Q4: b2 of the four latent columns this thread quantises
+    float bias4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int o = 4 * (tid % (DC / 4)) + e;
+        bias4[e] = (Q4 && b2) ? b2[o] : 0.f;
+    }
     // b2 of the two latent columns this thread stores (fixed across tiles)
     float bias2[2];
     {
@@ -317,6 +332,49 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 for (int r = 0; r < 4; ++r) zp[w][16 * md + 4 * lq + r][16 * nt + l16] = zc[md][r];
         }
         __syncthreads();
+        if constexpr (Q4) {
+            // ---- sum the waves' shares, add b2, round to bf16, quantise the
+            // row: d_c / 4 consecutive lanes per token, four columns each
+            constexpr int TPT = DC / 4;
+            static_assert(256 / TPT >= TT, "one pass over the tile's rows");
+            const int t = tid / TPT, j = tid % TPT;
+            const int tc = t < TT ? t : TT - 1;  // lanes past the tile repeat its last row
+            float z[4];
+            float zmin = INFINITY, zmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = 4 * j + e;
+                const float v = zp[0][o][tc] + zp[1][o][tc] + zp[2][o][tc] + zp[3][o][tc] + bias4[e];
+                z[e] = __uint_as_float(pack_bf16(v, v) << 16);  // the stored (bf16) value
+                zmin = fminf(zmin, z[e]);
+                zmax = fmaxf(zmax, z[e]);
+            }
+#pragma unroll
+            for (int o = 1; o < TPT; o <<= 1) {
+                zmin = fminf(zmin, __shfl_xor(zmin, o, TPT));
+                zmax = fmaxf(zmax, __shfl_xor(zmax, o, TPT));
+            }
+            const float rng = zmax - zmin;
+            const float q = rng / 15.0f;
+            const float scale = __uint_as_float(pack_bf16(q, q) << 16);
+            uint32_t nib = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float c = scale > 0.f ? rintf((z[e] - zmin) / scale) : 0.f;
+                c = fminf(fmaxf(c, 0.f), 15.f);
+                nib |= (uint32_t)c << (4 * e);
+            }
+            // lanes j, j + 1 (j even) make one 32-bit word of eight codes
+            const uint32_t hi = __shfl_down(nib, 1, TPT);
+            if (t < TT && (j & 1) == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(nib | (hi << 16), lat_rsrc,
+                                                      ((uint32_t)qt + t) * (DC / 2) + 2u * j, 0, 0);
+            if (t < TT && j == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    (pack_bf16(zmin, zmin) & 0xffffu) | (pack_bf16(scale, scale) << 16), par_rsrc,
+                    ((uint32_t)qt + t) * 4u, 0, 0);
+            continue;
+        }
         // ---- sum the waves' shares, add b2, round, store (pairs of latent
         // values; rows past the range fall outside the store resource)
         static_assert((TT * DC / 2) % 256 == 0, "whole store passes");
@@ -340,10 +398,17 @@ void launch_cmfma_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64
     const int64_t tiles = (nq + 31) / 32;
     const int tpb = (int)std::max<int64_t>(1, std::min<int64_t>(16, (tiles * U + 1023) / 1024));
     const int64_t nblk = (tiles + tpb - 1) / tpb;
-    auto kern = dm.k <= 4 ? (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 4, true>
-                                        : compress_mfma_kernel<D, HID, DC, 4, false>)
-                          : (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 8, true>
-                                        : compress_mfma_kernel<D, HID, DC, 8, false>);
+    auto kern = dm.k <= 4 ? (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 4, true, false>
+                                        : compress_mfma_kernel<D, HID, DC, 4, false, false>)
+                          : (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 8, true, false>
+                                        : compress_mfma_kernel<D, HID, DC, 8, false, false>);
+    if constexpr (DC <= 32) {
+        if (dm.lat_fmt)
+            kern = dm.k <= 4 ? (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 4, true, true>
+                                           : compress_mfma_kernel<D, HID, DC, 4, false, true>)
+                             : (m.act == 0 ? compress_mfma_kernel<D, HID, DC, 8, true, true>
+                                           : compress_mfma_kernel<D, HID, DC, 8, false, true>);
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)(nblk * U)), dim3(256), 0, st, (const bf16_t *)x, t0,
                        t1 - t0, dm.s, dm.k, (const bf16_t *)c.refs, dm.R, c.idx, dm.N, q0, nq, U,
                        tpb, (const bf16_t *)m.w1, m.b1, (const bf16_t *)m.w2, m.b2,
@@ -377,6 +442,14 @@ bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 }
 
 }  // namespace
+
+bool compress_q4_supported(const Dims &dm, const MlpArgs &comp) {
+    // the matrix-core Compressor is the one that writes 4-bit rows: its
+    // conditions (launch_compress_mfma), with d_c 16 or 32
+    return dm.dtype == 1 && (dm.dc == 16 || dm.dc == 32) &&
+           (comp.hidden == 128 || comp.hidden == 256) && dm.N * dm.k * 2 <= INT32_MAX &&
+           dm.R * dm.d * 2 <= INT32_MAX && dm.N * dm.dc * 2 <= INT32_MAX;
+}
 
 // Workspace of one compress call (bf16 path): a 256-byte header holding the
 // fallback counter, then one 8-byte fallback-list entry per compressed token

@@ -1405,7 +1405,7 @@ constexpr float kSlack = 8.f;
 
 // EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8).
 // KX: references per token (k = 4 or k = 8).
-template <int D, int DC, int HID, int EG, int KX, bool SP>
+template <int D, int DC, int HID, int EG, int KX, bool SP, bool Q4>
 __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -1574,6 +1574,29 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int Ntm1 = (int)Nt - 1;
     const bf16_t *klat_u = klat + (int64_t)unit * Ncap * DC;
     const bf16_t *vlat_u = vlat + (int64_t)unit * Ncap * DC;
+    // Q4: the unit's code rows (d_c / 2 bytes each), then its (shift, scale)
+    // words; a lane's eight latent values are one 32-bit word of codes
+    const uint8_t *kq_u = reinterpret_cast<const uint8_t *>(klat) + (int64_t)unit * Ncap * (DC / 2 + 4);
+    const uint8_t *vq_u = reinterpret_cast<const uint8_t *>(vlat) + (int64_t)unit * Ncap * (DC / 2 + 4);
+    const uint32_t qpar = (uint32_t)Ncap * (DC / 2);  // byte offset of the words
+    auto zrow = [&](const bf16_t *lat_u, const uint8_t *q_u, uint32_t tok) -> bf16x8 {
+        if (8 * lq >= DC) return as_bf16x8(zero4);
+        if constexpr (Q4) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(q_u + tok * (DC / 2) + 4u * lq);
+            const uint32_t pr = *reinterpret_cast<const uint32_t *>(q_u + qpar + tok * 4u);
+            const float shift = __uint_as_float(pr << 16), sc = __uint_as_float(pr & 0xffff0000u);
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __builtin_fmaf((float)((w >> (8 * e)) & 15u), sc, shift);
+                const float b = __builtin_fmaf((float)((w >> (8 * e + 4)) & 15u), sc, shift);
+                o[e] = pack_bf16(a, b);
+            }
+            return as_bf16x8(o);
+        } else {
+            return as_bf16x8(ld16(at_byte(lat_u, (tok * DC + 8 * lq) * 2u)));
+        }
+    };
     const uint16_t *kidx_u = kidx + (int64_t)unit * Ncap * KX;
     const uint16_t *vidx_u = vidx + (int64_t)unit * Ncap * KX;
 
@@ -1630,7 +1653,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // inputs of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = tok_of(t0 + TH * src + l16);
-            in.z = as_bf16x8(8 * lq < DC ? ld16(at_byte(klat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
+            in.z = zrow(klat_u, kq_u, tok);
             in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
             in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
         };
@@ -1867,7 +1890,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const uint32_t tok = tok_of(t0 + 16 * mb + l16);
-                z[mb] = as_bf16x8(8 * lq < DC ? ld16(at_byte(vlat_u, (tok * DC + 8 * lq) * 2u)) : zero4);
+                z[mb] = zrow(vlat_u, vq_u, tok);
             }
         };
 
@@ -2124,11 +2147,15 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
     const int U = dm.B * dm.H;
     const int G = Hq / dm.H;
     const bool sp = sa.ord != nullptr;
-    auto kern = dm.k == 4
-                    ? (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 4, true> : main_ws_kernel<D, DC, HID, 1, 4, false>)
-                              : (sp ? main_ws_kernel<D, DC, HID, 2, 4, true> : main_ws_kernel<D, DC, HID, 2, 4, false>))
-                    : (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 8, true> : main_ws_kernel<D, DC, HID, 1, 8, false>)
-                              : (sp ? main_ws_kernel<D, DC, HID, 2, 8, true> : main_ws_kernel<D, DC, HID, 2, 8, false>));
+    auto pick = [&](auto q4c) {
+        constexpr bool QF = decltype(q4c)::value;
+        return dm.k == 4
+                   ? (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 4, true, QF> : main_ws_kernel<D, DC, HID, 1, 4, false, QF>)
+                             : (sp ? main_ws_kernel<D, DC, HID, 2, 4, true, QF> : main_ws_kernel<D, DC, HID, 2, 4, false, QF>))
+                   : (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 8, true, QF> : main_ws_kernel<D, DC, HID, 1, 8, false, QF>)
+                             : (sp ? main_ws_kernel<D, DC, HID, 2, 8, true, QF> : main_ws_kernel<D, DC, HID, 2, 8, false, QF>));
+    };
+    auto kern = dm.lat_fmt ? pick(std::true_type()) : pick(std::false_type());
     hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
@@ -2182,6 +2209,11 @@ bool mfma_eligible(const Dims &dm, const MlpArgs &kd, const MlpArgs &vd) {
            kd.act == 0 && vd.act == 0 && dm.dc <= 64;
 }
 
+// 4-bit latents are read by the wave-specialised kernel only
+bool ws_eligible(const Dims &dm, const MlpArgs &kd, const MlpArgs &vd) {
+    return mfma_eligible(dm, kd, vd) && (dm.k == 4 || dm.k == 8) && dm.dc <= 32;
+}
+
 // One decode call; with pos non-null, the sparse call over the listed
 // positions pos[B][H][nsel] (the lists are split first, then the same
 // kernels walk them).
@@ -2220,7 +2252,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                        ? launch_ws_d<128>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st)
                        : launch_ws_d<64>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
         }
-        if (!done && mfma_eligible(dm, kd, vd)) {
+        if (!done && !dm.lat_fmt && mfma_eligible(dm, kd, vd)) {
             if (dm.d == 128) {
                 if (dm.dc == 16) done = launch_mfma_dc<128, 16>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
                 else if (dm.dc == 32) done = launch_mfma_dc<128, 32>(dm, Hq, pl, kc, kd, vc, vd, scale, u, cq, qr, part, sa, st);
@@ -2232,6 +2264,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
             }
         }
     }
+    if (!done && dm.lat_fmt) return hipErrorInvalidValue;  // (rejected before any launch)
     if (!done)
         hipLaunchKernelGGL(main_kernel<T>, dim3((unsigned)pl.P, dm.H, dm.B), dim3(256), 0, st, Hq,
                            G, dm.d, dm.dc, dm.k, dm.s, dm.R, dm.N, pl.Rt, pl.Nt, pl.Ptok,
@@ -2248,6 +2281,10 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
 }  // namespace
 
 size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T) { return plan_decode(dm, Hq, T).total; }
+
+bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec) {
+    return ws_eligible(dm, kdec, vdec);
+}
 
 size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel) {
     return plan_decode(dm, Hq, T, nsel).total;

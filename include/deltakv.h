@@ -56,6 +56,12 @@ typedef enum {
 
 typedef enum { DELTAKV_F32 = 0, DELTAKV_BF16 = 1 } deltakv_dtype;
 
+/* Storage of the latents (deltakv_shape.latent_format). */
+typedef enum {
+    DELTAKV_LATENT_DTYPE = 0,  /* d_c values per token in shape->dtype */
+    DELTAKV_LATENT_Q4 = 1      /* 4-bit codes and a per-token shift / scale; see deltakv_cache */
+} deltakv_latent_format;
+
 typedef enum {
     DELTAKV_ACT_GELU = 0,      /* GELU, erf form: u * Phi(u) */
     DELTAKV_ACT_IDENTITY = 1   /* linear MLP (used by the exact-reconstruction check) */
@@ -64,7 +70,10 @@ typedef enum {
 /* Sizes of one (layer, stream) cache: the quantities the method is stated in.
  * Supported: head_dim in {64, 128}; stride >= 1; 1 <= k <= 8;
  * d_c in {16, 32, 64, 128}; capacity >= 1 with ceil(capacity / stride) <= 65535
- * (reference ordinals are stored as uint16). */
+ * (reference ordinals are stored as uint16).  latent_format
+ * DELTAKV_LATENT_Q4 needs bf16, d_c in {16, 32}, and calls whose MLPs are
+ * GELU with hidden width 128 or 256 (the same for K and V) and k in {4, 8};
+ * other calls on such a cache return UNSUPPORTED. */
 typedef struct {
     int32_t batch;         /* B: sequences */
     int32_t num_kv_heads;  /* H: KV heads of the layer */
@@ -74,7 +83,7 @@ typedef struct {
     int32_t d_c;           /* latent width */
     int64_t capacity;      /* maximum context length in tokens (per sequence) */
     int32_t dtype;         /* deltakv_dtype */
-    int32_t reserved;      /* must be 0 */
+    int32_t latent_format; /* deltakv_latent_format (0: latents in dtype) */
 } deltakv_shape;
 
 /* A light MLP: out = W2 act(W1 in + b1) + b2 (section 3, step 4: the
@@ -97,6 +106,16 @@ typedef struct {
  *   refs        [B][H][R][d]     reference rows, verbatim copies of the input
  *   ref_sqnorm  [B][H][R]        fp32 squared L2 norm of each reference row
  *   latents     [B][H][N][d_c]   Compressor outputs, by token ordinal
+ *               (DELTAKV_LATENT_Q4: per unit, N rows of d_c / 2 bytes of 4-bit
+ *               codes, two per byte, the lower latent index in the low
+ *               nibble, then N 32-bit words holding the row's bf16 shift (low
+ *               half) and bf16 scale (high half).  The Compressor output z,
+ *               rounded to bf16, is stored as shift = min(z), scale =
+ *               bf16((max(z) - min(z)) / 15), code = clamp(rint((z - shift) /
+ *               scale), 0, 15) in fp32 arithmetic (scale 0: codes 0); the
+ *               decode reads shift + code * scale.  This is the 4-bit latent
+ *               storage that the DeltaKV page's section 5 quotes its memory
+ *               figure with; the page gives no format.)
  *   idx         [B][H][N][k]     reference ordinals averaged into KV_R, nearest
  *                                first; 0xFFFF marks an unused slot (a token at
  *                                position p has min(k, ceil(p / s)) candidates)

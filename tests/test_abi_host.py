@@ -243,3 +243,28 @@ def test_select_argument_errors_return_before_any_launch():
     with pytest.raises(dk.DeltaKVError) as e:
         call(_FakePos((1 << 20) + 1))                    # n_keep too large
     assert e.value.status == 1
+
+
+def test_q4_latent_bytes_and_unsupported_combinations():
+    sh = _shape(latent_format=dk.LATENT_Q4)
+    sz = dk.cache_bytes(sh)
+    assert sz["latents"] == 8 * 30720 * (32 // 2 + 4)          # codes + (shift, scale)
+    assert sz["refs"] == dk.cache_bytes(_shape())["refs"]
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.cache_bytes(_shape(latent_format=2))
+    assert e.value.status == 1
+    for bad in (dict(dtype=dk.F32), dict(d_c=64)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.cache_bytes(_shape(latent_format=dk.LATENT_Q4, **bad))
+        assert e.value.status == 2
+    x = _FakePtr()
+    with pytest.raises(dk.DeltaKVError) as e:  # no 4-bit writer for hidden 64
+        dk.compress(_shape(latent_format=dk.LATENT_Q4, capacity=4096), x, 0, 16,
+                    _mlp(128, 64, 32), _cache(), _FakePtr(0x30000, 1 << 20))
+    assert e.value.status == 2
+    sh3 = _shape(latent_format=dk.LATENT_Q4, capacity=4096, k=3)
+    dec = _mlp(32, 256, 128)
+    with pytest.raises(dk.DeltaKVError) as e:  # no 4-bit reader for k = 3
+        dk.decode_attn(sh3, 32, 4096, _FakePtr(), _cache(), dec, _cache(), dec, 0.088,
+                       _FakePtr(), _FakePtr(0x30000, 1 << 30))
+    assert e.value.status == 2
