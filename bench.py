@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-q4", action="store_true",
+                    help="skip the 4-bit latent leg (layer 0 compressed again, decode timed)")
     ap.add_argument("--sparse-select", type=int, default=4096,
                     help="positions per (sequence, KV head) of the timed sparse decode calls "
                          "(0: skip them)")
@@ -193,14 +195,16 @@ class Setup:
                            self.dws)
 
 
-def decode_bytes_per_layer(wl):
+def decode_bytes_per_layer(wl, q4=False):
     """Algorithmic HBM bytes one decode_attn call (one layer) must read:
     per unit and stream the reference rows, latents and index lists, plus the
-    two Decompressors, the queries and the output."""
+    two Decompressors, the queries and the output.  q4: latents stored as
+    4-bit codes plus a 4-byte (shift, scale) word per token."""
     elt = 4 if wl.dtype == "fp32" else 2
     R = -(-wl.T // wl.stride)
     N = wl.T - R
-    unit = R * wl.head_dim * elt + N * wl.d_c * elt + N * wl.k * 2
+    lat = N * (wl.d_c // 2 + 4) if q4 else N * wl.d_c * elt
+    unit = R * wl.head_dim * elt + lat + N * wl.k * 2
     dec = 2 * ((wl.d_c * wl.hidden + wl.hidden * wl.head_dim) * elt
                + (wl.hidden + wl.head_dim) * 4)
     qo = wl.batch * wl.q_heads * wl.head_dim * (elt + 4)
@@ -478,6 +482,49 @@ def main():
             f"dense decode with selection {sel_ms:.4f} ms")
         del sws
 
+    # 4-bit latents: layer 0 compressed again into 4-bit caches (codes plus a
+    # per-token shift and scale), its compression and decode call timed
+    q4 = None
+    if not wl.appends and not a.no_q4 and wl.dtype == "bf16" and wl.d_c in (16, 32):
+        dk = S.dk
+        sh4 = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, wl.T,
+                       dk.BF16, dk.LATENT_Q4)
+        c4 = [dk.Cache(sh4) for _ in (0, 1)]
+        cws4 = dk.workspace(dk.compress_workspace_bytes(sh4, 0, wl.T))
+        e0, e1 = ev(), ev()
+        for rep_ in range(2):   # the first pass warms up
+            e0.record(stream)
+            for st_ in (0, 1):
+                dk.build_refs(sh4, S.x[0][st_], 0, wl.T, c4[st_])
+                dk.compress(sh4, S.x[0][st_], 0, wl.T, S.comp[0][st_], c4[st_], cws4)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        q4_comp_ms = e0.elapsed_time(e1)
+        del cws4
+        dws4 = dk.workspace(dk.decode_workspace_bytes(sh4, S.Hq, wl.T))
+        qstarts, qends = [ev() for _ in range(n_launch)], [ev() for _ in range(n_launch)]
+        d0 = S.dec[0]
+        for rep_ in range(2):
+            for i in range(n_launch):
+                qstarts[i].record(stream)
+                dk.decode_attn(sh4, S.Hq, wl.T, qs[0], c4[0], d0[0], c4[1], d0[1], S.scale,
+                               S.out, dws4)
+                qends[i].record(stream)
+            torch.cuda.synchronize()
+        q4_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(qstarts, qends)]))
+        q4_bytes = decode_bytes_per_layer(wl, q4=True)
+        lay = lambda sh: sum(v for k_, v in dk.cache_bytes(sh).items() if k_ != "ref_sqnorm")
+        unc = 2 * wl.batch * wl.kv_heads * wl.T * wl.head_dim * 2
+        q4 = {"decode_launch_ms": q4_ms, "compress_ms_layer": q4_comp_ms,
+              "algorithmic_bytes_per_launch": q4_bytes,
+              "eff_hbm_gbs": q4_bytes / (q4_ms * 1e-3) / 1e9,
+              "cache_bytes_per_layer": 2 * lay(sh4),
+              "bf16_latent_cache_bytes_per_layer": 2 * lay(S.shape),
+              "fraction_of_uncompressed": 2 * lay(sh4) / unc}
+        log(f"[bench] 4-bit latents: decode {q4_ms:.4f} ms per layer, cache "
+            f"{2 * lay(sh4) / unc:.3f} of uncompressed")
+        del c4, dws4
+
     # one decode step (every layer) captured in a HIP graph and replayed, with
     # fresh queries copied into the captured query buffer before each replay
     graph_ms = None
@@ -547,6 +594,7 @@ def main():
         "fallback_tokens_per_compress": int(S.stats[0].item()) // a.steps,
         "measured_copy_gbs": copy_gbs,
         "sparse_decode": sparse,
+        "q4_latents": q4,
         "roofline": {"kernel": "deltakv_decode_attn (one layer)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(wl),
