@@ -132,3 +132,54 @@ def test_select_llama_layer_32k_two_heads():
     # per KV head; scores checked against the oracle on two heads
     _select_case("select-llama-32k", 1, 8, 4, 32768, 128, 16, 4, 32, 256, dk.BF16, seed=404,
                  n_keep=4096, heads=[(0, 0), (0, 6)])
+
+
+def test_sparse_and_select_calls_replay_in_a_graph():
+    # both calls captured in one HIP graph (fresh queries copied in before each
+    # replay); every replay must equal the eager calls bitwise
+    B, H, G, T, d, s, k, dc, hid = 1, 2, 4, 900, 128, 16, 4, 32, 256
+    shape = dk.Shape(B, H, d, s, k, dc, T, dk.BF16)
+    kx = make_kv(B, H, T, d, torch.bfloat16, key=(405, 0))
+    vx = make_kv(B, H, T, d, torch.bfloat16, key=(405, 1))
+    cw, _ = make_mlp(d, hid, dc, torch.bfloat16, key=(405, 10))
+    kc = gpu_compress(shape, kx, gpu_mlp(cw, dk.ACT_GELU))
+    vc = gpu_compress(shape, vx, gpu_mlp(cw, dk.ACT_GELU))
+    kd = gpu_mlp(make_mlp(dc, hid, d, torch.bfloat16, key=(405, 12))[0], dk.ACT_GELU)
+    vd = gpu_mlp(make_mlp(dc, hid, d, torch.bfloat16, key=(405, 13))[0], dk.ACT_GELU)
+    Hq, n_keep, scale = H * G, 120, 1.0 / math.sqrt(d)
+    qbank = [queries(B * Hq, d, key=(405, 20 + i), dtype=torch.bfloat16).reshape(B, Hq, d).cuda()
+             for i in range(4)]
+    qbuf = qbank[0].clone()
+    pos = torch.empty(B, H, n_keep, dtype=torch.int32, device="cuda")
+    out_sel = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    out_sp = torch.empty_like(out_sel)
+    sws = dk.workspace(dk.decode_select_workspace_bytes(shape, Hq, T))
+    pws = dk.workspace(dk.decode_sparse_workspace_bytes(shape, Hq, T, n_keep))
+
+    def step():
+        dk.decode_attn_select(shape, Hq, T, qbuf, kc, kd, vc, vd, scale, out_sel, pos, None, sws)
+        dk.decode_attn_sparse(shape, Hq, T, qbuf, kc, kd, vc, vd, pos, scale, out_sp, pws)
+
+    want = []
+    for qi in qbank:
+        qbuf.copy_(qi)
+        step()
+        torch.cuda.synchronize()
+        want.append((out_sel.clone(), pos.clone(), out_sp.clone()))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, qi in enumerate(qbank):
+            qbuf.copy_(qi)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_sel, want[i][0]), f"replay {rep}.{i}: select output"
+            assert torch.equal(pos, want[i][1]), f"replay {rep}.{i}: positions"
+            assert torch.equal(out_sp, want[i][2]), f"replay {rep}.{i}: sparse output"
