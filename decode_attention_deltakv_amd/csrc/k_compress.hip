@@ -355,12 +355,13 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 zmax = fmaxf(zmax, __shfl_xor(zmax, o, TPT));
             }
             const float rng = zmax - zmin;
-            const float q = rng / 15.0f;
+            const float q = rng * (1.0f / 15.0f);
             const float scale = __uint_as_float(pack_bf16(q, q) << 16);
+            const float inv = 1.0f / (scale > 0.f ? scale : 1.0f);  // correctly rounded
             uint32_t nib = 0u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float c = scale > 0.f ? rintf((z[e] - zmin) / scale) : 0.f;
+                float c = scale > 0.f ? rintf((z[e] - zmin) * inv) : 0.f;
                 c = fminf(fmaxf(c, 0.f), 15.f);
                 nib |= (uint32_t)c << (4 * e);
             }

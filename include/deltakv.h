@@ -111,9 +111,10 @@ typedef struct {
  *               nibble, then N 32-bit words holding the row's bf16 shift (low
  *               half) and bf16 scale (high half).  The Compressor output z,
  *               rounded to bf16, is stored as shift = min(z), scale =
- *               bf16((max(z) - min(z)) / 15), code = clamp(rint((z - shift) /
- *               scale), 0, 15) in fp32 arithmetic (scale 0: codes 0); the
- *               decode reads shift + code * scale.  This is the 4-bit latent
+ *               bf16((max(z) - min(z)) * fp32(1/15)), code = clamp(rint((z -
+ *               shift) * (1 / scale)), 0, 15) in fp32 arithmetic, the
+ *               reciprocal correctly rounded (scale 0: codes 0); the decode
+ *               reads shift + code * scale.  This is the 4-bit latent
  *               storage that the DeltaKV page's section 5 quotes its memory
  *               figure with; the page gives no format.)
  *   idx         [B][H][N][k]     reference ordinals averaged into KV_R, nearest

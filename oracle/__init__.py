@@ -282,14 +282,16 @@ def quantize_latents(z):
     project's reading): rows z [n, d_c] of bf16 values (as any float array)
     -> codes [n, d_c] uint8 in 0..15, shift [n] and scale [n] (bf16 values as
     fp32).  In fp32 arithmetic: shift = min of the row, scale = bf16((max -
-    min) / 15), code = clamp(rint((z - shift) / scale), 0, 15); a constant row
-    has scale 0 and codes 0."""
+    min) * c15) with c15 the fp32 value nearest 1/15, inv = 1 / scale
+    (correctly rounded), code = clamp(rint((z - shift) * inv), 0, 15); a
+    constant row has scale 0 and codes 0."""
     z = np.asarray(z, dtype=np.float32)
     shift = z.min(axis=1)
     rng = z.max(axis=1) - shift
-    scale = _bf16_round(rng / np.float32(15.0))
+    scale = _bf16_round(rng * np.float32(1.0 / 15.0))
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = np.rint((z - shift[:, None]) / safe[:, None])
+    inv = (np.float32(1.0) / safe).astype(np.float32)
+    q = np.rint((z - shift[:, None]) * inv[:, None])
     codes = np.clip(q, 0, 15).astype(np.uint8)
     codes[scale == 0] = 0
     return codes, shift.astype(np.float32), scale.astype(np.float32)
