@@ -29,6 +29,9 @@ Parity status per function (what pins it; the tests under tests/ hold them):
                     total mass = number of query rows.
   top_positions     pinned: a pure-Python sort on (-score, position) tuples,
                     crafted ties, n_keep >= T.
+  decode_head_window pinned: the identity pair gives SDPA over the input rows
+                    followed by the window rows; a window that repeats a row
+                    weighs it twice; order-free in the window.
   quantize_latents  pinned: every value within half a step of its code's value,
                     row extremes on codes 0 and 15, rows built from chosen codes
                     recovered exactly, constant rows exact; an independent
@@ -352,3 +355,16 @@ def select_head(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, T: int, s: int, scale
     khat = reconstruct(k_refs, k_lat, k_idx, T, s, k_dec)
     mass = group_attention_mass(q_heads, khat, scale)
     return top_positions(mass, n_keep), mass
+
+
+def decode_head_window(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat, v_idx,
+                       v_dec: MLP, T: int, s: int, scale: float, k_win, v_win) -> np.ndarray:
+    """Attention of q_heads [G, d] over the T rebuilt tokens of one head plus
+    n_win exact rows (k_win, v_win [n_win, d]: a recent window not yet
+    compressed, or attention sinks kept verbatim)."""
+    khat = reconstruct(k_refs, k_lat, k_idx, T, s, k_dec)
+    vhat = reconstruct(v_refs, v_lat, v_idx, T, s, v_dec)
+    keys = np.concatenate([khat, _f64(k_win)], axis=0)
+    vals = np.concatenate([vhat, _f64(v_win)], axis=0)
+    return attention(q_heads, keys, vals, scale)
+

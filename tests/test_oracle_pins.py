@@ -570,3 +570,45 @@ def test_quantized_constant_rows_are_exact():
     codes, shift, scale = oracle.quantize_latents(z)
     assert np.all(codes == 0) and np.all(scale == 0)
     assert np.array_equal(oracle.dequantize_latents(codes, shift, scale), z.astype(np.float64))
+
+
+# ------------------------------------------ exact rows beside the compressed cache
+
+def test_window_decode_with_identity_pair_is_attention_over_rows_and_window():
+    from deltakv_synth import kv_rows
+    T, d, s, k, W = 200, 32, 8, 4, 37
+    kx = kv_rows(T + W, d, 4, 16, key=(80, 0)).double().numpy()
+    vx = kv_rows(T + W, d, 4, 16, key=(80, 1)).double().numpy()
+    comp, dec = _orthogonal_pair(d, 81)
+    kr, ki, kl = oracle.compress_head(kx[:T], s, k, comp)
+    vr, vi, vl = oracle.compress_head(vx[:T], s, k, comp)
+    q = _rng(82).standard_normal((4, d))
+    scale = 1 / np.sqrt(d)
+    got = oracle.decode_head_window(q, kr, kl, ki, dec, vr, vl, vi, dec, T, s, scale,
+                                    kx[T:], vx[T:])
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kx)[None], torch.from_numpy(vx)[None],
+        scale=scale)[0].numpy()
+    assert np.max(np.abs(got - want)) <= 1e-10 * np.max(np.abs(want))
+
+
+def test_window_decode_weighs_a_repeated_row_twice_and_ignores_window_order():
+    rng, q, args = _sparse_setup(83)
+    kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, scale = args
+    d = kr.shape[1]
+    kw = rng.standard_normal((9, d))
+    vw = rng.standard_normal((9, d))
+    base = oracle.decode_head_window(q, *args, kw, vw)
+    perm = rng.permutation(9)
+    assert np.max(np.abs(oracle.decode_head_window(q, *args, kw[perm], vw[perm]) - base)) <= \
+        1e-13 * np.max(np.abs(base))
+    # repeating window row 0 = attention with its logit raised by ln 2
+    rep = oracle.decode_head_window(q, *args, np.vstack([kw, kw[:1]]), np.vstack([vw, vw[:1]]))
+    kh = np.vstack([oracle.reconstruct(kr, kl, ki, T, s, kdec), kw])
+    vh = np.vstack([oracle.reconstruct(vr, vl, vi, T, s, vdec), vw])
+    bias = torch.zeros(1, T + 9, dtype=torch.float64)
+    bias[0, T] = np.log(2.0)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kh)[None], torch.from_numpy(vh)[None],
+        attn_mask=bias[None], scale=scale)[0].numpy()
+    assert np.max(np.abs(rep - want)) <= 1e-12 * np.max(np.abs(want))
