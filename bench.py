@@ -473,11 +473,28 @@ def main():
         del selws
         sp_bytes = float(np.mean([sparse_bytes_per_layer(S, i % wl.layers, pos)
                                   for i in range(min(n_launch, wl.layers))]))
+        # a recent window of 4096 exact rows beside the compressed cache
+        # (layer 0's last rows stand in for tokens not yet compressed)
+        n_win = min(4096, wl.T)
+        kwin = S.x[0][0][:, :, wl.T - n_win:].contiguous()
+        vwin = S.x[0][1][:, :, wl.T - n_win:].contiguous()
+        wws = S.dk.workspace(S.dk.decode_window_workspace_bytes(S.shape, S.Hq, wl.T, n_win))
+        c, d = S.cache[0], S.dec[0]
+        for rep_ in range(2):
+            for i in range(n_launch):
+                sstarts[i].record(stream)
+                S.dk.decode_attn_window(S.shape, S.Hq, wl.T, qs[0], c[0], d[0], c[1], d[1],
+                                        kwin, vwin, S.scale, S.out, wws)
+                sends[i].record(stream)
+            torch.cuda.synchronize()
+        win_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
+        del wws, kwin, vwin
         sparse = {"positions_per_kv_head": n_sel, "selected_fraction": n_sel / wl.T,
                   "launch_ms": sp_ms, "speedup_vs_dense_launch": launch_ms / sp_ms,
                   "algorithmic_bytes_per_launch": sp_bytes,
                   "eff_hbm_gbs": sp_bytes / (sp_ms * 1e-3) / 1e9,
-                  "select_launch_ms": sel_ms}
+                  "select_launch_ms": sel_ms,
+                  "window_rows": n_win, "window_launch_ms": win_ms}
         log(f"[bench] sparse decode ({n_sel} positions per KV head): {sp_ms:.4f} ms per layer; "
             f"dense decode with selection {sel_ms:.4f} ms")
         del sws

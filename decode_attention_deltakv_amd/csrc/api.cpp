@@ -223,6 +223,20 @@ deltakv_status deltakv_decode_select_workspace_bytes(const deltakv_shape *shape,
     return ok();
 }
 
+deltakv_status deltakv_decode_window_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     int64_t n_win, size_t *bytes) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (n_win < 1 || n_win > 65535)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_win %lld not in [1, 65535]", (long long)n_win);
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::decode_window_ws_bytes(dm, num_q_heads, n_tokens, n_win);
+    return ok();
+}
+
 deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
                                   int64_t t1, const deltakv_cache *cache, void *stream) {
     dk::Dims dm;
@@ -393,6 +407,48 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
                                              softmax_scale, out, n_keep, positions, scores,
                                              workspace, workspace_bytes, (hipStream_t)stream),
                     "deltakv_decode_attn_select");
+}
+
+deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          const void *k_win, const void *v_win, int64_t n_win,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, n_tokens)) != DELTAKV_OK) return st;
+    if (n_win < 1 || n_win > 65535)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_win %lld not in [1, 65535]", (long long)n_win);
+    if (!k_win || !v_win) return fail(DELTAKV_ERR_INVALID_ARG, "k_win / v_win is NULL");
+    if (!aligned16(k_win) || !aligned16(v_win))
+        return fail(DELTAKV_ERR_INVALID_ARG, "k_win / v_win must be 16-byte aligned");
+    if (!q || !out) return fail(DELTAKV_ERR_INVALID_ARG, "q / out is NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(DELTAKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
+    if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
+                    "decompressors of one hidden width, 128 or 256");
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    const size_t need = dk::decode_window_ws_bytes(dm, num_q_heads, n_tokens, n_win);
+    if (workspace_bytes < need || !workspace)
+        return fail(DELTAKV_ERR_WORKSPACE, "decode with a window needs %zu workspace bytes, "
+                    "got %zu", need, workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return from_hip(dk::launch_decode_window(dm, num_q_heads, n_tokens, q, kc, km, vc, vm, k_win,
+                                             v_win, n_win, softmax_scale, out, workspace,
+                                             workspace_bytes, (hipStream_t)stream),
+                    "deltakv_decode_attn_window");
 }
 
 const char *deltakv_status_string(deltakv_status status) {

@@ -57,6 +57,14 @@ hipError_t launch_decode_select(const Dims &dm, int Hq, int64_t T, const void *q
                                 const MlpArgs &vdec, float scale, float *out, int n_keep,
                                 int32_t *positions, float *scores, void *ws, size_t ws_bytes,
                                 hipStream_t st);
+// dense decode attention over the compressed cache plus n_win exact rows
+// kwin / vwin [B][H][n_win][d] (a recent window or attention sinks)
+size_t decode_window_ws_bytes(const Dims &dm, int Hq, int64_t T, int64_t n_win);
+hipError_t launch_decode_window(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const void *kwin, const void *vwin,
+                                int64_t n_win, float scale, float *out, void *ws, size_t ws_bytes,
+                                hipStream_t st);
 // whether a call on a 4-bit latent cache has a kernel (compress / decode)
 bool compress_q4_supported(const Dims &dm, const MlpArgs &comp);
 bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec);

@@ -765,6 +765,24 @@ __global__ __launch_bounds__(kSelThreads) void select_topn_kernel(
     }
 }
 
+// Merge of two normalised attention results over disjoint key sets (the
+// compressed cache and exact window rows): with e_i = exp(lse_i - max),
+// out = (e_1 out_1 + e_2 out_2) / (e_1 + e_2).  grid B * Hq, d threads.
+__global__ __launch_bounds__(kMaxD) void merge2_kernel(const float *__restrict__ o1,
+                                                       const float *__restrict__ l1,
+                                                       const float *__restrict__ o2,
+                                                       const float *__restrict__ l2, int d,
+                                                       float *__restrict__ out) {
+    const int64_t r = blockIdx.x;
+    const int c = threadIdx.x;
+    const float a = l1[r], b = l2[r];
+    const float m = fmaxf(a, b);
+    const float ea = a == -INFINITY ? 0.f : __expf(a - m);
+    const float eb = b == -INFINITY ? 0.f : __expf(b - m);
+    const float den = ea + eb;
+    if (c < d) out[r * d + c] = den > 0.f ? (ea * o1[r * d + c] + eb * o2[r * d + c]) / den : 0.f;
+}
+
 // Log-sum-exp merge of the partitions of one query head, then W2V applied to
 // the merged hidden sum.  grid (Hq, B).  The merge of the record vectors runs
 // with one float4 column per thread and the partitions split across thread
@@ -2281,6 +2299,78 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
 }  // namespace
 
 size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T) { return plan_decode(dm, Hq, T).total; }
+
+// Dims of n_win exact rows [B][H][n_win][d] seen as a stride-1 cache: every
+// row is a reference (attended verbatim), nothing is compressed.
+static Dims window_dims(const Dims &dm, int64_t n_win) {
+    Dims w = dm;
+    w.s = 1;
+    w.cap = n_win;
+    w.R = n_win;
+    w.N = 0;
+    w.lat_fmt = 0;
+    return w;
+}
+
+// Workspace of a decode call with a window: the compressed cache's call, the
+// window's call, then each one's output and per-head log-sum-exp.
+struct WinPlan {
+    size_t off_w, off_o1, off_l1, off_o2, off_l2, total;
+};
+static WinPlan plan_window(const Dims &dm, int Hq, int64_t T, int64_t n_win) {
+    WinPlan p;
+    size_t off = align_up(plan_decode(dm, Hq, T).total);
+    p.off_w = off;
+    off += align_up(plan_decode(window_dims(dm, n_win), Hq, n_win).total);
+    const size_t ob = align_up((size_t)dm.B * Hq * dm.d * 4), lb = align_up((size_t)dm.B * Hq * 4);
+    p.off_o1 = off;
+    off += ob;
+    p.off_l1 = off;
+    off += lb;
+    p.off_o2 = off;
+    off += ob;
+    p.off_l2 = off;
+    off += lb;
+    p.total = off;
+    return p;
+}
+
+size_t decode_window_ws_bytes(const Dims &dm, int Hq, int64_t T, int64_t n_win) {
+    return plan_window(dm, Hq, T, n_win).total;
+}
+
+hipError_t launch_decode_window(const Dims &dm, int Hq, int64_t T, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const void *kwin, const void *vwin,
+                                int64_t n_win, float scale, float *out, void *ws, size_t ws_bytes,
+                                hipStream_t st) {
+    (void)ws_bytes;
+    const WinPlan wp = plan_window(dm, Hq, T, n_win);
+    char *w = (char *)ws;
+    float *o1 = (float *)(w + wp.off_o1), *l1 = (float *)(w + wp.off_l1);
+    float *o2 = (float *)(w + wp.off_o2), *l2 = (float *)(w + wp.off_l2);
+    const Dims dw = window_dims(dm, n_win);
+    const CacheArgs kw{const_cast<void *>(kwin), nullptr, nullptr, nullptr};
+    const CacheArgs vw{const_cast<void *>(vwin), nullptr, nullptr, nullptr};
+    hipError_t e;
+    if (dm.dtype == 0) {
+        e = launch_decode_t<float>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, o1, ws, nullptr, 0, st,
+                                   nullptr, nullptr, l1);
+        if (e == hipSuccess)
+            e = launch_decode_t<float>(dw, Hq, n_win, q, kw, kdec, vw, vdec, scale, o2,
+                                       w + wp.off_w, nullptr, 0, st, nullptr, nullptr, l2);
+    } else {
+        e = launch_decode_t<bf16_t>(dm, Hq, T, q, kc, kdec, vc, vdec, scale, o1, ws, nullptr, 0,
+                                    st, nullptr, nullptr, l1);
+        if (e == hipSuccess)
+            e = launch_decode_t<bf16_t>(dw, Hq, n_win, q, kw, kdec, vw, vdec, scale, o2,
+                                        w + wp.off_w, nullptr, 0, st, nullptr, nullptr, l2);
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge2_kernel, dim3((unsigned)(dm.B * Hq)), dim3(kMaxD), 0, st, o1, l1, o2,
+                       l2, dm.d, out);
+    return hipGetLastError();
+}
 
 bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec) {
     return ws_eligible(dm, kdec, vdec);

@@ -228,6 +228,31 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
                                           float softmax_scale, float *out, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* Host-only.  Workspace that deltakv_decode_attn_window needs. */
+deltakv_status deltakv_decode_window_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t n_tokens,
+                                                     int64_t n_win, size_t *bytes);
+
+/* Decode attention over the compressed cache plus n_win exact rows kept
+ * beside it: a recent window of tokens not yet compressed, or attention sinks
+ * kept verbatim (rows the method's reference set does not hold).  For each
+ * query head g of KV head h,
+ *   out[b][g] = sum over the n_tokens rebuilt tokens and the n_win rows of
+ *               softmax(scale * q . K) V,
+ * the cache part exactly as deltakv_decode_attn rebuilds it, the window part
+ * with the given rows.
+ *   k_win, v_win: [B][H][n_win][d] in shape->dtype, read-only.
+ * 1 <= n_win <= 65535; other arguments as for deltakv_decode_attn; workspace:
+ * deltakv_decode_window_workspace_bytes.  (The two parts run as two decode
+ * passes whose outputs are merged by their log-sum-exp.) */
+deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t num_q_heads,
+                                          int64_t n_tokens, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          const void *k_win, const void *v_win, int64_t n_win,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Host-only.  Workspace that deltakv_decode_attn_select needs for num_q_heads
  * query heads over n_tokens cached tokens. */
 deltakv_status deltakv_decode_select_workspace_bytes(const deltakv_shape *shape,

@@ -268,3 +268,31 @@ def test_q4_latent_bytes_and_unsupported_combinations():
         dk.decode_attn(sh3, 32, 4096, _FakePtr(), _cache(), dec, _cache(), dec, 0.088,
                        _FakePtr(), _FakePtr(0x30000, 1 << 30))
     assert e.value.status == 2
+
+
+def test_window_argument_errors_return_before_any_launch():
+    sh = _shape(capacity=4096)
+    dec = _mlp(32, 256, 128)
+    need = dk.decode_window_workspace_bytes(sh, 32, 4096, 100)
+    assert need > dk.decode_workspace_bytes(sh, 32, 4096)
+    for bad in (0, 65536):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.decode_window_workspace_bytes(sh, 32, 4096, bad)
+        assert e.value.status == 1
+
+    class _Win(_FakePtr):
+        shape = (1, 8, 100, 128)
+
+    def call(kw, vw, ws=_FakePtr(0x30000, need)):
+        dk.decode_attn_window(sh, 32, 4096, _FakePtr(), _cache(), dec, _cache(), dec, kw, vw,
+                              0.088, _FakePtr(), ws)
+
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_Win(0x60000), None)
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_Win(0x60008), _Win(0x70000))               # misaligned window rows
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_Win(0x60000), _Win(0x70000), ws=_FakePtr(0x30000, need - 1))
+    assert e.value.status == 4
