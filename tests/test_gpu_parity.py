@@ -357,3 +357,55 @@ def test_single_token_appends_over_many_references_match_offline():
     tail = [p for p in range(T - 40, T) if p % s != 0]
     check_compress_unit(shape, x[0, 1], ap, 0, 1, oracle_mlp(cw, dk.ACT_GELU),
                         positions=np.array(tail), tol=2e-2)
+
+
+def test_llama_layer_128k_sampled():
+    # one layer of the benchmark's Llama-3.1-8B-shaped 128k workload, in the
+    # launch configuration the benchmark times (one compress call per stream
+    # over the whole prefix, one decode call): inputs generated on the GPU,
+    # the oracle checks sampled tokens of two units (first / last 64 and 128
+    # random compressed positions: index lists bit-exact, latents within
+    # 2e-2) and the decode of one KV head over all 131072 positions
+    from deltakv_synth import WORKLOADS, workload_index, unit_key
+    w = WORKLOADS["llama8b-32layer-T128k-bf16"]
+    widx = workload_index(w.name)
+    B, H, G, T, d, s = 1, w.kv_heads, w.q_heads // w.kv_heads, w.T, w.head_dim, w.stride
+    shape = dk.Shape(B, H, d, s, w.k, w.d_c, T, dk.BF16)
+    say("[case] llama8b-T128k one layer: generating and compressing on the GPU")
+    xs, caches, comps = [], [], []
+    for st in (0, 1):
+        x = torch.stack([kv_rows(T, d, w.n_dirs, w.n_centroids, key=unit_key(widx, 0, 0, h, st),
+                                 dtype=torch.bfloat16, device="cuda") for h in range(H)])[None]
+        cw = xavier_mlp(d, w.hidden, w.d_c, key=(1, widx, 0, st), dtype=torch.bfloat16)
+        cache = dk.Cache(shape)
+        dk.build_refs(shape, x, 0, T, cache)
+        ws = dk.workspace(dk.compress_workspace_bytes(shape, 0, T))
+        dk.compress(shape, x, 0, T, gpu_mlp(cw, dk.ACT_GELU), cache, ws)
+        torch.cuda.synchronize()
+        xs.append(x.cpu())
+        caches.append(cache)
+        comps.append(cw)
+        del x, ws
+    nonref = oracle.nonref_positions(T, s)
+    rng = np.random.default_rng(11)
+    pos = np.unique(np.concatenate([nonref[:64], nonref[-64:],
+                                    rng.choice(nonref, 128, replace=False)]))
+    worst = 0.0
+    for st in (0, 1):
+        for h in (0, 7):
+            worst = max(worst, check_compress_unit(shape, xs[st][0, h], caches[st], 0, h,
+                                                   oracle_mlp(comps[st], dk.ACT_GELU), pos,
+                                                   TOL[dk.BF16]))
+    say(f"[case] llama8b-T128k: sampled latent rel err {worst:.3e}")
+    kdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 0), dtype=torch.bfloat16)
+    vdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 1), dtype=torch.bfloat16)
+    q = queries(H * G, d, key=(3, widx), dtype=torch.bfloat16).reshape(B, H * G, d)
+    scale = 1.0 / math.sqrt(d)
+    out = gpu_decode(shape, H * G, T, q, caches[0], gpu_mlp(kdw, dk.ACT_GELU), caches[1],
+                     gpu_mlp(vdw, dk.ACT_GELU), scale)
+    h = 3
+    want = oracle_decode_head(shape, T, to_np(q[0, h * G:(h + 1) * G]), caches[0], caches[1], 0,
+                              h, oracle_mlp(kdw, dk.ACT_GELU), oracle_mlp(vdw, dk.ACT_GELU), scale)
+    err = rel_err_rows(out[0, h * G:(h + 1) * G], want)
+    say(f"[case] llama8b-T128k: decode rel err {err:.3e} (KV head {h})")
+    assert err <= TOL[dk.BF16]
