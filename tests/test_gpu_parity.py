@@ -409,3 +409,64 @@ def test_llama_layer_128k_sampled():
     err = rel_err_rows(out[0, h * G:(h + 1) * G], want)
     say(f"[case] llama8b-T128k: decode rel err {err:.3e} (KV head {h})")
     assert err <= TOL[dk.BF16]
+
+
+def test_streaming_llama_layer_128k_sampled():
+    # one layer of the streaming workload at full size: a 131072-token prompt
+    # compressed in 4096-token chunks (references accumulate across chunks, up
+    # to 16384 per unit at stride 8), then 8 one-token appends, as the
+    # benchmark launches them; the oracle checks sampled tokens (prompt and
+    # every appended token) of two units per stream and the decode of one KV
+    # head over all 131080 positions
+    from deltakv_synth import WORKLOADS, workload_index, unit_key
+    w = WORKLOADS["llama8b-32layer-T128k-stream-s8k8-bf16"]
+    widx = workload_index(w.name)
+    A = 8
+    B, H, G, T, d, s = 1, w.kv_heads, w.q_heads // w.kv_heads, w.T, w.head_dim, w.stride
+    cap = T + A
+    shape = dk.Shape(B, H, d, s, w.k, w.d_c, cap, dk.BF16)
+    say("[case] stream-s8k8 one layer: generating, chunked compression, appends")
+    xs, caches, comps = [], [], []
+    for st in (0, 1):
+        x = torch.stack([kv_rows(cap, d, w.n_dirs, w.n_centroids, key=unit_key(widx, 0, 0, h, st),
+                                 dtype=torch.bfloat16, device="cuda") for h in range(H)])[None]
+        cw = xavier_mlp(d, w.hidden, w.d_c, key=(1, widx, 0, st), dtype=torch.bfloat16)
+        cm = gpu_mlp(cw, dk.ACT_GELU)
+        cache = dk.Cache(shape)
+        ws = dk.workspace(max(dk.compress_workspace_bytes(shape, a, b_)
+                              for a, b_ in [(c0, min(T, c0 + w.chunk)) for c0 in range(0, T, w.chunk)]
+                              + [(cap - 1, cap)]))
+        bounds = list(range(0, T, w.chunk)) + [T] + list(range(T + 1, cap + 1))
+        for t0, t1 in zip(bounds[:-1], bounds[1:]):
+            xc = x[:, :, t0:t1].contiguous()
+            dk.build_refs(shape, xc, t0, t1, cache)
+            dk.compress(shape, xc, t0, t1, cm, cache, ws)
+        torch.cuda.synchronize()
+        xs.append(x.cpu())
+        caches.append(cache)
+        comps.append(cw)
+        del x, ws
+    nonref = oracle.nonref_positions(cap, s)
+    rng = np.random.default_rng(12)
+    pos = np.unique(np.concatenate([nonref[:64], nonref[nonref >= T - 64],
+                                    rng.choice(nonref[nonref < T], 128, replace=False)]))
+    worst = 0.0
+    for st in (0, 1):
+        for h in (1, 6):
+            worst = max(worst, check_compress_unit(shape, xs[st][0, h], caches[st], 0, h,
+                                                   oracle_mlp(comps[st], dk.ACT_GELU), pos,
+                                                   TOL[dk.BF16]))
+    say(f"[case] stream-s8k8: sampled latent rel err {worst:.3e}")
+    kdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 0), dtype=torch.bfloat16)
+    vdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 1), dtype=torch.bfloat16)
+    q = queries(H * G, d, key=(3, widx), dtype=torch.bfloat16).reshape(B, H * G, d)
+    scale = 1.0 / math.sqrt(d)
+    out = gpu_decode(shape, H * G, cap, q, caches[0], gpu_mlp(kdw, dk.ACT_GELU), caches[1],
+                     gpu_mlp(vdw, dk.ACT_GELU), scale)
+    h = 5
+    want = oracle_decode_head(shape, cap, to_np(q[0, h * G:(h + 1) * G]), caches[0], caches[1],
+                              0, h, oracle_mlp(kdw, dk.ACT_GELU), oracle_mlp(vdw, dk.ACT_GELU),
+                              scale)
+    err = rel_err_rows(out[0, h * G:(h + 1) * G], want)
+    say(f"[case] stream-s8k8: decode rel err {err:.3e} (KV head {h})")
+    assert err <= TOL[dk.BF16]
