@@ -470,3 +470,57 @@ def test_streaming_llama_layer_128k_sampled():
     err = rel_err_rows(out[0, h * G:(h + 1) * G], want)
     say(f"[case] stream-s8k8: decode rel err {err:.3e} (KV head {h})")
     assert err <= TOL[dk.BF16]
+
+
+def test_batch8_llama_layer_128k_sampled():
+    # one layer of the batch-8 128k workload (8 sequences x 8 KV heads = 64
+    # units per stream, per-sequence seeds): one compress call per stream over
+    # every sequence's whole prefix and one decode call; the oracle checks
+    # sampled tokens of units in the first and last sequence and the decode of
+    # one KV head of sequence 6 over all 131072 positions
+    from deltakv_synth import WORKLOADS, workload_index, unit_key
+    w = WORKLOADS["llama8b-32layer-T128k-batch8-bf16"]
+    widx = workload_index(w.name)
+    B, H, G, T, d, s = w.batch, w.kv_heads, w.q_heads // w.kv_heads, w.T, w.head_dim, w.stride
+    shape = dk.Shape(B, H, d, s, w.k, w.d_c, T, dk.BF16)
+    say("[case] batch8-T128k one layer: generating and compressing on the GPU")
+    xs, caches, comps = [], [], []
+    for st in (0, 1):
+        x = torch.empty(B, H, T, d, dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            for h in range(H):
+                x[b, h] = kv_rows(T, d, w.n_dirs, w.n_centroids, key=unit_key(widx, b, 0, h, st),
+                                  dtype=torch.bfloat16, device="cuda")
+        cw = xavier_mlp(d, w.hidden, w.d_c, key=(1, widx, 0, st), dtype=torch.bfloat16)
+        cache = dk.Cache(shape)
+        dk.build_refs(shape, x, 0, T, cache)
+        ws = dk.workspace(dk.compress_workspace_bytes(shape, 0, T))
+        dk.compress(shape, x, 0, T, gpu_mlp(cw, dk.ACT_GELU), cache, ws)
+        torch.cuda.synchronize()
+        xs.append(x[[0, B - 1]].cpu())   # the sequences the oracle checks
+        caches.append(cache)
+        comps.append(cw)
+        del x, ws
+    nonref = oracle.nonref_positions(T, s)
+    rng = np.random.default_rng(13)
+    pos = np.unique(np.concatenate([nonref[:32], nonref[-32:],
+                                    rng.choice(nonref, 64, replace=False)]))
+    worst = 0.0
+    for st in (0, 1):
+        for i, (b, h) in enumerate([(0, 2), (B - 1, 5)]):
+            worst = max(worst, check_compress_unit(shape, xs[st][i, h], caches[st], b, h,
+                                                   oracle_mlp(comps[st], dk.ACT_GELU), pos,
+                                                   TOL[dk.BF16]))
+    say(f"[case] batch8-T128k: sampled latent rel err {worst:.3e}")
+    kdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 0), dtype=torch.bfloat16)
+    vdw = xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 1), dtype=torch.bfloat16)
+    q = queries(B * H * G, d, key=(3, widx), dtype=torch.bfloat16).reshape(B, H * G, d)
+    scale = 1.0 / math.sqrt(d)
+    out = gpu_decode(shape, H * G, T, q, caches[0], gpu_mlp(kdw, dk.ACT_GELU), caches[1],
+                     gpu_mlp(vdw, dk.ACT_GELU), scale)
+    b, h = 6, 1
+    want = oracle_decode_head(shape, T, to_np(q[b, h * G:(h + 1) * G]), caches[0], caches[1], b,
+                              h, oracle_mlp(kdw, dk.ACT_GELU), oracle_mlp(vdw, dk.ACT_GELU), scale)
+    err = rel_err_rows(out[b, h * G:(h + 1) * G], want)
+    say(f"[case] batch8-T128k: decode rel err {err:.3e} (sequence {b}, KV head {h})")
+    assert err <= TOL[dk.BF16]
