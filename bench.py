@@ -489,12 +489,26 @@ def main():
             torch.cuda.synchronize()
         win_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
         del wws, kwin, vwin
+        # the mixed-length call at each sequence's full length (every position
+        # listed): what the list-driven path costs against the dense call
+        lens = [wl.T] * wl.batch
+        vws = S.dk.workspace(S.dk.decode_varlen_workspace_bytes(S.shape, S.Hq, wl.T))
+        for rep_ in range(2):
+            for i in range(n_launch):
+                sstarts[i].record(stream)
+                S.dk.decode_attn_varlen(S.shape, S.Hq, lens, qs[0], c[0], d[0], c[1], d[1],
+                                        S.scale, S.out, vws)
+                sends[i].record(stream)
+            torch.cuda.synchronize()
+        vl_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(sstarts, sends)]))
+        del vws
         sparse = {"positions_per_kv_head": n_sel, "selected_fraction": n_sel / wl.T,
                   "launch_ms": sp_ms, "speedup_vs_dense_launch": launch_ms / sp_ms,
                   "algorithmic_bytes_per_launch": sp_bytes,
                   "eff_hbm_gbs": sp_bytes / (sp_ms * 1e-3) / 1e9,
                   "select_launch_ms": sel_ms,
-                  "window_rows": n_win, "window_launch_ms": win_ms}
+                  "window_rows": n_win, "window_launch_ms": win_ms,
+                  "varlen_full_length_launch_ms": vl_ms}
         log(f"[bench] sparse decode ({n_sel} positions per KV head): {sp_ms:.4f} ms per layer; "
             f"dense decode with selection {sel_ms:.4f} ms")
         del sws

@@ -20,6 +20,9 @@ available as an alias):
                        out, workspace)
     decode_select_workspace_bytes(shape, Hq, T) -> int
     decode_window_workspace_bytes(shape, Hq, T, n_win) -> int
+    decode_varlen_workspace_bytes(shape, Hq, max_T) -> int
+    decode_attn_varlen(shape, Hq, lengths, q, k_cache, k_dec, v_cache, v_dec, scale, out,
+                       workspace)
     decode_attn_window(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, k_win, v_win, scale,
                        out, workspace)
     decode_attn_select(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out,
@@ -118,12 +121,19 @@ def lib():
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp), _P,
                                              _P, ctypes.c_int64, ctypes.c_float, _P, _P, _SZ, _P]
+    L.deltakv_decode_varlen_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
+                                                        ctypes.POINTER(_SZ)]
+    L.deltakv_decode_attn_varlen.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                             _P, ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                             ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                             ctypes.c_float, _P, _P, _SZ, _P]
     for name in ("deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
                  "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
                  "deltakv_decode_attn_sparse", "deltakv_decode_select_workspace_bytes",
                  "deltakv_decode_attn_select", "deltakv_decode_window_workspace_bytes",
-                 "deltakv_decode_attn_window"):
+                 "deltakv_decode_attn_window", "deltakv_decode_varlen_workspace_bytes",
+                 "deltakv_decode_attn_varlen"):
         getattr(L, name).restype = ctypes.c_int
     L.deltakv_status_string.argtypes = [ctypes.c_int]
     L.deltakv_status_string.restype = ctypes.c_char_p
@@ -365,6 +375,27 @@ def decode_attn_window(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.T
                                             _stream()))
 
 
+def decode_varlen_workspace_bytes(shape: Shape, num_q_heads: int, max_tokens: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_decode_varlen_workspace_bytes(ctypes.byref(cs), num_q_heads, max_tokens,
+                                                       ctypes.byref(v)))
+    return v.value
+
+
+def decode_attn_varlen(shape: Shape, num_q_heads: int, lengths, q: torch.Tensor,
+                       k_cache: Cache, k_dec: Mlp, v_cache: Cache, v_dec: Mlp, scale: float,
+                       out: torch.Tensor, workspace: Optional[torch.Tensor]):
+    """lengths: B host integers, the tokens each sequence holds."""
+    cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lens = (ctypes.c_int64 * shape.batch)(*[int(v) for v in lengths])
+    _check(lib().deltakv_decode_attn_varlen(ctypes.byref(cs), num_q_heads, lens, _ptr(q),
+                                            ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
+                                            ctypes.byref(vm), float(scale), _ptr(out),
+                                            _ptr(workspace), wsb, _stream()))
+
+
 def status_string(status: int) -> str:
     return lib().deltakv_status_string(status).decode()
 
@@ -394,6 +425,8 @@ deltakv_decode_select_workspace_bytes = decode_select_workspace_bytes
 deltakv_decode_attn_select = decode_attn_select
 deltakv_decode_window_workspace_bytes = decode_window_workspace_bytes
 deltakv_decode_attn_window = decode_attn_window
+deltakv_decode_varlen_workspace_bytes = decode_varlen_workspace_bytes
+deltakv_decode_attn_varlen = decode_attn_varlen
 deltakv_status_string = status_string
 deltakv_last_error = last_error
 deltakv_version = version

@@ -4,6 +4,7 @@
 // argument can cause is returned synchronously and without a device.
 #include "deltakv.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -237,6 +238,21 @@ deltakv_status deltakv_decode_window_workspace_bytes(const deltakv_shape *shape,
     return ok();
 }
 
+deltakv_status deltakv_decode_varlen_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t max_tokens,
+                                                     size_t *bytes) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_heads_tokens(dm, num_q_heads, max_tokens)) != DELTAKV_OK) return st;
+    if (max_tokens > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_UNSUPPORTED, "max_tokens %lld above %d", (long long)max_tokens,
+                    DELTAKV_MAX_SPARSE_SELECT);
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::decode_varlen_ws_bytes(dm, num_q_heads, max_tokens);
+    return ok();
+}
+
 deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
                                   int64_t t1, const deltakv_cache *cache, void *stream) {
     dk::Dims dm;
@@ -449,6 +465,54 @@ deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t nu
                                              v_win, n_win, softmax_scale, out, workspace,
                                              workspace_bytes, (hipStream_t)stream),
                     "deltakv_decode_attn_window");
+}
+
+deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t num_q_heads,
+                                          const int64_t *lengths, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if (!lengths) return fail(DELTAKV_ERR_INVALID_ARG, "lengths is NULL");
+    int64_t nmax = 0;
+    for (int b = 0; b < dm.B; ++b) {
+        if (lengths[b] < 1 || lengths[b] > dm.cap)
+            return fail(lengths[b] > dm.cap ? DELTAKV_ERR_CAPACITY : DELTAKV_ERR_INVALID_ARG,
+                        "lengths[%d] = %lld not in [1, capacity %lld]", b,
+                        (long long)lengths[b], (long long)dm.cap);
+        nmax = std::max(nmax, lengths[b]);
+    }
+    if ((st = check_heads_tokens(dm, num_q_heads, nmax)) != DELTAKV_OK) return st;
+    if (nmax > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_UNSUPPORTED, "longest sequence %lld above %d", (long long)nmax,
+                    DELTAKV_MAX_SPARSE_SELECT);
+    if (!q || !out) return fail(DELTAKV_ERR_INVALID_ARG, "q / out is NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(DELTAKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+    if (!std::isfinite(softmax_scale))
+        return fail(DELTAKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((st = check_mlp(k_dec, "k_dec", dm.dc, dm.d, &km)) != DELTAKV_OK) return st;
+    if ((st = check_mlp(v_dec, "v_dec", dm.dc, dm.d, &vm)) != DELTAKV_OK) return st;
+    if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
+                    "decompressors of one hidden width, 128 or 256");
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    const size_t need = dk::decode_varlen_ws_bytes(dm, num_q_heads, nmax);
+    if (workspace_bytes < need || !workspace)
+        return fail(DELTAKV_ERR_WORKSPACE, "mixed-length decode needs %zu workspace bytes, "
+                    "got %zu", need, workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return from_hip(dk::launch_decode_varlen(dm, num_q_heads, lengths, nmax, q, kc, km, vc, vm,
+                                             softmax_scale, out, workspace, workspace_bytes,
+                                             (hipStream_t)stream),
+                    "deltakv_decode_attn_varlen");
 }
 
 const char *deltakv_status_string(deltakv_status status) {

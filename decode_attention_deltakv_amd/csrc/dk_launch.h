@@ -65,6 +65,13 @@ hipError_t launch_decode_window(const Dims &dm, int Hq, int64_t T, const void *q
                                 const MlpArgs &vdec, const void *kwin, const void *vwin,
                                 int64_t n_win, float scale, float *out, void *ws, size_t ws_bytes,
                                 hipStream_t st);
+// decode attention over a batch of sequences of different lengths
+// (lens_host[b] tokens of sequence b, at most nmax), through the sparse decode
+size_t decode_varlen_ws_bytes(const Dims &dm, int Hq, int64_t nmax);
+hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host, int64_t nmax,
+                                const void *q, const CacheArgs &kc, const MlpArgs &kdec,
+                                const CacheArgs &vc, const MlpArgs &vdec, float scale, float *out,
+                                void *ws, size_t ws_bytes, hipStream_t st);
 // whether a call on a 4-bit latent cache has a kernel (compress / decode)
 bool compress_q4_supported(const Dims &dm, const MlpArgs &comp);
 bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec);

@@ -1,0 +1,50 @@
+// k_varlen.hip -- decode attention over a batch whose sequences hold different
+// numbers of tokens (serving batches mix lengths).  Sequence b attends its
+// positions 0 .. len[b] - 1; the call runs as the sparse decode over position
+// lists written here (every position below the sequence's length, then -1
+// padding), which over a full list gives the dense result.
+#include "dk_common.h"
+#include "dk_launch.h"
+
+namespace dk {
+namespace {
+
+// pos[b][h][i] = i < len_b ? i : -1, for i < nmax.  grid (ceil(nmax / 256), H, B).
+__global__ __launch_bounds__(256) void varlen_lists_kernel(const int64_t *__restrict__ lens,
+                                                           int nmax, int32_t *__restrict__ pos) {
+    const int b = blockIdx.z, h = blockIdx.y, H = gridDim.y;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nmax) return;
+    const int64_t len = lens[b];
+    pos[((int64_t)b * H + h) * nmax + i] = i < len ? (int32_t)i : -1;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// Workspace: the device copy of the lengths, the lists, then the sparse call's.
+size_t decode_varlen_ws_bytes(const Dims &dm, int Hq, int64_t nmax) {
+    return align256((size_t)dm.B * 8) + align256((size_t)dm.B * dm.H * nmax * 4) +
+           decode_sparse_ws_bytes(dm, Hq, nmax, (int)nmax);
+}
+
+hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host, int64_t nmax,
+                                const void *q, const CacheArgs &kc, const MlpArgs &kdec,
+                                const CacheArgs &vc, const MlpArgs &vdec, float scale, float *out,
+                                void *ws, size_t ws_bytes, hipStream_t st) {
+    char *w = (char *)ws;
+    int64_t *lens = (int64_t *)w;
+    int32_t *pos = (int32_t *)(w + align256((size_t)dm.B * 8));
+    char *sws = w + align256((size_t)dm.B * 8) + align256((size_t)dm.B * dm.H * nmax * 4);
+    hipError_t e = hipMemcpyAsync(lens, lens_host, (size_t)dm.B * 8, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(varlen_lists_kernel, dim3((unsigned)((nmax + 255) / 256), dm.H, dm.B),
+                       dim3(256), 0, st, lens, (int)nmax, pos);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_sparse(dm, Hq, nmax, q, kc, kdec, vc, vdec, pos, (int)nmax, scale, out,
+                                sws, ws_bytes - (size_t)(sws - w), st);
+}
+
+}  // namespace dk

@@ -253,6 +253,29 @@ deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t nu
                                           float softmax_scale, float *out, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* Host-only.  Workspace that deltakv_decode_attn_varlen needs when the
+ * longest sequence holds max_tokens tokens. */
+deltakv_status deltakv_decode_varlen_workspace_bytes(const deltakv_shape *shape,
+                                                     int32_t num_q_heads, int64_t max_tokens,
+                                                     size_t *bytes);
+
+/* Decode attention over a batch whose sequences hold different numbers of
+ * tokens (a serving batch of mixed lengths): sequence b attends its positions
+ * 0 .. lengths[b] - 1, each rebuilt as deltakv_decode_attn rebuilds it.
+ *   lengths: HOST int64 [B], 1 <= lengths[b] <= capacity, read during the
+ *            call (copied to the workspace on `stream`).
+ * Positions at or past a sequence's length may hold anything.  Other
+ * arguments as for deltakv_decode_attn; max(lengths) <=
+ * DELTAKV_MAX_SPARSE_SELECT; workspace: deltakv_decode_varlen_workspace_bytes
+ * with max_tokens = max(lengths).  (Runs as the sparse decode over every
+ * position below each sequence's length.) */
+deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t num_q_heads,
+                                          const int64_t *lengths, const void *q,
+                                          const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                          const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Host-only.  Workspace that deltakv_decode_attn_select needs for num_q_heads
  * query heads over n_tokens cached tokens. */
 deltakv_status deltakv_decode_select_workspace_bytes(const deltakv_shape *shape,

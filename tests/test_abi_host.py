@@ -296,3 +296,18 @@ def test_window_argument_errors_return_before_any_launch():
     with pytest.raises(dk.DeltaKVError) as e:
         call(_Win(0x60000), _Win(0x70000), ws=_FakePtr(0x30000, need - 1))
     assert e.value.status == 4
+
+
+def test_varlen_length_errors_return_before_any_launch():
+    sh = _shape(capacity=4096, batch=3)
+    dec = _mlp(32, 256, 128)
+    need = dk.decode_varlen_workspace_bytes(sh, 32, 4096)
+    for bad, status in (((10, 0, 5), 1), ((10, 4097, 5), 3)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.decode_attn_varlen(sh, 32, bad, _FakePtr(), _cache(), dec, _cache(), dec, 0.088,
+                                  _FakePtr(), _FakePtr(0x30000, need))
+        assert e.value.status == status
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.decode_attn_varlen(sh, 32, (10, 4096, 5), _FakePtr(), _cache(), dec, _cache(), dec,
+                              0.088, _FakePtr(), _FakePtr(0x30000, need - 1))
+    assert e.value.status == 4
