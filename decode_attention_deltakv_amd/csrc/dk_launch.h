@@ -72,6 +72,13 @@ hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host
                                 const void *q, const CacheArgs &kc, const MlpArgs &kdec,
                                 const CacheArgs &vc, const MlpArgs &vdec, float scale, float *out,
                                 void *ws, size_t ws_bytes, hipStream_t st);
+// mixed lengths on the dense kernels: per-unit (compressed, reference) counts
+bool decode_counts_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec);
+size_t decode_counts_ws_bytes(const Dims &dm, int Hq, int64_t nmax);
+hipError_t launch_decode_counts(const Dims &dm, int Hq, int64_t nmax, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const int32_t *counts, float scale,
+                                float *out, void *ws, hipStream_t st);
 // whether a call on a 4-bit latent cache has a kernel (compress / decode)
 bool compress_q4_supported(const Dims &dm, const MlpArgs &comp);
 bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec);

@@ -1486,8 +1486,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     // consecutive ordinals; the lists' lengths are the unit's counts
     const int32_t *cord_u = SP ? sord + (int64_t)unit * nsel : nullptr;
     const int32_t *rord_u = SP ? sord + ((int64_t)U + unit) * nsel : nullptr;
-    const int64_t Nt_u = SP ? (int64_t)scnt[2 * unit] : Nt;
-    const int64_t Rt_u = SP ? (int64_t)scnt[2 * unit + 1] : Rt;
+    // counts mode (not SP, scnt non-null): consecutive ordinals, but each unit
+    // holds only scnt[unit] tokens (a batch of sequences of different lengths)
+    const bool cmode = !SP && scnt != nullptr;
+    const int64_t Nt_u = (SP || cmode) ? (int64_t)scnt[2 * unit] : Nt;
+    const int64_t Rt_u = (SP || cmode) ? (int64_t)scnt[2 * unit + 1] : Rt;
     __shared__ int32_t ordl[SP ? kSpTiles * 32 : 1];
 
     if (pidx >= Ptok) {
@@ -1513,7 +1516,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const int row = it / CH, c8 = it % CH;
                 const int sc8 = c8 ^ (2 * (row & 3));
                 const int64_t j = SP ? (int64_t)rord_u[min(j0 + row, je - 1)]
-                                     : min(j0 + row, Rt - 1);
+                                     : min(j0 + row, je - 1);
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(vref_u + j * D + 8 * sc8),
                     (__attribute__((address_space(3))) void *)&vbufA[(256 * m + 64 * w) / CH][0],
@@ -1582,7 +1585,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int64_t qa_ = (int64_t)pidx * tiles_per_part * TT;
     const int qa = (int)qa_;
     const int qe = (int)min(Nt_u, qa_ + (int64_t)tiles_per_part * TT);
-    if (SP && qa >= qe) {
+    if ((SP || cmode) && qa >= qe) {
         // a partition past the end of this unit's list: a neutral record
         for (int i = tid; i < G * kPStride; i += 256)
             prec[i] = (i % kPStride == 0) ? -INFINITY : 0.f;
@@ -1630,8 +1633,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     __syncthreads();
     // the stored token (ordinal) behind list position i of this partition,
     // clamped into it; dense: the ordinal itself, clamped to the stored ones
+    // (counts mode clamps to the unit's own last token: rows past a sequence's
+    // length are not its data)
+    const int tlast = cmode ? qe - 1 : Ntm1;
     auto tok_of = [&](int i) -> uint32_t {
-        return SP ? (uint32_t)ordl[min(i, qe - 1) - qa] : (uint32_t)min(i, Ntm1);
+        return SP ? (uint32_t)ordl[min(i, qe - 1) - qa] : (uint32_t)min(i, tlast);
     };
 
     if (w < 2) {
@@ -1863,7 +1869,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // source chunk of this lane's LDS slot (rows of a gather instruction
         // start at a multiple of 4, so the row's swizzle is lrow % 4)
         const uint32_t coff = 16u * (c8 ^ (2u * (lrow & 3u)));
-        const uint32_t rlast = (uint32_t)Rt - 1u;
+        // (counts mode: the unit's own last reference, rows past a sequence's
+        // length are not its data)
+        const uint32_t rlast = (uint32_t)(cmode ? Rt_u : Rt) - 1u;
         uint32_t gi[NDMA];
         // index entries of this wave's rows of the tile at t0 (k = 4: rows
         // [64 vj, 64 vj + 64) of the tile's buffer; k = 8: the 128 rows of
@@ -2241,7 +2249,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            const MlpArgs &vd, float scale, float *out, void *ws,
                            const int32_t *pos, int nsel, hipStream_t st,
                            float *logc = nullptr, float *logr = nullptr, float *lse = nullptr,
-                           uint32_t *hist0 = nullptr) {
+                           uint32_t *hist0 = nullptr, const int32_t *counts = nullptr) {
     const DecPlan pl = plan_decode(dm, Hq, T_, pos ? (int64_t)nsel : -1);
     const int G = Hq / dm.H;
     char *w = (char *)ws;
@@ -2249,7 +2257,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
     float *cq = (float *)(w + pl.off_cq);
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
-    SparseArgs sa{nullptr, nullptr, 0, logc, logr};
+    SparseArgs sa{nullptr, counts, 0, logc, logr};
     int32_t *ord = nullptr, *cnt = nullptr;
     if (pos) {
         ord = (int32_t *)(w + pl.off_ord);
@@ -2370,6 +2378,25 @@ hipError_t launch_decode_window(const Dims &dm, int Hq, int64_t T, const void *q
     hipLaunchKernelGGL(merge2_kernel, dim3((unsigned)(dm.B * Hq)), dim3(kMaxD), 0, st, o1, l1, o2,
                        l2, dm.d, out);
     return hipGetLastError();
+}
+
+// A batch of sequences of different lengths on the wave-specialised kernel:
+// counts[unit] = (compressed tokens, references) of the unit's sequence,
+// nmax the longest sequence (the partition plan's length).
+bool decode_counts_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec) {
+    return ws_eligible(dm, kdec, vdec);
+}
+
+size_t decode_counts_ws_bytes(const Dims &dm, int Hq, int64_t nmax) {
+    return plan_decode(dm, Hq, nmax).total;
+}
+
+hipError_t launch_decode_counts(const Dims &dm, int Hq, int64_t nmax, const void *q,
+                                const CacheArgs &kc, const MlpArgs &kdec, const CacheArgs &vc,
+                                const MlpArgs &vdec, const int32_t *counts, float scale,
+                                float *out, void *ws, hipStream_t st) {
+    return launch_decode_t<bf16_t>(dm, Hq, nmax, q, kc, kdec, vc, vdec, scale, out, ws, nullptr,
+                                   0, st, nullptr, nullptr, nullptr, nullptr, counts);
 }
 
 bool decode_q4_supported(const Dims &dm, const MlpArgs &kdec, const MlpArgs &vdec) {

@@ -1,8 +1,12 @@
 // k_varlen.hip -- decode attention over a batch whose sequences hold different
 // numbers of tokens (serving batches mix lengths).  Sequence b attends its
-// positions 0 .. len[b] - 1; the call runs as the sparse decode over position
-// lists written here (every position below the sequence's length, then -1
-// padding), which over a full list gives the dense result.
+// positions 0 .. len[b] - 1.  Where the wave-specialised decode kernel serves
+// the shape, it runs with per-unit token counts written here; otherwise the
+// call runs as the sparse decode over position lists written here (every
+// position below the sequence's length, then -1 padding), which over a full
+// list gives the dense result.
+#include <algorithm>
+
 #include "dk_common.h"
 #include "dk_launch.h"
 
@@ -19,14 +23,28 @@ __global__ __launch_bounds__(256) void varlen_lists_kernel(const int64_t *__rest
     pos[((int64_t)b * H + h) * nmax + i] = i < len ? (int32_t)i : -1;
 }
 
+// counts[b][h] = (compressed tokens, references) among positions 0 .. len_b - 1.
+// grid B, H threads (at most 1024 KV heads).
+__global__ void varlen_counts_kernel(const int64_t *__restrict__ lens, int s,
+                                     int32_t *__restrict__ counts) {
+    const int b = blockIdx.x, h = threadIdx.x, H = blockDim.x;
+    const int64_t len = lens[b];
+    const int64_t r = (len + s - 1) / s;
+    counts[2 * ((int64_t)b * H + h)] = (int32_t)(len - r);
+    counts[2 * ((int64_t)b * H + h) + 1] = (int32_t)r;
+}
+
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
 // Workspace: the device copy of the lengths, the lists, then the sparse call's.
+// (the larger of the two ways, so the size does not depend on the MLPs)
 size_t decode_varlen_ws_bytes(const Dims &dm, int Hq, int64_t nmax) {
-    return align256((size_t)dm.B * 8) + align256((size_t)dm.B * dm.H * nmax * 4) +
-           decode_sparse_ws_bytes(dm, Hq, nmax, (int)nmax);
+    const size_t lists = align256((size_t)dm.B * dm.H * nmax * 4) +
+                         decode_sparse_ws_bytes(dm, Hq, nmax, (int)nmax);
+    const size_t counts = align256((size_t)dm.B * dm.H * 8) + decode_counts_ws_bytes(dm, Hq, nmax);
+    return align256((size_t)dm.B * 8) + std::max(lists, counts);
 }
 
 hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host, int64_t nmax,
@@ -39,6 +57,16 @@ hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host
     char *sws = w + align256((size_t)dm.B * 8) + align256((size_t)dm.B * dm.H * nmax * 4);
     hipError_t e = hipMemcpyAsync(lens, lens_host, (size_t)dm.B * 8, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return e;
+    if (dm.H <= 1024 && decode_counts_supported(dm, kdec, vdec)) {
+        int32_t *counts = (int32_t *)(w + align256((size_t)dm.B * 8));
+        char *dws = w + align256((size_t)dm.B * 8) + align256((size_t)dm.B * dm.H * 8);
+        hipLaunchKernelGGL(varlen_counts_kernel, dim3((unsigned)dm.B), dim3((unsigned)dm.H), 0, st,
+                           lens, dm.s, counts);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_decode_counts(dm, Hq, nmax, q, kc, kdec, vc, vdec, counts, scale, out, dws,
+                                    st);
+    }
     hipLaunchKernelGGL(varlen_lists_kernel, dim3((unsigned)((nmax + 255) / 256), dm.H, dm.B),
                        dim3(256), 0, st, lens, (int)nmax, pos);
     e = hipGetLastError();
