@@ -42,8 +42,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # change to it the traffic is reported as null until it is measured again.
 DECODE_TRAFFIC = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "4c85635cd844",
-    "fetch_kib": {"main_ws": 85705.1, "prep": 8549.2, "combine2": 2393.0},
+    "source_sha256": "9a2787459cbd",
+    "fetch_kib": {"main_ws": 85677.9, "prep": 8549.3, "combine2": 2394.0},
     "write_kib": {"main_ws": 3880.2, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
