@@ -32,10 +32,14 @@ Parity status per function (what pins it; the tests under tests/ hold them):
   decode_head_window pinned: the identity pair gives SDPA over the input rows
                     followed by the window rows; a window that repeats a row
                     weighs it twice; order-free in the window.
-  quantize_latents  pinned: every value within half a step of its code's value,
-                    row extremes on codes 0 and 15, rows built from chosen codes
-                    recovered exactly, constant rows exact; an independent
-                    bf16 rounding through torch.
+  quantize_latents  pinned: exact rational arithmetic (fractions.Fraction) on
+                    random rows gives the same codes and scales; half-integer
+                    quotients go to the even code; every value within half a
+                    step of its code's value, row extremes on codes 0 and 15,
+                    rows built from chosen codes recovered exactly, constant
+                    rows exact.
+  bf16_from_f64     pinned: exact rational rounding on random and near-midpoint
+                    values; torch's fp32 -> bf16 rounding on fp32 inputs.
   Latent and decode values under random GELU weights have no printed value to
   compare with; they are pinned only through the pieces above.
 """
@@ -279,22 +283,37 @@ def _bf16_round(x32):
     return b.astype(np.uint32).view(np.float32)
 
 
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_from_f64(x):
+    """fp64 values -> the nearest bf16 value, ties to the even significand,
+    rounded once from the fp64 value (no passage through fp32), as fp64.
+    A bf16 value carries 8 significant bits; below 2^-126 its step is 2^-133.
+    Values that round past the largest finite bf16 become infinite."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # |x| in [2^(e-1), 2^e)
+    step = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(x, -step)), step)
+    return np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, x), r)
+
+
 def quantize_latents(z):
     """4-bit latent storage, one group per latent row (the 4-bit quantisation
     the DeltaKV page quotes its memory figure with; the format is this
     project's reading): rows z [n, d_c] of bf16 values (as any float array)
     -> codes [n, d_c] uint8 in 0..15, shift [n] and scale [n] (bf16 values as
-    fp32).  In fp32 arithmetic: shift = min of the row, scale = bf16((max -
-    min) * c15) with c15 the fp32 value nearest 1/15, inv = 1 / scale
-    (correctly rounded), code = clamp(rint((z - shift) * inv), 0, 15); a
-    constant row has scale 0 and codes 0."""
-    z = np.asarray(z, dtype=np.float32)
+    fp32).  Defined in IEEE fp64 arithmetic:
+        shift = min of the row,
+        scale = bf16(fl64(fl64(max - min) / 15)), rounded once from fp64,
+        code  = clamp(rint(fl64(fl64(z - shift) / scale)), 0, 15),
+    rint rounding half-integers to the even integer; a constant row has scale
+    0 and codes 0."""
+    z = np.asarray(z, dtype=np.float64)
     shift = z.min(axis=1)
-    rng = z.max(axis=1) - shift
-    scale = _bf16_round(rng * np.float32(1.0 / 15.0))
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    inv = (np.float32(1.0) / safe).astype(np.float32)
-    q = np.rint((z - shift[:, None]) * inv[:, None])
+    scale = bf16_from_f64((z.max(axis=1) - shift) / 15.0)
+    safe = np.where(scale > 0, scale, 1.0)
+    q = np.rint((z - shift[:, None]) / safe[:, None])
     codes = np.clip(q, 0, 15).astype(np.uint8)
     codes[scale == 0] = 0
     return codes, shift.astype(np.float32), scale.astype(np.float32)

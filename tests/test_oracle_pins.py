@@ -6,6 +6,7 @@ independent library routines (numpy, scipy, torch CPU).
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -532,6 +533,91 @@ def test_bf16_rounding_helper_matches_torch():
     x = _rng(70).standard_normal(5000).astype(np.float32) * 100
     want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
     assert np.array_equal(oracle._bf16_round(x), want)
+
+
+def _bf16_exact(v: Fraction) -> Fraction:
+    """Nearest bf16 value to the rational v (8 significant bits, step 2^-133
+    below 2^-126), ties to the even significand, in exact arithmetic."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1                                                   # 2^e <= a < 2^(e+1)
+    step = Fraction(2) ** max(e - 7, -133)
+    return round(v / step) * step                                # round(): half to even
+
+
+def test_bf16_from_f64_is_exact_rounding_including_near_midpoints():
+    rng = _rng(73)
+    x = rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000)
+    # values just off a bf16 midpoint: rounding through fp32 first lands on
+    # the midpoint and then goes to the even neighbour, which is wrong for
+    # half of them; the helper must round once
+    base = oracle._bf16_round(rng.standard_normal(400).astype(np.float32) * 4).astype(np.float64)
+    _, e = np.frexp(base)
+    mid = base + np.ldexp(1.0, e - 9)
+    off = np.concatenate([mid + np.ldexp(1.0, e - 40), mid - np.ldexp(1.0, e - 40), mid])
+    x = np.concatenate([x, off, [0.0, -0.0, 2.0 ** -130, 3.0 * 2.0 ** -134]])
+    got = oracle.bf16_from_f64(x)
+    for xi, gi in zip(x, got):
+        assert Fraction(float(gi)) == _bf16_exact(Fraction(float(xi))), xi
+    via_f32 = oracle._bf16_round(off.astype(np.float32)).astype(np.float64)
+    assert np.any(via_f32 != oracle.bf16_from_f64(off)), "expected double rounding to differ"
+
+
+def _quantize_exact(zrow):
+    """The 4-bit format in exact rational arithmetic (an independent
+    implementation): scale = bf16((max - min) / 15), code = nearest integer to
+    (z - min) / scale, half to even, clamped to 0..15."""
+    zf = [Fraction(float(v)) for v in zrow]
+    lo = min(zf)
+    scale = _bf16_exact((max(zf) - lo) / 15)
+    if scale == 0:
+        return [0] * len(zf), lo, scale, [None] * len(zf)
+    quo = [(v - lo) / scale for v in zf]
+    return [min(15, max(0, round(q))) for q in quo], lo, scale, quo
+
+
+def test_quantized_latents_equal_exact_rational_definition():
+    rng = _rng(74)
+    rows = [_bf16_rows(rng, 150, 32, 3.0), _bf16_rows(rng, 150, 16, 1e-3),
+            # magnitudes far apart in one row (small values beside large ones)
+            _bf16_rows(rng, 100, 32, 1.0) * (10.0 ** rng.integers(-12, 3, (100, 32)))]
+    near_ties = exact_ties = 0
+    for z in rows:
+        z = torch.from_numpy(z).to(torch.bfloat16).double().numpy()
+        codes, shift, scale = oracle.quantize_latents(z)
+        for i in range(z.shape[0]):
+            c, lo, sc, quo = _quantize_exact(z[i])
+            assert Fraction(float(shift[i])) == lo and Fraction(float(scale[i])) == sc, i
+            for j in range(z.shape[1]):
+                gap = None if quo[j] is None else \
+                    abs(quo[j] - round(quo[j] - Fraction(1, 2)) - Fraction(1, 2))
+                if gap is not None and 0 < gap < Fraction(1, 2 ** 40):
+                    near_ties += 1   # fp64 may resolve such a quotient either way
+                    continue
+                exact_ties += gap == 0
+                assert codes[i, j] == c[j], (i, j, z[i, j])
+    assert near_ties == 0 and exact_ties > 0
+
+
+def test_quantized_half_integer_quotients_go_to_the_even_code():
+    # scale 1/4 (range 15/4), entries at shift + (n + 1/2) / 4: every quotient
+    # is an exact half-integer and every value is exact in bf16
+    for shift in (0.0, -2.0, 1.5):
+        n = np.arange(15)
+        z = np.concatenate([[shift, shift + 3.75], shift + (n + 0.5) * 0.25])[None, :]
+        z = np.concatenate([z, z[:, :16]], axis=1)[:, :32]
+        assert np.array_equal(oracle._bf16_round(z.astype(np.float32)), z.astype(np.float32))
+        codes, sh, sc = oracle.quantize_latents(z)
+        assert sc[0] == 0.25 and sh[0] == shift
+        want = np.concatenate([[0, 15], 2 * np.round((n + 0.5) / 2)])   # even neighbour
+        want = np.concatenate([want, want[:16]])[:32]
+        assert np.array_equal(codes[0], want.astype(np.uint8))
+        assert list(codes[0, 2:7]) == [0, 2, 2, 4, 4]
 
 
 @pytest.mark.parametrize("dc", [16, 32])
