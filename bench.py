@@ -157,6 +157,9 @@ class Setup:
         """The whole prompt: one call per (layer, stream), or chunk by chunk
         for the streaming workload (references accumulate across chunks)."""
         dk, sh, T = self.dk, self.shape, self.wl.T
+        for row in self.cache:          # refill every cache from position 0
+            for c in row:
+                c.reset()
         for c0 in range(0, T, self.chunk):
             c1 = min(T, c0 + self.chunk)
             for l in range(self.wl.layers):
@@ -491,12 +494,12 @@ def main():
         del wws, kwin, vwin
         # the mixed-length call at each sequence's full length (every position
         # listed): what the list-driven path costs against the dense call
-        lens = [wl.T] * wl.batch
+        lens = torch.full((wl.batch,), wl.T, dtype=torch.int64, device="cuda")
         vws = S.dk.workspace(S.dk.decode_varlen_workspace_bytes(S.shape, S.Hq, wl.T))
         for rep_ in range(2):
             for i in range(n_launch):
                 sstarts[i].record(stream)
-                S.dk.decode_attn_varlen(S.shape, S.Hq, lens, qs[0], c[0], d[0], c[1], d[1],
+                S.dk.decode_attn_varlen(S.shape, S.Hq, lens, wl.T, qs[0], c[0], d[0], c[1], d[1],
                                         S.scale, S.out, vws)
                 sends[i].record(stream)
             torch.cuda.synchronize()
@@ -526,6 +529,7 @@ def main():
         for rep_ in range(2):   # the first pass warms up
             e0.record(stream)
             for st_ in (0, 1):
+                c4[st_].reset()
                 dk.build_refs(sh4, S.x[0][st_], 0, wl.T, c4[st_])
                 dk.compress(sh4, S.x[0][st_], 0, wl.T, S.comp[0][st_], c4[st_], cws4)
             e1.record(stream)

@@ -21,8 +21,8 @@ available as an alias):
     decode_select_workspace_bytes(shape, Hq, T) -> int
     decode_window_workspace_bytes(shape, Hq, T, n_win) -> int
     decode_varlen_workspace_bytes(shape, Hq, max_T) -> int
-    decode_attn_varlen(shape, Hq, lengths, q, k_cache, k_dec, v_cache, v_dec, scale, out,
-                       workspace)
+    decode_attn_varlen(shape, Hq, lengths, max_tokens, q, k_cache, k_dec, v_cache, v_dec,
+                       scale, out, workspace)
     decode_attn_window(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, k_win, v_win, scale,
                        out, workspace)
     decode_attn_select(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out,
@@ -70,7 +70,8 @@ class CMlp(ctypes.Structure):
 
 class CCache(ctypes.Structure):
     _fields_ = [("refs", ctypes.c_void_p), ("ref_sqnorm", ctypes.c_void_p),
-                ("latents", ctypes.c_void_p), ("idx", ctypes.c_void_p)]
+                ("latents", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("n_built", ctypes.c_int64), ("n_compressed", ctypes.c_int64)]
 
 
 _lib = None
@@ -123,7 +124,7 @@ def lib():
                                              _P, ctypes.c_int64, ctypes.c_float, _P, _P, _SZ, _P]
     L.deltakv_decode_varlen_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
                                                         ctypes.POINTER(_SZ)]
-    L.deltakv_decode_attn_varlen.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+    L.deltakv_decode_attn_varlen.argtypes = [sp, ctypes.c_int32, _P, ctypes.c_int64,
                                              _P, ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.c_float, _P, _P, _SZ, _P]
@@ -215,7 +216,12 @@ class Mlp:
 
 class Cache:
     """The four arrays of one (layer, stream) compressed cache, allocated with
-    torch on `device` at the sizes deltakv_cache_bytes reports."""
+    torch on `device` at the sizes deltakv_cache_bytes reports, and its two
+    filled lengths (n_built, n_compressed), which the library checks and
+    advances; reset() sets them back to 0 to refill the arrays."""
+
+    n_built = 0
+    n_compressed = 0
 
     def __init__(self, shape: Shape, device="cuda"):
         sz = cache_bytes(shape)
@@ -242,7 +248,15 @@ class Cache:
     def c(self) -> CCache:
         return CCache(_ptr(self.refs), _ptr(self.ref_sqnorm),
                       _ptr(self.latents) if self.latents.numel() else None,
-                      _ptr(self.idx) if self.idx.numel() else None)
+                      _ptr(self.idx) if self.idx.numel() else None,
+                      self.n_built, self.n_compressed)
+
+    def _took(self, cc: CCache):
+        """Keep the filled lengths the library left in the struct."""
+        self.n_built, self.n_compressed = cc.n_built, cc.n_compressed
+
+    def reset(self):
+        self.n_built = self.n_compressed = 0
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size()
@@ -277,6 +291,7 @@ def build_refs(shape: Shape, x: torch.Tensor, t0: int, t1: int, cache: Cache):
     cs, cc = shape.c(), cache.c()
     _check(lib().deltakv_build_refs(ctypes.byref(cs), _ptr(x), t0, t1, ctypes.byref(cc),
                                     _stream()))
+    cache._took(cc)
 
 
 def compress(shape: Shape, x: torch.Tensor, t0: int, t1: int, compressor: Mlp, cache: Cache,
@@ -286,6 +301,7 @@ def compress(shape: Shape, x: torch.Tensor, t0: int, t1: int, compressor: Mlp, c
     _check(lib().deltakv_compress(ctypes.byref(cs), _ptr(x), t0, t1, ctypes.byref(cm),
                                   ctypes.byref(cc), _ptr(workspace), wsb, _ptr(stats),
                                   _stream()))
+    cache._took(cc)
 
 
 def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, k_cache: Cache,
@@ -383,14 +399,18 @@ def decode_varlen_workspace_bytes(shape: Shape, num_q_heads: int, max_tokens: in
     return v.value
 
 
-def decode_attn_varlen(shape: Shape, num_q_heads: int, lengths, q: torch.Tensor,
-                       k_cache: Cache, k_dec: Mlp, v_cache: Cache, v_dec: Mlp, scale: float,
-                       out: torch.Tensor, workspace: Optional[torch.Tensor]):
-    """lengths: B host integers, the tokens each sequence holds."""
+def decode_attn_varlen(shape: Shape, num_q_heads: int, lengths: torch.Tensor,
+                       max_tokens: int, q: torch.Tensor, k_cache: Cache, k_dec: Mlp,
+                       v_cache: Cache, v_dec: Mlp, scale: float, out: torch.Tensor,
+                       workspace: Optional[torch.Tensor]):
+    """lengths: int64 [B] on the device, the tokens each sequence holds (read
+    by the kernels); max_tokens: an upper bound of every length."""
     cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    lens = (ctypes.c_int64 * shape.batch)(*[int(v) for v in lengths])
-    _check(lib().deltakv_decode_attn_varlen(ctypes.byref(cs), num_q_heads, lens, _ptr(q),
+    if lengths is not None and lengths.dtype != torch.int64:
+        raise ValueError("lengths must be int64")
+    _check(lib().deltakv_decode_attn_varlen(ctypes.byref(cs), num_q_heads, _ptr(lengths),
+                                            int(max_tokens), _ptr(q),
                                             ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
                                             ctypes.byref(vm), float(scale), _ptr(out),
                                             _ptr(workspace), wsb, _stream()))

@@ -105,9 +105,20 @@ deltakv_status check_mlp(const deltakv_mlp *m, const char *name, int in_dim, int
     return DELTAKV_OK;
 }
 
+// reads_upto > 0: the call reads positions [0, reads_upto), which must have
+// been compressed (the struct's host-side filled length).
 deltakv_status check_cache(const deltakv_cache *c, const dk::Dims &dm, const char *name,
-                           bool need_tokens, dk::CacheArgs *a) {
+                           bool need_tokens, dk::CacheArgs *a, int64_t reads_upto = 0) {
     if (!c) return fail(DELTAKV_ERR_INVALID_ARG, "%s is NULL", name);
+    if (c->n_compressed < 0 || c->n_compressed > c->n_built || c->n_built > dm.cap)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "%s: filled lengths need 0 <= n_compressed (%lld) <= n_built (%lld) <= "
+                    "capacity (%lld)", name, (long long)c->n_compressed, (long long)c->n_built,
+                    (long long)dm.cap);
+    if (reads_upto > c->n_compressed)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "%s: the call reads %lld positions but only %lld are compressed", name,
+                    (long long)reads_upto, (long long)c->n_compressed);
     if (!c->refs || !c->ref_sqnorm)
         return fail(DELTAKV_ERR_INVALID_ARG, "%s: refs / ref_sqnorm are NULL", name);
     if (need_tokens && dm.N > 0 && (!c->latents || !c->idx))
@@ -254,7 +265,7 @@ deltakv_status deltakv_decode_varlen_workspace_bytes(const deltakv_shape *shape,
 }
 
 deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
-                                  int64_t t1, const deltakv_cache *cache, void *stream) {
+                                  int64_t t1, deltakv_cache *cache, void *stream) {
     dk::Dims dm;
     dk::CacheArgs ca;
     deltakv_status st = check_shape(shape, &dm);
@@ -263,13 +274,19 @@ deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int
     if (!x) return fail(DELTAKV_ERR_INVALID_ARG, "x is NULL");
     if (!aligned16(x)) return fail(DELTAKV_ERR_INVALID_ARG, "x must be 16-byte aligned");
     if ((st = check_cache(cache, dm, "cache", false, &ca)) != DELTAKV_OK) return st;
-    return from_hip(dk::launch_build_refs(dm, x, t0, t1, ca, (hipStream_t)stream),
-                    "deltakv_build_refs");
+    if (t0 != cache->n_built)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "references are built in order: t0 (%lld) must equal n_built (%lld)",
+                    (long long)t0, (long long)cache->n_built);
+    st = from_hip(dk::launch_build_refs(dm, x, t0, t1, ca, (hipStream_t)stream),
+                  "deltakv_build_refs");
+    if (st == DELTAKV_OK) cache->n_built = t1;
+    return st;
 }
 
 deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64_t t0,
                                 int64_t t1, const deltakv_mlp *compressor,
-                                const deltakv_cache *cache, void *workspace,
+                                deltakv_cache *cache, void *workspace,
                                 size_t workspace_bytes, uint32_t *stats, void *stream) {
     dk::Dims dm;
     dk::CacheArgs ca;
@@ -284,16 +301,29 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: compressor must have hidden width "
                     "128 or 256");
     if ((st = check_cache(cache, dm, "cache", true, &ca)) != DELTAKV_OK) return st;
+    if (t0 != cache->n_compressed)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "tokens are compressed in order: t0 (%lld) must equal n_compressed (%lld)",
+                    (long long)t0, (long long)cache->n_compressed);
+    if (t1 > cache->n_built)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "compressing up to %lld needs the references built that far (n_built %lld)",
+                    (long long)t1, (long long)cache->n_built);
     const size_t need = dk::compress_ws_bytes(dm, t0, t1);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(DELTAKV_ERR_WORKSPACE, "compress needs %zu workspace bytes, got %zu", need,
                     workspace_bytes);
     if (workspace && !aligned16(workspace))
         return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    if (dk::toks_upto(t1, dm.s) == dk::toks_upto(t0, dm.s)) return ok();  // only references
-    return from_hip(dk::launch_compress(dm, x, t0, t1, ma, ca, workspace, workspace_bytes, stats,
-                                        (hipStream_t)stream),
-                    "deltakv_compress");
+    if (dk::toks_upto(t1, dm.s) == dk::toks_upto(t0, dm.s)) {  // only references
+        cache->n_compressed = t1;
+        return ok();
+    }
+    st = from_hip(dk::launch_compress(dm, x, t0, t1, ma, ca, workspace, workspace_bytes, stats,
+                                      (hipStream_t)stream),
+                  "deltakv_compress");
+    if (st == DELTAKV_OK) cache->n_compressed = t1;
+    return st;
 }
 
 deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
@@ -325,8 +355,8 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
     if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
                     "decompressors of one hidden width, 128 or 256");
-    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
-    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_ws_bytes(dm, num_q_heads, n_tokens);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(DELTAKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
@@ -368,8 +398,8 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
     if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
                     "decompressors of one hidden width, 128 or 256");
-    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
-    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_sparse_ws_bytes(dm, num_q_heads, n_tokens, n_sel);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "sparse decode needs %zu workspace bytes, got %zu",
@@ -411,8 +441,8 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
     if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
                     "decompressors of one hidden width, 128 or 256");
-    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
-    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_select_ws_bytes(dm, num_q_heads, n_tokens);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "decode with selection needs %zu workspace bytes, "
@@ -453,8 +483,8 @@ deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t nu
     if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
                     "decompressors of one hidden width, 128 or 256");
-    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
-    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_window_ws_bytes(dm, num_q_heads, n_tokens, n_win);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "decode with a window needs %zu workspace bytes, "
@@ -468,7 +498,8 @@ deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t nu
 }
 
 deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t num_q_heads,
-                                          const int64_t *lengths, const void *q,
+                                          const int64_t *lengths, int64_t max_tokens,
+                                          const void *q,
                                           const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
                                           const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
                                           float softmax_scale, float *out, void *workspace,
@@ -479,18 +510,13 @@ deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t nu
     deltakv_status st = check_shape(shape, &dm);
     if (st != DELTAKV_OK) return st;
     if (!lengths) return fail(DELTAKV_ERR_INVALID_ARG, "lengths is NULL");
-    int64_t nmax = 0;
-    for (int b = 0; b < dm.B; ++b) {
-        if (lengths[b] < 1 || lengths[b] > dm.cap)
-            return fail(lengths[b] > dm.cap ? DELTAKV_ERR_CAPACITY : DELTAKV_ERR_INVALID_ARG,
-                        "lengths[%d] = %lld not in [1, capacity %lld]", b,
-                        (long long)lengths[b], (long long)dm.cap);
-        nmax = std::max(nmax, lengths[b]);
-    }
-    if ((st = check_heads_tokens(dm, num_q_heads, nmax)) != DELTAKV_OK) return st;
-    if (nmax > DELTAKV_MAX_SPARSE_SELECT)
-        return fail(DELTAKV_ERR_UNSUPPORTED, "longest sequence %lld above %d", (long long)nmax,
+    if (reinterpret_cast<uintptr_t>(lengths) & 7u)
+        return fail(DELTAKV_ERR_INVALID_ARG, "lengths must be 8-byte aligned");
+    if ((st = check_heads_tokens(dm, num_q_heads, max_tokens)) != DELTAKV_OK) return st;
+    if (max_tokens > DELTAKV_MAX_SPARSE_SELECT)
+        return fail(DELTAKV_ERR_UNSUPPORTED, "max_tokens %lld above %d", (long long)max_tokens,
                     DELTAKV_MAX_SPARSE_SELECT);
+    const int64_t nmax = max_tokens;
     if (!q || !out) return fail(DELTAKV_ERR_INVALID_ARG, "q / out is NULL");
     if (!aligned16(q) || !aligned16(out))
         return fail(DELTAKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
@@ -501,8 +527,10 @@ deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t nu
     if (dm.lat_fmt && !dk::decode_q4_supported(dm, km, vm))
         return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: decode needs k 4 or 8 and GELU "
                     "decompressors of one hidden width, 128 or 256");
-    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc)) != DELTAKV_OK) return st;
-    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc)) != DELTAKV_OK) return st;
+    if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, max_tokens)) != DELTAKV_OK)
+        return st;
+    if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, max_tokens)) != DELTAKV_OK)
+        return st;
     const size_t need = dk::decode_varlen_ws_bytes(dm, num_q_heads, nmax);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "mixed-length decode needs %zu workspace bytes, "

@@ -48,6 +48,19 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
     return (bf16_t)(u >> 16);
 }
 
+// The bf16 value nearest to an fp64 value, ties to the even significand,
+// rounded once from fp64 (no intermediate fp32 rounding), returned as fp64:
+// a bf16 value has 8 significant bits and a step of 2^-133 below 2^-126, so
+// x is scaled by a power of two to put its last kept bit at 1, rounded to an
+// integer (round half to even) and scaled back, all exactly.  A result past
+// the largest finite bf16 converts to infinity in fp32 and bf16.
+__device__ __forceinline__ double bf16_grid_f64(double x) {
+    const int ex = (int)((__double_as_longlong(x) >> 52) & 0x7ff);  // biased exponent
+    if (ex == 0x7ff) return x;                                       // inf / NaN
+    const int step = max(ex - 1023 - 7, -133);
+    return ldexp(rint(ldexp(x, -step)), step);
+}
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf2f(v); }
 __device__ __forceinline__ double to_f64(float v) { return (double)v; }

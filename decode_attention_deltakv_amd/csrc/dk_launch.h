@@ -66,9 +66,9 @@ hipError_t launch_decode_window(const Dims &dm, int Hq, int64_t T, const void *q
                                 int64_t n_win, float scale, float *out, void *ws, size_t ws_bytes,
                                 hipStream_t st);
 // decode attention over a batch of sequences of different lengths
-// (lens_host[b] tokens of sequence b, at most nmax), through the sparse decode
+// (lens[b] tokens of sequence b, a device array, clamped into [1, nmax])
 size_t decode_varlen_ws_bytes(const Dims &dm, int Hq, int64_t nmax);
-hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens_host, int64_t nmax,
+hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens, int64_t nmax,
                                 const void *q, const CacheArgs &kc, const MlpArgs &kdec,
                                 const CacheArgs &vc, const MlpArgs &vdec, float scale, float *out,
                                 void *ws, size_t ws_bytes, hipStream_t st);

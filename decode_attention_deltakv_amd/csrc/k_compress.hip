@@ -354,15 +354,17 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
                 zmin = fminf(zmin, __shfl_xor(zmin, o, TPT));
                 zmax = fmaxf(zmax, __shfl_xor(zmax, o, TPT));
             }
-            const float rng = zmax - zmin;
-            const float q = rng * (1.0f / 15.0f);
-            const float scale = __uint_as_float(pack_bf16(q, q) << 16);
-            const float inv = 1.0f / (scale > 0.f ? scale : 1.0f);  // correctly rounded
+            // the format is defined in IEEE fp64: scale = bf16(fl64(fl64(max -
+            // min) / 15)) rounded once from fp64, code = rint(fl64(fl64(z -
+            // min) / scale)) clamped to 0..15 (correctly rounded divisions)
+            const double lo = (double)zmin;
+            const double scale64 = bf16_grid_f64(((double)zmax - lo) / 15.0);
+            const float scale = (float)scale64;  // exact: a bf16 value (or +inf)
             uint32_t nib = 0u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float c = scale > 0.f ? rintf((z[e] - zmin) * inv) : 0.f;
-                c = fminf(fmaxf(c, 0.f), 15.f);
+                double c = scale64 > 0.0 ? rint(((double)z[e] - lo) / scale64) : 0.0;
+                c = fmin(fmax(c, 0.0), 15.0);
                 nib |= (uint32_t)c << (4 * e);
             }
             // lanes j, j + 1 (j even) make one 32-bit word of eight codes

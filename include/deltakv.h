@@ -111,22 +111,40 @@ typedef struct {
  *               nibble, then N 32-bit words holding the row's bf16 shift (low
  *               half) and bf16 scale (high half).  The Compressor output z,
  *               rounded to bf16, is stored as shift = min(z), scale =
- *               bf16((max(z) - min(z)) * fp32(1/15)), code = clamp(rint((z -
- *               shift) * (1 / scale)), 0, 15) in fp32 arithmetic, the
- *               reciprocal correctly rounded (scale 0: codes 0); the decode
- *               reads shift + code * scale.  This is the 4-bit latent
+ *               bf16((max(z) - min(z)) / 15), code = clamp(rint((z - shift) /
+ *               scale), 0, 15), both evaluated in IEEE fp64 (correctly
+ *               rounded subtraction and division, the scale rounded to bf16
+ *               once from fp64, rint taking half-integers to the even code;
+ *               scale 0: codes 0); the decode reads shift + code * scale.
+ *               This is the 4-bit latent
  *               storage that the DeltaKV page's section 5 quotes its memory
  *               figure with; the page gives no format.)
  *   idx         [B][H][N][k]     reference ordinals averaged into KV_R, nearest
  *                                first; 0xFFFF marks an unused slot (a token at
  *                                position p has min(k, ceil(p / s)) candidates)
  * deltakv_cache_bytes gives the byte size of each array.  The caller allocates
- * them; the library reads and writes them in place. */
+ * them; the library reads and writes them in place.
+ *
+ * Filled lengths (host-side, kept in the struct so that the append-only order
+ * of section 3 -- references and compressed tokens grow with the sequence --
+ * is enforced by the library):
+ *   n_built       positions [0, n_built) have had their reference rows built;
+ *   n_compressed  positions [0, n_compressed) have been compressed.
+ * A new cache starts with both 0 (zero-initialise the struct).  Each call
+ * checks them before enqueueing anything and, on success, advances them on
+ * enqueue (not on completion): deltakv_build_refs(t0, t1) needs t0 == n_built
+ * and sets n_built = t1; deltakv_compress(t0, t1) needs t0 == n_compressed
+ * and t1 <= n_built and sets n_compressed = t1; the decode calls read at most
+ * min(n_compressed of the K and V caches) positions.  Always 0 <= n_compressed
+ * <= n_built <= capacity.  To refill the arrays from position 0, set both
+ * back to 0. */
 typedef struct {
     void *refs;
     float *ref_sqnorm;
     void *latents;
     uint16_t *idx;
+    int64_t n_built;       /* host-side filled length: references built */
+    int64_t n_compressed;  /* host-side filled length: tokens compressed */
 } deltakv_cache;
 
 /* Host-only.  Byte sizes of the four cache arrays for `shape` (any output
@@ -149,10 +167,12 @@ deltakv_status deltakv_decode_workspace_bytes(const deltakv_shape *shape, int32_
  * reference position p in [t0, t1), copy the input row into refs[p / s] and
  * store its fp32 squared norm.
  *   x: [B][H][t1 - t0][d], row i holding position t0 + i (read-only).
- * Requires 0 <= t0 < t1 <= capacity.  Streaming callers call it chunk by chunk
- * (t0 = previous t1); one call with t0 = 0, t1 = T builds an offline prefix. */
+ * Requires 0 <= t0 < t1 <= capacity and t0 == cache->n_built (append-only;
+ * INVALID_ARG otherwise); sets cache->n_built = t1.  Streaming callers call it
+ * chunk by chunk (t0 = previous t1); one call with t0 = 0, t1 = T builds an
+ * offline prefix. */
 deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int64_t t0,
-                                  int64_t t1, const deltakv_cache *cache, void *stream);
+                                  int64_t t1, deltakv_cache *cache, void *stream);
 
 /* Compression of the non-reference positions in [t0, t1) (section 3,
  * "Processo di Compressione", steps 1-4):
@@ -163,15 +183,16 @@ deltakv_status deltakv_build_refs(const deltakv_shape *shape, const void *x, int
  *   2. KV_R = mean of those k_eff = min(k, ceil(p / s)) reference rows;
  *   3. residual = x_p - KV_R;
  *   4. latents[q(p)] = compressor(residual).
- * x: as for deltakv_build_refs.  Precondition: deltakv_build_refs has covered
- * positions [0, t1) (earlier chunks included) and its work is ordered before
- * this call on `stream`.  compressor: in_dim = d, out_dim = d_c.
+ * x: as for deltakv_build_refs.  Requires t0 == cache->n_compressed and t1 <=
+ * cache->n_built: the references of every position before t1 were built (by
+ * calls ordered before this one on `stream`); INVALID_ARG otherwise.  Sets
+ * cache->n_compressed = t1.  compressor: in_dim = d, out_dim = d_c.
  * workspace: device scratch of deltakv_compress_workspace_bytes(shape, t0, t1).
  * stats: NULL or a device uint32 to which the number of tokens whose
  * selection needed the exhaustive fallback scan is added atomically. */
 deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64_t t0,
                                 int64_t t1, const deltakv_mlp *compressor,
-                                const deltakv_cache *cache, void *workspace,
+                                deltakv_cache *cache, void *workspace,
                                 size_t workspace_bytes, uint32_t *stats, void *stream);
 
 /* Decode attention over the compressed cache ("Ricostruzione" in section 3,
@@ -183,9 +204,9 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
  *   q:   [B][num_q_heads][d] in shape->dtype;  out: [B][num_q_heads][d] fp32.
  *   k_dec / v_dec: in_dim = d_c, out_dim = d.
  * num_q_heads must be a multiple of H with num_q_heads / H <= 8; 1 <= n_tokens
- * <= capacity and every position < n_tokens must have been built and
- * compressed.  workspace: deltakv_decode_workspace_bytes(shape, num_q_heads,
- * n_tokens) bytes. */
+ * <= capacity (CAPACITY otherwise) and n_tokens <= the n_compressed of both
+ * caches (INVALID_ARG otherwise).  workspace:
+ * deltakv_decode_workspace_bytes(shape, num_q_heads, n_tokens) bytes. */
 deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
                                    int64_t n_tokens, const void *q,
                                    const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
@@ -262,15 +283,21 @@ deltakv_status deltakv_decode_varlen_workspace_bytes(const deltakv_shape *shape,
 /* Decode attention over a batch whose sequences hold different numbers of
  * tokens (a serving batch of mixed lengths): sequence b attends its positions
  * 0 .. lengths[b] - 1, each rebuilt as deltakv_decode_attn rebuilds it.
- *   lengths: HOST int64 [B], 1 <= lengths[b] <= capacity, read during the
- *            call (copied to the workspace on `stream`).
+ *   lengths:    DEVICE int64 [B], read by the kernels (so the call can be
+ *               captured in a graph and replayed with new lengths), each in
+ *               [1, max_tokens]; a value outside is clamped into that range
+ *               (the result is then the one for the clamped length), so no
+ *               read leaves the cache.
+ *   max_tokens: host, an upper bound of every length; 1 <= max_tokens <=
+ *               the n_compressed of both caches and <= capacity.  The launch
+ *               plan is sized for it.
  * Positions at or past a sequence's length may hold anything.  Other
- * arguments as for deltakv_decode_attn; max(lengths) <=
+ * arguments as for deltakv_decode_attn; max_tokens <=
  * DELTAKV_MAX_SPARSE_SELECT; workspace: deltakv_decode_varlen_workspace_bytes
- * with max_tokens = max(lengths).  (Runs as the sparse decode over every
- * position below each sequence's length.) */
+ * with the same max_tokens. */
 deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t num_q_heads,
-                                          const int64_t *lengths, const void *q,
+                                          const int64_t *lengths, int64_t max_tokens,
+                                          const void *q,
                                           const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
                                           const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
                                           float softmax_scale, float *out, void *workspace,

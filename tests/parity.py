@@ -131,3 +131,46 @@ def oracle_decode_head(shape, T, q_rows, kc, vc, b, h, kdec_o, vdec_o, scale):
     kr, kl, ki = grab(kc)
     vr, vl, vi = grab(vc)
     return oracle.decode_head(q_rows, kr, kl, ki, kdec_o, vr, vl, vi, vdec_o, T, s, scale)
+
+
+def check_selection(scores_g, kept_g, mass_o, n_keep, eps):
+    """The selection of one (sequence, KV head) against the oracle's attention
+    masses mass_o [T] (fp64, rebuilt keys):
+      - scores, position by position: |g_p - o_p| <= eps * max(o_p, floor),
+        floor = 1e-3 * tau, tau = the oracle's n_keep-th largest mass (the
+        selection threshold), so every position near the cut is held to the
+        relative bound;
+      - the kept positions are a valid top n_keep of the oracle's masses up to
+        that bound: with e_p = eps * max(o_p, floor), a kept p and a dropped
+        p' can be in the wrong order only if o_p + e_p >= o_p' - e_p', which
+        bounds every kept o_p >= tau (1 - 3 eps) - 2 eps floor and every
+        dropped o_p <= tau (1 + 3 eps) + 2 eps floor.
+    Returns (largest per-position relative error, positions kept by exactly
+    one of the two sides)."""
+    o = np.asarray(mass_o, np.float64)
+    g = np.asarray(scores_g, np.float64)
+    T = len(o)
+    kept = np.asarray(kept_g)
+    kept = kept[kept >= 0]
+    tau = np.sort(o)[::-1][min(n_keep, T) - 1]
+    floor = 1e-3 * tau
+    den = np.maximum(o, floor)
+    rel = np.abs(g - o) / den
+    worst = float(rel.max())
+    assert worst <= eps, (f"score at position {int(rel.argmax())}: gpu {g[rel.argmax()]:.6e} "
+                          f"oracle {o[rel.argmax()]:.6e} (rel {worst:.3e} > {eps})")
+    if n_keep >= T:
+        assert np.array_equal(np.sort(kept), np.arange(T)), "n_keep >= T must keep everything"
+        return worst, 0
+    assert len(kept) == n_keep and len(np.unique(kept)) == n_keep
+    mask = np.zeros(T, bool)
+    mask[kept] = True
+    lo = tau * (1 - 3 * eps) - 2 * eps * floor
+    hi = tau * (1 + 3 * eps) + 2 * eps * floor
+    assert o[mask].min() >= lo, f"kept position with oracle mass {o[mask].min():.6e} < {lo:.6e}"
+    if (~mask).any():
+        assert o[~mask].max() <= hi, (f"dropped position with oracle mass {o[~mask].max():.6e} "
+                                      f"> {hi:.6e}")
+    ref = np.zeros(T, bool)
+    ref[np.lexsort((np.arange(T), -o))[:n_keep]] = True
+    return worst, int((mask != ref).sum())

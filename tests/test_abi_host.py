@@ -110,9 +110,12 @@ class _FakePtr:
         return 1
 
 
-def _cache(addr=0x10000):
+def _cache(addr=0x10000, filled=4096):
+    """A cache stand-in whose first `filled` positions count as built and
+    compressed (the decode calls read at most that many)."""
     c = dk.Cache.__new__(dk.Cache)
     c.refs = c.ref_sqnorm = c.latents = c.idx = _FakePtr(addr)
+    c.n_built = c.n_compressed = filled
     return c
 
 
@@ -135,11 +138,70 @@ def test_range_and_pointer_errors_return_before_any_launch():
         dk.build_refs(sh, _FakePtr(0x10008), 0, 16, _cache())   # misaligned x
     assert e.value.status == 1
     with pytest.raises(dk.DeltaKVError) as e:
-        dk.compress(sh, x, 0, 16, _mlp(128, 256, 16), _cache(), None)  # wrong d_c
+        dk.compress(sh, x, 0, 16, _mlp(128, 256, 16), _cache(filled=0), None)  # wrong d_c
     assert e.value.status == 1
     with pytest.raises(dk.DeltaKVError) as e:
-        dk.compress(sh, x, 0, 16, _mlp(128, 100, 32), _cache(), None)  # hidden 100
+        dk.compress(sh, x, 0, 16, _mlp(128, 100, 32), _cache(filled=0), None)  # hidden 100
     assert e.value.status == 2
+
+
+def _fresh(n_built=0, n_compressed=0):
+    c = _cache(filled=0)
+    c.n_built, c.n_compressed = n_built, n_compressed
+    return c
+
+
+def test_build_refs_is_append_only():
+    # references are built in order: t0 must be the filled length, which the
+    # library advances only on success
+    sh = _shape(capacity=4096)
+    x = _FakePtr()
+    for c, t0 in ((_fresh(), 16), (_fresh(64, 64), 0), (_fresh(64, 64), 128)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.build_refs(sh, x, t0, t0 + 16, c)
+        assert e.value.status == 1 and "n_built" in e.value.detail
+        assert c.n_built in (0, 64)
+    with pytest.raises(dk.DeltaKVError) as e:     # inconsistent filled lengths
+        dk.build_refs(sh, x, 64, 80, _fresh(64, 65))
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.build_refs(sh, x, 4097, 4098, _fresh(4097, 0))
+    assert e.value.status in (1, 3)
+
+
+def test_compress_needs_built_references_and_the_next_range():
+    sh = _shape(capacity=4096)
+    x = _FakePtr()
+    ws = _FakePtr(0x30000, 1 << 30)
+    comp = _mlp(128, 256, 32)
+    # positions whose references were never built
+    c = _fresh(n_built=1024, n_compressed=0)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.compress(sh, x, 0, 2048, comp, c, ws)
+    assert e.value.status == 1 and "n_built" in e.value.detail
+    assert c.n_compressed == 0
+    # a range that does not start at the compressed length (a gap, or a redo)
+    for t0 in (512, 0):
+        c = _fresh(n_built=2048, n_compressed=256)
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.compress(sh, x, t0, 1024, comp, c, ws)
+        assert e.value.status == 1 and "n_compressed" in e.value.detail
+        assert c.n_compressed == 256
+    # a range of references only: nothing to compute, the length still advances
+    c = _fresh(n_built=33, n_compressed=32)
+    dk.compress(sh, x, 32, 33, comp, c, ws)
+    assert c.n_compressed == 33
+
+
+def test_decode_reads_only_compressed_positions():
+    sh = _shape(capacity=4096)
+    dec = _mlp(32, 256, 128)
+    ws = _FakePtr(0x30000, 1 << 30)
+    for kf, vf in ((4095, 4096), (4096, 1000)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.decode_attn(sh, 32, 4096, _FakePtr(), _cache(filled=kf), dec, _cache(filled=vf),
+                           dec, 0.088, _FakePtr(), ws)
+        assert e.value.status == 1 and "compressed" in e.value.detail
 
 
 def test_workspace_too_small_is_reported():
@@ -298,16 +360,37 @@ def test_window_argument_errors_return_before_any_launch():
     assert e.value.status == 4
 
 
+class _FakeLens(_FakePtr):
+    """An int64 [B] device length array stand-in."""
+
+    def __init__(self, addr=0x80000):
+        super().__init__(addr, 8 * 3)
+        import torch
+        self.dtype = torch.int64
+
+
 def test_varlen_length_errors_return_before_any_launch():
     sh = _shape(capacity=4096, batch=3)
     dec = _mlp(32, 256, 128)
     need = dk.decode_varlen_workspace_bytes(sh, 32, 4096)
-    for bad, status in (((10, 0, 5), 1), ((10, 4097, 5), 3)):
+
+    def call(lens, max_tokens, ws=_FakePtr(0x30000, need), filled=4096):
+        dk.decode_attn_varlen(sh, 32, lens, max_tokens, _FakePtr(), _cache(filled=filled), dec,
+                              _cache(filled=filled), dec, 0.088, _FakePtr(), ws)
+
+    for max_tokens, status in ((0, 1), (4097, 3)):
         with pytest.raises(dk.DeltaKVError) as e:
-            dk.decode_attn_varlen(sh, 32, bad, _FakePtr(), _cache(), dec, _cache(), dec, 0.088,
-                                  _FakePtr(), _FakePtr(0x30000, need))
+            call(_FakeLens(), max_tokens)
         assert e.value.status == status
     with pytest.raises(dk.DeltaKVError) as e:
-        dk.decode_attn_varlen(sh, 32, (10, 4096, 5), _FakePtr(), _cache(), dec, _cache(), dec,
-                              0.088, _FakePtr(), _FakePtr(0x30000, need - 1))
+        call(None, 4096)
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakeLens(0x80004), 4096)                  # misaligned lengths
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakeLens(), 4096, filled=4000)            # past the compressed length
+    assert e.value.status == 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        call(_FakeLens(), 4096, ws=_FakePtr(0x30000, need - 1))
     assert e.value.status == 4

@@ -4,7 +4,8 @@ scale) against the CPU oracle.
   - The same inputs are compressed twice, with latents stored in bf16 and in
     4 bits: the index lists must be identical, and the 4-bit codes, shifts and
     scales must equal, bit for bit, the oracle's quantisation of the bf16 run's
-    latents (both sides quantise the same bf16 values in fp32 arithmetic).
+    latents (both sides quantise the same bf16 values by the format's fp64
+    definition: integer codes decided in the same precision on both sides).
   - Decode (dense, sparse and with selection) over the 4-bit cache must match
     the oracle's attention over the dequantised latents within the bf16
     tolerance (2e-2).
@@ -18,8 +19,8 @@ import torch
 import decode_attention_deltakv_amd as dk
 import oracle
 from deltakv_synth import queries
-from parity import (TOL, gpu_compress, gpu_mlp, idx_to_oracle, make_kv, make_mlp, oracle_mlp,
-                    rel_err_rows, say, to_np)
+from parity import (TOL, check_selection, gpu_compress, gpu_mlp, idx_to_oracle, make_kv,
+                    make_mlp, oracle_mlp, rel_err_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -150,7 +151,8 @@ def test_q4_decode_dense_sparse_and_select_match_oracle(cfg):
                                                                    vo, T, s, scale)))
             assert np.array_equal(pos[b, h], oracle.top_positions(sc[b, h], n_keep))
             _, mass = oracle.select_head(qo, kr, kl, ki, ko, T, s, scale, n_keep)
-            e_sc = max(e_sc, rel_err_rows(sc[b, h], mass))
+            e_sc = max(e_sc, check_selection(sc[b, h], pos[b, h], mass, n_keep,
+                                             TOL[dk.BF16])[0])
             e_sp = max(e_sp, rel_err_rows(out_sp[b, h * G:(h + 1) * G],
                                           oracle.decode_head_sparse(qo, kr, kl, ki, ko, vr, vl, vi,
                                                                     vo, T, s, scale, pos[b, h])))
