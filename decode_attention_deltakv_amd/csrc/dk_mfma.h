@@ -150,4 +150,31 @@ __device__ __forceinline__ void gelu4_f16(float a, float b, float c, float d, f1
     r1 = u1 * phi1;
 }
 
+// Two GELU pairs with a shorter polynomial: Phi(u) ~= clamp01(0.5 + u *
+// Q2(u * u)) with Q2 of degree 2 (minimax fit of the clamped form over the
+// real line, |u| <= 2.63 fitted, beyond it the positive leading coefficient
+// saturates Phi).  Largest error of Phi below 4.3e-3 before f16 rounding and
+// 5.2e-3 after it; of GELU below 5.5e-3 * max(1, |u|).  6 packed instructions
+// per pair.  Used for the value-side hidden units, whose errors enter the
+// output linearly (the scores, which are exponentiated, keep gelu4_f16).
+__device__ __forceinline__ void gelu4_f16_short(float a, float b, float c, float d, f16x2 &r0,
+                                                f16x2 &r1) {
+    const f16x2 u0 = pack_f16(a, b), u1 = pack_f16(c, d);
+    const f16x2 half = {(_Float16)0.5f, (_Float16)0.5f};
+    const f16x2 c2 = {(_Float16)2.95325e-03f, (_Float16)2.95325e-03f};
+    const f16x2 c1 = {(_Float16)-4.881304e-02f, (_Float16)-4.881304e-02f};
+    const f16x2 c0 = {(_Float16)3.8647556e-01f, (_Float16)3.8647556e-01f};
+    const f16x2 t0 = u0 * u0, t1 = u1 * u1;
+    f16x2 p0 = __builtin_elementwise_fma(c2, t0, c1);
+    f16x2 p1 = __builtin_elementwise_fma(c2, t1, c1);
+    p0 = __builtin_elementwise_fma(p0, t0, c0);
+    p1 = __builtin_elementwise_fma(p1, t1, c0);
+    f16x2 phi0, phi1;
+    asm("v_pk_fma_f16 %0, %2, %3, %6 clamp\n\tv_pk_fma_f16 %1, %4, %5, %6 clamp"
+        : "=&v"(phi0), "=v"(phi1)
+        : "v"(u0), "v"(p0), "v"(u1), "v"(p1), "v"(half));
+    r0 = u0 * phi0;
+    r1 = u1 * phi1;
+}
+
 }  // namespace dk

@@ -1493,10 +1493,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int64_t Rt_u = (SP || cmode) ? (int64_t)scnt[2 * unit + 1] : Rt;
     __shared__ int32_t ordl[SP ? kSpTiles * 32 : 1];
 
-    if (pidx >= Ptok) {
-        // ---------------- reference tokens ----------------
-        // score scale * qR[j], value = the stored row.  Tiles of 32 references,
-        // rows straight to LDS; the four waves split the value columns.
+    // ---------------- reference tokens ----------------
+    // Reference partition r: rows [r kRefPart, (r + 1) kRefPart) of the unit,
+    // record rec.  Score scale * qR[j], value = the stored row.  Tiles of 32
+    // references, rows straight to LDS; the four waves split the value columns.
+    auto ref_part = [&](int r, float *rec) {
         constexpr int NR = D / 64;
         const int sg = tid >> 5, st = tid & 31;
         const bool sg_ok = sg < G;
@@ -1506,7 +1507,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         f32x4 acc[NR];
 #pragma unroll
         for (int n = 0; n < NR; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int64_t ja = (int64_t)(pidx - Ptok) * kRefPart;
+        const int64_t ja = (int64_t)r * kRefPart;
         const int64_t je = min(Rt_u, ja + kRefPart);
         for (int64_t j0 = ja; j0 < je; j0 += TT) {
             __syncthreads();
@@ -1564,20 +1565,23 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
         }
         if (sg_ok && st == 0) {
-            prec[(int64_t)sg * kPStride + 0] = m_run;
-            prec[(int64_t)sg * kPStride + 1] = l_run;
-            prec[(int64_t)sg * kPStride + 2] = 0.f;
+            rec[(int64_t)sg * kPStride + 0] = m_run;
+            rec[(int64_t)sg * kPStride + 1] = l_run;
+            rec[(int64_t)sg * kPStride + 2] = 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int g = 4 * lq + r;
+        for (int rr = 0; rr < 4; ++rr) {
+            const int g = 4 * lq + rr;
             if (g >= G) continue;
-            float *pg = prec + (int64_t)g * kPStride;
+            float *pg = rec + (int64_t)g * kPStride;
 #pragma unroll
             for (int n = 0; n < HID / 64; ++n) pg[4 + kMaxD + w * (HID / 4) + 16 * n + l16] = 0.f;
 #pragma unroll
-            for (int n = 0; n < NR; ++n) pg[4 + cbase + 16 * n + l16] = acc[n][r];
+            for (int n = 0; n < NR; ++n) pg[4 + cbase + 16 * n + l16] = acc[n][rr];
         }
+    };
+    if (pidx >= Ptok) {
+        ref_part(pidx - Ptok, prec);
         return;
     }
 
@@ -1670,63 +1674,76 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             l_run[e] = 0.f;
         }
 
+        // a tile's inputs: the token's latent row and index rows, and the
+        // q.R^K table entries of its K references with their count.  Three
+        // slots rotate: the rows of tile i + 2 are requested while tile i is
+        // computed and the table entries of tile i + 1 (whose index rows are
+        // in by then), so no load of a tile waits inside that tile.
         struct KIn {
             bf16x8 z;
             IdxV ik, iv;
+            float qv[EG][KX];
+            float kek;
         };
-        // inputs of token (t0 + 16 src + l16), clamped to a stored token
+        // rows of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = tok_of(t0 + TH * src + l16);
             in.z = zrow(klat_u, kq_u, tok);
             in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
             in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
         };
-
-        // one tile: scores, softmax, publish into slot (it & 1); the inputs of
-        // tile (nt0) are loaded into `nxt` once this tile's table reads are out
-        auto ktile = [&](int it, int t0, const KIn &in, int nt0, KIn &nxt) {
-            const int sl = it & 1;
-            uint32_t jk[KX];
-#pragma unroll
-            for (int i = 0; i < KX; ++i) {
-                const uint32_t wv = in.ik[i >> 1];
-                jk[i] = (i & 1) ? (wv >> 16) : (wv & 0xffffu);
-            }
-            // q.R^K of the token's references for the lane's heads (unused
-            // slots read the all-zero row Rt)
-            float qv[EG][KX];
+        // q.R^K of the token's references for the lane's heads (unused slots
+        // read the all-zero row Rt)
+        auto qload = [&](KIn &in) {
             float kek = 0.f;
 #pragma unroll
             for (int i = 0; i < KX; ++i) {
-                const bool ok = jk[i] != kIdxUnused;
+                const uint32_t wv = in.ik[i >> 1];
+                const uint32_t j = (i & 1) ? (wv >> 16) : (wv & 0xffffu);
+                const bool ok = j != kIdxUnused;
                 kek += ok ? 1.f : 0.f;
-                const uint32_t row = (ok ? jk[i] : (uint32_t)Rt) * (uint32_t)GQ;
+                const uint32_t row = (ok ? j : (uint32_t)Rt) * (uint32_t)GQ;
 #pragma unroll
                 for (int e = 0; e < EG; ++e)
-                    qv[e][i] = *at_byte(qr_u, (row + (uint32_t)min(gh[e], GQ - 1)) * 4u);
+                    in.qv[e][i] = *at_byte(qr_u, (row + (uint32_t)min(gh[e], GQ - 1)) * 4u);
             }
-            // the next tile's loads go out after these table reads, so waiting
-            // for the table does not wait for them; they are issued on every
-            // tile (past the range they read a clamped, stored token) so the
-            // wait count does not depend on a branch
-            __builtin_amdgcn_sched_barrier(0);
-            kload(nt0, nxt);
-            __builtin_amdgcn_sched_barrier(0);
+            in.kek = kek;
+        };
+
+        // one tile: scores, softmax, publish into slot (it & 1).  Also starts
+        // the table reads of the next tile (n1, whose rows are in) and the row
+        // loads of the tile after it (into n2, at token t2).
+        // (4-bit latents with k = 8 read the table at the start of the tile
+        // itself: a table slot per ring entry would not fit the registers)
+        constexpr bool QPRE = !(Q4 && KX == 8);
+        auto ktile = [&](int it, int t0, KIn &in, KIn &n1, int t2, KIn &n2) {
+            const int sl = it & 1;
+            if constexpr (QPRE) qload(n1);
+            else qload(in);
+            kload(t2, n2);
             // hidden tile and partial scores, 32 hidden units per step; the
-            // products of step j + 1 are issued before the GELU of step j
+            // products of step j + 1 are issued before the GELU of step j, and
+            // the bias rows of step j + 2 are read from LDS before that
             f32x4 S = {0.f, 0.f, 0.f, 0.f};
-            auto hstep = [&](int j, f32x4 &c0, f32x4 &c1) {
-                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 4 * lq]);
-                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 16 + 4 * lq]);
-                c0 = mfma16_bf16(wK[2 * j], in.z, b0);
-                c1 = mfma16_bf16(wK[2 * j + 1], in.z, b1);
+            auto bload = [&](int j, f32x4 &b0, f32x4 &b1) {
+                b0 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 4 * lq]);
+                b1 = *reinterpret_cast<const f32x4 *>(&biask[32 * j + 16 + 4 * lq]);
             };
-            f32x4 cn0, cn1;
-            hstep(0, cn0, cn1);
+            f32x4 bn0, bn1, bm0, bm1;
+            bload(0, bn0, bn1);
+            if (KJ > 1) bload(1, bm0, bm1);
+            f32x4 cn0 = mfma16_bf16(wK[0], in.z, bn0);
+            f32x4 cn1 = mfma16_bf16(wK[1], in.z, bn1);
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
                 const f32x4 c0 = cn0, c1 = cn1;
-                if (j + 1 < KJ) hstep(j + 1, cn0, cn1);
+                if (j + 1 < KJ) {
+                    bn0 = bm0;
+                    bn1 = bm1;
+                    if (j + 2 < KJ) bload(j + 2, bm0, bm1);
+                    cn0 = mfma16_bf16(wK[2 * (j + 1)], in.z, bn0);
+                    cn1 = mfma16_bf16(wK[2 * (j + 1) + 1], in.z, bn1);
+                }
                 f16x2 g0, g1, g2, g3;
                 gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
                 gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
@@ -1745,13 +1762,14 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 sv[e] = lq == 0 ? x0 : lq == 1 ? x1 : lq == 2 ? x2 : x3;
             }
             const bool tok_ok = t0 + TH * src + l16 < qe;
-            const float inv_k = __builtin_amdgcn_rcpf(kek);
+            const float inv_k = __builtin_amdgcn_rcpf(in.kek);
             float s[EG], mref[EG];
             bool up = false;
 #pragma unroll
             for (int e = 0; e < EG; ++e) {
-                float rs = (qv[e][0] + qv[e][1]) + (qv[e][2] + qv[e][3]);
-                if constexpr (KX == 8) rs += (qv[e][4] + qv[e][5]) + (qv[e][6] + qv[e][7]);
+                float rs = (in.qv[e][0] + in.qv[e][1]) + (in.qv[e][2] + in.qv[e][3]);
+                if constexpr (KX == 8)
+                    rs += (in.qv[e][4] + in.qv[e][5]) + (in.qv[e][6] + in.qv[e][7]);
                 const float v = scale * (sv[e] + rs * inv_k + cqv[e]);
                 s[e] = (tok_ok && gh[e] < G) ? v : -INFINITY;
                 if (!SP && logc && tok_ok && gh[e] < G)
@@ -1811,9 +1829,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
         };
 
-        KIn X0, X1;
+        KIn X0, X1, X2;
         kload(qa, X0);
-        ktile(0, qa, X0, qa + TT, X1);
+        kload(qa + TT, X1);
+        if constexpr (QPRE) qload(X0);
+        ktile(0, qa, X0, X1, qa + 2 * TT, X2);
         __syncthreads();
         // the value waves' barriers of a tile: one at k = 4, two at k = 8
         // (mid-tile, once the tile's rows are gathered, and end of tile)
@@ -1821,13 +1841,19 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             __syncthreads();
             if constexpr (KX == 8) __syncthreads();
         };
-        for (int it = 0; it < ntile; it += 2) {
-            if (it + 1 < ntile) ktile(it + 1, qa + (it + 1) * TT, X1, qa + (it + 2) * TT, X0);
+        // tiles 1, 2, 3, ... with the slots rotating (tile i in slot i % 3)
+        for (int it = 1; it < ntile; it += 3) {
+            ktile(it, qa + it * TT, X1, X2, qa + (it + 2) * TT, X0);
             tile_sync();
             if (it + 1 >= ntile) break;
-            if (it + 2 < ntile) ktile(it + 2, qa + (it + 2) * TT, X0, qa + (it + 3) * TT, X1);
+            ktile(it + 1, qa + (it + 1) * TT, X2, X0, qa + (it + 3) * TT, X1);
+            tile_sync();
+            if (it + 2 >= ntile) break;
+            ktile(it + 2, qa + (it + 2) * TT, X0, X1, qa + (it + 4) * TT, X2);
             tile_sync();
         }
+        // the value waves run one tile behind: their last tile's barrier
+        tile_sync();
         // per-head sums of this wave's tokens
 #pragma unroll
         for (int e = 0; e < EG; ++e) {
@@ -1928,17 +1954,34 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         auto vbody = [&](auto kScl, const bf16x8 (&zv)[2], bf16_t (*cur)[D], const f16x4 (&pa)[2],
                          float es0, float es1, int sl) {
             constexpr bool SCL = decltype(kScl)::value;
+            const f16x8 pa8 = {pa[0][0], pa[0][1], pa[0][2], pa[0][3],
+                               pa[1][0], pa[1][1], pa[1][2], pa[1][3]};
             u32x4 pv = {0u, 0u, 0u, 0u};
             // reference-row step q: rows 64 s2 + 32 ks + 8 lq of score wave
-            // s2's tokens, value columns block nc
-            // reference steps spread over the hidden blocks (k = 4: score wave
-            // s2, half ks, block nc; k = 8 takes them after a barrier instead)
+            // s2's tokens, value columns block nc; the steps are spread over
+            // the hidden blocks (k = 4: score wave s2, half ks, block nc; k = 8
+            // takes them after a barrier instead).  The LDS operands of a
+            // block's steps are read one hidden block ahead (rread), so the
+            // products (rmma) do not wait for the transposing reads.
             constexpr int NQ = KX == 4 ? 4 * NC : 0;
-            auto rstep = [&](int q) {
+            constexpr int QPB = NQ / NBV;   // steps per hidden block
+            struct RIn {
+                u32x4 bv, pw;
+            };
+            auto rread = [&](int q, RIn &r) {
                 const int s2 = q / (2 * NC), ks = (q / NC) & 1, nc = q % NC;
                 const int rb = 64 * s2 + 32 * ks + 8 * lq;
+                if (nc == 0) r.pw = *reinterpret_cast<const u32x4 *>(&wr[sl][l16][rb]);
+                const int c = cb + 16 * nc + 4 * (l16 & 3);
+                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
+                const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
+                const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
+                r.bv = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            };
+            auto rmma = [&](int q, const RIn &r) {
+                const int s2 = q / (2 * NC), nc = q % NC;
                 if (nc == 0) {
-                    pv = *reinterpret_cast<const u32x4 *>(&wr[sl][l16][rb]);
+                    pv = r.pw;
                     if constexpr (SCL) {
                         const float es = s2 ? es1 : es0;
 #pragma unroll
@@ -1947,13 +1990,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                                               __uint_as_float(pv[e] & 0xffff0000u) * es);
                     }
                 }
-                const int c = cb + 16 * nc + 4 * (l16 & 3);
-                const int pcol = (((c >> 3) ^ (2 * (l16 >> 2))) << 3) | (c & 7);
-                const u32x2 lo = lds_read_tr16(&cur[rb + (l16 >> 2)][pcol]);
-                const u32x2 hi = lds_read_tr16(&cur[rb + 4 + (l16 >> 2)][pcol]);
-                const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
-                acc_r[nc] = mfma16_bf16(as_bf16x8(pv), as_bf16x8(bv), acc_r[nc]);
+                acc_r[nc] = mfma16_bf16(as_bf16x8(pv), as_bf16x8(r.bv), acc_r[nc]);
             };
+            RIn rc[QPB > 0 ? QPB : 1], rn[QPB > 0 ? QPB : 1];
+#pragma unroll
+            for (int i = 0; i < QPB; ++i) rread(i, rc[i]);
             f32x4 hn0 = mfma16_bf16(zv[0], wV[0], bV[0]);
             f32x4 hn1 = mfma16_bf16(zv[1], wV[0], bV[0]);
 #pragma unroll
@@ -1962,16 +2003,22 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 if (nb + 1 < NBV) {
                     hn0 = mfma16_bf16(zv[0], wV[nb + 1], bV[nb + 1]);
                     hn1 = mfma16_bf16(zv[1], wV[nb + 1], bV[nb + 1]);
+#pragma unroll
+                    for (int i = 0; i < QPB; ++i) rread(QPB * (nb + 1) + i, rn[i]);
                 }
                 f16x2 g0, g1, g2, g3;
-                gelu4_f16(c0[0], c0[1], c0[2], c0[3], g0, g1);
-                gelu4_f16(c1[0], c1[1], c1[2], c1[3], g2, g3);
-                const u32x2 h0 = {as_u32(g0), as_u32(g1)};
-                const u32x2 h1 = {as_u32(g2), as_u32(g3)};
-                acc_h[nb] = mfma16k16_f16(pa[0], __builtin_bit_cast(f16x4, h0), acc_h[nb]);
-                acc_h[nb] = mfma16k16_f16(pa[1], __builtin_bit_cast(f16x4, h1), acc_h[nb]);
+                gelu4_f16_short(c0[0], c0[1], c0[2], c0[3], g0, g1);
+                gelu4_f16_short(c1[0], c1[1], c1[2], c1[3], g2, g3);
+                // one 32-token product: K index 8 lq + i is token 4 lq + i of
+                // the first score wave's 16 (i < 4) or of the second's (i >= 4),
+                // the order in which pa8 holds the weights
+                const u32x4 hh = {as_u32(g0), as_u32(g1), as_u32(g2), as_u32(g3)};
+                acc_h[nb] = mfma16_f16(pa8, as_f16x8(hh), acc_h[nb]);
 #pragma unroll
-                for (int q = NQ * nb / NBV; q < NQ * (nb + 1) / NBV; ++q) rstep(q);
+                for (int i = 0; i < QPB; ++i) {
+                    rmma(QPB * nb + i, rc[i]);
+                    rc[i] = rn[i];
+                }
             }
         };
 
