@@ -15,6 +15,7 @@ available as an alias):
     build_refs(shape, x, t0, t1, cache)
     compress(shape, x, t0, t1, compressor, cache, workspace, stats=None)
     decode_attn(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out, workspace)
+    decode_attn_noalloc(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, scale, out)
     decode_sparse_workspace_bytes(shape, Hq, T, n_sel) -> int
     decode_attn_sparse(shape, Hq, T, q, k_cache, k_dec, v_cache, v_dec, positions, scale,
                        out, workspace)
@@ -103,6 +104,10 @@ def lib():
                                       ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                       ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                       ctypes.c_float, _P, _P, _SZ, _P]
+    L.deltakv_decode_attn_noalloc.argtypes = [sp, ctypes.c_int32, ctypes.c_int64, _P,
+                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
+                                              ctypes.c_float, _P, _P]
     L.deltakv_decode_sparse_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
                                                         ctypes.c_int32, ctypes.POINTER(_SZ)]
     L.deltakv_decode_attn_sparse.argtypes = [sp, ctypes.c_int32, ctypes.c_int64, _P,
@@ -134,7 +139,7 @@ def lib():
                  "deltakv_decode_attn_sparse", "deltakv_decode_select_workspace_bytes",
                  "deltakv_decode_attn_select", "deltakv_decode_window_workspace_bytes",
                  "deltakv_decode_attn_window", "deltakv_decode_varlen_workspace_bytes",
-                 "deltakv_decode_attn_varlen"):
+                 "deltakv_decode_attn_varlen", "deltakv_decode_attn_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.deltakv_status_string.argtypes = [ctypes.c_int]
     L.deltakv_status_string.restype = ctypes.c_char_p
@@ -315,6 +320,20 @@ def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, 
                                      _ptr(workspace), wsb, _stream()))
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_attn_noalloc(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor,
+                        k_cache: Cache, k_dec: Mlp, v_cache: Cache, v_dec: Mlp, scale: float,
+                        out: torch.Tensor):
+    """decode_attn with the library's own per-device scratch (no workspace)."""
+    cs, kc, km, vc, vm = shape.c(), k_cache.c(), k_dec.c(), v_cache.c(), v_dec.c()
+    _check(lib().deltakv_decode_attn_noalloc(ctypes.byref(cs), num_q_heads, n_tokens, _ptr(q),
+                                             ctypes.byref(kc), ctypes.byref(km),
+                                             ctypes.byref(vc), ctypes.byref(vm), float(scale),
+                                             _ptr(out), _stream()))
+
+
 def decode_sparse_workspace_bytes(shape: Shape, num_q_heads: int, n_tokens: int,
                                   n_sel: int) -> int:
     v = _SZ()
@@ -439,6 +458,7 @@ deltakv_decode_workspace_bytes = decode_workspace_bytes
 deltakv_build_refs = build_refs
 deltakv_compress = compress
 deltakv_decode_attn = decode_attn
+deltakv_decode_attn_noalloc = decode_attn_noalloc
 deltakv_decode_sparse_workspace_bytes = decode_sparse_workspace_bytes
 deltakv_decode_attn_sparse = decode_attn_sparse
 deltakv_decode_select_workspace_bytes = decode_select_workspace_bytes

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dk_common.h"
@@ -326,15 +327,17 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
     return st;
 }
 
-deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
-                                   int64_t n_tokens, const void *q,
-                                   const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
-                                   const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
-                                   float softmax_scale, float *out, void *workspace,
-                                   size_t workspace_bytes, void *stream) {
-    dk::Dims dm;
-    dk::CacheArgs kc, vc;
-    dk::MlpArgs km, vm;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the dense decode (everything but the workspace).
+deltakv_status check_decode(const deltakv_shape *shape, int32_t num_q_heads, int64_t n_tokens,
+                            const void *q, const deltakv_cache *k_cache,
+                            const deltakv_mlp *k_dec, const deltakv_cache *v_cache,
+                            const deltakv_mlp *v_dec, float softmax_scale, const float *out,
+                            dk::Dims &dm, dk::CacheArgs &kc, dk::MlpArgs &km, dk::CacheArgs &vc,
+                            dk::MlpArgs &vm) {
     deltakv_status st = check_shape(shape, &dm);
     if (st != DELTAKV_OK) return st;
     if (num_q_heads < 1 || num_q_heads % dm.H != 0 || num_q_heads / dm.H > 8)
@@ -357,6 +360,25 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
                     "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
+    return DELTAKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
+                                   int64_t n_tokens, const void *q,
+                                   const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
+                                   const deltakv_cache *v_cache, const deltakv_mlp *v_dec,
+                                   float softmax_scale, float *out, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_decode(shape, num_q_heads, n_tokens, q, k_cache, k_dec, v_cache,
+                                     v_dec, softmax_scale, out, dm, kc, km, vc, vm);
+    if (st != DELTAKV_OK) return st;
     const size_t need = dk::decode_ws_bytes(dm, num_q_heads, n_tokens);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(DELTAKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
@@ -367,6 +389,78 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
                                       softmax_scale, out, workspace, workspace_bytes,
                                       (hipStream_t)stream),
                     "deltakv_decode_attn");
+}
+
+}  // extern "C"
+
+// ---- the decode entry point that allocates nothing --------------------------
+// Its workspace is this file-scope device array: each device the library runs
+// on holds one copy, at its own address, from the first call on that device
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: the per-device address comes from
+// hipGetSymbolAddress and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[DELTAKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device, looked up once per device.
+deltakv_status scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DELTAKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DELTAKV_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DELTAKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DELTAKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+deltakv_status deltakv_decode_attn_noalloc(const deltakv_shape *shape, int32_t num_q_heads,
+                                           int64_t n_tokens, const void *q,
+                                           const deltakv_cache *k_cache,
+                                           const deltakv_mlp *k_dec,
+                                           const deltakv_cache *v_cache,
+                                           const deltakv_mlp *v_dec, float softmax_scale,
+                                           float *out, void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs kc, vc;
+    dk::MlpArgs km, vm;
+    deltakv_status st = check_decode(shape, num_q_heads, n_tokens, q, k_cache, k_dec, v_cache,
+                                     v_dec, softmax_scale, out, dm, kc, km, vc, vm);
+    if (st != DELTAKV_OK) return st;
+    const size_t need = dk::decode_ws_bytes(dm, num_q_heads, n_tokens);
+    if (need > (size_t)DELTAKV_NOALLOC_SCRATCH_BYTES)
+        return fail(DELTAKV_ERR_WORKSPACE,
+                    "decode needs %zu bytes of scratch, more than the %zu the allocation-free "
+                    "entry point holds; call deltakv_decode_attn with a workspace", need,
+                    (size_t)DELTAKV_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != DELTAKV_OK) return st;
+    // every region of the workspace is written by the call before it is read
+    // (query tables, then partial records, then the merge), so nothing has to
+    // be cleared first
+    return from_hip(dk::launch_decode(dm, num_q_heads, n_tokens, q, kc, km, vc, vm,
+                                      softmax_scale, out, ws,
+                                      (size_t)DELTAKV_NOALLOC_SCRATCH_BYTES,
+                                      (hipStream_t)stream),
+                    "deltakv_decode_attn_noalloc");
 }
 
 deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t num_q_heads,

@@ -214,6 +214,31 @@ deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_hea
                                    float softmax_scale, float *out, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* Bytes of device scratch that deltakv_decode_attn_noalloc holds per device. */
+#define DELTAKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* deltakv_decode_attn without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, result,
+ * requirements and errors are those of deltakv_decode_attn.  Its scratch is a
+ * device array inside the library, DELTAKV_NOALLOC_SCRATCH_BYTES bytes per
+ * device, held from the first call on a device until the process ends; the
+ * array of the CURRENT device (hipGetDevice) is used, so `stream` must belong
+ * to it.  A call needing more scratch than that (see
+ * deltakv_decode_workspace_bytes) returns DELTAKV_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on a device shares that device's array:
+ * calls that overlap in time on one device (on different streams, or from
+ * different host threads without ordering) race and give wrong results; calls
+ * ordered on one stream are safe.  Nothing in the scratch needs to start at
+ * zero (each call writes every region before reading it). */
+deltakv_status deltakv_decode_attn_noalloc(const deltakv_shape *shape, int32_t num_q_heads,
+                                           int64_t n_tokens, const void *q,
+                                           const deltakv_cache *k_cache,
+                                           const deltakv_mlp *k_dec,
+                                           const deltakv_cache *v_cache,
+                                           const deltakv_mlp *v_dec, float softmax_scale,
+                                           float *out, void *stream);
+
 /* Largest position list per (sequence, KV head) that the sparse decode takes. */
 #define DELTAKV_MAX_SPARSE_SELECT 1048576
 

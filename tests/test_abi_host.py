@@ -394,3 +394,17 @@ def test_varlen_length_errors_return_before_any_launch():
     with pytest.raises(dk.DeltaKVError) as e:
         call(_FakeLens(), 4096, ws=_FakePtr(0x30000, need - 1))
     assert e.value.status == 4
+
+
+def test_noalloc_decode_rejects_calls_beyond_its_scratch():
+    # batch 64 x 8 KV heads at 128k needs more than the 64 MiB the
+    # allocation-free entry point holds; the call fails before touching a device
+    sh = _shape(batch=64, capacity=131072)
+    assert dk.decode_workspace_bytes(sh, 32, 131072) > dk.NOALLOC_SCRATCH_BYTES
+    assert dk.decode_workspace_bytes(_shape(capacity=131072), 32, 131072) < \
+        dk.NOALLOC_SCRATCH_BYTES
+    dec = _mlp(32, 256, 128)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.decode_attn_noalloc(sh, 32, 131072, _FakePtr(), _cache(filled=131072), dec,
+                               _cache(filled=131072), dec, 0.088, _FakePtr())
+    assert e.value.status == 4 and "scratch" in e.value.detail
