@@ -33,20 +33,26 @@ import torch
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+# Vector-ALU issue peak: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD
+# every 4 cycles (16 lanes per cycle) at 2.4 GHz = 614.4 G wave-instructions/s.
+VALU_PEAK_GINSTR = 256 * 4 * 2.4 / 4
 
-# HBM traffic of one decode_attn call on the 128k, 32-layer workload, from two
-# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, summed over
-# the call's kernels).  FETCH_SIZE reads 0.5 KiB per KiB for a plain 1 GiB
-# device copy, so it is scaled by 2; WRITE_SIZE reads 1:1.  The figures hold
-# only for the decode source they were taken on (its SHA-256 prefix); after any
-# change to it the traffic is reported as null until it is measured again.
-DECODE_TRAFFIC = {
+# Counters of one decode_attn call on the 128k, 32-layer workload, from
+# rocprofv3 --pmc passes (per dispatch, summed over the call's three kernels:
+# prep, main, combine): FETCH_SIZE / WRITE_SIZE in KiB (HBM traffic; a 1 GiB
+# device copy reads FETCH_SIZE = 512 MiB and WRITE_SIZE = 1 GiB, so FETCH_SIZE
+# is scaled by 2), SQ_INSTS_VALU and SQ_INSTS_MFMA in wave instructions.  They
+# hold only for the decode sources they were taken on (SHA-256 prefix); after
+# any change the dependent figures are reported as null until measured again.
+DECODE_COUNTERS = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "9a2787459cbd",
-    "fetch_kib": {"main_ws": 85677.9, "prep": 8549.3, "combine2": 2394.0},
+    "source_sha256": "bea8b300c075",
+    "fetch_kib": {"main_ws": 86362.8, "prep": 8549.2, "combine2": 2387.0},
     "write_kib": {"main_ws": 3880.2, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
+    "valu_insts": {"main_ws": 44019448.3, "prep": 395776.0, "combine2": 100160.0},
+    "mfma_insts": {"main_ws": 3948544.0, "prep": 16416.0, "combine2": 0.0},
 }
 
 
@@ -60,13 +66,46 @@ def decode_source_sha():
     return h.hexdigest()[:12]
 
 
-def decode_traffic_bytes(wl):
-    t = DECODE_TRAFFIC
-    if wl.name != t["workload"] or decode_source_sha() != t["source_sha256"]:
+def decode_counters(wl):
+    """The counter record if it was taken on these sources and this workload."""
+    t = DECODE_COUNTERS
+    if wl.name != t["workload"] or t["source_sha256"] is None or \
+            decode_source_sha() != t["source_sha256"]:
         return None
-    kib = (sum(t["fetch_kib"].values()) * t["fetch_scale"]
-           + sum(t["write_kib"].values()) * t["write_scale"])
-    return kib * 1024.0
+    return t
+
+
+def decode_traffic_bytes(wl):
+    t = decode_counters(wl)
+    if t is None or t["fetch_kib"] is None:
+        return None
+    return (sum(t["fetch_kib"].values()) * t["fetch_scale"]
+            + sum(t["write_kib"].values()) * t["write_scale"]) * 1024.0
+
+
+def measured_peaks(dk, stream):
+    """The chip's own rates, timed with HIP events on the launch stream: a
+    register-resident bf16 matrix-core loop (TFLOP/s) and the decode's
+    packed-f16 GELU polynomial in a loop (GELU/s and the vector-ALU
+    wave-instruction rate it implies: 8 packed instructions per GELU pair)."""
+    sink = torch.zeros(4096, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+    for kind, blocks, iters in ((dk.PEAK_MFMA_BF16, 2048, 4000), (dk.PEAK_GELU_F16, 2048, 2000)):
+        dk.peak_probe(kind, blocks, 10, sink)          # warm up
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        dk.peak_probe(kind, blocks, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3
+        if kind == dk.PEAK_MFMA_BF16:
+            out["mfma_bf16_tflops"] = blocks * 4 * iters * 8 * 16384 / sec / 1e12
+        else:
+            n_gelu = blocks * 256 * iters * 8
+            out["gelu_f16_g_per_s"] = n_gelu / sec / 1e9
+            out["valu_g_wave_instr_per_s"] = blocks * 4 * iters * 32 / sec / 1e9
+    return out
 
 
 def log(*a):
@@ -263,13 +302,15 @@ def compress_flops(wl):
                                                    + wl.hidden * wl.d_c) * N)
 
 
-def cpu_baseline(wl, widx, threads, budget_s=12.0):
+def cpu_baseline(wl, widx, threads, budget_s=10.0, budget_1t_s=4.0):
     """The oracle as it is, timed on this host on bounded samples of the same
     workload (one unit: layer 0, KV head 0):
       compress: select + compress of uniformly sampled compressed positions,
-                pulled in chunks by `threads` host threads until `budget_s`;
-      decode:   one decode step of the 4 query heads of that KV head over all
-                T tokens (K and V rebuilt in two threads, then attention).
+                pulled in chunks by `threads` host threads until `budget_s`,
+                then by one thread until `budget_1t_s`;
+      decode:   one decode step of the query heads of that KV head over its
+                first min(T, 8192) tokens (K and V rebuilt in two threads, then
+                attention), scaled to T tokens and to every layer x KV head.
     Rates are scaled to the metric's units (a sequence position = every
     layer, KV head and stream; a decode token = every layer and KV head)."""
     import oracle
@@ -283,39 +324,44 @@ def cpu_baseline(wl, widx, threads, budget_s=12.0):
     mlp = lambda key, a, b, c: (lambda w: oracle.MLP(f(w["w1"]), f(w["b1"]), f(w["w2"]),
                                                      f(w["b2"]), oracle.ACT_GELU))(
         xavier_mlp(a, b, c, key=key, dtype=wl.torch_dtype))
-    ck, cv = mlp((1, widx, 0, 0), wl.head_dim, wl.hidden, wl.d_c), \
-        mlp((1, widx, 0, 1), wl.head_dim, wl.hidden, wl.d_c)
+    ck = mlp((1, widx, 0, 0), wl.head_dim, wl.hidden, wl.d_c)
     dk_, dv_ = mlp((2, widx, 0, 0), wl.d_c, wl.hidden, wl.head_dim), \
         mlp((2, widx, 0, 1), wl.d_c, wl.hidden, wl.head_dim)
+    cv = mlp((1, widx, 0, 1), wl.head_dim, wl.hidden, wl.d_c)
     refs = oracle.build_refs(xk, s)
     pos = np.random.default_rng(11).permutation(oracle.nonref_positions(T, s))
-    lock = threading.Lock()
-    state = {"next": 0, "done": 0}
-    chunk = 32
-    deadline = time.perf_counter() + budget_s
-
-    def work():
-        while time.perf_counter() < deadline:
-            with lock:
-                i = state["next"]
-                state["next"] += chunk
-            p = np.sort(pos[i:i + chunk])
-            if len(p) == 0:
-                return
-            idx = oracle.select(xk[p], p, refs, s, wl.k)
-            oracle.compress(xk[p], refs, idx, ck)
-            with lock:
-                state["done"] += len(p)
-
-    t0 = time.perf_counter()
-    ths = [threading.Thread(target=work) for _ in range(threads)]
-    for t in ths:
-        t.start()
-    for t in ths:
-        t.join()
-    dt = time.perf_counter() - t0
-    n_tok = state["done"]
     rows_per_token = wl.layers * wl.batch * wl.kv_heads * 2 * (1 - 1 / s)
+
+    def compress_rate(nthreads, budget):
+        lock = threading.Lock()
+        state = {"next": 0, "done": 0}
+        chunk = 32
+        deadline = time.perf_counter() + budget
+
+        def work():
+            while time.perf_counter() < deadline:
+                with lock:
+                    i = state["next"]
+                    state["next"] += chunk
+                p = np.sort(pos[i % len(pos):i % len(pos) + chunk])
+                if len(p) == 0:
+                    return
+                idx = oracle.select(xk[p], p, refs, s, wl.k)
+                oracle.compress(xk[p], refs, idx, ck)
+                with lock:
+                    state["done"] += len(p)
+
+        t0 = time.perf_counter()
+        ths = [threading.Thread(target=work) for _ in range(nthreads)]
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        dt = time.perf_counter() - t0
+        return state["done"], dt
+
+    n_tok, dt = compress_rate(threads, budget_s)
+    n_tok1, dt1 = compress_rate(1, budget_1t_s)
 
     # decode sample: the first Ts positions of the head, compressed by the
     # oracle, then one decode step; its time is scaled by T / Ts
@@ -347,27 +393,33 @@ def cpu_baseline(wl, widx, threads, budget_s=12.0):
     for t in th:
         t.join()
     oracle.attention(q, rec["k"], rec["v"], 1.0 / math.sqrt(wl.head_dim))
-    t_head = (time.perf_counter() - t1) * (T / Ts)
+    t_sample = time.perf_counter() - t1
     heads_per_step = wl.layers * wl.kv_heads * wl.batch
+    extrapolation = (T / Ts) * heads_per_step
     cpu = "unknown CPU"
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
                 if line.startswith("model name"):
                     cpu = line.split(":", 1)[1].strip()
                     break
     except OSError:
         pass
+    host_cores = len(os.sched_getaffinity(0))
     return {"value": n_tok / dt / rows_per_token, "unit": "tok/s", "cores": threads,
             "kind": "oracle",
-            "decode_attn_tok_s": wl.batch / (t_head * heads_per_step),
+            "value_1thread": n_tok1 / dt1 / rows_per_token,
+            "host_cores": host_cores, "host_cpu": cpu, "threads_used": threads,
+            "decode_attn_tok_s": wl.batch / (t_sample * extrapolation),
+            "decode_extrapolation_factor": extrapolation,
             "sample": f"compress: oracle select+compress of {n_tok} uniformly sampled compressed "
                       f"positions of one unit (layer 0, KV head 0, K) at T={T}, {dt:.1f}s on "
-                      f"{threads} threads, scaled by the {rows_per_token:.0f} compressed rows per "
-                      f"sequence position; decode: one step of one KV head ({G} query heads) over "
-                      f"its first {Ts} positions (K and V rebuilt on 2 threads), {t_head * Ts / T:.2f}s, "
-                      f"scaled by T/{Ts} and by the {heads_per_step} KV heads x layers of a step, "
-                      f"2 threads; host CPU {cpu}"}
+                      f"{threads} threads ({n_tok1} positions in {dt1:.1f}s on 1 thread), scaled "
+                      f"by the {rows_per_token:.0f} compressed rows per sequence position; "
+                      f"decode: one step of one KV head ({G} query heads) over its first {Ts} "
+                      f"positions (K and V rebuilt on 2 threads), {t_sample:.2f}s, multiplied by "
+                      f"{extrapolation:.0f} = (T/{Ts}) x the {heads_per_step} KV heads x layers "
+                      f"of a step; host: {host_cores} cores available, {cpu}"}
 
 
 def main():
@@ -600,8 +652,45 @@ def main():
     copy_gbs = 2 * src.numel() * 2 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    peaks = measured_peaks(S.dk, stream)
+    log(f"[bench] measured peaks: copy {copy_gbs:.0f} GB/s, bf16 MFMA "
+        f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s, GELU {peaks['gelu_f16_g_per_s']:.0f} G/s")
+
     B, T = wl.batch, wl.T
     step_bytes = per_layer_bytes * wl.layers
+    launch_s = launch_ms * 1e-3
+    # the decode's matrix-core work in absorbed form, per compressed token and
+    # KV head: both hidden layers (2 * 2 d_c h) and the query-side products
+    # with the hidden vectors (G * 4 h); the reference rows add 4 d G each
+    R_ = -(-T // wl.stride)
+    G_ = wl.q_heads // wl.kv_heads
+    dec_flops = B * wl.kv_heads * ((T - R_) * (4 * wl.d_c * wl.hidden + 4 * G_ * wl.hidden)
+                                   + T * 4 * wl.head_dim * G_)
+    cnt = decode_counters(wl)
+    valu = sum(cnt["valu_insts"].values()) if cnt and cnt["valu_insts"] else None
+    hbm = {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": per_layer_bytes,
+           "frac_of_measured_copy": achieved / copy_gbs}
+    mfma = {"achieved": dec_flops / launch_s / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": dec_flops / launch_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": dec_flops}
+    if valu is not None:
+        # the binding resource: vector-ALU issue (hardware count of the call's
+        # wave instructions over the call's duration, against 614.4 G/s)
+        roof = {"kernel": "deltakv_decode_attn, one layer (prep + main + combine)",
+                "bound": "alu", "achieved": valu / launch_s / 1e9, "peak": VALU_PEAK_GINSTR,
+                "unit": "G VALU wave-instructions/s",
+                "frac": valu / launch_s / 1e9 / VALU_PEAK_GINSTR,
+                "traffic": decode_traffic_bytes(wl), "valu_insts_per_launch": valu,
+                "frac_of_measured_valu": valu / launch_s / 1e9 / peaks["valu_g_wave_instr_per_s"],
+                "launch_ms": launch_ms, "hbm": hbm, "mfma": mfma}
+    else:
+        roof = {"kernel": "deltakv_decode_attn, one layer (prep + main + combine)",
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(wl),
+                "launch_ms": launch_ms, "hbm": hbm, "mfma": mfma,
+                "note": "vector-ALU counters not taken on these decode sources"}
+    cflops = compress_flops(wl)
     res = {
         "metric": "compressed KV tokens/s; decode-attn tok/s + effective HBM GB/s at 128k ctx",
         "value": B * T / (comp_ms * 1e-3),
@@ -621,25 +710,28 @@ def main():
                    "k": wl.k, "d_c": wl.d_c, "hidden": wl.hidden, "decode_steps": dsteps,
                    "prompt_chunk": wl.chunk, "appends_per_step": min(dsteps, wl.appends)},
         "compress_ms_per_step": comp_ms,
-        "compress_tflops": compress_flops(wl) / (comp_ms * 1e-3) / 1e12,
+        "compress_tflops": cflops / (comp_ms * 1e-3) / 1e12,
+        "compress_roofline": {"bound": "mfma", "achieved": cflops / (comp_ms * 1e-3) / 1e12,
+                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": cflops / (comp_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                              "frac_of_measured_mfma": cflops / (comp_ms * 1e-3) / 1e12
+                              / peaks["mfma_bf16_tflops"],
+                              "algorithmic_flops_per_step": cflops},
         "decode_ms_per_step": dec_ms,
         "decode_graph_ms_per_step": graph_ms,
         "decode_attn_tok_s": B * dsteps / (dec_ms * 1e-3),
+        "decode_graph_attn_tok_s": B / (graph_ms * 1e-3) if graph_ms else None,
         "decode_eff_hbm_gbs": step_bytes * dsteps / (dec_ms * 1e-3) / 1e9,
         "fallback_tokens_per_compress": int(S.stats[0].item()) // a.steps,
         "measured_copy_gbs": copy_gbs,
+        "measured_peaks": peaks,
         "sparse_decode": sparse,
         "q4_latents": q4,
-        "roofline": {"kernel": "deltakv_decode_attn (one layer)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(wl),
-                     "algorithmic_bytes_per_launch": per_layer_bytes,
-                     "launch_ms": launch_ms,
-                     "frac_of_measured_copy": achieved / copy_gbs},
+        "roofline": roof,
     }
     if not a.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
-        log(f"[bench] cpu baseline on {threads} threads")
+        log(f"[bench] cpu baseline on {threads} threads and on 1 thread")
         res["cpu_baseline"] = cpu_baseline(wl, widx, threads)
     print(json.dumps(res), flush=True)
 

@@ -141,6 +141,8 @@ def lib():
                  "deltakv_decode_attn_window", "deltakv_decode_varlen_workspace_bytes",
                  "deltakv_decode_attn_varlen", "deltakv_decode_attn_noalloc"):
         getattr(L, name).restype = ctypes.c_int
+    L.deltakv_peak_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
+    L.deltakv_peak_probe.restype = ctypes.c_int
     L.deltakv_status_string.argtypes = [ctypes.c_int]
     L.deltakv_status_string.restype = ctypes.c_char_p
     L.deltakv_last_error.argtypes = []
@@ -435,6 +437,14 @@ def decode_attn_varlen(shape: Shape, num_q_heads: int, lengths: torch.Tensor,
                                             _ptr(workspace), wsb, _stream()))
 
 
+PEAK_MFMA_BF16, PEAK_GELU_F16 = 0, 1
+
+
+def peak_probe(kind: int, blocks: int, iters: int, sink: torch.Tensor):
+    """Measurement helper: enqueue the matrix-core or GELU rate loop."""
+    _check(lib().deltakv_peak_probe(kind, blocks, iters, _ptr(sink), _stream()))
+
+
 def status_string(status: int) -> str:
     return lib().deltakv_status_string(status).decode()
 
@@ -467,6 +477,7 @@ deltakv_decode_window_workspace_bytes = decode_window_workspace_bytes
 deltakv_decode_attn_window = decode_attn_window
 deltakv_decode_varlen_workspace_bytes = decode_varlen_workspace_bytes
 deltakv_decode_attn_varlen = decode_attn_varlen
+deltakv_peak_probe = peak_probe
 deltakv_status_string = status_string
 deltakv_last_error = last_error
 deltakv_version = version

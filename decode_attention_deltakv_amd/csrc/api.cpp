@@ -637,6 +637,18 @@ deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t nu
                     "deltakv_decode_attn_varlen");
 }
 
+deltakv_status deltakv_peak_probe(int32_t kind, int32_t blocks, int32_t iters, float *sink,
+                                  void *stream) {
+    if (kind != DELTAKV_PEAK_MFMA_BF16 && kind != DELTAKV_PEAK_GELU_F16)
+        return fail(DELTAKV_ERR_INVALID_ARG, "probe kind %d unknown", kind);
+    if (blocks < 1 || iters < 1 || !sink)
+        return fail(DELTAKV_ERR_INVALID_ARG, "probe needs blocks >= 1, iters >= 1 and a sink");
+    const hipError_t e = kind == DELTAKV_PEAK_MFMA_BF16
+                             ? dk::launch_peak_mfma(blocks, iters, sink, (hipStream_t)stream)
+                             : dk::launch_peak_gelu(blocks, iters, sink, (hipStream_t)stream);
+    return from_hip(e, "deltakv_peak_probe");
+}
+
 const char *deltakv_status_string(deltakv_status status) {
     switch (status) {
         case DELTAKV_OK: return "DELTAKV_OK";

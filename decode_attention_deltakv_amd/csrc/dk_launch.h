@@ -121,4 +121,8 @@ namespace dk {
 hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                               int64_t nq, const CacheArgs &c, uint64_t *flist, uint32_t *fcount,
                               uint32_t *stats, hipStream_t st);
+// measured denominators (k_peaks.hip): `blocks` blocks of 256 threads
+hipError_t launch_peak_mfma(int blocks, int iters, float *sink, hipStream_t st);
+hipError_t launch_peak_gelu(int blocks, int iters, float *sink, hipStream_t st);
+
 }  // namespace dk

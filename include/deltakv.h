@@ -360,6 +360,20 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
                                           int32_t *positions, float *scores, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* Measurement helpers (not part of the method): loops that time the chip's
+ * own rates as denominators for roofline figures.
+ *   DELTAKV_PEAK_MFMA_BF16: each wave issues iters x 8 independent
+ *     16x16x32 bf16 matrix products on register operands
+ *     (iters * 8 * 16384 flops per wave);
+ *   DELTAKV_PEAK_GELU_F16: each lane evaluates iters x 8 GELUs with the
+ *     packed-f16 polynomial the decode uses (8 packed instructions per pair).
+ * `blocks` blocks of 256 threads (4 waves); sink: device float[blocks],
+ * written only in a case that does not occur (keeps the loop alive). */
+#define DELTAKV_PEAK_MFMA_BF16 0
+#define DELTAKV_PEAK_GELU_F16 1
+deltakv_status deltakv_peak_probe(int32_t kind, int32_t blocks, int32_t iters, float *sink,
+                                  void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *deltakv_status_string(deltakv_status status);
 
