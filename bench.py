@@ -191,6 +191,13 @@ class Setup:
         self.scale = 1.0 / math.sqrt(d)
         self.qbank = queries(64 * L * B * self.Hq, d, key=(3, widx), dtype=dt,
                              device="cuda").reshape(64, L, B, self.Hq, d)
+        if self.A:
+            # a decode step's appends: one token into every layer's K and V
+            # cache in one batched call
+            flat = [self.cache[l][st] for l in range(L) for st in (0, 1)]
+            comps = [self.comp[l][st] for l in range(L) for st in (0, 1)]
+            self.appender = dk.AppendBatch(self.shape, flat, comps)
+            self.aws = dk.workspace(dk.append_workspace_bytes(self.shape, cap - 1, len(flat)))
 
     def compress_all(self):
         """The whole prompt: one call per (layer, stream), or chunk by chunk
@@ -219,15 +226,32 @@ class Setup:
             return
         dk, sh, T = self.dk, self.shape, self.wl.T
         p = T + k
+        self.append_batched(k)
+        for l in range(self.wl.layers):
+            c, d = self.cache[l], self.dec[l]
+            dk.decode_attn(sh, self.Hq, p + 1, qs[l], c[0], d[0], c[1], d[1], self.scale,
+                           self.out, self.dws)
+
+    def append_batched(self, k):
+        """Token T + k into every cache: one deltakv_append call."""
+        self.appender(self.wl.T + k, [self.xa[l][st][k] for l in range(self.wl.layers)
+                                      for st in (0, 1)], self.aws)
+
+    def append_per_cache(self, k):
+        """Token T + k into every cache with the per-cache entry points."""
+        dk, sh, p = self.dk, self.shape, self.wl.T + k
         for l in range(self.wl.layers):
             for st in (0, 1):
                 xa = self.xa[l][st][k]
                 dk.build_refs(sh, xa, p, p + 1, self.cache[l][st])
                 dk.compress(sh, xa, p, p + 1, self.comp[l][st], self.cache[l][st], self.cws,
                             self.stats)
-            c, d = self.cache[l], self.dec[l]
-            dk.decode_attn(sh, self.Hq, p + 1, qs[l], c[0], d[0], c[1], d[1], self.scale,
-                           self.out, self.dws)
+
+    def rewind(self, n):
+        """Filled lengths back to n (the next appends rewrite those positions)."""
+        for row in self.cache:
+            for c in row:
+                c.n_built = c.n_compressed = n
 
     def decode_step_q(self, qs):
         dk, sh, T = self.dk, self.shape, self.wl.T
@@ -473,6 +497,31 @@ def main():
     dec_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs]))
     ms_per_step = wall * 1000 / a.steps
     log(f"[bench] compress {comp_ms:.2f} ms, decode {dec_ms:.2f} ms for {dsteps} steps")
+
+    # streaming: the appends of the last decode steps again (lengths rewound,
+    # the same tokens rewritten), one batched call per token against the
+    # per-cache calls
+    streaming = None
+    if wl.appends:
+        n_a = min(16, dsteps)
+        k0 = dsteps - n_a
+        per_tok = {}
+        for name, fn in (("batched", S.append_batched), ("per_cache", S.append_per_cache)):
+            for rep_ in range(2):   # the first pass warms up
+                S.rewind(wl.T + k0)
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for k in range(k0, k0 + n_a):
+                    fn(k)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            per_tok[name] = e0.elapsed_time(e1) / n_a
+        streaming = {"caches_per_append": 2 * wl.layers,
+                     "append_ms_per_token": per_tok["batched"],
+                     "append_ms_per_token_per_cache_calls": per_tok["per_cache"],
+                     "decode_step_ms_incl_append": dec_ms / dsteps}
+        log(f"[bench] appends: {per_tok['batched']:.4f} ms per token batched, "
+            f"{per_tok['per_cache']:.4f} ms with per-cache calls")
 
     # per-launch timing of the decode entry point (the step's dominant cost),
     # events on the launch stream around single calls
@@ -727,6 +776,7 @@ def main():
         "measured_peaks": peaks,
         "sparse_decode": sparse,
         "q4_latents": q4,
+        "streaming": streaming,
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

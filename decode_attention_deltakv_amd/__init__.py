@@ -75,6 +75,11 @@ class CCache(ctypes.Structure):
                 ("n_built", ctypes.c_int64), ("n_compressed", ctypes.c_int64)]
 
 
+class CAppendItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("cache", ctypes.POINTER(CCache)),
+                ("compressor", ctypes.POINTER(CMlp))]
+
+
 _lib = None
 _SZ = ctypes.c_size_t
 _P = ctypes.c_void_p
@@ -133,7 +138,12 @@ def lib():
                                              _P, ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.POINTER(CCache), ctypes.POINTER(CMlp),
                                              ctypes.c_float, _P, _P, _SZ, _P]
-    for name in ("deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
+    L.deltakv_append_workspace_bytes.argtypes = [sp, ctypes.c_int64, ctypes.c_int32,
+                                                 ctypes.POINTER(_SZ)]
+    L.deltakv_append.argtypes = [sp, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.POINTER(CAppendItem), _P, _SZ, _P]
+    for name in ("deltakv_append_workspace_bytes", "deltakv_append",
+                 "deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
                  "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
                  "deltakv_decode_attn_sparse", "deltakv_decode_select_workspace_bytes",
@@ -309,6 +319,54 @@ def compress(shape: Shape, x: torch.Tensor, t0: int, t1: int, compressor: Mlp, c
                                   ctypes.byref(cc), _ptr(workspace), wsb, _ptr(stats),
                                   _stream()))
     cache._took(cc)
+
+
+def append_workspace_bytes(shape: Shape, t: int, n_items: int) -> int:
+    v = _SZ()
+    cs = shape.c()
+    _check(lib().deltakv_append_workspace_bytes(ctypes.byref(cs), t, n_items, ctypes.byref(v)))
+    return v.value
+
+
+class AppendBatch:
+    """The argument arrays of deltakv_append over a fixed list of caches and
+    their compressors, built once; each call passes the position, the new
+    rows (one [B, H, 1, d] tensor per cache) and the workspace."""
+
+    def __init__(self, shape: Shape, caches, compressors):
+        if len(caches) != len(compressors):
+            raise ValueError("one compressor per cache")
+        n = len(caches)
+        self.shape, self._cs = shape, shape.c()
+        self.caches = list(caches)
+        self._cc = (CCache * n)(*[c.c() for c in caches])
+        self._cm = (CMlp * n)(*[m.c() for m in compressors])
+        self._items = (CAppendItem * n)()
+        cc0, cm0 = ctypes.addressof(self._cc), ctypes.addressof(self._cm)
+        for i in range(n):
+            self._items[i].cache = ctypes.cast(cc0 + i * ctypes.sizeof(CCache),
+                                               ctypes.POINTER(CCache))
+            self._items[i].compressor = ctypes.cast(cm0 + i * ctypes.sizeof(CMlp),
+                                                    ctypes.POINTER(CMlp))
+
+    def __call__(self, t: int, xs, workspace: Optional[torch.Tensor]):
+        n = len(self.caches)
+        if len(xs) != n:
+            raise ValueError(f"{len(xs)} rows for {n} caches")
+        for i, (x, c) in enumerate(zip(xs, self.caches)):
+            self._items[i].x = _ptr(x)
+            self._cc[i].n_built, self._cc[i].n_compressed = c.n_built, c.n_compressed
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().deltakv_append(ctypes.byref(self._cs), t, n, self._items, _ptr(workspace),
+                                    wsb, _stream()))
+        for i, c in enumerate(self.caches):
+            c._took(self._cc[i])
+
+
+def append(shape: Shape, t: int, xs, caches, compressors, workspace: Optional[torch.Tensor]):
+    """Position t appended to every cache (deltakv_append): xs[i] [B, H, 1, d]
+    is the new row of caches[i], compressed with compressors[i]."""
+    AppendBatch(shape, caches, compressors)(t, xs, workspace)
 
 
 def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, k_cache: Cache,

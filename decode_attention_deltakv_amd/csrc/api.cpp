@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "dk_common.h"
 #include "dk_launch.h"
@@ -17,6 +18,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int32_t kMaxAppendItems = 4096;
 
 deltakv_status fail(deltakv_status st, const char *fmt, ...) {
     char buf[512];
@@ -324,6 +327,108 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
                                       (hipStream_t)stream),
                   "deltakv_compress");
     if (st == DELTAKV_OK) cache->n_compressed = t1;
+    return st;
+}
+
+deltakv_status deltakv_append_workspace_bytes(const deltakv_shape *shape, int64_t t,
+                                              int32_t n_items, size_t *bytes) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_range(dm, t, t + 1)) != DELTAKV_OK) return st;
+    if (n_items < 1 || n_items > kMaxAppendItems)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_items %d not in [1, %d]", n_items,
+                    kMaxAppendItems);
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::append_ws_bytes(dm, t, n_items);
+    return ok();
+}
+
+deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_items,
+                              const deltakv_append_item *items, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_range(dm, t, t + 1)) != DELTAKV_OK) return st;
+    if (n_items < 1 || n_items > kMaxAppendItems)
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_items %d not in [1, %d]", n_items,
+                    kMaxAppendItems);
+    if (!items) return fail(DELTAKV_ERR_INVALID_ARG, "items is NULL");
+    // every check before anything is enqueued
+    std::vector<dk::CacheArgs> ca((size_t)n_items);
+    std::vector<dk::MlpArgs> ma((size_t)n_items);
+    bool batched = true;
+    for (int i = 0; i < n_items; ++i) {
+        const deltakv_append_item &it = items[i];
+        char name[48];
+        snprintf(name, sizeof(name), "items[%d].cache", i);
+        if (!it.x) return fail(DELTAKV_ERR_INVALID_ARG, "items[%d].x is NULL", i);
+        if (!aligned16(it.x))
+            return fail(DELTAKV_ERR_INVALID_ARG, "items[%d].x must be 16-byte aligned", i);
+        if ((st = check_mlp(it.compressor, "compressor", dm.d, dm.dc, &ma[i])) != DELTAKV_OK)
+            return st;
+        if (dm.lat_fmt && !dk::compress_q4_supported(dm, ma[i]))
+            return fail(DELTAKV_ERR_UNSUPPORTED, "4-bit latents: items[%d].compressor must "
+                        "have hidden width 128 or 256", i);
+        if ((st = check_cache(it.cache, dm, name, true, &ca[i])) != DELTAKV_OK) return st;
+        if (it.cache->n_built != t || it.cache->n_compressed != t)
+            return fail(DELTAKV_ERR_INVALID_ARG,
+                        "%s: appending position %lld needs n_built == n_compressed == %lld "
+                        "(have %lld, %lld)", name, (long long)t, (long long)t,
+                        (long long)it.cache->n_built, (long long)it.cache->n_compressed);
+        for (int j = 0; j < i; ++j)
+            if (items[j].cache == it.cache || items[j].cache->refs == it.cache->refs)
+                return fail(DELTAKV_ERR_INVALID_ARG, "items %d and %d name the same cache", j,
+                            i);
+        batched = batched && dk::append_batched_supported(dm, ma[i]) &&
+                  ma[i].hidden == ma[0].hidden && ma[i].act == ma[0].act;
+    }
+    const size_t need = dk::append_ws_bytes(dm, t, n_items);
+    const bool is_ref = t % dm.s == 0;
+    if (!is_ref && (workspace_bytes < need || !workspace))
+        return fail(DELTAKV_ERR_WORKSPACE, "append needs %zu workspace bytes, got %zu", need,
+                    workspace_bytes);
+    if (workspace && !aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (batched) {
+        for (int i0 = 0; i0 < n_items && e == hipSuccess; i0 += dk::kAppendMax) {
+            const int n = std::min(dk::kAppendMax, n_items - i0);
+            dk::AppendSet set{};
+            for (int i = 0; i < n; ++i) {
+                const int j = i0 + i;
+                set.x[i] = items[j].x;
+                set.refs[i] = ca[j].refs;
+                set.sqn[i] = ca[j].sqn;
+                set.lat[i] = ca[j].lat;
+                set.idx[i] = ca[j].idx;
+                set.w1[i] = ma[j].w1;
+                set.b1[i] = ma[j].b1;
+                set.w2[i] = ma[j].w2;
+                set.b2[i] = ma[j].b2;
+            }
+            if (is_ref) {
+                e = dk::launch_append_refs(dm, t, n, set, hs);
+            } else {
+                e = dk::launch_append_select(dm, t, n, set, workspace, hs);
+                if (e == hipSuccess)
+                    e = dk::launch_append_compress(dm, t, n, set, ma[0].hidden, ma[0].act, hs);
+            }
+        }
+    } else {
+        for (int i = 0; i < n_items && e == hipSuccess; ++i) {
+            e = dk::launch_build_refs(dm, items[i].x, t, t + 1, ca[i], hs);
+            if (e == hipSuccess && !is_ref)
+                e = dk::launch_compress(dm, items[i].x, t, t + 1, ma[i], ca[i], workspace,
+                                        workspace_bytes, nullptr, hs);
+        }
+    }
+    st = from_hip(e, "deltakv_append");
+    if (st == DELTAKV_OK)
+        for (int i = 0; i < n_items; ++i) items[i].cache->n_built = items[i].cache->n_compressed =
+            t + 1;
     return st;
 }
 

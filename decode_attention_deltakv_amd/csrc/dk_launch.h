@@ -125,4 +125,32 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
 hipError_t launch_peak_mfma(int blocks, int iters, float *sink, hipStream_t st);
 hipError_t launch_peak_gelu(int blocks, int iters, float *sink, hipStream_t st);
 
+// ---- batched one-token appends -----------------------------------------------
+// One position t appended to up to kAppendMax caches of the same shape in one
+// set of launches (a decode step appends one token to every layer and stream).
+// Passed to kernels by value.
+constexpr int kAppendMax = 32;
+struct AppendSet {
+    const void *x[kAppendMax];      // [B][H][1][d]: the row of position t of every unit
+    void *refs[kAppendMax];
+    float *sqn[kAppendMax];
+    void *lat[kAppendMax];
+    uint16_t *idx[kAppendMax];
+    const void *w1[kAppendMax];
+    const float *b1[kAppendMax];
+    const void *w2[kAppendMax];
+    const float *b2[kAppendMax];
+};
+// the batched kernels serve bf16 caches with the matrix-core Compressor's
+// shapes; other shapes run the per-cache calls
+bool append_batched_supported(const Dims &dm, const MlpArgs &comp);
+size_t append_ws_bytes(const Dims &dm, int64_t t, int n);
+size_t append_select_ws_bytes(const Dims &dm, int64_t t, int n);
+hipError_t launch_append_refs(const Dims &dm, int64_t t, int n, const AppendSet &set,
+                              hipStream_t st);
+hipError_t launch_append_select(const Dims &dm, int64_t t, int n, const AppendSet &set, void *ws,
+                                hipStream_t st);
+hipError_t launch_append_compress(const Dims &dm, int64_t t, int n, const AppendSet &set,
+                                  int hidden, int act, hipStream_t st);
+
 }  // namespace dk

@@ -91,9 +91,12 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
 // Each thread owns NI 16-byte chunks (token t, columns 8 c8 .. 8 c8 + 7) of
 // every tile.  KX: largest k (4 or 8).  Q4: latents stored as 4-bit codes
 // with a per-row bf16 shift and scale (d_c / 4 lanes per row quantise it).
+// The body of one block (bidx: the block's index over units x tile groups),
+// shared by the kernel over a range of one cache and the batched-append kernel
+// over one token of several caches, so both compute the same bits.
 template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
-__global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
-    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
+__device__ __forceinline__ void compress_mfma_body(
+    int bidx, const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
     int64_t Ncap, int64_t q0, int64_t nq, int U, int tiles_per_block,
     const bf16_t *__restrict__ w1, const float *__restrict__ b1, const bf16_t *__restrict__ w2,
@@ -112,14 +115,13 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
-    const int unit = blockIdx.x % U;
-    const int blk = blockIdx.x / U;
+    const int unit = bidx % U;
+    const int blk = bidx / U;
     const int hb = w * HW;
     const int64_t qend = q0 + nq;
     const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
     const bf16_t *ux = x + (int64_t)unit * nrows * D;
     const uint16_t *uidx = idx + (int64_t)unit * Ncap * k;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     bf16x8 a1[MT][KSD];
     f32x4 bias1[MT];
@@ -394,6 +396,61 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
     }
 }
 
+template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
+__global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
+    const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
+    const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
+    int64_t Ncap, int64_t q0, int64_t nq, int U, int tiles_per_block,
+    const bf16_t *__restrict__ w1, const float *__restrict__ b1, const bf16_t *__restrict__ w2,
+    const float *__restrict__ b2, bf16_t *__restrict__ lat) {
+    compress_mfma_body<D, HID, DC, KX, GELU, Q4>(blockIdx.x, x, t0, nrows, s, k, refs, Rcap, idx,
+                                                 Ncap, q0, nq, U, tiles_per_block, w1, b1, w2, b2,
+                                                 lat);
+}
+
+// Batched appends: the one token t (ordinal q) of every unit of cache
+// blockIdx.y of the set.  grid (U, n).
+template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
+__global__ __launch_bounds__(256, 2) void compress_append_kernel(AppendSet set, int64_t t, int s,
+                                                                 int k, int64_t Rcap,
+                                                                 int64_t Ncap, int64_t q, int U) {
+    const int item = blockIdx.y;
+    compress_mfma_body<D, HID, DC, KX, GELU, Q4>(
+        blockIdx.x, (const bf16_t *)set.x[item], t, 1, s, k, (const bf16_t *)set.refs[item],
+        Rcap, set.idx[item], Ncap, q, 1, U, 1, (const bf16_t *)set.w1[item], set.b1[item],
+        (const bf16_t *)set.w2[item], set.b2[item], (bf16_t *)set.lat[item]);
+}
+
+template <int D, int HID, int DC>
+void launch_cappend_t(const Dims &dm, int64_t t, int n, const AppendSet &set, int act,
+                      hipStream_t st) {
+    const int U = dm.B * dm.H;
+    const int64_t q = t - refs_upto(t + 1, dm.s);
+    auto kern = dm.k <= 4 ? (act == 0 ? compress_append_kernel<D, HID, DC, 4, true, false>
+                                      : compress_append_kernel<D, HID, DC, 4, false, false>)
+                          : (act == 0 ? compress_append_kernel<D, HID, DC, 8, true, false>
+                                      : compress_append_kernel<D, HID, DC, 8, false, false>);
+    if constexpr (DC <= 32) {
+        if (dm.lat_fmt)
+            kern = dm.k <= 4 ? (act == 0 ? compress_append_kernel<D, HID, DC, 4, true, true>
+                                         : compress_append_kernel<D, HID, DC, 4, false, true>)
+                             : (act == 0 ? compress_append_kernel<D, HID, DC, 8, true, true>
+                                         : compress_append_kernel<D, HID, DC, 8, false, true>);
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)U, (unsigned)n), dim3(256), 0, st, set, t, dm.s, dm.k,
+                       dm.R, dm.N, q, U);
+}
+
+template <int D, int HID>
+void launch_cappend_dc(const Dims &dm, int64_t t, int n, const AppendSet &set, int act,
+                       hipStream_t st) {
+    switch (dm.dc) {
+        case 16: launch_cappend_t<D, HID, 16>(dm, t, n, set, act, st); break;
+        case 32: launch_cappend_t<D, HID, 32>(dm, t, n, set, act, st); break;
+        default: launch_cappend_t<D, HID, 64>(dm, t, n, set, act, st); break;
+    }
+}
+
 template <int D, int HID, int DC>
 void launch_cmfma_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0, int64_t nq,
                     const MlpArgs &m, const CacheArgs &c, hipStream_t st) {
@@ -445,6 +502,36 @@ bool launch_compress_mfma(const Dims &dm, const void *x, int64_t t0, int64_t t1,
 }
 
 }  // namespace
+
+bool append_batched_supported(const Dims &dm, const MlpArgs &comp) {
+    // the matrix-core Compressor's conditions (launch_compress_mfma), and the
+    // 16-bit reference ordinals that the split scan writes
+    return dm.dtype == 1 && (comp.hidden == 128 || comp.hidden == 256) &&
+           (dm.dc == 16 || dm.dc == 32 || dm.dc == 64) && dm.N * dm.k * 2 <= INT32_MAX &&
+           dm.R * dm.d * 2 <= INT32_MAX && dm.N * dm.dc * 2 <= INT32_MAX;
+}
+
+size_t append_ws_bytes(const Dims &dm, int64_t t, int n) {
+    // the batched search's split lists for one launch set of up to kAppendMax
+    // caches, or a per-cache compress of one token; at a reference position
+    // (nothing to compress) the next position's size, so that the size never
+    // decreases with t
+    const int64_t tt = (dm.s > 1 && t % dm.s == 0) ? t + 1 : t;
+    return std::max(append_select_ws_bytes(dm, tt, std::min(n, kAppendMax)),
+                    compress_ws_bytes(dm, tt, tt + 1));
+}
+
+hipError_t launch_append_compress(const Dims &dm, int64_t t, int n, const AppendSet &set,
+                                  int hidden, int act, hipStream_t st) {
+    if (dm.d == 128) {
+        if (hidden == 256) launch_cappend_dc<128, 256>(dm, t, n, set, act, st);
+        else launch_cappend_dc<128, 128>(dm, t, n, set, act, st);
+    } else {
+        if (hidden == 256) launch_cappend_dc<64, 256>(dm, t, n, set, act, st);
+        else launch_cappend_dc<64, 128>(dm, t, n, set, act, st);
+    }
+    return hipGetLastError();
+}
 
 bool compress_q4_supported(const Dims &dm, const MlpArgs &comp) {
     // the matrix-core Compressor is the one that writes 4-bit rows: its

@@ -11,6 +11,22 @@
 namespace dk {
 namespace {
 
+// One reference row by one wave: copy, and the fp32 squared norm (lane-strided
+// partial sums, then a wave reduction).
+template <typename T>
+__device__ __forceinline__ void copy_ref_row(const T *__restrict__ src, T *__restrict__ dst,
+                                             float *__restrict__ sqn_dst, int d, int lane) {
+    float acc = 0.f;
+    for (int i = lane; i < d; i += 64) {
+        T v = src[i];
+        dst[i] = v;
+        float f = to_f32(v);
+        acc += f * f;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) *sqn_dst = acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void build_refs_kernel(const T *__restrict__ x, int64_t t0,
                                                          int64_t nrows, int s, int d,
@@ -22,20 +38,34 @@ __global__ __launch_bounds__(256) void build_refs_kernel(const T *__restrict__ x
     if (jj >= nj) return;
     const int64_t unit = blockIdx.y;
     const int64_t j = j0 + jj;
-    const T *src = x + (unit * nrows + (j * s - t0)) * d;
-    T *dst = refs + (unit * Rcap + j) * d;
-    float acc = 0.f;
-    for (int i = lane; i < d; i += 64) {
-        T v = src[i];
-        dst[i] = v;
-        float f = to_f32(v);
-        acc += f * f;
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) sqn[unit * Rcap + j] = acc;
+    copy_ref_row<T>(x + (unit * nrows + (j * s - t0)) * d, refs + (unit * Rcap + j) * d,
+                    sqn + unit * Rcap + j, d, lane);
+}
+
+// Batched appends at a reference position t: the row of every unit of every
+// cache of the set becomes reference t / s.  One wave per (unit, cache):
+// grid (ceil(U / 4), n).
+__global__ __launch_bounds__(256) void append_refs_kernel(AppendSet set, int64_t t, int s, int d,
+                                                          int64_t Rcap, int U) {
+    const int lane = threadIdx.x & 63;
+    const int unit = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= U) return;
+    const int item = blockIdx.y;
+    const int64_t j = t / s;
+    const bf16_t *x = (const bf16_t *)set.x[item];
+    copy_ref_row<bf16_t>(x + (int64_t)unit * d, (bf16_t *)set.refs[item] + (unit * Rcap + j) * d,
+                         set.sqn[item] + unit * Rcap + j, d, lane);
 }
 
 }  // namespace
+
+hipError_t launch_append_refs(const Dims &dm, int64_t t, int n, const AppendSet &set,
+                              hipStream_t st) {
+    const int U = dm.B * dm.H;
+    hipLaunchKernelGGL(append_refs_kernel, dim3((unsigned)((U + 3) / 4), (unsigned)n), dim3(256),
+                       0, st, set, t, dm.s, dm.d, dm.R, U);
+    return hipGetLastError();
+}
 
 hipError_t launch_build_refs(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                              const CacheArgs &c, hipStream_t st) {

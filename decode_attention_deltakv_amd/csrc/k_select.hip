@@ -47,9 +47,17 @@ void topk_split_plan(const Dims &dm, int64_t t1, int64_t nq, int *nsplit, int *c
 constexpr int kListLen4 = 7;
 constexpr int kListLen8 = 12;
 
+// Workspace sizes below are taken at the plans' upper bounds on the split
+// count, which never decrease as references accumulate, so a workspace sized
+// for a later position serves every earlier one.
 size_t topk_split_ws_bytes(const Dims &dm, int64_t t1, int64_t nq) {
-    int nsplit, chunk;
-    topk_split_plan(dm, t1, nq, &nsplit, &chunk);
+    const int64_t U0 = (int64_t)dm.B * dm.H;
+    const int64_t blocks = std::max<int64_t>(1, (nq + 255) / 256 * U0);
+    const int64_t R = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    // topk_split_plan's count n bounds its realised split count
+    const int64_t nsplit =
+        blocks < 512 ? std::max<int64_t>(1, std::min((768 + blocks - 1) / blocks, (R + 511) / 512))
+                     : 1;
     if (nsplit <= 1) return 0;
     const int LK = dm.k <= 4 ? kListLen4 : kListLen8;
     const int64_t U = (int64_t)dm.B * dm.H;
@@ -86,8 +94,9 @@ static void list_split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit)
 }
 
 size_t exact_list_ws_bytes(const Dims &dm, int64_t t1) {
-    int chunk, nsplit;
-    list_split_plan(dm, t1, &chunk, &nsplit);
+    // list_split_plan's chunk is at least 64 and at least rmax / 128
+    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    const int64_t nsplit = std::min<int64_t>((rmax + 63) / 64, 128);
     return (size_t)kListSplitCap * nsplit * kMaxK * (sizeof(double) + sizeof(int));
 }
 
@@ -545,6 +554,40 @@ __global__ __launch_bounds__(64) void select_merge_kernel(int nsplit, int k, int
     const int64_t unit = item / nq, q = q0 + item % nq;
     wave_merge_lists(nsplit, k, pd + item * nsplit * kMaxK, pj + item * nsplit * kMaxK,
                      idx + (unit * Ncap + q) * k);
+}
+
+// Batched appends: the exact top-k of the one new token t of every unit of
+// every cache of the set over its references [0, ceil(t / s)), split over
+// blocks as above.  grid (nsplit, U, n); lists at ((item U + unit) nsplit +
+// split) kMaxK.
+template <int D>
+__global__ __launch_bounds__(256) void append_split_kernel(AppendSet set, int64_t t, int s,
+                                                           int64_t Rcap, int chunk,
+                                                           double *__restrict__ pd,
+                                                           int *__restrict__ pj) {
+    __shared__ double xs[D];
+    __shared__ double wd[4];
+    __shared__ int wj[4];
+    const int item = blockIdx.z, U = gridDim.y;
+    const int64_t unit = blockIdx.y;
+    const int64_t ncand = (t + s - 1) / s;
+    const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
+    const size_t o = (size_t)(((int64_t)item * U + unit) * gridDim.x + blockIdx.x) * kMaxK;
+    block_range_topk<bf16_t, D>((const bf16_t *)set.x[item] + unit * D,
+                                (const bf16_t *)set.refs[item] + unit * Rcap * D, ja, jb, xs, wd,
+                                wj, pd + o, pj + o);
+}
+
+// The k best over the split lists of one (unit, cache), one wave each:
+// grid (U, n); the index row of token ordinal q.
+__global__ __launch_bounds__(64) void append_merge_kernel(AppendSet set, int nsplit, int k,
+                                                          int64_t q, int64_t Ncap,
+                                                          const double *__restrict__ pd,
+                                                          const int *__restrict__ pj) {
+    const int item = blockIdx.y, U = gridDim.x;
+    const int64_t unit = blockIdx.x;
+    const int64_t o = ((int64_t)item * U + unit) * nsplit * kMaxK;
+    wave_merge_lists(nsplit, k, pd + o, pj + o, set.idx[item] + (unit * Ncap + q) * k);
 }
 
 // Squared distance of one bf16 reference row (already loaded, u) from the
@@ -1570,10 +1613,54 @@ void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_
 size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
     if (nq <= 0 || nq > kSmallRange) return 0;
-    int chunk, nsplit;
-    split_plan(dm, t1, &chunk, &nsplit);
+    // split_plan's chunk is at least 256 and at least rmax / kSplitMax
+    const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
+    const int64_t nsplit = std::min<int64_t>((rmax + 255) / 256, kSplitMax);
     const size_t n = (size_t)dm.B * dm.H * nq * nsplit * kMaxK;
     return n * sizeof(double) + n * sizeof(int) + 256;
+}
+
+// Splits of a batched append: enough blocks to fill the GPU (about 4096 over
+// the set), whole 256-reference chunks.
+static int64_t append_split_bound(const Dims &dm, int64_t t, int n) {
+    const int64_t R = std::max<int64_t>(1, refs_upto(t, dm.s));
+    const int64_t items = std::max<int64_t>(1, (int64_t)n * dm.B * dm.H);
+    return std::max<int64_t>(1, std::min<int64_t>((4096 + items - 1) / items, (R + 255) / 256));
+}
+
+static void append_split_plan(const Dims &dm, int64_t t, int n, int *chunk, int *nsplit) {
+    const int64_t R = std::max<int64_t>(1, refs_upto(t, dm.s));
+    const int64_t ns = append_split_bound(dm, t, n);
+    int64_t c = (R + ns - 1) / ns;
+    c = (c + 63) / 64 * 64;
+    *chunk = (int)c;
+    *nsplit = (int)((R + c - 1) / c);   // <= ns
+}
+
+size_t append_select_ws_bytes(const Dims &dm, int64_t t, int n) {
+    const size_t m = (size_t)n * dm.B * dm.H * append_split_bound(dm, t, n) * kMaxK;
+    return m * sizeof(double) + m * sizeof(int) + 256;
+}
+
+hipError_t launch_append_select(const Dims &dm, int64_t t, int n, const AppendSet &set, void *ws,
+                                hipStream_t st) {
+    int chunk, nsplit;
+    append_split_plan(dm, t, n, &chunk, &nsplit);
+    const int U = dm.B * dm.H;
+    const size_t m = (size_t)n * U * nsplit * kMaxK;
+    double *pd = (double *)ws;
+    int *pj = (int *)((char *)ws + m * sizeof(double));
+    const dim3 grid((unsigned)nsplit, (unsigned)U, (unsigned)n);
+    if (dm.d == 128)
+        hipLaunchKernelGGL(append_split_kernel<128>, grid, dim3(256), 0, st, set, t, dm.s, dm.R,
+                           chunk, pd, pj);
+    else
+        hipLaunchKernelGGL(append_split_kernel<64>, grid, dim3(256), 0, st, set, t, dm.s, dm.R,
+                           chunk, pd, pj);
+    const int64_t q = t - refs_upto(t + 1, dm.s);   // token ordinal of position t
+    hipLaunchKernelGGL(append_merge_kernel, dim3((unsigned)U, (unsigned)n), dim3(64), 0, st, set,
+                       nsplit, dm.k, q, dm.N, pd, pj);
+    return hipGetLastError();
 }
 
 hipError_t launch_select_split(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,

@@ -195,6 +195,39 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
                                 deltakv_cache *cache, void *workspace,
                                 size_t workspace_bytes, uint32_t *stats, void *stream);
 
+/* One cache's share of a batched one-token append (host struct). */
+typedef struct {
+    const void *x;                   /* DEVICE [B][H][1][d]: the row of position t */
+    deltakv_cache *cache;            /* host struct; its filled lengths advance */
+    const deltakv_mlp *compressor;   /* in_dim = d, out_dim = d_c */
+} deltakv_append_item;
+
+/* Host-only.  Workspace that deltakv_append needs for position t over n_items
+ * caches of `shape`. */
+deltakv_status deltakv_append_workspace_bytes(const deltakv_shape *shape, int64_t t,
+                                              int32_t n_items, size_t *bytes);
+
+/* The decode-time growth of section 3 for several caches at once: position t
+ * (one new token per sequence) is appended to every cache of items[0 ..
+ * n_items) -- a decode step appends one token to every layer and to both the
+ * K and the V cache.  For each item the result is exactly (bit for bit) that
+ * of deltakv_build_refs(t, t + 1) followed by deltakv_compress(t, t + 1) on
+ * that cache: a reference position t is copied into the reference set, any
+ * other is compressed (steps 1-4 above) against the references [0, ceil(t /
+ * s)).  The caches share `shape`; bf16 caches whose compressors are matrix-
+ * core shaped (hidden 128 or 256, d_c 16, 32 or 64) and share hidden width
+ * and activation are served by three launches per 32 caches, other caches by
+ * the per-cache launches.
+ * Requires 1 <= n_items <= 4096, 0 <= t < capacity, every cache at n_built ==
+ * n_compressed == t, distinct caches (no two items with the same refs array),
+ * 16-byte aligned rows; every check happens before anything is enqueued
+ * (INVALID_ARG, UNSUPPORTED as for deltakv_compress).  Sets n_built =
+ * n_compressed = t + 1 in every cache.  workspace: device scratch of
+ * deltakv_append_workspace_bytes(shape, t, n_items) bytes. */
+deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_items,
+                              const deltakv_append_item *items, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Decode attention over the compressed cache ("Ricostruzione" in section 3,
  * with textbook softmax attention): for every query head g of sequence b,
  * with KV head h = g / (num_q_heads / H),

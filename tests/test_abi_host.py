@@ -408,3 +408,82 @@ def test_noalloc_decode_rejects_calls_beyond_its_scratch():
         dk.decode_attn_noalloc(sh, 32, 131072, _FakePtr(), _cache(filled=131072), dec,
                                _cache(filled=131072), dec, 0.088, _FakePtr())
     assert e.value.status == 4 and "scratch" in e.value.detail
+
+
+def _append_items(n, t, base=0x100000):
+    caches = []
+    for i in range(n):
+        c = _cache(addr=base + i * 0x1000, filled=0)
+        c.n_built = c.n_compressed = t
+        caches.append(c)
+    return caches, [_mlp(128, 256, 32) for _ in range(n)]
+
+
+def test_append_checks_every_item_before_anything_is_enqueued():
+    sh = _shape(capacity=4096)
+    ws = _FakePtr(0x30000, 1 << 30)
+    t = 1001                                   # not a reference position (s = 16)
+    # one cache behind the others: the call fails and no length moves
+    caches, comps = _append_items(5, t)
+    caches[3].n_compressed = t - 1
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append(sh, t, [_FakePtr()] * 5, caches, comps, ws)
+    assert e.value.status == 1 and "items[3]" in e.value.detail
+    assert [c.n_built for c in caches] == [t] * 5
+    assert [c.n_compressed for c in caches] == [t, t, t, t - 1, t]
+    # the same cache twice
+    caches, comps = _append_items(3, t)
+    caches[2] = caches[0]
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append(sh, t, [_FakePtr()] * 3, caches, comps, ws)
+    assert e.value.status == 1 and "same cache" in e.value.detail
+    # a misaligned row, a wrong compressor, a too-small workspace
+    caches, comps = _append_items(2, t)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append(sh, t, [_FakePtr(), _FakePtr(0x10008)], caches, comps, ws)
+    assert e.value.status == 1 and "items[1].x" in e.value.detail
+    comps[1] = _mlp(128, 256, 16)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append(sh, t, [_FakePtr()] * 2, caches, comps, ws)
+    assert e.value.status == 1
+    caches, comps = _append_items(2, t)
+    need = dk.append_workspace_bytes(sh, t, 2)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append(sh, t, [_FakePtr()] * 2, caches, comps, _FakePtr(0x30000, need - 1))
+    assert e.value.status == 4
+    assert all(c.n_built == t and c.n_compressed == t for c in caches)
+
+
+def test_append_position_and_item_count_limits():
+    sh = _shape(capacity=4096)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.append_workspace_bytes(sh, 4096, 4)       # position past the capacity
+    assert e.value.status == 3
+    for n in (0, 4097):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.append_workspace_bytes(sh, 100, n)
+        assert e.value.status == 1
+    caches, comps = _append_items(2, 50)
+    with pytest.raises(dk.DeltaKVError) as e:          # caches at 50, position 51
+        dk.append(sh, 51, [_FakePtr()] * 2, caches, comps, _FakePtr(0x30000, 1 << 30))
+    assert e.value.status == 1 and "n_built == n_compressed" in e.value.detail
+
+
+@pytest.mark.parametrize("kw", [dict(capacity=131072 + 1024, stride=8, k=8, d_c=16),
+                                dict(capacity=9000, stride=5, k=3, head_dim=64, num_kv_heads=2),
+                                dict(capacity=5000, stride=16, batch=3, dtype=dk.F32)])
+def test_append_workspace_covers_the_per_cache_compress_and_never_shrinks(kw):
+    # a workspace sized for the last position serves every earlier one,
+    # reference positions included
+    sh = _shape(**kw)
+    cap = sh.capacity
+    ts = sorted(set(list(range(0, min(cap, 700))) + list(range(0, cap, 97)) +
+                    list(range(cap - 40, cap))))
+    for n in (1, 7, 64):
+        prev = 0
+        for t in ts:
+            w = dk.append_workspace_bytes(sh, t, n)
+            assert w >= prev, (n, t)
+            if t % sh.stride:
+                assert w >= dk.compress_workspace_bytes(sh, t, t + 1)
+            prev = w
