@@ -33,6 +33,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 # Vector-ALU issue peak: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD
 # every 4 cycles (16 lanes per cycle) at 2.4 GHz = 614.4 G wave-instructions/s.
 VALU_PEAK_GINSTR = 256 * 4 * 2.4 / 4
@@ -121,6 +122,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train-rows", type=int, default=65536,
+                    help="residual rows of the Compressor / Decompressor training leg (0: skip)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit latent leg (layer 0 compressed again, decode timed)")
     ap.add_argument("--sparse-select", type=int, default=4096,
@@ -661,6 +664,67 @@ def main():
             f"{2 * lay(sh4) / unc:.3f} of uncompressed")
         del c4, dws4
 
+    # Compressor / Decompressor MSE training on residual rows of layer 0's K
+    # cache: the residual call, then timed training steps (fp32 matrix cores)
+    training = None
+    if not wl.appends and a.train_rows > 0:
+        dk = S.dk
+        c0 = S.cache[0][0]
+        nres = wl.T - (-(-wl.T // wl.stride))
+        res = torch.empty(wl.batch, wl.kv_heads, nres, wl.head_dim, device="cuda")
+        e0, e1 = ev(), ev()
+        for rep_ in range(2):
+            e0.record(stream)
+            dk.residuals(S.shape, S.x[0][0], 0, wl.T, c0, res)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        res_ms = e0.elapsed_time(e1)
+        n = min(a.train_rows, res.numel() // wl.head_dim)
+        delta = res.reshape(-1, wl.head_dim)[:n].contiguous()
+        del res
+        # fp32 master copies (the bench's own weights stay untouched)
+        f32 = lambda m: dk.MlpF32(m.w1.float().clone(), m.b1.float().clone(),
+                                  m.w2.float().clone(), m.b2.float().clone(), m.act)
+        tc, td = f32(S.comp[0][0]), f32(S.dec[0][0])
+        twsb, npar = dk.train_workspace_bytes(tc, td, n)
+        tws = dk.workspace(twsb)
+        vel = torch.zeros(npar, device="cuda")
+        tloss = torch.zeros(1, device="cuda")
+        curve = []
+        for i in range(3):                    # untimed
+            dk.train_step(delta, tc, td, 0.1, tws, 0.9, vel, tloss)
+            curve.append(float(tloss.item()))
+        n_t = 20
+        ts, te = [ev() for _ in range(n_t)], [ev() for _ in range(n_t)]
+        losses = torch.zeros(n_t, device="cuda")
+        for i in range(n_t):
+            ts[i].record(stream)
+            dk.train_step(delta, tc, td, 0.1, tws, 0.9, vel, losses[i:i + 1])
+            te[i].record(stream)
+        torch.cuda.synchronize()
+        curve += losses.cpu().tolist()
+        step_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(ts, te)]))
+        d_, h1, dc_, h2 = wl.head_dim, wl.hidden, wl.d_c, wl.hidden
+        fwd = d_ * h1 + h1 * dc_ + dc_ * h2 + h2 * d_
+        wgr = h1 * (d_ + 1) + dc_ * (h1 + 1) + h2 * (dc_ + 1) + d_ * (h2 + 1)
+        ingr = d_ * h2 + h2 * dc_ + dc_ * h1
+        tflop = 2.0 * n * (fwd + wgr + ingr)
+        # x rows, index rows, the reference rows once, fp32 residual rows out
+        res_bytes = (wl.batch * wl.kv_heads * (wl.T * wl.head_dim * 2 + nres * wl.k * 2 +
+                                               (wl.T - nres) * wl.head_dim * 2 +
+                                               nres * wl.head_dim * 4))
+        training = {"rows": n, "step_ms": step_ms, "flops_per_step": tflop,
+                    "roofline": {"bound": "mfma", "achieved": tflop / (step_ms * 1e-3) / 1e12,
+                                 "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": tflop / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS},
+                    "loss_first": curve[0], "loss_last": curve[-1], "steps_run": len(curve),
+                    "lr": 0.1, "momentum": 0.9,
+                    "residuals_ms": res_ms,
+                    "residuals_gbs": res_bytes / (res_ms * 1e-3) / 1e9}
+        log(f"[bench] training: {step_ms:.3f} ms per step on {n} rows, loss {curve[0]:.4f} -> "
+            f"{curve[-1]:.4f} over {len(curve)} steps")
+        del tws, delta, vel
+
     # one decode step (every layer) captured in a HIP graph and replayed, with
     # fresh queries copied into the captured query buffer before each replay
     graph_ms = None
@@ -777,6 +841,7 @@ def main():
         "sparse_decode": sparse,
         "q4_latents": q4,
         "streaming": streaming,
+        "training": training,
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

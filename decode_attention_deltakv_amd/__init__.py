@@ -75,6 +75,12 @@ class CCache(ctypes.Structure):
                 ("n_built", ctypes.c_int64), ("n_compressed", ctypes.c_int64)]
 
 
+class CMlpF32(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("in_dim", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("out_dim", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
 class CAppendItem(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("cache", ctypes.POINTER(CCache)),
                 ("compressor", ctypes.POINTER(CMlp))]
@@ -142,7 +148,16 @@ def lib():
                                                  ctypes.POINTER(_SZ)]
     L.deltakv_append.argtypes = [sp, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.POINTER(CAppendItem), _P, _SZ, _P]
-    for name in ("deltakv_append_workspace_bytes", "deltakv_append",
+    L.deltakv_residuals.argtypes = [sp, _P, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.POINTER(CCache), _P, _P]
+    L.deltakv_train_workspace_bytes.argtypes = [ctypes.POINTER(CMlpF32), ctypes.POINTER(CMlpF32),
+                                                ctypes.c_int64, ctypes.POINTER(_SZ),
+                                                ctypes.POINTER(ctypes.c_int64)]
+    L.deltakv_train_step.argtypes = [ctypes.c_int64, _P, ctypes.POINTER(CMlpF32),
+                                     ctypes.POINTER(CMlpF32), ctypes.c_float, ctypes.c_float,
+                                     _P, _P, _P, ctypes.POINTER(_P), _P, _SZ, _P]
+    for name in ("deltakv_residuals", "deltakv_train_workspace_bytes", "deltakv_train_step",
+                 "deltakv_append_workspace_bytes", "deltakv_append",
                  "deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
                  "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
@@ -367,6 +382,54 @@ def append(shape: Shape, t: int, xs, caches, compressors, workspace: Optional[to
     """Position t appended to every cache (deltakv_append): xs[i] [B, H, 1, d]
     is the new row of caches[i], compressed with compressors[i]."""
     AppendBatch(shape, caches, compressors)(t, xs, workspace)
+
+
+def residuals(shape: Shape, x: torch.Tensor, t0: int, t1: int, cache: Cache,
+              out: Optional[torch.Tensor]):
+    """Residual rows x_p - KV_R(p) of the non-reference positions of [t0, t1)
+    into out (fp32 [B, H, n_out, d]; None when there are none)."""
+    cs, cc = shape.c(), cache.c()
+    _check(lib().deltakv_residuals(ctypes.byref(cs), _ptr(x), t0, t1, ctypes.byref(cc),
+                                   _ptr(out), _stream()))
+
+
+class MlpF32:
+    """fp32 master weights of a Linear -> act -> Linear block (w1 [hidden, in],
+    b1 [hidden], w2 [out, hidden], b2 [out]), trained in place."""
+
+    def __init__(self, w1, b1, w2, b2, act=ACT_GELU):
+        self.w1, self.b1, self.w2, self.b2, self.act = w1, b1, w2, b2, act
+
+    def c(self) -> CMlpF32:
+        return CMlpF32(_ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2),
+                       self.w1.shape[1], self.w1.shape[0], self.w2.shape[0], self.act)
+
+
+def train_workspace_bytes(compressor: MlpF32, decompressor: MlpF32, n_rows: int):
+    """(workspace bytes, packed parameter count) of deltakv_train_step."""
+    v, npar = _SZ(), ctypes.c_int64()
+    cc, dd = compressor.c(), decompressor.c()
+    _check(lib().deltakv_train_workspace_bytes(ctypes.byref(cc), ctypes.byref(dd), n_rows,
+                                               ctypes.byref(v), ctypes.byref(npar)))
+    return v.value, npar.value
+
+
+def train_step(delta: torch.Tensor, compressor: MlpF32, decompressor: MlpF32, lr: float,
+               workspace: torch.Tensor, momentum: float = 0.0,
+               velocity: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
+               grad: Optional[torch.Tensor] = None, bf16_weights=None):
+    """One MSE training step (deltakv_train_step) on delta [n, d] fp32.
+    bf16_weights: None or four tensors (or None) receiving bf16 copies of
+    W1c, W2c, W1d, W2d."""
+    cc, dd = compressor.c(), decompressor.c()
+    bw = None
+    if bf16_weights is not None:
+        bw = (_P * 4)(*[_ptr(t) for t in bf16_weights])
+    _check(lib().deltakv_train_step(delta.shape[0], _ptr(delta), ctypes.byref(cc),
+                                    ctypes.byref(dd), float(lr), float(momentum),
+                                    _ptr(velocity), _ptr(loss), _ptr(grad), bw,
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream()))
 
 
 def decode_attn(shape: Shape, num_q_heads: int, n_tokens: int, q: torch.Tensor, k_cache: Cache,

@@ -330,6 +330,26 @@ deltakv_status deltakv_compress(const deltakv_shape *shape, const void *x, int64
     return st;
 }
 
+deltakv_status deltakv_residuals(const deltakv_shape *shape, const void *x, int64_t t0,
+                                 int64_t t1, const deltakv_cache *cache, float *out,
+                                 void *stream) {
+    dk::Dims dm;
+    dk::CacheArgs ca;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if ((st = check_range(dm, t0, t1)) != DELTAKV_OK) return st;
+    if (!x) return fail(DELTAKV_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned16(x)) return fail(DELTAKV_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    if ((st = check_cache(cache, dm, "cache", true, &ca, t1)) != DELTAKV_OK) return st;
+    const int64_t nq = dk::toks_upto(t1, dm.s) - dk::toks_upto(t0, dm.s);
+    if (nq == 0) return ok();
+    if (!out) return fail(DELTAKV_ERR_INVALID_ARG, "out is NULL");
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return fail(DELTAKV_ERR_INVALID_ARG, "out must be 4-byte aligned");
+    return from_hip(dk::launch_residuals(dm, x, t0, t1, ca, out, (hipStream_t)stream),
+                    "deltakv_residuals");
+}
+
 deltakv_status deltakv_append_workspace_bytes(const deltakv_shape *shape, int64_t t,
                                               int32_t n_items, size_t *bytes) {
     dk::Dims dm;
@@ -430,6 +450,109 @@ deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_i
         for (int i = 0; i < n_items; ++i) items[i].cache->n_built = items[i].cache->n_compressed =
             t + 1;
     return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+deltakv_status check_mlp_f32(const deltakv_mlp_f32 *m, const char *name, dk::MlpF32 *a) {
+    if (!m) return fail(DELTAKV_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!m->w1 || !m->b1 || !m->w2 || !m->b2)
+        return fail(DELTAKV_ERR_INVALID_ARG, "%s: w1, b1, w2 and b2 must all be given", name);
+    if (!aligned4(m->w1) || !aligned4(m->b1) || !aligned4(m->w2) || !aligned4(m->b2))
+        return fail(DELTAKV_ERR_INVALID_ARG, "%s: arrays must be 4-byte aligned", name);
+    if (m->in_dim < 1 || m->in_dim > 4096 || m->hidden < 1 || m->hidden > 4096 ||
+        m->out_dim < 1 || m->out_dim > 4096)
+        return fail(DELTAKV_ERR_INVALID_ARG, "%s: dimensions %d -> %d -> %d not in [1, 4096]",
+                    name, m->in_dim, m->hidden, m->out_dim);
+    if (m->act != DELTAKV_ACT_GELU && m->act != DELTAKV_ACT_IDENTITY)
+        return fail(DELTAKV_ERR_INVALID_ARG, "%s activation %d unknown", name, m->act);
+    *a = dk::MlpF32{m->w1, m->b1, m->w2, m->b2, m->in_dim, m->hidden, m->out_dim, m->act};
+    return DELTAKV_OK;
+}
+
+deltakv_status check_pair(const deltakv_mlp_f32 *c, const deltakv_mlp_f32 *d, int64_t n_rows,
+                          dk::MlpF32 *ca, dk::MlpF32 *da) {
+    deltakv_status st;
+    if ((st = check_mlp_f32(c, "compressor", ca)) != DELTAKV_OK) return st;
+    if ((st = check_mlp_f32(d, "decompressor", da)) != DELTAKV_OK) return st;
+    if (d->in_dim != c->out_dim || d->out_dim != c->in_dim)
+        return fail(DELTAKV_ERR_INVALID_ARG,
+                    "decompressor maps %d -> %d; the compressor maps %d -> %d", d->in_dim,
+                    d->out_dim, c->in_dim, c->out_dim);
+    if (n_rows < 1 || n_rows > ((int64_t)1 << 31))
+        return fail(DELTAKV_ERR_INVALID_ARG, "n_rows %lld not in [1, 2^31]",
+                    (long long)n_rows);
+    return DELTAKV_OK;
+}
+
+int64_t n_params(const dk::MlpF32 &c, const dk::MlpF32 &d) {
+    return (int64_t)c.hidden * (c.in + 1) + (int64_t)c.out * (c.hidden + 1) +
+           (int64_t)d.hidden * (d.in + 1) + (int64_t)d.out * (d.hidden + 1);
+}
+
+}  // namespace
+
+extern "C" {
+
+deltakv_status deltakv_train_workspace_bytes(const deltakv_mlp_f32 *compressor,
+                                             const deltakv_mlp_f32 *decompressor,
+                                             int64_t n_rows, size_t *bytes,
+                                             int64_t *n_params_out) {
+    dk::MlpF32 ca, da;
+    deltakv_status st = check_pair(compressor, decompressor, n_rows, &ca, &da);
+    if (st != DELTAKV_OK) return st;
+    if (!bytes) return fail(DELTAKV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dk::train_ws_bytes(ca.in, ca.hidden, ca.out, da.hidden, n_rows);
+    if (n_params_out) *n_params_out = n_params(ca, da);
+    return ok();
+}
+
+deltakv_status deltakv_train_step(int64_t n_rows, const float *delta,
+                                  const deltakv_mlp_f32 *compressor,
+                                  const deltakv_mlp_f32 *decompressor, float lr, float momentum,
+                                  float *velocity, float *loss, float *grad,
+                                  void *const *bf16_weights, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    dk::TrainArgs a{};
+    deltakv_status st = check_pair(compressor, decompressor, n_rows, &a.comp, &a.dec);
+    if (st != DELTAKV_OK) return st;
+    if (!delta || !aligned4(delta))
+        return fail(DELTAKV_ERR_INVALID_ARG, "delta must be a 4-byte aligned device array");
+    if (!std::isfinite(lr)) return fail(DELTAKV_ERR_INVALID_ARG, "lr must be finite");
+    if (!(momentum >= 0.f && momentum < 1.f))
+        return fail(DELTAKV_ERR_INVALID_ARG, "momentum %g not in [0, 1)", (double)momentum);
+    if (momentum != 0.f && !velocity)
+        return fail(DELTAKV_ERR_INVALID_ARG, "momentum %g needs a velocity array",
+                    (double)momentum);
+    if ((velocity && !aligned4(velocity)) || (loss && !aligned4(loss)) ||
+        (grad && !aligned4(grad)))
+        return fail(DELTAKV_ERR_INVALID_ARG, "velocity, loss and grad must be 4-byte aligned");
+    if (bf16_weights)
+        for (int i = 0; i < 4; ++i)
+            if (bf16_weights[i] && (reinterpret_cast<uintptr_t>(bf16_weights[i]) & 1u))
+                return fail(DELTAKV_ERR_INVALID_ARG, "bf16_weights[%d] must be 2-byte aligned",
+                            i);
+    const size_t need =
+        dk::train_ws_bytes(a.comp.in, a.comp.hidden, a.comp.out, a.dec.hidden, n_rows);
+    if (workspace_bytes < need || !workspace)
+        return fail(DELTAKV_ERR_WORKSPACE, "train step needs %zu workspace bytes, got %zu",
+                    need, workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(DELTAKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    a.n = n_rows;
+    a.delta = delta;
+    a.lr = lr;
+    a.momentum = momentum;
+    a.velocity = velocity;
+    a.grad = grad;
+    a.loss = loss;
+    for (int i = 0; i < 4; ++i) a.wexp[i] = bf16_weights ? bf16_weights[i] : nullptr;
+    a.ws = workspace;
+    return from_hip(dk::launch_train_step(a, (hipStream_t)stream), "deltakv_train_step");
 }
 
 }  // extern "C"

@@ -153,4 +153,26 @@ hipError_t launch_append_select(const Dims &dm, int64_t t, int n, const AppendSe
 hipError_t launch_append_compress(const Dims &dm, int64_t t, int n, const AppendSet &set,
                                   int hidden, int act, hipStream_t st);
 
+// ---- residual rows and Compressor / Decompressor training (k_train.hip) -------
+// residual rows of the compressed tokens of [t0, t1): out [B][H][nq][d] fp32
+hipError_t launch_residuals(const Dims &dm, const void *x, int64_t t0, int64_t t1,
+                            const CacheArgs &c, float *out, hipStream_t st);
+struct MlpF32 {
+    float *w1, *b1, *w2, *b2;   // [hidden][in], [hidden], [out][hidden], [out]
+    int in, hidden, out, act;
+};
+struct TrainArgs {
+    int64_t n;            // residual rows
+    const float *delta;   // [n][comp.in]
+    MlpF32 comp, dec;     // comp: d -> d_c, dec: d_c -> d
+    float lr, momentum;
+    float *velocity;      // packed parameters, or null (momentum 0)
+    float *grad;          // packed parameters, or null
+    float *loss;          // [1], or null
+    void *wexp[4];        // bf16 copies of W1c, W2c, W1d, W2d written after the update, or null
+    void *ws;
+};
+size_t train_ws_bytes(int d, int h1, int dc, int h2, int64_t n);
+hipError_t launch_train_step(const TrainArgs &a, hipStream_t st);
+
 }  // namespace dk

@@ -393,6 +393,74 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
                                           int32_t *positions, float *scores, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* Residual rows of the compressed tokens (section 3, "Processo di
+ * Compressione", steps 2-3): for every non-reference position p in [t0, t1),
+ * in position order, out row = x_p - KV_R(p), KV_R the mean of the reference
+ * rows listed in the cache's idx row of p (fp32 sum in slot order over the
+ * used slots, times 1 / k_eff).  These are the rows the Compressor maps and
+ * the training below fits.
+ *   x:   as for deltakv_build_refs (read-only);
+ *   out: DEVICE fp32 [B][H][n_out][d], n_out = the number of non-reference
+ *        positions in [t0, t1) (nothing is written when n_out = 0).
+ * Requires 0 <= t0 < t1 <= cache->n_compressed (the idx rows were written);
+ * INVALID_ARG otherwise. */
+deltakv_status deltakv_residuals(const deltakv_shape *shape, const void *x, int64_t t0,
+                                 int64_t t1, const deltakv_cache *cache, float *out,
+                                 void *stream);
+
+/* fp32 master weights of one Linear -> act -> Linear block (DEVICE arrays,
+ * updated in place by deltakv_train_step): w1 [hidden][in_dim], b1 [hidden],
+ * w2 [out_dim][hidden], b2 [out_dim], all non-NULL. */
+typedef struct {
+    float *w1;
+    float *b1;
+    float *w2;
+    float *b2;
+    int32_t in_dim;
+    int32_t hidden;
+    int32_t out_dim;
+    int32_t act;         /* deltakv_act */
+} deltakv_mlp_f32;
+
+/* Host-only.  Workspace of deltakv_train_step over n_rows rows, and the
+ * number of packed parameters (the length of the velocity and gradient
+ * vectors: W1c, b1c, W2c, b2c, W1d, b1d, W2d, b2d, each row-major, in that
+ * order). */
+deltakv_status deltakv_train_workspace_bytes(const deltakv_mlp_f32 *compressor,
+                                             const deltakv_mlp_f32 *decompressor,
+                                             int64_t n_rows, size_t *bytes,
+                                             int64_t *n_params);
+
+/* One training step of a Compressor / Decompressor pair by the
+ * reconstruction-fidelity (MSE) term of the training objective (section 3,
+ * "Obiettivo di Training Ibrido"; the next-token term needs a language model
+ * and is not part of this library).  With D = delta [n_rows][d] (fp32, e.g.
+ * from deltakv_residuals), the reconstruction is
+ *   Y = decompressor(compressor(D)),  and  L = mean over n_rows x d of (Y - D)^2,
+ * which equals the mean squared error of the rebuilt rows KV_R + Y against
+ * the input rows.  The step computes the exact gradient g of L (fp32
+ * products on the matrix cores, partial sums added in a fixed order: the
+ * result is deterministic), then velocity v <- momentum v + g (v = g when
+ * velocity is NULL) and every parameter w <- w - lr v.
+ *   compressor:   in_dim d, out_dim d_c;  decompressor: in_dim d_c, out_dim d;
+ *   velocity:     DEVICE fp32 [n_params], read and written; NULL requires
+ *                 momentum 0;
+ *   loss:         NULL or DEVICE fp32 [1]: L at the weights before the step;
+ *   grad:         NULL or DEVICE fp32 [n_params]: g;
+ *   bf16_weights: NULL or 4 DEVICE pointers (W1c, W2c, W1d, W2d, each NULL or
+ *                 of its matrix's size) that receive bf16 copies (round to
+ *                 nearest even) of the updated matrices, ready for
+ *                 deltakv_compress and the decode calls;
+ *   workspace:    deltakv_train_workspace_bytes bytes.
+ * Requires n_rows >= 1, matching dimensions, hidden widths and dimensions
+ * in [1, 4096], finite lr, 0 <= momentum < 1; INVALID_ARG otherwise. */
+deltakv_status deltakv_train_step(int64_t n_rows, const float *delta,
+                                  const deltakv_mlp_f32 *compressor,
+                                  const deltakv_mlp_f32 *decompressor, float lr, float momentum,
+                                  float *velocity, float *loss, float *grad,
+                                  void *const *bf16_weights, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Measurement helpers (not part of the method): loops that time the chip's
  * own rates as denominators for roofline figures.
  *   DELTAKV_PEAK_MFMA_BF16: each wave issues iters x 8 independent

@@ -40,6 +40,16 @@ Parity status per function (what pins it; the tests under tests/ hold them):
                     rows exact.
   bf16_from_f64     pinned: exact rational rounding on random and near-midpoint
                     values; torch's fp32 -> bf16 rounding on fp32 inputs.
+  reconstruction_loss pinned: zero for an orthogonal linear pair with d_c = d;
+                    the oracle's own pinned MLP forward pass.
+  reconstruction_grad pinned: central finite differences of
+                    reconstruction_loss (which shares no code with it) on
+                    every parameter of small GELU and identity pairs; zero
+                    at the orthogonal pair; its loss equals
+                    reconstruction_loss.
+  gelu_vec / gelu_deriv pinned: the C oracle's gelu; finite differences.
+  train_step        pinned: small steps lower the loss (descent direction);
+                    the update is the stated rule on the pinned gradient.
   Latent and decode values under random GELU weights have no printed value to
   compare with; they are pinned only through the pieces above.
 """
@@ -387,3 +397,101 @@ def decode_head_window(q_heads, k_refs, k_lat, k_idx, k_dec: MLP, v_refs, v_lat,
     vals = np.concatenate([vhat, _f64(v_win)], axis=0)
     return attention(q_heads, keys, vals, scale)
 
+
+
+# ---------------------------------------------------------------- training (MSE)
+# DeltaKV page, section 3, "Obiettivo di Training Ibrido": the Compressor and
+# Decompressor are trained with a reconstruction-fidelity (MSE) term next to a
+# next-token term.  Only the MSE term is defined without a language model:
+# for residual rows D [n, d], the loss is the mean over the n x d entries of
+# (decompressor(compressor(D)) - D)^2, which is the mean squared error of the
+# rebuilt rows KV_R + decompressor(latent) against the input rows.  The pages
+# name no optimiser; the plainest reading is gradient descent, here with an
+# optional heavy-ball momentum: v <- mu v + g, w <- w - lr v (mu = 0: plain).
+
+def _erf_vec(u):
+    from scipy.special import erf
+    return erf(u)
+
+
+def gelu_vec(u):
+    """GELU, erf form, elementwise in fp64."""
+    u = _f64(u)
+    return 0.5 * u * (1.0 + _erf_vec(u / np.sqrt(2.0)))
+
+
+def gelu_deriv(u):
+    """d GELU / du = Phi(u) + u phi(u) (Phi, phi: the standard normal cdf and
+    density), elementwise in fp64."""
+    u = _f64(u)
+    return 0.5 * (1.0 + _erf_vec(u / np.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / np.sqrt(2.0 * np.pi)
+
+
+def reconstruction_loss(delta, comp: MLP, dec: MLP) -> float:
+    """The MSE term: mean over all entries of (dec(comp(delta)) - delta)^2,
+    with the forward pass of the oracle's MLP."""
+    delta = _f64(delta)
+    y = mlp(mlp(delta, comp), dec)
+    return float(np.mean((y - delta) ** 2))
+
+
+def pack_params(comp: MLP, dec: MLP) -> np.ndarray:
+    """W1c, b1c, W2c, b2c, W1d, b1d, W2d, b2d, each row-major, concatenated."""
+    return np.concatenate([a.reshape(-1) for a in (comp.w1, comp.b1, comp.w2, comp.b2,
+                                                   dec.w1, dec.b1, dec.w2, dec.b2)])
+
+
+def unpack_params(vec, comp: MLP, dec: MLP):
+    """New (comp, dec) with the shapes and activations of comp, dec and the
+    values of vec (the order of pack_params)."""
+    vec = _f64(vec)
+    shapes = [a.shape for a in (comp.w1, comp.b1, comp.w2, comp.b2, dec.w1, dec.b1, dec.w2,
+                                dec.b2)]
+    parts, o = [], 0
+    for sh in shapes:
+        n = int(np.prod(sh))
+        parts.append(vec[o:o + n].reshape(sh))
+        o += n
+    assert o == len(vec)
+    return (MLP(parts[0], parts[1], parts[2], parts[3], comp.act),
+            MLP(parts[4], parts[5], parts[6], parts[7], dec.act))
+
+
+def reconstruction_grad(delta, comp: MLP, dec: MLP):
+    """(loss, packed gradient) of the MSE term by backpropagation through the
+    two blocks: each layer u = a W^T + b passes dL/du back as dL/da =
+    (dL/du) W and contributes dL/dW = (dL/du)^T a, dL/db = sum over rows of
+    dL/du; an activation passes dL/dphi times phi'(u)."""
+    D = _f64(delta)
+    n, d = D.shape
+    phi = lambda u, act: gelu_vec(u) if act == ACT_GELU else u
+    dphi = lambda u, act: gelu_deriv(u) if act == ACT_GELU else np.ones_like(u)
+    a1 = D @ comp.w1.T + comp.b1
+    h1 = phi(a1, comp.act)
+    z = h1 @ comp.w2.T + comp.b2
+    a2 = z @ dec.w1.T + dec.b1
+    h2 = phi(a2, dec.act)
+    y = h2 @ dec.w2.T + dec.b2
+    e = y - D
+    loss = float(np.mean(e * e))
+    gy = 2.0 * e / (n * d)
+    g_w2d, g_b2d = gy.T @ h2, gy.sum(axis=0)
+    ga2 = (gy @ dec.w2) * dphi(a2, dec.act)
+    g_w1d, g_b1d = ga2.T @ z, ga2.sum(axis=0)
+    gz = ga2 @ dec.w1
+    g_w2c, g_b2c = gz.T @ h1, gz.sum(axis=0)
+    ga1 = (gz @ comp.w2) * dphi(a1, comp.act)
+    g_w1c, g_b1c = ga1.T @ D, ga1.sum(axis=0)
+    grad = np.concatenate([a.reshape(-1) for a in (g_w1c, g_b1c, g_w2c, g_b2c, g_w1d, g_b1d,
+                                                   g_w2d, g_b2d)])
+    return loss, grad
+
+
+def train_step(delta, comp: MLP, dec: MLP, lr: float, momentum: float = 0.0, velocity=None):
+    """One step: (loss before the step, gradient, new comp, new dec, new
+    velocity)."""
+    loss, g = reconstruction_grad(delta, comp, dec)
+    v = g if velocity is None else momentum * _f64(velocity) + g
+    new = pack_params(comp, dec) - lr * v
+    c2, d2 = unpack_params(new, comp, dec)
+    return loss, g, c2, d2, v
