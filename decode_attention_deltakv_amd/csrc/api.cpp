@@ -344,8 +344,7 @@ deltakv_status deltakv_residuals(const deltakv_shape *shape, const void *x, int6
     const int64_t nq = dk::toks_upto(t1, dm.s) - dk::toks_upto(t0, dm.s);
     if (nq == 0) return ok();
     if (!out) return fail(DELTAKV_ERR_INVALID_ARG, "out is NULL");
-    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
-        return fail(DELTAKV_ERR_INVALID_ARG, "out must be 4-byte aligned");
+    if (!aligned16(out)) return fail(DELTAKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
     return from_hip(dk::launch_residuals(dm, x, t0, t1, ca, out, (hipStream_t)stream),
                     "deltakv_residuals");
 }

@@ -204,9 +204,30 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateP p) {
     if (isw && L.wexp) L.wexp[e] = f2bf(nv);
 }
 
-// Residual rows: one wave per compressed token of [q0, q0 + nq): x_p minus the
-// mean of its reference rows (fp32 sum over the used slots in slot order,
-// times 1 / k_eff).  grid (ceil(nq / 4), units).
+// Residual rows: 8 consecutive columns per thread (16-byte row loads), d / 8
+// threads per compressed token of [q0, q0 + nq): x_p minus the mean of its
+// reference rows (fp32 sum over the used slots in slot order, times 1 /
+// k_eff).  grid (ceil(nq / (256 / (d / 8))), units).
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float (&v)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = a[i];
+            v[4 + i] = b[i];
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void residual_kernel(const T *__restrict__ x, int64_t t0,
                                                        int64_t nrows, int s, int k, int d,
@@ -214,26 +235,41 @@ __global__ __launch_bounds__(256) void residual_kernel(const T *__restrict__ x, 
                                                        const uint16_t *__restrict__ idx,
                                                        int64_t Ncap, int64_t q0, int64_t nq,
                                                        float *__restrict__ out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t qq = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int cpr = d / 8;                     // threads per token
+    const int tpb = 256 / cpr;                 // tokens per block
+    const int64_t qq = (int64_t)blockIdx.x * tpb + threadIdx.x / cpr;
     if (qq >= nq) return;
+    const int c0 = 8 * (threadIdx.x % cpr);
     const int64_t unit = blockIdx.y;
     const int64_t q = q0 + qq;
     const int64_t pos = tok_pos(q, s);
-    const T *xr = x + (unit * nrows + (pos - t0)) * d;
     const uint16_t *ir = idx + (unit * Ncap + q) * k;
-    const T *ur = refs + unit * Rcap * d;
+    const T *ur = refs + unit * Rcap * d + c0;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     int keff = 0;
-    for (int i = 0; i < k; ++i) keff += ir[i] != kIdxUnused ? 1 : 0;
-    const float inv = 1.f / (float)max(keff, 1);
-    for (int c = lane; c < d; c += 64) {
-        float acc = 0.f;
-        for (int i = 0; i < k; ++i) {
-            const uint16_t j = ir[i];
-            if (j != kIdxUnused) acc += to_f32(ur[(int64_t)j * d + c]);
-        }
-        out[(unit * nq + qq) * d + c] = to_f32(xr[c]) - acc * inv;
+    for (int sl = 0; sl < k; ++sl) {
+        const uint16_t j = ir[sl];
+        if (j == kIdxUnused) continue;
+        ++keff;
+        float r[8];
+        load8<T>(ur + (int64_t)j * d, r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += r[i];
     }
+    const float inv = 1.f / (float)max(keff, 1);
+    float xv[8];
+    load8<T>(x + (unit * nrows + (pos - t0)) * d + c0, xv);
+    float *o = out + (unit * nq + qq) * d + c0;
+    f32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = xv[i] - acc[i] * inv;
+        hi[i] = xv[4 + i] - acc[4 + i] * inv;
+    }
+    *reinterpret_cast<f32x4 *>(o) = lo;
+    *reinterpret_cast<f32x4 *>(o + 4) = hi;
 }
 
 template <int EP>
@@ -296,7 +332,8 @@ hipError_t launch_residuals(const Dims &dm, const void *x, int64_t t0, int64_t t
     const int64_t q0 = toks_upto(t0, dm.s);
     const int64_t nq = toks_upto(t1, dm.s) - q0;
     if (nq <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((nq + 3) / 4), (unsigned)(dm.B * dm.H));
+    const int tpb = 256 / (dm.d / 8);
+    const dim3 grid((unsigned)((nq + tpb - 1) / tpb), (unsigned)(dm.B * dm.H));
     if (dm.dtype == 0)
         hipLaunchKernelGGL(residual_kernel<float>, grid, dim3(256), 0, st, (const float *)x, t0,
                            t1 - t0, dm.s, dm.k, dm.d, (const float *)c.refs, dm.R, c.idx, dm.N,

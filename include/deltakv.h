@@ -15,8 +15,9 @@
  *   V).  Units are independent; a call covers the B x H units of one
  *   (layer, stream) cache.
  * - Pointers are DEVICE pointers unless a comment says "host".  The caller owns
- *   every buffer; the library keeps no allocation between calls and allocates
- *   nothing itself (scratch space is the caller's workspace argument).
+ *   every buffer; the library allocates nothing itself (scratch space is the
+ *   caller's workspace argument), except the static per-device scratch array of
+ *   deltakv_decode_attn_noalloc.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *   the call returns at once.  Argument errors are returned synchronously,
  *   before anything is enqueued.  Faults inside a kernel surface at the
@@ -239,7 +240,10 @@ deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_i
  * num_q_heads must be a multiple of H with num_q_heads / H <= 8; 1 <= n_tokens
  * <= capacity (CAPACITY otherwise) and n_tokens <= the n_compressed of both
  * caches (INVALID_ARG otherwise).  workspace:
- * deltakv_decode_workspace_bytes(shape, num_q_heads, n_tokens) bytes. */
+ * deltakv_decode_workspace_bytes(shape, num_q_heads, n_tokens) bytes.
+ * bf16 caches: the Decompressors' hidden pre-activations (W1 latent + b1)
+ * enter the matrix cores as f16, rounded toward zero; they must lie within
+ * +-65504 (larger values saturate there; not checked). */
 deltakv_status deltakv_decode_attn(const deltakv_shape *shape, int32_t num_q_heads,
                                    int64_t n_tokens, const void *q,
                                    const deltakv_cache *k_cache, const deltakv_mlp *k_dec,
@@ -400,8 +404,8 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
  * used slots, times 1 / k_eff).  These are the rows the Compressor maps and
  * the training below fits.
  *   x:   as for deltakv_build_refs (read-only);
- *   out: DEVICE fp32 [B][H][n_out][d], n_out = the number of non-reference
- *        positions in [t0, t1) (nothing is written when n_out = 0).
+ *   out: DEVICE fp32 [B][H][n_out][d], 16-byte aligned, n_out = the number of
+ *        non-reference positions in [t0, t1) (nothing is written when n_out = 0).
  * Requires 0 <= t0 < t1 <= cache->n_compressed (the idx rows were written);
  * INVALID_ARG otherwise. */
 deltakv_status deltakv_residuals(const deltakv_shape *shape, const void *x, int64_t t0,
