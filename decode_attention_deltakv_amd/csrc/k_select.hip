@@ -718,12 +718,23 @@ __global__ __launch_bounds__(256) void select_list_split_kernel(
     }
 }
 
+__global__ void zero_u32_kernel(uint32_t *p) {
+    if (threadIdx.x == 0) *p = 0u;
+}
+
+__global__ void add_stats_kernel(const uint32_t *count, uint32_t *stats) {
+    if (threadIdx.x == 0) atomicAdd(stats, *count);
+}
+
 // Merge of select_list_split_kernel's lists: one wave per entry, grid-stride.
+// Also adds the list's length to *stats (when given), once.
 __global__ __launch_bounds__(256) void select_list_merge_kernel(
     int nsplit, int k, int64_t q0, int64_t Ncap, const uint64_t *__restrict__ list,
     const uint32_t *__restrict__ list_count, int64_t cap, const double *__restrict__ pd,
-    const int *__restrict__ pj, uint16_t *__restrict__ idx) {
-    const int64_t n = min((int64_t)*list_count, cap);
+    const int *__restrict__ pj, uint16_t *__restrict__ idx, uint32_t *__restrict__ stats) {
+    const uint32_t cnt = *list_count;
+    if (stats && blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(stats, cnt);
+    const int64_t n = min((int64_t)cnt, cap);
     const int64_t wstep = (int64_t)gridDim.x * 4;
     for (int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); e < n; e += wstep) {
         const uint64_t ent = list[e];
@@ -738,8 +749,10 @@ template <typename T, int D>
 hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0,
                           int64_t nq, const CacheArgs &c, const uint64_t *list,
                           const uint32_t *list_count, int64_t list_cap, void *scratch,
-                          size_t scratch_bytes, hipStream_t st) {
+                          size_t scratch_bytes, uint32_t *stats, hipStream_t st) {
     if (list) {
+        // grids sized for the usual few entries (the count is on the device);
+        // the kernels walk longer lists grid-stride
         // the first entries with their references split over blocks (as many
         // as the scratch holds partial lists for), the rest one block each
         int64_t first = 0;
@@ -752,20 +765,22 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
             if (cap > 0) {
                 double *pd = (double *)scratch;
                 int *pj = (int *)((char *)scratch + (size_t)cap * nsplit * kMaxK * sizeof(double));
-                const unsigned g = (unsigned)std::min<int64_t>((cap * nsplit + 3) / 4, 2048);
+                const unsigned g = (unsigned)std::min<int64_t>((cap * nsplit + 3) / 4, 256);
                 hipLaunchKernelGGL((select_list_split_kernel<D>), dim3(g), dim3(256), 0, st,
                                    (const bf16_t *)x, t0, t1 - t0, dm.s, (const bf16_t *)c.refs,
                                    dm.R, q0, list, list_count, cap, nsplit, chunk, pd, pj);
                 hipLaunchKernelGGL(select_list_merge_kernel,
-                                   dim3((unsigned)std::min<int64_t>((cap + 3) / 4, 256)), dim3(256),
+                                   dim3((unsigned)std::min<int64_t>((cap + 3) / 4, 64)), dim3(256),
                                    0, st, nsplit, dm.k, q0, dm.N, list, list_count, cap, pd, pj,
-                                   c.idx);
+                                   c.idx, stats);
+                stats = nullptr;   // counted
                 first = cap;
             }
         }
+        if (stats) hipLaunchKernelGGL(add_stats_kernel, dim3(1), dim3(64), 0, st, list_count, stats);
         if (first < list_cap) {
             const unsigned g =
-                (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap - first, 256));
+                (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap - first, 64));
             hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0,
                                st, (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N,
                                q0, dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq, first);
@@ -1573,13 +1588,6 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
                               ((uint64_t)unit << 32) | (uint64_t)qi, flist, fcount);
 }
 
-__global__ void zero_u32_kernel(uint32_t *p) {
-    if (threadIdx.x == 0) *p = 0u;
-}
-
-__global__ void add_stats_kernel(const uint32_t *count, uint32_t *stats) {
-    if (threadIdx.x == 0) atomicAdd(stats, *count);
-}
 
 template <int D, int LK>
 void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_t q0, int64_t nq,
@@ -1688,16 +1696,16 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
                                int64_t q0, int64_t nq, const CacheArgs &c,
                                const uint64_t *list, const uint32_t *list_count,
                                int64_t list_cap, void *scratch, size_t scratch_bytes,
-                               hipStream_t st) {
+                               hipStream_t st, uint32_t *stats) {
     if (dm.dtype == 0)
         return dm.d == 64 ? launch_exact_t<float, 64>(dm, x, t0, t1, q0, nq, c, list, list_count,
-                                                      list_cap, scratch, scratch_bytes, st)
+                                                      list_cap, scratch, scratch_bytes, stats, st)
                           : launch_exact_t<float, 128>(dm, x, t0, t1, q0, nq, c, list, list_count,
-                                                       list_cap, scratch, scratch_bytes, st);
+                                                       list_cap, scratch, scratch_bytes, stats, st);
     return dm.d == 64 ? launch_exact_t<bf16_t, 64>(dm, x, t0, t1, q0, nq, c, list, list_count,
-                                                   list_cap, scratch, scratch_bytes, st)
+                                                   list_cap, scratch, scratch_bytes, stats, st)
                       : launch_exact_t<bf16_t, 128>(dm, x, t0, t1, q0, nq, c, list, list_count,
-                                                    list_cap, scratch, scratch_bytes, st);
+                                                    list_cap, scratch, scratch_bytes, stats, st);
 }
 
 }  // namespace dk
@@ -1725,9 +1733,8 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
     // the split lists of the search are consumed: their space holds the
     // partial lists of the split exact scan
     e = launch_select_exact(dm, x, t0, t1, q0, nq, c, flist, fcount, (int64_t)nq * dm.B * dm.H,
-                            tail, exact_list_ws_bytes(dm, t1), st);
+                            tail, exact_list_ws_bytes(dm, t1), st, stats);
     if (e != hipSuccess) return e;
-    if (stats) hipLaunchKernelGGL(add_stats_kernel, dim3(1), dim3(64), 0, st, fcount, stats);
     return hipGetLastError();
 }
 
