@@ -57,50 +57,129 @@ __device__ __forceinline__ float act_df(float u, int act) {
                     : 1.f;
 }
 
-template <int EP>
+// Four consecutive operand values from p (stride 1) when all are inside
+// [0, lim) and the vector form is allowed, else one by one (out-of-range
+// values 0, and `ones_from` onwards (< lim) 1: the appended column of ones).
+__device__ __forceinline__ f32x4 ld4(const float *p, int64_t idx0, int64_t lim,
+                                     int64_t ones_from, bool vec) {
+    if (vec && idx0 + 3 < ones_from) return *reinterpret_cast<const f32x4 *>(p + idx0);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = idx0 + e;
+        v[e] = i < ones_from ? p[i] : (i < lim ? 1.f : 0.f);
+    }
+    return v;
+}
+
+// BM x 64 output tile per 256-thread block (4 waves, each (BM / 2) x 32),
+// k steps of 32 staged through LDS; the next step's operands are loaded into
+// registers while the current one is multiplied.
+template <int EP, int BM>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmP p) {
-    constexpr int BM = 64, BN = 64, BK = 16, PAD = 4;
-    __shared__ float As[BK][BM + PAD];
-    __shared__ float Bs[BK][BN + PAD];
+    constexpr int BN = 64, BK = 32, PAD = 4;
+    constexpr int MI = BM / 32;                 // 16-row tiles per wave
+    constexpr int NA = BM * BK / 4 / 256;       // A float4 groups per thread
+    constexpr int NBG = BN * BK / 4 / 256;      // B float4 groups per thread
+    __shared__ __attribute__((aligned(16))) float As[BK][BM + PAD];
+    __shared__ __attribute__((aligned(16))) float Bs[BK][BN + PAD];
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
     const int64_t kb = (int64_t)blockIdx.z * p.kchunk;
     const int64_t ke = min(p.K, kb + p.kchunk);
-    f32x4 acc[2][2];
+    f32x4 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // staging order: the operand's contiguous dimension fastest, so that a
-    // wave's loads are consecutive addresses
+    // operand orientation (contiguous dimension) and whether 16-byte loads
+    // are aligned
     const bool a_kc = p.sak == 1, b_nc = p.sbn == 1;
-    for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+    const auto al16 = [](const float *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+    const bool avec = al16(p.A) && ((a_kc ? p.sam : p.sak) % 4 == 0);
+    const bool bvec = al16(p.B) && ((b_nc ? p.sbk : p.sbn) % 4 == 0);
+    f32x4 ra[NA], rb[NBG];
+    auto load = [&](int64_t k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + 256 * i;
-            const int am = a_kc ? (e >> 4) : (e & 63), ak = a_kc ? (e & 15) : (e >> 6);
-            const int64_t gm = m0 + am, gk = k0 + ak;
-            As[ak][am] = (gm < p.M && gk < ke) ? p.A[gm * p.sam + gk * p.sak] : 0.f;
-            const int bn = b_nc ? (e & 63) : (e >> 4), bk = b_nc ? (e >> 6) : (e & 15);
-            const int64_t gn = n0 + bn, gk2 = k0 + bk;
-            float bv = 0.f;
-            if (gk2 < ke && gn < p.N) bv = gn < p.NB ? p.B[gk2 * p.sbk + gn * p.sbn] : 1.f;
-            Bs[bk][bn] = bv;
+        for (int i = 0; i < NA; ++i) {
+            const int g = tid + 256 * i;
+            if (a_kc) {   // rows of A, four k at a time
+                const int am = g / (BK / 4), ak = 4 * (g % (BK / 4));
+                const int64_t gm = m0 + am;
+                ra[i] = gm < p.M ? ld4(p.A + gm * p.sam, k0 + ak, ke, ke, avec)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {      // columns of A, four m at a time
+                const int ak = g / (BM / 4), am = 4 * (g % (BM / 4));
+                const int64_t gk = k0 + ak;
+                ra[i] = gk < ke ? ld4(p.A + gk * p.sak, m0 + am, p.M, p.M, avec)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+#pragma unroll
+        for (int i = 0; i < NBG; ++i) {
+            const int g = tid + 256 * i;
+            if (b_nc) {   // rows of B, four n at a time (the ones column past NB)
+                const int bk = g / (BN / 4), bn = 4 * (g % (BN / 4));
+                const int64_t gk = k0 + bk;
+                rb[i] = gk < ke ? ld4(p.B + gk * p.sbk, n0 + bn, p.N, p.NB, bvec)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {      // columns of B, four k at a time
+                const int bn = g / (BK / 4), bk = 4 * (g % (BK / 4));
+                const int64_t gn = n0 + bn;
+                if (gn < p.NB)
+                    rb[i] = ld4(p.B + gn * p.sbn, k0 + bk, ke, ke, bvec);
+                else {
+                    const float one = gn < p.N ? 1.f : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rb[i][e] = k0 + bk + e < ke ? one : 0.f;
+                }
+            }
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int g = tid + 256 * i;
+            if (a_kc) {
+                const int am = g / (BK / 4), ak = 4 * (g % (BK / 4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) As[ak + e][am] = ra[i][e];
+            } else {
+                const int ak = g / (BM / 4), am = 4 * (g % (BM / 4));
+                *reinterpret_cast<f32x4 *>(&As[ak][am]) = ra[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NBG; ++i) {
+            const int g = tid + 256 * i;
+            if (b_nc) {
+                const int bk = g / (BN / 4), bn = 4 * (g % (BN / 4));
+                *reinterpret_cast<f32x4 *>(&Bs[bk][bn]) = rb[i];
+            } else {
+                const int bn = g / (BK / 4), bk = 4 * (g % (BK / 4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Bs[bk + e][bn] = rb[i][e];
+            }
+        }
+    };
+    if (kb < ke) load(kb);
+    for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+        store();
         __syncthreads();
+        if (k0 + BK < ke) load(k0 + BK);
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 4) {
             // 16x16x4: lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]
             const int kr = kk + (lane >> 4);
-            float a[2], b[2];
+            float a[MI], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = As[kr][32 * wm + 16 * i + (lane & 15)];
+            for (int i = 0; i < MI; ++i) a[i] = As[kr][(BM / 2) * wm + 16 * i + (lane & 15)];
 #pragma unroll
             for (int j = 0; j < 2; ++j) b[j] = Bs[kr][32 * wn + 16 * j + (lane & 15)];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -110,12 +189,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmP p) {
     // epilogue: lane l holds C[4 (l / 16) + r][l % 16] of each 16 x 16 tile
     float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + r;
+                const int64_t row = m0 + (BM / 2) * wm + 16 * i + 4 * (lane >> 4) + r;
                 const int64_t col = n0 + 32 * wn + 16 * j + (lane & 15);
                 if (row >= p.M || col >= p.N) continue;
                 const float v = acc[i][j][r];
@@ -173,10 +252,16 @@ struct UpdateP {
 // export; block 0 also adds the loss partials in order.
 __global__ __launch_bounds__(256) void update_kernel(UpdateP p) {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && p.loss) {
+    if (blockIdx.x == 0 && p.loss) {
+        // every thread sums a strided share of the loss partials, then a
+        // fixed reduction tree (deterministic)
+        __shared__ float part[4];
         float s = 0.f;
-        for (int i = 0; i < p.nloss; ++i) s += p.lossp[i];
-        *p.loss = s * p.inv_count;
+        for (int i = threadIdx.x; i < p.nloss; i += 256) s += p.lossp[i];
+        s = wave_sum(s);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+        __syncthreads();
+        if (threadIdx.x == 0) *p.loss = ((part[0] + part[1]) + (part[2] + part[3])) * p.inv_count;
     }
     if (g >= p.total) return;
     int li = 0;
@@ -189,8 +274,19 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateP p) {
     const int64_t row = isw ? e / L.in : e - nw;
     const int64_t col = isw ? e % L.in : L.in;
     const int64_t ld = (int64_t)L.in + 1, ps = (int64_t)L.out * ld;
-    float gr = 0.f;
-    for (int z = 0; z < L.nsplit; ++z) gr += L.part[z * ps + row * ld + col];
+    // four running sums over interleaved splits (loads of four splits in
+    // flight), added in a fixed order
+    const float *pp = L.part + row * ld + col;
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
+    int z = 0;
+    for (; z + 4 <= L.nsplit; z += 4) {
+        g0 += pp[(int64_t)z * ps];
+        g1 += pp[(int64_t)(z + 1) * ps];
+        g2 += pp[(int64_t)(z + 2) * ps];
+        g3 += pp[(int64_t)(z + 3) * ps];
+    }
+    for (; z < L.nsplit; ++z) g0 += pp[(int64_t)z * ps];
+    const float gr = (g0 + g1) + (g2 + g3);
     if (p.grad) p.grad[g] = gr;
     float step = gr;
     if (p.vel) {
@@ -272,19 +368,27 @@ __global__ __launch_bounds__(256) void residual_kernel(const T *__restrict__ x, 
     *reinterpret_cast<f32x4 *>(o + 4) = hi;
 }
 
+// 128-row tiles for the products over the n rows, 64-row tiles for the
+// weight gradients (at most a few hundred output rows).  The loss epilogue's
+// partial sums are laid out per 128-row tile (train_layout).
 template <int EP>
 void gemm(const GemmP &p, int nsplit, hipStream_t st) {
-    const dim3 grid((unsigned)((p.M + 63) / 64), (unsigned)((p.N + 63) / 64), (unsigned)nsplit);
-    hipLaunchKernelGGL(gemm_f32_kernel<EP>, grid, dim3(256), 0, st, p);
+    if (p.M >= 1024 || EP == kEpiLoss) {
+        const dim3 grid((unsigned)((p.M + 127) / 128), (unsigned)((p.N + 63) / 64), (unsigned)nsplit);
+        hipLaunchKernelGGL((gemm_f32_kernel<EP, 128>), grid, dim3(256), 0, st, p);
+    } else {
+        const dim3 grid((unsigned)((p.M + 63) / 64), (unsigned)((p.N + 63) / 64), (unsigned)nsplit);
+        hipLaunchKernelGGL((gemm_f32_kernel<EP, 64>), grid, dim3(256), 0, st, p);
+    }
 }
 
 // Split of a weight-gradient product over its n rows: about 768 blocks,
-// chunks of whole 16-row steps.
+// chunks of whole 32-row steps.
 void wsplit(int64_t n, int out, int in, int *nsplit, int64_t *kchunk) {
     const int64_t tiles = ((out + 63) / 64) * ((in + 1 + 63) / 64);
     int64_t s = std::max<int64_t>(1, std::min<int64_t>((768 + tiles - 1) / tiles, (n + 63) / 64));
     int64_t c = (n + s - 1) / s;
-    c = (c + 15) / 16 * 16;
+    c = (c + 31) / 32 * 32;
     *kchunk = c;
     *nsplit = (int)((n + c - 1) / c);
 }
@@ -310,7 +414,7 @@ TrainLayout train_layout(int d, int h1, int dc, int h2, int64_t n) {
     t.h2 = take((size_t)n * h2);
     t.g4 = take((size_t)n * d);
     t.dz = take((size_t)n * dc);
-    t.nloss = (int)(((n + 63) / 64) * ((d + 63) / 64));
+    t.nloss = (int)(((n + 127) / 128) * ((d + 63) / 64));
     t.lossp = take((size_t)t.nloss);
     const int outs[4] = {h1, dc, h2, d}, ins[4] = {d, h1, dc, h2};
     for (int l = 0; l < 4; ++l) {
