@@ -122,6 +122,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compress-streams", type=int, default=4,
+                    help="streams the prompt compression's independent per-cache calls are "
+                         "spread over (1 to 4)")
     ap.add_argument("--train-rows", type=int, default=65536,
                     help="residual rows of the Compressor / Decompressor training leg (0: skip)")
     ap.add_argument("--no-q4", action="store_true",
@@ -138,7 +141,7 @@ def parse():
 class Setup:
     """Inputs, weights, caches and workspaces of one workload, on the GPU."""
 
-    def __init__(self, wl, widx):
+    def __init__(self, wl, widx, streams=4):
         import decode_attention_deltakv_amd as dk
         from deltakv_synth import kv_rows, queries, xavier_mlp, unit_key
         self.dk = dk
@@ -187,6 +190,12 @@ class Setup:
         ranges = [(c0, min(T, c0 + self.chunk)) for c0 in range(0, T, self.chunk)]
         ranges.append((cap - 1, cap))
         self.cws = dk.workspace(max(dk.compress_workspace_bytes(self.shape, a, b) for a, b in ranges))
+        # the caches are independent: their compression calls are spread over
+        # a few streams (each cache's calls stay in order on its own stream,
+        # each stream with its own workspace), so small calls overlap
+        self.n_streams = max(1, min(4, streams))
+        self.streams = [torch.cuda.Stream() for _ in range(self.n_streams)]
+        self.cws_s = [self.cws] + [torch.empty_like(self.cws) for _ in range(self.n_streams - 1)]
         self.Hq = wl.q_heads
         self.dws = dk.workspace(dk.decode_workspace_bytes(self.shape, self.Hq, cap))
         self.out = torch.empty(B, self.Hq, d, dtype=torch.float32, device="cuda")
@@ -209,15 +218,22 @@ class Setup:
         for row in self.cache:          # refill every cache from position 0
             for c in row:
                 c.reset()
+        main = torch.cuda.current_stream()
+        for s_ in self.streams:
+            s_.wait_stream(main)
         for c0 in range(0, T, self.chunk):
             c1 = min(T, c0 + self.chunk)
             for l in range(self.wl.layers):
                 for st in (0, 1):
-                    x = self.x[l][st] if (c0, c1) == (0, T) else \
-                        self.x[l][st][:, :, c0:c1].contiguous()
-                    dk.build_refs(sh, x, c0, c1, self.cache[l][st])
-                    dk.compress(sh, x, c0, c1, self.comp[l][st], self.cache[l][st], self.cws,
-                                self.stats)
+                    i = (2 * l + st) % self.n_streams
+                    with torch.cuda.stream(self.streams[i]):
+                        x = self.x[l][st] if (c0, c1) == (0, T) else \
+                            self.x[l][st][:, :, c0:c1].contiguous()
+                        dk.build_refs(sh, x, c0, c1, self.cache[l][st])
+                        dk.compress(sh, x, c0, c1, self.comp[l][st], self.cache[l][st],
+                                    self.cws_s[i], self.stats)
+        for s_ in self.streams:
+            main.wait_stream(s_)
 
     def decode_step(self, i, k=0):
         """Decode step k of a bench step, queries i.  Streaming: first append
@@ -462,7 +478,7 @@ def main():
     if wl.appends:
         dsteps = min(dsteps, wl.appends)   # each streaming decode step appends a token
     torch.cuda.set_device(0)
-    S = Setup(wl, widx)
+    S = Setup(wl, widx, a.compress_streams)
     stream = torch.cuda.current_stream()
     if a.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -821,7 +837,8 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "batch": B, "kv_heads": wl.kv_heads,
                    "q_heads": wl.q_heads, "head_dim": wl.head_dim, "T": T, "stride": wl.stride,
                    "k": wl.k, "d_c": wl.d_c, "hidden": wl.hidden, "decode_steps": dsteps,
-                   "prompt_chunk": wl.chunk, "appends_per_step": min(dsteps, wl.appends)},
+                   "prompt_chunk": wl.chunk, "appends_per_step": min(dsteps, wl.appends),
+                   "compress_streams": S.n_streams},
         "compress_ms_per_step": comp_ms,
         "compress_tflops": cflops / (comp_ms * 1e-3) / 1e12,
         "compress_roofline": {"bound": "mfma", "achieved": cflops / (comp_ms * 1e-3) / 1e12,

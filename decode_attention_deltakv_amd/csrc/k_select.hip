@@ -25,14 +25,18 @@ static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Reference-range splits of the matrix-core top-k search: when the token tiles
 // of a call give fewer than two blocks per CU (a prompt compressed in chunks),
-// each tile's references are split over up to three blocks per CU's worth of
-// blocks, at least 512 references (8 stages) per split.
+// each tile's references are split so that the call has about kSplitTarget
+// blocks, at least 512 references (8 stages) per split.  Each split warms up
+// its own candidate lists (insertions while they fill), so half a round of
+// resident blocks measures faster than a full one.
+constexpr int64_t kSplitTarget = 384;
+
 void topk_split_plan(const Dims &dm, int64_t t1, int64_t nq, int *nsplit, int *chunk) {
     const int64_t U = (int64_t)dm.B * dm.H;
     const int64_t blocks = std::max<int64_t>(1, (nq + 255) / 256 * U);
     const int64_t R = std::max<int64_t>(1, refs_upto(t1, dm.s));
     int64_t n = 1;
-    if (blocks < 512) n = std::max<int64_t>(1, std::min((768 + blocks - 1) / blocks, (R + 511) / 512));
+    if (blocks < 512) n = std::max<int64_t>(1, std::min((kSplitTarget + blocks - 1) / blocks, (R + 511) / 512));
     int64_t c = (R + n - 1) / n;
     c = (c + 63) / 64 * 64;
     *nsplit = (int)((R + c - 1) / c);
@@ -56,7 +60,7 @@ size_t topk_split_ws_bytes(const Dims &dm, int64_t t1, int64_t nq) {
     const int64_t R = std::max<int64_t>(1, refs_upto(t1, dm.s));
     // topk_split_plan's count n bounds its realised split count
     const int64_t nsplit =
-        blocks < 512 ? std::max<int64_t>(1, std::min((768 + blocks - 1) / blocks, (R + 511) / 512))
+        blocks < 512 ? std::max<int64_t>(1, std::min((kSplitTarget + blocks - 1) / blocks, (R + 511) / 512))
                      : 1;
     if (nsplit <= 1) return 0;
     const int LK = dm.k <= 4 ? kListLen4 : kListLen8;
