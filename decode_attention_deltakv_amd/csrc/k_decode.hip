@@ -562,7 +562,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
 
 // Query-aware token selection from the logits a dense decode wrote (the
 // selector a sparse attention uses at a filter layer: tokens are ranked by
-// the attention they received).  Two launches.
+// the attention they received).  Six launches: the keys, three histogram
+// passes, the per-slice counts and the ordered write.
 //
 // select_keys_kernel, grid (ceil(T / 2048), U), 256 threads: for every
 // position p < T of unit u,
@@ -572,6 +573,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
 // significant) byte are added to hist0[u][256], which the merge kernel
 // cleared.
 constexpr int kKeyPer = 8;  // positions per thread of the key kernel
+constexpr int kSelHist = 4 * 256;  // histogram words per unit (four radix passes)
 __global__ __launch_bounds__(256) void select_keys_kernel(
     const float *__restrict__ logc, const float *__restrict__ logr,
     const float *__restrict__ lse, int Hq, int G, int H, int64_t T, int64_t Nt, int64_t Rt,
@@ -611,74 +613,36 @@ __global__ __launch_bounds__(256) void select_keys_kernel(
     }
     __syncthreads();
     // the block's counts of the keys' first byte into the unit's histogram
-    if (lh[threadIdx.x]) atomicAdd(&hist0[unit * 256 + threadIdx.x], lh[threadIdx.x]);
+    if (lh[threadIdx.x]) atomicAdd(&hist0[unit * kSelHist + threadIdx.x], lh[threadIdx.x]);
 }
 
-// select_topn_kernel, grid U, kSelThreads threads: positions[u][0..n_keep)
-// = the n_keep positions of largest key, equal keys ordered by the lower
-// position, written in increasing position order (n_keep >= T: every
-// position, then -1).  The n_keep-th largest key is found by a 4 x 8-bit
-// radix select on the keys' bit patterns (non-negative floats order as their
-// bits): the first byte's histogram comes from the key kernel, the other
-// three count only the keys that share the bytes fixed so far.  One ordered
-// pass then takes every key above the threshold and the first equal ones.
-// Keys are read with 16-byte loads, all of a batch's loads first; a unit's
-// keys start at a multiple of 4 entries (keys_stride).
-constexpr int kSelThreads = 1024;
-__global__ __launch_bounds__(kSelThreads) void select_topn_kernel(
-    const uint32_t *__restrict__ keys, const uint32_t *__restrict__ hist0, int64_t T,
-    int n_keep, int32_t *__restrict__ positions) {
-    constexpr int NT = kSelThreads, NW = NT / 64;
-    constexpr int HB = 8;   // 16-byte loads per thread per histogram batch (coalesced)
-    constexpr int OB = 4;   // 16-byte loads per thread per ordered batch (contiguous)
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wtot[NW];
-    __shared__ uint32_t sel[2];
+// The multi-block radix select that follows the key kernel.  Per unit the
+// workspace holds four 256-bin histograms (hist[u][j]: counts of byte 3 - j of
+// the keys that share the bytes fixed by passes 0 .. j - 1), cleared by the
+// merge kernel; every block re-derives the fixed bytes from them.  Keys of a
+// unit are cut into slices of kSelSlice positions, one block each.
+constexpr int kSelSlice = 4096;
+
+// prefix / mask of the bytes fixed by the first np passes and rem, the rank
+// (from the top, 1-based) of the n_keep-th largest key among the keys that
+// share them; sh: 256 + 2 words of LDS; all threads of the block call it.
+__device__ __forceinline__ void sel_resolve(const uint32_t *__restrict__ uh, int np,
+                                            uint32_t n_keep, uint32_t *sh, uint32_t &prefix,
+                                            uint32_t &mask, uint32_t &rem) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int unit = blockIdx.x;
-    const int64_t T4 = keys_stride(T) / 4;
-    const u32x4 *ku4 = reinterpret_cast<const u32x4 *>(keys + (int64_t)unit * keys_stride(T));
-    int32_t *pu = positions + (int64_t)unit * n_keep;
-    if (n_keep >= T) {
-        for (int64_t i = tid; i < n_keep; i += NT) pu[i] = i < T ? (int32_t)i : -1;
-        return;
-    }
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    // radix select of the n_keep-th largest key: prefix / mask of the bits
-    // fixed so far, rem = its rank (from the top, 1-based) among the keys
-    // that share them
-    uint32_t prefix = 0u, mask = 0u, rem = (uint32_t)n_keep;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (shift == 24) {
-            // the first byte's counts come from the key kernel
-            for (int i = tid; i < 256; i += NT) hist[i] = hist0[(int64_t)unit * 256 + i];
-        } else {
-            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-            __syncthreads();
-            for (int64_t b4 = 0; b4 < T4; b4 += (int64_t)NT * HB) {
-                u32x4 kv[HB];
-#pragma unroll
-                for (int e = 0; e < HB; ++e) {
-                    const int64_t i4 = b4 + (int64_t)e * NT + tid;
-                    kv[e] = i4 < T4 ? ku4[i4] : zero4;
-                }
-#pragma unroll
-                for (int e = 0; e < HB; ++e)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int64_t p = (b4 + (int64_t)e * NT + tid) * 4 + j;
-                        if (p < T && (kv[e][j] & mask) == prefix)
-                            atomicAdd(&hist[(kv[e][j] >> shift) & 255u], 1u);
-                    }
-            }
-        }
+    prefix = 0u;
+    mask = 0u;
+    rem = n_keep;
+    for (int j = 0; j < np; ++j) {
+        __syncthreads();
+        for (int i = tid; i < 256; i += blockDim.x) sh[i] = uh[256 * j + i];
         __syncthreads();
         if (w == 0) {
             // lane l holds bins 255 - 4 l .. 252 - 4 l (from the top)
             uint32_t c[4], tot = 0u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                c[i] = hist[255 - 4 * lane - i];
+                c[i] = sh[255 - 4 * lane - i];
                 tot += c[i];
             }
             uint32_t inc = tot;
@@ -693,8 +657,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topn_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (r <= c[i]) {
-                        sel[0] = (uint32_t)(255 - 4 * lane - i);
-                        sel[1] = r;
+                        sh[256] = (uint32_t)(255 - 4 * lane - i);
+                        sh[257] = r;
                         break;
                     }
                     r -= c[i];
@@ -702,67 +666,184 @@ __global__ __launch_bounds__(kSelThreads) void select_topn_kernel(
             }
         }
         __syncthreads();
-        prefix |= sel[0] << shift;
+        const int shift = 24 - 8 * j;
+        prefix |= sh[256] << shift;
         mask |= 255u << shift;
-        rem = sel[1];
-        __syncthreads();  // sel and hist are rewritten by the next pass
+        rem = sh[257];
     }
-    // ordered pass (each thread 16 consecutive positions): keys above the
-    // threshold, and the first rem equal ones; the out index of a taken
-    // position = keys above it taken before it + min(equal keys before it, rem)
-    const uint32_t thr = prefix;
-    uint32_t gt_run = 0u, eq_run = 0u;
-    for (int64_t b4 = 0; b4 < T4; b4 += (int64_t)NT * OB) {
-        u32x4 kv[OB];
+    __syncthreads();
+}
+
+// Pass `pass` (1..3) of the radix select: the counts of byte 3 - pass of the
+// slice's keys that share the bytes fixed so far, added to hist[u][pass].
+// grid (slices, U), 256 threads.
+__global__ __launch_bounds__(256) void select_hist_kernel(const uint32_t *__restrict__ keys,
+                                                          uint32_t *__restrict__ hist, int64_t T,
+                                                          int n_keep, int pass) {
+    __shared__ uint32_t sh[258];
+    __shared__ uint32_t lh[256];
+    if (n_keep >= T) return;
+    const int unit = blockIdx.y, tid = threadIdx.x;
+    uint32_t *uh = hist + (int64_t)unit * kSelHist;
+    uint32_t prefix, mask, rem;
+    sel_resolve(uh, pass, (uint32_t)n_keep, sh, prefix, mask, rem);
+    lh[tid] = 0u;
+    __syncthreads();
+    const int shift = 24 - 8 * pass;
+    const int64_t p0 = (int64_t)blockIdx.x * kSelSlice;
+    const uint32_t *ku = keys + (int64_t)unit * keys_stride(T);
+    // 16 consecutive keys per thread (16-byte loads; the slice start and the
+    // unit's row are multiples of 4 entries)
+    constexpr int PER = kSelSlice / 256;
+    u32x4 kv[PER / 4];
+    const int64_t pt = p0 + (int64_t)tid * PER;
 #pragma unroll
-        for (int e = 0; e < OB; ++e) {
-            const int64_t i4 = b4 + (int64_t)tid * OB + e;
-            kv[e] = i4 < T4 ? ku4[i4] : zero4;
-        }
-        const int64_t p0 = (b4 + (int64_t)tid * OB) * 4;
-        uint32_t cg = 0u, ce = 0u;
-#pragma unroll
-        for (int e = 0; e < OB; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool inr = p0 + 4 * e + j < T;
-                cg += (inr && kv[e][j] > thr) ? 1u : 0u;
-                ce += (inr && kv[e][j] == thr) ? 1u : 0u;
-            }
-        const uint32_t mine = cg | (ce << 16);
-        uint32_t inc = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        if (lane == 63) wtot[w] = inc;
-        __syncthreads();
-        uint32_t before = inc - mine, total = 0u;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            before += i < w ? wtot[i] : 0u;
-            total += wtot[i];
-        }
-        uint32_t g0 = gt_run + (before & 0xffffu), e0 = eq_run + (before >> 16);
-#pragma unroll
-        for (int e = 0; e < OB; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t p = p0 + 4 * e + j;
-                const uint32_t k = kv[e][j];
-                if (p < T && k > thr) {
-                    pu[g0 + min(e0, rem)] = (int32_t)p;
-                    ++g0;
-                } else if (p < T && k == thr) {
-                    if (e0 < rem) pu[g0 + e0] = (int32_t)p;
-                    ++e0;
-                }
-            }
-        gt_run += total & 0xffffu;
-        eq_run += total >> 16;
-        __syncthreads();  // wtot is rewritten by the next chunk
+    for (int e = 0; e < PER / 4; ++e) {
+        const int64_t p = pt + 4 * e;
+        kv[e] = p < T ? *reinterpret_cast<const u32x4 *>(ku + p) : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (pt + 4 * e + j < T && (kv[e][j] & mask) == prefix)
+                atomicAdd(&lh[(kv[e][j] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (lh[tid]) atomicAdd(&uh[256 * pass + tid], lh[tid]);
+}
+
+// The ordered write.  select_count_kernel: per slice, the numbers of keys
+// above the threshold and equal to it (cnt[u][slice][0..1]).
+// select_write_kernel: every taken position of the slice at its place in the
+// unit's list (position order; of the keys equal to the threshold, the first
+// rem of the unit are taken).
+__global__ __launch_bounds__(256) void select_count_kernel(const uint32_t *__restrict__ keys,
+                                                           const uint32_t *__restrict__ hist,
+                                                           int64_t T, int n_keep,
+                                                           uint32_t *__restrict__ cnt) {
+    __shared__ uint32_t sh[258];
+    __shared__ uint32_t red[2][4];
+    if (n_keep >= T) return;
+    const int unit = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t thr, mask, rem;
+    sel_resolve(hist + (int64_t)unit * kSelHist, 4, (uint32_t)n_keep, sh, thr, mask, rem);
+    const int64_t p0 = (int64_t)blockIdx.x * kSelSlice;
+    const uint32_t *ku = keys + (int64_t)unit * keys_stride(T);
+    constexpr int PER = kSelSlice / 256;
+    const int64_t pt = p0 + (int64_t)tid * PER;
+    uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e) {
+        const int64_t p = pt + 4 * e;
+        const u32x4 v = p < T ? *reinterpret_cast<const u32x4 *>(ku + p) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool inr = p + j < T;
+            cg += (inr && v[j] > thr) ? 1u : 0u;
+            ce += (inr && v[j] == thr) ? 1u : 0u;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        cg += __shfl_xor(cg, o, 64);
+        ce += __shfl_xor(ce, o, 64);
+    }
+    if (lane == 0) {
+        red[0][w] = cg;
+        red[1][w] = ce;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t *c = cnt + ((int64_t)unit * gridDim.x + blockIdx.x) * 2;
+        c[0] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+        c[1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    }
+}
+
+__global__ __launch_bounds__(256) void select_write_kernel(const uint32_t *__restrict__ keys,
+                                                           const uint32_t *__restrict__ hist,
+                                                           const uint32_t *__restrict__ cnt,
+                                                           int64_t T, int n_keep,
+                                                           int32_t *__restrict__ positions) {
+    __shared__ uint32_t sh[258];
+    __shared__ uint32_t wtot[4];
+    __shared__ uint32_t base[2];
+    const int unit = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t *pu = positions + (int64_t)unit * n_keep;
+    const int64_t p0 = (int64_t)blockIdx.x * kSelSlice;
+    if (n_keep >= T) {
+        // every position in order, then -1 (the first slice writes the tail)
+        for (int64_t i = p0 + tid; i < min(T, p0 + kSelSlice); i += 256) pu[i] = (int32_t)i;
+        if (blockIdx.x == 0)
+            for (int64_t i = T + tid; i < n_keep; i += 256) pu[i] = -1;
+        return;
+    }
+    uint32_t thr, mask, rem;
+    sel_resolve(hist + (int64_t)unit * kSelHist, 4, (uint32_t)n_keep, sh, thr, mask, rem);
+    // taken keys before this slice (slices in order)
+    if (w == 0) {
+        uint32_t g = 0u, e = 0u;
+        for (int i = lane; i < (int)blockIdx.x; i += 64) {
+            const uint32_t *c = cnt + ((int64_t)unit * gridDim.x + i) * 2;
+            g += c[0];
+            e += c[1];
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            g += __shfl_xor(g, o, 64);
+            e += __shfl_xor(e, o, 64);
+        }
+        if (lane == 0) {
+            base[0] = g;
+            base[1] = e;
+        }
+    }
+    __syncthreads();
+    const uint32_t *ku = keys + (int64_t)unit * keys_stride(T);
+    constexpr int PER = kSelSlice / 256;
+    const int64_t pt = p0 + (int64_t)tid * PER;
+    u32x4 kv[PER / 4];
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e) {
+        const int64_t p = pt + 4 * e;
+        kv[e] = p < T ? *reinterpret_cast<const u32x4 *>(ku + p) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool inr = pt + 4 * e + j < T;
+            cg += (inr && kv[e][j] > thr) ? 1u : 0u;
+            ce += (inr && kv[e][j] == thr) ? 1u : 0u;
+        }
+    const uint32_t mine = cg | (ce << 16);   // at most 16 per thread
+    uint32_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    uint32_t before = inc - mine;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) before += i < w ? wtot[i] : 0u;
+    uint32_t g0 = base[0] + (before & 0xffffu), e0 = base[1] + (before >> 16);
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t p = pt + 4 * e + j;
+            const uint32_t k = kv[e][j];
+            if (p < T && k > thr) {
+                pu[g0 + min(e0, rem)] = (int32_t)p;
+                ++g0;
+            } else if (p < T && k == thr) {
+                if (e0 < rem) pu[g0 + e0] = (int32_t)p;
+                ++e0;
+            }
+        }
 }
 
 // Merge of two normalised attention results over disjoint key sets (the
@@ -809,7 +890,7 @@ __global__ __launch_bounds__(kCombThreads) void combine2_kernel(int Hq, int G, i
     // token selection: the first query head of the group clears the unit's
     // key histogram that the key kernel fills next
     if (hist0 && g == 0)
-        for (int i = tid; i < 256; i += NT) hist0[unit * 256 + i] = 0u;
+        for (int i = tid; i < kSelHist; i += NT) hist0[unit * kSelHist + i] = 0u;
     const int64_t pstep = (int64_t)G * kPStride;
     float mx = -INFINITY;
     for (int64_t p = tid; p < P; p += NT) mx = fmaxf(mx, base[p * pstep]);
@@ -2459,7 +2540,7 @@ size_t decode_sparse_ws_bytes(const Dims &dm, int Hq, int64_t T, int nsel) {
 // selection keys.
 struct SelPlan {
     DecPlan dec;
-    size_t off_logc, off_logr, off_lse, off_keys, off_hist, total;
+    size_t off_logc, off_logr, off_lse, off_keys, off_hist, off_cnt, total;
 };
 SelPlan plan_select(const Dims &dm, int Hq, int64_t T) {
     SelPlan p;
@@ -2475,7 +2556,9 @@ SelPlan plan_select(const Dims &dm, int Hq, int64_t T) {
     p.off_keys = off;
     off += align_up(U * (size_t)keys_stride(T) * 4);
     p.off_hist = off;
-    off += align_up(U * 256 * 4);
+    off += align_up(U * kSelHist * 4);
+    p.off_cnt = off;
+    off += align_up(U * (size_t)((T + kSelSlice - 1) / kSelSlice) * 2 * 4);
     p.total = off;
     return p;
 }
@@ -2507,8 +2590,13 @@ hipError_t launch_decode_select(const Dims &dm, int Hq, int64_t T, const void *q
                        dim3((unsigned)((T + 256 * kKeyPer - 1) / (256 * kKeyPer)), U), dim3(256), 0,
                        st, logc, logr, lse, Hq, Hq / dm.H, dm.H, T, sp.dec.Nt, sp.dec.Rt, dm.s,
                        keys, scores, hist0);
-    hipLaunchKernelGGL(select_topn_kernel, dim3(U), dim3(kSelThreads), 0, st, keys, hist0, T,
-                       n_keep, positions);
+    const dim3 sg((unsigned)((T + kSelSlice - 1) / kSelSlice), U);
+    for (int pass = 1; pass < 4; ++pass)
+        hipLaunchKernelGGL(select_hist_kernel, sg, dim3(256), 0, st, keys, hist0, T, n_keep, pass);
+    uint32_t *cnt = (uint32_t *)(w + sp.off_cnt);
+    hipLaunchKernelGGL(select_count_kernel, sg, dim3(256), 0, st, keys, hist0, T, n_keep, cnt);
+    hipLaunchKernelGGL(select_write_kernel, sg, dim3(256), 0, st, keys, hist0, cnt, T, n_keep,
+                       positions);
     return hipGetLastError();
 }
 
