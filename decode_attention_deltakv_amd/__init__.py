@@ -60,7 +60,8 @@ class CShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("stride", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_c", ctypes.c_int32), ("capacity", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("latent_format", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("latent_format", ctypes.c_int32),
+                ("page_refs", ctypes.c_int32)]
 
 
 class CMlp(ctypes.Structure):
@@ -72,7 +73,8 @@ class CMlp(ctypes.Structure):
 class CCache(ctypes.Structure):
     _fields_ = [("refs", ctypes.c_void_p), ("ref_sqnorm", ctypes.c_void_p),
                 ("latents", ctypes.c_void_p), ("idx", ctypes.c_void_p),
-                ("n_built", ctypes.c_int64), ("n_compressed", ctypes.c_int64)]
+                ("n_built", ctypes.c_int64), ("n_compressed", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int64)]
 
 
 class CMlpF32(ctypes.Structure):
@@ -103,6 +105,9 @@ def lib():
     sp = ctypes.POINTER(CShape)
     L.deltakv_cache_bytes.argtypes = [sp, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
                                       ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+    L.deltakv_page_bytes.argtypes = [sp, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
+                                     ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
+                                     ctypes.POINTER(ctypes.c_int32)]
     L.deltakv_compress_workspace_bytes.argtypes = [sp, ctypes.c_int64, ctypes.c_int64,
                                                    ctypes.POINTER(_SZ)]
     L.deltakv_decode_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int64,
@@ -158,7 +163,7 @@ def lib():
                                      _P, _P, _P, ctypes.POINTER(_P), _P, _SZ, _P]
     for name in ("deltakv_residuals", "deltakv_train_workspace_bytes", "deltakv_train_step",
                  "deltakv_append_workspace_bytes", "deltakv_append",
-                 "deltakv_cache_bytes", "deltakv_compress_workspace_bytes",
+                 "deltakv_cache_bytes", "deltakv_page_bytes", "deltakv_compress_workspace_bytes",
                  "deltakv_decode_workspace_bytes", "deltakv_build_refs", "deltakv_compress",
                  "deltakv_decode_attn", "deltakv_decode_sparse_workspace_bytes",
                  "deltakv_decode_attn_sparse", "deltakv_decode_select_workspace_bytes",
@@ -210,10 +215,11 @@ class Shape:
     capacity: int
     dtype: int = BF16
     latent_format: int = 0   # LATENT_DTYPE or LATENT_Q4
+    page_refs: int = 0       # 0: unit-contiguous arrays; else reference rows per page
 
     def c(self) -> CShape:
         return CShape(self.batch, self.num_kv_heads, self.head_dim, self.stride, self.k,
-                      self.d_c, self.capacity, self.dtype, self.latent_format)
+                      self.d_c, self.capacity, self.dtype, self.latent_format, self.page_refs)
 
     @property
     def torch_dtype(self):
@@ -281,7 +287,7 @@ class Cache:
         return CCache(_ptr(self.refs), _ptr(self.ref_sqnorm),
                       _ptr(self.latents) if self.latents.numel() else None,
                       _ptr(self.idx) if self.idx.numel() else None,
-                      self.n_built, self.n_compressed)
+                      self.n_built, self.n_compressed, None, 0)
 
     def _took(self, cc: CCache):
         """Keep the filled lengths the library left in the struct."""
@@ -295,6 +301,36 @@ class Cache:
                    for t in (self.refs, self.ref_sqnorm, self.latents, self.idx))
 
 
+class PagedCache(Cache):
+    """A paged cache (shape.page_refs > 0): pools of n_pages pages for the four
+    arrays (refs [n_pages, P, d], ref_sqnorm [n_pages, P], latents [n_pages,
+    P (s - 1), d_c], idx [n_pages, P (s - 1), k]) and the block table (int32
+    [B, H, max_pages] on the device).  The caller assigns pages: write the
+    table (e.g. from a free list) before a call touches the positions an
+    entry covers."""
+
+    def __init__(self, shape: Shape, n_pages: int, block_table: torch.Tensor, device="cuda"):
+        pb = page_bytes(shape)
+        P, npp = shape.page_refs, shape.page_refs * (shape.stride - 1)
+        dt = shape.torch_dtype
+        self.refs = torch.empty(n_pages, P, shape.head_dim, dtype=dt, device=device)
+        self.ref_sqnorm = torch.empty(n_pages, P, dtype=torch.float32, device=device)
+        self.latents = torch.empty(n_pages, npp, shape.d_c, dtype=dt, device=device)
+        self.idx = torch.empty(n_pages, npp, shape.k, dtype=torch.uint16, device=device)
+        assert self.refs[0].numel() * self.refs.element_size() == pb["refs"]
+        assert self.latents[0].numel() * self.latents.element_size() == pb["latents"]
+        if tuple(block_table.shape) != (shape.batch, shape.num_kv_heads, pb["max_pages"]) or \
+                block_table.dtype != torch.int32:
+            raise ValueError(f"block_table must be int32 [B, H, {pb['max_pages']}]")
+        self.block_table = block_table
+        self.n_pages = n_pages
+
+    def c(self) -> CCache:
+        return CCache(_ptr(self.refs), _ptr(self.ref_sqnorm), _ptr(self.latents),
+                      _ptr(self.idx), self.n_built, self.n_compressed, _ptr(self.block_table),
+                      self.n_pages)
+
+
 # --------------------------------------------------------------------- entry points
 
 def cache_bytes(shape: Shape) -> dict:
@@ -302,6 +338,19 @@ def cache_bytes(shape: Shape) -> dict:
     cs = shape.c()
     _check(lib().deltakv_cache_bytes(ctypes.byref(cs), *[ctypes.byref(v) for v in vals]))
     return dict(zip(("refs", "ref_sqnorm", "latents", "idx"), (v.value for v in vals)))
+
+
+def page_bytes(shape: Shape) -> dict:
+    """Bytes of one page of each pool of a paged shape, and max_pages (the
+    block table's row length)."""
+    vals = [_SZ() for _ in range(4)]
+    mp = ctypes.c_int32()
+    cs = shape.c()
+    _check(lib().deltakv_page_bytes(ctypes.byref(cs), *[ctypes.byref(v) for v in vals],
+                                    ctypes.byref(mp)))
+    out = dict(zip(("refs", "ref_sqnorm", "latents", "idx"), (v.value for v in vals)))
+    out["max_pages"] = mp.value
+    return out
 
 
 def compress_workspace_bytes(shape: Shape, t0: int, t1: int) -> int:

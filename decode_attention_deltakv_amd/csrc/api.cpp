@@ -66,6 +66,16 @@ deltakv_status check_shape(const deltakv_shape *sh, dk::Dims *dm) {
     // keep every array's element count far inside int64
     const double elems = (double)sh->batch * sh->num_kv_heads * (double)sh->capacity * 128.0;
     if (elems > 9.0e15) return fail(DELTAKV_ERR_CAPACITY, "cache too large");
+    if (sh->page_refs != 0) {
+        const int pr = sh->page_refs;
+        if (pr < 128 || pr > 4096 || (pr & (pr - 1)) != 0)
+            return fail(DELTAKV_ERR_UNSUPPORTED,
+                        "page_refs %d: a paged cache needs a power of two in [128, 4096]", pr);
+        if (sh->stride < 2 || sh->dtype != DELTAKV_BF16 ||
+            sh->latent_format != DELTAKV_LATENT_DTYPE)
+            return fail(DELTAKV_ERR_UNSUPPORTED,
+                        "a paged cache needs stride >= 2, bf16 storage and latents in bf16");
+    }
     if (dm) {
         dm->B = sh->batch;
         dm->H = sh->num_kv_heads;
@@ -78,6 +88,7 @@ deltakv_status check_shape(const deltakv_shape *sh, dk::Dims *dm) {
         dm->cap = sh->capacity;
         dm->R = R;
         dm->N = sh->capacity - R;
+        dm->pr = sh->page_refs;
     }
     return DELTAKV_OK;
 }
@@ -134,6 +145,18 @@ deltakv_status check_cache(const deltakv_cache *c, const dk::Dims &dm, const cha
     a->sqn = c->ref_sqnorm;
     a->lat = c->latents;
     a->idx = c->idx;
+    a->tbl = nullptr;
+    a->npages = 0;
+    if (dm.pr) {
+        if (!c->block_table || (reinterpret_cast<uintptr_t>(c->block_table) & 3u))
+            return fail(DELTAKV_ERR_INVALID_ARG,
+                        "%s: a paged cache needs a 4-byte aligned block_table", name);
+        if (c->n_pages < 1 || c->n_pages > INT32_MAX)
+            return fail(DELTAKV_ERR_INVALID_ARG, "%s: n_pages %lld not in [1, 2^31)", name,
+                        (long long)c->n_pages);
+        a->tbl = c->block_table;
+        a->npages = c->n_pages;
+    }
     return DELTAKV_OK;
 }
 
@@ -177,10 +200,36 @@ deltakv_status deltakv_cache_bytes(const deltakv_shape *shape, size_t *refs_byte
     deltakv_status st = check_shape(shape, &dm);
     if (st != DELTAKV_OK) return st;
     const size_t units = (size_t)dm.B * dm.H;
+    if (dm.pr) {
+        // pools with every logical page of every unit backed
+        const size_t pages = units * (size_t)dk::pages_per_unit(dm);
+        const size_t pr = (size_t)dm.pr, npp = pr * (size_t)(dm.s - 1);
+        if (refs_bytes) *refs_bytes = pages * pr * dm.d * elt_bytes(dm);
+        if (ref_sqnorm_bytes) *ref_sqnorm_bytes = pages * pr * sizeof(float);
+        if (latents_bytes) *latents_bytes = pages * npp * dm.dc * elt_bytes(dm);
+        if (idx_bytes) *idx_bytes = pages * npp * dm.k * sizeof(uint16_t);
+        return ok();
+    }
     if (refs_bytes) *refs_bytes = units * dm.R * dm.d * elt_bytes(dm);
     if (ref_sqnorm_bytes) *ref_sqnorm_bytes = units * dm.R * sizeof(float);
     if (latents_bytes) *latents_bytes = units * (size_t)dk::lat_unit_bytes(dm);
     if (idx_bytes) *idx_bytes = units * dm.N * dm.k * sizeof(uint16_t);
+    return ok();
+}
+
+deltakv_status deltakv_page_bytes(const deltakv_shape *shape, size_t *refs_bytes,
+                                  size_t *ref_sqnorm_bytes, size_t *latents_bytes,
+                                  size_t *idx_bytes, int32_t *max_pages) {
+    dk::Dims dm;
+    deltakv_status st = check_shape(shape, &dm);
+    if (st != DELTAKV_OK) return st;
+    if (!dm.pr) return fail(DELTAKV_ERR_INVALID_ARG, "page_refs is 0: the shape is not paged");
+    const size_t pr = (size_t)dm.pr, npp = pr * (size_t)(dm.s - 1);
+    if (refs_bytes) *refs_bytes = pr * dm.d * elt_bytes(dm);
+    if (ref_sqnorm_bytes) *ref_sqnorm_bytes = pr * sizeof(float);
+    if (latents_bytes) *latents_bytes = npp * dm.dc * elt_bytes(dm);
+    if (idx_bytes) *idx_bytes = npp * dm.k * sizeof(uint16_t);
+    if (max_pages) *max_pages = (int32_t)dk::pages_per_unit(dm);
     return ok();
 }
 
@@ -341,6 +390,7 @@ deltakv_status deltakv_residuals(const deltakv_shape *shape, const void *x, int6
     if (!x) return fail(DELTAKV_ERR_INVALID_ARG, "x is NULL");
     if (!aligned16(x)) return fail(DELTAKV_ERR_INVALID_ARG, "x must be 16-byte aligned");
     if ((st = check_cache(cache, dm, "cache", true, &ca, t1)) != DELTAKV_OK) return st;
+    if (dm.pr) return fail(DELTAKV_ERR_UNSUPPORTED, "residual rows of a paged cache");
     const int64_t nq = dk::toks_upto(t1, dm.s) - dk::toks_upto(t0, dm.s);
     if (nq == 0) return ok();
     if (!out) return fail(DELTAKV_ERR_INVALID_ARG, "out is NULL");
@@ -396,11 +446,14 @@ deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_i
                         "%s: appending position %lld needs n_built == n_compressed == %lld "
                         "(have %lld, %lld)", name, (long long)t, (long long)t,
                         (long long)it.cache->n_built, (long long)it.cache->n_compressed);
+        // (paged caches may share a pool: then their block tables tell them apart)
         for (int j = 0; j < i; ++j)
-            if (items[j].cache == it.cache || items[j].cache->refs == it.cache->refs)
+            if (items[j].cache == it.cache ||
+                (items[j].cache->refs == it.cache->refs &&
+                 (!dm.pr || items[j].cache->block_table == it.cache->block_table)))
                 return fail(DELTAKV_ERR_INVALID_ARG, "items %d and %d name the same cache", j,
                             i);
-        batched = batched && dk::append_batched_supported(dm, ma[i]) &&
+        batched = batched && !dm.pr && dk::append_batched_supported(dm, ma[i]) &&
                   ma[i].hidden == ma[0].hidden && ma[i].act == ma[0].act;
     }
     const size_t need = dk::append_ws_bytes(dm, t, n_items);
@@ -558,6 +611,20 @@ deltakv_status deltakv_train_step(int64_t n_rows, const float *delta,
 
 namespace {
 
+// Paged caches: the wave-specialised decode's shapes and one block table for
+// K and V.
+deltakv_status check_paged_decode(const dk::Dims &dm, const deltakv_cache *k_cache,
+                                  const dk::MlpArgs &km, const deltakv_cache *v_cache,
+                                  const dk::MlpArgs &vm) {
+    if (!dm.pr) return DELTAKV_OK;
+    if (!dk::decode_counts_supported(dm, km, vm))
+        return fail(DELTAKV_ERR_UNSUPPORTED, "paged caches: decode needs k 4 or 8, d_c <= 32 and "
+                    "GELU decompressors of one hidden width, 128 or 256");
+    if (k_cache->block_table != v_cache->block_table)
+        return fail(DELTAKV_ERR_UNSUPPORTED, "paged caches: K and V must share one block table");
+    return DELTAKV_OK;
+}
+
 // Argument checks of the dense decode (everything but the workspace).
 deltakv_status check_decode(const deltakv_shape *shape, int32_t num_q_heads, int64_t n_tokens,
                             const void *q, const deltakv_cache *k_cache,
@@ -587,7 +654,7 @@ deltakv_status check_decode(const deltakv_shape *shape, int32_t num_q_heads, int
                     "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
-    return DELTAKV_OK;
+    return check_paged_decode(dm, k_cache, km, v_cache, vm);
 }
 
 }  // namespace
@@ -721,6 +788,7 @@ deltakv_status deltakv_decode_attn_sparse(const deltakv_shape *shape, int32_t nu
                     "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
+    if (dm.pr) return fail(DELTAKV_ERR_UNSUPPORTED, "sparse decode over a paged cache");
     const size_t need = dk::decode_sparse_ws_bytes(dm, num_q_heads, n_tokens, n_sel);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "sparse decode needs %zu workspace bytes, got %zu",
@@ -764,6 +832,7 @@ deltakv_status deltakv_decode_attn_select(const deltakv_shape *shape, int32_t nu
                     "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_paged_decode(dm, k_cache, km, v_cache, vm)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_select_ws_bytes(dm, num_q_heads, n_tokens);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "decode with selection needs %zu workspace bytes, "
@@ -806,6 +875,7 @@ deltakv_status deltakv_decode_attn_window(const deltakv_shape *shape, int32_t nu
                     "decompressors of one hidden width, 128 or 256");
     if ((st = check_cache(k_cache, dm, "k_cache", true, &kc, n_tokens)) != DELTAKV_OK) return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, n_tokens)) != DELTAKV_OK) return st;
+    if ((st = check_paged_decode(dm, k_cache, km, v_cache, vm)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_window_ws_bytes(dm, num_q_heads, n_tokens, n_win);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "decode with a window needs %zu workspace bytes, "
@@ -852,6 +922,7 @@ deltakv_status deltakv_decode_attn_varlen(const deltakv_shape *shape, int32_t nu
         return st;
     if ((st = check_cache(v_cache, dm, "v_cache", true, &vc, max_tokens)) != DELTAKV_OK)
         return st;
+    if ((st = check_paged_decode(dm, k_cache, km, v_cache, vm)) != DELTAKV_OK) return st;
     const size_t need = dk::decode_varlen_ws_bytes(dm, num_q_heads, nmax);
     if (workspace_bytes < need || !workspace)
         return fail(DELTAKV_ERR_WORKSPACE, "mixed-length decode needs %zu workspace bytes, "

@@ -36,6 +36,41 @@ __host__ __device__ inline int64_t tok_pos(int64_t q, int s) {
     return (q / (s - 1)) * s + (q % (s - 1)) + 1;
 }
 
+// ---- paged layout ------------------------------------------------------------------
+// A paged cache keeps the rows of every unit in fixed-size pages of one pool
+// per array, as a paged KV cache for batched serving does: a page holds the
+// rows of pr * s consecutive positions of one unit (pr reference rows and
+// pr (s - 1) compressed-token rows), and a block table lists, for each unit,
+// the pool page behind each of its logical pages.  Logical page lp of a unit
+// covers reference ordinals [lp pr, (lp + 1) pr) and token ordinals
+// [lp npp, (lp + 1) npp), npp = pr (s - 1).
+constexpr int kMaxPages = 512;   // logical pages per unit (65535 references / 128 per page)
+
+struct PageMap {
+    const int32_t *tbl = nullptr;  // [units][maxp]; null: unit-contiguous arrays
+    int64_t maxp = 0;              // table row length (logical pages per unit)
+    int32_t lg = 0;                // log2 of the reference rows per page
+    int32_t npp = 0;               // compressed-token rows per page
+    int32_t npages = 0;            // pool pages: entries are clamped into [0, npages)
+};
+
+// Pool page behind logical page lp of `unit` (both clamped into range, so a
+// bad table entry cannot move an access out of the pool).
+__device__ __forceinline__ int64_t pg_page(const PageMap &pm, int64_t unit, int64_t lp) {
+    lp = lp < 0 ? 0 : (lp >= pm.maxp ? pm.maxp - 1 : lp);
+    const uint32_t v = (uint32_t)pm.tbl[unit * pm.maxp + lp];
+    return (int64_t)(v < (uint32_t)pm.npages ? v : (uint32_t)pm.npages - 1u);
+}
+// Pool row of reference ordinal j of `unit`.
+__device__ __forceinline__ int64_t pg_ref_row(const PageMap &pm, int64_t unit, int64_t j) {
+    return (pg_page(pm, unit, j >> pm.lg) << pm.lg) + (j & (((int64_t)1 << pm.lg) - 1));
+}
+// Pool row of token ordinal q of `unit`.
+__device__ __forceinline__ int64_t pg_tok_row(const PageMap &pm, int64_t unit, int64_t q) {
+    const int64_t lp = q / pm.npp;
+    return pg_page(pm, unit, lp) * pm.npp + (q - lp * pm.npp);
+}
+
 // ---- scalar conversions ----------------------------------------------------------
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }

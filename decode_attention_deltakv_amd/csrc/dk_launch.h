@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dk_common.h"
+
 namespace dk {
 
 // Sizes of one (layer, stream) cache, derived from deltakv_shape.
@@ -17,6 +19,7 @@ struct Dims {
     int64_t cap;        // capacity (positions)
     int64_t R;          // reference rows per unit = ceil(cap / s)
     int64_t N;          // compressed-token rows per unit = cap - R
+    int pr = 0;         // paged layout: reference rows per page (0: unit-contiguous arrays)
 };
 
 struct MlpArgs {
@@ -32,7 +35,27 @@ struct CacheArgs {
     float *sqn;
     void *lat;
     uint16_t *idx;
+    const int32_t *tbl = nullptr;  // paged layout: block table [B][H][max_pages]
+    int64_t npages = 0;            // paged layout: pages in each pool
 };
+
+// Paged layout: logical pages per unit, and the device-side page map of a
+// cache (dm.pr != 0).
+inline int64_t pages_per_unit(const Dims &dm) {
+    const int64_t pp = (int64_t)dm.pr * dm.s;
+    return (dm.cap + pp - 1) / pp;
+}
+inline PageMap page_map(const Dims &dm, const CacheArgs &c) {
+    PageMap pm;
+    pm.tbl = c.tbl;
+    pm.maxp = pages_per_unit(dm);
+    int lg = 0;
+    while ((1 << lg) < dm.pr) ++lg;
+    pm.lg = lg;
+    pm.npp = dm.pr * (dm.s - 1);
+    pm.npages = (int32_t)c.npages;
+    return pm;
+}
 
 // reference-set build
 hipError_t launch_build_refs(const Dims &dm, const void *x, int64_t t0, int64_t t1,
@@ -43,6 +66,14 @@ size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);
 hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                            const MlpArgs &comp, const CacheArgs &c, void *ws, size_t ws_bytes,
                            uint32_t *stats, hipStream_t st);
+
+// compression into a paged cache (k_paged.hip): the unit's reference pages
+// staged contiguously, the unit-contiguous kernels, the range's rows copied
+// into their pages
+size_t paged_compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);
+hipError_t launch_compress_paged(const Dims &dm, const void *x, int64_t t0, int64_t t1,
+                                 const MlpArgs &comp, const CacheArgs &c, void *ws,
+                                 size_t ws_bytes, uint32_t *stats, hipStream_t st);
 
 // decode attention
 size_t decode_ws_bytes(const Dims &dm, int Hq, int64_t T);

@@ -171,9 +171,10 @@ __device__ __forceinline__ void compress_mfma_body(
     auto chunk_q = [&](uint32_t qt, int m) { return min(qt + (uint32_t)((tid + 256 * m) / CH), qlast); };
     // index lists and reference rows through buffer resources: every load
     // is issued (no branch, so the wait counts stay exact) and a read past a
-    // resource's end returns zeros
+    // resource's end returns zeros (the index rows end at the range's last
+    // token: the slots past k of that token are masked where used)
     const __amdgpu_buffer_rsrc_t idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)uidx, (short)0, (int)(Ncap * k * 2), 0x00020000);
+        (void *)uidx, (short)0, (int)(qend * k * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t ref_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)urefs, (short)0, (int)(Rcap * D * 2), 0x00020000);
 
@@ -546,6 +547,7 @@ bool compress_q4_supported(const Dims &dm, const MlpArgs &comp) {
 // of the range and unit, then (when the top-k search splits its reference
 // ranges) each split's candidate lists and largest reference norms.
 size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
+    if (dm.pr) return paged_compress_ws_bytes(dm, t0, t1);
     if (dm.dtype != 1) return 0;
     const int64_t nq = toks_upto(t1, dm.s) - toks_upto(t0, dm.s);
     const size_t flist = ((size_t)nq * dm.B * dm.H * sizeof(uint64_t) + 255) & ~(size_t)255;
@@ -559,7 +561,7 @@ size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
 hipError_t launch_compress(const Dims &dm, const void *x, int64_t t0, int64_t t1,
                            const MlpArgs &comp, const CacheArgs &c, void *ws, size_t ws_bytes,
                            uint32_t *stats, hipStream_t st) {
-    (void)ws_bytes;
+    if (dm.pr) return launch_compress_paged(dm, x, t0, t1, comp, c, ws, ws_bytes, stats, st);
     const int64_t q0 = toks_upto(t0, dm.s);
     const int64_t nq = toks_upto(t1, dm.s) - q0;
     if (nq <= 0) return hipSuccess;

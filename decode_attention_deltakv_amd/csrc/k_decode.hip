@@ -424,7 +424,8 @@ __device__ __forceinline__ void sparse_split_block(const int32_t *__restrict__ p
 //                      g = x - nrb of the KV head
 //   x == nrb + G       (sparse calls only, pos non-null, one more block) the
 //                      split of the unit's position list (sparse_split_block)
-template <typename T>
+// PG: paged reference rows, looked up through the block table in pm.
+template <typename T, bool PG>
 __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int Hq, int G, int d,
                                                    const T *__restrict__ krefs, int64_t Rcap,
                                                    int64_t Rt, int nrb, const T *__restrict__ w2,
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
                                                    float *__restrict__ qr,
                                                    const int32_t *__restrict__ pos, int nsel,
                                                    int64_t ntok, int s, int32_t *__restrict__ ord,
-                                                   int32_t *__restrict__ cnt) {
+                                                   int32_t *__restrict__ cnt, PageMap pm) {
     __shared__ float qs[kMaxG][kMaxD];
     __shared__ float red[1][32][kMaxH];
     const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, H = gridDim.y;
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
             for (int it = 0; it < 4; ++it) {
                 const int64_t j0 = (int64_t)blockIdx.x * 256 + 64 * it + 16 * w;
                 const int64_t jr = min(j0 + l16, Rt - 1 < 0 ? 0 : Rt - 1);
-                const T *r = krefs + (unit * Rcap + jr) * d;
+                const T *r = krefs + (PG ? pg_ref_row(pm, unit, jr) : unit * Rcap + jr) * d;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) rv[it][ks] = ld16(r + min(32 * ks, d - 32) + 8 * lq);
             }
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T *__restrict__ q, int 
 #pragma unroll
             for (int g = 0; g < kMaxG; ++g) acc[g] = 0.f;
             if (j < Rt) {
-                const T *r = krefs + (unit * Rcap + j) * d;
+                const T *r = krefs + (PG ? pg_ref_row(pm, unit, j) : unit * Rcap + j) * d;
                 for (int c0 = 0; c0 < d; c0 += 8) {
                     float v[8];
                     load8(r + c0, v);
@@ -1504,7 +1505,11 @@ constexpr float kSlack = 8.f;
 
 // EG: groups of 4 query heads per KV head (1 for G <= 4, 2 for G <= 8).
 // KX: references per token (k = 4 or k = 8).
-template <int D, int DC, int HID, int EG, int KX, bool SP, bool Q4>
+// PG: paged caches (K and V share the block table in pm): the unit's table row
+// is staged in LDS; a tile's latent and index rows lie in one page (tiles and
+// pages are whole multiples of 32 tokens), and each gathered or reference row
+// is looked up by its ordinal.
+template <int D, int DC, int HID, int EG, int KX, bool SP, bool Q4, bool PG>
 __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     int U, int Hq, int G, int64_t Rcap, int64_t Ncap, int64_t Rt, int64_t Nt,
     int tiles_per_part, int Ptok, int P, const bf16_t *__restrict__ klat,
@@ -1514,7 +1519,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const bf16_t *__restrict__ vw1, const float *__restrict__ vb1, float scale,
     const float *__restrict__ ubuf, const float *__restrict__ cq, const float *__restrict__ qr,
     float *__restrict__ part, float *__restrict__ logc, float *__restrict__ logr,
-    const int32_t *__restrict__ sord, const int32_t *__restrict__ scnt, int nsel) {
+    const int32_t *__restrict__ sord, const int32_t *__restrict__ scnt, int nsel, PageMap pm) {
     constexpr int TT = 32;             // tokens per tile
     constexpr int TH = 16;             // tokens per score wave
     constexpr int MB = HID / 16;       // 16-row hidden blocks (score waves)
@@ -1535,6 +1540,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     static_assert(HID == 128 || HID == 256, "hidden width");
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(KX == 4 || KX == 8, "references per token");
+    static_assert(!(PG && (SP || Q4)), "paged caches: dense calls with latents in bf16");
     using IdxV = typename std::conditional<KX == 4, u32x2, u32x4>::type;
 
     // V rows of two tiles: two objects, so the compiler can tell the DMA fill
@@ -1573,6 +1579,19 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int64_t Nt_u = (SP || cmode) ? (int64_t)scnt[2 * unit] : Nt;
     const int64_t Rt_u = (SP || cmode) ? (int64_t)scnt[2 * unit + 1] : Rt;
     __shared__ int32_t ordl[SP ? kSpTiles * 32 : 1];
+    // paged layout: the unit's block-table row, clamped into the pool
+    __shared__ int32_t ptab[PG ? kMaxPages : 1];
+    if constexpr (PG) {
+        for (int i = tid; i < (int)pm.maxp; i += 256) ptab[i] = (int32_t)pg_page(pm, unit, i);
+        __syncthreads();
+    }
+    // pool row of reference ordinal j (paged), its unit row otherwise
+    auto ref_row = [&](uint32_t j) -> int64_t {
+        if constexpr (PG)
+            return ((int64_t)ptab[j >> pm.lg] << pm.lg) | (int64_t)(j & ((1u << pm.lg) - 1u));
+        else
+            return (int64_t)unit * Rcap + j;
+    };
 
     // ---------------- reference tokens ----------------
     // Reference partition r: rows [r kRefPart, (r + 1) kRefPart) of the unit,
@@ -1600,7 +1619,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const int64_t j = SP ? (int64_t)rord_u[min(j0 + row, je - 1)]
                                      : min(j0 + row, je - 1);
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(vref_u + j * D + 8 * sc8),
+                    (const void *)(PG ? vref + ref_row((uint32_t)j) * D + 8 * sc8
+                                      : vref_u + j * D + 8 * sc8),
                     (__attribute__((address_space(3))) void *)&vbufA[(256 * m + 64 * w) / CH][0],
                     16, 0, 0);
             }
@@ -1724,6 +1744,14 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     auto tok_of = [&](int i) -> uint32_t {
         return SP ? (uint32_t)ordl[min(i, qe - 1) - qa] : (uint32_t)min(i, tlast);
     };
+    // paged layout: logical page of the tile at t0 (its clamped tokens lie in
+    // the page of min(t0, tlast)) and the offset, in rows, from a token's
+    // ordinal to its pool row
+    auto tile_page = [&](int t0) -> int { return min(t0, tlast) / pm.npp; };
+    auto tok_shift = [&](int t0) -> int64_t {
+        const int lp = tile_page(t0);
+        return (int64_t)(__builtin_amdgcn_readfirstlane(ptab[lp]) - lp) * pm.npp;
+    };
 
     if (w < 2) {
         // ================= score waves =================
@@ -1769,9 +1797,16 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // rows of token (t0 + 16 src + l16), clamped to a stored token
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = tok_of(t0 + TH * src + l16);
-            in.z = zrow(klat_u, kq_u, tok);
-            in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
-            in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
+            if constexpr (PG) {
+                const int64_t sh = tok_shift(t0);
+                in.z = zrow(klat + sh * DC, kq_u, tok);
+                in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx + sh * KX, tok * (KX * 2)));
+                in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx + sh * KX, tok * (KX * 2)));
+            } else {
+                in.z = zrow(klat_u, kq_u, tok);
+                in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx_u, tok * (KX * 2)));
+                in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx_u, tok * (KX * 2)));
+            }
         };
         // q.R^K of the token's references for the lane's heads (unused slots
         // read the all-zero row Rt)
@@ -1991,7 +2026,22 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         // (the tile offset goes in the per-lane offset, which the range check
         // covers, not in the scalar offset)
         auto gload = [&](int t0) {
-            if constexpr (SP) {
+            if constexpr (PG) {
+                // the tile's page as a buffer of its stored rows: offsets
+                // relative to the page start, rows past it (or past the stored
+                // tokens) read 0
+                const int lp = tile_page(t0);
+                const int pstart = lp * pm.npp;
+                const int pp = __builtin_amdgcn_readfirstlane(ptab[lp]);
+                const int nrec = min(pm.npp, (int)Nt - pstart);
+                const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(vidx + (int64_t)pp * pm.npp * KX), (short)0, nrec * (KX * 2),
+                    0x00020000);
+                const int vbase = (t0 - pstart + TH * vj) * (KX * 2) + (int)(lrow * 2u);
+#pragma unroll
+                for (int m = 0; m < NDMA; ++m)
+                    gi[m] = __builtin_amdgcn_raw_buffer_load_b16(prsrc, vbase + 2 * RPD * m, 0, 0);
+            } else if constexpr (SP) {
                 // row r = lrow + RPD m is (token r / KX, slot r % KX) of this
                 // wave's 16 tokens, looked up through the list
 #pragma unroll
@@ -2015,7 +2065,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             for (int m = 0; m < NDMA; ++m) {
                 const uint32_t j = min(gi[m], rlast);
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)((const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
+                    (const void *)(PG ? (const char *)vref + ((uint64_t)ref_row(j) * (D * 2) + coff)
+                                      : (const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
                     (__attribute__((address_space(3))) void *)&dst[(KX == 4 ? 64 * vj : 0) + RPD * m][0], 16, 0, 0);
             }
         };
@@ -2023,7 +2074,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const uint32_t tok = tok_of(t0 + 16 * mb + l16);
-                z[mb] = zrow(vlat_u, vq_u, tok);
+                z[mb] = zrow(PG ? vlat + tok_shift(t0) * DC : vlat_u, vq_u, tok);
             }
         };
 
@@ -2275,6 +2326,7 @@ struct SparseArgs {
     int nsel;
     float *logc;
     float *logr;
+    PageMap pm;   // paged caches (pm.tbl non-null)
 };
 
 template <int D, int DC, int HID, int KP>
@@ -2304,18 +2356,23 @@ void launch_ws_t(const Dims &dm, int Hq, const DecPlan &pl, const CacheArgs &kc,
     auto pick = [&](auto q4c) {
         constexpr bool QF = decltype(q4c)::value;
         return dm.k == 4
-                   ? (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 4, true, QF> : main_ws_kernel<D, DC, HID, 1, 4, false, QF>)
-                             : (sp ? main_ws_kernel<D, DC, HID, 2, 4, true, QF> : main_ws_kernel<D, DC, HID, 2, 4, false, QF>))
-                   : (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 8, true, QF> : main_ws_kernel<D, DC, HID, 1, 8, false, QF>)
-                             : (sp ? main_ws_kernel<D, DC, HID, 2, 8, true, QF> : main_ws_kernel<D, DC, HID, 2, 8, false, QF>));
+                   ? (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 4, true, QF, false> : main_ws_kernel<D, DC, HID, 1, 4, false, QF, false>)
+                             : (sp ? main_ws_kernel<D, DC, HID, 2, 4, true, QF, false> : main_ws_kernel<D, DC, HID, 2, 4, false, QF, false>))
+                   : (G <= 4 ? (sp ? main_ws_kernel<D, DC, HID, 1, 8, true, QF, false> : main_ws_kernel<D, DC, HID, 1, 8, false, QF, false>)
+                             : (sp ? main_ws_kernel<D, DC, HID, 2, 8, true, QF, false> : main_ws_kernel<D, DC, HID, 2, 8, false, QF, false>));
     };
     auto kern = dm.lat_fmt ? pick(std::true_type()) : pick(std::false_type());
+    if (sa.pm.tbl)
+        kern = dm.k == 4 ? (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 4, false, false, true>
+                                   : main_ws_kernel<D, DC, HID, 2, 4, false, false, true>)
+                         : (G <= 4 ? main_ws_kernel<D, DC, HID, 1, 8, false, false, true>
+                                   : main_ws_kernel<D, DC, HID, 2, 8, false, false, true>);
     hipLaunchKernelGGL(kern, dim3((unsigned)(pl.P * U)), dim3(256), 0, st,
                        U, Hq, G, dm.R, dm.N, pl.Rt, pl.Nt, pl.tiles_per_part, (int)pl.Ptok,
                        (int)pl.P, (const bf16_t *)kc.lat, kc.idx, (const bf16_t *)vc.refs,
                        (const bf16_t *)vc.lat, vc.idx, (const bf16_t *)kd.w1, kd.b1,
                        (const bf16_t *)vd.w1, vd.b1, scale, u, cq, qr, part, sa.logc, sa.logr,
-                       sa.ord, sa.cnt, sa.nsel);
+                       sa.ord, sa.cnt, sa.nsel, sa.pm);
 }
 
 // The wave-specialised kernel covers k = 4 or 8 and d_c <= 32.
@@ -2379,26 +2436,34 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
                            float *logc = nullptr, float *logr = nullptr, float *lse = nullptr,
                            uint32_t *hist0 = nullptr, const int32_t *counts = nullptr) {
     const DecPlan pl = plan_decode(dm, Hq, T_, pos ? (int64_t)nsel : -1);
+    // paged caches: K and V share one block table (entries clamped into the
+    // smaller pool)
+    PageMap pm;
+    if (dm.pr) {
+        pm = page_map(dm, kc);
+        pm.npages = (int32_t)std::min(kc.npages, vc.npages);
+    }
     const int G = Hq / dm.H;
     char *w = (char *)ws;
     float *u = (float *)(w + pl.off_u);
     float *cq = (float *)(w + pl.off_cq);
     float *qr = (float *)(w + pl.off_qr);
     float *part = (float *)(w + pl.off_part);
-    SparseArgs sa{nullptr, counts, 0, logc, logr};
+    SparseArgs sa{nullptr, counts, 0, logc, logr, pm};
     int32_t *ord = nullptr, *cnt = nullptr;
     if (pos) {
         ord = (int32_t *)(w + pl.off_ord);
         cnt = (int32_t *)(w + pl.off_cnt);
-        sa = SparseArgs{ord, cnt, nsel, nullptr, nullptr};
+        sa = SparseArgs{ord, cnt, nsel, nullptr, nullptr, PageMap{}};
     }
     // the query-side tables, and for a sparse call the list split (one more
     // block per unit)
     const int nrb = (int)((qr_rows(pl.Rt) + 255) / 256);
-    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)(nrb + G + (pos ? 1 : 0)), dm.H, dm.B),
+    hipLaunchKernelGGL((dm.pr ? prep_kernel<T, true> : prep_kernel<T, false>),
+                       dim3((unsigned)(nrb + G + (pos ? 1 : 0)), dm.H, dm.B),
                        dim3(256), 0, st, (const T *)q, Hq, G, dm.d, (const T *)kc.refs, dm.R,
                        pl.Rt, nrb, (const T *)kd.w2, kd.hidden, kd.b2, u, cq, qr, pos, nsel, T_,
-                       dm.s, ord, cnt);
+                       dm.s, ord, cnt, pm);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
         if (mfma_eligible(dm, kd, vd)) {
@@ -2418,7 +2483,7 @@ hipError_t launch_decode_t(const Dims &dm, int Hq, int64_t T_, const void *q,
             }
         }
     }
-    if (!done && dm.lat_fmt) return hipErrorInvalidValue;  // (rejected before any launch)
+    if (!done && (dm.lat_fmt || dm.pr)) return hipErrorInvalidValue;  // (rejected before any launch)
     if (!done)
         hipLaunchKernelGGL(main_kernel<T>, dim3((unsigned)pl.P, dm.H, dm.B), dim3(256), 0, st, Hq,
                            G, dm.d, dm.dc, dm.k, dm.s, dm.R, dm.N, pl.Rt, pl.Nt, pl.Ptok,
@@ -2445,6 +2510,7 @@ static Dims window_dims(const Dims &dm, int64_t n_win) {
     w.R = n_win;
     w.N = 0;
     w.lat_fmt = 0;
+    w.pr = 0;   // the window rows are one contiguous array
     return w;
 }
 

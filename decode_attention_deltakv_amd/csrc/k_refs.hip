@@ -27,19 +27,20 @@ __device__ __forceinline__ void copy_ref_row(const T *__restrict__ src, T *__res
     if (lane == 0) *sqn_dst = acc;
 }
 
+// (paged layout, pm.tbl non-null: the row goes to its pool page)
 template <typename T>
 __global__ __launch_bounds__(256) void build_refs_kernel(const T *__restrict__ x, int64_t t0,
                                                          int64_t nrows, int s, int d,
                                                          int64_t Rcap, int64_t j0, int64_t nj,
                                                          T *__restrict__ refs,
-                                                         float *__restrict__ sqn) {
+                                                         float *__restrict__ sqn, PageMap pm) {
     const int lane = threadIdx.x & 63;
     const int64_t jj = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (jj >= nj) return;
     const int64_t unit = blockIdx.y;
     const int64_t j = j0 + jj;
-    copy_ref_row<T>(x + (unit * nrows + (j * s - t0)) * d, refs + (unit * Rcap + j) * d,
-                    sqn + unit * Rcap + j, d, lane);
+    const int64_t row = pm.tbl ? pg_ref_row(pm, unit, j) : unit * Rcap + j;
+    copy_ref_row<T>(x + (unit * nrows + (j * s - t0)) * d, refs + row * d, sqn + row, d, lane);
 }
 
 // Batched appends at a reference position t: the row of every unit of every
@@ -73,14 +74,15 @@ hipError_t launch_build_refs(const Dims &dm, const void *x, int64_t t0, int64_t 
     const int64_t nj = refs_upto(t1, dm.s) - j0;
     if (nj <= 0) return hipSuccess;
     dim3 grid((unsigned)((nj + 3) / 4), (unsigned)(dm.B * dm.H));
+    const PageMap pm = dm.pr ? page_map(dm, c) : PageMap{};
     if (dm.dtype == 0)
         hipLaunchKernelGGL(build_refs_kernel<float>, grid, dim3(256), 0, st,
                            (const float *)x, t0, t1 - t0, dm.s, dm.d, dm.R, j0, nj,
-                           (float *)c.refs, c.sqn);
+                           (float *)c.refs, c.sqn, pm);
     else
         hipLaunchKernelGGL(build_refs_kernel<bf16_t>, grid, dim3(256), 0, st,
                            (const bf16_t *)x, t0, t1 - t0, dm.s, dm.d, dm.R, j0, nj,
-                           (bf16_t *)c.refs, c.sqn);
+                           (bf16_t *)c.refs, c.sqn, pm);
     return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ hipError_t launch_decode_varlen(const Dims &dm, int Hq, const int64_t *lens, int
         return launch_decode_counts(dm, Hq, nmax, q, kc, kdec, vc, vdec, counts, scale, out, dws,
                                     st);
     }
+    if (dm.pr) return hipErrorInvalidValue;  // paged caches take the counts path only
     hipLaunchKernelGGL(varlen_lists_kernel, dim3((unsigned)((nmax + 255) / 256), dm.H, dm.B),
                        dim3(256), 0, st, lens, (int)nmax, pos);
     e = hipGetLastError();

@@ -74,7 +74,11 @@ typedef enum {
  * (reference ordinals are stored as uint16).  latent_format
  * DELTAKV_LATENT_Q4 needs bf16, d_c in {16, 32}, and calls whose MLPs are
  * GELU with hidden width 128 or 256 (the same for K and V) and k in {4, 8};
- * other calls on such a cache return UNSUPPORTED. */
+ * other calls on such a cache return UNSUPPORTED.
+ * page_refs selects the layout of the cache arrays: 0 for one contiguous
+ * block per unit (below), or the reference rows per page of a paged cache
+ * (see deltakv_cache): a power of two in [128, 4096], with stride >= 2, bf16
+ * storage and latent_format 0 (UNSUPPORTED otherwise). */
 typedef struct {
     int32_t batch;         /* B: sequences */
     int32_t num_kv_heads;  /* H: KV heads of the layer */
@@ -85,6 +89,7 @@ typedef struct {
     int64_t capacity;      /* maximum context length in tokens (per sequence) */
     int32_t dtype;         /* deltakv_dtype */
     int32_t latent_format; /* deltakv_latent_format (0: latents in dtype) */
+    int32_t page_refs;     /* 0: unit-contiguous arrays; else reference rows per page */
 } deltakv_shape;
 
 /* A light MLP: out = W2 act(W1 in + b1) + b2 (section 3, step 4: the
@@ -138,7 +143,32 @@ typedef struct {
  * and t1 <= n_built and sets n_compressed = t1; the decode calls read at most
  * min(n_compressed of the K and V caches) positions.  Always 0 <= n_compressed
  * <= n_built <= capacity.  To refill the arrays from position 0, set both
- * back to 0. */
+ * back to 0.
+ *
+ * Paged layout (shape->page_refs = P > 0; section 4 of the DeltaKV page asks
+ * for a cache manager for irregular compressed layouts; this is the block-
+ * table layout of paged KV caches for batched serving, with sequences and
+ * heads of different lengths sharing one pool).  A page holds the rows of
+ * P * stride consecutive positions of one unit: P reference rows and P *
+ * (stride - 1) token rows.  The four arrays are then pools of n_pages pages:
+ *   refs        [n_pages][P][d],  ref_sqnorm [n_pages][P],
+ *   latents     [n_pages][P * (stride - 1)][d_c],
+ *   idx         [n_pages][P * (stride - 1)][k]
+ * (deltakv_page_bytes gives one page of each), and
+ *   block_table DEVICE int32 [B][H][max_pages], max_pages = ceil(capacity /
+ *               (P * stride)): entry (b, h, i) is the pool page holding
+ *               positions [i P stride, (i + 1) P stride) of unit (b, h).
+ * The caller owns the pool and the table and assigns pages (e.g. from a free
+ * list as sequences grow); the entries covering the positions a call touches
+ * must name distinct pages in [0, n_pages) (entries outside that range are
+ * clamped into it, so no access leaves the pool).  The K and V caches of a
+ * decode call must share one block table.  Paged caches are served by
+ * deltakv_build_refs, deltakv_compress, deltakv_append (per-cache launches),
+ * and the decode calls without a position list (deltakv_decode_attn, _noalloc,
+ * _select, _window, _varlen) when the wave-specialised decode covers their
+ * shapes (k 4 or 8, d_c <= 32, GELU decompressors of one hidden width, 128 or
+ * 256); other calls return UNSUPPORTED.  Results equal those of the unit-
+ * contiguous layout bit for bit. */
 typedef struct {
     void *refs;
     float *ref_sqnorm;
@@ -146,14 +176,24 @@ typedef struct {
     uint16_t *idx;
     int64_t n_built;       /* host-side filled length: references built */
     int64_t n_compressed;  /* host-side filled length: tokens compressed */
+    const int32_t *block_table;  /* paged layout only (else ignored) */
+    int64_t n_pages;             /* paged layout only: pages in each pool */
 } deltakv_cache;
 
 /* Host-only.  Byte sizes of the four cache arrays for `shape` (any output
- * pointer may be NULL).  Returns INVALID_ARG / UNSUPPORTED / CAPACITY for a
- * shape the other entry points would reject. */
+ * pointer may be NULL); for a paged shape, of pools that hold every unit at
+ * full capacity (B * H * max_pages pages).  Returns INVALID_ARG / UNSUPPORTED /
+ * CAPACITY for a shape the other entry points would reject. */
 deltakv_status deltakv_cache_bytes(const deltakv_shape *shape, size_t *refs_bytes,
                                    size_t *ref_sqnorm_bytes, size_t *latents_bytes,
                                    size_t *idx_bytes);
+
+/* Host-only.  Byte size of one page of each of the four pools of a paged
+ * shape (page_refs > 0; INVALID_ARG otherwise), and max_pages, the block
+ * table's row length (any output pointer may be NULL). */
+deltakv_status deltakv_page_bytes(const deltakv_shape *shape, size_t *refs_bytes,
+                                  size_t *ref_sqnorm_bytes, size_t *latents_bytes,
+                                  size_t *idx_bytes, int32_t *max_pages);
 
 /* Host-only.  Workspace that deltakv_compress needs for positions [t0, t1). */
 deltakv_status deltakv_compress_workspace_bytes(const deltakv_shape *shape, int64_t t0,

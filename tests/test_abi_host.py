@@ -471,7 +471,8 @@ def test_append_position_and_item_count_limits():
 
 @pytest.mark.parametrize("kw", [dict(capacity=131072 + 1024, stride=8, k=8, d_c=16),
                                 dict(capacity=9000, stride=5, k=3, head_dim=64, num_kv_heads=2),
-                                dict(capacity=5000, stride=16, batch=3, dtype=dk.F32)])
+                                dict(capacity=5000, stride=16, batch=3, dtype=dk.F32),
+                                dict(capacity=40000, stride=16, page_refs=128)])
 def test_append_workspace_covers_the_per_cache_compress_and_never_shrinks(kw):
     # a workspace sized for the last position serves every earlier one,
     # reference positions included
@@ -487,3 +488,82 @@ def test_append_workspace_covers_the_per_cache_compress_and_never_shrinks(kw):
             if t % sh.stride:
                 assert w >= dk.compress_workspace_bytes(sh, t, t + 1)
             prev = w
+
+
+# ---- paged layout -------------------------------------------------------------------
+
+
+def test_paged_page_sizes_and_shape_checks():
+    sh = _shape(page_refs=256)                 # stride 16: 4096 positions per page
+    pb = dk.page_bytes(sh)
+    assert pb["refs"] == 256 * 128 * 2 and pb["ref_sqnorm"] == 256 * 4
+    assert pb["latents"] == 256 * 15 * 32 * 2 and pb["idx"] == 256 * 15 * 4 * 2
+    assert pb["max_pages"] == 32768 // 4096
+    full = dk.cache_bytes(sh)                  # every logical page of every unit backed
+    for a in ("refs", "ref_sqnorm", "latents", "idx"):
+        assert full[a] == 8 * pb["max_pages"] * pb[a]
+    # a ragged capacity: the last page is partly used
+    assert dk.page_bytes(_shape(page_refs=128, capacity=5000))["max_pages"] == 3
+    with pytest.raises(dk.DeltaKVError) as e:  # not a paged shape
+        dk.page_bytes(_shape())
+    assert e.value.status == 1
+    for bad in (dict(page_refs=100), dict(page_refs=64), dict(page_refs=8192),
+                dict(page_refs=256, stride=1), dict(page_refs=256, dtype=dk.F32),
+                dict(page_refs=256, latent_format=dk.LATENT_Q4)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.page_bytes(_shape(**bad))
+        assert e.value.status == 2, bad
+
+
+def _pcache(addr=0x10000, filled=4096, table=0x50000, n_pages=64):
+    c = dk.PagedCache.__new__(dk.PagedCache)
+    c.refs = c.ref_sqnorm = c.latents = c.idx = _FakePtr(addr)
+    c.block_table = _FakePtr(table) if table else None
+    c.n_pages = n_pages
+    c.n_built = c.n_compressed = filled
+    return c
+
+
+def test_paged_cache_arguments_checked_before_any_launch():
+    sh = _shape(capacity=4096, page_refs=128)
+    x = _FakePtr()
+    for c in (_pcache(filled=0, table=0), _pcache(filled=0, table=0x50002),
+              _pcache(filled=0, n_pages=0)):
+        with pytest.raises(dk.DeltaKVError) as e:
+            dk.build_refs(sh, x, 0, 16, c)
+        assert e.value.status == 1 and ("block_table" in e.value.detail or
+                                        "n_pages" in e.value.detail)
+    dec = _mlp(32, 256, 128)
+    ws = _FakePtr(0x30000, 1 << 30)
+    # K and V must share one block table
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.decode_attn(sh, 32, 4096, _FakePtr(), _pcache(), dec, _pcache(table=0x60000), dec,
+                       0.088, _FakePtr(), ws)
+    assert e.value.status == 2 and "block table" in e.value.detail
+    # shapes the wave-specialised decode does not cover
+    sh3 = _shape(capacity=4096, page_refs=128, k=3)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.decode_attn(sh3, 32, 4096, _FakePtr(), _pcache(), dec, _pcache(), dec, 0.088,
+                       _FakePtr(), ws)
+    assert e.value.status == 2
+    # calls without a paged path
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.decode_attn_sparse(sh, 32, 4096, _FakePtr(), _pcache(), dec, _pcache(), dec,
+                              _FakePos(64), 0.088, _FakePtr(), ws)
+    assert e.value.status == 2
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.residuals(sh, x, 0, 64, _pcache(), _FakePtr())
+    assert e.value.status == 2
+
+
+def test_paged_compress_workspace_holds_the_staged_rows():
+    # a paged compress stages the unit's references and the range's index
+    # and latent rows ahead of the unit-contiguous call's own workspace
+    for t0, t1 in ((0, 131072), (65536, 69632), (100000, 100001)):
+        pg = dk.compress_workspace_bytes(_shape(capacity=131072, page_refs=256), t0, t1)
+        ct = dk.compress_workspace_bytes(_shape(capacity=131072), t0, t1)
+        R = -(-t1 // 16)
+        nq = (t1 - R) - (t0 - -(-t0 // 16))
+        staged = 8 * (R * 128 * 2 + R * 4 + nq * 4 * 2 + nq * 32 * 2)
+        assert pg >= ct + staged, (t0, t1)
+        assert pg <= ct + staged + 4 * 256 * 8 + 4 * 256, (t0, t1)
