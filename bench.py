@@ -129,6 +129,9 @@ def parse():
                     help="residual rows of the Compressor / Decompressor training leg (0: skip)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit latent leg (layer 0 compressed again, decode timed)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-layout leg (layer 0 compressed again into pages, "
+                         "decode timed beside the contiguous layer 0)")
     ap.add_argument("--sparse-select", type=int, default=4096,
                     help="positions per (sequence, KV head) of the timed sparse decode calls "
                          "(0: skip them)")
@@ -680,6 +683,65 @@ def main():
             f"{2 * lay(sh4) / unc:.3f} of uncompressed")
         del c4, dws4
 
+    # paged layout: layer 0 compressed again into paged caches (pages of 128
+    # references, handed out from a shuffled pool, one block table for K and
+    # V), its compression and decode calls timed beside the same calls on
+    # contiguous caches of layer 0 (same inputs, weights and queries)
+    paged = None
+    if not wl.appends and not a.no_paged and wl.dtype == "bf16":
+        dk = S.dk
+        P = 128
+        shp = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, wl.T,
+                       dk.BF16, 0, P)
+        mp = dk.page_bytes(shp)["max_pages"]
+        n_pages = wl.batch * wl.kv_heads * mp
+        g = torch.Generator().manual_seed(7)
+        tbl = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(
+            wl.batch, wl.kv_heads, mp).cuda()
+        pcs = [dk.PagedCache(shp, n_pages, tbl) for _ in (0, 1)]
+        ccs = [dk.Cache(S.shape) for _ in (0, 1)]
+        pws = dk.workspace(dk.compress_workspace_bytes(shp, 0, wl.T))
+        pg_comp_ms = {}
+        for name, sh_, cs_, ws_ in (("paged", shp, pcs, pws), ("contiguous", S.shape, ccs, S.cws)):
+            e0, e1 = ev(), ev()
+            for rep_ in range(2):   # the first pass warms up
+                e0.record(stream)
+                for st_ in (0, 1):
+                    cs_[st_].reset()
+                    dk.build_refs(sh_, S.x[0][st_], 0, wl.T, cs_[st_])
+                    dk.compress(sh_, S.x[0][st_], 0, wl.T, S.comp[0][st_], cs_[st_], ws_)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            pg_comp_ms[name] = e0.elapsed_time(e1)
+        del pws
+        d0 = S.dec[0]
+        outs = {n_: torch.empty_like(S.out) for n_ in ("paged", "contiguous")}
+        pstarts = {n_: [ev() for _ in range(n_launch)] for n_ in outs}
+        pends = {n_: [ev() for _ in range(n_launch)] for n_ in outs}
+        for rep_ in range(2):
+            for i in range(n_launch):
+                for name, sh_, cs_ in (("paged", shp, pcs), ("contiguous", S.shape, ccs)):
+                    pstarts[name][i].record(stream)
+                    dk.decode_attn(sh_, S.Hq, wl.T, qs[0], cs_[0], d0[0], cs_[1], d0[1],
+                                   S.scale, outs[name], S.dws)
+                    pends[name][i].record(stream)
+            torch.cuda.synchronize()
+        pms = {n_: float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(pstarts[n_], pends[n_])]))
+               for n_ in outs}
+        paged = {"page_refs": P, "positions_per_page": P * wl.stride,
+                 "pages_per_cache": n_pages,
+                 "decode_launch_ms": pms["paged"], "contiguous_decode_launch_ms": pms["contiguous"],
+                 "decode_time_ratio": pms["paged"] / pms["contiguous"],
+                 "compress_ms_layer": pg_comp_ms["paged"],
+                 "contiguous_compress_ms_layer": pg_comp_ms["contiguous"],
+                 "output_bitwise_equal": bool(torch.equal(outs["paged"].view(torch.int32),
+                                                          outs["contiguous"].view(torch.int32)))}
+        log(f"[bench] paged layout: decode {pms['paged']:.4f} ms per layer (contiguous "
+            f"{pms['contiguous']:.4f}), compression {pg_comp_ms['paged']:.2f} ms per layer "
+            f"(contiguous {pg_comp_ms['contiguous']:.2f}), outputs equal: "
+            f"{paged['output_bitwise_equal']}")
+        del pcs, ccs, tbl, outs
+
     # Compressor / Decompressor MSE training on residual rows of layer 0's K
     # cache: the residual call, then timed training steps (fp32 matrix cores)
     training = None
@@ -857,6 +919,7 @@ def main():
         "measured_peaks": peaks,
         "sparse_decode": sparse,
         "q4_latents": q4,
+        "paged": paged,
         "streaming": streaming,
         "training": training,
         "roofline": roof,

@@ -75,6 +75,11 @@ deltakv_status check_shape(const deltakv_shape *sh, dk::Dims *dm) {
             sh->latent_format != DELTAKV_LATENT_DTYPE)
             return fail(DELTAKV_ERR_UNSUPPORTED,
                         "a paged cache needs stride >= 2, bf16 storage and latents in bf16");
+        // token ordinals are split into pages by a multiply-shift that is
+        // exact while (tokens per unit) x (tokens per page) < 2^40
+        if ((double)sh->capacity * (double)pr * (double)(sh->stride - 1) >= 1099511627776.0)
+            return fail(DELTAKV_ERR_UNSUPPORTED,
+                        "paged cache: capacity x page_refs x (stride - 1) must stay below 2^40");
     }
     if (dm) {
         dm->B = sh->batch;
@@ -154,6 +159,9 @@ deltakv_status check_cache(const deltakv_cache *c, const dk::Dims &dm, const cha
         if (c->n_pages < 1 || c->n_pages > INT32_MAX)
             return fail(DELTAKV_ERR_INVALID_ARG, "%s: n_pages %lld not in [1, 2^31)", name,
                         (long long)c->n_pages);
+        // the decode addresses reference rows by 32-bit byte offsets into the pool
+        if ((double)c->n_pages * dm.pr * dm.d * 2.0 > 2147483648.0)
+            return fail(DELTAKV_ERR_UNSUPPORTED, "%s: a reference pool above 2 GiB", name);
         a->tbl = c->block_table;
         a->npages = c->n_pages;
     }

@@ -52,6 +52,7 @@ struct PageMap {
     int32_t lg = 0;                // log2 of the reference rows per page
     int32_t npp = 0;               // compressed-token rows per page
     int32_t npages = 0;            // pool pages: entries are clamped into [0, npages)
+    uint64_t mag = 0;              // t / npp == (t mag) >> 40 for 0 <= t < 2^24
 };
 
 // Pool page behind logical page lp of `unit` (both clamped into range, so a
@@ -67,7 +68,7 @@ __device__ __forceinline__ int64_t pg_ref_row(const PageMap &pm, int64_t unit, i
 }
 // Pool row of token ordinal q of `unit`.
 __device__ __forceinline__ int64_t pg_tok_row(const PageMap &pm, int64_t unit, int64_t q) {
-    const int64_t lp = q / pm.npp;
+    const int64_t lp = (int64_t)(((uint64_t)q * pm.mag) >> 40);
     return pg_page(pm, unit, lp) * pm.npp + (q - lp * pm.npp);
 }
 

@@ -54,6 +54,8 @@ inline PageMap page_map(const Dims &dm, const CacheArgs &c) {
     pm.lg = lg;
     pm.npp = dm.pr * (dm.s - 1);
     pm.npages = (int32_t)c.npages;
+    // ceil(2^40 / npp): exact quotients while t npp < 2^40
+    pm.mag = (((uint64_t)1 << 40) + (uint64_t)pm.npp - 1) / (uint64_t)pm.npp;
     return pm;
 }
 

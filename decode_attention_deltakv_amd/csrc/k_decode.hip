@@ -1579,18 +1579,25 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     const int64_t Nt_u = (SP || cmode) ? (int64_t)scnt[2 * unit] : Nt;
     const int64_t Rt_u = (SP || cmode) ? (int64_t)scnt[2 * unit + 1] : Rt;
     __shared__ int32_t ordl[SP ? kSpTiles * 32 : 1];
-    // paged layout: the unit's block-table row, clamped into the pool
+    // paged layout: the unit's block-table row, clamped into the pool, held
+    // as byte shifts of the reference pool: entry lp is (page - lp) P 2D, so
+    // that reference j lies at byte j 2D + ptab[j / P] of the pool (32-bit
+    // arithmetic: the pool holds at most 2 GiB, so the shifts fit an int32
+    // and the offsets an unsigned one); the page itself is lp + ptab[lp] >>
+    // (log2 P + log2 2D)
+    constexpr int LRB = D == 128 ? 8 : 7;   // log2 of a row's bytes
     __shared__ int32_t ptab[PG ? kMaxPages : 1];
     if constexpr (PG) {
-        for (int i = tid; i < (int)pm.maxp; i += 256) ptab[i] = (int32_t)pg_page(pm, unit, i);
+        for (int i = tid; i < (int)pm.maxp; i += 256)
+            ptab[i] = (int32_t)((pg_page(pm, unit, i) - i) << (pm.lg + LRB));
         __syncthreads();
     }
-    // pool row of reference ordinal j (paged), its unit row otherwise
-    auto ref_row = [&](uint32_t j) -> int64_t {
+    // byte offset of reference row j (paged: in the pool; else in the unit's rows)
+    auto ref_off = [&](uint32_t j) -> uint32_t {
         if constexpr (PG)
-            return ((int64_t)ptab[j >> pm.lg] << pm.lg) | (int64_t)(j & ((1u << pm.lg) - 1u));
+            return j * (uint32_t)(D * 2) + (uint32_t)ptab[j >> pm.lg];
         else
-            return (int64_t)unit * Rcap + j;
+            return j * (uint32_t)(D * 2);
     };
 
     // ---------------- reference tokens ----------------
@@ -1619,8 +1626,8 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
                 const int64_t j = SP ? (int64_t)rord_u[min(j0 + row, je - 1)]
                                      : min(j0 + row, je - 1);
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(PG ? vref + ref_row((uint32_t)j) * D + 8 * sc8
-                                      : vref_u + j * D + 8 * sc8),
+                    (const void *)(PG ? (const char *)vref + (ref_off((uint32_t)j) + 16u * sc8)
+                                      : (const char *)(vref_u + j * D + 8 * sc8)),
                     (__attribute__((address_space(3))) void *)&vbufA[(256 * m + 64 * w) / CH][0],
                     16, 0, 0);
             }
@@ -1747,10 +1754,27 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     // paged layout: logical page of the tile at t0 (its clamped tokens lie in
     // the page of min(t0, tlast)) and the offset, in rows, from a token's
     // ordinal to its pool row
-    auto tile_page = [&](int t0) -> int { return min(t0, tlast) / pm.npp; };
-    auto tok_shift = [&](int t0) -> int64_t {
+    auto tile_page = [&](int t0) -> int {
+        return (int)(((uint64_t)(uint32_t)min(t0, tlast) * pm.mag) >> 40);
+    };
+    auto page_shift = [&](int lp) -> int {   // (pool page) - lp
+        return __builtin_amdgcn_readfirstlane(ptab[lp]) >> (pm.lg + LRB);
+    };
+    // the last page a loader looked up (lp, its pool page lp + dp) and the
+    // row shift from a token's ordinal to its pool row: consecutive tiles
+    // mostly stay in one page, so the table is read when the page changes
+    struct PgMemo {
+        int lp = -1, dp = 0;
+        int64_t sh = 0;
+    };
+    auto tok_shift_memo = [&](PgMemo &m, int t0) -> int64_t {
         const int lp = tile_page(t0);
-        return (int64_t)(__builtin_amdgcn_readfirstlane(ptab[lp]) - lp) * pm.npp;
+        if (lp != m.lp) {
+            m.lp = lp;
+            m.dp = page_shift(lp);
+            m.sh = (int64_t)m.dp * pm.npp;
+        }
+        return m.sh;
     };
 
     if (w < 2) {
@@ -1795,10 +1819,11 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             float kek;
         };
         // rows of token (t0 + 16 src + l16), clamped to a stored token
+        PgMemo kmemo;
         auto kload = [&](int t0, KIn &in) {
             const uint32_t tok = tok_of(t0 + TH * src + l16);
             if constexpr (PG) {
-                const int64_t sh = tok_shift(t0);
+                const int64_t sh = tok_shift_memo(kmemo, t0);
                 in.z = zrow(klat + sh * DC, kq_u, tok);
                 in.ik = *reinterpret_cast<const IdxV *>(at_byte(kidx + sh * KX, tok * (KX * 2)));
                 in.iv = *reinterpret_cast<const IdxV *>(at_byte(vidx + sh * KX, tok * (KX * 2)));
@@ -2025,14 +2050,16 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             __builtin_amdgcn_make_buffer_rsrc((void *)vidx_u, (short)0, (int)(Nt * KX * 2), 0x00020000);
         // (the tile offset goes in the per-lane offset, which the range check
         // covers, not in the scalar offset)
+        PgMemo gmemo, zmemo;
         auto gload = [&](int t0) {
             if constexpr (PG) {
                 // the tile's page as a buffer of its stored rows: offsets
                 // relative to the page start, rows past it (or past the stored
                 // tokens) read 0
-                const int lp = tile_page(t0);
+                (void)tok_shift_memo(gmemo, t0);
+                const int lp = gmemo.lp;
                 const int pstart = lp * pm.npp;
-                const int pp = __builtin_amdgcn_readfirstlane(ptab[lp]);
+                const int pp = lp + gmemo.dp;
                 const int nrec = min(pm.npp, (int)Nt - pstart);
                 const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
                     (void *)(vidx + (int64_t)pp * pm.npp * KX), (short)0, nrec * (KX * 2),
@@ -2065,16 +2092,24 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             for (int m = 0; m < NDMA; ++m) {
                 const uint32_t j = min(gi[m], rlast);
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(PG ? (const char *)vref + ((uint64_t)ref_row(j) * (D * 2) + coff)
+                    (const void *)(PG ? (const char *)vref + gi[m]
                                       : (const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
                     (__attribute__((address_space(3))) void *)&dst[(KX == 4 ? 64 * vj : 0) + RPD * m][0], 16, 0, 0);
+            }
+        };
+        // paged: the loaded index entries become byte offsets of their rows
+        // in the pool, while the wave waits at the barrier after the loads
+        auto gready = [&]() {
+            if constexpr (PG) {
+#pragma unroll
+                for (int m = 0; m < NDMA; ++m) gi[m] = ref_off(min(gi[m], rlast)) + coff;
             }
         };
         auto zload = [&](int t0, bf16x8 (&z)[2]) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const uint32_t tok = tok_of(t0 + 16 * mb + l16);
-                z[mb] = zrow(PG ? vlat + tok_shift(t0) * DC : vlat_u, vq_u, tok);
+                z[mb] = zrow(PG ? vlat + tok_shift_memo(zmemo, t0) * DC : vlat_u, vq_u, tok);
             }
         };
 
@@ -2249,26 +2284,31 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             gload(qa);
             zload(qa, zA);
             wait_vm_all();
+            gready();
             __syncthreads();
             for (int it = 0; it < ntile; it += 2) {
                 gissue(own);
                 zload(qa + (it + 1) * TT, zB);
                 gload(qa + (it + 1) * TT);
-                vtile(it, zA, own);
+                vtile(it, zA, own);   // (waits for the index loads mid-tile)
+                gready();
                 __syncthreads();
                 if (it + 1 >= ntile) break;
                 gissue(own);
                 zload(qa + (it + 2) * TT, zA);
                 gload(qa + (it + 2) * TT);
                 vtile(it + 1, zB, own);
+                gready();
                 __syncthreads();
             }
         } else {
         gload(qa);
+        gready();
         gissue(vbufA);
         zload(qa, zA);
         if (ntile > 1) gload(qa + TT);
         wait_vm_all();
+        if (ntile > 1) gready();
         __syncthreads();
         for (int it = 0; it < ntile; it += 2) {
             if (it + 1 < ntile) {
@@ -2278,6 +2318,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
             vtile(it, zA, vbufA);
             wait_vm_all();
+            if (it + 2 < ntile) gready();
             __syncthreads();
             if (it + 1 >= ntile) break;
             if (it + 2 < ntile) {
@@ -2287,6 +2328,7 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
             vtile(it + 1, zB, vbufB);
             wait_vm_all();
+            if (it + 3 < ntile) gready();
             __syncthreads();
         }
         }

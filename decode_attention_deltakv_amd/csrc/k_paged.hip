@@ -100,7 +100,13 @@ __global__ __launch_bounds__(256) void scatter_tokens_kernel(const uint16_t *__r
     if (i >= nq) return;
     const int64_t row = pg_tok_row(pm, unit, q0 + i);
     const uint16_t *si = sidx + (unit * nq + i) * k;
-    for (int r = 0; r < k; ++r) idx[row * k + r] = si[r];
+    if (k == 4) {
+        *reinterpret_cast<uint2 *>(idx + row * 4) = *reinterpret_cast<const uint2 *>(si);
+    } else if (k == 8) {
+        *reinterpret_cast<uint4 *>(idx + row * 8) = *reinterpret_cast<const uint4 *>(si);
+    } else {
+        for (int r = 0; r < k; ++r) idx[row * k + r] = si[r];
+    }
     const uint4 *sl = reinterpret_cast<const uint4 *>(slat + (unit * nq + i) * dc);
     uint4 *dl = reinterpret_cast<uint4 *>(lat + row * dc);
     for (int c = 0; c < dc / 8; ++c) dl[c] = sl[c];

@@ -161,7 +161,10 @@ typedef struct {
  * The caller owns the pool and the table and assigns pages (e.g. from a free
  * list as sequences grow); the entries covering the positions a call touches
  * must name distinct pages in [0, n_pages) (entries outside that range are
- * clamped into it, so no access leaves the pool).  The K and V caches of a
+ * clamped into it, so no access leaves the pool).  Limits: n_pages * P * d *
+ * 2 <= 2^31 (the reference pool within 2 GiB: the decode addresses it with
+ * 32-bit offsets) and capacity * P * (stride - 1) < 2^40 (UNSUPPORTED
+ * otherwise).  The K and V caches of a
  * decode call must share one block table.  Paged caches are served by
  * deltakv_build_refs, deltakv_compress, deltakv_append (per-cache launches),
  * and the decode calls without a position list (deltakv_decode_attn, _noalloc,

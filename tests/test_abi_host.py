@@ -554,6 +554,10 @@ def test_paged_cache_arguments_checked_before_any_launch():
     with pytest.raises(dk.DeltaKVError) as e:
         dk.residuals(sh, x, 0, 64, _pcache(), _FakePtr())
     assert e.value.status == 2
+    # a reference pool beyond 2 GiB (65536 pages of 128 rows of 256 bytes)
+    with pytest.raises(dk.DeltaKVError) as e:
+        dk.build_refs(sh, x, 0, 16, _pcache(filled=0, n_pages=65537))
+    assert e.value.status == 2 and "2 GiB" in e.value.detail
 
 
 def test_paged_compress_workspace_holds_the_staged_rows():
