@@ -137,7 +137,7 @@ hipError_t launch_select_exact(const Dims &dm, const void *x, int64_t t0, int64_
                                const uint64_t *list, const uint32_t *list_count,
                                int64_t list_cap, void *scratch, size_t scratch_bytes,
                                hipStream_t st, uint32_t *stats = nullptr);
-size_t exact_list_ws_bytes(const Dims &dm, int64_t t1);
+size_t exact_list_ws_bytes(const Dims &dm, int64_t t1, int64_t nitems);
 // exact selection of a few tokens (bf16) with the references split over
 // blocks; workspace of select_split_ws_bytes
 size_t select_split_ws_bytes(const Dims &dm, int64_t t0, int64_t t1);

@@ -554,7 +554,8 @@ size_t compress_ws_bytes(const Dims &dm, int64_t t0, int64_t t1) {
     // fallback list, then the search's split lists, whose space the split
     // exact scan of the fallback list reuses
     return std::max<size_t>(
-        256 + flist + std::max(topk_split_ws_bytes(dm, t1, nq), exact_list_ws_bytes(dm, t1)),
+        256 + flist + std::max(topk_split_ws_bytes(dm, t1, nq),
+                               exact_list_ws_bytes(dm, t1, nq * dm.B * dm.H)),
         select_split_ws_bytes(dm, t0, t1));
 }
 

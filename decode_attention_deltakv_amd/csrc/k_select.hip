@@ -83,7 +83,7 @@ static void split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit) {
 
 // Listed tokens whose exact scan is split over waves; further entries of a
 // fallback list take one block each.
-constexpr int64_t kListSplitCap = 1024;
+constexpr int64_t kListSplitCap = 4096;
 constexpr int kMaxK = 8;
 
 // Reference chunk per wave and wave count per token of the split scan of a
@@ -97,11 +97,13 @@ static void list_split_plan(const Dims &dm, int64_t t1, int *chunk, int *nsplit)
     *nsplit = (int)((rmax + c - 1) / c);
 }
 
-size_t exact_list_ws_bytes(const Dims &dm, int64_t t1) {
+size_t exact_list_ws_bytes(const Dims &dm, int64_t t1, int64_t nitems) {
     // list_split_plan's chunk is at least 64 and at least rmax / 128
     const int64_t rmax = std::max<int64_t>(1, refs_upto(t1, dm.s));
     const int64_t nsplit = std::min<int64_t>((rmax + 63) / 64, 128);
-    return (size_t)kListSplitCap * nsplit * kMaxK * (sizeof(double) + sizeof(int));
+    // (a list holds at most one entry per unit and token of the call)
+    return (size_t)std::min<int64_t>(kListSplitCap, std::max<int64_t>(1, nitems)) * nsplit *
+           kMaxK * (sizeof(double) + sizeof(int));
 }
 
 namespace {
@@ -272,19 +274,19 @@ __global__ __launch_bounds__(256) void select_exact_kernel(
 }
 
 // Exact top-k of listed tokens, one block per token (grid-stride over the
-// list): the kExactThreads threads split the candidate references (bf16: four
-// per thread and pass, so four independent fp64 sums are in flight), each
-// keeps a sorted top-k of its share, and the block merges the lists by k
-// rounds of a lexicographic (distance, ordinal) minimum.  Same arithmetic as
-// the wave-per-token scan; used for the few tokens the matrix-core search
-// could not certify.
-template <typename T, int D>
-__global__ __launch_bounds__(kExactThreads) void select_exact_block_kernel(
+// list): the NT threads split the candidate references (bf16: four per
+// thread and pass, so four independent fp64 sums are in flight), each keeps
+// a sorted top-k of its share, and the block merges the lists by k rounds of
+// a lexicographic (distance, ordinal) minimum.  Same arithmetic as the
+// wave-per-token scan (the result does not depend on NT); used for the few
+// tokens the matrix-core search could not certify.
+template <typename T, int D, int NT = kExactThreads>
+__global__ __launch_bounds__(NT) void select_exact_block_kernel(
     const T *__restrict__ x, int64_t t0, int64_t nrows, int s, const T *__restrict__ refs,
     int64_t Rcap, int64_t Ncap, int64_t q0, int k, uint16_t *__restrict__ idx,
     const uint64_t *__restrict__ list, const uint32_t *__restrict__ list_count, int64_t nunits,
     int64_t nq, int64_t first) {
-    constexpr int NT = kExactThreads, NW = NT / 64;
+    constexpr int NW = NT / 64;
     __shared__ double xs[D];
     __shared__ double wd[NW];
     __shared__ int wj[NW];
@@ -783,9 +785,13 @@ hipError_t launch_exact_t(const Dims &dm, const void *x, int64_t t0, int64_t t1,
         }
         if (stats) hipLaunchKernelGGL(add_stats_kernel, dim3(1), dim3(64), 0, st, list_count, stats);
         if (first < list_cap) {
+            // entries past the split scan's share (rarely any): blocks of 256
+            // threads, which find room on a CU that other streams' kernels
+            // share (a 1024-thread block can wait long for one, and the
+            // stream's later kernels with it)
             const unsigned g =
-                (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap - first, 64));
-            hipLaunchKernelGGL((select_exact_block_kernel<T, D>), dim3(g), dim3(kExactThreads), 0,
+                (unsigned)std::max<int64_t>(1, std::min<int64_t>(list_cap - first, 256));
+            hipLaunchKernelGGL((select_exact_block_kernel<T, D, 256>), dim3(g), dim3(256), 0,
                                st, (const T *)x, t0, t1 - t0, dm.s, (const T *)c.refs, dm.R, dm.N,
                                q0, dm.k, c.idx, list, list_count, (int64_t)dm.B * dm.H, nq, first);
         }
@@ -1737,7 +1743,8 @@ hipError_t launch_select_mfma(const Dims &dm, const void *x, int64_t t0, int64_t
     // the split lists of the search are consumed: their space holds the
     // partial lists of the split exact scan
     e = launch_select_exact(dm, x, t0, t1, q0, nq, c, flist, fcount, (int64_t)nq * dm.B * dm.H,
-                            tail, exact_list_ws_bytes(dm, t1), st, stats);
+                            tail, exact_list_ws_bytes(dm, t1, (int64_t)nq * dm.B * dm.H), st,
+                            stats);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
