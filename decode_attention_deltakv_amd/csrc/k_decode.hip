@@ -1587,6 +1587,12 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     // (log2 P + log2 2D)
     constexpr int LRB = D == 128 ? 8 : 7;   // log2 of a row's bytes
     __shared__ int32_t ptab[PG ? kMaxPages : 1];
+    // paged, k = 4: the score waves, which read every token's V index entries
+    // a tile ahead anyway, turn them into the pool offsets of the V rows (one
+    // entry per lane) for the value waves' gathers of that tile (two slots:
+    // tile i + 1 is written while the value waves gather tile i)
+    constexpr bool PGS = PG && KX == 4;
+    __shared__ uint32_t voff[PGS ? 2 : 1][PGS ? 32 * KX : 1];
     if constexpr (PG) {
         for (int i = tid; i < (int)pm.maxp; i += 256)
             ptab[i] = (int32_t)((pg_page(pm, unit, i) - i) << (pm.lg + LRB));
@@ -1751,6 +1757,9 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     auto tok_of = [&](int i) -> uint32_t {
         return SP ? (uint32_t)ordl[min(i, qe - 1) - qa] : (uint32_t)min(i, tlast);
     };
+    // the last reference row a gathered row may name (counts mode: the unit's
+    // own last reference, rows past a sequence's length are not its data)
+    const uint32_t rlast_u = (uint32_t)(cmode ? Rt_u : Rt) - 1u;
     // paged layout: logical page of the tile at t0 (its clamped tokens lie in
     // the page of min(t0, tlast)) and the offset, in rows, from a token's
     // ordinal to its pool row
@@ -1861,6 +1870,12 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             const int sl = it & 1;
             if constexpr (QPRE) qload(n1);
             else qload(in);
+            if constexpr (PGS) {
+                // V rows of tile it + 1: slot lq of token l16 of this wave
+                const uint32_t wv = n1.iv[lq >> 1];
+                const uint32_t j = min((lq & 1) ? (wv >> 16) : (wv & 0xffffu), rlast_u);
+                voff[(it + 1) & 1][(TH * src + l16) * KX + lq] = ref_off(j);
+            }
             kload(t2, n2);
             // hidden tile and partial scores, 32 hidden units per step; the
             // products of step j + 1 are issued before the GELU of step j, and
@@ -2087,12 +2102,17 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         };
         // unused slots (0xFFFF) and rows past the stored range read the last
         // stored reference row: finite data under a zero weight
-        auto gissue = [&](bf16_t (*dst)[D]) {
+        // (paged: gi holds pool offsets for tile 0, and the score waves'
+        // offsets in voff serve later tiles at k = 4)
+        auto gissue = [&](bf16_t (*dst)[D], int tile) {
 #pragma unroll
             for (int m = 0; m < NDMA; ++m) {
                 const uint32_t j = min(gi[m], rlast);
+                uint32_t pof = gi[m];
+                if constexpr (PGS)
+                    if (tile > 0) pof = voff[tile & 1][64 * vj + RPD * m + lrow] + coff;
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(PG ? (const char *)vref + gi[m]
+                    (const void *)(PG ? (const char *)vref + pof
                                       : (const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
                     (__attribute__((address_space(3))) void *)&dst[(KX == 4 ? 64 * vj : 0) + RPD * m][0], 16, 0, 0);
             }
@@ -2287,14 +2307,14 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             gready();
             __syncthreads();
             for (int it = 0; it < ntile; it += 2) {
-                gissue(own);
+                gissue(own, 0);
                 zload(qa + (it + 1) * TT, zB);
                 gload(qa + (it + 1) * TT);
                 vtile(it, zA, own);   // (waits for the index loads mid-tile)
                 gready();
                 __syncthreads();
                 if (it + 1 >= ntile) break;
-                gissue(own);
+                gissue(own, 0);
                 zload(qa + (it + 2) * TT, zA);
                 gload(qa + (it + 2) * TT);
                 vtile(it + 1, zB, own);
@@ -2304,31 +2324,31 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         } else {
         gload(qa);
         gready();
-        gissue(vbufA);
+        gissue(vbufA, 0);
         zload(qa, zA);
-        if (ntile > 1) gload(qa + TT);
+        if (!PGS && ntile > 1) gload(qa + TT);
         wait_vm_all();
-        if (ntile > 1) gready();
+        if (!PGS && ntile > 1) gready();
         __syncthreads();
         for (int it = 0; it < ntile; it += 2) {
             if (it + 1 < ntile) {
-                gissue(vbufB);
+                gissue(vbufB, it + 1);
                 zload(qa + (it + 1) * TT, zB);
-                if (it + 2 < ntile) gload(qa + (it + 2) * TT);
+                if (!PGS && it + 2 < ntile) gload(qa + (it + 2) * TT);
             }
             vtile(it, zA, vbufA);
             wait_vm_all();
-            if (it + 2 < ntile) gready();
+            if (!PGS && it + 2 < ntile) gready();
             __syncthreads();
             if (it + 1 >= ntile) break;
             if (it + 2 < ntile) {
-                gissue(vbufA);
+                gissue(vbufA, it + 2);
                 zload(qa + (it + 2) * TT, zA);
-                if (it + 3 < ntile) gload(qa + (it + 3) * TT);
+                if (!PGS && it + 3 < ntile) gload(qa + (it + 3) * TT);
             }
             vtile(it + 1, zB, vbufB);
             wait_vm_all();
-            if (it + 3 < ntile) gready();
+            if (!PGS && it + 3 < ntile) gready();
             __syncthreads();
         }
         }

@@ -264,3 +264,55 @@ def test_paged_units_of_different_lengths_share_one_pool():
         outs.append(out)
     _same_bits(outs[0], outs[1], "mixed-length paged decode")
     assert torch.isfinite(outs[0]).all()
+
+
+def test_paged_llama_layer_128k_equals_contiguous():
+    # one layer of the Llama-3.1-8B-shaped 128k workload at full size, in the
+    # launch configuration the benchmark times (one compress call per stream,
+    # one decode call), into paged caches (pages of 128 references = 2048
+    # positions, shuffled over the pool) and into contiguous ones: the stored
+    # rows read back through the table and the decode output equal bit for bit
+    # (the contiguous layer is checked against the oracle in test_gpu_parity)
+    from deltakv_synth import WORKLOADS, kv_rows, unit_key, workload_index, xavier_mlp
+    w = WORKLOADS["llama8b-32layer-T128k-bf16"]
+    widx = workload_index(w.name)
+    B, H, G, T, d, s = 1, w.kv_heads, w.q_heads // w.kv_heads, w.T, w.head_dim, w.stride
+    cshape = dk.Shape(B, H, d, s, w.k, w.d_c, T, dk.BF16)
+    pshape = dk.Shape(B, H, d, s, w.k, w.d_c, T, dk.BF16, 0, 128)
+    tbl, n_pages = _table(pshape, 77)
+    say(f"[case] paged llama8b-T128k one layer: {n_pages} pages per cache")
+    cc, pc = [], []
+    for st in (0, 1):
+        x = torch.stack([kv_rows(T, d, w.n_dirs, w.n_centroids, key=unit_key(widx, 0, 0, h, st),
+                                 dtype=torch.bfloat16, device="cuda") for h in range(H)])[None]
+        comp = gpu_mlp(xavier_mlp(d, w.hidden, w.d_c, key=(1, widx, 0, st),
+                                  dtype=torch.bfloat16), dk.ACT_GELU)
+        for sh, cache, out in ((cshape, dk.Cache(cshape), cc),
+                               (pshape, dk.PagedCache(pshape, n_pages, tbl), pc)):
+            dk.build_refs(sh, x, 0, T, cache)
+            dk.compress(sh, x, 0, T, comp, cache,
+                        dk.workspace(dk.compress_workspace_bytes(sh, 0, T)))
+            out.append(cache)
+        torch.cuda.synchronize()
+        del x
+    R, N = oracle.num_refs(T, s), T - oracle.num_refs(T, s)
+    for name, c, p in zip(("K", "V"), cc, pc):
+        refs, sqn, lat, idx = _logical(p, pshape, R, N)
+        _same_bits(refs, c.refs, f"{name} reference rows")
+        _same_bits(sqn, c.ref_sqnorm, f"{name} squared norms")
+        _same_bits(idx, c.idx, f"{name} index lists")
+        _same_bits(lat, c.latents, f"{name} latents")
+    kd = gpu_mlp(xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 0), dtype=torch.bfloat16),
+                 dk.ACT_GELU)
+    vd = gpu_mlp(xavier_mlp(w.d_c, w.hidden, d, key=(2, widx, 0, 1), dtype=torch.bfloat16),
+                 dk.ACT_GELU)
+    q = queries(H * G, d, key=(3, widx), dtype=torch.bfloat16).reshape(B, H * G, d).cuda()
+    outs = []
+    for sh, caches in ((cshape, cc), (pshape, pc)):
+        out = torch.full((B, H * G, d), float("nan"), device="cuda")
+        dk.decode_attn(sh, H * G, T, q, caches[0], kd, caches[1], vd, 1.0 / math.sqrt(d), out,
+                       dk.workspace(dk.decode_workspace_bytes(sh, H * G, T)))
+        torch.cuda.synchronize()
+        outs.append(out)
+    _same_bits(outs[1], outs[0], "128k paged decode output")
+    say("[case] paged llama8b-T128k: arrays and decode output bitwise equal")
