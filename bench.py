@@ -47,8 +47,8 @@ VALU_PEAK_GINSTR = 256 * 4 * 2.4 / 4
 # any change the dependent figures are reported as null until measured again.
 DECODE_COUNTERS = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "f356a4ffefb2",
-    "fetch_kib": {"main_ws": 86364.4, "prep": 8543.1, "combine2": 2393.0},
+    "source_sha256": "fd2fe00d6d25",
+    "fetch_kib": {"main_ws": 86367.3, "prep": 8549.2, "combine2": 2394.5},
     "write_kib": {"main_ws": 3880.3, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
@@ -122,9 +122,10 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode steps per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--compress-streams", type=int, default=4,
+    ap.add_argument("--compress-streams", type=int, default=None,
                     help="streams the prompt compression's independent per-cache calls are "
-                         "spread over (1 to 4)")
+                         "spread over (1 to 4; default 4, or 1 when one call covers 64 units "
+                         "or more and fills the GPU by itself: measured 1-3%% either way)")
     ap.add_argument("--train-rows", type=int, default=65536,
                     help="residual rows of the Compressor / Decompressor training leg (0: skip)")
     ap.add_argument("--no-q4", action="store_true",
@@ -481,7 +482,9 @@ def main():
     if wl.appends:
         dsteps = min(dsteps, wl.appends)   # each streaming decode step appends a token
     torch.cuda.set_device(0)
-    S = Setup(wl, widx, a.compress_streams)
+    streams = a.compress_streams if a.compress_streams is not None else \
+        (1 if wl.batch * wl.kv_heads >= 64 and not wl.chunk else 4)
+    S = Setup(wl, widx, streams)
     stream = torch.cuda.current_stream()
     if a.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
