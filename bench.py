@@ -693,19 +693,21 @@ def main():
     paged = None
     if not wl.appends and not a.no_paged and wl.dtype == "bf16":
         dk = S.dk
-        P = 128
-        shp = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, wl.T,
+        P, n_app = 128, 16
+        cap = wl.T + n_app   # room for the appends timed below
+        shp = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, cap,
                        dk.BF16, 0, P)
+        shc = dk.Shape(wl.batch, wl.kv_heads, wl.head_dim, wl.stride, wl.k, wl.d_c, cap, dk.BF16)
         mp = dk.page_bytes(shp)["max_pages"]
         n_pages = wl.batch * wl.kv_heads * mp
         g = torch.Generator().manual_seed(7)
         tbl = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(
             wl.batch, wl.kv_heads, mp).cuda()
         pcs = [dk.PagedCache(shp, n_pages, tbl) for _ in (0, 1)]
-        ccs = [dk.Cache(S.shape) for _ in (0, 1)]
+        ccs = [dk.Cache(shc) for _ in (0, 1)]
         pws = dk.workspace(dk.compress_workspace_bytes(shp, 0, wl.T))
         pg_comp_ms = {}
-        for name, sh_, cs_, ws_ in (("paged", shp, pcs, pws), ("contiguous", S.shape, ccs, S.cws)):
+        for name, sh_, cs_, ws_ in (("paged", shp, pcs, pws), ("contiguous", shc, ccs, S.cws)):
             e0, e1 = ev(), ev()
             for rep_ in range(2):   # the first pass warms up
                 e0.record(stream)
@@ -717,13 +719,32 @@ def main():
                 torch.cuda.synchronize()
             pg_comp_ms[name] = e0.elapsed_time(e1)
         del pws
+        # one-token appends to both caches of the layer (one deltakv_append
+        # call per position; layer 0's last rows stand in for new tokens)
+        xa = [[S.x[0][st_][:, :, wl.T - n_app + i:wl.T - n_app + i + 1].contiguous()
+               for st_ in (0, 1)] for i in range(n_app)]
+        pg_app_ms = {}
+        for name, sh_, cs_ in (("paged", shp, pcs), ("contiguous", shc, ccs)):
+            batch = dk.AppendBatch(sh_, cs_, [S.comp[0][0], S.comp[0][1]])
+            aws = dk.workspace(dk.append_workspace_bytes(sh_, cap - 1, 2))
+            for rep_ in range(2):
+                for c_ in cs_:
+                    c_.n_built = c_.n_compressed = wl.T
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for i in range(n_app):
+                    batch(wl.T + i, xa[i], aws)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            pg_app_ms[name] = e0.elapsed_time(e1) / n_app
+            del aws
         d0 = S.dec[0]
         outs = {n_: torch.empty_like(S.out) for n_ in ("paged", "contiguous")}
         pstarts = {n_: [ev() for _ in range(n_launch)] for n_ in outs}
         pends = {n_: [ev() for _ in range(n_launch)] for n_ in outs}
         for rep_ in range(2):
             for i in range(n_launch):
-                for name, sh_, cs_ in (("paged", shp, pcs), ("contiguous", S.shape, ccs)):
+                for name, sh_, cs_ in (("paged", shp, pcs), ("contiguous", shc, ccs)):
                     pstarts[name][i].record(stream)
                     dk.decode_attn(sh_, S.Hq, wl.T, qs[0], cs_[0], d0[0], cs_[1], d0[1],
                                    S.scale, outs[name], S.dws)
@@ -737,11 +758,14 @@ def main():
                  "decode_time_ratio": pms["paged"] / pms["contiguous"],
                  "compress_ms_layer": pg_comp_ms["paged"],
                  "contiguous_compress_ms_layer": pg_comp_ms["contiguous"],
+                 "append_ms_per_token_layer": pg_app_ms["paged"],
+                 "contiguous_append_ms_per_token_layer": pg_app_ms["contiguous"],
                  "output_bitwise_equal": bool(torch.equal(outs["paged"].view(torch.int32),
                                                           outs["contiguous"].view(torch.int32)))}
         log(f"[bench] paged layout: decode {pms['paged']:.4f} ms per layer (contiguous "
             f"{pms['contiguous']:.4f}), compression {pg_comp_ms['paged']:.2f} ms per layer "
-            f"(contiguous {pg_comp_ms['contiguous']:.2f}), outputs equal: "
+            f"(contiguous {pg_comp_ms['contiguous']:.2f}), append {pg_app_ms['paged']:.4f} ms "
+            f"per token and layer (contiguous {pg_app_ms['contiguous']:.4f}), outputs equal: "
             f"{paged['output_bitwise_equal']}")
         del pcs, ccs, tbl, outs
 

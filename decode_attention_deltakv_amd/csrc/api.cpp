@@ -461,7 +461,7 @@ deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_i
                  (!dm.pr || items[j].cache->block_table == it.cache->block_table)))
                 return fail(DELTAKV_ERR_INVALID_ARG, "items %d and %d name the same cache", j,
                             i);
-        batched = batched && !dm.pr && dk::append_batched_supported(dm, ma[i]) &&
+        batched = batched && dk::append_batched_supported(dm, ma[i]) &&
                   ma[i].hidden == ma[0].hidden && ma[i].act == ma[0].act;
     }
     const size_t need = dk::append_ws_bytes(dm, t, n_items);
@@ -488,6 +488,8 @@ deltakv_status deltakv_append(const deltakv_shape *shape, int64_t t, int32_t n_i
                 set.b1[i] = ma[j].b1;
                 set.w2[i] = ma[j].w2;
                 set.b2[i] = ma[j].b2;
+                set.tbl[i] = ca[j].tbl;
+                set.npages[i] = (int32_t)ca[j].npages;
             }
             if (is_ref) {
                 e = dk::launch_append_refs(dm, t, n, set, hs);

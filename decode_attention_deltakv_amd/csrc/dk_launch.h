@@ -173,7 +173,18 @@ struct AppendSet {
     const float *b1[kAppendMax];
     const void *w2[kAppendMax];
     const float *b2[kAppendMax];
+    // paged caches: each cache's block table and pool size (the page geometry,
+    // common to the set, travels in a PageMap beside the set)
+    const int32_t *tbl[kAppendMax];
+    int32_t npages[kAppendMax];
 };
+// the page map of cache `item` of a set (pg: the set's common page geometry)
+__host__ __device__ inline PageMap item_pages(const PageMap &pg, const AppendSet &set, int item) {
+    PageMap pm = pg;
+    pm.tbl = set.tbl[item];
+    pm.npages = set.npages[item];
+    return pm;
+}
 // the batched kernels serve bf16 caches with the matrix-core Compressor's
 // shapes; other shapes run the per-cache calls
 bool append_batched_supported(const Dims &dm, const MlpArgs &comp);
@@ -181,6 +192,12 @@ size_t append_ws_bytes(const Dims &dm, int64_t t, int n);
 size_t append_select_ws_bytes(const Dims &dm, int64_t t, int n);
 hipError_t launch_append_refs(const Dims &dm, int64_t t, int n, const AppendSet &set,
                               hipStream_t st);
+// the set's common page geometry (dm.pr != 0), tables left to the items
+inline PageMap set_pages(const Dims &dm) {
+    if (!dm.pr) return PageMap{};
+    CacheArgs none{};
+    return page_map(dm, none);
+}
 hipError_t launch_append_select(const Dims &dm, int64_t t, int n, const AppendSet &set, void *ws,
                                 hipStream_t st);
 hipError_t launch_append_compress(const Dims &dm, int64_t t, int n, const AppendSet &set,

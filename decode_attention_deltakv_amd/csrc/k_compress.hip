@@ -93,14 +93,17 @@ __global__ __launch_bounds__(256) void compress_mlp_kernel(
 // with a per-row bf16 shift and scale (d_c / 4 lanes per row quantise it).
 // The body of one block (bidx: the block's index over units x tile groups),
 // shared by the kernel over a range of one cache and the batched-append kernel
-// over one token of several caches, so both compute the same bits.
-template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
+// over one token of several caches, so both compute the same bits.  PG: a
+// paged cache (appends only: the range [q0, q0 + nq) lies in one page), whose
+// index and latent rows are found through pm once and whose reference rows are
+// looked up by ordinal.
+template <int D, int HID, int DC, int KX, bool GELU, bool Q4, bool PG = false>
 __device__ __forceinline__ void compress_mfma_body(
     int bidx, const bf16_t *__restrict__ x, int64_t t0, int64_t nrows, int s, int k,
     const bf16_t *__restrict__ refs, int64_t Rcap, const uint16_t *__restrict__ idx,
     int64_t Ncap, int64_t q0, int64_t nq, int U, int tiles_per_block,
     const bf16_t *__restrict__ w1, const float *__restrict__ b1, const bf16_t *__restrict__ w2,
-    const float *__restrict__ b2, bf16_t *__restrict__ lat) {
+    const float *__restrict__ b2, bf16_t *__restrict__ lat, PageMap pm = PageMap{}) {
     constexpr int TT = 32;
     constexpr int HW = HID / 4;
     constexpr int MT = HW / 16;
@@ -119,9 +122,13 @@ __device__ __forceinline__ void compress_mfma_body(
     const int blk = bidx / U;
     const int hb = w * HW;
     const int64_t qend = q0 + nq;
+    static_assert(!(PG && Q4), "paged caches hold bf16 latents");
     const bf16_t *urefs = refs + (int64_t)unit * Rcap * D;
     const bf16_t *ux = x + (int64_t)unit * nrows * D;
-    const uint16_t *uidx = idx + (int64_t)unit * Ncap * k;
+    // (paged: the offset, in rows, from token ordinal q to its pool row in the
+    // page that holds the range)
+    const int64_t tsh = PG ? pg_tok_row(pm, unit, q0) - q0 : 0;
+    const uint16_t *uidx = PG ? idx + tsh * k : idx + (int64_t)unit * Ncap * k;
 
     bf16x8 a1[MT][KSD];
     f32x4 bias1[MT];
@@ -184,8 +191,9 @@ __device__ __forceinline__ void compress_mfma_body(
     const __amdgpu_buffer_rsrc_t lat_rsrc =
         Q4 ? __builtin_amdgcn_make_buffer_rsrc((void *)lat_q4, (short)0, (int)(qend * (DC / 2)),
                                                0x00020000)
-           : __builtin_amdgcn_make_buffer_rsrc((void *)(lat + (int64_t)unit * Ncap * DC),
-                                               (short)0, (int)(qend * DC * 2), 0x00020000);
+           : __builtin_amdgcn_make_buffer_rsrc(
+                 (void *)(PG ? lat + tsh * DC : lat + (int64_t)unit * Ncap * DC), (short)0,
+                 (int)(qend * DC * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t par_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(lat_q4 + Ncap * (DC / 2)), (short)0, (int)(qend * 4), 0x00020000);
     // Q4: b2 of the four latent columns this thread quantises
@@ -231,9 +239,15 @@ __device__ __forceinline__ void compress_mfma_body(
             for (int r = 0; r < KX; ++r) {
                 const bool used = r < k && jn[m][r] != kIdxUnused;
                 keff += used ? 1 : 0;
-                const uint32_t off = used ? (jn[m][r] * D + 8u * c8) * 2u : 0x80000000u;
-                rv[m][r] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(ref_rsrc, off, 0, 0));
+                if constexpr (PG) {
+                    const int64_t row = pg_ref_row(pm, unit, used ? jn[m][r] : 0u);
+                    const u32x4 v = ld16(refs + row * D + 8 * c8);
+                    rv[m][r] = used ? v : u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    const uint32_t off = used ? (jn[m][r] * D + 8u * c8) * 2u : 0x80000000u;
+                    rv[m][r] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ref_rsrc, off, 0, 0));
+                }
             }
             // 1 / k_eff (exact for 1, 2, 4, 8; within an ulp otherwise,
             // far below the bf16 rounding of the residual)
@@ -411,15 +425,17 @@ __global__ __launch_bounds__(256, 2) void compress_mfma_kernel(
 
 // Batched appends: the one token t (ordinal q) of every unit of cache
 // blockIdx.y of the set.  grid (U, n).
-template <int D, int HID, int DC, int KX, bool GELU, bool Q4>
+template <int D, int HID, int DC, int KX, bool GELU, bool Q4, bool PG = false>
 __global__ __launch_bounds__(256, 2) void compress_append_kernel(AppendSet set, int64_t t, int s,
                                                                  int k, int64_t Rcap,
-                                                                 int64_t Ncap, int64_t q, int U) {
+                                                                 int64_t Ncap, int64_t q, int U,
+                                                                 PageMap pg) {
     const int item = blockIdx.y;
-    compress_mfma_body<D, HID, DC, KX, GELU, Q4>(
+    compress_mfma_body<D, HID, DC, KX, GELU, Q4, PG>(
         blockIdx.x, (const bf16_t *)set.x[item], t, 1, s, k, (const bf16_t *)set.refs[item],
         Rcap, set.idx[item], Ncap, q, 1, U, 1, (const bf16_t *)set.w1[item], set.b1[item],
-        (const bf16_t *)set.w2[item], set.b2[item], (bf16_t *)set.lat[item]);
+        (const bf16_t *)set.w2[item], set.b2[item], (bf16_t *)set.lat[item],
+        PG ? item_pages(pg, set, item) : PageMap{});
 }
 
 template <int D, int HID, int DC>
@@ -438,8 +454,14 @@ void launch_cappend_t(const Dims &dm, int64_t t, int n, const AppendSet &set, in
                              : (act == 0 ? compress_append_kernel<D, HID, DC, 8, true, true>
                                          : compress_append_kernel<D, HID, DC, 8, false, true>);
     }
+    if (dm.pr)
+        kern = dm.k <= 4
+                   ? (act == 0 ? compress_append_kernel<D, HID, DC, 4, true, false, true>
+                               : compress_append_kernel<D, HID, DC, 4, false, false, true>)
+                   : (act == 0 ? compress_append_kernel<D, HID, DC, 8, true, false, true>
+                               : compress_append_kernel<D, HID, DC, 8, false, false, true>);
     hipLaunchKernelGGL(kern, dim3((unsigned)U, (unsigned)n), dim3(256), 0, st, set, t, dm.s, dm.k,
-                       dm.R, dm.N, q, U);
+                       dm.R, dm.N, q, U, set_pages(dm));
 }
 
 template <int D, int HID>

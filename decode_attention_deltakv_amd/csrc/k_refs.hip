@@ -46,16 +46,19 @@ __global__ __launch_bounds__(256) void build_refs_kernel(const T *__restrict__ x
 // Batched appends at a reference position t: the row of every unit of every
 // cache of the set becomes reference t / s.  One wave per (unit, cache):
 // grid (ceil(U / 4), n).
+// (paged caches, pg.npp != 0: the row goes to its pool page)
 __global__ __launch_bounds__(256) void append_refs_kernel(AppendSet set, int64_t t, int s, int d,
-                                                          int64_t Rcap, int U) {
+                                                          int64_t Rcap, int U, PageMap pg) {
     const int lane = threadIdx.x & 63;
     const int unit = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= U) return;
     const int item = blockIdx.y;
     const int64_t j = t / s;
+    const int64_t row = pg.npp ? pg_ref_row(item_pages(pg, set, item), unit, j)
+                               : (int64_t)unit * Rcap + j;
     const bf16_t *x = (const bf16_t *)set.x[item];
-    copy_ref_row<bf16_t>(x + (int64_t)unit * d, (bf16_t *)set.refs[item] + (unit * Rcap + j) * d,
-                         set.sqn[item] + unit * Rcap + j, d, lane);
+    copy_ref_row<bf16_t>(x + (int64_t)unit * d, (bf16_t *)set.refs[item] + row * d,
+                         set.sqn[item] + row, d, lane);
 }
 
 }  // namespace
@@ -64,7 +67,7 @@ hipError_t launch_append_refs(const Dims &dm, int64_t t, int n, const AppendSet 
                               hipStream_t st) {
     const int U = dm.B * dm.H;
     hipLaunchKernelGGL(append_refs_kernel, dim3((unsigned)((U + 3) / 4), (unsigned)n), dim3(256),
-                       0, st, set, t, dm.s, dm.d, dm.R, U);
+                       0, st, set, t, dm.s, dm.d, dm.R, U, set_pages(dm));
     return hipGetLastError();
 }
 

@@ -388,8 +388,10 @@ __global__ __launch_bounds__(NT) void select_exact_block_kernel(
 // above), then kMaxK rounds of a block-wide lexicographic minimum write the
 // merged list to od / oj (unused slots: +inf, INT_MAX).  Every thread of the
 // block must call it; xs, wd and wj are the block's LDS scratch.
-template <typename T, int D>
-__device__ __forceinline__ void block_range_topk(const T *__restrict__ xrow, const T *__restrict__ ubase,
+// (rows: reference ordinal -> its row, e.g. ubase + j D, or a pool row of a
+// paged cache)
+template <typename T, int D, typename Rows>
+__device__ __forceinline__ void block_range_topk(const T *__restrict__ xrow, Rows rows,
                                  int64_t ja, int64_t jb, double *xs, double *wd, int *wj,
                                  double *__restrict__ od, int *__restrict__ oj) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -404,7 +406,7 @@ __device__ __forceinline__ void block_range_topk(const T *__restrict__ xrow, con
         bj[i] = INT_MAX;
     }
     for (int64_t j = ja + tid; j < jb; j += 256) {
-        double cd = exact_sq_dist<T, D>(xs, ubase + j * D);
+        double cd = exact_sq_dist<T, D>(xs, rows(j));
         int cj = (int)j;
         if (!(cd < bd[kMaxK - 1] || (cd == bd[kMaxK - 1] && cj < bj[kMaxK - 1]))) continue;
 #pragma unroll
@@ -545,7 +547,9 @@ __global__ __launch_bounds__(256) void select_split_kernel(
     const int64_t ncand = (p + s - 1) / s;
     const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
     const size_t o = (size_t)(item * gridDim.x + blockIdx.x) * kMaxK;
-    block_range_topk<T, D>(x + (unit * nrows + (p - t0)) * D, refs + unit * Rcap * D, ja, jb, xs,
+    const T *ubase = refs + unit * Rcap * D;
+    block_range_topk<T, D>(x + (unit * nrows + (p - t0)) * D,
+                           [=](int64_t j) { return ubase + j * D; }, ja, jb, xs,
                            wd, wj, pd + o, pj + o);
 }
 
@@ -570,7 +574,7 @@ template <int D>
 __global__ __launch_bounds__(256) void append_split_kernel(AppendSet set, int64_t t, int s,
                                                            int64_t Rcap, int chunk,
                                                            double *__restrict__ pd,
-                                                           int *__restrict__ pj) {
+                                                           int *__restrict__ pj, PageMap pg) {
     __shared__ double xs[D];
     __shared__ double wd[4];
     __shared__ int wj[4];
@@ -579,9 +583,18 @@ __global__ __launch_bounds__(256) void append_split_kernel(AppendSet set, int64_
     const int64_t ncand = (t + s - 1) / s;
     const int64_t ja = (int64_t)blockIdx.x * chunk, jb = min(ncand, ja + (int64_t)chunk);
     const size_t o = (size_t)(((int64_t)item * U + unit) * gridDim.x + blockIdx.x) * kMaxK;
-    block_range_topk<bf16_t, D>((const bf16_t *)set.x[item] + unit * D,
-                                (const bf16_t *)set.refs[item] + unit * Rcap * D, ja, jb, xs, wd,
-                                wj, pd + o, pj + o);
+    const bf16_t *rb = (const bf16_t *)set.refs[item];
+    if (pg.npp) {   // paged: each reference row found through the cache's table
+        const PageMap pm = item_pages(pg, set, item);
+        block_range_topk<bf16_t, D>((const bf16_t *)set.x[item] + unit * D,
+                                    [=](int64_t j) { return rb + pg_ref_row(pm, unit, j) * D; },
+                                    ja, jb, xs, wd, wj, pd + o, pj + o);
+    } else {
+        const bf16_t *ub = rb + unit * Rcap * D;
+        block_range_topk<bf16_t, D>((const bf16_t *)set.x[item] + unit * D,
+                                    [=](int64_t j) { return ub + j * D; }, ja, jb, xs, wd, wj,
+                                    pd + o, pj + o);
+    }
 }
 
 // The k best over the split lists of one (unit, cache), one wave each:
@@ -589,11 +602,12 @@ __global__ __launch_bounds__(256) void append_split_kernel(AppendSet set, int64_
 __global__ __launch_bounds__(64) void append_merge_kernel(AppendSet set, int nsplit, int k,
                                                           int64_t q, int64_t Ncap,
                                                           const double *__restrict__ pd,
-                                                          const int *__restrict__ pj) {
+                                                          const int *__restrict__ pj, PageMap pg) {
     const int item = blockIdx.y, U = gridDim.x;
     const int64_t unit = blockIdx.x;
     const int64_t o = ((int64_t)item * U + unit) * nsplit * kMaxK;
-    wave_merge_lists(nsplit, k, pd + o, pj + o, set.idx[item] + (unit * Ncap + q) * k);
+    const int64_t row = pg.npp ? pg_tok_row(item_pages(pg, set, item), unit, q) : unit * Ncap + q;
+    wave_merge_lists(nsplit, k, pd + o, pj + o, set.idx[item] + row * k);
 }
 
 // Squared distance of one bf16 reference row (already loaded, u) from the
@@ -1669,15 +1683,16 @@ hipError_t launch_append_select(const Dims &dm, int64_t t, int n, const AppendSe
     double *pd = (double *)ws;
     int *pj = (int *)((char *)ws + m * sizeof(double));
     const dim3 grid((unsigned)nsplit, (unsigned)U, (unsigned)n);
+    const PageMap pg = set_pages(dm);
     if (dm.d == 128)
         hipLaunchKernelGGL(append_split_kernel<128>, grid, dim3(256), 0, st, set, t, dm.s, dm.R,
-                           chunk, pd, pj);
+                           chunk, pd, pj, pg);
     else
         hipLaunchKernelGGL(append_split_kernel<64>, grid, dim3(256), 0, st, set, t, dm.s, dm.R,
-                           chunk, pd, pj);
+                           chunk, pd, pj, pg);
     const int64_t q = t - refs_upto(t + 1, dm.s);   // token ordinal of position t
     hipLaunchKernelGGL(append_merge_kernel, dim3((unsigned)U, (unsigned)n), dim3(64), 0, st, set,
-                       nsplit, dm.k, q, dm.N, pd, pj);
+                       nsplit, dm.k, q, dm.N, pd, pj, pg);
     return hipGetLastError();
 }
 

@@ -166,7 +166,8 @@ typedef struct {
  * 32-bit offsets) and capacity * P * (stride - 1) < 2^40 (UNSUPPORTED
  * otherwise).  The K and V caches of a
  * decode call must share one block table.  Paged caches are served by
- * deltakv_build_refs, deltakv_compress, deltakv_append (per-cache launches),
+ * deltakv_build_refs, deltakv_compress, deltakv_append (batched as for
+ * contiguous caches; a set may mix caches of one pool with different tables),
  * and the decode calls without a position list (deltakv_decode_attn, _noalloc,
  * _select, _window, _varlen) when the wave-specialised decode covers their
  * shapes (k 4 or 8, d_c <= 32, GELU decompressors of one hidden width, 128 or
