@@ -16,8 +16,16 @@ Parity status per function (what pins it; the tests under tests/ hold them):
   mlp / gelu        pinned: numpy matmul + scipy erf, standard-normal table
                     values, GELU limits.
   compress          pinned: closed form when all candidate refs are equal,
-                    orthogonal identity pair round trip.
-  reconstruct       pinned: orthogonal identity pair gives back the input.
+                    orthogonal identity pair round trip; latents under random
+                    GELU weights equal numpy matmuls + scipy erf applied to
+                    the numpy mean-and-residual of the listed references.
+  reconstruct       pinned: orthogonal identity pair gives back the input;
+                    under random GELU weights it equals the numpy rebuild.
+  decode_head       pinned: with the identity pair it is dense attention over
+                    the input rows; under random GELU weights it equals fp64
+                    SDPA over rows rebuilt by numpy + scipy erf; with GELU
+                    saturated off (each row KV_R + b2) or on (an affine
+                    Decompressor) it equals SDPA over the closed-form rows.
   attention         pinned: torch scaled_dot_product_attention in fp64 and the
                     q = 0 closed form.
   reconstruct_at    pinned: orthogonal identity pair gives back the input rows
@@ -50,8 +58,9 @@ Parity status per function (what pins it; the tests under tests/ hold them):
   gelu_vec / gelu_deriv pinned: the C oracle's gelu; finite differences.
   train_step        pinned: small steps lower the loss (descent direction);
                     the update is the stated rule on the pinned gradient.
-  Latent and decode values under random GELU weights have no printed value to
-  compare with; they are pinned only through the pieces above.
+  No page prints an intermediate value, so latents and decode outputs under
+  random GELU weights are pinned by independent compositions (numpy, scipy,
+  torch CPU) and closed forms, not by printed numbers.
 """
 import ctypes
 import os

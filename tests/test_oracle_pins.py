@@ -343,6 +343,74 @@ def _gelu_pair(rng, d, dc, h):
     return comp, dec
 
 
+def _sdpa64(q, kk, vv, scale):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(kk)[None], torch.from_numpy(vv)[None],
+        scale=scale)[0].numpy()
+
+
+def _np_rebuild(refs, lat, idx, T, s, dec, decoded=None):
+    """Rows of one head rebuilt by NumPy: reference positions copy their row;
+    every other position is the mean of its listed references plus the
+    Decompressor's output (or plus `decoded`, a closed form of that output)."""
+    pos = np.array([t for t in range(T) if t % s], dtype=np.int64)
+    out = np.empty((T, refs.shape[1]))
+    out[::s] = refs[:len(range(0, T, s))]
+    kvr = np.stack([refs[row[row >= 0]].mean(axis=0) for row in idx])
+    out[pos] = kvr + (_np_mlp(lat, dec) if decoded is None else decoded)
+    return out
+
+
+def _gelu_decode_case(seed, T=150, d=16, s=6, k=3, dc=5, h=24, G=3):
+    rng = _rng(seed)
+    kx = rng.standard_normal((T, d)) * 2
+    vx = rng.standard_normal((T, d))
+    kcomp, kdec = _gelu_pair(rng, d, dc, h)
+    vcomp, vdec = _gelu_pair(rng, d, dc, h)
+    kc = oracle.compress_head(kx, s, k, kcomp)
+    vc = oracle.compress_head(vx, s, k, vcomp)
+    q = rng.standard_normal((G, d))
+    return T, d, s, q, kc, kdec, vc, vdec
+
+
+def test_decode_with_gelu_weights_matches_numpy_rebuild_and_sdpa():
+    # random GELU Decompressors: the oracle's decode equals fp64 SDPA over rows
+    # rebuilt by NumPy matmuls and scipy's erf
+    T, d, s, q, (kr, ki, kl), kdec, (vr, vi, vl), vdec = _gelu_decode_case(31)
+    scale = 1 / np.sqrt(d)
+    got = oracle.decode_head(q, kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, scale)
+    want = _sdpa64(q, _np_rebuild(kr, kl, ki, T, s, kdec),
+                   _np_rebuild(vr, vl, vi, T, s, vdec), scale)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+@pytest.mark.parametrize("regime", ["off", "linear"])
+def test_decode_gelu_saturated_decompressor_closed_forms(regime):
+    # GELU(u) = u * Phi(u): with every hidden pre-activation pushed far below zero
+    # it is 0 in fp64 (Phi(-60) underflows), so each rebuilt row is KV_R + b2;
+    # pushed far above zero Phi is 1, the Decompressor is affine, and each row is
+    # KV_R + W2 (W1 latent + b1) + b2
+    T, d, s, q, (kr, ki, kl), kdec, (vr, vi, vl), vdec = _gelu_decode_case(32)
+    shift = -60.0 if regime == "off" else 60.0
+    kdec = MLP(kdec.w1, kdec.b1 + shift, kdec.w2, kdec.b2, ACT_GELU)
+    vdec = MLP(vdec.w1, vdec.b1 + shift, vdec.w2, vdec.b2, ACT_GELU)
+    for lat, m in ((kl, kdec), (vl, vdec)):
+        pre = lat @ m.w1.T + m.b1
+        assert (np.max(pre) < -40) if regime == "off" else (np.min(pre) > 40)
+
+    def closed(lat, m):
+        if regime == "off":
+            return np.broadcast_to(m.b2, (len(lat), len(m.b2)))
+        return (lat @ m.w1.T + m.b1) @ m.w2.T + m.b2
+
+    scale = 0.4
+    got = oracle.decode_head(q, kr, kl, ki, kdec, vr, vl, vi, vdec, T, s, scale)
+    khat = _np_rebuild(kr, kl, ki, T, s, kdec, closed(kl, kdec))
+    vhat = _np_rebuild(vr, vl, vi, T, s, vdec, closed(vl, vdec))
+    want = _sdpa64(q, khat, vhat, scale)
+    assert np.max(np.abs(got - want)) <= 1e-11 * np.max(np.abs(want))
+
+
 @pytest.mark.parametrize("d,s,k", [(32, 16, 4), (16, 5, 3), (16, 1, 2)])
 def test_reconstruct_at_identity_pair_gives_input_rows(d, s, k):
     # any order, references and compressed tokens mixed, repeats allowed
