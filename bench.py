@@ -472,8 +472,8 @@ def cpu_baseline(wl, widx, threads, budget_s=10.0, budget_1t_s=4.0):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); nothing to do for "
-              "more GPUs in this build", flush=True)
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}): the library runs "
+              "one GPU's share of the work and has no multi-GPU path", flush=True)
         sys.exit(2)
     from deltakv_synth import WORKLOADS, workload_index
     wl = WORKLOADS[a.workload]
