@@ -1587,11 +1587,16 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
     // (log2 P + log2 2D)
     constexpr int LRB = D == 128 ? 8 : 7;   // log2 of a row's bytes
     __shared__ int32_t ptab[PG ? kMaxPages : 1];
-    // paged, k = 4: the score waves, which read every token's V index entries
-    // a tile ahead anyway, turn them into the pool offsets of the V rows (one
-    // entry per lane) for the value waves' gathers of that tile (two slots:
-    // tile i + 1 is written while the value waves gather tile i)
-    constexpr bool PGS = PG && KX == 4;
+    // the score waves, which read every token's V index entries a tile ahead
+    // anyway, turn them into the byte offsets of the V rows (pool offsets for
+    // paged caches; one entry per (token, slot) row) for the value waves'
+    // gathers of that tile, which then need no index loads of their own after
+    // the first tile (two slots: the value waves gather tile i + 1 while the
+    // score waves write tile i + 2).  At k = 4 only: at k = 8 the value waves
+    // gather a tile at its start, and reading 32 offsets per lane from LDS
+    // there puts the LDS latency ahead of every gather (measured 15% slower
+    // than their own index loads, issued a tile ahead)
+    constexpr bool PGS = KX == 4;
     __shared__ uint32_t voff[PGS ? 2 : 1][PGS ? 32 * KX : 1];
     if constexpr (PG) {
         for (int i = tid; i < (int)pm.maxp; i += 256)
@@ -2101,19 +2106,20 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
             }
         };
         // unused slots (0xFFFF) and rows past the stored range read the last
-        // stored reference row: finite data under a zero weight
-        // (paged: gi holds pool offsets for tile 0, and the score waves'
-        // offsets in voff serve later tiles at k = 4)
+        // stored reference row: finite data under a zero weight.  Tile 0 takes
+        // its rows from the index entries in gi (paged: already pool offsets),
+        // later tiles from the offsets the score waves left in voff (without
+        // them, every tile from gi)
         auto gissue = [&](bf16_t (*dst)[D], int tile) {
 #pragma unroll
             for (int m = 0; m < NDMA; ++m) {
-                const uint32_t j = min(gi[m], rlast);
-                uint32_t pof = gi[m];
-                if constexpr (PGS)
-                    if (tile > 0) pof = voff[tile & 1][64 * vj + RPD * m + lrow] + coff;
+                uint32_t pof;
+                if (PGS && tile > 0)
+                    pof = voff[tile & 1][64 * vj + RPD * m + lrow] + coff;
+                else
+                    pof = PG ? gi[m] : min(gi[m], rlast) * (uint32_t)(D * 2) + coff;
                 __builtin_amdgcn_global_load_lds(
-                    (const void *)(PG ? (const char *)vref + pof
-                                      : (const char *)vref_u + (j * (uint32_t)(D * 2) + coff)),
+                    (const void *)((const char *)(PG ? vref : vref_u) + pof),
                     (__attribute__((address_space(3))) void *)&dst[(KX == 4 ? 64 * vj : 0) + RPD * m][0], 16, 0, 0);
             }
         };
@@ -2326,29 +2332,23 @@ __global__ __launch_bounds__(256, 2) void main_ws_kernel(
         gready();
         gissue(vbufA, 0);
         zload(qa, zA);
-        if (!PGS && ntile > 1) gload(qa + TT);
         wait_vm_all();
-        if (!PGS && ntile > 1) gready();
         __syncthreads();
         for (int it = 0; it < ntile; it += 2) {
             if (it + 1 < ntile) {
                 gissue(vbufB, it + 1);
                 zload(qa + (it + 1) * TT, zB);
-                if (!PGS && it + 2 < ntile) gload(qa + (it + 2) * TT);
             }
             vtile(it, zA, vbufA);
             wait_vm_all();
-            if (!PGS && it + 2 < ntile) gready();
             __syncthreads();
             if (it + 1 >= ntile) break;
             if (it + 2 < ntile) {
                 gissue(vbufA, it + 2);
                 zload(qa + (it + 2) * TT, zA);
-                if (!PGS && it + 3 < ntile) gload(qa + (it + 3) * TT);
             }
             vtile(it + 1, zB, vbufB);
             wait_vm_all();
-            if (!PGS && it + 3 < ntile) gready();
             __syncthreads();
         }
         }
