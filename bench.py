@@ -47,12 +47,12 @@ VALU_PEAK_GINSTR = 256 * 4 * 2.4 / 4
 # any change the dependent figures are reported as null until measured again.
 DECODE_COUNTERS = {
     "workload": "llama8b-32layer-T128k-bf16",
-    "source_sha256": "fd2fe00d6d25",
-    "fetch_kib": {"main_ws": 86367.3, "prep": 8549.2, "combine2": 2394.5},
-    "write_kib": {"main_ws": 3880.3, "prep": 1061.1, "combine2": 16.0},
+    "source_sha256": "9d028e5c45cb",
+    "fetch_kib": {"main_ws": 86439.0, "prep": 8549.1, "combine2": 2394.0},
+    "write_kib": {"main_ws": 3880.2, "prep": 1061.1, "combine2": 16.0},
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "valu_insts": {"main_ws": 44019448.3, "prep": 395776.0, "combine2": 100384.0},
+    "valu_insts": {"main_ws": 42491640.3, "prep": 395776.0, "combine2": 100384.0},
     "mfma_insts": {"main_ws": 3948544.0, "prep": 16416.0, "combine2": 0.0},
 }
 
