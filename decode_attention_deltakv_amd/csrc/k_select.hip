@@ -1619,8 +1619,12 @@ void launch_topk_t(const Dims &dm, const void *x, int64_t t0, int64_t t1, int64_
                    hipStream_t st) {
     const int U = dm.B * dm.H;
     const int ntiles = (int)((nq + 255) / 256);
+    // ordinal bits of the packed scores: enough for the references this call
+    // can see (those before t1), not for the cache's capacity, so that a
+    // chunk early in a prompt keeps more of each score's mantissa and fewer
+    // of its tokens fail the certificate
     int ibits = 1;
-    while (((int64_t)1 << ibits) < dm.R) ++ibits;
+    while (((int64_t)1 << ibits) < refs_upto(t1, dm.s)) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u;
     int nsplit, chunk;
     topk_split_plan(dm, t1, nq, &nsplit, &chunk);
